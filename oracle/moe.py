@@ -1,0 +1,281 @@
+"""Routing, quantize+permute, grouped expert forward and STE backward (oracle).
+
+TEST INFRASTRUCTURE ONLY -- see the package docstring.
+
+Notation: T tokens, H hidden, E experts, k experts per token, I SwiGLU width,
+A row alignment of each expert group.  Expert e's FC1 weight W1[e] is [2I, H]
+(rows 0..I-1 are the gate half, rows I..2I-1 the up half); its FC2 weight
+W2[e] is [H, I].  All arithmetic is float64; the BF16 roundings sit exactly
+where the GPU path stores BF16 tensors.
+
+The pages (rainbus review, "prerequisites: MoE and grouped GEMM"; AI summary,
+"Methodology in Plain English"; miniTE Technical Report, section 5.1) fix:
+per-token activation outer scales, per-row weight outer scales, expert FFN
+FC1 -> SwiGLU -> FC2 over ragged, possibly empty expert groups with
+device-side offsets, FP32 epilogue rescaling by g_x * g_w after the block-scaled
+product, BF16 only at the end, and a straight-through BF16 backward on the
+saved high-precision operands.  Points they leave open are marked READING.
+"""
+
+import numpy as np
+
+from . import nvfp4 as q
+
+
+# ---------------------------------------------------------------------------
+# a1: routing.
+# ---------------------------------------------------------------------------
+def rows_capacity(T, k, E, row_align):
+    """Upper bound on the padded dispatched-row count: T*k + E*(A-1)."""
+    return T * k + E * (row_align - 1)
+
+
+def route(topk_idx, E, row_align=1):
+    """Expert-contiguous row assignment.
+
+    READING (the rainbus review's method step 6 only says "sort" and
+    "padding carries statistics"; padding strategy is an implementation
+    freedom): rows of expert e are its tokens in ascending token order,
+    starting at off[e]; each group is padded to a multiple of ``row_align``;
+    pad rows have src_row = -1.
+
+    Returns (offsets int32 [E+1], row_map int32 [T, k], src_row int32 [off[E]]).
+    """
+    topk_idx = np.asarray(topk_idx, dtype=np.int64)
+    T, k = topk_idx.shape
+    counts = np.zeros(E, dtype=np.int64)
+    for e in topk_idx.reshape(-1):
+        counts[e] += 1
+    padded = (counts + row_align - 1) // row_align * row_align
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(padded)
+    row_map = np.empty((T, k), dtype=np.int64)
+    src_row = np.full(offsets[E], -1, dtype=np.int64)
+    fill = offsets[:E].copy()
+    for t in range(T):                       # ascending token order = stable
+        for j in range(k):
+            e = topk_idx[t, j]
+            row_map[t, j] = fill[e]
+            src_row[fill[e]] = t
+            fill[e] += 1
+    return offsets.astype(np.int32), row_map.astype(np.int32), src_row.astype(np.int32)
+
+
+def route_fast(topk_idx, E, row_align=1):
+    """Same result as ``route`` via vectorised numpy (for large T)."""
+    topk_idx = np.asarray(topk_idx, dtype=np.int64)
+    T, k = topk_idx.shape
+    flat = topk_idx.reshape(-1)
+    counts = np.bincount(flat, minlength=E)
+    padded = (counts + row_align - 1) // row_align * row_align
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(padded)
+    order = np.argsort(flat, kind="stable")          # entries grouped by expert, t ascending
+    starts = np.zeros(E + 1, dtype=np.int64)
+    starts[1:] = np.cumsum(counts)
+    e_sorted = flat[order]
+    rank = np.arange(flat.size) - starts[e_sorted]
+    rows = offsets[e_sorted] + rank
+    row_map = np.empty(flat.size, dtype=np.int64)
+    row_map[order] = rows
+    src_row = np.full(offsets[E], -1, dtype=np.int64)
+    src_row[rows] = order // k
+    return offsets.astype(np.int32), row_map.reshape(T, k).astype(np.int32), src_row.astype(np.int32)
+
+
+# ---------------------------------------------------------------------------
+# a2-a3: quantize + permute.
+# ---------------------------------------------------------------------------
+def quantize_permute(x, topk_idx, E, row_align=1, routed=None):
+    """Per-token NVFP4 of x, written to every destination row of the token.
+
+    The amax is per token (per dispatched row; the k copies of a token are
+    identical because the scale domain is the row), as in the rainbus
+    review's method step 4.  Pad rows get codes 0, scales 0 and g = 0.
+
+    Returns dict(codes [rows, K] unpacked, packed [rows, K/2], scales
+    [rows, K/16], outer [rows], offsets, row_map, src_row).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if routed is None:
+        routed = route_fast(topk_idx, E, row_align)
+    offsets, row_map, src_row = routed
+    rows = int(offsets[-1])
+    T, K = x.shape
+    tc, ts, tg = q.quantize_rows(x)          # token rows; copies share them
+    codes = np.zeros((rows, K), dtype=np.uint8)
+    scales = np.zeros((rows, K // q.BLOCK), dtype=np.uint8)
+    outer = np.zeros(rows, dtype=np.float32)
+    live = src_row >= 0
+    codes[live] = tc[src_row[live]]
+    scales[live] = ts[src_row[live]]
+    outer[live] = tg[src_row[live]]
+    return dict(codes=codes, packed=q.pack_codes(codes), scales=scales, outer=outer,
+                offsets=offsets, row_map=row_map, src_row=src_row)
+
+
+def quantize_weights(w):
+    """a4: per-row NVFP4 of stacked expert weights [E, N, K] (per output row n).
+
+    READING of "per row of the flattened expert weights" (Technical Report,
+    section 4.3 table): one outer scale per output feature n, over the
+    reduction axis K.
+    """
+    w = np.asarray(w, dtype=np.float64)
+    E, N, K = w.shape
+    c, s, g = q.quantize_rows(w.reshape(E * N, K))
+    return dict(codes=c.reshape(E, N, K), packed=q.pack_codes(c).reshape(E, N, K // 2),
+                scales=s.reshape(E, N, K // q.BLOCK), outer=g.reshape(E, N))
+
+
+# ---------------------------------------------------------------------------
+# a5-a9: forward.
+# ---------------------------------------------------------------------------
+def expert_of_rows(offsets):
+    """Expert id of every padded row."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    return np.repeat(np.arange(offsets.size - 1), np.diff(offsets))
+
+
+def grouped_gemm_nvfp4(a_codes, a_scales, a_outer, offsets, w_codes, w_scales, w_outer):
+    """Block-scaled grouped product with the FP32-epilogue outer factors.
+
+    For row r of expert e and output n:
+        out[r, n] = g_a[r] * g_w[e, n] * sum_k (d c)_a[r, k] (d c)_w[e, n, k]
+    (rainbus review, "core method": U_e = MMA(X_e, W_e^T), then g_x g_w
+    broadcast in the epilogue; the outer factors do not depend on k).
+    Returns float64 [rows, N]: the pre-cast value the GPU's FP32 epilogue
+    approximates.
+    """
+    offsets = np.asarray(offsets, dtype=np.int64)
+    rows = int(offsets[-1])
+    E, N, _ = w_codes.shape
+    out = np.zeros((rows, N))
+    for e in range(E):
+        r0, r1 = offsets[e], offsets[e + 1]
+        if r1 == r0:
+            continue
+        av = q.block_values(a_codes[r0:r1], a_scales[r0:r1])
+        wv = q.block_values(w_codes[e], w_scales[e])
+        acc = av @ wv.T
+        out[r0:r1] = acc * a_outer[r0:r1].astype(np.float64)[:, None] \
+            * w_outer[e].astype(np.float64)[None, :]
+    return out
+
+
+def swiglu(h, I):
+    """a = silu(gate) * up with gate = h[:, :I], up = h[:, I:] (float64).
+
+    READING: the pages name SwiGLU between FC1 and FC2 (rainbus review,
+    "prerequisites: MoE") but not the half order; the first I features are
+    the gate.
+    """
+    gate, up = h[:, :I], h[:, I:]
+    return gate / (1.0 + np.exp(-gate)) * up
+
+
+def forward(x, topk_idx, topk_w, w1q, w2q, E, row_align=1):
+    """Whole forward: quantize+permute, FC1, SwiGLU, requantize, FC2, unpermute.
+
+    Cast points (READING of "casts to BF16 only at the end", AI summary):
+    h = bf16(FC1); a = bf16(SwiGLU(h)); o = bf16(FC2); y = bf16(sum_j p o).
+    Router coefficients (READING; their position is an explicit
+    implementation freedom on the pages): applied in the unpermute, to the
+    bf16 o, summed over j in ascending order, one final bf16 rounding.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    T, H = x.shape
+    I = w1q["codes"].shape[1] // 2
+    xq = quantize_permute(x, topk_idx, E, row_align)
+    h64 = grouped_gemm_nvfp4(xq["codes"], xq["scales"], xq["outer"], xq["offsets"],
+                             w1q["codes"], w1q["scales"], w1q["outer"])
+    h = q.round_bf16(h64)
+    a = q.round_bf16(swiglu(h, I))
+    ac, as_, ag = q.quantize_rows(a)
+    live = xq["src_row"] >= 0
+    o64 = grouped_gemm_nvfp4(ac, as_, ag, xq["offsets"],
+                             w2q["codes"], w2q["scales"], w2q["outer"])
+    o = q.round_bf16(o64)
+    y = q.round_bf16(unpermute_sum(o, xq["row_map"], topk_w))
+    return dict(xq=xq, h64=h64, h=h, a=a, a_codes=ac, a_scales=as_, a_outer=ag,
+                o64=o64, o=o, y=y, live=live)
+
+
+def unpermute_sum(o, row_map, topk_w):
+    """y[t] = sum_j p[t, j] * o[row_map[t, j]] (float64, before the bf16 cast)."""
+    T, k = row_map.shape
+    p = np.asarray(topk_w, dtype=np.float64)
+    y = np.zeros((T, o.shape[1]))
+    for j in range(k):
+        y += p[:, j:j + 1] * o[row_map[:, j]]
+    return y
+
+
+# ---------------------------------------------------------------------------
+# b1-b7: straight-through BF16 backward.
+# ---------------------------------------------------------------------------
+def backward(dy, x, w1, w2, h, a, topk_w, offsets, row_map, src_row, rnd=True):
+    """Straight-through backward on the saved BF16 operands.
+
+    The quantisers are treated as identity (AI summary, "Methodology in
+    Plain English": a straight-through estimator on saved original BF16
+    activations and weights; Technical Report, section 4.3: the "layer
+    bypass" skips backward quantisation).  Saved operands: x, W1, W2 (bf16
+    originals), h (bf16 FC1 output), a (bf16 SwiGLU output).
+
+      b1  dO[r]   = p[t,j] dY[t]                 r = row_map[t, j]
+      b2  dA      = dO_e W2[e]                   [n_e, I]
+      b3  dW2[e]  = dO_e^T a_e                   [H, I]
+      b4  dgate   = dA * up * s (1 + gate (1 - s)),  dup = dA * gate * s,
+          s = sigmoid(gate)
+      b5  dXp     = dH_e W1[e]                   [n_e, H]
+      b6  dW1[e]  = dH_e^T x[src_row]            [2I, H]
+      b7  dX[t]   = sum_j dXp[row_map[t, j]]
+
+    With ``rnd`` every stored tensor (dO, dA, dH, dXp, dX, dW) is rounded to
+    bf16 as the GPU stores it; without it the function is the exact float64
+    derivative (used to pin it against autograd).
+    READINGS: dW and dX are bf16 tensors with FP32 accumulation on the GPU;
+    the router-weight gradient is not produced; dW of an empty expert is 0.
+    """
+    R = q.round_bf16 if rnd else (lambda v: v)
+    x = np.asarray(x, dtype=np.float64)
+    T, H = x.shape
+    E, I2, _ = w1.shape
+    I = I2 // 2
+    offsets = np.asarray(offsets, dtype=np.int64)
+    rows = int(offsets[-1])
+    k = row_map.shape[1]
+    p = np.asarray(topk_w, dtype=np.float64)
+
+    dO = np.zeros((rows, H))
+    for j in range(k):
+        dO[row_map[:, j]] = R(p[:, j:j + 1] * dy)
+
+    dA = np.zeros((rows, I))
+    dW2 = np.zeros((E, H, I))
+    for e in range(E):
+        r0, r1 = offsets[e], offsets[e + 1]
+        dA[r0:r1] = R(dO[r0:r1] @ w2[e])
+        dW2[e] = R(dO[r0:r1].T @ a[r0:r1])
+
+    gate, up = h[:, :I], h[:, I:]
+    s = 1.0 / (1.0 + np.exp(-gate))
+    dH = np.concatenate([R(dA * up * s * (1.0 + gate * (1.0 - s))),
+                         R(dA * gate * s)], axis=1)
+
+    xs = np.zeros((rows, H))
+    live = src_row >= 0
+    xs[live] = x[src_row[live]]
+    dXp = np.zeros((rows, H))
+    dW1 = np.zeros((E, I2, H))
+    for e in range(E):
+        r0, r1 = offsets[e], offsets[e + 1]
+        dXp[r0:r1] = R(dH[r0:r1] @ w1[e])
+        dW1[e] = R(dH[r0:r1].T @ xs[r0:r1])
+
+    dX = np.zeros((T, H))
+    for j in range(k):
+        dX += dXp[row_map[:, j]]
+    dX = R(dX)
+    return dict(dO=dO, dA=dA, dH=dH, dXp=dXp, dX=dX, dW1=dW1, dW2=dW2)
