@@ -1,0 +1,211 @@
+/*
+ * w4a4_moe.h -- C ABI of the MI355X (gfx950) per-token NVFP4 W4A4 MoE expert
+ * path: quantize+permute, grouped expert forward, straight-through backward.
+ *
+ * Conventions for every call
+ * --------------------------
+ *  - Pointers are DEVICE pointers unless marked (host).  Tensors are dense and
+ *    row-major with the shapes given.  bf16 tensors are passed as void*.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream).  The library never synchronises, never reads device data on the
+ *    host and never allocates or frees memory: the caller owns every buffer,
+ *    including the workspace, whose size w4a4_workspace_size() returns.
+ *  - Host-checkable arguments are validated before anything is launched; an
+ *    invalid call returns a negative status and launches nothing.  No C++
+ *    exception crosses this interface.  w4a4_last_error() gives detail.
+ *  - Routing validity (0 <= topk_idx < E, k distinct experts per token) is the
+ *    caller's contract and is not checked on the device.
+ *  - Results are bitwise reproducible from run to run, and a token's results
+ *    do not depend on the other tokens of the batch (per-token scale domain).
+ *  - Calls are thread-safe; concurrent calls on different streams need
+ *    different workspaces.
+ *
+ * Data formats (miniTE Technical Report, sections 2.2 and 5.1; rainbus review
+ * of the miniTE paper, "prerequisites: the NVFP4 format" and method step 4):
+ *  - E2M1 codes: 4 bits per element (sign in bit 3, magnitudes
+ *    {0,.5,1,1.5,2,3,4,6}), two per byte, element 2j in the low nibble of
+ *    byte j of the row.
+ *  - E4M3FN block scales: one byte per 16 consecutive elements of a row,
+ *    d = Q_E4M3(amax(block) / (6 g)).
+ *  - FP32 outer scale g per row: g = RN_f32(max|row| / (6*448)).
+ *    Activations: one per dispatched token row.  Weights: one per output row.
+ *  - Rounding is round-to-nearest-even of the exact quotient, ties to the
+ *    even code, E2M1 saturating at 6; a zero row or an underflowed block
+ *    encodes zero codes that keep the sign bit of x.
+ *
+ * Expert-contiguous layout (AI summary, "Methodology in Plain English"; rainbus
+ * review, method step 6): dispatched rows are grouped by expert, expert e
+ * owning rows [expert_offsets[e], expert_offsets[e+1]), its tokens in
+ * ascending token order, each group padded up to a multiple of row_align with
+ * pad rows whose codes, scales and g are zero.  The offsets live on the device
+ * only.  cap = w4a4_rows_capacity(T, k, E, row_align) bounds the padded row
+ * count; rows in [expert_offsets[E], cap) are never written.
+ */
+#ifndef W4A4_MOE_H
+#define W4A4_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  W4A4_OK = 0,
+  W4A4_ERR_INVALID_ARG = -1,  /* null / misaligned pointer, bad size or shape */
+  W4A4_ERR_UNSUPPORTED = -2,  /* valid but outside what the kernels support   */
+  W4A4_ERR_WORKSPACE = -3,    /* workspace pointer null or too small          */
+  W4A4_ERR_LAUNCH = -4        /* a kernel launch failed (HIP error)           */
+} w4a4_status;
+
+/* Which call a workspace is sized for. */
+typedef enum {
+  W4A4_WS_QUANTIZE_PERMUTE = 0,
+  W4A4_WS_FORWARD = 1,
+  W4A4_WS_BACKWARD = 2
+} w4a4_workspace_kind;
+
+/* Padded dispatched-row capacity: T*k + E*(row_align-1).  Returns -1 on bad
+ * arguments.  Host only, no device work. */
+int64_t w4a4_rows_capacity(int64_t T, int k, int E, int row_align);
+
+/* Workspace bytes needed by one call of the given kind.  For
+ * W4A4_WS_QUANTIZE_PERMUTE, K is the row length and I is ignored.  Returns 0
+ * on bad arguments.  Host only. */
+size_t w4a4_workspace_size(int kind, int64_t T, int H, int I, int E, int k, int row_align);
+
+/*
+ * w4a4_quantize_permute -- steps a1-a3: route the tokens to their experts and
+ * write each token's two-level NVFP4 encoding into every one of its k
+ * expert-contiguous destination rows.  The per-token amax is gathered in the
+ * same pass that reads the token (no separate amax scan).
+ *   Defined by: rainbus review, method steps 4 and 6 (per-token g, fused sort
+ *   and amax, padding that carries the statistics); miniTE Technical Report,
+ *   section 5.1 (block-scale equation); AI summary, "Methodology in Plain
+ *   English" (packed codes, block scales and outer scales written straight
+ *   into contiguous GEMM-consumed buffers, device-side expert offsets).
+ *
+ *   x          [T, K] bf16, K % 16 == 0, K >= 16.
+ *   topk_idx   [T, k] int32 expert ids, or NULL for identity routing (then
+ *              k must be 1, E must be 1 and row r is token r: this is how
+ *              weight rows are quantised, one outer scale per row).
+ *   row_align  1, 16, 32, 64 or 128.
+ *   codes      [cap, K/2] uint8 out.   scales [cap, K/16] uint8 out.
+ *   outer      [cap] float out.
+ *   expert_offsets [E+1] int32 out.    row_map [T, k] int32 out (dispatched
+ *              row of token t's j-th expert).  src_row [cap] int32 out (token
+ *              of each row, -1 for pad rows).
+ *   workspace  >= w4a4_workspace_size(W4A4_WS_QUANTIZE_PERMUTE, ...) bytes.
+ */
+w4a4_status w4a4_quantize_permute(
+    const void* x, int64_t T, int K,
+    const int32_t* topk_idx, int k, int E, int row_align,
+    uint8_t* codes, uint8_t* scales, float* outer,
+    int32_t* expert_offsets, int32_t* row_map, int32_t* src_row,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * w4a4_grouped_expert_fwd -- steps a5-a9: FC1 -> SwiGLU -> requantise -> FC2
+ * over ragged, possibly empty expert groups, then the router-weighted
+ * unpermute.
+ *   Defined by: rainbus review, "core method" and method steps 5-6 (block-
+ *   scaled accumulate U_e = MMA(X_e, W_e^T), then g_x g_w applied in FP32 in
+ *   the epilogue, BF16 cast at the end; FC1 and FC2 with their own tile
+ *   configurations); AI summary, "Methodology in Plain English" (each
+ *   dispatched row its own outer scale, decoded operands never materialised).
+ *
+ *   FC1: h[r, n] = bf16( (g_x[r] * g_w1[e,n]) * sum_k (d c)_x (d c)_w1 )
+ *        over n in [0, 2I); the first I rows of W1[e] are the SwiGLU gate,
+ *        the next I the up projection.
+ *   a   = bf16( silu(h_gate) * h_up ), FP32 arithmetic on the bf16 h.
+ *   a is requantised per dispatched row exactly as the activations are.
+ *   FC2: o[r, n] = bf16( (g_a[r] * g_w2[e,n]) * sum_i (d c)_a (d c)_w2 ).
+ *   y[t] = bf16( sum_{j=0..k-1} topk_w[t,j] * o[row_map[t,j]] ), FP32 sum
+ *        in ascending j.
+ *
+ *   x_codes/x_scales/x_outer, expert_offsets, row_map, src_row: as written by
+ *              w4a4_quantize_permute with K = H.
+ *   topk_w     [T, k] float router weights.
+ *   w1_codes [E, 2I, H/2], w1_scales [E, 2I, H/16], w1_outer [E, 2I];
+ *   w2_codes [E, H, I/2],  w2_scales [E, H, I/16],  w2_outer [E, H]
+ *              (weights quantised per row, e.g. by w4a4_quantize_permute
+ *              with identity routing on the [E*N, K] weight matrix).
+ *   y          [T, H] bf16 out.
+ *   save_h     optional [cap, 2I] bf16 out (FC1 output, for the backward).
+ *   save_a     optional [cap, I] bf16 out (SwiGLU output, for the backward).
+ *   dbg_fc1_f32 optional [cap, 2I] float out: FC1 epilogue values before the
+ *              bf16 cast.
+ *   dbg_a_codes [cap, I/2], dbg_a_scales [cap, I/16], dbg_a_outer [cap]:
+ *              optional copies of the FC2-input quantisation (all three or
+ *              none).
+ *   Optional outputs are skipped when NULL.  Rows of pad rows hold zeros.
+ *   Requirements: H % 256 == 0, I % 128 == 0 (else W4A4_ERR_UNSUPPORTED).
+ */
+w4a4_status w4a4_grouped_expert_fwd(
+    int64_t T, int H, int I, int E, int k, int row_align,
+    const uint8_t* x_codes, const uint8_t* x_scales, const float* x_outer,
+    const int32_t* expert_offsets, const int32_t* row_map, const int32_t* src_row,
+    const float* topk_w,
+    const uint8_t* w1_codes, const uint8_t* w1_scales, const float* w1_outer,
+    const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_outer,
+    void* y,
+    void* save_h, void* save_a,
+    float* dbg_fc1_f32,
+    uint8_t* dbg_a_codes, uint8_t* dbg_a_scales, float* dbg_a_outer,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * w4a4_expert_bwd -- steps b1-b7: the straight-through BF16 backward on the
+ * saved high-precision operands (no backward quantisation).
+ *   Defined by: AI summary, "Methodology in Plain English" (straight-through
+ *   estimator using saved original BF16 activations and weights); miniTE
+ *   Technical Report, section 4.3 (BF16 backward through the layer bypass on
+ *   the saved original operands).
+ *
+ *   dO[r]  = bf16(topk_w[t,j] * dy[t])                     (r = row_map[t,j])
+ *   dA     = bf16(dO_e W2[e]);        dW2[e] = bf16(dO_e^T a_e)
+ *   dgate  = bf16(dA * up * s * (1 + gate * (1 - s))),  s = sigmoid(gate)
+ *   dup    = bf16(dA * gate * s)      (gate, up = halves of the saved h)
+ *   dXp    = bf16(dH_e W1[e]);        dW1[e] = bf16(dH_e^T x[src_row])
+ *   dx[t]  = bf16(sum_j dXp[row_map[t,j]])
+ *   All products accumulate in FP32.
+ *
+ *   dy, x      [T, H] bf16.   w1 [E, 2I, H] bf16.   w2 [E, H, I] bf16.
+ *   save_h     [cap, 2I] bf16, save_a [cap, I] bf16 from the forward.
+ *   topk_w, expert_offsets, row_map, src_row as in the forward.
+ *   dx [T, H], dw1 [E, 2I, H], dw2 [E, H, I] bf16 out, fully overwritten
+ *   (zeros for an expert with no rows).
+ *   Requirements: H % 256 == 0, I % 128 == 0 (else W4A4_ERR_UNSUPPORTED).
+ */
+w4a4_status w4a4_expert_bwd(
+    int64_t T, int H, int I, int E, int k, int row_align,
+    const void* dy, const void* x,
+    const void* w1, const void* w2,
+    const void* save_h, const void* save_a, const float* topk_w,
+    const int32_t* expert_offsets, const int32_t* row_map, const int32_t* src_row,
+    void* dx, void* dw1, void* dw2,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* w4a4_status_string(int status);
+
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char* w4a4_last_error(void);
+
+/*
+ * Kernel timing (diagnostics; not a step of the method).  While enabled, every
+ * kernel the library launches is bracketed by HIP events on its stream.
+ * w4a4_profiler_report() synchronises those events and writes a JSON object
+ * {"kernel": {"count": n, "total_ms": t}, ...} into `buf` (host, `len`
+ * bytes, NUL-terminated); it returns the full length needed, or -1.
+ * Enabling, disabling or resetting drops the recorded events.  Not
+ * thread-safe; meant for single-threaded benchmarks.
+ */
+int w4a4_profiler_enable(int on);
+int w4a4_profiler_report(char* buf, size_t len);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* W4A4_MOE_H */

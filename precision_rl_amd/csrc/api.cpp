@@ -1,0 +1,371 @@
+// Host side of the C ABI declared in include/w4a4_moe.h: argument validation,
+// workspace carving and the launch sequence of each call.  No allocation, no
+// synchronisation, no device reads on the host.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+namespace w4a4 {
+namespace {
+
+thread_local std::string g_last_error;
+
+w4a4_status fail(w4a4_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+w4a4_status fail(w4a4_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool valid_align(int a) { return a == 1 || a == 16 || a == 32 || a == 64 || a == 128; }
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 8;
+constexpr int kMaxRowLen = 8192;
+
+// ------------------------------------------------------------------ profiler
+struct ProfEntry {
+  const char* name;
+  hipEvent_t start, stop;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfEntry> g_prof_entries;
+std::vector<hipEvent_t> g_prof_pool;
+size_t g_prof_pool_used = 0;
+
+hipEvent_t prof_event() {
+  if (g_prof_pool_used == g_prof_pool.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    g_prof_pool.push_back(e);
+  }
+  return g_prof_pool[g_prof_pool_used++];
+}
+
+void prof_clear() {
+  g_prof_entries.clear();
+  g_prof_pool_used = 0;
+}
+
+// Workspace layouts ---------------------------------------------------------
+struct FwdWs {
+  size_t a, a_codes, a_scales, a_outer, o, total;
+};
+FwdWs fwd_ws(int64_t cap, int H, int I) {
+  FwdWs w;
+  size_t off = 0;
+  w.a = off; off += round_up(static_cast<size_t>(cap) * I * 2);
+  w.a_codes = off; off += round_up(static_cast<size_t>(cap) * I / 2);
+  w.a_scales = off; off += round_up(static_cast<size_t>(cap) * I / 16);
+  w.a_outer = off; off += round_up(static_cast<size_t>(cap) * 4);
+  w.o = off; off += round_up(static_cast<size_t>(cap) * H * 2);
+  w.total = off;
+  return w;
+}
+struct BwdWs {
+  size_t dO, dH, dXp, total;
+};
+BwdWs bwd_ws(int64_t cap, int H, int I) {
+  BwdWs w;
+  size_t off = 0;
+  w.dO = off; off += round_up(static_cast<size_t>(cap) * H * 2);
+  w.dH = off; off += round_up(static_cast<size_t>(cap) * 2 * I * 2);
+  w.dXp = off; off += round_up(static_cast<size_t>(cap) * H * 2);
+  w.total = off;
+  return w;
+}
+
+w4a4_status check_moe_shape(int64_t T, int H, int I, int E, int k, int row_align) {
+  if (T < 0 || H <= 0 || I <= 0 || E <= 0 || k <= 0)
+    return fail(W4A4_ERR_INVALID_ARG, "non-positive size (T=%lld H=%d I=%d E=%d k=%d)",
+                static_cast<long long>(T), H, I, E, k);
+  if (H % 32 || I % 32) return fail(W4A4_ERR_INVALID_ARG, "H and I must be multiples of 32");
+  if (k > E) return fail(W4A4_ERR_INVALID_ARG, "k=%d > E=%d", k, E);
+  if (!valid_align(row_align)) return fail(W4A4_ERR_INVALID_ARG, "row_align %d not in {1,16,32,64,128}", row_align);
+  if (H % 256 || I % 128)
+    return fail(W4A4_ERR_UNSUPPORTED, "kernels need H %% 256 == 0 and I %% 128 == 0 (H=%d I=%d)", H, I);
+  if (H > kMaxRowLen || 2 * I > kMaxRowLen * 2 || I > kMaxRowLen)
+    return fail(W4A4_ERR_UNSUPPORTED, "H and I must be <= %d", kMaxRowLen);
+  if (E > kMaxExperts || k > kMaxTopK)
+    return fail(W4A4_ERR_UNSUPPORTED, "E <= %d and k <= %d supported", kMaxExperts, kMaxTopK);
+  return W4A4_OK;
+}
+
+#define REQUIRE_PTR(p)                                                                   \
+  do {                                                                                   \
+    if ((p) == nullptr) return fail(W4A4_ERR_INVALID_ARG, "%s is NULL", #p);             \
+    if (!aligned16(p)) return fail(W4A4_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p); \
+  } while (0)
+#define OPTIONAL_PTR(p)                                                                  \
+  do {                                                                                   \
+    if ((p) != nullptr && !aligned16(p))                                                 \
+      return fail(W4A4_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p);                 \
+  } while (0)
+
+}  // namespace
+
+void prof_begin(const char* name, hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on) return;
+  ProfEntry e{name, prof_event(), prof_event()};
+  if (!e.start || !e.stop) return;
+  (void)hipEventRecord(e.start, s);
+  g_prof_entries.push_back(e);
+}
+
+void prof_end(hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on || g_prof_entries.empty()) return;
+  (void)hipEventRecord(g_prof_entries.back().stop, s);
+}
+
+bool launch_ok(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    fail(W4A4_ERR_LAUNCH, "launch of %s failed: %s", what, hipGetErrorString(e));
+    return false;
+  }
+  return true;
+}
+
+}  // namespace w4a4
+
+using namespace w4a4;
+
+extern "C" {
+
+int64_t w4a4_rows_capacity(int64_t T, int k, int E, int row_align) {
+  if (T < 0 || k <= 0 || E <= 0 || !valid_align(row_align)) return -1;
+  return T * k + static_cast<int64_t>(E) * (row_align - 1);
+}
+
+size_t w4a4_workspace_size(int kind, int64_t T, int H, int I, int E, int k, int row_align) {
+  const int64_t cap = w4a4_rows_capacity(T, k, E, row_align);
+  if (cap < 0 || H <= 0) return 0;
+  switch (kind) {
+    case W4A4_WS_QUANTIZE_PERMUTE:
+      return round_up(route_workspace_bytes(T, E));
+    case W4A4_WS_FORWARD:
+      if (I <= 0) return 0;
+      return fwd_ws(cap, H, I).total;
+    case W4A4_WS_BACKWARD:
+      if (I <= 0) return 0;
+      return bwd_ws(cap, H, I).total;
+    default:
+      return 0;
+  }
+}
+
+w4a4_status w4a4_quantize_permute(const void* x, int64_t T, int K, const int32_t* topk_idx, int k,
+                                  int E, int row_align, uint8_t* codes, uint8_t* scales,
+                                  float* outer, int32_t* expert_offsets, int32_t* row_map,
+                                  int32_t* src_row, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  g_last_error.clear();
+  if (T < 0) return fail(W4A4_ERR_INVALID_ARG, "T < 0");
+  if (K < 16 || K % 16) return fail(W4A4_ERR_INVALID_ARG, "K=%d must be a positive multiple of 16", K);
+  if (K > kMaxRowLen) return fail(W4A4_ERR_UNSUPPORTED, "K=%d > %d", K, kMaxRowLen);
+  if (!valid_align(row_align)) return fail(W4A4_ERR_INVALID_ARG, "row_align %d not in {1,16,32,64,128}", row_align);
+  if (topk_idx == nullptr && T > 0) {
+    if (k != 1 || E != 1 || row_align != 1)
+      return fail(W4A4_ERR_INVALID_ARG, "identity routing needs k=1, E=1, row_align=1");
+  } else {
+    if (k <= 0 || E <= 0 || k > E) return fail(W4A4_ERR_INVALID_ARG, "bad k=%d / E=%d", k, E);
+    if (k > kMaxTopK || E > kMaxExperts)
+      return fail(W4A4_ERR_UNSUPPORTED, "E <= %d and k <= %d supported", kMaxExperts, kMaxTopK);
+    if (!aligned16(topk_idx)) return fail(W4A4_ERR_INVALID_ARG, "topk_idx is not 16-byte aligned");
+  }
+  REQUIRE_PTR(expert_offsets);
+  if (T > 0) {
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(codes);
+    REQUIRE_PTR(scales);
+    REQUIRE_PTR(outer);
+    REQUIRE_PTR(row_map);
+    REQUIRE_PTR(src_row);
+  }
+  if (T * static_cast<int64_t>(k) > (int64_t{1} << 31) - 1)
+    return fail(W4A4_ERR_UNSUPPORTED, "T*k exceeds int32 row indices");
+  const size_t need = w4a4_workspace_size(W4A4_WS_QUANTIZE_PERMUTE, T, K, 0, E, k, row_align);
+  if (topk_idx != nullptr && T > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(W4A4_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  OPTIONAL_PTR(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!launch_quantize_permute(static_cast<const uint16_t*>(x), T, K, topk_idx, k, E, row_align,
+                               codes, scales, outer, expert_offsets, row_map, src_row, workspace, s))
+    return W4A4_ERR_LAUNCH;
+  return W4A4_OK;
+}
+
+w4a4_status w4a4_grouped_expert_fwd(
+    int64_t T, int H, int I, int E, int k, int row_align, const uint8_t* x_codes,
+    const uint8_t* x_scales, const float* x_outer, const int32_t* expert_offsets,
+    const int32_t* row_map, const int32_t* src_row, const float* topk_w, const uint8_t* w1_codes,
+    const uint8_t* w1_scales, const float* w1_outer, const uint8_t* w2_codes,
+    const uint8_t* w2_scales, const float* w2_outer, void* y, void* save_h, void* save_a,
+    float* dbg_fc1_f32, uint8_t* dbg_a_codes, uint8_t* dbg_a_scales, float* dbg_a_outer,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  w4a4_status st = check_moe_shape(T, H, I, E, k, row_align);
+  if (st != W4A4_OK) return st;
+  REQUIRE_PTR(expert_offsets);
+  REQUIRE_PTR(w1_codes); REQUIRE_PTR(w1_scales); REQUIRE_PTR(w1_outer);
+  REQUIRE_PTR(w2_codes); REQUIRE_PTR(w2_scales); REQUIRE_PTR(w2_outer);
+  if (T > 0) {
+    REQUIRE_PTR(x_codes); REQUIRE_PTR(x_scales); REQUIRE_PTR(x_outer);
+    REQUIRE_PTR(row_map); REQUIRE_PTR(src_row); REQUIRE_PTR(topk_w); REQUIRE_PTR(y);
+  }
+  OPTIONAL_PTR(save_h); OPTIONAL_PTR(save_a); OPTIONAL_PTR(dbg_fc1_f32);
+  OPTIONAL_PTR(dbg_a_codes); OPTIONAL_PTR(dbg_a_scales); OPTIONAL_PTR(dbg_a_outer);
+  const int nd = (dbg_a_codes != nullptr) + (dbg_a_scales != nullptr) + (dbg_a_outer != nullptr);
+  if (nd != 0 && nd != 3)
+    return fail(W4A4_ERR_INVALID_ARG, "dbg_a_codes, dbg_a_scales, dbg_a_outer: all or none");
+  const int64_t cap = w4a4_rows_capacity(T, k, E, row_align);
+  const FwdWs L = fwd_ws(cap, H, I);
+  if (workspace == nullptr || workspace_bytes < L.total)
+    return fail(W4A4_ERR_WORKSPACE, "workspace needs %zu bytes", L.total);
+  OPTIONAL_PTR(workspace);
+  if (cap == 0) return W4A4_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint16_t* a_buf = save_a ? static_cast<uint16_t*>(save_a) : reinterpret_cast<uint16_t*>(ws + L.a);
+  uint8_t* a_codes = nd ? dbg_a_codes : ws + L.a_codes;
+  uint8_t* a_scales = nd ? dbg_a_scales : ws + L.a_scales;
+  float* a_outer = nd ? dbg_a_outer : reinterpret_cast<float*>(ws + L.a_outer);
+  uint16_t* o_buf = reinterpret_cast<uint16_t*>(ws + L.o);
+
+  if (!launch_fc1(cap, H, I, E, expert_offsets, Fp4Operand{x_codes, x_scales, x_outer},
+                  Fp4Operand{w1_codes, w1_scales, w1_outer}, static_cast<uint16_t*>(save_h), a_buf,
+                  dbg_fc1_f32, s))
+    return W4A4_ERR_LAUNCH;
+  if (!launch_requant(a_buf, cap, I, expert_offsets, E, src_row, a_codes, a_scales, a_outer, s))
+    return W4A4_ERR_LAUNCH;
+  if (!launch_fc2(cap, H, I, E, expert_offsets, Fp4Operand{a_codes, a_scales, a_outer},
+                  Fp4Operand{w2_codes, w2_scales, w2_outer}, o_buf, s))
+    return W4A4_ERR_LAUNCH;
+  if (!launch_unpermute(T, H, k, o_buf, row_map, topk_w, static_cast<uint16_t*>(y), s))
+    return W4A4_ERR_LAUNCH;
+  return W4A4_OK;
+}
+
+w4a4_status w4a4_expert_bwd(int64_t T, int H, int I, int E, int k, int row_align, const void* dy,
+                            const void* x, const void* w1, const void* w2, const void* save_h,
+                            const void* save_a, const float* topk_w,
+                            const int32_t* expert_offsets, const int32_t* row_map,
+                            const int32_t* src_row, void* dx, void* dw1, void* dw2,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  w4a4_status st = check_moe_shape(T, H, I, E, k, row_align);
+  if (st != W4A4_OK) return st;
+  REQUIRE_PTR(expert_offsets);
+  REQUIRE_PTR(w1); REQUIRE_PTR(w2); REQUIRE_PTR(dw1); REQUIRE_PTR(dw2);
+  if (T > 0) {
+    REQUIRE_PTR(dy); REQUIRE_PTR(x); REQUIRE_PTR(save_h); REQUIRE_PTR(save_a);
+    REQUIRE_PTR(topk_w); REQUIRE_PTR(row_map); REQUIRE_PTR(src_row); REQUIRE_PTR(dx);
+  }
+  const int64_t cap = w4a4_rows_capacity(T, k, E, row_align);
+  const BwdWs L = bwd_ws(cap, H, I);
+  if (workspace == nullptr || workspace_bytes < L.total)
+    return fail(W4A4_ERR_WORKSPACE, "workspace needs %zu bytes", L.total);
+  OPTIONAL_PTR(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint16_t* dO = reinterpret_cast<uint16_t*>(ws + L.dO);
+  uint16_t* dH = reinterpret_cast<uint16_t*>(ws + L.dH);
+  uint16_t* dXp = reinterpret_cast<uint16_t*>(ws + L.dXp);
+  const uint16_t* h = static_cast<const uint16_t*>(save_h);
+  const uint16_t* a = static_cast<const uint16_t*>(save_a);
+  const uint16_t* W1 = static_cast<const uint16_t*>(w1);
+  const uint16_t* W2 = static_cast<const uint16_t*>(w2);
+
+  if (cap > 0) {
+    if (!launch_gather_scale(cap, H, k, static_cast<const uint16_t*>(dy), row_map, src_row, topk_w,
+                             expert_offsets, E, dO, s))
+      return W4A4_ERR_LAUNCH;
+    if (!launch_dgrad_fc2(cap, H, I, E, expert_offsets, dO, W2, h, dH, s)) return W4A4_ERR_LAUNCH;
+  }
+  if (!launch_wgrad_fc2(H, I, E, expert_offsets, dO, a, static_cast<uint16_t*>(dw2), s))
+    return W4A4_ERR_LAUNCH;
+  if (cap > 0 && !launch_dgrad_fc1(cap, H, I, E, expert_offsets, dH, W1, dXp, s))
+    return W4A4_ERR_LAUNCH;
+  if (!launch_wgrad_fc1(H, I, E, expert_offsets, dH, static_cast<const uint16_t*>(x), src_row,
+                        static_cast<uint16_t*>(dw1), s))
+    return W4A4_ERR_LAUNCH;
+  if (!launch_gather_sum(T, H, k, dXp, row_map, static_cast<uint16_t*>(dx), s))
+    return W4A4_ERR_LAUNCH;
+  return W4A4_OK;
+}
+
+const char* w4a4_status_string(int status) {
+  switch (status) {
+    case W4A4_OK: return "ok";
+    case W4A4_ERR_INVALID_ARG: return "invalid argument";
+    case W4A4_ERR_UNSUPPORTED: return "unsupported configuration";
+    case W4A4_ERR_WORKSPACE: return "workspace missing or too small";
+    case W4A4_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* w4a4_last_error(void) { return g_last_error.c_str(); }
+
+int w4a4_profiler_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  prof_clear();
+  g_prof_on = on != 0;
+  return 0;
+}
+
+int w4a4_profiler_report(char* buf, size_t len) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  struct Agg {
+    int count = 0;
+    double ms = 0.0;
+  };
+  std::map<std::string, Agg> agg;
+  for (const ProfEntry& e : g_prof_entries) {
+    if (hipEventSynchronize(e.stop) != hipSuccess) return -1;
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, e.start, e.stop) != hipSuccess) return -1;
+    Agg& a = agg[e.name];
+    a.count += 1;
+    a.ms += ms;
+  }
+  std::string out = "{";
+  bool first = true;
+  for (const auto& kv : agg) {
+    char item[256];
+    snprintf(item, sizeof item, "%s\"%s\": {\"count\": %d, \"total_ms\": %.6f}", first ? "" : ", ",
+             kv.first.c_str(), kv.second.count, kv.second.ms);
+    out += item;
+    first = false;
+  }
+  out += "}";
+  if (buf != nullptr && len > 0) {
+    const size_t n = out.size() < len - 1 ? out.size() : len - 1;
+    memcpy(buf, out.data(), n);
+    buf[n] = '\0';
+  }
+  return static_cast<int>(out.size());
+}
+
+}  // extern "C"

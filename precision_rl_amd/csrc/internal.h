@@ -1,0 +1,86 @@
+// Internal declarations shared by the HIP sources of libw4a4moe (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/w4a4_moe.h"
+
+namespace w4a4 {
+
+// ---------------------------------------------------------------- profiling
+// Brackets a launch with HIP events when kernel timing is enabled.
+void prof_begin(const char* name, hipStream_t s);
+void prof_end(hipStream_t s);
+
+struct ProfScope {
+  hipStream_t s;
+  ProfScope(const char* name, hipStream_t st) : s(st) { prof_begin(name, st); }
+  ~ProfScope() { prof_end(s); }
+};
+
+// Records the HIP error of the last launch; returns false on failure.
+bool launch_ok(const char* what);
+
+// ------------------------------------------------------------ routing / quant
+constexpr int kRouteChunk = 256;      // tokens per routing chunk (one workgroup)
+
+size_t route_workspace_bytes(int64_t T, int E);
+
+// a1 + a2 + a3: route, per-token amax, two-level NVFP4, scatter to k rows.
+bool launch_quantize_permute(const uint16_t* x, int64_t T, int K, const int32_t* topk_idx,
+                             int k, int E, int row_align, uint8_t* codes, uint8_t* scales,
+                             float* outer, int32_t* offsets, int32_t* row_map, int32_t* src_row,
+                             void* ws, hipStream_t s);
+
+// a7: per-row NVFP4 of the bf16 rows of `a` ([rows_alloc, K]) for the rows
+// [0, offsets[E]) (device bound); pad rows (src_row < 0) get zeros.
+bool launch_requant(const uint16_t* a, int64_t rows_alloc, int K, const int32_t* offsets, int E,
+                    const int32_t* src_row, uint8_t* codes, uint8_t* scales, float* outer,
+                    hipStream_t s);
+
+// --------------------------------------------------------------- grouped GEMMs
+struct Fp4Operand {
+  const uint8_t* codes;   // [rows, K/2]
+  const uint8_t* scales;  // [rows, K/16]
+  const float* outer;     // [rows]
+};
+
+// a5 (+ fused a6): FC1 over expert groups, SwiGLU in the epilogue.
+bool launch_fc1(int64_t rows_alloc, int H, int I, int E, const int32_t* offsets, Fp4Operand x,
+                Fp4Operand w1, uint16_t* h_out, uint16_t* a_out, float* dbg_f32, hipStream_t s);
+
+// a8: FC2 over expert groups.
+bool launch_fc2(int64_t rows_alloc, int H, int I, int E, const int32_t* offsets, Fp4Operand a,
+                Fp4Operand w2, uint16_t* o_out, hipStream_t s);
+
+// a9: y[t] = bf16(sum_j p[t,j] o[row_map[t,j]]).
+bool launch_unpermute(int64_t T, int H, int k, const uint16_t* o, const int32_t* row_map,
+                      const float* topk_w, uint16_t* y, hipStream_t s);
+
+// b1: dO[r] = bf16(p dY[t]); pad rows zero.
+bool launch_gather_scale(int64_t rows_alloc, int H, int k, const uint16_t* dy,
+                         const int32_t* row_map, const int32_t* src_row, const float* topk_w,
+                         const int32_t* offsets, int E, uint16_t* dO, hipStream_t s);
+
+// b2 + fused b4: dA = bf16(dO_e W2[e]) then the SwiGLU backward -> dH.
+bool launch_dgrad_fc2(int64_t rows_alloc, int H, int I, int E, const int32_t* offsets,
+                      const uint16_t* dO, const uint16_t* w2, const uint16_t* h, uint16_t* dH,
+                      hipStream_t s);
+
+// b5: dXp = bf16(dH_e W1[e]).
+bool launch_dgrad_fc1(int64_t rows_alloc, int H, int I, int E, const int32_t* offsets,
+                      const uint16_t* dH, const uint16_t* w1, uint16_t* dXp, hipStream_t s);
+
+// b3: dW2[e] = bf16(dO_e^T a_e).   b6: dW1[e] = bf16(dH_e^T x[src_row]).
+bool launch_wgrad_fc2(int H, int I, int E, const int32_t* offsets, const uint16_t* dO,
+                      const uint16_t* a, uint16_t* dW2, hipStream_t s);
+bool launch_wgrad_fc1(int H, int I, int E, const int32_t* offsets, const uint16_t* dH,
+                      const uint16_t* x, const int32_t* src_row, uint16_t* dW1, hipStream_t s);
+
+// b7: dX[t] = bf16(sum_j dXp[row_map[t,j]]).
+bool launch_gather_sum(int64_t T, int H, int k, const uint16_t* dXp, const int32_t* row_map,
+                       uint16_t* dx, hipStream_t s);
+
+}  // namespace w4a4

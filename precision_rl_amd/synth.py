@@ -113,7 +113,7 @@ def t3_bf16(rng, shape):
 
 
 def make_inputs(T, H, E, k, I=0, routing="uniform", x_dist="normal", backward=False,
-                seed=1000, weights=True):
+                seed=1000, weights=True, n_empty=ZIPF_EMPTY):
     """Draw one workload's inputs.  Returns a dict of numpy arrays.
 
     x, w1, w2, dy are bf16 bit patterns (uint16); topk_idx int32 [T, k];
@@ -124,8 +124,10 @@ def make_inputs(T, H, E, k, I=0, routing="uniform", x_dist="normal", backward=Fa
     if routing == "uniform":
         out["topk_idx"], out["topk_w"] = uniform_router(rs["router"], T, E, k)
     elif routing == "zipf":
+        if E - n_empty < k:
+            raise ValueError("the skewed router needs at least k experts with tokens")
         out["topk_idx"], out["topk_w"], out["empty_experts"] = zipf_router(
-            rs["router"], rs["popularity"], T, E, k)
+            rs["router"], rs["popularity"], T, E, k, n_empty=n_empty)
     else:
         raise ValueError(routing)
     out["x"] = t3_bf16(rs["x"], (T, H)) if x_dist == "t3" else normal_bf16(rs["x"], (T, H))

@@ -1,0 +1,85 @@
+"""The C-ABI library loads on the host, exports every symbol its header
+declares, and rejects invalid arguments with the documented status before
+any launch (host-side checks only: no compute call needs a GPU here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+pytestmark = pytest.mark.cpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a4_moe.h")
+
+
+def _lib():
+    from precision_rl_amd import build, binding
+    if not os.path.exists(build.LIB):
+        build.build()
+    return binding.load()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4a4_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_calls():
+    syms = declared_symbols()
+    for name in ("w4a4_quantize_permute", "w4a4_grouped_expert_fwd", "w4a4_expert_bwd"):
+        assert name in syms
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_capacity_and_workspace_sizes():
+    lib = _lib()
+    assert lib.w4a4_rows_capacity(16384, 8, 128, 1) == 131072
+    assert lib.w4a4_rows_capacity(10, 2, 8, 16) == 20 + 8 * 15
+    assert lib.w4a4_rows_capacity(10, 2, 8, 3) == -1
+    assert lib.w4a4_workspace_size(1, 8192, 2048, 768, 128, 8, 1) > 0
+    assert lib.w4a4_workspace_size(7, 8192, 2048, 768, 128, 8, 1) == 0
+
+
+def test_invalid_arguments_rejected_before_launch():
+    lib = _lib()
+    from precision_rl_amd import binding as b
+    buf = ctypes.create_string_buffer(4096)
+    p = ctypes.c_void_p(ctypes.addressof(buf) + (-ctypes.addressof(buf)) % 16)
+
+    def qp(T=4, K=32, idx=p, k=2, E=8, A=1, x=p, ws=p, wsb=1024):
+        return lib.w4a4_quantize_permute(x, T, K, idx, k, E, A, p, p, p, p, p, p, ws, wsb, None)
+
+    assert qp(K=24) == -1                              # K % 16 != 0
+    assert qp(A=3) == -1                               # bad row_align
+    assert qp(k=9, E=8) == -1                          # k > E
+    assert qp(k=9, E=16) == -2                         # k > 8 unsupported
+    assert qp(x=None) == -1                            # null input
+    assert qp(x=ctypes.c_void_p(p.value + 2)) == -1    # misaligned
+    assert qp(ws=None) == -3                           # no workspace
+    assert qp(idx=None, k=2) == -1                     # identity needs k = 1
+    assert b.load().w4a4_last_error().decode()
+    assert lib.w4a4_status_string(-3).decode() == "workspace missing or too small"
+
+    def fwd(H=256, I=128, T=4, ws=p, wsb=1 << 40):
+        return lib.w4a4_grouped_expert_fwd(T, H, I, 8, 2, 1, p, p, p, p, p, p, p, p, p, p, p, p, p,
+                                           p, None, None, None, None, None, None, ws, wsb, None)
+
+    assert fwd(H=250) == -1                            # not a multiple of 32
+    assert fwd(H=288) == -2                            # multiple of 32 but not of 256
+    assert fwd(I=96) == -2
+    assert fwd(ws=None) == -3
+    assert fwd(wsb=16) == -3
+
+    def bwd(H=256, I=128, T=4):
+        return lib.w4a4_expert_bwd(T, H, I, 8, 2, 1, p, p, p, p, p, p, p, p, p, p, p, p, p,
+                                   None, 0, None)
+
+    assert bwd() == -3                                 # no workspace
+    assert bwd(I=100) == -1

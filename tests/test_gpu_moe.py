@@ -1,0 +1,249 @@
+"""GPU parity of the grouped expert forward (a5-a9) and the straight-through
+backward (b1-b7) against the FP64 oracle.
+
+Bars: FC1 pre-cast values rel-L2 <= 1e-5 (bit-exact on lossless inputs);
+<= 0.1 % of the requantised FC2-input codes differ; y rel-L2 <= 2e-3;
+dX, dW1, dW2 rel-L2 <= 1e-2 each; codes, scales, outer scales and the
+permutation bit-exact.
+"""
+import numpy as np
+import pytest
+
+from oracle import moe, nvfp4 as q
+from precision_rl_amd import synth
+from gpu_util import bf16_dev, bf16_host, u8, f32_bits, rel_l2, print_case
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+FC1_TOL = 1e-5
+Y_TOL = 2e-3
+CODE_FLIP_BUDGET = 1e-3
+BWD_TOL = 1e-2
+
+
+def _binding():
+    from precision_rl_amd import binding
+    return binding
+
+
+class Run:
+    """One GPU forward (+ optional backward) of a workload through the C ABI."""
+
+    def __init__(self, d, T, H, E, k, I, A=1, backward=False):
+        b = _binding()
+        self.d, self.T, self.H, self.E, self.k, self.I, self.A = d, T, H, E, k, I, A
+        self.x = bf16_dev(d["x"], torch)
+        self.idx = torch.from_numpy(d["topk_idx"]).cuda()
+        self.p = torch.from_numpy(d["topk_w"]).cuda()
+        self.w1 = bf16_dev(d["w1"], torch)
+        self.w2 = bf16_dev(d["w2"], torch)
+        self.w1q = b.quantize_weights(self.w1)
+        self.w2q = b.quantize_weights(self.w2)
+        self.xq = b.w4a4_quantize_permute(self.x, self.idx, E, A)
+        self.f = b.w4a4_grouped_expert_fwd(self.xq, self.p, self.w1q, self.w2q, T, H, I, E, k, A,
+                                           save=True, debug=True)
+        if backward:
+            self.dy = bf16_dev(d["dy"], torch)
+            self.g = b.w4a4_expert_bwd(self.dy, self.x, self.w1, self.w2, self.f["h"], self.f["a"],
+                                       self.p, self.xq, T, H, I, E, k, A)
+        torch.cuda.synchronize()
+        self.rows = int(self.xq["offsets"][-1].item())
+
+
+def _oracle_fwd(d, E, A):
+    x = q.bf16_bits_to_f64(d["x"])
+    w1q = moe.quantize_weights(q.bf16_bits_to_f64(d["w1"]))
+    w2q = moe.quantize_weights(q.bf16_bits_to_f64(d["w2"]))
+    return moe.forward(x, d["topk_idx"], d["topk_w"], w1q, w2q, E, A), w1q, w2q
+
+
+def _check_forward(run, ref):
+    rows = run.rows
+    live = ref["xq"]["src_row"] >= 0
+    # permutation and activation encoding: bit-exact
+    assert np.array_equal(run.xq["row_map"].cpu().numpy(), ref["xq"]["row_map"])
+    assert np.array_equal(u8(run.xq["codes"])[:rows], ref["xq"]["packed"])
+    # FC1 pre-cast values
+    fc1 = run.f["fc1_f32"].cpu().numpy()[:rows]
+    e1 = rel_l2(fc1[live], ref["h64"][live])
+    assert e1 <= FC1_TOL, e1
+    # pad rows are zeros
+    assert not fc1[~live].any()
+    # FC2-input codes
+    gc = q.unpack_codes(u8(run.f["a_codes"])[:rows])[live]
+    flips = np.mean(gc != ref["a_codes"][live])
+    assert flips <= CODE_FLIP_BUDGET, flips
+    # final output
+    y = bf16_host(run.f["y"])
+    ey = rel_l2(y, ref["y"])
+    assert ey <= Y_TOL, ey
+    return e1, flips, ey
+
+
+@pytest.mark.parametrize("A", [1, 16])
+def test_forward_tiny(A):
+    w = synth.WORKLOADS["tiny"]
+    d = synth.workload_inputs("tiny")
+    print_case("forward_tiny", T=w.T, H=w.H, E=w.E, k=w.k, I=w.I, A=A)
+    run = Run(d, w.T, w.H, w.E, w.k, w.I, A)
+    ref, _, _ = _oracle_fwd(d, w.E, A)
+    print(_check_forward(run, ref))
+
+
+def test_forward_ragged_empty_multi_tile():
+    """Skewed routing, empty experts, groups spanning several 256-row tiles
+    with ragged tails, several N tiles, row_align 32."""
+    T, H, E, k, I = 1200, 512, 12, 4, 256
+    d = synth.make_inputs(T, H, E, k, I, routing="zipf", seed=91, n_empty=3)
+    empty = set(range(E)) - set(np.unique(d["topk_idx"]))
+    print_case("forward_ragged", T=T, H=H, E=E, k=k, I=I, empty=len(empty))
+    run = Run(d, T, H, E, k, I, A=32)
+    ref, _, _ = _oracle_fwd(d, E, 32)
+    print(_check_forward(run, ref))
+
+
+def test_forward_lossless_fc1_bit_exact():
+    """Inputs NVFP4 encodes exactly (g = 2^j, elements g d c): the FC1 sums
+    are exact in FP32 in any order, so the GPU's pre-cast FC1 values must equal
+    the oracle's bit for bit."""
+    rng = np.random.default_rng(17)
+    T, H, E, k, I = 96, 256, 4, 2, 128
+
+    def lossless(R, K, gexp):
+        out = np.zeros((R, K))
+        for r in range(R):
+            g = 2.0 ** gexp[r]
+            for bk in range(K // 16):
+                dd = 448.0 * 2.0 ** -int(rng.integers(0, 3)) if bk else 448.0
+                c = rng.choice(q.E2M1_MAGNITUDES, 16) * rng.choice([-1, 1], 16)
+                c[0] = 6.0
+                out[r, bk * 16:(bk + 1) * 16] = g * dd * c
+        return out
+
+    x = lossless(T, H, rng.integers(-14, -10, T))
+    w1 = lossless(E * 2 * I, H, rng.integers(-14, -10, E * 2 * I)).reshape(E, 2 * I, H)
+    d = synth.make_inputs(T, H, E, k, I, seed=3)
+    d["x"] = q.f64_to_bf16_bits(x)
+    d["w1"] = q.f64_to_bf16_bits(w1)
+    assert np.array_equal(q.bf16_bits_to_f64(d["x"]), x)
+    print_case("forward_lossless", T=T, H=H, E=E, k=k, I=I)
+    run = Run(d, T, H, E, k, I)
+    ref, _, _ = _oracle_fwd(d, E, 1)
+    rows = run.rows
+    fc1 = run.f["fc1_f32"].cpu().numpy()[:rows].astype(np.float64)
+    assert np.array_equal(fc1, ref["h64"]), np.abs(fc1 - ref["h64"]).max()
+
+
+def test_forward_deterministic():
+    T, H, E, k, I = 256, 512, 8, 2, 256
+    d = synth.make_inputs(T, H, E, k, I, seed=8)
+    print_case("forward_determinism", T=T, H=H, E=E, k=k, I=I)
+    r1 = Run(d, T, H, E, k, I)
+    r2 = Run(d, T, H, E, k, I)
+    for key in ("y", "h", "a", "fc1_f32", "a_codes"):
+        assert torch.equal(r1.f[key], r2.f[key]), key
+
+
+def test_forward_full_fwd_workload_sampled():
+    """The forward workload at full size (T=8192, H=2048, E=128, k=8, I=768);
+    outputs of sampled tokens checked against the oracle computed on those
+    tokens alone (a token's outputs depend only on its own row)."""
+    w = synth.WORKLOADS["fwd"]
+    d = synth.workload_inputs("fwd")
+    print_case("forward_full_sampled", T=w.T, H=w.H, E=w.E, k=w.k, I=w.I)
+    run = Run(d, w.T, w.H, w.E, w.k, w.I)
+    sample = np.array([0, 1, 4097, w.T - 1])
+    experts = np.unique(d["topk_idx"][sample])
+    # oracle on the sampled tokens, with only the experts they use
+    remap = -np.ones(w.E, dtype=np.int64)
+    remap[experts] = np.arange(experts.size)
+    sub = dict(x=d["x"][sample], topk_idx=remap[d["topk_idx"][sample]].astype(np.int32),
+               topk_w=d["topk_w"][sample], w1=d["w1"][experts], w2=d["w2"][experts])
+    ref, w1q, _ = _oracle_fwd(sub, experts.size, 1)
+    # weight encodings of those experts: bit-exact
+    assert np.array_equal(u8(run.w1q["codes"])[experts], w1q["packed"])
+    assert np.array_equal(u8(run.w1q["scales"])[experts], w1q["scales"])
+    rows_gpu = run.xq["row_map"].cpu().numpy()[sample].reshape(-1)
+    rows_ref = ref["xq"]["row_map"].reshape(-1)
+    fc1 = run.f["fc1_f32"].cpu().numpy()[rows_gpu]
+    assert rel_l2(fc1, ref["h64"][rows_ref]) <= FC1_TOL
+    gc = q.unpack_codes(u8(run.f["a_codes"])[rows_gpu])
+    assert np.mean(gc != ref["a_codes"][rows_ref]) <= CODE_FLIP_BUDGET
+    y = bf16_host(run.f["y"])[sample]
+    assert rel_l2(y, ref["y"]) <= Y_TOL
+
+
+# ------------------------------------------------------------------ backward
+def _oracle_bwd(d, E, A, ref_fwd):
+    x = q.bf16_bits_to_f64(d["x"])
+    w1 = q.bf16_bits_to_f64(d["w1"])
+    w2 = q.bf16_bits_to_f64(d["w2"])
+    dy = q.bf16_bits_to_f64(d["dy"])
+    xq = ref_fwd["xq"]
+    return moe.backward(dy, x, w1, w2, ref_fwd["h"], ref_fwd["a"], d["topk_w"], xq["offsets"],
+                        xq["row_map"], xq["src_row"])
+
+
+def _check_backward(run, ref_b):
+    dx = bf16_host(run.g["dx"])
+    dw1 = bf16_host(run.g["dw1"])
+    dw2 = bf16_host(run.g["dw2"])
+    errs = (rel_l2(dx, ref_b["dX"]), rel_l2(dw1, ref_b["dW1"]), rel_l2(dw2, ref_b["dW2"]))
+    assert max(errs) <= BWD_TOL, errs
+    return errs
+
+
+@pytest.mark.parametrize("A", [1, 16])
+def test_backward_tiny(A):
+    w = synth.WORKLOADS["tiny"]
+    d = synth.make_inputs(w.T, w.H, w.E, w.k, w.I, backward=True, seed=1000)
+    print_case("backward_tiny", T=w.T, H=w.H, E=w.E, k=w.k, I=w.I, A=A)
+    run = Run(d, w.T, w.H, w.E, w.k, w.I, A, backward=True)
+    ref, _, _ = _oracle_fwd(d, w.E, A)
+    print(_check_backward(run, _oracle_bwd(d, w.E, A, ref)))
+
+
+def test_backward_ragged_empty():
+    T, H, E, k, I = 900, 512, 10, 3, 256
+    d = synth.make_inputs(T, H, E, k, I, routing="zipf", backward=True, seed=55, n_empty=2)
+    print_case("backward_ragged", T=T, H=H, E=E, k=k, I=I)
+    run = Run(d, T, H, E, k, I, A=16, backward=True)
+    ref, _, _ = _oracle_fwd(d, E, 16)
+    rb = _oracle_bwd(d, E, 16, ref)
+    print(_check_backward(run, rb))
+    counts = np.bincount(d["topk_idx"].reshape(-1), minlength=E)
+    for e in np.nonzero(counts == 0)[0]:
+        assert not run.g["dw1"][e].any() and not run.g["dw2"][e].any()
+
+
+def test_backward_full_learner_workload_sampled():
+    """Learner workload at full size (T=16384, H=2048, E=128, k=8, I=768):
+    dX of sampled tokens and dW of sampled experts against the oracle on the
+    corresponding sub-problems (a token's dX needs only its own k rows; an
+    expert's dW needs only the rows routed to it)."""
+    w = synth.WORKLOADS["learner"]
+    d = synth.workload_inputs("learner")
+    print_case("backward_full_sampled", T=w.T, H=w.H, E=w.E, k=w.k, I=w.I)
+    run = Run(d, w.T, w.H, w.E, w.k, w.I, backward=True)
+    # dX of a few tokens
+    sample = np.array([3, 9000, w.T - 2])
+    experts = np.unique(d["topk_idx"][sample])
+    remap = -np.ones(w.E, dtype=np.int64)
+    remap[experts] = np.arange(experts.size)
+    sub = dict(x=d["x"][sample], topk_idx=remap[d["topk_idx"][sample]].astype(np.int32),
+               topk_w=d["topk_w"][sample], w1=d["w1"][experts], w2=d["w2"][experts],
+               dy=d["dy"][sample])
+    ref, _, _ = _oracle_fwd(sub, experts.size, 1)
+    rb = _oracle_bwd(sub, experts.size, 1, ref)
+    assert rel_l2(bf16_host(run.g["dx"])[sample], rb["dX"]) <= BWD_TOL
+    # dW of two experts: sub-problem of the tokens routed to e with k = 1
+    for e in (5, 77):
+        tok, slot = np.nonzero(d["topk_idx"] == e)
+        sub = dict(x=d["x"][tok], topk_idx=np.zeros((tok.size, 1), np.int32),
+                   topk_w=d["topk_w"][tok, slot][:, None].copy(), w1=d["w1"][e:e + 1],
+                   w2=d["w2"][e:e + 1], dy=d["dy"][tok])
+        ref, _, _ = _oracle_fwd(sub, 1, 1)
+        rb = _oracle_bwd(sub, 1, 1, ref)
+        assert rel_l2(bf16_host(run.g["dw1"][e]), rb["dW1"][0]) <= BWD_TOL
+        assert rel_l2(bf16_host(run.g["dw2"][e]), rb["dW2"][0]) <= BWD_TOL
