@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X W4A4 MoE expert path: one learner step of a
+Qwen3-30B-A3B-shaped MoE layer (T=16384 tokens, H=2048, E=128, top-8, I=768).
+
+A step is the whole hot path over one batch of synthetic inputs resident in
+HBM: quantize+permute (route, per-token amax, NVFP4 encode, scatter), the
+grouped expert forward (FC1 + SwiGLU, requantise, FC2, unpermute; h and a
+saved) and the straight-through BF16 backward (dX, dW1, dW2).  Weights are
+quantised once before timing (offline, as on the pages).
+
+Prints ONE JSON line.  `value` is tokens/s of the whole step; `roofline`
+reports the dominant kernel (by total time in the timed region) against its
+bound, from HIP events recorded around each library launch on the launch
+stream; `cpu_baseline` times the FP64 oracle on a bounded sample on the host.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W4A4 MoE expert fwd+bwd tokens/s and % MFMA/HBM peak, Qwen3-30B-A3B layer"
+WORKLOAD = "learner"
+PEAK_MFMA_TFLOPS = 2500.0      # MI355X dense f16 / bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+# kernel name -> source file whose content decides whether stored counters still apply
+KERNEL_SOURCES = {
+    "gemm_fc1": "gemm_fwd.hip", "gemm_fc2": "gemm_fwd.hip",
+    "gemm_dgrad_fc1": "gemm_bwd.hip", "gemm_dgrad_fc2": "gemm_bwd.hip",
+    "gemm_wgrad_fc1": "gemm_bwd.hip", "gemm_wgrad_fc2": "gemm_bwd.hip",
+    "quantize_scatter": "quantize.hip", "requant": "quantize.hip",
+    "unpermute": "elementwise.hip", "do_gather_scale": "elementwise.hip",
+    "dx_gather_sum": "elementwise.hip",
+}
+
+
+def algorithmic_work(T, H, E, k, I):
+    """Per-launch algorithmic flops (MFMA kernels) or bytes (HBM kernels).
+    Rows M = T*k dispatched rows (padding excluded)."""
+    M = T * k
+    fl = {
+        "gemm_fc1": 2.0 * M * H * 2 * I,
+        "gemm_fc2": 2.0 * M * I * H,
+        "gemm_dgrad_fc2": 2.0 * M * H * I,
+        "gemm_wgrad_fc2": 2.0 * M * H * I,
+        "gemm_dgrad_fc1": 2.0 * M * 2 * I * H,
+        "gemm_wgrad_fc1": 2.0 * M * 2 * I * H,
+    }
+    by = {
+        # read x and topk_idx; write k copies of codes/scales/outer, row_map, src_row
+        "quantize_scatter": T * (H * 2 + k * 4) + M * (H // 2 + H // 16 + 4) + T * k * 4 + M * 4,
+        "requant": M * (I * 2 + I // 2 + I // 16 + 4),
+        "unpermute": T * (k * H * 2 + k * 8 + H * 2),
+        "do_gather_scale": T * (H * 2 + k * 8) + M * H * 2,
+        "dx_gather_sum": T * (k * H * 2 + k * 4 + H * 2),
+    }
+    return fl, by
+
+
+def source_hash(name):
+    path = os.path.join(ROOT, "precision_rl_amd", "csrc", KERNEL_SOURCES[name])
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(name):
+    """HBM bytes per launch from committed rocprofv3 --pmc summaries, or None
+    when none exist or the kernel source changed since they were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(name)
+    if not rec or rec.get("source_sha256_16") != source_hash(name):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(d, w, tokens=512, experts=8):
+    """The FP64 oracle on a bounded sample of the learner workload: the first
+    `tokens` tokens, each routed to all `experts` experts (k = 8 per token as
+    in the workload, so the per-token work is the same), expert weights
+    quantised before timing.  Times quantize+permute + forward + backward."""
+    from oracle import moe, nvfp4 as q
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    k = w.k
+    assert experts == k
+    x = q.bf16_bits_to_f64(d["x"][:tokens])
+    dy = q.bf16_bits_to_f64(d["dy"][:tokens])
+    w1 = q.bf16_bits_to_f64(d["w1"][:experts])
+    w2 = q.bf16_bits_to_f64(d["w2"][:experts])
+    idx = np.tile(np.arange(k, dtype=np.int32), (tokens, 1))
+    p = d["topk_w"][:tokens]
+    w1q, w2q = moe.quantize_weights(w1), moe.quantize_weights(w2)
+    t0 = time.perf_counter()
+    f = moe.forward(x, idx, p, w1q, w2q, experts)
+    xq = f["xq"]
+    moe.backward(dy, x, w1, w2, f["h"], f["a"], p, xq["offsets"], xq["row_map"], xq["src_row"])
+    dt = time.perf_counter() - t0
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{tokens} tokens of the learner workload (H={w.H}, I={w.I}, k={k}) routed "
+                      f"to {experts} experts, FP64 numpy, quantize+permute+forward+backward, "
+                      f"{dt:.1f} s", "seconds": dt,
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the expert path is single-GPU here, see the sharding notes in the design document.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from precision_rl_amd import binding as b, synth
+
+    w = synth.WORKLOADS[WORKLOAD]
+    T, H, E, k, I, A = w.T, w.H, w.E, w.k, w.I, 1
+    d = synth.workload_inputs(WORKLOAD)
+    dev = torch.device("cuda:0")
+
+    def bf(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x, w1, w2, dy = bf(d["x"]), bf(d["w1"]), bf(d["w2"]), bf(d["dy"])
+    idx = torch.from_numpy(d["topk_idx"]).to(dev)
+    p = torch.from_numpy(d["topk_w"]).to(dev)
+    w1q, w2q = b.quantize_weights(w1), b.quantize_weights(w2)      # offline, untimed
+
+    cap = b.rows_capacity(T, k, E, A)
+    xq = dict(codes=torch.empty(cap, H // 2, dtype=torch.uint8, device=dev),
+              scales=torch.empty(cap, H // 16, dtype=torch.uint8, device=dev),
+              outer=torch.empty(cap, dtype=torch.float32, device=dev),
+              offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+              row_map=torch.empty(T, k, dtype=torch.int32, device=dev),
+              src_row=torch.empty(cap, dtype=torch.int32, device=dev))
+    ws_qp = torch.empty(b.workspace_size(b.WS_QUANTIZE_PERMUTE, T, H, I, E, k, A) + 256,
+                        dtype=torch.uint8, device=dev)
+    ws_f = torch.empty(b.workspace_size(b.WS_FORWARD, T, H, I, E, k, A), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(b.workspace_size(b.WS_BACKWARD, T, H, I, E, k, A), dtype=torch.uint8, device=dev)
+    y = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    saved = dict(h=torch.empty(cap, 2 * I, dtype=torch.bfloat16, device=dev),
+                 a=torch.empty(cap, I, dtype=torch.bfloat16, device=dev))
+    grads = dict(dx=torch.empty(T, H, dtype=torch.bfloat16, device=dev),
+                 dw1=torch.empty(E, 2 * I, H, dtype=torch.bfloat16, device=dev),
+                 dw2=torch.empty(E, H, I, dtype=torch.bfloat16, device=dev))
+
+    # a plain elementwise copy of known size, for scaling HBM counters (--pmc runs)
+    calib = torch.empty(128 << 20, dtype=torch.bfloat16, device=dev)
+    calib_out = torch.empty_like(calib)
+    torch.neg(calib, out=calib_out)
+
+    def step():
+        b.w4a4_quantize_permute(x, idx, E, A, out=xq, workspace=ws_qp)
+        b.w4a4_grouped_expert_fwd(xq, p, w1q, w2q, T, H, I, E, k, A, save=True, y=y,
+                                  workspace=ws_f, saved=saved)
+        b.w4a4_expert_bwd(dy, x, w1, w2, saved["h"], saved["a"], p, xq, T, H, I, E, k, A,
+                          out=grads, workspace=ws_b)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    b.w4a4_profiler_enable(True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    kern = b.w4a4_profiler_report()
+    b.w4a4_profiler_enable(False)
+    print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+
+    fl, by = algorithmic_work(T, H, E, k, I)
+    per_kernel = {}
+    for name, rec in sorted(kern.items(), key=lambda kv: -kv[1]["total_ms"]):
+        avg_ms = rec["total_ms"] / rec["count"]
+        entry = {"avg_ms": round(avg_ms, 4), "launches": rec["count"],
+                 "share": round(rec["total_ms"] / (ms * args.steps), 4)}
+        if name in fl:
+            entry["tflops"] = round(fl[name] / (avg_ms * 1e-3) / 1e12, 1)
+            entry["frac_mfma"] = round(entry["tflops"] / PEAK_MFMA_TFLOPS, 4)
+        elif name in by:
+            entry["gbs"] = round(by[name] / (avg_ms * 1e-3) / 1e9, 1)
+            entry["frac_hbm"] = round(entry["gbs"] / PEAK_HBM_GBS, 4)
+        per_kernel[name] = entry
+    dom = max(kern, key=lambda n: kern[n]["total_ms"])
+    dom_avg_s = kern[dom]["total_ms"] / kern[dom]["count"] * 1e-3
+    if dom in fl:
+        ach = fl[dom] / dom_avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_MFMA_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_MFMA_TFLOPS, 4)}
+    else:
+        ach = by[dom] / dom_avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4)}
+    roof["kernel"] = dom
+    roof["avg_ms"] = round(dom_avg_s * 1e3, 4)
+    roof["traffic"] = stored_traffic(dom)
+
+    gemm_ms = sum(kern[n]["total_ms"] for n in kern if n in fl) / args.steps
+    total_flop = sum(fl.values())
+    out = {
+        "metric": METRIC,
+        "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4->f16 MFMA fwd, bf16 MFMA bwd, fp32 accumulate",
+        "data": "synthetic (seeded; random-init weights of the layer's shape)",
+        "config": {"workload": f"{WORKLOAD}: quantize+permute + grouped expert fwd + BF16 STE bwd",
+                   "T": T, "H": H, "E": E, "top_k": k, "I": I, "row_align": A,
+                   "routing": w.routing},
+        "roofline": roof,
+        "step_mfma_tflops": round(total_flop / (ms * 1e-3) / 1e12, 1),
+        "gemm_ms_per_step": round(gemm_ms, 4),
+        "kernels": per_kernel,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the FP64 oracle on the host", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(d, w, tokens=args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

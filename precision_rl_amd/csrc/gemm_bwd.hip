@@ -73,12 +73,24 @@ struct KRowLoader {
 };
 
 // Transposed operand: element (tile row p, k) lives at krow(k)[col0 + p].
-// Thread t owns tile rows 8 (t % 32) .. +7 and k-rows 8 (t / 32) .. +7.
+// Thread t owns k-rows 8 (t % 8) .. +7 and the 8 tile rows 8 cb .. +7, with
+// cb = t / 8 for A and cb = t / 8 with bits 0 and 2 swapped for B (whose LDS
+// rows are permuted).  Either way the 16 lanes of one LDS write cycle hit 16
+// distinct 16-byte bank groups, and a wave's global loads cover 8 k-rows x
+// 128 contiguous bytes.
+template <bool PERMUTE_ROWS>
+__device__ __forceinline__ int t_col_block(int tid) {
+  const int g8 = tid >> 3;
+  if constexpr (PERMUTE_ROWS) return (g8 & ~5) | ((g8 & 1) << 2) | ((g8 >> 2) & 1);
+  return g8;
+}
+__device__ __forceinline__ int t_k_block(int tid) { return tid & 7; }
+
 template <bool PERMUTE_ROWS>
 __device__ __forceinline__ void store_transposed(uint16_t* s, int tid, const Regs8& in) {
   Regs8 out;
   transpose8x8(in, out);
-  const int c0 = 8 * (tid & 31), kb = 8 * (tid >> 5);
+  const int c0 = 8 * t_col_block<PERMUTE_ROWS>(tid), kb = 8 * t_k_block(tid);
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
     const int p = PERMUTE_ROWS ? b_lds_row_of_col(c0 + r) : c0 + r;
@@ -147,10 +159,12 @@ dgrad_kernel(DgradArgs args) {
     if (r >= args.rows_alloc) r = args.rows_alloc - 1;
     la.rowp[i] = args.g + r * args.K + (q & 7) * 8;
   }
-  // B = W[e] viewed as [K][N]: k-row kk, columns n0 + 8 (t % 32) .. +7
-  const uint16_t* wb = args.w + static_cast<int64_t>(tc.e) * args.K * args.N + n0 + 8 * (tid & 31);
-  const int kb = 8 * (tid >> 5);
-  const bool b_live = n0 + 8 * (tid & 31) < args.N;   // N % 8 == 0: whole group in or out
+  // B = W[e] viewed as [K][N]: k-rows kb .. kb+7, columns n0 + 8 cb .. +7
+  const int bcol = 8 * t_col_block<true>(tid);
+  const uint16_t* wb = args.w + static_cast<int64_t>(tc.e) * args.K * args.N + n0 + bcol;
+  const int kb = 8 * t_k_block(tid);
+  const bool b_live = n0 + bcol < args.N;   // N % 8 == 0: whole group in or out
+
 
   auto load_b = [&](int64_t k0, Regs8& r) {
 #pragma unroll
@@ -187,26 +201,39 @@ dgrad_kernel(DgradArgs args) {
   if (n >= args.N) return;
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
+    if (tc.m0 + wm * 128 + mi * 32 >= tc.m_end) continue;
+    if constexpr (MODE == DgradMode::FC1) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int64_t row = tc.m0 + wm * 128 + mi * 32 + (v & 3) + 4 * hl + 8 * (v >> 2);
-      if (row >= tc.m_end) continue;
-      if constexpr (MODE == DgradMode::FC1) {
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = tc.m0 + wm * 128 + mi * 32 + (v & 3) + 4 * hl + 8 * (v >> 2);
+        if (row >= tc.m_end) continue;
         u32x2_t pk;
         pk[0] = pack_bf16x2(acc[mi][0][v], acc[mi][1][v]);
         pk[1] = pack_bf16x2(acc[mi][2][v], acc[mi][3][v]);
         *reinterpret_cast<u32x2_t*>(args.out + row * args.N + n) = pk;
-      } else {
-        const int I = args.I;
-        const u32x2_t hg = *reinterpret_cast<const u32x2_t*>(args.h + row * (2 * I) + n);
-        const u32x2_t hu = *reinterpret_cast<const u32x2_t*>(args.h + row * (2 * I) + I + n);
+      }
+    } else {
+      // SwiGLU backward: issue the 16 rows' h loads together, then compute
+      const int I = args.I;
+      u32x2_t hg[16], hu[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        int64_t row = tc.m0 + wm * 128 + mi * 32 + (v & 3) + 4 * hl + 8 * (v >> 2);
+        if (row >= tc.m_end) row = tc.m_end - 1;   // clamped: value unused
+        hg[v] = *reinterpret_cast<const u32x2_t*>(args.h + row * (2 * I) + n);
+        hu[v] = *reinterpret_cast<const u32x2_t*>(args.h + row * (2 * I) + I + n);
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = tc.m0 + wm * 128 + mi * 32 + (v & 3) + 4 * hl + 8 * (v >> 2);
+        if (row >= tc.m_end) continue;
         float dg[4], du[4];
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
           // dA is stored as bf16 before the SwiGLU backward
           const float da = bf16_to_f32(f32_to_bf16(acc[mi][ni][v]));
-          const float gt = bf16_to_f32(static_cast<uint16_t>(hg[ni >> 1] >> (16 * (ni & 1))));
-          const float up = bf16_to_f32(static_cast<uint16_t>(hu[ni >> 1] >> (16 * (ni & 1))));
+          const float gt = bf16_to_f32(static_cast<uint16_t>(hg[v][ni >> 1] >> (16 * (ni & 1))));
+          const float up = bf16_to_f32(static_cast<uint16_t>(hu[v][ni >> 1] >> (16 * (ni & 1))));
           const float sg = 1.0f / (1.0f + expf(-gt));
           dg[ni] = da * up * sg * (1.0f + gt * (1.0f - sg));
           du[ni] = da * gt * sg;
@@ -235,6 +262,8 @@ struct WgradArgs {
   uint16_t* out;           // [E, M, N]
 };
 
+// GATHER: B rows are S[src_row[r]] (x gathered by token), else S[r].
+template <bool GATHER>
 __global__ void __launch_bounds__(kGemmThreads, 1)
 wgrad_kernel(WgradArgs args) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
@@ -254,25 +283,30 @@ wgrad_kernel(WgradArgs args) {
   const int m0 = mt * kTileM, n0 = nt * kTileN;
   const int64_t r_begin = args.offsets[e], r_end = args.offsets[e + 1];
 
-  const int c8 = 8 * (tid & 31), kb = 8 * (tid >> 5);
-  const uint16_t* ga = args.g + m0 + c8;
-  const uint16_t* sbp = args.s + n0 + c8;
-  const bool b_live = n0 + c8 < args.N;
+  const int kb = 8 * t_k_block(tid);
+  const int acol = 8 * t_col_block<false>(tid), bcol = 8 * t_col_block<true>(tid);
+  const uint16_t* ga = args.g + m0 + acol;
+  const uint16_t* sbp = args.s + n0 + bcol;
+  const bool b_live = n0 + bcol < args.N;
+  // Source rows of the B operand, one stage ahead of the data loads.
+  int32_t src[8];
+  auto load_src = [&](int64_t r0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t r = r0 + kb + i;
+      if constexpr (GATHER) src[i] = r < r_end ? args.src_row[r] : -1;
+      else src[i] = r < r_end ? static_cast<int32_t>(r) : -1;
+    }
+  };
   auto load = [&](int64_t r0, Regs8& ra, Regs8& rb) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int64_t r = r0 + kb + i;
-      if (r < r_end) {
-        ra.v[i] = *reinterpret_cast<const u32x4_t*>(ga + r * args.g_stride);
-        const int64_t src = args.src_row ? args.src_row[r] : r;
-        if (src >= 0 && b_live)
-          rb.v[i] = *reinterpret_cast<const u32x4_t*>(sbp + src * args.s_stride);
-        else
-          rb.v[i] = u32x4_t{0u, 0u, 0u, 0u};
-      } else {
-        ra.v[i] = u32x4_t{0u, 0u, 0u, 0u};
-        rb.v[i] = u32x4_t{0u, 0u, 0u, 0u};
-      }
+      ra.v[i] = r < r_end ? *reinterpret_cast<const u32x4_t*>(ga + r * args.g_stride)
+                          : u32x4_t{0u, 0u, 0u, 0u};
+      rb.v[i] = (src[i] >= 0 && b_live)
+                    ? *reinterpret_cast<const u32x4_t*>(sbp + static_cast<int64_t>(src[i]) * args.s_stride)
+                    : u32x4_t{0u, 0u, 0u, 0u};
     }
   };
 
@@ -281,12 +315,17 @@ wgrad_kernel(WgradArgs args) {
   const int64_t nk = (r_end - r_begin + kBK - 1) / kBK;
   if (nk > 0) {
     Regs8 ra, rb;
+    load_src(r_begin);
     load(r_begin, ra, rb);
+    load_src(r_begin + kBK);
     store_transposed<false>(lds, tid, ra);
     store_transposed<true>(lds + kOpElems, tid, rb);
     __syncthreads();
     for (int64_t kt = 0; kt < nk; ++kt) {
-      if (kt + 1 < nk) load(r_begin + (kt + 1) * kBK, ra, rb);
+      if (kt + 1 < nk) {
+        load(r_begin + (kt + 1) * kBK, ra, rb);
+        load_src(r_begin + (kt + 2) * kBK);
+      }
       const uint16_t* sa = lds + (kt & 1) * kStageElems;
       mma_stage(sa, sa + kOpElems, wm, wn, r32, hl, acc);
       if (kt + 1 < nk) {
@@ -332,14 +371,15 @@ bool launch_dgrad(const DgradArgs& a, const char* name, hipStream_t s) {
   return launch_ok(name);
 }
 
+template <bool GATHER>
 bool launch_wgrad(const WgradArgs& a, const char* name, hipStream_t s) {
-  static const hipError_t attr = set_lds(&wgrad_kernel);
+  static const hipError_t attr = set_lds(&wgrad_kernel<GATHER>);
   if (attr != hipSuccess) return launch_ok(name) && false;
   const int64_t tiles = static_cast<int64_t>(a.E) * (a.M / kTileM) * ((a.N + kTileN - 1) / kTileN);
   if (tiles == 0) return true;
   {
     ProfScope p(name, s);
-    wgrad_kernel<<<dim3(xcd_grid(tiles)), dim3(kGemmThreads), kLdsBytes, s>>>(a);
+    wgrad_kernel<GATHER><<<dim3(xcd_grid(tiles)), dim3(kGemmThreads), kLdsBytes, s>>>(a);
   }
   return launch_ok(name);
 }
@@ -362,13 +402,13 @@ bool launch_dgrad_fc1(int64_t rows_alloc, int H, int I, int E, const int32_t* of
 bool launch_wgrad_fc2(int H, int I, int E, const int32_t* offsets, const uint16_t* dO,
                       const uint16_t* a, uint16_t* dW2, hipStream_t s) {
   WgradArgs w{H, I, E, H, I, offsets, dO, a, nullptr, dW2};
-  return launch_wgrad(w, "gemm_wgrad_fc2", s);
+  return launch_wgrad<false>(w, "gemm_wgrad_fc2", s);
 }
 
 bool launch_wgrad_fc1(int H, int I, int E, const int32_t* offsets, const uint16_t* dH,
                       const uint16_t* x, const int32_t* src_row, uint16_t* dW1, hipStream_t s) {
   WgradArgs w{2 * I, H, E, 2 * I, H, offsets, dH, x, src_row, dW1};
-  return launch_wgrad(w, "gemm_wgrad_fc1", s);
+  return launch_wgrad<true>(w, "gemm_wgrad_fc1", s);
 }
 
 }  // namespace w4a4

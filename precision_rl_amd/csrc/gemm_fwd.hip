@@ -34,7 +34,8 @@ constexpr int kOpCodes = kTileM * kCodeStride;      // bytes of one operand's co
 constexpr int kOpScales = kTileM * kScaleRow;
 constexpr int kOpBytes = kOpCodes + kOpScales;
 constexpr int kStageBytes = 2 * kOpBytes;
-constexpr int kLdsBytes = 2 * kStageBytes;          // 2 stages
+constexpr int kGxOffset = 2 * kStageBytes;          // 2 stages, then the tile's g_x
+constexpr int kLdsBytes = kGxOffset + kTileM * 4;
 
 enum class FwdMode { FC1, FC2 };
 
@@ -116,6 +117,9 @@ fwd_gemm_kernel(FwdArgs args) {
   }
   int64_t ar_s = tc.m0 + tid;
   if (ar_s >= args.rows_alloc) ar_s = args.rows_alloc - 1;
+  // outer scales of the tile's rows, read by the epilogue from LDS
+  float* s_gx = reinterpret_cast<float*>(lds + kGxOffset);
+  s_gx[tid] = args.a.outer[ar_s];
   const uint8_t* a_scale_src = args.a.scales + ar_s * K16;
   const uint8_t* b_scale_src = wscales + static_cast<int64_t>(b_row_of<MODE>(tid, tc.n_tile, args.I)) * K16;
 
@@ -152,6 +156,9 @@ fwd_gemm_kernel(FwdArgs args) {
       for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
 
   const int nk = args.K / kBK;
+  bool mi_live[4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) mi_live[mi] = tc.m0 + wm * 128 + mi * 32 < tc.m_end;
   StageRegs regs;
   load_stage(0, regs);
   store_stage(0, regs);
@@ -198,10 +205,12 @@ fwd_gemm_kernel(FwdArgs args) {
           bf[f] = decode8(bc[f][s4], s4 < 2 ? bd[f] : bd2[f]);
         }
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+        for (int mi = 0; mi < 4; ++mi) {
+          if (!mi_live[mi]) continue;   // all 32 rows past the expert's end
 #pragma unroll
           for (int ni = 0; ni < 4; ++ni)
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
+        }
       }
     }
     if (kt + 1 < nk) store_stage((kt + 1) & 1, regs);
@@ -219,9 +228,10 @@ fwd_gemm_kernel(FwdArgs args) {
     for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t row = tc.m0 + wm * 128 + mi * 32 + (v & 3) + 4 * hl + 8 * (v >> 2);
+        const int lrow = wm * 128 + mi * 32 + (v & 3) + 4 * hl + 8 * (v >> 2);
+        const int64_t row = tc.m0 + lrow;
         if (row >= tc.m_end) continue;
-        const float gx = args.a.outer[row];
+        const float gx = s_gx[lrow];
         float o[4];
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) o[ni] = acc[mi][ni][v] * (gx * gw[ni]);
@@ -240,9 +250,10 @@ fwd_gemm_kernel(FwdArgs args) {
     for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t row = tc.m0 + wm * 128 + mi * 32 + (v & 3) + 4 * hl + 8 * (v >> 2);
+        const int lrow = wm * 128 + mi * 32 + (v & 3) + 4 * hl + 8 * (v >> 2);
+        const int64_t row = tc.m0 + lrow;
         if (row >= tc.m_end) continue;
-        const float gx = args.a.outer[row];
+        const float gx = s_gx[lrow];
         const float g0 = acc[mi][0][v] * (gx * gw_g0);
         const float g1 = acc[mi][1][v] * (gx * gw_g1);
         const float u0 = acc[mi][2][v] * (gx * gw_u0);
