@@ -10,15 +10,17 @@
 //     b3: dW2[e] = dO_e^T . a_e            M = H,  N = I
 //     b6: dW1[e] = dH_e^T . x[src_row]     M = 2I, N = H
 //
-// 256 x 256 output tile per workgroup, 4 waves of 128 x 128, MFMA 32x32x16 bf16,
-// FP32 accumulation.  K advances 64 per stage through double-buffered LDS
-// holding both operands K-contiguous (row stride 144 B, conflict-free b128
-// fragment reads).  Operands stored K-contiguous in HBM (dO, dH rows of the
-// dgrad) are copied in 16 B chunks; operands stored the other way round
-// (weights in the dgrad, both operands of the wgrad) are read as 8 x 8 bf16
-// micro-blocks, transposed in registers with v_perm_b32 and written as 16 B
-// rows.  B's LDS rows are permuted so that each lane ends up owning 4
-// consecutive output columns (8 B stores in the epilogue).
+// 256 x 256 output tile per workgroup of 8 waves (4 x 2, 64 x 128 per wave, two
+// waves per SIMD), MFMA 32x32x16 bf16, FP32 accumulation.  K advances 64 per
+// stage through double-buffered LDS holding both operands K-contiguous (row
+// stride 144 B, conflict-free b128 fragment reads).  Waves 0-3 stage one
+// operand and waves 4-7 the other, one stage ahead of the MFMAs.  Operands
+// stored K-contiguous in HBM (dO, dH rows of the dgrad) are copied in 16 B
+// chunks; operands stored the other way round (weights in the dgrad, both
+// operands of the wgrad) are read as 8 x 8 bf16 micro-blocks, transposed in
+// registers with v_perm_b32 and written as 16 B rows.  B's LDS rows are
+// permuted so that each lane ends up owning 4 consecutive output columns
+// (8 B stores in the epilogue).
 
 #include "gemm_common.h"
 #include "internal.h"
@@ -31,6 +33,7 @@ constexpr int kRowElems = kBK + 8;         // 72 bf16 = 144 B per LDS row
 constexpr int kOpElems = kTileM * kRowElems;
 constexpr int kStageElems = 2 * kOpElems;
 constexpr int kLdsBytes = 2 * kStageElems * 2;  // 2 stages, bf16
+constexpr int kLoaders = kGemmThreads / 2;      // threads staging one operand
 
 // Global column of B staged into LDS row p: lane j of wave column wn owns
 // columns n0 + wn*128 + 4j + {0,1,2,3} (one per MFMA tile ni).
@@ -55,42 +58,35 @@ __device__ __forceinline__ void transpose8x8(const Regs8& in, Regs8& out) {
   }
 }
 
-// K-contiguous operand: tile row p reads src_row_ptr(p) + k0 .. k0+63.
-// Thread t handles chunks q = t + 256 i (i < 8): row q / 8, 16 B column q % 8.
-struct KRowLoader {
-  const uint16_t* rowp[8];
-  __device__ __forceinline__ void load(int64_t k0, Regs8& r) const {
+// K-contiguous operand staged by 256 threads: chunk q = lt + 256 i (i < 8) is
+// row q / 8, 16 B column q % 8 of the stage.
+__device__ __forceinline__ void store_krows(uint16_t* s, int lt, const Regs8& r) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r.v[i] = *reinterpret_cast<const u32x4_t*>(rowp[i] + k0);
+  for (int i = 0; i < 8; ++i) {
+    const int q = lt + i * kLoaders;
+    *reinterpret_cast<u32x4_t*>(s + (q >> 3) * kRowElems + (q & 7) * 8) = r.v[i];
   }
-  __device__ __forceinline__ static void store(uint16_t* s, int tid, const Regs8& r) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int q = tid + i * kGemmThreads;
-      *reinterpret_cast<u32x4_t*>(s + (q >> 3) * kRowElems + (q & 7) * 8) = r.v[i];
-    }
-  }
-};
+}
 
-// Transposed operand: element (tile row p, k) lives at krow(k)[col0 + p].
-// Thread t owns k-rows 8 (t % 8) .. +7 and the 8 tile rows 8 cb .. +7, with
-// cb = t / 8 for A and cb = t / 8 with bits 0 and 2 swapped for B (whose LDS
-// rows are permuted).  Either way the 16 lanes of one LDS write cycle hit 16
-// distinct 16-byte bank groups, and a wave's global loads cover 8 k-rows x
-// 128 contiguous bytes.
+// Transposed operand staged by 256 threads: element (tile row p, k) lives at
+// krow(k)[col0 + p].  Thread lt owns k-rows 8 (lt % 8) .. +7 and the 8 tile
+// rows 8 cb .. +7, with cb = lt / 8 for A and cb = lt / 8 with bits 0 and 2
+// swapped for B (whose LDS rows are permuted).  Either way the 16 lanes of one
+// LDS write cycle hit 16 distinct 16-byte bank groups, and a wave's global
+// loads cover 8 k-rows x 128 contiguous bytes.
 template <bool PERMUTE_ROWS>
-__device__ __forceinline__ int t_col_block(int tid) {
-  const int g8 = tid >> 3;
+__device__ __forceinline__ int t_col_block(int lt) {
+  const int g8 = lt >> 3;
   if constexpr (PERMUTE_ROWS) return (g8 & ~5) | ((g8 & 1) << 2) | ((g8 >> 2) & 1);
   return g8;
 }
-__device__ __forceinline__ int t_k_block(int tid) { return tid & 7; }
+__device__ __forceinline__ int t_k_block(int lt) { return lt & 7; }
 
 template <bool PERMUTE_ROWS>
-__device__ __forceinline__ void store_transposed(uint16_t* s, int tid, const Regs8& in) {
+__device__ __forceinline__ void store_transposed(uint16_t* s, int lt, const Regs8& in) {
   Regs8 out;
   transpose8x8(in, out);
-  const int c0 = 8 * t_col_block<PERMUTE_ROWS>(tid), kb = 8 * t_k_block(tid);
+  const int c0 = 8 * t_col_block<PERMUTE_ROWS>(lt), kb = 8 * t_k_block(lt);
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
     const int p = PERMUTE_ROWS ? b_lds_row_of_col(c0 + r) : c0 + r;
@@ -98,27 +94,28 @@ __device__ __forceinline__ void store_transposed(uint16_t* s, int tid, const Reg
   }
 }
 
-__device__ __forceinline__ void mma_stage(const uint16_t* sa, const uint16_t* sb, int wm, int wn,
-                                          int r32, int hl, floatx16_t (&acc)[4][4]) {
+__device__ __forceinline__ void mma_stage(const uint16_t* sa, const uint16_t* sb, int a_row0,
+                                          int b_row0, int hl, floatx16_t (&acc)[2][4]) {
 #pragma unroll
   for (int ks = 0; ks < kBK / 16; ++ks) {
-    bf16x8_t af[4], bf[4];
+    bf16x8_t af[2], bf[4];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      af[f] = *reinterpret_cast<const bf16x8_t*>(sa + (wm * 128 + f * 32 + r32) * kRowElems + ks * 16 + hl * 8);
-      bf[f] = *reinterpret_cast<const bf16x8_t*>(sb + (wn * 128 + f * 32 + r32) * kRowElems + ks * 16 + hl * 8);
-    }
+    for (int f = 0; f < 2; ++f)
+      af[f] = *reinterpret_cast<const bf16x8_t*>(sa + (a_row0 + f * 32) * kRowElems + ks * 16 + hl * 8);
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int f = 0; f < 4; ++f)
+      bf[f] = *reinterpret_cast<const bf16x8_t*>(sb + (b_row0 + f * 32) * kRowElems + ks * 16 + hl * 8);
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni)
         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
   }
 }
 
-__device__ __forceinline__ void zero_acc(floatx16_t (&acc)[4][4]) {
+__device__ __forceinline__ void zero_acc(floatx16_t (&acc)[2][4]) {
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
@@ -144,68 +141,72 @@ dgrad_kernel(DgradArgs args) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
   uint16_t* lds = reinterpret_cast<uint16_t*>(lds_raw);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1, r32 = lane & 31, hl = lane >> 5;
+  const int wm = wave & 3, wn = wave >> 2, r32 = lane & 31, hl = lane >> 5;
   const int n_tiles = (args.N + kTileN - 1) / kTileN;
   TileCoord tc = grouped_m_tile(args.offsets, args.E, n_tiles, reinterpret_cast<int*>(lds_raw));
   if (!tc.valid) return;
   __syncthreads();
   const int n0 = tc.n_tile * kTileN;
 
-  KRowLoader la;
+  // waves 0-3: B = W[e] viewed as [K][N] (transposed staging);
+  // waves 4-7: A = rows of dO / dH (K-contiguous staging)
+  const bool loads_a = tid >= kLoaders;
+  const int lt = tid & (kLoaders - 1);
+  const uint16_t* src[8];
+  bool live = true;
+  if (loads_a) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int q = tid + i * kGemmThreads;
-    int64_t r = tc.m0 + (q >> 3);
-    if (r >= args.rows_alloc) r = args.rows_alloc - 1;
-    la.rowp[i] = args.g + r * args.K + (q & 7) * 8;
+    for (int i = 0; i < 8; ++i) {
+      const int q = lt + i * kLoaders;
+      int64_t r = tc.m0 + (q >> 3);
+      if (r >= args.rows_alloc) r = args.rows_alloc - 1;   // in bounds; never stored
+      src[i] = args.g + r * args.K + (q & 7) * 8;
+    }
+  } else {
+    const int bcol = 8 * t_col_block<true>(lt);
+    const int kb = 8 * t_k_block(lt);
+    live = n0 + bcol < args.N;   // N % 8 == 0: whole group in or out
+    const uint16_t* wb = args.w + static_cast<int64_t>(tc.e) * args.K * args.N + n0 + bcol;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) src[i] = wb + static_cast<int64_t>(kb + i) * args.N;
   }
-  // B = W[e] viewed as [K][N]: k-rows kb .. kb+7, columns n0 + 8 cb .. +7
-  const int bcol = 8 * t_col_block<true>(tid);
-  const uint16_t* wb = args.w + static_cast<int64_t>(tc.e) * args.K * args.N + n0 + bcol;
-  const int kb = 8 * t_k_block(tid);
-  const bool b_live = n0 + bcol < args.N;   // N % 8 == 0: whole group in or out
-
-
-  auto load_b = [&](int64_t k0, Regs8& r) {
+  const int64_t kstep = loads_a ? kBK : static_cast<int64_t>(kBK) * args.N;  // elements per stage
+  Regs8 pf;
+  auto load = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      r.v[i] = b_live ? *reinterpret_cast<const u32x4_t*>(wb + (k0 + kb + i) * args.N)
-                      : u32x4_t{0u, 0u, 0u, 0u};
+      pf.v[i] = live ? *reinterpret_cast<const u32x4_t*>(src[i] + kt * kstep) : u32x4_t{0u, 0u, 0u, 0u};
+  };
+  auto store = [&](int buf) {
+    uint16_t* s = lds + buf * kStageElems;
+    if (loads_a) store_krows(s, lt, pf);
+    else store_transposed<true>(s + kOpElems, lt, pf);
   };
 
-  floatx16_t acc[4][4];
+  floatx16_t acc[2][4];
   zero_acc(acc);
+  const int a_row0 = wm * kWaveM + r32, b_row0 = wn * kWaveN + r32;
   const int nk = args.K / kBK;
-  Regs8 ra, rb;
-  la.load(0, ra);
-  load_b(0, rb);
-  KRowLoader::store(lds, tid, ra);
-  store_transposed<true>(lds + kOpElems, tid, rb);
+  load(0);
+  store(0);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) {
-      la.load(static_cast<int64_t>(kt + 1) * kBK, ra);
-      load_b(static_cast<int64_t>(kt + 1) * kBK, rb);
-    }
+    if (kt + 1 < nk) load(kt + 1);
     const uint16_t* sa = lds + (kt & 1) * kStageElems;
-    mma_stage(sa, sa + kOpElems, wm, wn, r32, hl, acc);
-    if (kt + 1 < nk) {
-      uint16_t* sn = lds + ((kt + 1) & 1) * kStageElems;
-      KRowLoader::store(sn, tid, ra);
-      store_transposed<true>(sn + kOpElems, tid, rb);
-    }
+    mma_stage(sa, sa + kOpElems, a_row0, b_row0, hl, acc);
+    if (kt + 1 < nk) store((kt + 1) & 1);
     __syncthreads();
   }
 
-  const int n = n0 + wn * 128 + 4 * r32;
+  const int n = n0 + wn * kWaveN + 4 * r32;
   if (n >= args.N) return;
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
-    if (tc.m0 + wm * 128 + mi * 32 >= tc.m_end) continue;
+  for (int mi = 0; mi < 2; ++mi) {
+    if (tc.m0 + wm * kWaveM + mi * 32 >= tc.m_end) continue;
     if constexpr (MODE == DgradMode::FC1) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t row = tc.m0 + wm * 128 + mi * 32 + (v & 3) + 4 * hl + 8 * (v >> 2);
+        const int64_t row = tc.m0 + acc_row(wm * kWaveM, mi, v, hl);
         if (row >= tc.m_end) continue;
         u32x2_t pk;
         pk[0] = pack_bf16x2(acc[mi][0][v], acc[mi][1][v]);
@@ -218,14 +219,14 @@ dgrad_kernel(DgradArgs args) {
       u32x2_t hg[16], hu[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        int64_t row = tc.m0 + wm * 128 + mi * 32 + (v & 3) + 4 * hl + 8 * (v >> 2);
+        int64_t row = tc.m0 + acc_row(wm * kWaveM, mi, v, hl);
         if (row >= tc.m_end) row = tc.m_end - 1;   // clamped: value unused
         hg[v] = *reinterpret_cast<const u32x2_t*>(args.h + row * (2 * I) + n);
         hu[v] = *reinterpret_cast<const u32x2_t*>(args.h + row * (2 * I) + I + n);
       }
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t row = tc.m0 + wm * 128 + mi * 32 + (v & 3) + 4 * hl + 8 * (v >> 2);
+        const int64_t row = tc.m0 + acc_row(wm * kWaveM, mi, v, hl);
         if (row >= tc.m_end) continue;
         float dg[4], du[4];
 #pragma unroll
@@ -258,7 +259,7 @@ struct WgradArgs {
   const int32_t* offsets;
   const uint16_t* g;       // G [rows, M]:  A(m, r) = G[r][m]
   const uint16_t* s;       // S [*, N]:     B(r, n) = S[src(r)][n]
-  const int32_t* src_row;  // null: src(r) = r; else src(r) = src_row[r] (-1 = zero row)
+  const int32_t* src_row;  // gather variant: src(r) = src_row[r] (-1 = zero row)
   uint16_t* out;           // [E, M, N]
 };
 
@@ -269,7 +270,7 @@ wgrad_kernel(WgradArgs args) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
   uint16_t* lds = reinterpret_cast<uint16_t*>(lds_raw);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1, r32 = lane & 31, hl = lane >> 5;
+  const int wm = wave & 3, wn = wave >> 2, r32 = lane & 31, hl = lane >> 5;
   const int m_tiles = args.M / kTileM, n_tiles = (args.N + kTileN - 1) / kTileN;
   const int64_t total = static_cast<int64_t>(args.E) * m_tiles * n_tiles;
   const int64_t per_xcd = (total + kXcds - 1) / kXcds;
@@ -283,67 +284,77 @@ wgrad_kernel(WgradArgs args) {
   const int m0 = mt * kTileM, n0 = nt * kTileN;
   const int64_t r_begin = args.offsets[e], r_end = args.offsets[e + 1];
 
-  const int kb = 8 * t_k_block(tid);
-  const int acol = 8 * t_col_block<false>(tid), bcol = 8 * t_col_block<true>(tid);
-  const uint16_t* ga = args.g + m0 + acol;
-  const uint16_t* sbp = args.s + n0 + bcol;
-  const bool b_live = n0 + bcol < args.N;
-  // Source rows of the B operand, one stage ahead of the data loads.
+  // waves 0-3 stage A (rows of G), waves 4-7 stage B (rows of S); both transposed
+  const bool loads_b = tid >= kLoaders;
+  const int lt = tid & (kLoaders - 1);
+  const int kb = 8 * t_k_block(lt);
+  const uint16_t* base;
+  int64_t stride;
+  bool live;
+  if (loads_b) {
+    const int bcol = 8 * t_col_block<true>(lt);
+    base = args.s + n0 + bcol;
+    stride = args.s_stride;
+    live = n0 + bcol < args.N;
+  } else {
+    base = args.g + m0 + 8 * t_col_block<false>(lt);
+    stride = args.g_stride;
+    live = true;
+  }
+  // Source rows, one stage ahead of the data loads (the gather's index loads
+  // would otherwise sit on the critical path).
   int32_t src[8];
   auto load_src = [&](int64_t r0) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int64_t r = r0 + kb + i;
-      if constexpr (GATHER) src[i] = r < r_end ? args.src_row[r] : -1;
+      if (GATHER && loads_b) src[i] = r < r_end ? args.src_row[r] : -1;
       else src[i] = r < r_end ? static_cast<int32_t>(r) : -1;
     }
   };
-  auto load = [&](int64_t r0, Regs8& ra, Regs8& rb) {
+  Regs8 pf;
+  auto load = [&]() {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t r = r0 + kb + i;
-      ra.v[i] = r < r_end ? *reinterpret_cast<const u32x4_t*>(ga + r * args.g_stride)
-                          : u32x4_t{0u, 0u, 0u, 0u};
-      rb.v[i] = (src[i] >= 0 && b_live)
-                    ? *reinterpret_cast<const u32x4_t*>(sbp + static_cast<int64_t>(src[i]) * args.s_stride)
+    for (int i = 0; i < 8; ++i)
+      pf.v[i] = (src[i] >= 0 && live)
+                    ? *reinterpret_cast<const u32x4_t*>(base + static_cast<int64_t>(src[i]) * stride)
                     : u32x4_t{0u, 0u, 0u, 0u};
-    }
+  };
+  auto store = [&](int buf) {
+    uint16_t* s = lds + buf * kStageElems;
+    if (loads_b) store_transposed<true>(s + kOpElems, lt, pf);
+    else store_transposed<false>(s, lt, pf);
   };
 
-  floatx16_t acc[4][4];
+  floatx16_t acc[2][4];
   zero_acc(acc);
+  const int a_row0 = wm * kWaveM + r32, b_row0 = wn * kWaveN + r32;
   const int64_t nk = (r_end - r_begin + kBK - 1) / kBK;
   if (nk > 0) {
-    Regs8 ra, rb;
     load_src(r_begin);
-    load(r_begin, ra, rb);
+    load();
     load_src(r_begin + kBK);
-    store_transposed<false>(lds, tid, ra);
-    store_transposed<true>(lds + kOpElems, tid, rb);
+    store(0);
     __syncthreads();
     for (int64_t kt = 0; kt < nk; ++kt) {
       if (kt + 1 < nk) {
-        load(r_begin + (kt + 1) * kBK, ra, rb);
+        load();
         load_src(r_begin + (kt + 2) * kBK);
       }
       const uint16_t* sa = lds + (kt & 1) * kStageElems;
-      mma_stage(sa, sa + kOpElems, wm, wn, r32, hl, acc);
-      if (kt + 1 < nk) {
-        uint16_t* sn = lds + ((kt + 1) & 1) * kStageElems;
-        store_transposed<false>(sn, tid, ra);
-        store_transposed<true>(sn + kOpElems, tid, rb);
-      }
+      mma_stage(sa, sa + kOpElems, a_row0, b_row0, hl, acc);
+      if (kt + 1 < nk) store((kt + 1) & 1);
       __syncthreads();
     }
   }
   uint16_t* out = args.out + static_cast<int64_t>(e) * args.M * args.N;
-  const int n = n0 + wn * 128 + 4 * r32;
+  const int n = n0 + wn * kWaveN + 4 * r32;
   if (n >= args.N) return;
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
+  for (int mi = 0; mi < 2; ++mi) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int64_t m = m0 + wm * 128 + mi * 32 + (v & 3) + 4 * hl + 8 * (v >> 2);
+      const int64_t m = m0 + acc_row(wm * kWaveM, mi, v, hl);
       u32x2_t pk;
       pk[0] = pack_bf16x2(acc[mi][0][v], acc[mi][1][v]);
       pk[1] = pack_bf16x2(acc[mi][2][v], acc[mi][3][v]);

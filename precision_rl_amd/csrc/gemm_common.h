@@ -5,9 +5,14 @@
 
 namespace w4a4 {
 
-constexpr int kGemmThreads = 256;  // 4 waves, 2 x 2, each owning a 128 x 128 sub-tile
+// 8 waves per workgroup, two per SIMD: while one wave waits on memory or
+// decodes operands, the other keeps the SIMD's matrix core busy.  Waves are
+// laid out 4 (M) x 2 (N); each owns a 64 x 128 sub-tile of the 256 x 256 tile.
+constexpr int kGemmThreads = 512;
 constexpr int kTileM = 256;
 constexpr int kTileN = 256;
+constexpr int kWaveM = 64;
+constexpr int kWaveN = 128;
 constexpr int kXcds = 8;           // MI355X: workgroups are dealt round-robin over 8 XCDs
 
 struct TileCoord {
@@ -24,11 +29,10 @@ struct TileCoord {
 // it from the offsets (a scan over E in LDS).  Logical tiles are ordered
 // expert-major, N fastest, and dealt out in contiguous runs per XCD so that an
 // expert's weight tiles and an M tile's activations stay in one XCD's L2.
-// `scratch` must hold E + 1 ints of LDS.
+// `scratch` must hold kGemmThreads + E ints of LDS.
 __device__ inline TileCoord grouped_m_tile(const int32_t* __restrict__ offsets, int E, int n_tiles,
                                            int* scratch) {
   const int tid = threadIdx.x;
-  // inclusive scan of per-expert M-tile counts, chunked over E
   int carry = 0;
   for (int e0 = 0; e0 < E; e0 += kGemmThreads) {
     const int e = e0 + tid;
@@ -88,6 +92,12 @@ inline int64_t grouped_m_tiles_bound(int64_t rows_alloc, int E) {
 
 inline unsigned xcd_grid(int64_t tiles) {
   return static_cast<unsigned>((tiles + kXcds - 1) / kXcds * kXcds);
+}
+
+// Row of the output tile held in accumulator element v of lane (r32, hl) for
+// MFMA 32x32 tile mi of a wave whose rows start at wave_row0.
+__device__ __forceinline__ int acc_row(int wave_row0, int mi, int v, int hl) {
+  return wave_row0 + mi * 32 + (v & 3) + 4 * hl + 8 * (v >> 2);
 }
 
 }  // namespace w4a4

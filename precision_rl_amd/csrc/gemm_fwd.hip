@@ -8,17 +8,19 @@
 // is decoded exactly to f16: d * c has at most 6 significant bits and lies in
 // [2^-10, 2688], so the f16 value is exact, f16 x f16 products are exact in
 // FP32, and only the MFMA's FP32 accumulation rounds.  Decoding happens in
-// registers right before the MFMA (hardware fp4 -> f16 conversion, then one
-// v_pk_mul_f16 by the block scale); decoded operands never touch memory.
+// registers right before the MFMA (hardware fp4 -> f16 conversion, which
+// applies only the exponent of its scale operand, then one v_pk_mul_f16 by the
+// E4M3 block scale); decoded operands never touch memory.
 //
-// Tiling: 256 x 256 output tile per workgroup, 4 waves of 128 x 128, MFMA
-// 32x32x16 f16.  Each pipeline stage covers 128 of K: packed codes (64 B per
-// row) and block scales (8 B per row) of both operands go through LDS, double
-// buffered, with the next stage's global loads in flight during the MFMAs.
-// Inside a stage, lane half h (lanes 32-63) owns the stage's second 64 k of
-// its row; A and B use the same assignment, so every MFMA k slot pairs equal
-// k indices (the K order of the reduction is a permutation; FP32 rounding of
-// the sum is covered by the tolerance).
+// Tiling: 256 x 256 output tile per workgroup of 8 waves (4 x 2, 64 x 128 per
+// wave, two waves per SIMD), MFMA 32x32x16 f16.  Each pipeline stage covers 128
+// of K: packed codes (64 B per row) and block scales (8 B per row) of both
+// operands go through LDS, double buffered; waves 0-3 fetch the activation tile
+// and waves 4-7 the weight tile, one stage ahead of the MFMAs.  Inside a stage,
+// lane half h (lanes 32-63) owns the stage's second 64 k of its row; A and B
+// use the same assignment, so every MFMA k slot pairs equal k indices (the
+// reduction runs in a permuted K order; FP32 rounding of the sum is covered by
+// the tolerance, and sums that are exact in FP32 are order independent).
 
 #include "gemm_common.h"
 #include "internal.h"
@@ -26,16 +28,17 @@
 namespace w4a4 {
 namespace {
 
-constexpr int kBK = 128;                  // K per stage
-constexpr int kCodeRow = kBK / 2;         // 64 B of codes per row per stage
+constexpr int kBK = 128;                    // K per stage
+constexpr int kCodeRow = kBK / 2;           // 64 B of codes per row per stage
 constexpr int kCodeStride = kCodeRow + 16;  // 80 B: conflict-free b128 reads
-constexpr int kScaleRow = kBK / 16;       // 8 scale bytes per row per stage
-constexpr int kOpCodes = kTileM * kCodeStride;      // bytes of one operand's codes
+constexpr int kScaleRow = kBK / 16;         // 8 scale bytes per row per stage
+constexpr int kOpCodes = kTileM * kCodeStride;
 constexpr int kOpScales = kTileM * kScaleRow;
 constexpr int kOpBytes = kOpCodes + kOpScales;
 constexpr int kStageBytes = 2 * kOpBytes;
-constexpr int kGxOffset = 2 * kStageBytes;          // 2 stages, then the tile's g_x
+constexpr int kGxOffset = 2 * kStageBytes;  // 2 stages, then the tile's g_x
 constexpr int kLdsBytes = kGxOffset + kTileM * 4;
+constexpr int kLoaders = kGemmThreads / 2;  // threads fetching one operand
 
 enum class FwdMode { FC1, FC2 };
 
@@ -53,7 +56,9 @@ struct FwdArgs {
   float* dbg;        // FC1: pre-cast [rows, 2I] (may be null)
 };
 
-// Global row of B (weights) staged into LDS row p of the tile.
+// Global row of B (weights) staged into LDS row p of the tile: lane j of wave
+// column wn ends up owning 4 consecutive outputs (FC2: columns; FC1: the gate
+// and up halves of two consecutive SwiGLU features).
 template <FwdMode MODE>
 __device__ __forceinline__ int b_row_of(int p, int n_tile, int I) {
   const int wn = p >> 7, ni = (p >> 5) & 3, j = p & 31;
@@ -66,13 +71,6 @@ __device__ __forceinline__ int b_row_of(int p, int n_tile, int I) {
   }
 }
 
-struct StageRegs {
-  u32x4_t a_code[4];
-  u32x4_t b_code[4];
-  u32x2_t a_scale;
-  u32x2_t b_scale;
-};
-
 __device__ __forceinline__ half8_t decode8(uint32_t codes8, half2_t d2) {
   half2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes8, 1.0f, 0) * d2;
   half2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes8, 1.0f, 1) * d2;
@@ -84,6 +82,14 @@ __device__ __forceinline__ half8_t decode8(uint32_t codes8, half2_t d2) {
   return r;
 }
 
+// Two of the four E4M3 scale bytes in `sc` (selected by HI) as f16 pairs.
+template <bool HI>
+__device__ __forceinline__ void scale_pairs(uint32_t sc, half2_t& d0, half2_t& d1) {
+  const half2_t v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, HI);
+  d0 = half2_t{v[0], v[0]};
+  d1 = half2_t{v[1], v[1]};
+}
+
 template <FwdMode MODE>
 __global__ void __launch_bounds__(kGemmThreads, 1)
 fwd_gemm_kernel(FwdArgs args) {
@@ -91,7 +97,7 @@ fwd_gemm_kernel(FwdArgs args) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave & 3, wn = wave >> 2;
   const int r32 = lane & 31, hl = lane >> 5;
 
   const int n_tiles = MODE == FwdMode::FC1 ? args.I / 128 : args.N / kTileN;
@@ -100,112 +106,114 @@ fwd_gemm_kernel(FwdArgs args) {
   __syncthreads();  // the scan scratch aliases the stage buffers
 
   const int64_t K2 = args.K / 2, K16 = args.K / 16;
-  // ---- global source pointers of this thread's loads
-  // codes: 4 chunks of 16 B per operand: chunk q = tid + 256 i -> row q/4, col q%4
-  const uint8_t* a_code_src[4];
-  const uint8_t* b_code_src[4];
-  const uint8_t* wcodes = args.w.codes + static_cast<int64_t>(tc.e) * args.N * K2;
-  const uint8_t* wscales = args.w.scales + static_cast<int64_t>(tc.e) * args.N * K16;
+  // ---- this thread's loads: waves 0-3 fetch A (activations), 4-7 fetch B (weights)
+  const bool loads_b = tid >= kLoaders;
+  const int lt = tid & (kLoaders - 1);
+  const uint8_t* code_src[4];
+  const uint8_t* scale_src;
+  {
+    const uint8_t* wcodes = args.w.codes + static_cast<int64_t>(tc.e) * args.N * K2;
+    const uint8_t* wscales = args.w.scales + static_cast<int64_t>(tc.e) * args.N * K16;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = tid + i * kGemmThreads;
-    const int row = q >> 2, col = q & 3;
-    int64_t ar = tc.m0 + row;
-    if (ar >= args.rows_alloc) ar = args.rows_alloc - 1;   // stays in bounds; never stored
-    a_code_src[i] = args.a.codes + ar * K2 + col * 16;
-    b_code_src[i] = wcodes + static_cast<int64_t>(b_row_of<MODE>(row, tc.n_tile, args.I)) * K2 + col * 16;
+    for (int i = 0; i < 4; ++i) {
+      const int q = lt + i * kLoaders;
+      const int row = q >> 2, col = q & 3;
+      if (loads_b) {
+        code_src[i] = wcodes + static_cast<int64_t>(b_row_of<MODE>(row, tc.n_tile, args.I)) * K2 + col * 16;
+      } else {
+        int64_t ar = tc.m0 + row;
+        if (ar >= args.rows_alloc) ar = args.rows_alloc - 1;   // in bounds; never stored
+        code_src[i] = args.a.codes + ar * K2 + col * 16;
+      }
+    }
+    if (loads_b) {
+      scale_src = wscales + static_cast<int64_t>(b_row_of<MODE>(lt, tc.n_tile, args.I)) * K16;
+    } else {
+      int64_t ar = tc.m0 + lt;
+      if (ar >= args.rows_alloc) ar = args.rows_alloc - 1;
+      scale_src = args.a.scales + ar * K16;
+      // outer scales of the tile's rows, read by the epilogue from LDS
+      reinterpret_cast<float*>(lds + kGxOffset)[lt] = args.a.outer[ar];
+    }
   }
-  int64_t ar_s = tc.m0 + tid;
-  if (ar_s >= args.rows_alloc) ar_s = args.rows_alloc - 1;
-  // outer scales of the tile's rows, read by the epilogue from LDS
-  float* s_gx = reinterpret_cast<float*>(lds + kGxOffset);
-  s_gx[tid] = args.a.outer[ar_s];
-  const uint8_t* a_scale_src = args.a.scales + ar_s * K16;
-  const uint8_t* b_scale_src = wscales + static_cast<int64_t>(b_row_of<MODE>(tid, tc.n_tile, args.I)) * K16;
+  const float* s_gx = reinterpret_cast<const float*>(lds + kGxOffset);
+  const int op_off = loads_b ? kOpBytes : 0;
 
-  auto load_stage = [&](int kt, StageRegs& r) {
+  u32x4_t pf_code[4];
+  u32x2_t pf_scale;
+  auto load_stage = [&](int kt) {
     const int64_t cb = static_cast<int64_t>(kt) * kCodeRow;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      r.a_code[i] = *reinterpret_cast<const u32x4_t*>(a_code_src[i] + cb);
-      r.b_code[i] = *reinterpret_cast<const u32x4_t*>(b_code_src[i] + cb);
-    }
-    const int64_t sb = static_cast<int64_t>(kt) * kScaleRow;
-    r.a_scale = *reinterpret_cast<const u32x2_t*>(a_scale_src + sb);
-    r.b_scale = *reinterpret_cast<const u32x2_t*>(b_scale_src + sb);
+    for (int i = 0; i < 4; ++i) pf_code[i] = *reinterpret_cast<const u32x4_t*>(code_src[i] + cb);
+    pf_scale = *reinterpret_cast<const u32x2_t*>(scale_src + static_cast<int64_t>(kt) * kScaleRow);
   };
-  auto store_stage = [&](int buf, const StageRegs& r) {
-    uint8_t* base = lds + buf * kStageBytes;
+  auto store_stage = [&](int buf) {
+    uint8_t* base = lds + buf * kStageBytes + op_off;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int q = tid + i * kGemmThreads;
-      const int row = q >> 2, col = q & 3;
-      *reinterpret_cast<u32x4_t*>(base + row * kCodeStride + col * 16) = r.a_code[i];
-      *reinterpret_cast<u32x4_t*>(base + kOpBytes + row * kCodeStride + col * 16) = r.b_code[i];
+      const int q = lt + i * kLoaders;
+      *reinterpret_cast<u32x4_t*>(base + (q >> 2) * kCodeStride + (q & 3) * 16) = pf_code[i];
     }
-    *reinterpret_cast<u32x2_t*>(base + kOpCodes + tid * kScaleRow) = r.a_scale;
-    *reinterpret_cast<u32x2_t*>(base + kOpBytes + kOpCodes + tid * kScaleRow) = r.b_scale;
+    *reinterpret_cast<u32x2_t*>(base + kOpCodes + lt * kScaleRow) = pf_scale;
   };
 
-  floatx16_t acc[4][4];
+  floatx16_t acc[2][4];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
-
-  const int nk = args.K / kBK;
-  bool mi_live[4];
+  bool mi_live[2];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) mi_live[mi] = tc.m0 + wm * 128 + mi * 32 < tc.m_end;
-  StageRegs regs;
-  load_stage(0, regs);
-  store_stage(0, regs);
+  for (int mi = 0; mi < 2; ++mi) mi_live[mi] = tc.m0 + wm * kWaveM + mi * 32 < tc.m_end;
+
+  const int a_row0 = wm * kWaveM + r32, b_row0 = wn * kWaveN + r32;
+  const int nk = args.K / kBK;
+  load_stage(0);
+  store_stage(0);
   __syncthreads();
 
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) load_stage(kt + 1, regs);
+    if (kt + 1 < nk) load_stage(kt + 1);
     const uint8_t* sa = lds + (kt & 1) * kStageBytes;
     const uint8_t* sb = sa + kOpBytes;
-    // block scales of this lane's 4 blocks, per fragment
-    uint32_t a_sc[4], b_sc[4];
+    uint32_t a_sc[2], b_sc[4];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      a_sc[f] = *reinterpret_cast<const uint32_t*>(sa + kOpCodes + (wm * 128 + f * 32 + r32) * kScaleRow + hl * 4);
-      b_sc[f] = *reinterpret_cast<const uint32_t*>(sb + kOpCodes + (wn * 128 + f * 32 + r32) * kScaleRow + hl * 4);
-    }
+    for (int f = 0; f < 2; ++f)
+      a_sc[f] = *reinterpret_cast<const uint32_t*>(sa + kOpCodes + (a_row0 + f * 32) * kScaleRow + hl * 4);
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+      b_sc[f] = *reinterpret_cast<const uint32_t*>(sb + kOpCodes + (b_row0 + f * 32) * kScaleRow + hl * 4);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      u32x4_t ac[4], bc[4];
+      u32x4_t ac[2], bc[4];
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        ac[f] = *reinterpret_cast<const u32x4_t*>(sa + (wm * 128 + f * 32 + r32) * kCodeStride + hl * 32 + hh * 16);
-        bc[f] = *reinterpret_cast<const u32x4_t*>(sb + (wn * 128 + f * 32 + r32) * kCodeStride + hl * 32 + hh * 16);
+      for (int f = 0; f < 2; ++f)
+        ac[f] = *reinterpret_cast<const u32x4_t*>(sa + (a_row0 + f * 32) * kCodeStride + hl * 32 + hh * 16);
+#pragma unroll
+      for (int f = 0; f < 4; ++f)
+        bc[f] = *reinterpret_cast<const u32x4_t*>(sb + (b_row0 + f * 32) * kCodeStride + hl * 32 + hh * 16);
+      half2_t ad[2][2], bd[4][2];   // block scales of blocks 2hh, 2hh+1 as f16 pairs
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        if (hh == 0) scale_pairs<false>(a_sc[f], ad[f][0], ad[f][1]);
+        else scale_pairs<true>(a_sc[f], ad[f][0], ad[f][1]);
       }
-      half2_t ad[4], bd[4];   // block scales as f16 pairs for blocks 2hh, 2hh+1
-      half2_t ad2[4], bd2[4];
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
-        half2_t av = hh == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a_sc[f], 1.0f, false)
-                             : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a_sc[f], 1.0f, true);
-        half2_t bv = hh == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b_sc[f], 1.0f, false)
-                             : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b_sc[f], 1.0f, true);
-        ad[f] = half2_t{av[0], av[0]};
-        ad2[f] = half2_t{av[1], av[1]};
-        bd[f] = half2_t{bv[0], bv[0]};
-        bd2[f] = half2_t{bv[1], bv[1]};
+        if (hh == 0) scale_pairs<false>(b_sc[f], bd[f][0], bd[f][1]);
+        else scale_pairs<true>(b_sc[f], bd[f][0], bd[f][1]);
       }
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
-        half8_t af[4], bf[4];
+        half8_t af[2], bf[4];
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
-          af[f] = decode8(ac[f][s4], s4 < 2 ? ad[f] : ad2[f]);
-          bf[f] = decode8(bc[f][s4], s4 < 2 ? bd[f] : bd2[f]);
-        }
+        for (int f = 0; f < 2; ++f) af[f] = decode8(ac[f][s4], ad[f][s4 >> 1]);
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
+        for (int f = 0; f < 4; ++f) bf[f] = decode8(bc[f][s4], bd[f][s4 >> 1]);
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) {
           if (!mi_live[mi]) continue;   // all 32 rows past the expert's end
 #pragma unroll
           for (int ni = 0; ni < 4; ++ni)
@@ -213,22 +221,22 @@ fwd_gemm_kernel(FwdArgs args) {
         }
       }
     }
-    if (kt + 1 < nk) store_stage((kt + 1) & 1, regs);
+    if (kt + 1 < nk) store_stage((kt + 1) & 1);
     __syncthreads();
   }
 
   // ---------------------------------------------------------------- epilogue
   const float* wouter = args.w.outer + static_cast<int64_t>(tc.e) * args.N;
   if constexpr (MODE == FwdMode::FC2) {
-    const int n = tc.n_tile * kTileN + wn * 128 + 4 * r32;
+    const int n = tc.n_tile * kTileN + wn * kWaveN + 4 * r32;
     float gw[4];
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) gw[ni] = wouter[n + ni];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
+    for (int mi = 0; mi < 2; ++mi) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int lrow = wm * 128 + mi * 32 + (v & 3) + 4 * hl + 8 * (v >> 2);
+        const int lrow = acc_row(wm * kWaveM, mi, v, hl);
         const int64_t row = tc.m0 + lrow;
         if (row >= tc.m_end) continue;
         const float gx = s_gx[lrow];
@@ -247,10 +255,10 @@ fwd_gemm_kernel(FwdArgs args) {
     const float gw_g0 = wouter[i], gw_g1 = wouter[i + 1];
     const float gw_u0 = wouter[I + i], gw_u1 = wouter[I + i + 1];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
+    for (int mi = 0; mi < 2; ++mi) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int lrow = wm * 128 + mi * 32 + (v & 3) + 4 * hl + 8 * (v >> 2);
+        const int lrow = acc_row(wm * kWaveM, mi, v, hl);
         const int64_t row = tc.m0 + lrow;
         if (row >= tc.m_end) continue;
         const float gx = s_gx[lrow];
