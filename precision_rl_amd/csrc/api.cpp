@@ -82,7 +82,7 @@ FwdWs fwd_ws(int64_t cap, int H, int I) {
   return w;
 }
 struct BwdWs {
-  size_t dO, dH, dXp, total;
+  size_t dO, dH, dXp, xp, total;
 };
 BwdWs bwd_ws(int64_t cap, int H, int I) {
   BwdWs w;
@@ -90,6 +90,7 @@ BwdWs bwd_ws(int64_t cap, int H, int I) {
   w.dO = off; off += round_up(static_cast<size_t>(cap) * H * 2);
   w.dH = off; off += round_up(static_cast<size_t>(cap) * 2 * I * 2);
   w.dXp = off; off += round_up(static_cast<size_t>(cap) * H * 2);
+  w.xp = off; off += round_up(static_cast<size_t>(cap) * H * 2);
   w.total = off;
   return w;
 }
@@ -292,6 +293,7 @@ w4a4_status w4a4_expert_bwd(int64_t T, int H, int I, int E, int k, int row_align
   uint16_t* dO = reinterpret_cast<uint16_t*>(ws + L.dO);
   uint16_t* dH = reinterpret_cast<uint16_t*>(ws + L.dH);
   uint16_t* dXp = reinterpret_cast<uint16_t*>(ws + L.dXp);
+  uint16_t* xp = reinterpret_cast<uint16_t*>(ws + L.xp);
   const uint16_t* h = static_cast<const uint16_t*>(save_h);
   const uint16_t* a = static_cast<const uint16_t*>(save_a);
   const uint16_t* W1 = static_cast<const uint16_t*>(w1);
@@ -307,8 +309,10 @@ w4a4_status w4a4_expert_bwd(int64_t T, int H, int I, int E, int k, int row_align
     return W4A4_ERR_LAUNCH;
   if (cap > 0 && !launch_dgrad_fc1(cap, H, I, E, expert_offsets, dH, W1, dXp, s))
     return W4A4_ERR_LAUNCH;
-  if (!launch_wgrad_fc1(H, I, E, expert_offsets, dH, static_cast<const uint16_t*>(x), src_row,
-                        static_cast<uint16_t*>(dw1), s))
+  if (cap > 0 && !launch_gather_rows(cap, H, static_cast<const uint16_t*>(x), src_row,
+                                     expert_offsets, E, xp, s))
+    return W4A4_ERR_LAUNCH;
+  if (!launch_wgrad_fc1(H, I, E, expert_offsets, dH, xp, static_cast<uint16_t*>(dw1), s))
     return W4A4_ERR_LAUNCH;
   if (!launch_gather_sum(T, H, k, dXp, row_map, static_cast<uint16_t*>(dx), s))
     return W4A4_ERR_LAUNCH;

@@ -83,7 +83,32 @@ gather_scale_kernel(int64_t rows_alloc, int H, int k, const uint16_t* __restrict
   }
 }
 
+// One workgroup per dispatched row: xp[r] = x[src_row[r]], zeros for pad rows.
+__global__ void __launch_bounds__(kThreads)
+gather_rows_kernel(int H, const uint16_t* __restrict__ x, const int32_t* __restrict__ src_row,
+                   const int32_t* __restrict__ offsets, int E, uint16_t* __restrict__ xp) {
+  const int64_t r = blockIdx.x;
+  if (r >= offsets[E]) return;
+  const int32_t t = src_row[r];
+  for (int c = threadIdx.x; c < H / 8; c += kThreads) {
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (t >= 0) v = *reinterpret_cast<const u32x4_t*>(x + static_cast<int64_t>(t) * H + c * 8);
+    *reinterpret_cast<u32x4_t*>(xp + r * H + c * 8) = v;
+  }
+}
+
 }  // namespace
+
+bool launch_gather_rows(int64_t rows_alloc, int H, const uint16_t* x, const int32_t* src_row,
+                        const int32_t* offsets, int E, uint16_t* xp, hipStream_t s) {
+  if (rows_alloc == 0) return true;
+  {
+    ProfScope p("x_gather_rows", s);
+    gather_rows_kernel<<<dim3(static_cast<unsigned>(rows_alloc)), dim3(kThreads), 0, s>>>(
+        H, x, src_row, offsets, E, xp);
+  }
+  return launch_ok("x_gather_rows");
+}
 
 bool launch_unpermute(int64_t T, int H, int k, const uint16_t* o, const int32_t* row_map,
                       const float* topk_w, uint16_t* y, hipStream_t s) {

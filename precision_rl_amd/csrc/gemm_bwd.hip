@@ -8,19 +8,17 @@
 //     b5: dXp = dH_e . W1[e]     K = 2I, N = H
 //   wgrad (K = dispatched rows of expert e, ragged, possibly empty):
 //     b3: dW2[e] = dO_e^T . a_e            M = H,  N = I
-//     b6: dW1[e] = dH_e^T . x[src_row]     M = 2I, N = H
+//     b6: dW1[e] = dH_e^T . xp_e           M = 2I, N = H   (xp = x gathered by row)
 //
-// 256 x 256 output tile per workgroup of 8 waves (4 x 2, 64 x 128 per wave, two
-// waves per SIMD), MFMA 32x32x16 bf16, FP32 accumulation.  K advances 64 per
-// stage through double-buffered LDS holding both operands K-contiguous (row
-// stride 144 B, conflict-free b128 fragment reads).  Waves 0-3 stage one
-// operand and waves 4-7 the other, one stage ahead of the MFMAs.  Operands
-// stored K-contiguous in HBM (dO, dH rows of the dgrad) are copied in 16 B
-// chunks; operands stored the other way round (weights in the dgrad, both
-// operands of the wgrad) are read as 8 x 8 bf16 micro-blocks, transposed in
-// registers with v_perm_b32 and written as 16 B rows.  B's LDS rows are
-// permuted so that each lane ends up owning 4 consecutive output columns
-// (8 B stores in the epilogue).
+// 256 x 256 output tile per workgroup, MFMA 32x32x16 bf16, FP32 accumulation.
+// K advances 32 per stage through a 4-deep LDS ring filled by the hardware's
+// global -> LDS copies three stages ahead of the MFMAs (no register staging).
+// Tiles that are K-contiguous in HBM (dO, dH rows in the dgrad) keep rows of
+// 64 B with their 16-byte chunks XOR-swizzled by (row / 4) % 4; tiles that are
+// contiguous along M or N in HBM (the weights in the dgrad, both wgrad
+// operands) are kept as [k][256] rows of 512 B, chunks swizzled by 4 (k % 4),
+// and read with ds_read_b64_tr_b16, which hands each lane four consecutive k
+// of its column.  Both layouts make every read cycle conflict-free.
 
 #include "gemm_common.h"
 #include "internal.h"
@@ -28,98 +26,83 @@
 namespace w4a4 {
 namespace {
 
-constexpr int kBK = 64;
-constexpr int kRowElems = kBK + 8;         // 72 bf16 = 144 B per LDS row
-constexpr int kOpElems = kTileM * kRowElems;
-constexpr int kStageElems = 2 * kOpElems;
-constexpr int kLdsBytes = 2 * kStageElems * 2;  // 2 stages, bf16
-constexpr int kLoaders = kGemmThreads / 2;      // threads staging one operand
+typedef short short4_t __attribute__((ext_vector_type(4)));
 
-// Global column of B staged into LDS row p: lane j of wave column wn owns
-// columns n0 + wn*128 + 4j + {0,1,2,3} (one per MFMA tile ni).
-__device__ __forceinline__ int b_lds_row_of_col(int c) {  // c = column offset in tile
-  const int wn = c >> 7, rem = c & 127, j = rem >> 2, ni = rem & 3;
-  return wn * 128 + ni * 32 + j;
-}
+constexpr int kBK = 32;
+constexpr int kStages = 4;
+constexpr int kAhead = kStages - 1;
+constexpr int kTileBytes = kTileM * kBK * 2;       // 16 KB: one operand, one stage
+constexpr int kStageBytes = 2 * kTileBytes;
+constexpr int kRingBytes = kStages * kStageBytes;  // 128 KB
+constexpr int kSlotOffset = kRingBytes;
+constexpr int kLdsBytes = kSlotOffset + 16;
+constexpr int kCopiesPerStage = 2 * kTileBytes / 1024;  // 1 KB per wave-wide copy
 
-struct Regs8 {
-  u32x4_t v[8];
+// Wave grid of a workgroup: WAVES_M x WAVES_N waves over the 256 x 256 tile.
+template <int WAVES_M, int WAVES_N>
+struct Grid {
+  static constexpr int kWaves = WAVES_M * WAVES_N;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kRows = kTileM / WAVES_M;   // per wave
+  static constexpr int kCols = kTileN / WAVES_N;
+  static constexpr int kMI = kRows / 32;
+  static constexpr int kNI = kCols / 32;
+  static constexpr int kCopies = kCopiesPerStage / kWaves;  // copies per wave per stage
 };
 
-// 8 x 8 bf16 transpose: in.v[i] holds columns c..c+7 of k-row i; out.v[r]
-// holds k-rows 0..7 of column c+r.
-__device__ __forceinline__ void transpose8x8(const Regs8& in, Regs8& out) {
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const uint32_t sel = (r & 1) ? 0x07060302u : 0x05040100u;
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-      out.v[r][d] = __builtin_amdgcn_perm(in.v[2 * d + 1][r >> 1], in.v[2 * d][r >> 1], sel);
-  }
+__device__ __forceinline__ bf16x8_t join_bf16(short4_t lo, short4_t hi) {
+  typedef short short8_t __attribute__((ext_vector_type(8)));
+  const short8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// K-contiguous operand staged by 256 threads: chunk q = lt + 256 i (i < 8) is
-// row q / 8, 16 B column q % 8 of the stage.
-__device__ __forceinline__ void store_krows(uint16_t* s, int lt, const Regs8& r) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int q = lt + i * kLoaders;
-    *reinterpret_cast<u32x4_t*>(s + (q >> 3) * kRowElems + (q & 7) * 8) = r.v[i];
-  }
+__device__ __forceinline__ short4_t ds_read_tr(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) short4_t*)(p));
 }
 
-// Transposed operand staged by 256 threads: element (tile row p, k) lives at
-// krow(k)[col0 + p].  Thread lt owns k-rows 8 (lt % 8) .. +7 and the 8 tile
-// rows 8 cb .. +7, with cb = lt / 8 for A and cb = lt / 8 with bits 0 and 2
-// swapped for B (whose LDS rows are permuted).  Either way the 16 lanes of one
-// LDS write cycle hit 16 distinct 16-byte bank groups, and a wave's global
-// loads cover 8 k-rows x 128 contiguous bytes.
-template <bool PERMUTE_ROWS>
-__device__ __forceinline__ int t_col_block(int lt) {
-  const int g8 = lt >> 3;
-  if constexpr (PERMUTE_ROWS) return (g8 & ~5) | ((g8 & 1) << 2) | ((g8 >> 2) & 1);
-  return g8;
+// ---- K-contiguous tile: 256 rows x 32 k, 64 B per row, chunk c of row r at
+// slot c ^ ((r >> 2) & 3).  Copy q (16 rows): lane i fills row 16 q + i / 4,
+// slot i % 4.
+__device__ __forceinline__ int krow_src_chunk(int row, int lane) {
+  return (lane & 3) ^ ((row >> 2) & 3);
 }
-__device__ __forceinline__ int t_k_block(int lt) { return lt & 7; }
-
-template <bool PERMUTE_ROWS>
-__device__ __forceinline__ void store_transposed(uint16_t* s, int lt, const Regs8& in) {
-  Regs8 out;
-  transpose8x8(in, out);
-  const int c0 = 8 * t_col_block<PERMUTE_ROWS>(lt), kb = 8 * t_k_block(lt);
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const int p = PERMUTE_ROWS ? b_lds_row_of_col(c0 + r) : c0 + r;
-    *reinterpret_cast<u32x4_t*>(s + p * kRowElems + kb) = out.v[r];
-  }
+__device__ __forceinline__ int krow_frag_offset(int row, int ks, int hl) {
+  return row * 64 + (((ks * 2 + hl) ^ ((row >> 2) & 3)) * 16);
 }
 
-__device__ __forceinline__ void mma_stage(const uint16_t* sa, const uint16_t* sb, int a_row0,
-                                          int b_row0, int hl, floatx16_t (&acc)[2][4]) {
-#pragma unroll
-  for (int ks = 0; ks < kBK / 16; ++ks) {
-    bf16x8_t af[2], bf[4];
-#pragma unroll
-    for (int f = 0; f < 2; ++f)
-      af[f] = *reinterpret_cast<const bf16x8_t*>(sa + (a_row0 + f * 32) * kRowElems + ks * 16 + hl * 8);
-#pragma unroll
-    for (int f = 0; f < 4; ++f)
-      bf[f] = *reinterpret_cast<const bf16x8_t*>(sb + (b_row0 + f * 32) * kRowElems + ks * 16 + hl * 8);
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
-  }
+// ---- [k][256] tile: 32 k-rows of 512 B, 16-byte chunk c of k-row k at slot
+// c ^ (4 (k & 3)).  Copy q (2 k-rows): lane i fills k-row 2 q + i / 32, slot
+// i % 32.
+__device__ __forceinline__ int kcol_src_chunk(int k, int lane) {
+  return (lane & 31) ^ (4 * (k & 3));
+}
+// Byte offset of the 8-byte piece lane l reads with ds_read_tr for the 32 x 16
+// MFMA operand block whose columns start at col0 (multiple of 32), for k block
+// ks (16 k) and half r (k +0..3 or +4..7).
+__device__ __forceinline__ int kcol_frag_offset(int col0, int ks, int r, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int k = ks * 16 + 8 * (g >> 1) + 4 * r + (j >> 2);
+  const int col = col0 + 16 * (g & 1) + 4 * (j & 3);
+  return k * 512 + (((col >> 3) ^ (4 * (k & 3))) * 16) + (col & 7) * 2;
 }
 
-__device__ __forceinline__ void zero_acc(floatx16_t (&acc)[2][4]) {
+template <int MI, int NI>
+__device__ __forceinline__ void zero_acc(floatx16_t (&acc)[MI][NI]) {
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
+    for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_stage(int later) {
+  // later = stages issued after the one being waited for (0 .. kAhead-1)
+  if (later >= 2) wait_vm_barrier<2 * N>();
+  else if (later == 1) wait_vm_barrier<N>();
+  else wait_vm_barrier<0>();
 }
 
 // ------------------------------------------------------------------ dgrad
@@ -135,117 +118,118 @@ struct DgradArgs {
   uint16_t* out;       // dH [rows, 2I] or dXp [rows, H]
 };
 
-template <DgradMode MODE>
-__global__ void __launch_bounds__(kGemmThreads, 1)
+template <DgradMode MODE, class G>
+__global__ void __launch_bounds__(G::kThreads, 1)
 dgrad_kernel(DgradArgs args) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
-  uint16_t* lds = reinterpret_cast<uint16_t*>(lds_raw);
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 3, wn = wave >> 2, r32 = lane & 31, hl = lane >> 5;
+  const int wrow = (wave % (kTileM / G::kRows)) * G::kRows;
+  const int wcol = (wave / (kTileM / G::kRows)) * G::kCols;
+  const int r32 = lane & 31, hl = lane >> 5;
   const int n_tiles = (args.N + kTileN - 1) / kTileN;
-  TileCoord tc = grouped_m_tile(args.offsets, args.E, n_tiles, reinterpret_cast<int*>(lds_raw));
+  TileCoord tc = grouped_m_tile(args.offsets, args.E, n_tiles, reinterpret_cast<int*>(lds + kSlotOffset));
   if (!tc.valid) return;
-  __syncthreads();
   const int n0 = tc.n_tile * kTileN;
+  const int64_t last_row = args.rows_alloc - 1;
 
-  // waves 0-3: B = W[e] viewed as [K][N] (transposed staging);
-  // waves 4-7: A = rows of dO / dH (K-contiguous staging)
-  const bool loads_a = tid >= kLoaders;
-  const int lt = tid & (kLoaders - 1);
-  const uint16_t* src[8];
-  bool live = true;
-  if (loads_a) {
+  // ---- copy sources: A = rows of dO / dH (K-contiguous), B = W[e] as [K][N]
+  const uint8_t* a_src[G::kCopies / 2];
+  const uint8_t* b_src[G::kCopies / 2];
+  const uint16_t* we = args.w + static_cast<int64_t>(tc.e) * args.K * args.N;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int q = lt + i * kLoaders;
-      int64_t r = tc.m0 + (q >> 3);
-      if (r >= args.rows_alloc) r = args.rows_alloc - 1;   // in bounds; never stored
-      src[i] = args.g + r * args.K + (q & 7) * 8;
+  for (int c = 0; c < G::kCopies / 2; ++c) {
+    const int q = wave * (G::kCopies / 2) + c;
+    const int row = 16 * q + (lane >> 2);
+    a_src[c] = reinterpret_cast<const uint8_t*>(args.g + min(tc.m0 + row, last_row) * args.K) +
+               krow_src_chunk(row, lane) * 16;
+    const int k = 2 * q + (lane >> 5);
+    int col = n0 + kcol_src_chunk(k, lane) * 8;
+    col = min(col, args.N - 8);   // columns past N only feed outputs never stored
+    b_src[c] = reinterpret_cast<const uint8_t*>(we + static_cast<int64_t>(k) * args.N + col);
+  }
+  const int64_t a_step = kBK * 2, b_step = static_cast<int64_t>(kBK) * args.N * 2;  // bytes per stage
+  auto issue = [&](int kt) {
+    uint8_t* st = lds + (kt % kStages) * kStageBytes;
+#pragma unroll
+    for (int c = 0; c < G::kCopies / 2; ++c) {
+      const int q = wave * (G::kCopies / 2) + c;
+      dma16(a_src[c] + kt * a_step, st + q * 1024);
+      dma16(b_src[c] + kt * b_step, st + kTileBytes + q * 1024);
     }
-  } else {
-    const int bcol = 8 * t_col_block<true>(lt);
-    const int kb = 8 * t_k_block(lt);
-    live = n0 + bcol < args.N;   // N % 8 == 0: whole group in or out
-    const uint16_t* wb = args.w + static_cast<int64_t>(tc.e) * args.K * args.N + n0 + bcol;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) src[i] = wb + static_cast<int64_t>(kb + i) * args.N;
-  }
-  const int64_t kstep = loads_a ? kBK : static_cast<int64_t>(kBK) * args.N;  // elements per stage
-  Regs8 pf;
-  auto load = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      pf.v[i] = live ? *reinterpret_cast<const u32x4_t*>(src[i] + kt * kstep) : u32x4_t{0u, 0u, 0u, 0u};
-  };
-  auto store = [&](int buf) {
-    uint16_t* s = lds + buf * kStageElems;
-    if (loads_a) store_krows(s, lt, pf);
-    else store_transposed<true>(s + kOpElems, lt, pf);
   };
 
-  floatx16_t acc[2][4];
+  // ---- fragment addresses (within a stage)
+  int a_off[G::kMI][2], b_off[G::kNI][2][2];
+#pragma unroll
+  for (int f = 0; f < G::kMI; ++f)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) a_off[f][ks] = krow_frag_offset(wrow + f * 32 + r32, ks, hl);
+#pragma unroll
+  for (int f = 0; f < G::kNI; ++f)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) b_off[f][ks][r] = kTileBytes + kcol_frag_offset(wcol + f * 32, ks, r, lane);
+
+  floatx16_t acc[G::kMI][G::kNI];
   zero_acc(acc);
-  const int a_row0 = wm * kWaveM + r32, b_row0 = wn * kWaveN + r32;
   const int nk = args.K / kBK;
-  load(0);
-  store(0);
-  __syncthreads();
+  for (int s = 0; s < kAhead && s < nk; ++s) issue(s);
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) load(kt + 1);
-    const uint16_t* sa = lds + (kt & 1) * kStageElems;
-    mma_stage(sa, sa + kOpElems, a_row0, b_row0, hl, acc);
-    if (kt + 1 < nk) store((kt + 1) & 1);
-    __syncthreads();
+    wait_stage<G::kCopies>(min(kAhead - 1, nk - 1 - kt));
+    if (kt + kAhead < nk) issue(kt + kAhead);
+    const uint8_t* st = lds + (kt % kStages) * kStageBytes;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8_t af[G::kMI], bf[G::kNI];
+#pragma unroll
+      for (int f = 0; f < G::kMI; ++f) af[f] = *reinterpret_cast<const bf16x8_t*>(st + a_off[f][ks]);
+#pragma unroll
+      for (int f = 0; f < G::kNI; ++f)
+        bf[f] = join_bf16(ds_read_tr(st + b_off[f][ks][0]), ds_read_tr(st + b_off[f][ks][1]));
+#pragma unroll
+      for (int mi = 0; mi < G::kMI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < G::kNI; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
+    }
   }
 
-  const int n = n0 + wn * kWaveN + 4 * r32;
-  if (n >= args.N) return;
+  // ---- epilogue: lane (r32, hl) holds column wcol + 32 ni + r32 of 16 rows per mi
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
-    if (tc.m0 + wm * kWaveM + mi * 32 >= tc.m_end) continue;
-    if constexpr (MODE == DgradMode::FC1) {
+  for (int mi = 0; mi < G::kMI; ++mi) {
+    if (tc.m0 + wrow + mi * 32 >= tc.m_end) continue;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = tc.m0 + acc_row(wm * kWaveM, mi, v, hl);
-        if (row >= tc.m_end) continue;
-        u32x2_t pk;
-        pk[0] = pack_bf16x2(acc[mi][0][v], acc[mi][1][v]);
-        pk[1] = pack_bf16x2(acc[mi][2][v], acc[mi][3][v]);
-        *reinterpret_cast<u32x2_t*>(args.out + row * args.N + n) = pk;
-      }
-    } else {
-      // SwiGLU backward: issue the 16 rows' h loads together, then compute
-      const int I = args.I;
-      u32x2_t hg[16], hu[16];
+    for (int ni = 0; ni < G::kNI; ++ni) {
+      const int n = n0 + wcol + ni * 32 + r32;
+      if (n >= args.N) continue;
+      if constexpr (MODE == DgradMode::FC1) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        int64_t row = tc.m0 + acc_row(wm * kWaveM, mi, v, hl);
-        if (row >= tc.m_end) row = tc.m_end - 1;   // clamped: value unused
-        hg[v] = *reinterpret_cast<const u32x2_t*>(args.h + row * (2 * I) + n);
-        hu[v] = *reinterpret_cast<const u32x2_t*>(args.h + row * (2 * I) + I + n);
-      }
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = tc.m0 + acc_row(wm * kWaveM, mi, v, hl);
-        if (row >= tc.m_end) continue;
-        float dg[4], du[4];
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-          // dA is stored as bf16 before the SwiGLU backward
-          const float da = bf16_to_f32(f32_to_bf16(acc[mi][ni][v]));
-          const float gt = bf16_to_f32(static_cast<uint16_t>(hg[v][ni >> 1] >> (16 * (ni & 1))));
-          const float up = bf16_to_f32(static_cast<uint16_t>(hu[v][ni >> 1] >> (16 * (ni & 1))));
-          const float sg = 1.0f / (1.0f + expf(-gt));
-          dg[ni] = da * up * sg * (1.0f + gt * (1.0f - sg));
-          du[ni] = da * gt * sg;
+        for (int v = 0; v < 16; ++v) {
+          const int64_t row = tc.m0 + acc_row(wrow, mi, v, hl);
+          if (row < tc.m_end) args.out[row * args.N + n] = f32_to_bf16(acc[mi][ni][v]);
         }
-        u32x2_t pg, pu;
-        pg[0] = pack_bf16x2(dg[0], dg[1]);
-        pg[1] = pack_bf16x2(dg[2], dg[3]);
-        pu[0] = pack_bf16x2(du[0], du[1]);
-        pu[1] = pack_bf16x2(du[2], du[3]);
-        *reinterpret_cast<u32x2_t*>(args.out + row * (2 * I) + n) = pg;
-        *reinterpret_cast<u32x2_t*>(args.out + row * (2 * I) + I + n) = pu;
+      } else {
+        // SwiGLU backward on bf16 dA, gate / up from the saved bf16 h
+        const int I = args.I;
+        uint16_t hg[16], hu[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          int64_t row = tc.m0 + acc_row(wrow, mi, v, hl);
+          if (row >= tc.m_end) row = tc.m_end - 1;   // clamped: value unused
+          hg[v] = args.h[row * (2 * I) + n];
+          hu[v] = args.h[row * (2 * I) + I + n];
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t row = tc.m0 + acc_row(wrow, mi, v, hl);
+          if (row >= tc.m_end) continue;
+          const float da = bf16_to_f32(f32_to_bf16(acc[mi][ni][v]));
+          const float gt = bf16_to_f32(hg[v]), up = bf16_to_f32(hu[v]);
+          const float sg = 1.0f / (1.0f + expf(-gt));
+          args.out[row * (2 * I) + n] = f32_to_bf16(da * up * sg * (1.0f + gt * (1.0f - sg)));
+          args.out[row * (2 * I) + I + n] = f32_to_bf16(da * gt * sg);
+        }
       }
     }
   }
@@ -254,23 +238,20 @@ dgrad_kernel(DgradArgs args) {
 // ------------------------------------------------------------------ wgrad
 struct WgradArgs {
   int M, N, E;             // dW[e] is [M, N]
-  int64_t g_stride;        // row stride of G (= M)
-  int64_t s_stride;        // row stride of S (= N)
   const int32_t* offsets;
   const uint16_t* g;       // G [rows, M]:  A(m, r) = G[r][m]
-  const uint16_t* s;       // S [*, N]:     B(r, n) = S[src(r)][n]
-  const int32_t* src_row;  // gather variant: src(r) = src_row[r] (-1 = zero row)
+  const uint16_t* s;       // S [rows, N]:  B(r, n) = S[r][n]
   uint16_t* out;           // [E, M, N]
 };
 
-// GATHER: B rows are S[src_row[r]] (x gathered by token), else S[r].
-template <bool GATHER>
-__global__ void __launch_bounds__(kGemmThreads, 1)
+template <class G>
+__global__ void __launch_bounds__(G::kThreads, 1)
 wgrad_kernel(WgradArgs args) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
-  uint16_t* lds = reinterpret_cast<uint16_t*>(lds_raw);
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 3, wn = wave >> 2, r32 = lane & 31, hl = lane >> 5;
+  const int wrow = (wave % (kTileM / G::kRows)) * G::kRows;
+  const int wcol = (wave / (kTileM / G::kRows)) * G::kCols;
+  const int r32 = lane & 31, hl = lane >> 5;
   const int m_tiles = args.M / kTileM, n_tiles = (args.N + kTileN - 1) / kTileN;
   const int64_t total = static_cast<int64_t>(args.E) * m_tiles * n_tiles;
   const int64_t per_xcd = (total + kXcds - 1) / kXcds;
@@ -283,85 +264,92 @@ wgrad_kernel(WgradArgs args) {
   const int nt = static_cast<int>(L % n_tiles);
   const int m0 = mt * kTileM, n0 = nt * kTileN;
   const int64_t r_begin = args.offsets[e], r_end = args.offsets[e + 1];
+  const int64_t nrows = r_end - r_begin;
+  const int nk = static_cast<int>((nrows + kBK - 1) / kBK);
 
-  // waves 0-3 stage A (rows of G), waves 4-7 stage B (rows of S); both transposed
-  const bool loads_b = tid >= kLoaders;
-  const int lt = tid & (kLoaders - 1);
-  const int kb = 8 * t_k_block(lt);
-  const uint16_t* base;
-  int64_t stride;
-  bool live;
-  if (loads_b) {
-    const int bcol = 8 * t_col_block<true>(lt);
-    base = args.s + n0 + bcol;
-    stride = args.s_stride;
-    live = n0 + bcol < args.N;
-  } else {
-    base = args.g + m0 + 8 * t_col_block<false>(lt);
-    stride = args.g_stride;
-    live = true;
-  }
-  // Source rows, one stage ahead of the data loads (the gather's index loads
-  // would otherwise sit on the critical path).
-  int32_t src[8];
-  auto load_src = [&](int64_t r0) {
+  // ---- copy sources: both operands [k = row][256 columns]
+  int a_col[G::kCopies / 2], b_col[G::kCopies / 2], kk[G::kCopies / 2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t r = r0 + kb + i;
-      if (GATHER && loads_b) src[i] = r < r_end ? args.src_row[r] : -1;
-      else src[i] = r < r_end ? static_cast<int32_t>(r) : -1;
+  for (int c = 0; c < G::kCopies / 2; ++c) {
+    const int q = wave * (G::kCopies / 2) + c;
+    kk[c] = 2 * q + (lane >> 5);
+    a_col[c] = m0 + kcol_src_chunk(kk[c], lane) * 8;
+    b_col[c] = min(n0 + kcol_src_chunk(kk[c], lane) * 8, args.N - 8);  // past N: never stored
+  }
+  auto issue = [&](int kt) {
+    uint8_t* st = lds + (kt % kStages) * kStageBytes;
+#pragma unroll
+    for (int c = 0; c < G::kCopies / 2; ++c) {
+      const int q = wave * (G::kCopies / 2) + c;
+      // rows past the expert's end are re-read from its last row and zeroed in LDS
+      const int64_t r = min(r_begin + static_cast<int64_t>(kt) * kBK + kk[c], r_end - 1);
+      dma16(args.g + r * args.M + a_col[c], st + q * 1024);
+      dma16(args.s + r * args.N + b_col[c], st + kTileBytes + q * 1024);
     }
   };
-  Regs8 pf;
-  auto load = [&]() {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      pf.v[i] = (src[i] >= 0 && live)
-                    ? *reinterpret_cast<const u32x4_t*>(base + static_cast<int64_t>(src[i]) * stride)
-                    : u32x4_t{0u, 0u, 0u, 0u};
-  };
-  auto store = [&](int buf) {
-    uint16_t* s = lds + buf * kStageElems;
-    if (loads_b) store_transposed<true>(s + kOpElems, lt, pf);
-    else store_transposed<false>(s, lt, pf);
-  };
 
-  floatx16_t acc[2][4];
+  int a_off[G::kMI][2][2], b_off[G::kNI][2][2];
+#pragma unroll
+  for (int f = 0; f < G::kMI; ++f)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) a_off[f][ks][r] = kcol_frag_offset(wrow + f * 32, ks, r, lane);
+#pragma unroll
+  for (int f = 0; f < G::kNI; ++f)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) b_off[f][ks][r] = kTileBytes + kcol_frag_offset(wcol + f * 32, ks, r, lane);
+
+  floatx16_t acc[G::kMI][G::kNI];
   zero_acc(acc);
-  const int a_row0 = wm * kWaveM + r32, b_row0 = wn * kWaveN + r32;
-  const int64_t nk = (r_end - r_begin + kBK - 1) / kBK;
-  if (nk > 0) {
-    load_src(r_begin);
-    load();
-    load_src(r_begin + kBK);
-    store(0);
-    __syncthreads();
-    for (int64_t kt = 0; kt < nk; ++kt) {
-      if (kt + 1 < nk) {
-        load();
-        load_src(r_begin + (kt + 2) * kBK);
+  const int tail = static_cast<int>(nrows - static_cast<int64_t>(nk - 1) * kBK);  // valid k of the last stage
+  for (int s = 0; s < kAhead && s < nk; ++s) issue(s);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_stage<G::kCopies>(min(kAhead - 1, nk - 1 - kt));
+    uint8_t* st = lds + (kt % kStages) * kStageBytes;
+    if (kt == nk - 1 && tail < kBK) {
+      // every copy of the workgroup has landed (vmcnt 0 + barrier above): zero
+      // the k-rows past the expert's end in both operands, then sync again
+      for (int i = tid; i < (kBK - tail) * 64; i += G::kThreads) {
+        const int op = i / ((kBK - tail) * 32), rem = i % ((kBK - tail) * 32);
+        *reinterpret_cast<u32x4_t*>(st + op * kTileBytes + (tail + rem / 32) * 512 + (rem % 32) * 16) =
+            u32x4_t{0u, 0u, 0u, 0u};
       }
-      const uint16_t* sa = lds + (kt & 1) * kStageElems;
-      mma_stage(sa, sa + kOpElems, a_row0, b_row0, hl, acc);
-      if (kt + 1 < nk) store((kt + 1) & 1);
-      __syncthreads();
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    if (kt + kAhead < nk) issue(kt + kAhead);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8_t af[G::kMI], bf[G::kNI];
+#pragma unroll
+      for (int f = 0; f < G::kMI; ++f)
+        af[f] = join_bf16(ds_read_tr(st + a_off[f][ks][0]), ds_read_tr(st + a_off[f][ks][1]));
+#pragma unroll
+      for (int f = 0; f < G::kNI; ++f)
+        bf[f] = join_bf16(ds_read_tr(st + b_off[f][ks][0]), ds_read_tr(st + b_off[f][ks][1]));
+#pragma unroll
+      for (int mi = 0; mi < G::kMI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < G::kNI; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
     }
   }
   uint16_t* out = args.out + static_cast<int64_t>(e) * args.M * args.N;
-  const int n = n0 + wn * kWaveN + 4 * r32;
-  if (n >= args.N) return;
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
+  for (int ni = 0; ni < G::kNI; ++ni) {
+    const int n = n0 + wcol + ni * 32 + r32;
+    if (n >= args.N) continue;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int64_t m = m0 + acc_row(wm * kWaveM, mi, v, hl);
-      u32x2_t pk;
-      pk[0] = pack_bf16x2(acc[mi][0][v], acc[mi][1][v]);
-      pk[1] = pack_bf16x2(acc[mi][2][v], acc[mi][3][v]);
-      *reinterpret_cast<u32x2_t*>(out + m * args.N + n) = pk;
-    }
+    for (int mi = 0; mi < G::kMI; ++mi)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        out[static_cast<int64_t>(m0 + acc_row(wrow, mi, v, hl)) * args.N + n] = f32_to_bf16(acc[mi][ni][v]);
   }
 }
+
+using BwdGrid = Grid<4, 2>;   // 8 waves, 64 x 128 per wave
 
 template <typename Kern>
 hipError_t set_lds(Kern k) {
@@ -371,26 +359,25 @@ hipError_t set_lds(Kern k) {
 
 template <DgradMode MODE>
 bool launch_dgrad(const DgradArgs& a, const char* name, hipStream_t s) {
-  static const hipError_t attr = set_lds(&dgrad_kernel<MODE>);
+  static const hipError_t attr = set_lds(&dgrad_kernel<MODE, BwdGrid>);
   if (attr != hipSuccess) return launch_ok(name) && false;
   const int64_t tiles = grouped_m_tiles_bound(a.rows_alloc, a.E) * ((a.N + kTileN - 1) / kTileN);
   if (tiles == 0) return true;
   {
     ProfScope p(name, s);
-    dgrad_kernel<MODE><<<dim3(xcd_grid(tiles)), dim3(kGemmThreads), kLdsBytes, s>>>(a);
+    dgrad_kernel<MODE, BwdGrid><<<dim3(xcd_grid(tiles)), dim3(BwdGrid::kThreads), kLdsBytes, s>>>(a);
   }
   return launch_ok(name);
 }
 
-template <bool GATHER>
 bool launch_wgrad(const WgradArgs& a, const char* name, hipStream_t s) {
-  static const hipError_t attr = set_lds(&wgrad_kernel<GATHER>);
+  static const hipError_t attr = set_lds(&wgrad_kernel<BwdGrid>);
   if (attr != hipSuccess) return launch_ok(name) && false;
   const int64_t tiles = static_cast<int64_t>(a.E) * (a.M / kTileM) * ((a.N + kTileN - 1) / kTileN);
   if (tiles == 0) return true;
   {
     ProfScope p(name, s);
-    wgrad_kernel<GATHER><<<dim3(xcd_grid(tiles)), dim3(kGemmThreads), kLdsBytes, s>>>(a);
+    wgrad_kernel<BwdGrid><<<dim3(xcd_grid(tiles)), dim3(BwdGrid::kThreads), kLdsBytes, s>>>(a);
   }
   return launch_ok(name);
 }
@@ -412,14 +399,14 @@ bool launch_dgrad_fc1(int64_t rows_alloc, int H, int I, int E, const int32_t* of
 
 bool launch_wgrad_fc2(int H, int I, int E, const int32_t* offsets, const uint16_t* dO,
                       const uint16_t* a, uint16_t* dW2, hipStream_t s) {
-  WgradArgs w{H, I, E, H, I, offsets, dO, a, nullptr, dW2};
-  return launch_wgrad<false>(w, "gemm_wgrad_fc2", s);
+  WgradArgs w{H, I, E, offsets, dO, a, dW2};
+  return launch_wgrad(w, "gemm_wgrad_fc2", s);
 }
 
 bool launch_wgrad_fc1(int H, int I, int E, const int32_t* offsets, const uint16_t* dH,
-                      const uint16_t* x, const int32_t* src_row, uint16_t* dW1, hipStream_t s) {
-  WgradArgs w{2 * I, H, E, 2 * I, H, offsets, dH, x, src_row, dW1};
-  return launch_wgrad<true>(w, "gemm_wgrad_fc1", s);
+                      const uint16_t* xp, uint16_t* dW1, hipStream_t s) {
+  WgradArgs w{2 * I, H, E, offsets, dH, xp, dW1};
+  return launch_wgrad(w, "gemm_wgrad_fc1", s);
 }
 
 }  // namespace w4a4

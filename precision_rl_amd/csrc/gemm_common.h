@@ -25,62 +25,61 @@ struct TileCoord {
 
 // Maps blockIdx.x onto (expert, M tile, N tile) for a GEMM whose M dimension
 // is the concatenation of the expert row groups [offsets[e], offsets[e+1]).
-// The number of tiles exists only on the device; every workgroup recomputes
-// it from the offsets (a scan over E in LDS).  Logical tiles are ordered
-// expert-major, N fastest, and dealt out in contiguous runs per XCD so that an
-// expert's weight tiles and an M tile's activations stay in one XCD's L2.
-// `scratch` must hold kGemmThreads + E ints of LDS.
+// The number of tiles exists only on the device; wave 0 of every workgroup
+// recomputes it from the offsets (lane-local sums and a wave prefix scan) and
+// publishes the result through `slot` (LDS, 4 ints).  Logical tiles are
+// ordered expert-major, N fastest, and dealt out in contiguous runs per XCD
+// so that an expert's weight tiles and an M tile's activations stay in one
+// XCD's L2.  Contains one __syncthreads().
 __device__ inline TileCoord grouped_m_tile(const int32_t* __restrict__ offsets, int E, int n_tiles,
-                                           int* scratch) {
+                                           int* slot) {
   const int tid = threadIdx.x;
-  int carry = 0;
-  for (int e0 = 0; e0 < E; e0 += kGemmThreads) {
-    const int e = e0 + tid;
-    int v = 0;
-    if (e < E) {
-      const int rows = offsets[e + 1] - offsets[e];
-      v = (rows + kTileM - 1) / kTileM;
+  if (tid < kWave) {
+    const int lane = tid;
+    const int per = (E + kWave - 1) / kWave;
+    const int e0 = lane * per, e1 = min(E, e0 + per);
+    int cnt = 0;
+    for (int e = e0; e < e1; ++e) cnt += (offsets[e + 1] - offsets[e] + kTileM - 1) / kTileM;
+    int incl = cnt;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int t = __shfl_up(incl, d, kWave);
+      if (lane >= d) incl += t;
     }
-    scratch[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < kGemmThreads; off <<= 1) {
-      int add = tid >= off ? scratch[tid - off] : 0;
-      __syncthreads();
-      scratch[tid] += add;
-      __syncthreads();
+    const int total_m = __shfl(incl, kWave - 1, kWave);
+    const int64_t total = static_cast<int64_t>(total_m) * n_tiles;
+    const int64_t per_xcd = (total + kXcds - 1) / kXcds;
+    const int64_t b = blockIdx.x;
+    const int64_t y = b / kXcds, x = b % kXcds;
+    const int64_t L = x * per_xcd + y;
+    const bool valid = y < per_xcd && L < total;
+    if (!valid) {
+      if (lane == 0) slot[0] = -1;
+    } else {
+      const int mt = static_cast<int>(L / n_tiles);
+      if (mt >= incl - cnt && mt < incl) {   // exactly one lane owns tile mt
+        int first = incl - cnt;
+        for (int e = e0; e < e1; ++e) {
+          const int t = (offsets[e + 1] - offsets[e] + kTileM - 1) / kTileM;
+          if (mt < first + t) {
+            slot[0] = e;
+            slot[1] = offsets[e] + (mt - first) * kTileM;
+            slot[2] = offsets[e + 1];
+            slot[3] = static_cast<int>(L % n_tiles);
+            break;
+          }
+          first += t;
+        }
+      }
     }
-    const int incl = scratch[tid] + carry;
-    const int chunk_total = scratch[kGemmThreads - 1];
-    __syncthreads();
-    if (e < E) scratch[kGemmThreads + e] = incl;  // parked above the scan window
-    carry += chunk_total;
-    __syncthreads();
   }
-  const int total_m = carry;
+  __syncthreads();
   TileCoord tc;
-  tc.valid = false;
-  const int64_t total = static_cast<int64_t>(total_m) * n_tiles;
-  const int64_t per_xcd = (total + kXcds - 1) / kXcds;
-  const int64_t b = blockIdx.x;
-  const int64_t y = b / kXcds, x = b % kXcds;
-  if (y >= per_xcd) return tc;
-  const int64_t L = x * per_xcd + y;
-  if (L >= total) return tc;
-  const int mt = static_cast<int>(L / n_tiles);
-  tc.n_tile = static_cast<int>(L % n_tiles);
-  // find expert e with incl[e-1] <= mt < incl[e]
-  const int* incl = scratch + kGemmThreads;
-  int lo = 0, hi = E - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi) / 2;
-    if (incl[mid] > mt) hi = mid; else lo = mid + 1;
-  }
-  const int e = lo;
-  const int first = e ? incl[e - 1] : 0;
-  tc.e = e;
-  tc.m0 = offsets[e] + static_cast<int64_t>(mt - first) * kTileM;
-  tc.m_end = offsets[e + 1];
-  tc.valid = true;
+  tc.e = slot[0];
+  tc.valid = tc.e >= 0;
+  tc.m0 = slot[1];
+  tc.m_end = slot[2];
+  tc.n_tile = slot[3];
   return tc;
 }
 
@@ -98,6 +97,46 @@ inline unsigned xcd_grid(int64_t tiles) {
 // MFMA 32x32 tile mi of a wave whose rows start at wave_row0.
 __device__ __forceinline__ int acc_row(int wave_row0, int mi, int v, int hl) {
   return wave_row0 + mi * 32 + (v & 3) + 4 * hl + 8 * (v >> 2);
+}
+
+// s_waitcnt immediate (gfx9 encoding) that waits until at most `vm`
+// vector-memory operations of this wave are outstanding; LDS and export
+// counters are left alone.
+constexpr int waitcnt_vm(int vm) {
+  return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+}
+
+// Asynchronous copy global -> LDS (global_load_lds_dwordx4 / _dword): lane
+// i's 16 bytes (4 bytes) land at lds_base + 16 i (4 i); lds_base must be
+// wave-uniform.  The copy counts on this wave's vector-memory counter and has
+// landed once wait_vm_barrier<> allows fewer outstanding operations than were
+// issued after it.  Issued from inline assembly so that the compiler's
+// dependency tracking does not treat every later LDS read as aliasing the
+// in-flight copies (it would wait for all of them); the kernels order LDS
+// reads after copies explicitly.  M0 (the copy's LDS base) is not used for
+// anything else in these kernels.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));   // low half of the flat address
+}
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"   // M0 is reserved; nothing else here uses it
+__device__ __forceinline__ void dma16(const void* g, const void* lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               ::"v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_base))) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, const void* lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+               ::"v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_base))) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Pipeline step: wait until at most VM vector-memory operations of this wave
+// are outstanding (older global->LDS copies have landed), then a workgroup
+// barrier.  No memory fence: later LDS reads are ordered by the asm's memory
+// clobber, and the copies' completion by the counter.
+template <int VM>
+__device__ __forceinline__ void wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(VM) : "memory");
 }
 
 }  // namespace w4a4

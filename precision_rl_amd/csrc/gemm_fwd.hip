@@ -15,8 +15,10 @@
 // Tiling: 256 x 256 output tile per workgroup of 8 waves (4 x 2, 64 x 128 per
 // wave, two waves per SIMD), MFMA 32x32x16 f16.  Each pipeline stage covers 128
 // of K: packed codes (64 B per row) and block scales (8 B per row) of both
-// operands go through LDS, double buffered; waves 0-3 fetch the activation tile
-// and waves 4-7 the weight tile, one stage ahead of the MFMAs.  Inside a stage,
+// operands, copied global -> LDS by the hardware (no register staging) into a
+// 4-deep ring, three stages ahead of the MFMAs.  Code rows are stored with
+// their four 16-byte chunks XOR-swizzled by (row / 4) % 4, so fragment reads
+// of 16 consecutive rows hit 16 distinct bank groups.  Inside a stage,
 // lane half h (lanes 32-63) owns the stage's second 64 k of its row; A and B
 // use the same assignment, so every MFMA k slot pairs equal k indices (the
 // reduction runs in a permuted K order; FP32 rounding of the sum is covered by
@@ -28,17 +30,18 @@
 namespace w4a4 {
 namespace {
 
-constexpr int kBK = 128;                    // K per stage
-constexpr int kCodeRow = kBK / 2;           // 64 B of codes per row per stage
-constexpr int kCodeStride = kCodeRow + 16;  // 80 B: conflict-free b128 reads
-constexpr int kScaleRow = kBK / 16;         // 8 scale bytes per row per stage
-constexpr int kOpCodes = kTileM * kCodeStride;
-constexpr int kOpScales = kTileM * kScaleRow;
-constexpr int kOpBytes = kOpCodes + kOpScales;
-constexpr int kStageBytes = 2 * kOpBytes;
-constexpr int kGxOffset = 2 * kStageBytes;  // 2 stages, then the tile's g_x
-constexpr int kLdsBytes = kGxOffset + kTileM * 4;
-constexpr int kLoaders = kGemmThreads / 2;  // threads fetching one operand
+constexpr int kBK = 128;                     // K per stage
+constexpr int kStages = 4;                   // LDS ring depth
+constexpr int kAhead = kStages - 1;          // stages in flight ahead of the MFMAs
+constexpr int kCodeRow = kBK / 2;            // 64 B of codes per row per stage
+constexpr int kScaleRow = kBK / 16;          // 8 scale bytes per row per stage
+constexpr int kCodes = kTileM * kCodeRow;    // 16 KB per operand per stage
+constexpr int kScales = kTileM * kScaleRow;  // 2 KB
+constexpr int kStageBytes = 2 * kCodes + 2 * kScales;
+constexpr int kGxOffset = kStages * kStageBytes;
+constexpr int kSlotOffset = kGxOffset + kTileM * 4;
+constexpr int kLdsBytes = kSlotOffset + 16;
+constexpr int kDmaPerStage = 6;              // per wave: 2 + 2 code copies, 1 + 1 scale copies
 
 enum class FwdMode { FC1, FC2 };
 
@@ -101,61 +104,46 @@ fwd_gemm_kernel(FwdArgs args) {
   const int r32 = lane & 31, hl = lane >> 5;
 
   const int n_tiles = MODE == FwdMode::FC1 ? args.I / 128 : args.N / kTileN;
-  TileCoord tc = grouped_m_tile(args.offsets, args.E, n_tiles, reinterpret_cast<int*>(lds));
+  TileCoord tc = grouped_m_tile(args.offsets, args.E, n_tiles,
+                                reinterpret_cast<int*>(lds + kSlotOffset));
   if (!tc.valid) return;
-  __syncthreads();  // the scan scratch aliases the stage buffers
 
   const int64_t K2 = args.K / 2, K16 = args.K / 16;
-  // ---- this thread's loads: waves 0-3 fetch A (activations), 4-7 fetch B (weights)
-  const bool loads_b = tid >= kLoaders;
-  const int lt = tid & (kLoaders - 1);
-  const uint8_t* code_src[4];
-  const uint8_t* scale_src;
-  {
-    const uint8_t* wcodes = args.w.codes + static_cast<int64_t>(tc.e) * args.N * K2;
-    const uint8_t* wscales = args.w.scales + static_cast<int64_t>(tc.e) * args.N * K16;
+  const int64_t last_row = args.rows_alloc - 1;
+  // ---- per-lane sources of this wave's copies (rows past the allocation are
+  // clamped: they only feed accumulator rows that are never stored)
+  const uint8_t* wcodes = args.w.codes + static_cast<int64_t>(tc.e) * args.N * K2;
+  const uint8_t* wscales = args.w.scales + static_cast<int64_t>(tc.e) * args.N * K16;
+  const uint8_t* a_code_src[2];
+  const uint8_t* b_code_src[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = lt + i * kLoaders;
-      const int row = q >> 2, col = q & 3;
-      if (loads_b) {
-        code_src[i] = wcodes + static_cast<int64_t>(b_row_of<MODE>(row, tc.n_tile, args.I)) * K2 + col * 16;
-      } else {
-        int64_t ar = tc.m0 + row;
-        if (ar >= args.rows_alloc) ar = args.rows_alloc - 1;   // in bounds; never stored
-        code_src[i] = args.a.codes + ar * K2 + col * 16;
-      }
-    }
-    if (loads_b) {
-      scale_src = wscales + static_cast<int64_t>(b_row_of<MODE>(lt, tc.n_tile, args.I)) * K16;
-    } else {
-      int64_t ar = tc.m0 + lt;
-      if (ar >= args.rows_alloc) ar = args.rows_alloc - 1;
-      scale_src = args.a.scales + ar * K16;
-      // outer scales of the tile's rows, read by the epilogue from LDS
-      reinterpret_cast<float*>(lds + kGxOffset)[lt] = args.a.outer[ar];
-    }
+  for (int c = 0; c < 2; ++c) {
+    const int j = 2 * wave + c;                      // 16-row block of this copy
+    const int row = 16 * j + (lane >> 2);
+    const int chunk = (lane & 3) ^ ((row >> 2) & 3); // logical chunk stored at lane's slot
+    a_code_src[c] = args.a.codes + min(tc.m0 + row, last_row) * K2 + chunk * 16;
+    b_code_src[c] = wcodes + static_cast<int64_t>(b_row_of<MODE>(row, tc.n_tile, args.I)) * K2 + chunk * 16;
   }
-  const float* s_gx = reinterpret_cast<const float*>(lds + kGxOffset);
-  const int op_off = loads_b ? kOpBytes : 0;
-
-  u32x4_t pf_code[4];
-  u32x2_t pf_scale;
-  auto load_stage = [&](int kt) {
-    const int64_t cb = static_cast<int64_t>(kt) * kCodeRow;
+  const int srow = 32 * wave + (lane >> 1);           // scale row of this lane's dword copy
+  const uint8_t* a_scale_src = args.a.scales + min(tc.m0 + srow, last_row) * K16 + (lane & 1) * 4;
+  const uint8_t* b_scale_src =
+      wscales + static_cast<int64_t>(b_row_of<MODE>(srow, tc.n_tile, args.I)) * K16 + (lane & 1) * 4;
+  auto issue = [&](int kt) {
+    uint8_t* st = lds + (kt % kStages) * kStageBytes;
+    const int64_t cb = static_cast<int64_t>(kt) * kCodeRow, sb = static_cast<int64_t>(kt) * kScaleRow;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pf_code[i] = *reinterpret_cast<const u32x4_t*>(code_src[i] + cb);
-    pf_scale = *reinterpret_cast<const u32x2_t*>(scale_src + static_cast<int64_t>(kt) * kScaleRow);
-  };
-  auto store_stage = [&](int buf) {
-    uint8_t* base = lds + buf * kStageBytes + op_off;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = lt + i * kLoaders;
-      *reinterpret_cast<u32x4_t*>(base + (q >> 2) * kCodeStride + (q & 3) * 16) = pf_code[i];
+    for (int c = 0; c < 2; ++c) {
+      const int j = 2 * wave + c;
+      dma16(a_code_src[c] + cb, st + j * 1024);
+      dma16(b_code_src[c] + cb, st + kCodes + j * 1024);
     }
-    *reinterpret_cast<u32x2_t*>(base + kOpCodes + lt * kScaleRow) = pf_scale;
+    dma4(a_scale_src + sb, st + 2 * kCodes + wave * 256);
+    dma4(b_scale_src + sb, st + 2 * kCodes + kScales + wave * 256);
   };
+
+  // outer scales of the tile's rows, read by the epilogue
+  float* s_gx = reinterpret_cast<float*>(lds + kGxOffset);
+  if (tid < kTileM) s_gx[tid] = args.a.outer[min(tc.m0 + tid, last_row)];
 
   floatx16_t acc[2][4];
 #pragma unroll
@@ -164,36 +152,43 @@ fwd_gemm_kernel(FwdArgs args) {
     for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
-  bool mi_live[2];
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi) mi_live[mi] = tc.m0 + wm * kWaveM + mi * 32 < tc.m_end;
 
   const int a_row0 = wm * kWaveM + r32, b_row0 = wn * kWaveN + r32;
   const int nk = args.K / kBK;
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
+  for (int s = 0; s < kAhead && s < nk; ++s) issue(s);
 
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) load_stage(kt + 1);
-    const uint8_t* sa = lds + (kt & 1) * kStageBytes;
-    const uint8_t* sb = sa + kOpBytes;
+    // stage kt has landed once at most the later stages' copies are pending
+    const int later = min(kAhead - 1, nk - 1 - kt);
+    if (later >= 2) wait_vm_barrier<2 * kDmaPerStage>();
+    else if (later == 1) wait_vm_barrier<kDmaPerStage>();
+    else wait_vm_barrier<0>();
+    if (kt + kAhead < nk) issue(kt + kAhead);   // refills the slot read in iteration kt-1
+
+    const uint8_t* sa = lds + (kt % kStages) * kStageBytes;
+    const uint8_t* sb = sa + kCodes;
+    const uint8_t* ssa = sa + 2 * kCodes;
+    const uint8_t* ssb = ssa + kScales;
     uint32_t a_sc[2], b_sc[4];
 #pragma unroll
     for (int f = 0; f < 2; ++f)
-      a_sc[f] = *reinterpret_cast<const uint32_t*>(sa + kOpCodes + (a_row0 + f * 32) * kScaleRow + hl * 4);
+      a_sc[f] = *reinterpret_cast<const uint32_t*>(ssa + (a_row0 + f * 32) * kScaleRow + hl * 4);
 #pragma unroll
     for (int f = 0; f < 4; ++f)
-      b_sc[f] = *reinterpret_cast<const uint32_t*>(sb + kOpCodes + (b_row0 + f * 32) * kScaleRow + hl * 4);
+      b_sc[f] = *reinterpret_cast<const uint32_t*>(ssb + (b_row0 + f * 32) * kScaleRow + hl * 4);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       u32x4_t ac[2], bc[4];
 #pragma unroll
-      for (int f = 0; f < 2; ++f)
-        ac[f] = *reinterpret_cast<const u32x4_t*>(sa + (a_row0 + f * 32) * kCodeStride + hl * 32 + hh * 16);
+      for (int f = 0; f < 2; ++f) {
+        const int row = a_row0 + f * 32;
+        ac[f] = *reinterpret_cast<const u32x4_t*>(sa + row * kCodeRow + (((hl * 2 + hh) ^ ((row >> 2) & 3)) * 16));
+      }
 #pragma unroll
-      for (int f = 0; f < 4; ++f)
-        bc[f] = *reinterpret_cast<const u32x4_t*>(sb + (b_row0 + f * 32) * kCodeStride + hl * 32 + hh * 16);
+      for (int f = 0; f < 4; ++f) {
+        const int row = b_row0 + f * 32;
+        bc[f] = *reinterpret_cast<const u32x4_t*>(sb + row * kCodeRow + (((hl * 2 + hh) ^ ((row >> 2) & 3)) * 16));
+      }
       half2_t ad[2][2], bd[4][2];   // block scales of blocks 2hh, 2hh+1 as f16 pairs
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
@@ -213,17 +208,14 @@ fwd_gemm_kernel(FwdArgs args) {
 #pragma unroll
         for (int f = 0; f < 4; ++f) bf[f] = decode8(bc[f][s4], bd[f][s4 >> 1]);
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi) {
-          if (!mi_live[mi]) continue;   // all 32 rows past the expert's end
+        for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
           for (int ni = 0; ni < 4; ++ni)
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
-        }
       }
     }
-    if (kt + 1 < nk) store_stage((kt + 1) & 1);
-    __syncthreads();
   }
+  __syncthreads();   // s_gx visible (written before the loop; every wave passed a barrier since)
 
   // ---------------------------------------------------------------- epilogue
   const float* wouter = args.w.outer + static_cast<int64_t>(tc.e) * args.N;

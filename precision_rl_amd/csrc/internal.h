@@ -77,7 +77,11 @@ bool launch_dgrad_fc1(int64_t rows_alloc, int H, int I, int E, const int32_t* of
 bool launch_wgrad_fc2(int H, int I, int E, const int32_t* offsets, const uint16_t* dO,
                       const uint16_t* a, uint16_t* dW2, hipStream_t s);
 bool launch_wgrad_fc1(int H, int I, int E, const int32_t* offsets, const uint16_t* dH,
-                      const uint16_t* x, const int32_t* src_row, uint16_t* dW1, hipStream_t s);
+                      const uint16_t* xp, uint16_t* dW1, hipStream_t s);
+
+// xp[r] = x[src_row[r]] (zeros for pad rows), rows [0, offsets[E]).
+bool launch_gather_rows(int64_t rows_alloc, int H, const uint16_t* x, const int32_t* src_row,
+                        const int32_t* offsets, int E, uint16_t* xp, hipStream_t s);
 
 // b7: dX[t] = bf16(sum_j dXp[row_map[t,j]]).
 bool launch_gather_sum(int64_t T, int H, int k, const uint16_t* dXp, const int32_t* row_map,
