@@ -37,7 +37,7 @@ KERNEL_SOURCES = {
     "gemm_wgrad_fc1": "gemm_bwd.hip", "gemm_wgrad_fc2": "gemm_bwd.hip",
     "quantize_scatter": "quantize.hip", "requant": "quantize.hip",
     "unpermute": "elementwise.hip", "do_gather_scale": "elementwise.hip",
-    "dx_gather_sum": "elementwise.hip",
+    "dx_gather_sum": "elementwise.hip", "x_gather_rows": "elementwise.hip",
 }
 
 
@@ -60,6 +60,8 @@ def algorithmic_work(T, H, E, k, I):
         "unpermute": T * (k * H * 2 + k * 8 + H * 2),
         "do_gather_scale": T * (H * 2 + k * 8) + M * H * 2,
         "dx_gather_sum": T * (k * H * 2 + k * 4 + H * 2),
+        # read each token once (the k copies come from cache), src_row; write M rows
+        "x_gather_rows": T * H * 2 + M * 4 + M * H * 2,
     }
     return fl, by
 
@@ -121,7 +123,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-tokens", type=int, default=6144)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
@@ -163,10 +165,13 @@ def main():
                  dw1=torch.empty(E, 2 * I, H, dtype=torch.bfloat16, device=dev),
                  dw2=torch.empty(E, H, I, dtype=torch.bfloat16, device=dev))
 
-    # a plain elementwise copy of known size, for scaling HBM counters (--pmc runs)
-    calib = torch.empty(128 << 20, dtype=torch.bfloat16, device=dev)
+    # a plain elementwise copy of known size (reads 256 MiB, writes 256 MiB), for
+    # scaling the HBM counters of --pmc runs
+    calib = torch.ones(128 << 20, dtype=torch.bfloat16, device=dev)
     calib_out = torch.empty_like(calib)
+    torch.cuda.synchronize()
     torch.neg(calib, out=calib_out)
+    del calib, calib_out
 
     def step():
         b.w4a4_quantize_permute(x, idx, E, A, out=xq, workspace=ws_qp)

@@ -76,7 +76,7 @@ int64_t w4a4_rows_capacity(int64_t T, int k, int E, int row_align);
 size_t w4a4_workspace_size(int kind, int64_t T, int H, int I, int E, int k, int row_align);
 
 /*
- * w4a4_quantize_permute -- steps a1-a3: route the tokens to their experts and
+ * w4a4_quantize_permute -- route the tokens to their experts and
  * write each token's two-level NVFP4 encoding into every one of its k
  * expert-contiguous destination rows.  The per-token amax is gathered in the
  * same pass that reads the token (no separate amax scan).
@@ -106,7 +106,7 @@ w4a4_status w4a4_quantize_permute(
     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * w4a4_grouped_expert_fwd -- steps a5-a9: FC1 -> SwiGLU -> requantise -> FC2
+ * w4a4_grouped_expert_fwd -- FC1 -> SwiGLU -> requantise -> FC2
  * over ragged, possibly empty expert groups, then the router-weighted
  * unpermute.
  *   Defined by: rainbus review, "core method" and method steps 5-6 (block-
@@ -156,7 +156,7 @@ w4a4_status w4a4_grouped_expert_fwd(
     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * w4a4_expert_bwd -- steps b1-b7: the straight-through BF16 backward on the
+ * w4a4_expert_bwd -- the straight-through BF16 backward on the
  * saved high-precision operands (no backward quantisation).
  *   Defined by: AI summary, "Methodology in Plain English" (straight-through
  *   estimator using saved original BF16 activations and weights); miniTE

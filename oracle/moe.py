@@ -23,7 +23,7 @@ from . import nvfp4 as q
 
 
 # ---------------------------------------------------------------------------
-# a1: routing.
+# Routing.
 # ---------------------------------------------------------------------------
 def rows_capacity(T, k, E, row_align):
     """Upper bound on the padded dispatched-row count: T*k + E*(A-1)."""
@@ -84,7 +84,7 @@ def route_fast(topk_idx, E, row_align=1):
 
 
 # ---------------------------------------------------------------------------
-# a2-a3: quantize + permute.
+# Quantize + permute (per-token amax, encode, scatter).
 # ---------------------------------------------------------------------------
 def quantize_permute(x, topk_idx, E, row_align=1, routed=None):
     """Per-token NVFP4 of x, written to every destination row of the token.
@@ -115,7 +115,7 @@ def quantize_permute(x, topk_idx, E, row_align=1, routed=None):
 
 
 def quantize_weights(w):
-    """a4: per-row NVFP4 of stacked expert weights [E, N, K] (per output row n).
+    """Offline weight quantisation: per-row NVFP4 of stacked expert weights [E, N, K] (per output row n).
 
     READING of "per row of the flattened expert weights" (Technical Report,
     section 4.3 table): one outer scale per output feature n, over the
@@ -129,7 +129,7 @@ def quantize_weights(w):
 
 
 # ---------------------------------------------------------------------------
-# a5-a9: forward.
+# Forward: FC1, SwiGLU, requantise, FC2, unpermute.
 # ---------------------------------------------------------------------------
 def expert_of_rows(offsets):
     """Expert id of every padded row."""
@@ -212,7 +212,7 @@ def unpermute_sum(o, row_map, topk_w):
 
 
 # ---------------------------------------------------------------------------
-# b1-b7: straight-through BF16 backward.
+# Straight-through BF16 backward.
 # ---------------------------------------------------------------------------
 def backward(dy, x, w1, w2, h, a, topk_w, offsets, row_map, src_row, rnd=True):
     """Straight-through backward on the saved BF16 operands.
@@ -223,14 +223,14 @@ def backward(dy, x, w1, w2, h, a, topk_w, offsets, row_map, src_row, rnd=True):
     bypass" skips backward quantisation).  Saved operands: x, W1, W2 (bf16
     originals), h (bf16 FC1 output), a (bf16 SwiGLU output).
 
-      b1  dO[r]   = p[t,j] dY[t]                 r = row_map[t, j]
-      b2  dA      = dO_e W2[e]                   [n_e, I]
-      b3  dW2[e]  = dO_e^T a_e                   [H, I]
-      b4  dgate   = dA * up * s (1 + gate (1 - s)),  dup = dA * gate * s,
+      dO gather:  dO[r]   = p[t,j] dY[t]                 r = row_map[t, j]
+      FC2 dgrad:  dA      = dO_e W2[e]                   [n_e, I]
+      FC2 wgrad:  dW2[e]  = dO_e^T a_e                   [H, I]
+      SwiGLU bwd: dgate   = dA * up * s (1 + gate (1 - s)),  dup = dA * gate * s,
           s = sigmoid(gate)
-      b5  dXp     = dH_e W1[e]                   [n_e, H]
-      b6  dW1[e]  = dH_e^T x[src_row]            [2I, H]
-      b7  dX[t]   = sum_j dXp[row_map[t, j]]
+      FC1 dgrad:  dXp     = dH_e W1[e]                   [n_e, H]
+      FC1 wgrad:  dW1[e]  = dH_e^T x[src_row]            [2I, H]
+      dX gather:  dX[t]   = sum_j dXp[row_map[t, j]]
 
     With ``rnd`` every stored tensor (dO, dA, dH, dXp, dX, dW) is rounded to
     bf16 as the GPU stores it; without it the function is the exact float64

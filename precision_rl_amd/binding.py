@@ -94,7 +94,7 @@ def _workspace(nbytes, device, ws=None):
 
 # ----------------------------------------------------------------- wrappers
 def w4a4_quantize_permute(x, topk_idx, E, row_align=1, out=None, workspace=None):
-    """Steps a1-a3.  x: [T, K] bf16 cuda; topk_idx: [T, k] int32 or None
+    """Route + per-token amax + NVFP4 encode + scatter.  x: [T, K] bf16 cuda; topk_idx: [T, k] int32 or None
     (identity routing, one encoded row per input row).  Returns a dict of
     tensors: codes [cap, K/2] u8, scales [cap, K/16] u8, outer [cap] f32,
     offsets [E+1], row_map [T, k], src_row [cap] (int32)."""
@@ -124,7 +124,7 @@ def w4a4_quantize_permute(x, topk_idx, E, row_align=1, out=None, workspace=None)
 
 
 def quantize_weights(w):
-    """Per-row NVFP4 of stacked expert weights w [E, N, K] bf16 (a4).
+    """Per-row NVFP4 of stacked expert weights w [E, N, K] bf16 (offline, identity routing).
     Returns dict(codes [E, N, K/2], scales [E, N, K/16], outer [E, N])."""
     E, N, K = w.shape
     q = w4a4_quantize_permute(w.reshape(E * N, K), None, 1)
@@ -134,7 +134,7 @@ def quantize_weights(w):
 
 def w4a4_grouped_expert_fwd(xq, topk_w, w1q, w2q, T, H, I, E, k, row_align=1,
                             save=False, debug=False, y=None, workspace=None, saved=None):
-    """Steps a5-a9.  xq: result of ``w4a4_quantize_permute``; w1q / w2q: results
+    """Grouped expert forward: FC1 -> SwiGLU -> requantise -> FC2 -> unpermute.  xq: result of ``w4a4_quantize_permute``; w1q / w2q: results
     of ``quantize_weights``.  Returns dict(y, and h/a when ``save``, and the
     FC1 pre-cast values plus the FC2-input encoding when ``debug``)."""
     lib = load()
@@ -168,7 +168,7 @@ def w4a4_grouped_expert_fwd(xq, topk_w, w1q, w2q, T, H, I, E, k, row_align=1,
 
 def w4a4_expert_bwd(dy, x, w1, w2, h, a, topk_w, xq, T, H, I, E, k, row_align=1,
                     out=None, workspace=None):
-    """Steps b1-b7.  Returns dict(dx [T, H], dw1 [E, 2I, H], dw2 [E, H, I]) bf16."""
+    """Straight-through BF16 backward.  Returns dict(dx [T, H], dw1 [E, 2I, H], dw2 [E, H, I]) bf16."""
     lib = load()
     dev = dy.device
     if out is None:

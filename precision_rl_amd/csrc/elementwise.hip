@@ -1,7 +1,7 @@
 // HBM-bound gathers of the expert path (gfx950):
-//   a9  unpermute:     y[t]  = bf16( sum_j p[t,j] * o[row_map[t,j]] )
-//   b7  gather-sum:    dX[t] = bf16( sum_j dXp[row_map[t,j]] )
-//   b1  gather-scale:  dO[r] = bf16( p[t,j] * dY[t] ),  t = src_row[r], pad rows 0
+//   unpermute:     y[t]  = bf16( sum_j p[t,j] * o[row_map[t,j]] )
+//   gather-sum:    dX[t] = bf16( sum_j dXp[row_map[t,j]] )
+//   gather-scale:  dO[r] = bf16( p[t,j] * dY[t] ),  t = src_row[r], pad rows 0
 // The router coefficients enter in the unpermute, on the bf16 expert outputs,
 // summed in FP32 in ascending j (a reading of the pages, which name the
 // router-coefficient position as a choice the execution specification must fix:

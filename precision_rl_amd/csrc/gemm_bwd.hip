@@ -1,14 +1,14 @@
-// Steps b2-b6: the straight-through BF16 backward GEMMs on gfx950 (AI summary,
+// The straight-through BF16 backward GEMMs on gfx950 (AI summary,
 // "Methodology in Plain English": straight-through estimator on the saved
 // original BF16 operands; miniTE Technical Report, section 4.3: BF16 backward
 // through the layer bypass, no backward quantisation).
 //
 //   dgrad (M = dispatched rows of expert e, ragged):
-//     b2: dA  = dO_e . W2[e]     K = H,  N = I, epilogue = SwiGLU backward (b4)
-//     b5: dXp = dH_e . W1[e]     K = 2I, N = H
+//     FC2 dgrad: dA  = dO_e . W2[e]     K = H,  N = I, epilogue = SwiGLU backward
+//     FC1 dgrad: dXp = dH_e . W1[e]     K = 2I, N = H
 //   wgrad (K = dispatched rows of expert e, ragged, possibly empty):
-//     b3: dW2[e] = dO_e^T . a_e            M = H,  N = I
-//     b6: dW1[e] = dH_e^T . xp_e           M = 2I, N = H   (xp = x gathered by row)
+//     FC2 wgrad: dW2[e] = dO_e^T . a_e            M = H,  N = I
+//     FC1 wgrad: dW1[e] = dH_e^T . xp_e           M = 2I, N = H   (xp = x gathered by row)
 //
 // 256 x 256 output tile per workgroup, MFMA 32x32x16 bf16, FP32 accumulation.
 // K advances 32 per stage through a 4-deep LDS ring filled by the hardware's

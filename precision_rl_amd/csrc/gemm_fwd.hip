@@ -1,4 +1,4 @@
-// Steps a5 (+a6) and a8: grouped block-scaled GEMMs FC1 and FC2 on gfx950.
+// FC1 (with the SwiGLU in its epilogue) and FC2: grouped block-scaled GEMMs FC1 and FC2 on gfx950.
 //
 // The pages' recipe (rainbus review, "core method"; AI summary, "Methodology in
 // Plain English") accumulates the block-scaled product U_e = MMA(X_e, W_e^T)

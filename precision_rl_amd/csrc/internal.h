@@ -28,13 +28,13 @@ constexpr int kRouteChunk = 256;      // tokens per routing chunk (one workgroup
 
 size_t route_workspace_bytes(int64_t T, int E);
 
-// a1 + a2 + a3: route, per-token amax, two-level NVFP4, scatter to k rows.
+// Route, per-token amax, two-level NVFP4, scatter to k rows.
 bool launch_quantize_permute(const uint16_t* x, int64_t T, int K, const int32_t* topk_idx,
                              int k, int E, int row_align, uint8_t* codes, uint8_t* scales,
                              float* outer, int32_t* offsets, int32_t* row_map, int32_t* src_row,
                              void* ws, hipStream_t s);
 
-// a7: per-row NVFP4 of the bf16 rows of `a` ([rows_alloc, K]) for the rows
+// Requantise: per-row NVFP4 of the bf16 rows of `a` ([rows_alloc, K]) for the rows
 // [0, offsets[E]) (device bound); pad rows (src_row < 0) get zeros.
 bool launch_requant(const uint16_t* a, int64_t rows_alloc, int K, const int32_t* offsets, int E,
                     const int32_t* src_row, uint8_t* codes, uint8_t* scales, float* outer,
@@ -47,33 +47,33 @@ struct Fp4Operand {
   const float* outer;     // [rows]
 };
 
-// a5 (+ fused a6): FC1 over expert groups, SwiGLU in the epilogue.
+// FC1 (SwiGLU fused into the epilogue): over expert groups, SwiGLU in the epilogue.
 bool launch_fc1(int64_t rows_alloc, int H, int I, int E, const int32_t* offsets, Fp4Operand x,
                 Fp4Operand w1, uint16_t* h_out, uint16_t* a_out, float* dbg_f32, hipStream_t s);
 
-// a8: FC2 over expert groups.
+// FC2 over expert groups.
 bool launch_fc2(int64_t rows_alloc, int H, int I, int E, const int32_t* offsets, Fp4Operand a,
                 Fp4Operand w2, uint16_t* o_out, hipStream_t s);
 
-// a9: y[t] = bf16(sum_j p[t,j] o[row_map[t,j]]).
+// Unpermute: y[t] = bf16(sum_j p[t,j] o[row_map[t,j]]).
 bool launch_unpermute(int64_t T, int H, int k, const uint16_t* o, const int32_t* row_map,
                       const float* topk_w, uint16_t* y, hipStream_t s);
 
-// b1: dO[r] = bf16(p dY[t]); pad rows zero.
+// dO gather-scale: dO[r] = bf16(p dY[t]); pad rows zero.
 bool launch_gather_scale(int64_t rows_alloc, int H, int k, const uint16_t* dy,
                          const int32_t* row_map, const int32_t* src_row, const float* topk_w,
                          const int32_t* offsets, int E, uint16_t* dO, hipStream_t s);
 
-// b2 + fused b4: dA = bf16(dO_e W2[e]) then the SwiGLU backward -> dH.
+// FC2 dgrad with the SwiGLU backward fused: dA = bf16(dO_e W2[e]) then the SwiGLU backward -> dH.
 bool launch_dgrad_fc2(int64_t rows_alloc, int H, int I, int E, const int32_t* offsets,
                       const uint16_t* dO, const uint16_t* w2, const uint16_t* h, uint16_t* dH,
                       hipStream_t s);
 
-// b5: dXp = bf16(dH_e W1[e]).
+// FC1 dgrad: dXp = bf16(dH_e W1[e]).
 bool launch_dgrad_fc1(int64_t rows_alloc, int H, int I, int E, const int32_t* offsets,
                       const uint16_t* dH, const uint16_t* w1, uint16_t* dXp, hipStream_t s);
 
-// b3: dW2[e] = bf16(dO_e^T a_e).   b6: dW1[e] = bf16(dH_e^T x[src_row]).
+// FC2 wgrad: dW2[e] = bf16(dO_e^T a_e).   FC1 wgrad: dW1[e] = bf16(dH_e^T x[src_row]).
 bool launch_wgrad_fc2(int H, int I, int E, const int32_t* offsets, const uint16_t* dO,
                       const uint16_t* a, uint16_t* dW2, hipStream_t s);
 bool launch_wgrad_fc1(int H, int I, int E, const int32_t* offsets, const uint16_t* dH,
@@ -83,7 +83,7 @@ bool launch_wgrad_fc1(int H, int I, int E, const int32_t* offsets, const uint16_
 bool launch_gather_rows(int64_t rows_alloc, int H, const uint16_t* x, const int32_t* src_row,
                         const int32_t* offsets, int E, uint16_t* xp, hipStream_t s);
 
-// b7: dX[t] = bf16(sum_j dXp[row_map[t,j]]).
+// dX gather-sum: dX[t] = bf16(sum_j dXp[row_map[t,j]]).
 bool launch_gather_sum(int64_t T, int H, int k, const uint16_t* dXp, const int32_t* row_map,
                        uint16_t* dx, hipStream_t s);
 

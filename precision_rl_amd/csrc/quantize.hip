@@ -1,4 +1,4 @@
-// Steps a1-a3 and a7 of the W4A4 MoE expert path on gfx950:
+// Routing and NVFP4 encoding kernels of the W4A4 MoE expert path on gfx950:
 //   route_count / route_scan  -- stable counting sort of (token, slot) entries
 //                                into expert-contiguous rows, offsets on device;
 //   quantize_scatter          -- per-token amax, two-level NVFP4 encoding and

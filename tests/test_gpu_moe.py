@@ -1,5 +1,5 @@
-"""GPU parity of the grouped expert forward (a5-a9) and the straight-through
-backward (b1-b7) against the FP64 oracle.
+"""GPU parity of the grouped expert forward and the straight-through
+BF16 backward against the FP64 oracle.
 
 Bars: FC1 pre-cast values rel-L2 <= 1e-5 (bit-exact on lossless inputs);
 <= 0.1 % of the requantised FC2-input codes differ; y rel-L2 <= 2e-3;

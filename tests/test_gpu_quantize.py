@@ -1,4 +1,4 @@
-"""GPU parity of steps a1-a3 (route, per-token amax, NVFP4 encode, scatter)
+"""GPU parity of quantize+permute (route, per-token amax, NVFP4 encode, scatter)
 and of the weight (identity-routing) quantisation: bit-exact against the
 FP64 oracle on the same seeded inputs."""
 import numpy as np

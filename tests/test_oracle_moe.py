@@ -191,7 +191,7 @@ def _dense_loss_grads(x, w1, w2, topk_idx, topk_w, dy):
 
 
 def test_backward_formulas_against_autograd():
-    """b1-b7 without bf16 roundings equal float64 autograd of the dense
+    """The backward steps without bf16 roundings equal float64 autograd of the dense
     (quantiser-free) MoE function: a textbook special case of the
     straight-through estimator with exact saved operands."""
     d, x, w1, w2 = _tiny(T=24, H=32, E=5, k=2, I=16, seed=9)
