@@ -23,14 +23,16 @@ struct TileCoord {
   bool valid;
 };
 
-// Maps blockIdx.x onto (expert, M tile, N tile) for a GEMM whose M dimension
-// is the concatenation of the expert row groups [offsets[e], offsets[e+1]).
+// Maps blockIdx.x onto (expert, M tile of TM rows, N tile) for a GEMM whose M
+// dimension is the concatenation of the expert row groups
+// [offsets[e], offsets[e+1]).
 // The number of tiles exists only on the device; wave 0 of every workgroup
 // recomputes it from the offsets (lane-local sums and a wave prefix scan) and
 // publishes the result through `slot` (LDS, 4 ints).  Logical tiles are
 // ordered expert-major, N fastest, and dealt out in contiguous runs per XCD
 // so that an expert's weight tiles and an M tile's activations stay in one
 // XCD's L2.  Contains one __syncthreads().
+template <int TM = kTileM>
 __device__ inline TileCoord grouped_m_tile(const int32_t* __restrict__ offsets, int E, int n_tiles,
                                            int* slot) {
   const int tid = threadIdx.x;
@@ -39,7 +41,7 @@ __device__ inline TileCoord grouped_m_tile(const int32_t* __restrict__ offsets, 
     const int per = (E + kWave - 1) / kWave;
     const int e0 = lane * per, e1 = min(E, e0 + per);
     int cnt = 0;
-    for (int e = e0; e < e1; ++e) cnt += (offsets[e + 1] - offsets[e] + kTileM - 1) / kTileM;
+    for (int e = e0; e < e1; ++e) cnt += (offsets[e + 1] - offsets[e] + TM - 1) / TM;
     int incl = cnt;
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) {
@@ -60,10 +62,10 @@ __device__ inline TileCoord grouped_m_tile(const int32_t* __restrict__ offsets, 
       if (mt >= incl - cnt && mt < incl) {   // exactly one lane owns tile mt
         int first = incl - cnt;
         for (int e = e0; e < e1; ++e) {
-          const int t = (offsets[e + 1] - offsets[e] + kTileM - 1) / kTileM;
+          const int t = (offsets[e + 1] - offsets[e] + TM - 1) / TM;
           if (mt < first + t) {
             slot[0] = e;
-            slot[1] = offsets[e] + (mt - first) * kTileM;
+            slot[1] = offsets[e] + (mt - first) * TM;
             slot[2] = offsets[e + 1];
             slot[3] = static_cast<int>(L % n_tiles);
             break;
@@ -74,19 +76,20 @@ __device__ inline TileCoord grouped_m_tile(const int32_t* __restrict__ offsets, 
     }
   }
   __syncthreads();
+  // the values are the same in every lane: keep them in scalar registers
   TileCoord tc;
-  tc.e = slot[0];
+  tc.e = __builtin_amdgcn_readfirstlane(slot[0]);
   tc.valid = tc.e >= 0;
-  tc.m0 = slot[1];
-  tc.m_end = slot[2];
-  tc.n_tile = slot[3];
+  tc.m0 = __builtin_amdgcn_readfirstlane(slot[1]);
+  tc.m_end = __builtin_amdgcn_readfirstlane(slot[2]);
+  tc.n_tile = __builtin_amdgcn_readfirstlane(slot[3]);
   return tc;
 }
 
 // Upper bound of the M-tile count for a grouped GEMM: every expert adds at
 // most one partial tile.
-inline int64_t grouped_m_tiles_bound(int64_t rows_alloc, int E) {
-  return (rows_alloc + kTileM - 1) / kTileM + E;
+inline int64_t grouped_m_tiles_bound(int64_t rows_alloc, int E, int tm = kTileM) {
+  return (rows_alloc + tm - 1) / tm + E;
 }
 
 inline unsigned xcd_grid(int64_t tiles) {
@@ -127,6 +130,18 @@ __device__ __forceinline__ void dma16(const void* g, const void* lds_base) {
 __device__ __forceinline__ void dma4(const void* g, const void* lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
                ::"v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_base))) : "memory", "m0");
+}
+// Same copies addressed as a wave-uniform base (SGPR pair) plus a 32-bit
+// per-lane byte offset, which saves the per-lane 64-bit address registers.
+__device__ __forceinline__ void dma16_off(const void* base, uint32_t off, const void* lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               ::"v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_base)))
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_off(const void* base, uint32_t off, const void* lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+               ::"v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_base)))
+               : "memory", "m0");
 }
 #pragma clang diagnostic pop
 

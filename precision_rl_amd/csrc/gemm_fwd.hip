@@ -1,4 +1,4 @@
-// FC1 (with the SwiGLU in its epilogue) and FC2: grouped block-scaled GEMMs FC1 and FC2 on gfx950.
+// FC1 (with the SwiGLU in its epilogue) and FC2: grouped block-scaled GEMMs on gfx950.
 //
 // The pages' recipe (rainbus review, "core method"; AI summary, "Methodology in
 // Plain English") accumulates the block-scaled product U_e = MMA(X_e, W_e^T)
@@ -12,17 +12,22 @@
 // applies only the exponent of its scale operand, then one v_pk_mul_f16 by the
 // E4M3 block scale); decoded operands never touch memory.
 //
-// Tiling: 256 x 256 output tile per workgroup of 8 waves (4 x 2, 64 x 128 per
-// wave, two waves per SIMD), MFMA 32x32x16 f16.  Each pipeline stage covers 128
-// of K: packed codes (64 B per row) and block scales (8 B per row) of both
-// operands, copied global -> LDS by the hardware (no register staging) into a
-// 4-deep ring, three stages ahead of the MFMAs.  Code rows are stored with
-// their four 16-byte chunks XOR-swizzled by (row / 4) % 4, so fragment reads
-// of 16 consecutive rows hit 16 distinct bank groups.  Inside a stage,
-// lane half h (lanes 32-63) owns the stage's second 64 k of its row; A and B
-// use the same assignment, so every MFMA k slot pairs equal k indices (the
-// reduction runs in a permuted K order; FP32 rounding of the sum is covered by
-// the tolerance, and sums that are exact in FP32 are order independent).
+// Tiling: 128 x 256 output tile per workgroup of 4 waves (2 x 2, 64 x 128 per
+// wave), MFMA 32x32x16 f16, and two workgroups per CU (58 KB of LDS and at
+// most 256 registers per wave each), so that one workgroup's epilogue, tile
+// set-up and barrier waits overlap the other's MFMAs, and each SIMD holds two
+// waves whose operand decode interleaves with the other's matrix work.  The
+// 128-row tile also bounds the padding work of an expert's last, partial M
+// tile.  Each pipeline stage covers 64 of K: packed codes (32 B per row) and
+// block scales (4 B per row) of both operands, copied global -> LDS by the
+// hardware (no register staging) into a 4-deep ring, three stages ahead of
+// the MFMAs.  Code rows keep their two 16-byte chunks swapped on every other
+// group of 8 rows, so fragment reads of 16 consecutive rows hit 16 distinct
+// bank groups.  Inside a stage, lane half h (lanes 32-63) owns the stage's
+// second 32 k of its row; A and B use the same assignment, so every MFMA k
+// slot pairs equal k indices (the reduction runs in a permuted K order; FP32
+// rounding of the sum is covered by the tolerance, and sums that are exact in
+// FP32 are order independent).
 
 #include "gemm_common.h"
 #include "internal.h"
@@ -30,18 +35,28 @@
 namespace w4a4 {
 namespace {
 
-constexpr int kBK = 128;                     // K per stage
+constexpr int kThreads = 256;                // 4 waves, 2 (M) x 2 (N)
+constexpr int kBM = 128, kBN = 256;          // workgroup tile
+constexpr int kWM = 64, kWN = 128;           // wave tile
+constexpr int kBK = 64;                      // K per stage
 constexpr int kStages = 4;                   // LDS ring depth
 constexpr int kAhead = kStages - 1;          // stages in flight ahead of the MFMAs
-constexpr int kCodeRow = kBK / 2;            // 64 B of codes per row per stage
-constexpr int kScaleRow = kBK / 16;          // 8 scale bytes per row per stage
-constexpr int kCodes = kTileM * kCodeRow;    // 16 KB per operand per stage
-constexpr int kScales = kTileM * kScaleRow;  // 2 KB
-constexpr int kStageBytes = 2 * kCodes + 2 * kScales;
+constexpr int kCodeRow = kBK / 2;            // 32 B of codes per row per stage
+constexpr int kScaleRow = kBK / 16;          // 4 scale bytes per row per stage
+constexpr int kACodes = kBM * kCodeRow;      // 4 KB
+constexpr int kBCodes = kBN * kCodeRow;      // 8 KB
+// Scale rows of a stage, 4 B each: A rows 0..127, B rows 128..383, and 128
+// filler rows so that every wave issues the same two copies.
+constexpr int kScaleRows = 512;
+constexpr int kBScaleRow0 = kBM;
+constexpr int kScalesOffset = kACodes + kBCodes;
+constexpr int kStageBytes = kScalesOffset + kScaleRows * 4;     // 14 KB
 constexpr int kGxOffset = kStages * kStageBytes;
-constexpr int kSlotOffset = kGxOffset + kTileM * 4;
-constexpr int kLdsBytes = kSlotOffset + 16;
-constexpr int kDmaPerStage = 6;              // per wave: 2 + 2 code copies, 1 + 1 scale copies
+constexpr int kSlotOffset = kGxOffset + kBM * 4;
+constexpr int kLdsBytes = kSlotOffset + 16;                     // 57.9 KB: two workgroups per CU
+constexpr int kDmaPerStage = 5;              // per wave: 1 A-code, 2 B-code, 2 scale copies
+
+static_assert(2 * kLdsBytes <= 160 * 1024, "two workgroups per CU must fit in LDS");
 
 enum class FwdMode { FC1, FC2 };
 
@@ -66,13 +81,16 @@ template <FwdMode MODE>
 __device__ __forceinline__ int b_row_of(int p, int n_tile, int I) {
   const int wn = p >> 7, ni = (p >> 5) & 3, j = p & 31;
   if constexpr (MODE == FwdMode::FC2) {
-    return n_tile * kTileN + wn * 128 + 4 * j + ni;
+    return n_tile * kBN + wn * 128 + 4 * j + ni;
   } else {
     const int half = ni >> 1;
     const int i = n_tile * 128 + wn * 64 + 2 * j + (ni & 1);
     return half * I + i;
   }
 }
+
+// LDS position (in 16-byte chunks within the row) of logical code chunk c of row r.
+__device__ __forceinline__ int code_slot(int r, int c) { return c ^ ((r >> 3) & 1); }
 
 __device__ __forceinline__ half8_t decode8(uint32_t codes8, half2_t d2) {
   half2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes8, 1.0f, 0) * d2;
@@ -85,65 +103,76 @@ __device__ __forceinline__ half8_t decode8(uint32_t codes8, half2_t d2) {
   return r;
 }
 
-// Two of the four E4M3 scale bytes in `sc` (selected by HI) as f16 pairs.
-template <bool HI>
-__device__ __forceinline__ void scale_pairs(uint32_t sc, half2_t& d0, half2_t& d1) {
-  const half2_t v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, HI);
+// The lane's two E4M3 block scales of a stage (blocks 2h, 2h+1 of the row's
+// four) as f16 pairs (d, d).
+__device__ __forceinline__ void scale_pairs(uint32_t word, int hl, half2_t& d0, half2_t& d1) {
+  const half2_t v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word >> (16 * hl), 1.0f, false);
   d0 = half2_t{v[0], v[0]};
   d1 = half2_t{v[1], v[1]};
 }
 
 template <FwdMode MODE>
-__global__ void __launch_bounds__(kGemmThreads, 1)
+__global__ void __launch_bounds__(kThreads, 2)
 fwd_gemm_kernel(FwdArgs args) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave & 3, wn = wave >> 2;
+  const int wm = wave & 1, wn = wave >> 1;
   const int r32 = lane & 31, hl = lane >> 5;
 
-  const int n_tiles = MODE == FwdMode::FC1 ? args.I / 128 : args.N / kTileN;
-  TileCoord tc = grouped_m_tile(args.offsets, args.E, n_tiles,
-                                reinterpret_cast<int*>(lds + kSlotOffset));
+  const int n_tiles = MODE == FwdMode::FC1 ? args.I / 128 : args.N / kBN;
+  TileCoord tc = grouped_m_tile<kBM>(args.offsets, args.E, n_tiles,
+                                     reinterpret_cast<int*>(lds + kSlotOffset));
   if (!tc.valid) return;
 
   const int64_t K2 = args.K / 2, K16 = args.K / 16;
   const int64_t last_row = args.rows_alloc - 1;
-  // ---- per-lane sources of this wave's copies (rows past the allocation are
-  // clamped: they only feed accumulator rows that are never stored)
-  const uint8_t* wcodes = args.w.codes + static_cast<int64_t>(tc.e) * args.N * K2;
-  const uint8_t* wscales = args.w.scales + static_cast<int64_t>(tc.e) * args.N * K16;
-  const uint8_t* a_code_src[2];
-  const uint8_t* b_code_src[2];
+  // ---- this wave's copies.  Codes: a wave-uniform base (the tile's first
+  // row, resp. the expert's weights, advanced per stage) plus a small per-lane
+  // offset.  Rows past the allocation are clamped: they only feed accumulator
+  // rows that are never stored.
+  const uint8_t* a_codes = args.a.codes + tc.m0 * K2;
+  const uint8_t* w_codes = args.w.codes + static_cast<int64_t>(tc.e) * args.N * K2;
+  const uint8_t* w_scales = args.w.scales + static_cast<int64_t>(tc.e) * args.N * K16;
+  const int a_rows = static_cast<int>(min<int64_t>(kBM, last_row + 1 - tc.m0));   // >= 1
+  uint32_t a_code_off, b_code_off[2];
+  {
+    const int row = 32 * wave + (lane >> 1);                  // A row of this lane's copy
+    a_code_off = static_cast<uint32_t>(min(row, a_rows - 1) * K2 + code_slot(row, lane & 1) * 16);
+  }
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    const int j = 2 * wave + c;                      // 16-row block of this copy
-    const int row = 16 * j + (lane >> 2);
-    const int chunk = (lane & 3) ^ ((row >> 2) & 3); // logical chunk stored at lane's slot
-    a_code_src[c] = args.a.codes + min(tc.m0 + row, last_row) * K2 + chunk * 16;
-    b_code_src[c] = wcodes + static_cast<int64_t>(b_row_of<MODE>(row, tc.n_tile, args.I)) * K2 + chunk * 16;
+    const int row = 64 * wave + 32 * c + (lane >> 1);        // B row of this lane's copy
+    b_code_off[c] = static_cast<uint32_t>(b_row_of<MODE>(row, tc.n_tile, args.I) * K2 +
+                                          code_slot(row, lane & 1) * 16);
   }
-  const int srow = 32 * wave + (lane >> 1);           // scale row of this lane's dword copy
-  const uint8_t* a_scale_src = args.a.scales + min(tc.m0 + srow, last_row) * K16 + (lane & 1) * 4;
-  const uint8_t* b_scale_src =
-      wscales + static_cast<int64_t>(b_row_of<MODE>(srow, tc.n_tile, args.I)) * K16 + (lane & 1) * 4;
+  // Scales: one dword per scale row per stage, from A or B (per-lane pointer).
+  const uint8_t* scale_src[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int q = 128 * wave + 64 * c + lane;
+    if (q < kBScaleRow0) {
+      scale_src[c] = args.a.scales + (tc.m0 + min(q, a_rows - 1)) * K16;
+    } else if (q < kBScaleRow0 + kBN) {
+      scale_src[c] = w_scales + static_cast<int64_t>(b_row_of<MODE>(q - kBScaleRow0, tc.n_tile, args.I)) * K16;
+    } else {
+      scale_src[c] = args.a.scales + tc.m0 * K16;            // filler: a valid row, never read
+    }
+  }
   auto issue = [&](int kt) {
     uint8_t* st = lds + (kt % kStages) * kStageBytes;
-    const int64_t cb = static_cast<int64_t>(kt) * kCodeRow, sb = static_cast<int64_t>(kt) * kScaleRow;
+    const int cb = kt * kCodeRow;
+    dma16_off(a_codes + cb, a_code_off, st + wave * 1024);
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int j = 2 * wave + c;
-      dma16(a_code_src[c] + cb, st + j * 1024);
-      dma16(b_code_src[c] + cb, st + kCodes + j * 1024);
-    }
-    dma4(a_scale_src + sb, st + 2 * kCodes + wave * 256);
-    dma4(b_scale_src + sb, st + 2 * kCodes + kScales + wave * 256);
+    for (int c = 0; c < 2; ++c) dma16_off(w_codes + cb, b_code_off[c], st + kACodes + (2 * wave + c) * 1024);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) dma4(scale_src[c] + kt * kScaleRow, st + kScalesOffset + (2 * wave + c) * 256);
   };
 
   // outer scales of the tile's rows, read by the epilogue
   float* s_gx = reinterpret_cast<float*>(lds + kGxOffset);
-  if (tid < kTileM) s_gx[tid] = args.a.outer[min(tc.m0 + tid, last_row)];
+  if (tid < kBM) s_gx[tid] = args.a.outer[tc.m0 + min(tid, a_rows - 1)];
 
   floatx16_t acc[2][4];
 #pragma unroll
@@ -153,7 +182,7 @@ fwd_gemm_kernel(FwdArgs args) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
 
-  const int a_row0 = wm * kWaveM + r32, b_row0 = wn * kWaveN + r32;
+  const int a_row0 = wm * kWM + r32, b_row0 = wn * kWN + r32;
   const int nk = args.K / kBK;
   for (int s = 0; s < kAhead && s < nk; ++s) issue(s);
 
@@ -165,54 +194,38 @@ fwd_gemm_kernel(FwdArgs args) {
     else wait_vm_barrier<0>();
     if (kt + kAhead < nk) issue(kt + kAhead);   // refills the slot read in iteration kt-1
 
-    const uint8_t* sa = lds + (kt % kStages) * kStageBytes;
-    const uint8_t* sb = sa + kCodes;
-    const uint8_t* ssa = sa + 2 * kCodes;
-    const uint8_t* ssb = ssa + kScales;
-    uint32_t a_sc[2], b_sc[4];
+    const uint8_t* st = lds + (kt % kStages) * kStageBytes;
+    u32x4_t ac[2], bc[4];
+    uint32_t as[2], bs[4];
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
-      a_sc[f] = *reinterpret_cast<const uint32_t*>(ssa + (a_row0 + f * 32) * kScaleRow + hl * 4);
+    for (int f = 0; f < 2; ++f) {
+      const int r = a_row0 + f * 32;
+      ac[f] = *reinterpret_cast<const u32x4_t*>(st + r * kCodeRow + code_slot(r, hl) * 16);
+      as[f] = *reinterpret_cast<const uint32_t*>(st + kScalesOffset + r * 4);
+    }
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
-      b_sc[f] = *reinterpret_cast<const uint32_t*>(ssb + (b_row0 + f * 32) * kScaleRow + hl * 4);
+    for (int f = 0; f < 4; ++f) {
+      const int r = b_row0 + f * 32;
+      bc[f] = *reinterpret_cast<const u32x4_t*>(st + kACodes + r * kCodeRow + code_slot(r, hl) * 16);
+      bs[f] = *reinterpret_cast<const uint32_t*>(st + kScalesOffset + (kBScaleRow0 + r) * 4);
+    }
+    half2_t ad[2][2], bd[4][2];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      u32x4_t ac[2], bc[4];
+    for (int f = 0; f < 2; ++f) scale_pairs(as[f], hl, ad[f][0], ad[f][1]);
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        const int row = a_row0 + f * 32;
-        ac[f] = *reinterpret_cast<const u32x4_t*>(sa + row * kCodeRow + (((hl * 2 + hh) ^ ((row >> 2) & 3)) * 16));
-      }
+    for (int f = 0; f < 4; ++f) scale_pairs(bs[f], hl, bd[f][0], bd[f][1]);
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        const int row = b_row0 + f * 32;
-        bc[f] = *reinterpret_cast<const u32x4_t*>(sb + row * kCodeRow + (((hl * 2 + hh) ^ ((row >> 2) & 3)) * 16));
-      }
-      half2_t ad[2][2], bd[4][2];   // block scales of blocks 2hh, 2hh+1 as f16 pairs
+    for (int s4 = 0; s4 < 4; ++s4) {
+      half8_t af[2], bf[4];
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        if (hh == 0) scale_pairs<false>(a_sc[f], ad[f][0], ad[f][1]);
-        else scale_pairs<true>(a_sc[f], ad[f][0], ad[f][1]);
-      }
+      for (int f = 0; f < 2; ++f) af[f] = decode8(ac[f][s4], ad[f][s4 >> 1]);
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        if (hh == 0) scale_pairs<false>(b_sc[f], bd[f][0], bd[f][1]);
-        else scale_pairs<true>(b_sc[f], bd[f][0], bd[f][1]);
-      }
+      for (int f = 0; f < 4; ++f) bf[f] = decode8(bc[f][s4], bd[f][s4 >> 1]);
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        half8_t af[2], bf[4];
+      for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-        for (int f = 0; f < 2; ++f) af[f] = decode8(ac[f][s4], ad[f][s4 >> 1]);
-#pragma unroll
-        for (int f = 0; f < 4; ++f) bf[f] = decode8(bc[f][s4], bd[f][s4 >> 1]);
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < 4; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
-      }
+        for (int ni = 0; ni < 4; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
     }
   }
   __syncthreads();   // s_gx visible (written before the loop; every wave passed a barrier since)
@@ -220,7 +233,7 @@ fwd_gemm_kernel(FwdArgs args) {
   // ---------------------------------------------------------------- epilogue
   const float* wouter = args.w.outer + static_cast<int64_t>(tc.e) * args.N;
   if constexpr (MODE == FwdMode::FC2) {
-    const int n = tc.n_tile * kTileN + wn * kWaveN + 4 * r32;
+    const int n = tc.n_tile * kBN + wn * kWN + 4 * r32;
     float gw[4];
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) gw[ni] = wouter[n + ni];
@@ -228,7 +241,7 @@ fwd_gemm_kernel(FwdArgs args) {
     for (int mi = 0; mi < 2; ++mi) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int lrow = acc_row(wm * kWaveM, mi, v, hl);
+        const int lrow = acc_row(wm * kWM, mi, v, hl);
         const int64_t row = tc.m0 + lrow;
         if (row >= tc.m_end) continue;
         const float gx = s_gx[lrow];
@@ -250,7 +263,7 @@ fwd_gemm_kernel(FwdArgs args) {
     for (int mi = 0; mi < 2; ++mi) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int lrow = acc_row(wm * kWaveM, mi, v, hl);
+        const int lrow = acc_row(wm * kWM, mi, v, hl);
         const int64_t row = tc.m0 + lrow;
         if (row >= tc.m_end) continue;
         const float gx = s_gx[lrow];
@@ -288,11 +301,11 @@ bool launch_fwd(const FwdArgs& args, int n_tiles, const char* name, hipStream_t 
       reinterpret_cast<const void*>(&fwd_gemm_kernel<MODE>),
       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
   if (attr != hipSuccess) return launch_ok(name) && false;
-  const int64_t tiles = grouped_m_tiles_bound(args.rows_alloc, args.E) * n_tiles;
+  const int64_t tiles = grouped_m_tiles_bound(args.rows_alloc, args.E, kBM) * n_tiles;
   if (tiles == 0) return true;
   {
     ProfScope p(name, s);
-    fwd_gemm_kernel<MODE><<<dim3(xcd_grid(tiles)), dim3(kGemmThreads), kLdsBytes, s>>>(args);
+    fwd_gemm_kernel<MODE><<<dim3(xcd_grid(tiles)), dim3(kThreads), kLdsBytes, s>>>(args);
   }
   return launch_ok(name);
 }
@@ -308,7 +321,7 @@ bool launch_fc1(int64_t rows_alloc, int H, int I, int E, const int32_t* offsets,
 bool launch_fc2(int64_t rows_alloc, int H, int I, int E, const int32_t* offsets, Fp4Operand a,
                 Fp4Operand w2, uint16_t* o_out, hipStream_t s) {
   FwdArgs args{rows_alloc, I, H, I, E, offsets, a, w2, o_out, nullptr, nullptr};
-  return launch_fwd<FwdMode::FC2>(args, H / kTileN, "gemm_fc2", s);
+  return launch_fwd<FwdMode::FC2>(args, H / kBN, "gemm_fc2", s);
 }
 
 }  // namespace w4a4
