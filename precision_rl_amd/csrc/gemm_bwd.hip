@@ -10,15 +10,31 @@
 //     FC2 wgrad: dW2[e] = dO_e^T . a_e            M = H,  N = I
 //     FC1 wgrad: dW1[e] = dH_e^T . xp_e           M = 2I, N = H   (xp = x gathered by row)
 //
-// 256 x 256 output tile per workgroup, MFMA 32x32x16 bf16, FP32 accumulation.
-// K advances 32 per stage through a 4-deep LDS ring filled by the hardware's
-// global -> LDS copies three stages ahead of the MFMAs (no register staging).
-// Tiles that are K-contiguous in HBM (dO, dH rows in the dgrad) keep rows of
-// 64 B with their 16-byte chunks XOR-swizzled by (row / 4) % 4; tiles that are
-// contiguous along M or N in HBM (the weights in the dgrad, both wgrad
-// operands) are kept as [k][256] rows of 512 B, chunks swizzled by 4 (k % 4),
-// and read with ds_read_b64_tr_b16, which hands each lane four consecutive k
-// of its column.  Both layouts make every read cycle conflict-free.
+// MFMA 32x32x16 bf16, FP32 accumulation, waves of 64 x 128 (two per SIMD).
+// Operands go global -> LDS through the hardware's copies (no register
+// staging) into a ring a few stages ahead of the MFMAs.  Tiles that are
+// K-contiguous in HBM (dO, dH rows in the dgrad) keep rows of 64 B with their
+// 16-byte chunks XOR-swizzled by (row / 4) % 4; tiles that are contiguous
+// along M or N in HBM (the weights in the dgrad, both wgrad operands) are kept
+// as [k][columns] rows, chunks swizzled by 4 (k % 4), and read with
+// ds_read_b64_tr_b16, which hands each lane four consecutive k of its column.
+// Both layouts make every read cycle conflict-free.
+//
+// dgrad: 128 x 256 tiles, 4 waves, two workgroups per CU (72 KB of LDS each),
+// so that one workgroup's epilogue and waits overlap the other's MFMAs, and
+// an expert's partial last M tile costs at most 128 padded rows.  K advances
+// 32 per stage through a 3-deep ring.  The epilogue stages the bf16 tile in
+// the (then idle) ring and writes it, and reads the saved h of the SwiGLU
+// backward, with 16-byte row-contiguous accesses.
+//
+// wgrad: 256 x 256 tiles, 8 waves, one persistent workgroup per CU with a
+// 4-deep ring of 32 KB stages; at the end of a tile the copies of the next
+// tile's first stages are issued before the epilogue, which moves the bf16
+// tile in four 64-row rounds through a 32 KB staging area with 16-byte stores.
+// Both operands are streamed (K = the expert's rows), and the larger tile
+// halves the copy traffic per flop.
+
+#include <algorithm>
 
 #include "gemm_common.h"
 #include "internal.h"
@@ -27,28 +43,6 @@ namespace w4a4 {
 namespace {
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
-
-constexpr int kBK = 32;
-constexpr int kStages = 4;
-constexpr int kAhead = kStages - 1;
-constexpr int kTileBytes = kTileM * kBK * 2;       // 16 KB: one operand, one stage
-constexpr int kStageBytes = 2 * kTileBytes;
-constexpr int kRingBytes = kStages * kStageBytes;  // 128 KB
-constexpr int kSlotOffset = kRingBytes;
-constexpr int kLdsBytes = kSlotOffset + 16;
-constexpr int kCopiesPerStage = 2 * kTileBytes / 1024;  // 1 KB per wave-wide copy
-
-// Wave grid of a workgroup: WAVES_M x WAVES_N waves over the 256 x 256 tile.
-template <int WAVES_M, int WAVES_N>
-struct Grid {
-  static constexpr int kWaves = WAVES_M * WAVES_N;
-  static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kRows = kTileM / WAVES_M;   // per wave
-  static constexpr int kCols = kTileN / WAVES_N;
-  static constexpr int kMI = kRows / 32;
-  static constexpr int kNI = kCols / 32;
-  static constexpr int kCopies = kCopiesPerStage / kWaves;  // copies per wave per stage
-};
 
 __device__ __forceinline__ bf16x8_t join_bf16(short4_t lo, short4_t hi) {
   typedef short short8_t __attribute__((ext_vector_type(8)));
@@ -74,9 +68,8 @@ __device__ __forceinline__ int krow_frag_offset(int row, int ks, int hl) {
 // ---- [k][256] tile: 32 k-rows of 512 B, 16-byte chunk c of k-row k at slot
 // c ^ (4 (k & 3)).  Copy q (2 k-rows): lane i fills k-row 2 q + i / 32, slot
 // i % 32.
-__device__ __forceinline__ int kcol_src_chunk(int k, int lane) {
-  return (lane & 31) ^ (4 * (k & 3));
-}
+__device__ __forceinline__ int kcol_copy_k(int q, int lane) { return 2 * q + (lane >> 5); }
+__device__ __forceinline__ int kcol_src_chunk(int k, int lane) { return (lane & 31) ^ (4 * (k & 3)); }
 // Byte offset of the 8-byte piece lane l reads with ds_read_tr for the 32 x 16
 // MFMA operand block whose columns start at col0 (multiple of 32), for k block
 // ks (16 k) and half r (k +0..3 or +4..7).
@@ -87,22 +80,99 @@ __device__ __forceinline__ int kcol_frag_offset(int col0, int ks, int r, int lan
   return k * 512 + (((col >> 3) ^ (4 * (k & 3))) * 16) + (col & 7) * 2;
 }
 
-template <int MI, int NI>
-__device__ __forceinline__ void zero_acc(floatx16_t (&acc)[MI][NI]) {
+
+// ======================================================================= dgrad
+namespace dg {
+
+constexpr int kThreads = 256;                       // 4 waves, 2 (M) x 2 (N)
+constexpr int kBM = 128, kBN = 256;                 // workgroup tile
+constexpr int kWM = 64, kWN = 128;                  // wave tile
+constexpr int kMI = kWM / 32, kNI = kWN / 32;
+constexpr int kBK = 32;
+constexpr int kStages = 3;
+constexpr int kAhead = kStages - 1;
+constexpr int kABytes = kBM * kBK * 2;              // 8 KB: A, one stage
+constexpr int kBBytes = kBN * kBK * 2;              // 16 KB: B, one stage
+constexpr int kStageBytes = kABytes + kBBytes;
+constexpr int kRingBytes = kStages * kStageBytes;   // 72 KB
+constexpr int kACopies = kABytes / 1024 / 4;        // 1 KB copies per wave per stage
+constexpr int kBCopies = kBBytes / 1024 / 4;
+constexpr int kDmaPerStage = kACopies + kBCopies;
+// Epilogue staging of the bf16 tile: rows of 512 B padded to 528 B, so the
+// two lane halves of an accumulator write (rows 4 apart) hit different banks.
+constexpr int kOutPitch = kBN * 2 + 16;
+constexpr int kSlotOffset = kRingBytes;
+constexpr int kLdsBytes = kSlotOffset + 16;
+
+static_assert(kBM * kOutPitch <= kRingBytes, "output staging must fit in the ring");
+static_assert(2 * kLdsBytes <= 160 * 1024, "two workgroups per CU must fit in LDS");
+
+
+
+// ---- K-contiguous tile: kBM rows x 32 k, 64 B per row, chunk c of row r at
+// slot c ^ ((r >> 2) & 3).  Copy q (16 rows): lane i fills row 16 q + i / 4,
+// slot i % 4.
+__device__ __forceinline__ int krow_src_chunk(int row, int lane) {
+  return (lane & 3) ^ ((row >> 2) & 3);
+}
+__device__ __forceinline__ int krow_frag_offset(int row, int ks, int hl) {
+  return row * 64 + (((ks * 2 + hl) ^ ((row >> 2) & 3)) * 16);
+}
+
+// ---- [k][COLS] tile: 32 k-rows of 2 COLS bytes, 16-byte chunk c of k-row k
+// at slot c ^ (4 (k & 3)).  Copy q (1 KB): lane i fills k-row
+// (64 / chunks) q + i / chunks, slot i % chunks, with chunks = COLS / 8.
+template <int COLS>
+struct KCol {
+  static constexpr int kChunks = COLS / 8;     // 16-byte chunks per k-row
+  static constexpr int kRowBytes = COLS * 2;
+  static constexpr int kRowsPerCopy = 64 / kChunks;
+  __device__ static int copy_k(int q, int lane) { return kRowsPerCopy * q + lane / kChunks; }
+  __device__ static int src_chunk(int k, int lane) { return (lane % kChunks) ^ (4 * (k & 3)); }
+  // Byte offset of the 8-byte piece lane l reads with ds_read_tr for the
+  // 32 x 16 MFMA operand block whose columns start at col0 (multiple of 32),
+  // for k block ks (16 k) and half r (k +0..3 or +4..7).
+  __device__ static int frag_offset(int col0, int ks, int r, int lane) {
+    const int g = lane >> 4, j = lane & 15;
+    const int k = ks * 16 + 8 * (g >> 1) + 4 * r + (j >> 2);
+    const int col = col0 + 16 * (g & 1) + 4 * (j & 3);
+    return k * kRowBytes + (((col >> 3) ^ (4 * (k & 3))) * 16) + (col & 7) * 2;
+  }
+};
+
+__device__ __forceinline__ void zero_acc(floatx16_t (&acc)[kMI][kNI]) {
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
+  for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < NI; ++ni)
+    for (int ni = 0; ni < kNI; ++ni)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
 }
 
-template <int N>
+// Waits for stage kt: later = stages issued after it (0 or 1).
 __device__ __forceinline__ void wait_stage(int later) {
-  // later = stages issued after the one being waited for (0 .. kAhead-1)
-  if (later >= 2) wait_vm_barrier<2 * N>();
-  else if (later == 1) wait_vm_barrier<N>();
+  if (later >= 1) wait_vm_barrier<kDmaPerStage>();
   else wait_vm_barrier<0>();
+}
+
+// Writes the wave's accumulators as bf16 into the staging tile (row-major,
+// kOutPitch bytes per row); the caller synchronises around it.
+__device__ __forceinline__ void stage_out(uint8_t* out_lds, const floatx16_t (&acc)[kMI][kNI],
+                                          int wrow, int wcol, int r32, int hl) {
+#pragma unroll
+  for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        *reinterpret_cast<uint16_t*>(out_lds + acc_row(wrow, mi, v, hl) * kOutPitch +
+                                     (wcol + ni * 32 + r32) * 2) = f32_to_bf16(acc[mi][ni][v]);
+}
+
+// All waves are past their last LDS read of the ring and every copy has
+// landed (the last stage waits for vmcnt 0): the ring may be overwritten.
+__device__ __forceinline__ void ring_idle_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // ------------------------------------------------------------------ dgrad
@@ -118,122 +188,210 @@ struct DgradArgs {
   uint16_t* out;       // dH [rows, 2I] or dXp [rows, H]
 };
 
-template <DgradMode MODE, class G>
-__global__ void __launch_bounds__(G::kThreads, 1)
+using BCol = KCol<kBN>;
+
+template <DgradMode MODE>
+__global__ void __launch_bounds__(kThreads, 2)
 dgrad_kernel(DgradArgs args) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wrow = (wave % (kTileM / G::kRows)) * G::kRows;
-  const int wcol = (wave / (kTileM / G::kRows)) * G::kCols;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wrow = (wave & 1) * kWM, wcol = (wave >> 1) * kWN;
   const int r32 = lane & 31, hl = lane >> 5;
-  const int n_tiles = (args.N + kTileN - 1) / kTileN;
-  TileCoord tc = grouped_m_tile(args.offsets, args.E, n_tiles, reinterpret_cast<int*>(lds + kSlotOffset));
+  const int n_tiles = (args.N + kBN - 1) / kBN;
+  TileCoord tc = grouped_m_tile<kBM>(args.offsets, args.E, n_tiles,
+                                     reinterpret_cast<int*>(lds + kSlotOffset));
   if (!tc.valid) return;
-  const int n0 = tc.n_tile * kTileN;
-  const int64_t last_row = args.rows_alloc - 1;
+  const int n0 = tc.n_tile * kBN;
+  const int a_rows = static_cast<int>(min<int64_t>(kBM, args.rows_alloc - tc.m0));   // >= 1
 
-  // ---- copy sources: A = rows of dO / dH (K-contiguous), B = W[e] as [K][N]
-  const uint8_t* a_src[G::kCopies / 2];
-  const uint8_t* b_src[G::kCopies / 2];
-  const uint16_t* we = args.w + static_cast<int64_t>(tc.e) * args.K * args.N;
+  // ---- copies.  A = rows of dO / dH (K-contiguous): scalar base at the
+  // tile's first row plus a lane offset; rows past the allocation are clamped
+  // (they only feed accumulator rows that are never stored).  B = W[e] as
+  // [K][N]: columns past N are clamped (never stored either).
+  const uint8_t* a_base = reinterpret_cast<const uint8_t*>(args.g + tc.m0 * args.K);
+  const uint8_t* b_base = reinterpret_cast<const uint8_t*>(args.w + static_cast<int64_t>(tc.e) * args.K * args.N);
+  uint32_t a_off_src[kACopies], b_off_src[kBCopies];
 #pragma unroll
-  for (int c = 0; c < G::kCopies / 2; ++c) {
-    const int q = wave * (G::kCopies / 2) + c;
-    const int row = 16 * q + (lane >> 2);
-    a_src[c] = reinterpret_cast<const uint8_t*>(args.g + min(tc.m0 + row, last_row) * args.K) +
-               krow_src_chunk(row, lane) * 16;
-    const int k = 2 * q + (lane >> 5);
-    int col = n0 + kcol_src_chunk(k, lane) * 8;
-    col = min(col, args.N - 8);   // columns past N only feed outputs never stored
-    b_src[c] = reinterpret_cast<const uint8_t*>(we + static_cast<int64_t>(k) * args.N + col);
+  for (int c = 0; c < kACopies; ++c) {
+    const int row = 16 * (kACopies * wave + c) + (lane >> 2);
+    a_off_src[c] = static_cast<uint32_t>((min(row, a_rows - 1) * args.K + krow_src_chunk(row, lane) * 8) * 2);
   }
-  const int64_t a_step = kBK * 2, b_step = static_cast<int64_t>(kBK) * args.N * 2;  // bytes per stage
-  auto issue = [&](int kt) {
-    uint8_t* st = lds + (kt % kStages) * kStageBytes;
 #pragma unroll
-    for (int c = 0; c < G::kCopies / 2; ++c) {
-      const int q = wave * (G::kCopies / 2) + c;
-      dma16(a_src[c] + kt * a_step, st + q * 1024);
-      dma16(b_src[c] + kt * b_step, st + kTileBytes + q * 1024);
-    }
+  for (int c = 0; c < kBCopies; ++c) {
+    const int k = BCol::copy_k(kBCopies * wave + c, lane);
+    const int col = min(n0 + BCol::src_chunk(k, lane) * 8, args.N - 8);
+    b_off_src[c] = static_cast<uint32_t>((k * args.N + col) * 2);
+  }
+  const int a_step = kBK * 2, b_step = kBK * args.N * 2;   // bytes per stage
+  const uint32_t lds0 = lds_addr(lds);
+  auto issue = [&](int kt) {
+    const uint32_t st = lds0 + (kt % kStages) * kStageBytes;
+#pragma unroll
+    for (int c = 0; c < kACopies; ++c)
+      dma16_off(a_base + static_cast<int64_t>(kt) * a_step, a_off_src[c], st + (kACopies * wave + c) * 1024);
+#pragma unroll
+    for (int c = 0; c < kBCopies; ++c)
+      dma16_off(b_base + static_cast<int64_t>(kt) * b_step, b_off_src[c],
+                st + kABytes + (kBCopies * wave + c) * 1024);
   };
 
   // ---- fragment addresses (within a stage)
-  int a_off[G::kMI][2], b_off[G::kNI][2][2];
+  int a_off[kMI][2], b_off[kNI][2][2];
 #pragma unroll
-  for (int f = 0; f < G::kMI; ++f)
+  for (int f = 0; f < kMI; ++f)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) a_off[f][ks] = krow_frag_offset(wrow + f * 32 + r32, ks, hl);
 #pragma unroll
-  for (int f = 0; f < G::kNI; ++f)
+  for (int f = 0; f < kNI; ++f)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int r = 0; r < 2; ++r) b_off[f][ks][r] = kTileBytes + kcol_frag_offset(wcol + f * 32, ks, r, lane);
+      for (int r = 0; r < 2; ++r) b_off[f][ks][r] = kABytes + BCol::frag_offset(wcol + f * 32, ks, r, lane);
 
-  floatx16_t acc[G::kMI][G::kNI];
+  floatx16_t acc[kMI][kNI];
   zero_acc(acc);
   const int nk = args.K / kBK;
   for (int s = 0; s < kAhead && s < nk; ++s) issue(s);
   for (int kt = 0; kt < nk; ++kt) {
-    wait_stage<G::kCopies>(min(kAhead - 1, nk - 1 - kt));
+    wait_stage(min(kAhead - 1, nk - 1 - kt));
     if (kt + kAhead < nk) issue(kt + kAhead);
     const uint8_t* st = lds + (kt % kStages) * kStageBytes;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      bf16x8_t af[G::kMI], bf[G::kNI];
+      bf16x8_t af[kMI], bf[kNI];
 #pragma unroll
-      for (int f = 0; f < G::kMI; ++f) af[f] = *reinterpret_cast<const bf16x8_t*>(st + a_off[f][ks]);
+      for (int f = 0; f < kMI; ++f) af[f] = *reinterpret_cast<const bf16x8_t*>(st + a_off[f][ks]);
 #pragma unroll
-      for (int f = 0; f < G::kNI; ++f)
+      for (int f = 0; f < kNI; ++f)
         bf[f] = join_bf16(ds_read_tr(st + b_off[f][ks][0]), ds_read_tr(st + b_off[f][ks][1]));
 #pragma unroll
-      for (int mi = 0; mi < G::kMI; ++mi)
+      for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < G::kNI; ++ni)
+        for (int ni = 0; ni < kNI; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
     }
   }
 
-  // ---- epilogue: lane (r32, hl) holds column wcol + 32 ni + r32 of 16 rows per mi
+  ring_idle_barrier();
+  stage_out(lds, acc, wrow, wcol, r32, hl);
+  __syncthreads();
+  const int rows = static_cast<int>(min<int64_t>(kBM, tc.m_end - tc.m0));
+  constexpr int kChunksPerRow = kBN / 8;
+  for (int c = tid; c < kBM * kChunksPerRow; c += kThreads) {
+    const int lrow = c / kChunksPerRow, n = n0 + (c % kChunksPerRow) * 8;
+    if (lrow >= rows || n >= args.N) continue;
+    const int64_t row = tc.m0 + lrow;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(lds + lrow * kOutPitch + (n - n0) * 2);
+    if constexpr (MODE == DgradMode::FC1) {
+      *reinterpret_cast<u32x4_t*>(args.out + row * args.N + n) = v;
+    } else {
+      // SwiGLU backward on bf16 dA, gate / up from the saved bf16 h
+      const int I = args.I;
+      const u32x4_t hg = *reinterpret_cast<const u32x4_t*>(args.h + row * (2 * I) + n);
+      const u32x4_t hu = *reinterpret_cast<const u32x4_t*>(args.h + row * (2 * I) + I + n);
+      u32x4_t dg, du;
 #pragma unroll
-  for (int mi = 0; mi < G::kMI; ++mi) {
-    if (tc.m0 + wrow + mi * 32 >= tc.m_end) continue;
+      for (int d = 0; d < 4; ++d) {
+        float rg[2], ru[2];
 #pragma unroll
-    for (int ni = 0; ni < G::kNI; ++ni) {
-      const int n = n0 + wcol + ni * 32 + r32;
-      if (n >= args.N) continue;
-      if constexpr (MODE == DgradMode::FC1) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int64_t row = tc.m0 + acc_row(wrow, mi, v, hl);
-          if (row < tc.m_end) args.out[row * args.N + n] = f32_to_bf16(acc[mi][ni][v]);
-        }
-      } else {
-        // SwiGLU backward on bf16 dA, gate / up from the saved bf16 h
-        const int I = args.I;
-        uint16_t hg[16], hu[16];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          int64_t row = tc.m0 + acc_row(wrow, mi, v, hl);
-          if (row >= tc.m_end) row = tc.m_end - 1;   // clamped: value unused
-          hg[v] = args.h[row * (2 * I) + n];
-          hu[v] = args.h[row * (2 * I) + I + n];
-        }
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int64_t row = tc.m0 + acc_row(wrow, mi, v, hl);
-          if (row >= tc.m_end) continue;
-          const float da = bf16_to_f32(f32_to_bf16(acc[mi][ni][v]));
-          const float gt = bf16_to_f32(hg[v]), up = bf16_to_f32(hu[v]);
+        for (int p = 0; p < 2; ++p) {
+          const float da = bf16_to_f32(static_cast<uint16_t>(v[d] >> (16 * p)));
+          const float gt = bf16_to_f32(static_cast<uint16_t>(hg[d] >> (16 * p)));
+          const float up = bf16_to_f32(static_cast<uint16_t>(hu[d] >> (16 * p)));
           const float sg = 1.0f / (1.0f + expf(-gt));
-          args.out[row * (2 * I) + n] = f32_to_bf16(da * up * sg * (1.0f + gt * (1.0f - sg)));
-          args.out[row * (2 * I) + I + n] = f32_to_bf16(da * gt * sg);
+          rg[p] = da * up * sg * (1.0f + gt * (1.0f - sg));
+          ru[p] = da * gt * sg;
         }
+        dg[d] = pack_bf16x2(rg[0], rg[1]);
+        du[d] = pack_bf16x2(ru[0], ru[1]);
       }
+      *reinterpret_cast<u32x4_t*>(args.out + row * (2 * I) + n) = dg;
+      *reinterpret_cast<u32x4_t*>(args.out + row * (2 * I) + I + n) = du;
     }
   }
 }
+
+}  // namespace dg
+
+// ======================================================================= wgrad
+namespace wg {
+
+constexpr int kThreads = 512;                       // 8 waves, 4 (M) x 2 (N)
+constexpr int kBM = 256, kBN = 256;                 // workgroup tile
+constexpr int kWM = 64, kWN = 128;                  // wave tile
+constexpr int kMI = kWM / 32, kNI = kWN / 32;
+constexpr int kBK = 32;
+constexpr int kStages = 4;
+constexpr int kAhead = kStages - 1;
+constexpr int kABytes = kBM * kBK * 2;              // 16 KB: A, one stage
+constexpr int kBBytes = kBN * kBK * 2;              // 16 KB: B, one stage
+constexpr int kStageBytes = kABytes + kBBytes;
+constexpr int kRingBytes = kStages * kStageBytes;   // 128 KB
+constexpr int kACopies = kABytes / 1024 / 8;        // 1 KB copies per wave per stage
+constexpr int kBCopies = kBBytes / 1024 / 8;
+constexpr int kDmaPerStage = kACopies + kBCopies;
+// Epilogue staging: 64 rows of 512 B, 16-byte chunks of rows with bit 2 set
+// swapped by 4 so that the two lane halves of an accumulator write (rows 4
+// apart) land in different banks.
+constexpr int kRoundRows = 64;
+constexpr int kRowBytes = kBN * 2;
+constexpr int kOutOffset = kRingBytes;
+constexpr int kLdsBytes = kOutOffset + kRoundRows * kRowBytes;   // 160 KB: one workgroup per CU
+// The next tile's coordinates are published through ring slot 3, which holds
+// no data between the end of a tile's last stage and the first copy of the
+// next tile's stage 3.
+constexpr int kSlotOffset = (kStages - 1) * kStageBytes;
+
+static_assert(kLdsBytes <= 160 * 1024, "LDS of one workgroup");
+
+__device__ __forceinline__ void zero_acc(floatx16_t (&acc)[kMI][kNI]) {
+#pragma unroll
+  for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
+}
+
+// Waits for stage kt: later = stages issued after it (0 .. kAhead-1).
+__device__ __forceinline__ void wait_stage(int later) {
+  if (later >= 2) wait_vm_barrier<2 * kDmaPerStage>();
+  else if (later == 1) wait_vm_barrier<kDmaPerStage>();
+  else wait_vm_barrier<0>();
+}
+
+// All waves are past their last LDS read of the ring and every copy has
+// landed (the last stage waits for vmcnt 0): the ring may be overwritten.
+__device__ __forceinline__ void ring_idle_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Byte offset in the staging area of column col of staging row s.
+__device__ __forceinline__ int stage_offset(int s, int col) {
+  return s * kRowBytes + (((col >> 3) ^ (((s >> 2) & 1) * 4)) * 16) + (col & 7) * 2;
+}
+
+// Round q of the epilogue, first half: every wave writes its accumulator rows
+// [16 q, 16 q + 16) (wave-local) as bf16 into staging rows wm * 16 + 0..15.
+template <int Q>
+__device__ __forceinline__ void stage_round(uint8_t* so, const floatx16_t (&acc)[kMI][kNI], int wm,
+                                            int wcol, int r32, int hl) {
+  constexpr int mi = Q >> 1;
+#pragma unroll
+  for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+    for (int vl = 0; vl < 4; ++vl) {
+      const int v = 4 * (2 * (Q & 1) + vb) + vl;
+      const int s = wm * 16 + 8 * vb + 4 * hl + vl;
+#pragma unroll
+      for (int ni = 0; ni < kNI; ++ni)
+        *reinterpret_cast<uint16_t*>(so + stage_offset(s, wcol + ni * 32 + r32)) =
+            f32_to_bf16(acc[mi][ni][v]);
+    }
+}
+
+// Tile row held by staging row s in round q.
+__device__ __forceinline__ int round_tile_row(int s, int q) { return (s >> 4) * kWM + 16 * q + (s & 15); }
 
 // ------------------------------------------------------------------ wgrad
 struct WgradArgs {
@@ -244,140 +402,195 @@ struct WgradArgs {
   uint16_t* out;           // [E, M, N]
 };
 
-template <class G>
-__global__ void __launch_bounds__(G::kThreads, 1)
+struct WTile {
+  int e, m0, n0;
+  int64_t r_begin, r_end;
+  int nk;
+};
+
+__global__ void __launch_bounds__(kThreads, 1)
 wgrad_kernel(WgradArgs args) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wrow = (wave % (kTileM / G::kRows)) * G::kRows;
-  const int wcol = (wave / (kTileM / G::kRows)) * G::kCols;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 3;
+  const int wrow = wm * kWM, wcol = (wave >> 2) * kWN;
   const int r32 = lane & 31, hl = lane >> 5;
-  const int m_tiles = args.M / kTileM, n_tiles = (args.N + kTileN - 1) / kTileN;
+  const int m_tiles = args.M / kBM, n_tiles = (args.N + kBN - 1) / kBN;
   const int64_t total = static_cast<int64_t>(args.E) * m_tiles * n_tiles;
   const int64_t per_xcd = (total + kXcds - 1) / kXcds;
-  const int64_t y = blockIdx.x / kXcds, x = blockIdx.x % kXcds;
-  if (y >= per_xcd) return;
-  const int64_t L = x * per_xcd + y;
-  if (L >= total) return;
-  const int e = static_cast<int>(L / (m_tiles * n_tiles));
-  const int mt = static_cast<int>((L / n_tiles) % m_tiles);
-  const int nt = static_cast<int>(L % n_tiles);
-  const int m0 = mt * kTileM, n0 = nt * kTileN;
-  const int64_t r_begin = args.offsets[e], r_end = args.offsets[e + 1];
-  const int64_t nrows = r_end - r_begin;
-  const int nk = static_cast<int>((nrows + kBK - 1) / kBK);
+  // This workgroup's i-th tile (false: none left).  Logical tiles are
+  // expert-major, N fastest; XCD x owns a contiguous run of them.
+  auto tile = [&](int i, WTile& t) -> bool {
+    const int64_t y = blockIdx.x / kXcds + static_cast<int64_t>(i) * (gridDim.x / kXcds);
+    const int64_t L = (blockIdx.x % kXcds) * per_xcd + y;
+    if (!(y < per_xcd && L < total)) return false;
+    t.e = static_cast<int>(L / (m_tiles * n_tiles));
+    t.m0 = static_cast<int>((L / n_tiles) % m_tiles) * kBM;
+    t.n0 = static_cast<int>(L % n_tiles) * kBN;
+    t.r_begin = args.offsets[t.e];
+    t.r_end = args.offsets[t.e + 1];
+    t.nk = static_cast<int>((t.r_end - t.r_begin + kBK - 1) / kBK);
+    return true;
+  };
+  WTile tc;
+  if (!tile(0, tc)) return;
 
-  // ---- copy sources: both operands [k = row][256 columns]
-  int a_col[G::kCopies / 2], b_col[G::kCopies / 2], kk[G::kCopies / 2];
+  // ---- copies: both operands [k = row][256 columns]; rows past the expert's
+  // end are re-read from its last row and zeroed in LDS; columns past N are
+  // clamped (never stored)
+  int kk[kACopies], a_col[kACopies], b_col[kBCopies];
+  auto setup = [&](const WTile& t) {
 #pragma unroll
-  for (int c = 0; c < G::kCopies / 2; ++c) {
-    const int q = wave * (G::kCopies / 2) + c;
-    kk[c] = 2 * q + (lane >> 5);
-    a_col[c] = m0 + kcol_src_chunk(kk[c], lane) * 8;
-    b_col[c] = min(n0 + kcol_src_chunk(kk[c], lane) * 8, args.N - 8);  // past N: never stored
-  }
-  auto issue = [&](int kt) {
-    uint8_t* st = lds + (kt % kStages) * kStageBytes;
+    for (int c = 0; c < kACopies; ++c) {
+      kk[c] = kcol_copy_k(kACopies * wave + c, lane);
+      a_col[c] = t.m0 + kcol_src_chunk(kk[c], lane) * 8;
+      b_col[c] = min(t.n0 + kcol_src_chunk(kk[c], lane) * 8, args.N - 8);
+    }
+  };
+  static_assert(kACopies == kBCopies, "A and B copies share their k rows");
+  const uint32_t lds0 = lds_addr(lds);
+  auto issue = [&](const WTile& t, int kt) {
+    const uint32_t st = lds0 + (kt % kStages) * kStageBytes;
+    const int64_t r0 = t.r_begin + static_cast<int64_t>(kt) * kBK;
 #pragma unroll
-    for (int c = 0; c < G::kCopies / 2; ++c) {
-      const int q = wave * (G::kCopies / 2) + c;
-      // rows past the expert's end are re-read from its last row and zeroed in LDS
-      const int64_t r = min(r_begin + static_cast<int64_t>(kt) * kBK + kk[c], r_end - 1);
-      dma16(args.g + r * args.M + a_col[c], st + q * 1024);
-      dma16(args.s + r * args.N + b_col[c], st + kTileBytes + q * 1024);
+    for (int c = 0; c < kACopies; ++c) {
+      const int64_t r = min(r0 + kk[c], t.r_end - 1);
+      dma16(args.g + r * args.M + a_col[c], st + (kACopies * wave + c) * 1024);
+      dma16(args.s + r * args.N + b_col[c], st + kABytes + (kBCopies * wave + c) * 1024);
     }
   };
 
-  int a_off[G::kMI][2][2], b_off[G::kNI][2][2];
+  int a_off[kMI][2][2], b_off[kNI][2][2];
 #pragma unroll
-  for (int f = 0; f < G::kMI; ++f)
+  for (int f = 0; f < kMI; ++f)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int r = 0; r < 2; ++r) a_off[f][ks][r] = kcol_frag_offset(wrow + f * 32, ks, r, lane);
 #pragma unroll
-  for (int f = 0; f < G::kNI; ++f)
+  for (int f = 0; f < kNI; ++f)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int r = 0; r < 2; ++r) b_off[f][ks][r] = kTileBytes + kcol_frag_offset(wcol + f * 32, ks, r, lane);
+      for (int r = 0; r < 2; ++r) b_off[f][ks][r] = kABytes + kcol_frag_offset(wcol + f * 32, ks, r, lane);
 
-  floatx16_t acc[G::kMI][G::kNI];
-  zero_acc(acc);
-  const int tail = static_cast<int>(nrows - static_cast<int64_t>(nk - 1) * kBK);  // valid k of the last stage
-  for (int s = 0; s < kAhead && s < nk; ++s) issue(s);
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_stage<G::kCopies>(min(kAhead - 1, nk - 1 - kt));
-    uint8_t* st = lds + (kt % kStages) * kStageBytes;
-    if (kt == nk - 1 && tail < kBK) {
-      // every copy of the workgroup has landed (vmcnt 0 + barrier above): zero
-      // the k-rows past the expert's end in both operands, then sync again
-      for (int i = tid; i < (kBK - tail) * 64; i += G::kThreads) {
-        const int op = i / ((kBK - tail) * 32), rem = i % ((kBK - tail) * 32);
-        *reinterpret_cast<u32x4_t*>(st + op * kTileBytes + (tail + rem / 32) * 512 + (rem % 32) * 16) =
-            u32x4_t{0u, 0u, 0u, 0u};
+  setup(tc);
+  for (int s = 0; s < kAhead && s < tc.nk; ++s) issue(tc, s);
+  uint8_t* so = lds + kOutOffset;
+  for (int it = 1;; ++it) {
+    floatx16_t acc[kMI][kNI];
+    zero_acc(acc);
+    const int nk = tc.nk;
+    const int tail = static_cast<int>(tc.r_end - tc.r_begin - static_cast<int64_t>(nk - 1) * kBK);
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_stage(min(kAhead - 1, nk - 1 - kt));
+      uint8_t* st = lds + (kt % kStages) * kStageBytes;
+      if (kt == nk - 1 && tail < kBK) {
+        // every copy of the workgroup has landed (vmcnt 0 + barrier above): zero
+        // the k-rows past the expert's end in both operands, then sync again
+        for (int i = tid; i < (kBK - tail) * 64; i += kThreads) {
+          const int op = i / ((kBK - tail) * 32), rem = i % ((kBK - tail) * 32);
+          *reinterpret_cast<u32x4_t*>(st + op * kABytes + (tail + rem / 32) * 512 + (rem % 32) * 16) =
+              u32x4_t{0u, 0u, 0u, 0u};
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       }
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (kt + kAhead < nk) issue(tc, kt + kAhead);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        bf16x8_t af[kMI], bf[kNI];
+#pragma unroll
+        for (int f = 0; f < kMI; ++f)
+          af[f] = join_bf16(ds_read_tr(st + a_off[f][ks][0]), ds_read_tr(st + a_off[f][ks][1]));
+#pragma unroll
+        for (int f = 0; f < kNI; ++f)
+          bf[f] = join_bf16(ds_read_tr(st + b_off[f][ks][0]), ds_read_tr(st + b_off[f][ks][1]));
+#pragma unroll
+        for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < kNI; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
+      }
     }
-    if (kt + kAhead < nk) issue(kt + kAhead);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8_t af[G::kMI], bf[G::kNI];
-#pragma unroll
-      for (int f = 0; f < G::kMI; ++f)
-        af[f] = join_bf16(ds_read_tr(st + a_off[f][ks][0]), ds_read_tr(st + a_off[f][ks][1]));
-#pragma unroll
-      for (int f = 0; f < G::kNI; ++f)
-        bf[f] = join_bf16(ds_read_tr(st + b_off[f][ks][0]), ds_read_tr(st + b_off[f][ks][1]));
-#pragma unroll
-      for (int mi = 0; mi < G::kMI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < G::kNI; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
+
+    // ---- next tile's first stages, then the epilogue of this one
+    ring_idle_barrier();
+    WTile tn;
+    const bool more = tile(it, tn);
+    if (more) {
+      setup(tn);
+      for (int s = 0; s < kAhead && s < tn.nk; ++s) issue(tn, s);
     }
-  }
-  uint16_t* out = args.out + static_cast<int64_t>(e) * args.M * args.N;
+    uint16_t* out = args.out + static_cast<int64_t>(tc.e) * args.M * args.N;
 #pragma unroll
-  for (int ni = 0; ni < G::kNI; ++ni) {
-    const int n = n0 + wcol + ni * 32 + r32;
-    if (n >= args.N) continue;
+    for (int q = 0; q < 4; ++q) {
+      if (q == 0) stage_round<0>(so, acc, wm, wcol, r32, hl);
+      else if (q == 1) stage_round<1>(so, acc, wm, wcol, r32, hl);
+      else if (q == 2) stage_round<2>(so, acc, wm, wcol, r32, hl);
+      else stage_round<3>(so, acc, wm, wcol, r32, hl);
+      __syncthreads();
 #pragma unroll
-    for (int mi = 0; mi < G::kMI; ++mi)
-#pragma unroll
-      for (int v = 0; v < 16; ++v)
-        out[static_cast<int64_t>(m0 + acc_row(wrow, mi, v, hl)) * args.N + n] = f32_to_bf16(acc[mi][ni][v]);
+      for (int j = 0; j < kRoundRows * 32 / kThreads; ++j) {
+        const int c = tid + j * kThreads;
+        const int s = c >> 5, n = tc.n0 + (c & 31) * 8;
+        if (n >= args.N) continue;
+        *reinterpret_cast<u32x4_t*>(out + static_cast<int64_t>(tc.m0 + round_tile_row(s, q)) * args.N + n) =
+            *reinterpret_cast<const u32x4_t*>(so + stage_offset(s, n - tc.n0));
+      }
+      if (q < 3) __syncthreads();   // staging free for the next round
+    }
+    if (!more) break;
+    tc = tn;
   }
 }
 
-using BwdGrid = Grid<4, 2>;   // 8 waves, 64 x 128 per wave
+}  // namespace wg
+
+int cu_count() {
+  static const int n = [] {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    return cus;
+  }();
+  return n;
+}
+
+// Persistent grid: one workgroup per CU (a multiple of the XCD count), or
+// fewer when there are fewer tiles.
+unsigned persistent_grid(int64_t tiles) {
+  const int64_t cap = std::max<int64_t>(kXcds, cu_count() / kXcds * kXcds);
+  return xcd_grid(std::min<int64_t>(tiles, cap));
+}
 
 template <typename Kern>
-hipError_t set_lds(Kern k) {
+hipError_t set_lds(Kern k, int bytes) {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
-template <DgradMode MODE>
-bool launch_dgrad(const DgradArgs& a, const char* name, hipStream_t s) {
-  static const hipError_t attr = set_lds(&dgrad_kernel<MODE, BwdGrid>);
+template <dg::DgradMode MODE>
+bool launch_dgrad(const dg::DgradArgs& a, const char* name, hipStream_t s) {
+  static const hipError_t attr = set_lds(&dg::dgrad_kernel<MODE>, dg::kLdsBytes);
   if (attr != hipSuccess) return launch_ok(name) && false;
-  const int64_t tiles = grouped_m_tiles_bound(a.rows_alloc, a.E) * ((a.N + kTileN - 1) / kTileN);
+  const int64_t tiles = grouped_m_tiles_bound(a.rows_alloc, a.E, dg::kBM) * ((a.N + dg::kBN - 1) / dg::kBN);
   if (tiles == 0) return true;
   {
     ProfScope p(name, s);
-    dgrad_kernel<MODE, BwdGrid><<<dim3(xcd_grid(tiles)), dim3(BwdGrid::kThreads), kLdsBytes, s>>>(a);
+    dg::dgrad_kernel<MODE><<<dim3(xcd_grid(tiles)), dim3(dg::kThreads), dg::kLdsBytes, s>>>(a);
   }
   return launch_ok(name);
 }
 
-bool launch_wgrad(const WgradArgs& a, const char* name, hipStream_t s) {
-  static const hipError_t attr = set_lds(&wgrad_kernel<BwdGrid>);
+bool launch_wgrad(const wg::WgradArgs& a, const char* name, hipStream_t s) {
+  static const hipError_t attr = set_lds(&wg::wgrad_kernel, wg::kLdsBytes);
   if (attr != hipSuccess) return launch_ok(name) && false;
-  const int64_t tiles = static_cast<int64_t>(a.E) * (a.M / kTileM) * ((a.N + kTileN - 1) / kTileN);
+  const int64_t tiles = static_cast<int64_t>(a.E) * (a.M / wg::kBM) * ((a.N + wg::kBN - 1) / wg::kBN);
   if (tiles == 0) return true;
   {
     ProfScope p(name, s);
-    wgrad_kernel<BwdGrid><<<dim3(xcd_grid(tiles)), dim3(BwdGrid::kThreads), kLdsBytes, s>>>(a);
+    wg::wgrad_kernel<<<dim3(persistent_grid(tiles)), dim3(wg::kThreads), wg::kLdsBytes, s>>>(a);
   }
   return launch_ok(name);
 }
@@ -387,25 +600,25 @@ bool launch_wgrad(const WgradArgs& a, const char* name, hipStream_t s) {
 bool launch_dgrad_fc2(int64_t rows_alloc, int H, int I, int E, const int32_t* offsets,
                       const uint16_t* dO, const uint16_t* w2, const uint16_t* h, uint16_t* dH,
                       hipStream_t s) {
-  DgradArgs a{rows_alloc, H, I, I, E, offsets, dO, w2, h, dH};
-  return launch_dgrad<DgradMode::FC2_SWIGLU>(a, "gemm_dgrad_fc2", s);
+  dg::DgradArgs a{rows_alloc, H, I, I, E, offsets, dO, w2, h, dH};
+  return launch_dgrad<dg::DgradMode::FC2_SWIGLU>(a, "gemm_dgrad_fc2", s);
 }
 
 bool launch_dgrad_fc1(int64_t rows_alloc, int H, int I, int E, const int32_t* offsets,
                       const uint16_t* dH, const uint16_t* w1, uint16_t* dXp, hipStream_t s) {
-  DgradArgs a{rows_alloc, 2 * I, H, I, E, offsets, dH, w1, nullptr, dXp};
-  return launch_dgrad<DgradMode::FC1>(a, "gemm_dgrad_fc1", s);
+  dg::DgradArgs a{rows_alloc, 2 * I, H, I, E, offsets, dH, w1, nullptr, dXp};
+  return launch_dgrad<dg::DgradMode::FC1>(a, "gemm_dgrad_fc1", s);
 }
 
 bool launch_wgrad_fc2(int H, int I, int E, const int32_t* offsets, const uint16_t* dO,
                       const uint16_t* a, uint16_t* dW2, hipStream_t s) {
-  WgradArgs w{H, I, E, offsets, dO, a, dW2};
+  wg::WgradArgs w{H, I, E, offsets, dO, a, dW2};
   return launch_wgrad(w, "gemm_wgrad_fc2", s);
 }
 
 bool launch_wgrad_fc1(int H, int I, int E, const int32_t* offsets, const uint16_t* dH,
                       const uint16_t* xp, uint16_t* dW1, hipStream_t s) {
-  WgradArgs w{2 * I, H, E, offsets, dH, xp, dW1};
+  wg::WgradArgs w{2 * I, H, E, offsets, dH, xp, dW1};
   return launch_wgrad(w, "gemm_wgrad_fc1", s);
 }
 

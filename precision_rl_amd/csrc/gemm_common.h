@@ -110,37 +110,44 @@ constexpr int waitcnt_vm(int vm) {
 }
 
 // Asynchronous copy global -> LDS (global_load_lds_dwordx4 / _dword): lane
-// i's 16 bytes (4 bytes) land at lds_base + 16 i (4 i); lds_base must be
-// wave-uniform.  The copy counts on this wave's vector-memory counter and has
-// landed once wait_vm_barrier<> allows fewer outstanding operations than were
-// issued after it.  Issued from inline assembly so that the compiler's
-// dependency tracking does not treat every later LDS read as aliasing the
-// in-flight copies (it would wait for all of them); the kernels order LDS
-// reads after copies explicitly.  M0 (the copy's LDS base) is not used for
-// anything else in these kernels.
+// i's 16 bytes (4 bytes) land at LDS byte address lds + 16 i (4 i); `lds` is
+// wave-uniform (it is moved to M0).  The copy counts on this wave's
+// vector-memory counter and has landed once wait_vm_barrier<> allows fewer
+// outstanding operations than were issued after it.  Issued from inline
+// assembly so that the compiler's dependency tracking does not treat every
+// later LDS read as aliasing the in-flight copies (it would wait for all of
+// them); the kernels order LDS reads after copies explicitly.  M0 (the copy's
+// LDS base) is not used for anything else in these kernels.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));   // low half of the flat address
 }
+// A pointer that is the same in every lane, moved to scalar registers.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"   // M0 is reserved; nothing else here uses it
-__device__ __forceinline__ void dma16(const void* g, const void* lds_base) {
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               ::"v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_base))) : "memory", "m0");
+               ::"v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(const void* g, const void* lds_base) {
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
-               ::"v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_base))) : "memory", "m0");
+               ::"v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
 }
 // Same copies addressed as a wave-uniform base (SGPR pair) plus a 32-bit
 // per-lane byte offset, which saves the per-lane 64-bit address registers.
-__device__ __forceinline__ void dma16_off(const void* base, uint32_t off, const void* lds_base) {
+__device__ __forceinline__ void dma16_off(const void* base, uint32_t off, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               ::"v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_base)))
+               ::"v"(off), "s"(uniform_ptr(base)), "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory", "m0");
 }
-__device__ __forceinline__ void dma4_off(const void* base, uint32_t off, const void* lds_base) {
+__device__ __forceinline__ void dma4_off(const void* base, uint32_t off, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
-               ::"v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_base)))
+               ::"v"(off), "s"(uniform_ptr(base)), "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory", "m0");
 }
 #pragma clang diagnostic pop

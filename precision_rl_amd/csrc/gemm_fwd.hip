@@ -117,7 +117,7 @@ fwd_gemm_kernel(FwdArgs args) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
   const int r32 = lane & 31, hl = lane >> 5;
 
@@ -160,8 +160,9 @@ fwd_gemm_kernel(FwdArgs args) {
       scale_src[c] = args.a.scales + tc.m0 * K16;            // filler: a valid row, never read
     }
   }
+  const uint32_t lds0 = lds_addr(lds);
   auto issue = [&](int kt) {
-    uint8_t* st = lds + (kt % kStages) * kStageBytes;
+    const uint32_t st = lds0 + (kt % kStages) * kStageBytes;
     const int cb = kt * kCodeRow;
     dma16_off(a_codes + cb, a_code_off, st + wave * 1024);
 #pragma unroll
