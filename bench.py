@@ -36,8 +36,8 @@ KERNEL_SOURCES = {
     "gemm_dgrad_fc1": "gemm_bwd.hip", "gemm_dgrad_fc2": "gemm_bwd.hip",
     "gemm_wgrad_fc1": "gemm_bwd.hip", "gemm_wgrad_fc2": "gemm_bwd.hip",
     "quantize_scatter": "quantize.hip", "requant": "quantize.hip",
-    "unpermute": "elementwise.hip", "do_gather_scale": "elementwise.hip",
-    "dx_gather_sum": "elementwise.hip", "x_gather_rows": "elementwise.hip",
+    "unpermute": "elementwise.hip", "dy_x_scatter": "elementwise.hip",
+    "dx_gather_sum": "elementwise.hip",
 }
 
 
@@ -58,10 +58,9 @@ def algorithmic_work(T, H, E, k, I):
         "quantize_scatter": T * (H * 2 + k * 4) + M * (H // 2 + H // 16 + 4) + T * k * 4 + M * 4,
         "requant": M * (I * 2 + I // 2 + I // 16 + 4),
         "unpermute": T * (k * H * 2 + k * 8 + H * 2),
-        "do_gather_scale": T * (H * 2 + k * 8) + M * H * 2,
+        # read dY[t], x[t] and the token's k maps / weights; write k rows of dO and of xp
+        "dy_x_scatter": T * (2 * H * 2 + k * 8) + 2 * M * H * 2,
         "dx_gather_sum": T * (k * H * 2 + k * 4 + H * 2),
-        # read each token once (the k copies come from cache), src_row; write M rows
-        "x_gather_rows": T * H * 2 + M * 4 + M * H * 2,
     }
     return fl, by
 

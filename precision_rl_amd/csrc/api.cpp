@@ -299,18 +299,15 @@ w4a4_status w4a4_expert_bwd(int64_t T, int H, int I, int E, int k, int row_align
   const uint16_t* W1 = static_cast<const uint16_t*>(w1);
   const uint16_t* W2 = static_cast<const uint16_t*>(w2);
 
-  if (cap > 0) {
-    if (!launch_gather_scale(cap, H, k, static_cast<const uint16_t*>(dy), row_map, src_row, topk_w,
-                             expert_offsets, E, dO, s))
-      return W4A4_ERR_LAUNCH;
-    if (!launch_dgrad_fc2(cap, H, I, E, expert_offsets, dO, W2, h, dH, s)) return W4A4_ERR_LAUNCH;
-  }
+  if (!launch_scatter(T, H, k, static_cast<const uint16_t*>(dy), static_cast<const uint16_t*>(x), row_map,
+                      topk_w, dO, xp, s))
+    return W4A4_ERR_LAUNCH;
+  if (row_align > 1 && !launch_zero_pad_rows(cap, H, src_row, expert_offsets, E, dO, xp, s))
+    return W4A4_ERR_LAUNCH;
+  if (cap > 0 && !launch_dgrad_fc2(cap, H, I, E, expert_offsets, dO, W2, h, dH, s)) return W4A4_ERR_LAUNCH;
   if (!launch_wgrad_fc2(H, I, E, expert_offsets, dO, a, static_cast<uint16_t*>(dw2), s))
     return W4A4_ERR_LAUNCH;
   if (cap > 0 && !launch_dgrad_fc1(cap, H, I, E, expert_offsets, dH, W1, dXp, s))
-    return W4A4_ERR_LAUNCH;
-  if (cap > 0 && !launch_gather_rows(cap, H, static_cast<const uint16_t*>(x), src_row,
-                                     expert_offsets, E, xp, s))
     return W4A4_ERR_LAUNCH;
   if (!launch_wgrad_fc1(H, I, E, expert_offsets, dH, xp, static_cast<uint16_t*>(dw1), s))
     return W4A4_ERR_LAUNCH;

@@ -1,7 +1,7 @@
 // HBM-bound gathers of the expert path (gfx950):
 //   unpermute:     y[t]  = bf16( sum_j p[t,j] * o[row_map[t,j]] )
 //   gather-sum:    dX[t] = bf16( sum_j dXp[row_map[t,j]] )
-//   gather-scale:  dO[r] = bf16( p[t,j] * dY[t] ),  t = src_row[r], pad rows 0
+//   scatter:       dO[row_map[t,j]] = bf16( p[t,j] * dY[t] ),  xp[row_map[t,j]] = x[t]
 // The router coefficients enter in the unpermute, on the bf16 expert outputs,
 // summed in FP32 in ascending j (a reading of the pages, which name the
 // router-coefficient position as a choice the execution specification must fix:
@@ -54,61 +54,55 @@ gather_sum_kernel(int H, int k, const uint16_t* __restrict__ src, const int32_t*
   }
 }
 
-// One wave per dispatched row.
+// One workgroup per token t: dY[t] and x[t] are read once and written, dY
+// scaled by the router weight, to each of the token's k dispatched rows.
+// Token order keeps the reads sequential; the writes are whole rows.
 __global__ void __launch_bounds__(kThreads)
-gather_scale_kernel(int64_t rows_alloc, int H, int k, const uint16_t* __restrict__ dy,
-                    const int32_t* __restrict__ row_map, const int32_t* __restrict__ src_row,
-                    const float* __restrict__ w, const int32_t* __restrict__ offsets, int E,
-                    uint16_t* __restrict__ dO) {
-  const int lane = threadIdx.x & 63;
-  const int64_t r = static_cast<int64_t>(blockIdx.x) * (kThreads / kWave) + (threadIdx.x >> 6);
-  if (r >= rows_alloc || r >= offsets[E]) return;
-  const int32_t t = src_row[r];
-  float p = 0.0f;
-  if (t >= 0) {
-    for (int j = 0; j < k; ++j)
-      if (row_map[static_cast<int64_t>(t) * k + j] == r) p = w[static_cast<int64_t>(t) * k + j];
-  }
-  const int chunks = H / 8;
-  for (int c = lane; c < chunks; c += kWave) {
-    u32x4_t o = {0u, 0u, 0u, 0u};
-    if (t >= 0) {
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(dy + static_cast<int64_t>(t) * H + c * 8);
+scatter_kernel(int H, int k, const uint16_t* __restrict__ dy, const uint16_t* __restrict__ x,
+               const int32_t* __restrict__ row_map, const float* __restrict__ w,
+               uint16_t* __restrict__ dO, uint16_t* __restrict__ xp) {
+  const int64_t t = blockIdx.x;
+  int32_t rows[16];
+  float ps[16];
 #pragma unroll
-      for (int d = 0; d < 4; ++d)
-        o[d] = pack_bf16x2(p * bf16_to_f32(static_cast<uint16_t>(v[d] & 0xFFFFu)),
-                           p * bf16_to_f32(static_cast<uint16_t>(v[d] >> 16)));
+  for (int j = 0; j < 16; ++j) {
+    if (j < k) {
+      rows[j] = row_map[t * k + j];
+      ps[j] = w[t * k + j];
     }
-    *reinterpret_cast<u32x4_t*>(dO + r * H + c * 8) = o;
+  }
+  for (int c = threadIdx.x; c < H / 8; c += kThreads) {
+    const u32x4_t g = *reinterpret_cast<const u32x4_t*>(dy + t * H + c * 8);
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(x + t * H + c * 8);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j < k) {
+        u32x4_t o;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          o[d] = pack_bf16x2(ps[j] * bf16_to_f32(static_cast<uint16_t>(g[d] & 0xFFFFu)),
+                             ps[j] * bf16_to_f32(static_cast<uint16_t>(g[d] >> 16)));
+        const int64_t r = rows[j];
+        *reinterpret_cast<u32x4_t*>(dO + r * H + c * 8) = o;
+        *reinterpret_cast<u32x4_t*>(xp + r * H + c * 8) = v;
+      }
+    }
   }
 }
 
-// One workgroup per dispatched row: xp[r] = x[src_row[r]], zeros for pad rows.
+// Pad rows (src_row < 0, rows [0, offsets[E])) of dO and xp: zeros.
 __global__ void __launch_bounds__(kThreads)
-gather_rows_kernel(int H, const uint16_t* __restrict__ x, const int32_t* __restrict__ src_row,
-                   const int32_t* __restrict__ offsets, int E, uint16_t* __restrict__ xp) {
+zero_pad_rows_kernel(int H, const int32_t* __restrict__ src_row, const int32_t* __restrict__ offsets,
+                     int E, uint16_t* __restrict__ dO, uint16_t* __restrict__ xp) {
   const int64_t r = blockIdx.x;
-  if (r >= offsets[E]) return;
-  const int32_t t = src_row[r];
+  if (r >= offsets[E] || src_row[r] >= 0) return;
   for (int c = threadIdx.x; c < H / 8; c += kThreads) {
-    u32x4_t v = {0u, 0u, 0u, 0u};
-    if (t >= 0) v = *reinterpret_cast<const u32x4_t*>(x + static_cast<int64_t>(t) * H + c * 8);
-    *reinterpret_cast<u32x4_t*>(xp + r * H + c * 8) = v;
+    *reinterpret_cast<u32x4_t*>(dO + r * H + c * 8) = u32x4_t{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4_t*>(xp + r * H + c * 8) = u32x4_t{0u, 0u, 0u, 0u};
   }
 }
 
 }  // namespace
-
-bool launch_gather_rows(int64_t rows_alloc, int H, const uint16_t* x, const int32_t* src_row,
-                        const int32_t* offsets, int E, uint16_t* xp, hipStream_t s) {
-  if (rows_alloc == 0) return true;
-  {
-    ProfScope p("x_gather_rows", s);
-    gather_rows_kernel<<<dim3(static_cast<unsigned>(rows_alloc)), dim3(kThreads), 0, s>>>(
-        H, x, src_row, offsets, E, xp);
-  }
-  return launch_ok("x_gather_rows");
-}
 
 bool launch_unpermute(int64_t T, int H, int k, const uint16_t* o, const int32_t* row_map,
                       const float* topk_w, uint16_t* y, hipStream_t s) {
@@ -132,17 +126,27 @@ bool launch_gather_sum(int64_t T, int H, int k, const uint16_t* dXp, const int32
   return launch_ok("dx_gather_sum");
 }
 
-bool launch_gather_scale(int64_t rows_alloc, int H, int k, const uint16_t* dy,
-                         const int32_t* row_map, const int32_t* src_row, const float* topk_w,
-                         const int32_t* offsets, int E, uint16_t* dO, hipStream_t s) {
-  const int64_t blocks = (rows_alloc + kThreads / kWave - 1) / (kThreads / kWave);
-  if (blocks == 0) return true;
+bool launch_scatter(int64_t T, int H, int k, const uint16_t* dy, const uint16_t* x,
+                    const int32_t* row_map, const float* topk_w, uint16_t* dO, uint16_t* xp,
+                    hipStream_t s) {
+  if (T == 0) return true;
   {
-    ProfScope p("do_gather_scale", s);
-    gather_scale_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s>>>(
-        rows_alloc, H, k, dy, row_map, src_row, topk_w, offsets, E, dO);
+    ProfScope p("dy_x_scatter", s);
+    scatter_kernel<<<dim3(static_cast<unsigned>(T)), dim3(kThreads), 0, s>>>(H, k, dy, x, row_map, topk_w,
+                                                                             dO, xp);
   }
-  return launch_ok("do_gather_scale");
+  return launch_ok("dy_x_scatter");
+}
+
+bool launch_zero_pad_rows(int64_t rows_alloc, int H, const int32_t* src_row, const int32_t* offsets,
+                          int E, uint16_t* dO, uint16_t* xp, hipStream_t s) {
+  if (rows_alloc == 0) return true;
+  {
+    ProfScope p("zero_pad_rows", s);
+    zero_pad_rows_kernel<<<dim3(static_cast<unsigned>(rows_alloc)), dim3(kThreads), 0, s>>>(
+        H, src_row, offsets, E, dO, xp);
+  }
+  return launch_ok("zero_pad_rows");
 }
 
 }  // namespace w4a4

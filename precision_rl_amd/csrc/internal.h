@@ -59,10 +59,14 @@ bool launch_fc2(int64_t rows_alloc, int H, int I, int E, const int32_t* offsets,
 bool launch_unpermute(int64_t T, int H, int k, const uint16_t* o, const int32_t* row_map,
                       const float* topk_w, uint16_t* y, hipStream_t s);
 
-// dO gather-scale: dO[r] = bf16(p dY[t]); pad rows zero.
-bool launch_gather_scale(int64_t rows_alloc, int H, int k, const uint16_t* dy,
-                         const int32_t* row_map, const int32_t* src_row, const float* topk_w,
-                         const int32_t* offsets, int E, uint16_t* dO, hipStream_t s);
+// Token-order scatter of the backward's row operands: for each token t and
+// slot j, dO[row_map[t,j]] = bf16(p[t,j] dY[t]) and xp[row_map[t,j]] = x[t].
+bool launch_scatter(int64_t T, int H, int k, const uint16_t* dy, const uint16_t* x,
+                    const int32_t* row_map, const float* topk_w, uint16_t* dO, uint16_t* xp,
+                    hipStream_t s);
+// Zeros in the pad rows (src_row < 0) of dO and xp.
+bool launch_zero_pad_rows(int64_t rows_alloc, int H, const int32_t* src_row, const int32_t* offsets,
+                          int E, uint16_t* dO, uint16_t* xp, hipStream_t s);
 
 // FC2 dgrad with the SwiGLU backward fused: dA = bf16(dO_e W2[e]) then the SwiGLU backward -> dH.
 bool launch_dgrad_fc2(int64_t rows_alloc, int H, int I, int E, const int32_t* offsets,
@@ -78,10 +82,6 @@ bool launch_wgrad_fc2(int H, int I, int E, const int32_t* offsets, const uint16_
                       const uint16_t* a, uint16_t* dW2, hipStream_t s);
 bool launch_wgrad_fc1(int H, int I, int E, const int32_t* offsets, const uint16_t* dH,
                       const uint16_t* xp, uint16_t* dW1, hipStream_t s);
-
-// xp[r] = x[src_row[r]] (zeros for pad rows), rows [0, offsets[E]).
-bool launch_gather_rows(int64_t rows_alloc, int H, const uint16_t* x, const int32_t* src_row,
-                        const int32_t* offsets, int E, uint16_t* xp, hipStream_t s);
 
 // dX gather-sum: dX[t] = bf16(sum_j dXp[row_map[t,j]]).
 bool launch_gather_sum(int64_t T, int H, int k, const uint16_t* dXp, const int32_t* row_map,
