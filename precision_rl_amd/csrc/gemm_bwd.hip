@@ -298,7 +298,7 @@ dgrad_kernel(DgradArgs args) {
           const float da = bf16_to_f32(static_cast<uint16_t>(v[d] >> (16 * p)));
           const float gt = bf16_to_f32(static_cast<uint16_t>(hg[d] >> (16 * p)));
           const float up = bf16_to_f32(static_cast<uint16_t>(hu[d] >> (16 * p)));
-          const float sg = 1.0f / (1.0f + expf(-gt));
+          const float sg = sigmoid_fast(gt);
           rg[p] = da * up * sg * (1.0f + gt * (1.0f - sg));
           ru[p] = da * gt * sg;
         }

@@ -283,13 +283,13 @@ fwd_gemm_kernel(FwdArgs args) {
           *reinterpret_cast<uint32_t*>(h + i) = hg;
           *reinterpret_cast<uint32_t*>(h + I + i) = hu;
         }
-        // SwiGLU on the bf16-rounded h, FP32 arithmetic
+        // SwiGLU on the bf16-rounded h, FP32 arithmetic (hardware exp2 / rcp)
         const float bg0 = bf16_to_f32(static_cast<uint16_t>(hg & 0xFFFFu));
         const float bg1 = bf16_to_f32(static_cast<uint16_t>(hg >> 16));
         const float bu0 = bf16_to_f32(static_cast<uint16_t>(hu & 0xFFFFu));
         const float bu1 = bf16_to_f32(static_cast<uint16_t>(hu >> 16));
-        const float a0 = bg0 / (1.0f + expf(-bg0)) * bu0;
-        const float a1 = bg1 / (1.0f + expf(-bg1)) * bu1;
+        const float a0 = bg0 * sigmoid_fast(bg0) * bu0;
+        const float a1 = bg1 * sigmoid_fast(bg1) * bu1;
         *reinterpret_cast<uint32_t*>(args.act + row * I + i) = pack_bf16x2(a0, a1);
       }
     }

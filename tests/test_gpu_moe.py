@@ -247,3 +247,58 @@ def test_backward_full_learner_workload_sampled():
         rb = _oracle_bwd(sub, 1, 1, ref)
         assert rel_l2(bf16_host(run.g["dw1"][e]), rb["dW1"][0]) <= BWD_TOL
         assert rel_l2(bf16_host(run.g["dw2"][e]), rb["dW2"][0]) <= BWD_TOL
+
+
+def test_full_skew_workload_sampled():
+    """Skewed workload at full size (T=32768, H=2048, E=128, k=8, I=768;
+    Zipf(1.2) expert popularity, 10 experts without tokens), forward and
+    backward: the permutation bit-exact against the oracle's routing of all
+    tokens; forward outputs and dX of sampled tokens, including the last
+    tokens of the most popular expert (its last, partial M tile) and of the
+    least popular live one; dW of the least popular live expert against the
+    oracle on its rows; dW of the empty experts exactly zero."""
+    w = synth.WORKLOADS["skew"]
+    d = synth.make_inputs(w.T, w.H, w.E, w.k, w.I, w.routing, w.x_dist, backward=True,
+                          seed=1000 + w.index)
+    print_case("skew_full_sampled", T=w.T, H=w.H, E=w.E, k=w.k, I=w.I)
+    run = Run(d, w.T, w.H, w.E, w.k, w.I, backward=True)
+    offsets, row_map, src_row = moe.route_fast(d["topk_idx"], w.E, 1)
+    assert np.array_equal(run.xq["offsets"].cpu().numpy(), offsets)
+    assert np.array_equal(run.xq["row_map"].cpu().numpy(), row_map)
+    assert np.array_equal(run.xq["src_row"].cpu().numpy()[:offsets[-1]], src_row)
+    counts = np.diff(offsets)
+    empty = np.nonzero(counts == 0)[0]
+    assert empty.size == 10
+    big = int(np.argmax(counts))
+    small = int(np.argmin(np.where(counts > 0, counts, counts.max() + 1)))
+    # sampled tokens: first / last rows of the largest and smallest experts
+    picks = [src_row[offsets[big]], src_row[offsets[big + 1] - 1], src_row[offsets[big + 1] - 2],
+             src_row[offsets[small]], src_row[offsets[small + 1] - 1], 0, w.T - 1]
+    sample = np.unique(np.array(picks))
+    experts = np.unique(d["topk_idx"][sample])
+    remap = -np.ones(w.E, dtype=np.int64)
+    remap[experts] = np.arange(experts.size)
+    sub = dict(x=d["x"][sample], topk_idx=remap[d["topk_idx"][sample]].astype(np.int32),
+               topk_w=d["topk_w"][sample], w1=d["w1"][experts], w2=d["w2"][experts],
+               dy=d["dy"][sample])
+    ref, _, _ = _oracle_fwd(sub, experts.size, 1)
+    rows_gpu = row_map[sample].reshape(-1)
+    rows_ref = ref["xq"]["row_map"].reshape(-1)
+    fc1 = run.f["fc1_f32"].cpu().numpy()[rows_gpu]
+    assert rel_l2(fc1, ref["h64"][rows_ref]) <= FC1_TOL
+    gc = q.unpack_codes(u8(run.f["a_codes"])[rows_gpu])
+    assert np.mean(gc != ref["a_codes"][rows_ref]) <= CODE_FLIP_BUDGET
+    assert rel_l2(bf16_host(run.f["y"])[sample], ref["y"]) <= Y_TOL
+    rb = _oracle_bwd(sub, experts.size, 1, ref)
+    assert rel_l2(bf16_host(run.g["dx"])[sample], rb["dX"]) <= BWD_TOL
+    # dW of the least popular live expert: its rows alone, k = 1
+    tok, slot = np.nonzero(d["topk_idx"] == small)
+    sub = dict(x=d["x"][tok], topk_idx=np.zeros((tok.size, 1), np.int32),
+               topk_w=d["topk_w"][tok, slot][:, None].copy(), w1=d["w1"][small:small + 1],
+               w2=d["w2"][small:small + 1], dy=d["dy"][tok])
+    ref, _, _ = _oracle_fwd(sub, 1, 1)
+    rb = _oracle_bwd(sub, 1, 1, ref)
+    assert rel_l2(bf16_host(run.g["dw1"][small]), rb["dW1"][0]) <= BWD_TOL
+    assert rel_l2(bf16_host(run.g["dw2"][small]), rb["dW2"][0]) <= BWD_TOL
+    for e in empty:
+        assert not run.g["dw1"][e].any() and not run.g["dw2"][e].any()
