@@ -18,6 +18,9 @@
 // bf16 |x| must reach to cross it (ties resolved towards the even code), so
 // the per-element work is seven integer compares on the bf16 bit pattern.
 
+#include <algorithm>
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -201,49 +204,49 @@ route_count_kernel(const int32_t* __restrict__ topk_idx, int64_t T, int k, int E
 
 // Single workgroup: per expert, exclusive prefix of the chunk counts (in
 // place, giving each chunk's first rank), the expert totals, and the padded
-// expert offsets.
+// expert offsets.  Thread (e, s) owns expert e and a contiguous segment s of
+// the chunks (S = 1024 / E segments): it sums its segment, the segment sums
+// are scanned in LDS, and it then writes its chunks' running prefix.
 constexpr int kScanThreads = 1024;
-constexpr int kScanTile = 8192;  // ints of the count matrix staged per pass
 
 __global__ void __launch_bounds__(kScanThreads)
 route_scan_kernel(int32_t* __restrict__ counts, int n_chunks, int E, int row_align,
                   int32_t* __restrict__ offsets, int32_t* __restrict__ expert_count) {
-  __shared__ int32_t buf[kScanTile];
-  __shared__ int32_t carry[1024];
-  __shared__ int32_t scan[1024];
+  __shared__ int32_t seg[kScanThreads];
+  __shared__ int32_t scan[kScanThreads];
   const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += kScanThreads) carry[e] = 0;
-  const int rows_per_tile = kScanTile / E > 0 ? kScanTile / E : 1;
+  const int S = max(1, kScanThreads / E);
+  const int e = tid % E, sgi = tid / E;
+  const bool owner = sgi < S && tid < E * S;
+  const int per = (n_chunks + S - 1) / S;
+  const int c0 = min(n_chunks, sgi * per), c1 = min(n_chunks, c0 + per);
+  int sum = 0;
+  if (owner)
+    for (int c = c0; c < c1; ++c) sum += counts[static_cast<int64_t>(c) * E + e];
+  seg[tid] = sum;
   __syncthreads();
-  for (int c0 = 0; c0 < n_chunks; c0 += rows_per_tile) {
-    const int rows = min(rows_per_tile, n_chunks - c0);
-    const int64_t base = static_cast<int64_t>(c0) * E;
-    for (int i = tid; i < rows * E; i += kScanThreads) buf[i] = counts[base + i];
-    __syncthreads();
-    for (int e = tid; e < E; e += kScanThreads) {
-      int run = carry[e];
-      for (int r = 0; r < rows; ++r) {
-        int v = buf[r * E + e];
-        buf[r * E + e] = run;
-        run += v;
-      }
-      carry[e] = run;
+  if (owner) {
+    int run = 0;
+    for (int j = 0; j < sgi; ++j) run += seg[j * E + e];   // segments before mine
+    for (int c = c0; c < c1; ++c) {
+      const int64_t i = static_cast<int64_t>(c) * E + e;
+      const int v = counts[i];
+      counts[i] = run;
+      run += v;
     }
-    __syncthreads();
-    for (int i = tid; i < rows * E; i += kScanThreads) counts[base + i] = buf[i];
-    __syncthreads();
   }
-  // Exclusive scan of the padded group sizes over experts (E <= 1024).
+  // expert totals and the exclusive scan of the padded group sizes (E <= 1024)
   int padded = 0;
   if (tid < E) {
-    int n = carry[tid];
+    int n = 0;
+    for (int j = 0; j < S; ++j) n += seg[j * E + tid];
     expert_count[tid] = n;
     padded = (n + row_align - 1) / row_align * row_align;
   }
   scan[tid] = padded;
   __syncthreads();
   for (int off = 1; off < kScanThreads; off <<= 1) {
-    int v = tid >= off ? scan[tid - off] : 0;
+    const int v = tid >= off ? scan[tid - off] : 0;
     __syncthreads();
     scan[tid] += v;
     __syncthreads();
@@ -398,6 +401,261 @@ requant_kernel(const uint16_t* __restrict__ a, int64_t rows_alloc, int K,
   if (lane == 0) outer[r] = g;
 }
 
+// ------------------------------------------------ row encoder, K % 32 == 0
+// The E2M1 magnitude code of a bf16 magnitude m is the number of the block's
+// seven crossing thresholds t_0 < ... < t_6 that m reaches.  It is found by
+// a three-step binary search, two elements at a time in packed 16-bit
+// integer arithmetic: with t' = t - 1, m reaches t exactly when t' - m is
+// negative (no overflow: both lie in [-1, 0x7FFF]).  The never-crossed
+// sentinel becomes t' = 0x7FFF.
+struct PackedThr {
+  uint32_t t[7];   // t - 1 in both 16-bit halves
+};
+
+__device__ __forceinline__ PackedThr pack_thresholds(const BlockThresholds& th) {
+  PackedThr p;
+#pragma unroll
+  for (int j = 0; j < 7; ++j) {
+    const uint32_t v = th.t[j] >= 0x8000u ? 0x7FFFu : ((th.t[j] - 1u) & 0xFFFFu);
+    p.t[j] = v * 0x00010001u;
+  }
+  return p;
+}
+
+// 0xFFFF in each 16-bit half whose magnitude reaches the threshold: the sign
+// of t' - m, spread over the half (two packed 16-bit integer instructions,
+// written out because the compiler otherwise unpacks them into compares).
+__device__ __forceinline__ uint32_t reach(uint32_t tp, uint32_t m) {
+  uint32_t r;
+  asm("v_pk_sub_i16 %0, %1, %2\n\tv_pk_ashrrev_i16 %0, %3, %0"
+      : "=&v"(r) : "v"(tp), "v"(m), "s"(0x000F000Fu));   // shift count 15 in both halves
+  return r;
+}
+
+__device__ __forceinline__ uint32_t select_bits(uint32_t mask, uint32_t a, uint32_t b) {
+  return (a & mask) | (b & ~mask);   // v_bfi_b32
+}
+
+// Two bf16 (one dword, element 2j low) -> two 4-bit codes in the low nibble
+// of each 16-bit half.
+__device__ __forceinline__ uint32_t code_pair(uint32_t w, const PackedThr& p) {
+  const uint32_t m = w & 0x7FFF7FFFu;
+  const uint32_t s4 = reach(p.t[3], m);
+  const uint32_t s2 = reach(select_bits(s4, p.t[5], p.t[1]), m);
+  const uint32_t t1 = select_bits(s4, select_bits(s2, p.t[6], p.t[4]), select_bits(s2, p.t[2], p.t[0]));
+  const uint32_t s1 = reach(t1, m);
+  return (s4 & 0x00040004u) | (s2 & 0x00020002u) | (s1 & 0x00010001u) | ((w >> 12) & 0x00080008u);
+}
+
+// 16 bf16 (8 dwords) -> 8 code bytes (2 dwords), element 2j in the low nibble of byte j.
+__device__ __forceinline__ u32x2_t encode16(const uint32_t (&w)[8], const PackedThr& p) {
+  u32x2_t out;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t c = code_pair(w[4 * h + i], p);
+      v |= ((c | (c >> 12)) & 0xFFu) << (8 * i);
+    }
+    out[h] = v;
+  }
+  return out;
+}
+
+__device__ __forceinline__ uint32_t amax16_of(const uint32_t (&w)[8]) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t a = w[i] & 0x7FFF7FFFu;
+    const uint32_t lo = a & 0xFFFFu, hi = a >> 16;
+    m = max(m, max(lo, hi));
+  }
+  return m;
+}
+
+enum class RowMode { Scatter, Identity, Requant };
+
+// One team of TEAM lanes per row; lane l of a team owns block pairs
+// l, l + TEAM, ... (PB of them), i.e. 32 consecutive elements each: 64 B
+// loaded, 16 B of codes and 2 B of scales stored per destination row.  The
+// workgroups stride over the rows and each wave loads its next row before
+// encoding the current one.
+//   Scatter:  rows are tokens, written to their k expert rows (routing done);
+//   Identity: row r -> row r (weights), also writes row_map / src_row / offsets;
+//   Requant:  row r -> row r for the rows [0, offsets[E]).
+template <int TEAM, int PB, RowMode MODE>
+__global__ void __launch_bounds__(kThreads)
+quant_rows_kernel(const uint16_t* __restrict__ x, int64_t n_rows, int K,
+                  const int32_t* __restrict__ topk_idx, int k, int E,
+                  uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ outer,
+                  int32_t* __restrict__ offsets, int32_t* __restrict__ row_map,
+                  int32_t* __restrict__ src_row, const int32_t* __restrict__ chunk_base) {
+  constexpr int kRowsPerWave = kWave / TEAM;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int team = lane / TEAM, tl = lane % TEAM;
+  const int pairs = K / 32;
+  const int64_t K2 = K / 2, K16 = K / 16;
+  int64_t n = n_rows;
+  if constexpr (MODE == RowMode::Requant) n = min<int64_t>(n, offsets[E]);
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kWavesPerBlock * kRowsPerWave;
+  int64_t r = (static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave) * kRowsPerWave + team;
+
+  u32x4_t cur[PB][4], nxt[PB][4];
+  auto load = [&](int64_t row, u32x4_t (&buf)[PB][4]) {
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + row * K);
+#pragma unroll
+    for (int i = 0; i < PB; ++i) {
+      const int p = tl + i * TEAM;
+      if (p < pairs) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) buf[i][q] = src[p * 4 + q];
+      }
+    }
+  };
+  if (r < n) load(r, cur);
+  for (; r < n; r += stride) {
+    if (r + stride < n) load(r + stride, nxt);
+
+    // row amax over the team
+    uint32_t bm[PB][2];
+    uint32_t amax = 0;
+#pragma unroll
+    for (int i = 0; i < PB; ++i) {
+      const int p = tl + i * TEAM;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t w[8] = {cur[i][2 * h][0], cur[i][2 * h][1], cur[i][2 * h][2], cur[i][2 * h][3],
+                               cur[i][2 * h + 1][0], cur[i][2 * h + 1][1], cur[i][2 * h + 1][2], cur[i][2 * h + 1][3]};
+        bm[i][h] = p < pairs ? amax16_of(w) : 0u;
+        amax = max(amax, bm[i][h]);
+      }
+    }
+#pragma unroll
+    for (int off = TEAM / 2; off > 0; off >>= 1) amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), off, kWave)));
+    const float g = outer_scale(amax);
+
+    // destination rows
+    int64_t dst[8];
+    int ndst = 1;
+    dst[0] = r;
+    if constexpr (MODE == RowMode::Scatter) {
+      int32_t myrow = 0;
+      if (tl < k) {
+        const int e = topk_idx[r * k + tl];
+        myrow = offsets[e] + chunk_base[(r / kRouteChunk) * E + e] + row_map[r * k + tl];
+        row_map[r * k + tl] = myrow;
+        src_row[myrow] = static_cast<int32_t>(r);
+      }
+      ndst = k;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dst[j] = __shfl(myrow, team * TEAM + j, kWave);
+    } else if constexpr (MODE == RowMode::Identity) {
+      if (tl == 0) {
+        row_map[r] = static_cast<int32_t>(r);
+        src_row[r] = static_cast<int32_t>(r);
+        if (r == 0) {
+          offsets[0] = 0;
+          offsets[1] = static_cast<int32_t>(n_rows);
+        }
+      }
+    }
+
+#pragma unroll
+    for (int i = 0; i < PB; ++i) {
+      const int p = tl + i * TEAM;
+      if (p >= pairs) continue;
+      u32x4_t cw;
+      uint32_t sc2 = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t w[8] = {cur[i][2 * h][0], cur[i][2 * h][1], cur[i][2 * h][2], cur[i][2 * h][3],
+                               cur[i][2 * h + 1][0], cur[i][2 * h + 1][1], cur[i][2 * h + 1][2], cur[i][2 * h + 1][3]};
+        const double ab = static_cast<double>(bf16_to_f32(static_cast<uint16_t>(bm[i][h])));
+        double dval = 0.0;
+        uint32_t dbits = 0;
+        if (g > 0.0f) dbits = e4m3_rne(ab / (6.0 * static_cast<double>(g)), &dval);
+        const PackedThr pt = pack_thresholds(make_thresholds(static_cast<double>(g) * dval));
+        const u32x2_t c2 = encode16(w, pt);
+        cw[2 * h] = c2[0];
+        cw[2 * h + 1] = c2[1];
+        sc2 |= dbits << (8 * h);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j < ndst) {
+          *reinterpret_cast<u32x4_t*>(codes + dst[j] * K2 + p * 16) = cw;
+          *reinterpret_cast<uint16_t*>(scales + dst[j] * K16 + p * 2) = static_cast<uint16_t>(sc2);
+        }
+      }
+    }
+    if (tl < ndst) {
+      int64_t d = dst[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j)
+        if (tl == j) d = dst[j];
+      outer[d] = g;
+    }
+#pragma unroll
+    for (int i = 0; i < PB; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) cur[i][q] = nxt[i][q];
+  }
+}
+
+// Pad rows of the expert groups (rows [offsets[e] + count[e], offsets[e+1])):
+// zero codes, scales and g; src_row = -1.  One wave per expert.
+__global__ void __launch_bounds__(kThreads)
+pad_rows_kernel(int K, int E, const int32_t* __restrict__ offsets, const int32_t* __restrict__ expert_count,
+                uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ outer,
+                int32_t* __restrict__ src_row) {
+  const int lane = threadIdx.x % kWave;
+  const int e = static_cast<int>(blockIdx.x) * kWavesPerBlock + static_cast<int>(threadIdx.x / kWave);
+  if (e >= E) return;
+  const int64_t K2 = K / 2, K16 = K / 16;
+  const int64_t r0 = offsets[e] + expert_count[e], r1 = offsets[e + 1];
+  for (int64_t r = r0; r < r1; ++r) {
+    for (int b = lane; b < K / 16; b += kWave) {
+      *reinterpret_cast<u32x2_t*>(codes + r * K2 + b * 8) = u32x2_t{0u, 0u};
+      scales[r * K16 + b] = 0;
+    }
+    if (lane == 0) {
+      outer[r] = 0.0f;
+      src_row[r] = -1;
+    }
+  }
+}
+
+// Launches quant_rows_kernel with the team shape for K (K % 32 == 0, K <= 4096).
+template <RowMode MODE>
+bool launch_rows(const char* name, const uint16_t* x, int64_t n_rows, int K, const int32_t* topk_idx, int k,
+                 int E, uint8_t* codes, uint8_t* scales, float* outer, int32_t* offsets,
+                 int32_t* row_map, int32_t* src_row, const int32_t* chunk_base, hipStream_t s) {
+  const int pairs = K / 32;
+  auto go = [&](auto team, auto pb) {
+    constexpr int TEAM = decltype(team)::value, PB = decltype(pb)::value;
+    constexpr int rows_per_block = kWavesPerBlock * (kWave / TEAM);
+    // enough workgroups to fill the chip twice over; each wave then loops
+    const int64_t need = (n_rows + rows_per_block - 1) / rows_per_block;
+    const int64_t blocks = std::min<int64_t>(need, 256 * 16);
+    if (blocks == 0) return true;
+    {
+      ProfScope p(name, s);
+      quant_rows_kernel<TEAM, PB, MODE><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s>>>(
+          x, n_rows, K, topk_idx, k, E, codes, scales, outer, offsets, row_map, src_row, chunk_base);
+    }
+    return launch_ok(name);
+  };
+  using I1 = std::integral_constant<int, 1>;
+  if (pairs <= 8) return go(std::integral_constant<int, 8>{}, I1{});
+  if (pairs <= 16) return go(std::integral_constant<int, 16>{}, I1{});
+  if (pairs <= 32) return go(std::integral_constant<int, 32>{}, I1{});
+  if (pairs <= 64) return go(std::integral_constant<int, 64>{}, I1{});
+  return go(std::integral_constant<int, 64>{}, std::integral_constant<int, 2>{});
+}
+
+bool rows_path(int K) { return K % 32 == 0 && K <= 4096; }
+
 __global__ void zero_offsets_kernel(int32_t* offsets, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) offsets[i] = 0;
 }
@@ -449,6 +707,23 @@ bool launch_quantize_permute(const uint16_t* x, int64_t T, int K, const int32_t*
     }
     if (!launch_ok("route_scan")) return false;
   }
+  if (rows_path(K)) {
+    const bool ok = topk_idx != nullptr
+        ? launch_rows<RowMode::Scatter>("quantize_scatter", x, T, K, topk_idx, k, E, codes, scales, outer,
+                                        offsets, row_map, src_row, counts, s)
+        : launch_rows<RowMode::Identity>("quantize_scatter", x, T, K, nullptr, 1, 1, codes, scales, outer,
+                                         offsets, row_map, src_row, nullptr, s);
+    if (!ok) return false;
+    if (topk_idx != nullptr && row_align > 1) {
+      {
+        ProfScope p("pad_rows", s);
+        pad_rows_kernel<<<dim3(static_cast<unsigned>((E + kWavesPerBlock - 1) / kWavesPerBlock)), dim3(kThreads),
+                          0, s>>>(K, E, offsets, expert_count, codes, scales, outer, src_row);
+      }
+      return launch_ok("pad_rows");
+    }
+    return true;
+  }
   const int64_t token_blocks = (T + kWavesPerBlock - 1) / kWavesPerBlock;
   const int64_t pad_blocks = (topk_idx != nullptr && row_align > 1)
                                  ? (E + kWavesPerBlock - 1) / kWavesPerBlock : 0;
@@ -469,6 +744,9 @@ bool launch_quantize_permute(const uint16_t* x, int64_t T, int K, const int32_t*
 bool launch_requant(const uint16_t* a, int64_t rows_alloc, int K, const int32_t* offsets, int E,
                     const int32_t* /*src_row*/, uint8_t* codes, uint8_t* scales, float* outer,
                     hipStream_t s) {
+  if (rows_path(K))
+    return launch_rows<RowMode::Requant>("requant", a, rows_alloc, K, nullptr, 1, E, codes, scales, outer,
+                                         const_cast<int32_t*>(offsets), nullptr, nullptr, nullptr, s);
   const int64_t blocks = (rows_alloc + kWavesPerBlock - 1) / kWavesPerBlock;
   if (blocks == 0) return true;
   return dispatch_maxb(K, [&](auto mb) {
