@@ -51,12 +51,27 @@ constexpr int kScaleRows = 512;
 constexpr int kBScaleRow0 = kBM;
 constexpr int kScalesOffset = kACodes + kBCodes;
 constexpr int kStageBytes = kScalesOffset + kScaleRows * 4;     // 14 KB
-constexpr int kGxOffset = kStages * kStageBytes;
-constexpr int kSlotOffset = kGxOffset + kBM * 4;
-constexpr int kLdsBytes = kSlotOffset + 16;                     // 57.9 KB: two workgroups per CU
 constexpr int kDmaPerStage = 5;              // per wave: 1 A-code, 2 B-code, 2 scale copies
 
-static_assert(2 * kLdsBytes <= 160 * 1024, "two workgroups per CU must fit in LDS");
+// Grouped scales (K a multiple of 256): the scales of four stages, 16 B per
+// row, arrive in one copy issued with the codes of every fourth stage, into
+// one of two 8 KB buffers (same 512-row numbering as above); the ring then
+// holds codes only.
+constexpr int kGroup = 4;
+constexpr int kCodeStageBytes = kACodes + kBCodes;             // 12 KB
+constexpr int kScaleBufBytes = kScaleRows * 16;                // 8 KB
+constexpr int kGsScaleOffset = kStages * kCodeStageBytes;      // 48 KB
+constexpr int kCodeDmaPerStage = 3;          // per wave: 1 A-code, 2 B-code copies
+constexpr int kScaleDmaPerGroup = 2;         // per wave
+
+template <bool GS>
+struct FwdLds {
+  static constexpr int kStage = GS ? kCodeStageBytes : kStageBytes;
+  static constexpr int kGx = GS ? kGsScaleOffset + 2 * kScaleBufBytes : kStages * kStageBytes;
+  static constexpr int kSlot = kGx + kBM * 4;
+  static constexpr int kBytes = kSlot + 16;      // 57.9 / 64 KB: two workgroups per CU
+  static_assert(2 * kBytes <= 160 * 1024, "two workgroups per CU must fit in LDS");
+};
 
 enum class FwdMode { FC1, FC2 };
 
@@ -111,9 +126,10 @@ __device__ __forceinline__ void scale_pairs(uint32_t word, int hl, half2_t& d0, 
   d1 = half2_t{v[1], v[1]};
 }
 
-template <FwdMode MODE>
+template <FwdMode MODE, bool GS>
 __global__ void __launch_bounds__(kThreads, 2)
 fwd_gemm_kernel(FwdArgs args) {
+  using L = FwdLds<GS>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -123,7 +139,7 @@ fwd_gemm_kernel(FwdArgs args) {
 
   const int n_tiles = MODE == FwdMode::FC1 ? args.I / 128 : args.N / kBN;
   TileCoord tc = grouped_m_tile<kBM>(args.offsets, args.E, n_tiles,
-                                     reinterpret_cast<int*>(lds + kSlotOffset));
+                                     reinterpret_cast<int*>(lds + L::kSlot));
   if (!tc.valid) return;
 
   const int64_t K2 = args.K / 2, K16 = args.K / 16;
@@ -160,19 +176,66 @@ fwd_gemm_kernel(FwdArgs args) {
       scale_src[c] = args.a.scales + tc.m0 * K16;            // filler: a valid row, never read
     }
   }
+  // Grouped scales: copy q = 2 wave + c moves scale rows 64 q .. 64 q + 63,
+  // 16 B each (A rows, then B rows, then filler).
+  const uint8_t* gscale_src[2];
+  if constexpr (GS) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int q = 64 * (2 * wave + c) + lane;
+      if (q < kBScaleRow0) {
+        gscale_src[c] = args.a.scales + (tc.m0 + min(q, a_rows - 1)) * K16;
+      } else if (q < kBScaleRow0 + kBN) {
+        gscale_src[c] = w_scales + static_cast<int64_t>(b_row_of<MODE>(q - kBScaleRow0, tc.n_tile, args.I)) * K16;
+      } else {
+        gscale_src[c] = args.a.scales + tc.m0 * K16;          // filler: a valid row, never read
+      }
+    }
+  }
   const uint32_t lds0 = lds_addr(lds);
   auto issue = [&](int kt) {
-    const uint32_t st = lds0 + (kt % kStages) * kStageBytes;
+    const uint32_t st = lds0 + (kt % kStages) * L::kStage;
+    if constexpr (GS) {
+      if (kt % kGroup == 0) {   // the group's scales go out first: they land before the stage's codes
+        const uint32_t sb = lds0 + kGsScaleOffset + ((kt / kGroup) % 2) * kScaleBufBytes;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) dma16(gscale_src[c] + (kt / kGroup) * 16, sb + (2 * wave + c) * 1024);
+      }
+    }
     const int cb = kt * kCodeRow;
     dma16_off(a_codes + cb, a_code_off, st + wave * 1024);
 #pragma unroll
     for (int c = 0; c < 2; ++c) dma16_off(w_codes + cb, b_code_off[c], st + kACodes + (2 * wave + c) * 1024);
+    if constexpr (!GS) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) dma4(scale_src[c] + kt * kScaleRow, st + kScalesOffset + (2 * wave + c) * 256);
+      for (int c = 0; c < 2; ++c) dma4(scale_src[c] + kt * kScaleRow, st + kScalesOffset + (2 * wave + c) * 256);
+    }
+  };
+  // Waits until stage kt (codes and, grouped, its scales) has landed in every
+  // wave: at most the copies this wave issued after stage kt's codes may be
+  // pending.
+  auto stage_ready = [&](int kt, int nk) {
+    const int later = min(kAhead - 1, nk - 1 - kt);
+    if constexpr (!GS) {
+      if (later >= 2) wait_vm_barrier<2 * kDmaPerStage>();
+      else if (later == 1) wait_vm_barrier<kDmaPerStage>();
+      else wait_vm_barrier<0>();
+    } else {
+      int after = 0;
+      for (int s = kt + 1; s <= kt + later; ++s)
+        after += kCodeDmaPerStage + (s % kGroup == 0 ? kScaleDmaPerGroup : 0);
+      switch (after) {
+        case 8: wait_vm_barrier<8>(); break;
+        case 6: wait_vm_barrier<6>(); break;
+        case 5: wait_vm_barrier<5>(); break;
+        case 3: wait_vm_barrier<3>(); break;
+        default: wait_vm_barrier<0>(); break;
+      }
+    }
   };
 
   // outer scales of the tile's rows, read by the epilogue
-  float* s_gx = reinterpret_cast<float*>(lds + kGxOffset);
+  float* s_gx = reinterpret_cast<float*>(lds + L::kGx);
   if (tid < kBM) s_gx[tid] = args.a.outer[tc.m0 + min(tid, a_rows - 1)];
 
   floatx16_t acc[2][4];
@@ -188,27 +251,27 @@ fwd_gemm_kernel(FwdArgs args) {
   for (int s = 0; s < kAhead && s < nk; ++s) issue(s);
 
   for (int kt = 0; kt < nk; ++kt) {
-    // stage kt has landed once at most the later stages' copies are pending
-    const int later = min(kAhead - 1, nk - 1 - kt);
-    if (later >= 2) wait_vm_barrier<2 * kDmaPerStage>();
-    else if (later == 1) wait_vm_barrier<kDmaPerStage>();
-    else wait_vm_barrier<0>();
+    stage_ready(kt, nk);
     if (kt + kAhead < nk) issue(kt + kAhead);   // refills the slot read in iteration kt-1
-
-    const uint8_t* st = lds + (kt % kStages) * kStageBytes;
+                                                // (grouped scales: buffer of group kt/4 - 1, done)
+    const uint8_t* st = lds + (kt % kStages) * L::kStage;
+    // scale dword of row r (scale-row numbering) for this stage
+    const uint8_t* sbase = GS ? lds + kGsScaleOffset + ((kt / kGroup) % 2) * kScaleBufBytes + (kt % kGroup) * 4
+                              : st + kScalesOffset;
+    const int sstride = GS ? 16 : 4;
     u32x4_t ac[2], bc[4];
     uint32_t as[2], bs[4];
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
       const int r = a_row0 + f * 32;
       ac[f] = *reinterpret_cast<const u32x4_t*>(st + r * kCodeRow + code_slot(r, hl) * 16);
-      as[f] = *reinterpret_cast<const uint32_t*>(st + kScalesOffset + r * 4);
+      as[f] = *reinterpret_cast<const uint32_t*>(sbase + r * sstride);
     }
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       const int r = b_row0 + f * 32;
       bc[f] = *reinterpret_cast<const u32x4_t*>(st + kACodes + r * kCodeRow + code_slot(r, hl) * 16);
-      bs[f] = *reinterpret_cast<const uint32_t*>(st + kScalesOffset + (kBScaleRow0 + r) * 4);
+      bs[f] = *reinterpret_cast<const uint32_t*>(sbase + (kBScaleRow0 + r) * sstride);
     }
     half2_t ad[2][2], bd[4][2];
 #pragma unroll
@@ -296,19 +359,25 @@ fwd_gemm_kernel(FwdArgs args) {
   }
 }
 
-template <FwdMode MODE>
-bool launch_fwd(const FwdArgs& args, int n_tiles, const char* name, hipStream_t s) {
+template <FwdMode MODE, bool GS>
+bool launch_fwd_variant(const FwdArgs& args, int64_t tiles, const char* name, hipStream_t s) {
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&fwd_gemm_kernel<MODE>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+      reinterpret_cast<const void*>(&fwd_gemm_kernel<MODE, GS>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, FwdLds<GS>::kBytes);
   if (attr != hipSuccess) return launch_ok(name) && false;
-  const int64_t tiles = grouped_m_tiles_bound(args.rows_alloc, args.E, kBM) * n_tiles;
-  if (tiles == 0) return true;
   {
     ProfScope p(name, s);
-    fwd_gemm_kernel<MODE><<<dim3(xcd_grid(tiles)), dim3(kThreads), kLdsBytes, s>>>(args);
+    fwd_gemm_kernel<MODE, GS><<<dim3(xcd_grid(tiles)), dim3(kThreads), FwdLds<GS>::kBytes, s>>>(args);
   }
   return launch_ok(name);
+}
+
+template <FwdMode MODE>
+bool launch_fwd(const FwdArgs& args, int n_tiles, const char* name, hipStream_t s) {
+  const int64_t tiles = grouped_m_tiles_bound(args.rows_alloc, args.E, kBM) * n_tiles;
+  if (tiles == 0) return true;
+  if (args.K % (kGroup * kBK) == 0) return launch_fwd_variant<MODE, true>(args, tiles, name, s);
+  return launch_fwd_variant<MODE, false>(args, tiles, name, s);
 }
 
 }  // namespace
