@@ -27,7 +27,9 @@
 // second 32 k of its row; A and B use the same assignment, so every MFMA k
 // slot pairs equal k indices (the reduction runs in a permuted K order; FP32
 // rounding of the sum is covered by the tolerance, and sums that are exact in
-// FP32 are order independent).
+// FP32 are order independent).  The epilogue writes the bf16 tile through
+// the idle ring so that global stores are whole 16-byte row chunks
+// (non-temporal: the outputs are read once, by a later kernel).
 
 #include "gemm_common.h"
 #include "internal.h"
@@ -63,6 +65,13 @@ constexpr int kScaleBufBytes = kScaleRows * 16;                // 8 KB
 constexpr int kGsScaleOffset = kStages * kCodeStageBytes;      // 48 KB
 constexpr int kCodeDmaPerStage = 3;          // per wave: 1 A-code, 2 B-code copies
 constexpr int kScaleDmaPerGroup = 2;         // per wave
+
+// Epilogue staging in the ring: 64 rows of 512 B of bf16 per round, rows
+// padded by 16 B so that the two lane halves' writes (4 rows apart) fall on
+// different banks.
+constexpr int kOutRows = 64;
+constexpr int kOutPitch = 528;
+static_assert(kOutRows * kOutPitch <= kStages * kCodeStageBytes, "staging fits in the ring");
 
 template <bool GS>
 struct FwdLds {
@@ -295,65 +304,98 @@ fwd_gemm_kernel(FwdArgs args) {
   __syncthreads();   // s_gx visible (written before the loop; every wave passed a barrier since)
 
   // ---------------------------------------------------------------- epilogue
+  // The tile leaves in two rounds of 64 rows (MFMA row block mi = q of both
+  // wave rows) staged as bf16 in the idle ring, so that every global store is
+  // a 16-byte chunk of a row and a wave writes whole rows.  Staging row s holds
+  // tile row (s / 32) * 64 + 32 q + s % 32.  FC1 stages h (gate half, then up
+  // half, 128 features each) and computes the SwiGLU on the staged bf16 values
+  // while storing.
   const float* wouter = args.w.outer + static_cast<int64_t>(tc.e) * args.N;
+  uint8_t* so = lds;
+  auto tile_row = [&](int s, int q) { return (s >> 5) * kWM + 32 * q + (s & 31); };
   if constexpr (MODE == FwdMode::FC2) {
-    const int n = tc.n_tile * kBN + wn * kWN + 4 * r32;
+    const int n_loc = wn * kWN + 4 * r32;
     float gw[4];
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) gw[ni] = wouter[n + ni];
+    for (int ni = 0; ni < 4; ++ni) gw[ni] = wouter[tc.n_tile * kBN + n_loc + ni];
+    uint16_t* out = args.out + tc.n_tile * kBN;
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
+    for (int q = 0; q < 2; ++q) {
+      if (q > 0) __syncthreads();   // previous round's reads done
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int lrow = acc_row(wm * kWM, mi, v, hl);
-        const int64_t row = tc.m0 + lrow;
-        if (row >= tc.m_end) continue;
-        const float gx = s_gx[lrow];
-        float o[4];
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) o[ni] = acc[mi][ni][v] * (gx * gw[ni]);
+        const int s = wm * 32 + acc_row(0, 0, v, hl);
+        const float gx = s_gx[tile_row(s, q)];
         u32x2_t pk;
-        pk[0] = pack_bf16x2(o[0], o[1]);
-        pk[1] = pack_bf16x2(o[2], o[3]);
-        *reinterpret_cast<u32x2_t*>(args.out + row * args.N + n) = pk;
+        pk[0] = pack_bf16x2(acc[q][0][v] * (gx * gw[0]), acc[q][1][v] * (gx * gw[1]));
+        pk[1] = pack_bf16x2(acc[q][2][v] * (gx * gw[2]), acc[q][3][v] * (gx * gw[3]));
+        *reinterpret_cast<u32x2_t*>(so + s * kOutPitch + n_loc * 2) = pk;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kOutRows * 32 / kThreads; ++j) {
+        const int c = tid + j * kThreads;
+        const int s = c >> 5, ch = c & 31;
+        const int64_t row = tc.m0 + tile_row(s, q);
+        if (row < tc.m_end)
+          __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t*>(so + s * kOutPitch + ch * 16),
+                                      reinterpret_cast<u32x4_t*>(out + row * args.N + ch * 8));
       }
     }
   } else {
     const int I = args.I;
-    const int i = tc.n_tile * 128 + wn * 64 + 2 * r32;
+    const int i_loc = wn * 64 + 2 * r32;
+    const int i = tc.n_tile * 128 + i_loc;
     const float gw_g0 = wouter[i], gw_g1 = wouter[i + 1];
     const float gw_u0 = wouter[I + i], gw_u1 = wouter[I + i + 1];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
+    for (int q = 0; q < 2; ++q) {
+      if (q > 0) __syncthreads();   // previous round's reads done
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int lrow = acc_row(wm * kWM, mi, v, hl);
-        const int64_t row = tc.m0 + lrow;
-        if (row >= tc.m_end) continue;
-        const float gx = s_gx[lrow];
-        const float g0 = acc[mi][0][v] * (gx * gw_g0);
-        const float g1 = acc[mi][1][v] * (gx * gw_g1);
-        const float u0 = acc[mi][2][v] * (gx * gw_u0);
-        const float u1 = acc[mi][3][v] * (gx * gw_u1);
+        const int s = wm * 32 + acc_row(0, 0, v, hl);
+        const float gx = s_gx[tile_row(s, q)];
+        const float g0 = acc[q][0][v] * (gx * gw_g0);
+        const float g1 = acc[q][1][v] * (gx * gw_g1);
+        const float u0 = acc[q][2][v] * (gx * gw_u0);
+        const float u1 = acc[q][3][v] * (gx * gw_u1);
         if (args.dbg != nullptr) {
-          float* d = args.dbg + row * (2 * I);
-          *reinterpret_cast<float2*>(d + i) = make_float2(g0, g1);
-          *reinterpret_cast<float2*>(d + I + i) = make_float2(u0, u1);
+          const int64_t row = tc.m0 + tile_row(s, q);
+          if (row < tc.m_end) {
+            float* d = args.dbg + row * (2 * I);
+            *reinterpret_cast<float2*>(d + i) = make_float2(g0, g1);
+            *reinterpret_cast<float2*>(d + I + i) = make_float2(u0, u1);
+          }
         }
-        const uint32_t hg = pack_bf16x2(g0, g1), hu = pack_bf16x2(u0, u1);
+        *reinterpret_cast<uint32_t*>(so + s * kOutPitch + i_loc * 2) = pack_bf16x2(g0, g1);
+        *reinterpret_cast<uint32_t*>(so + s * kOutPitch + 256 + i_loc * 2) = pack_bf16x2(u0, u1);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kOutRows * 16 / kThreads; ++j) {
+        const int c = tid + j * kThreads;
+        const int s = c >> 4, ch = c & 15;
+        const int64_t row = tc.m0 + tile_row(s, q);
+        if (row >= tc.m_end) continue;
+        const u32x4_t hg = *reinterpret_cast<const u32x4_t*>(so + s * kOutPitch + ch * 16);
+        const u32x4_t hu = *reinterpret_cast<const u32x4_t*>(so + s * kOutPitch + 256 + ch * 16);
+        const int64_t col = tc.n_tile * 128 + ch * 8;
         if (args.out != nullptr) {
-          uint16_t* h = args.out + row * (2 * I);
-          *reinterpret_cast<uint32_t*>(h + i) = hg;
-          *reinterpret_cast<uint32_t*>(h + I + i) = hu;
+          uint16_t* h = args.out + row * (2 * I) + col;
+          __builtin_nontemporal_store(hg, reinterpret_cast<u32x4_t*>(h));
+          __builtin_nontemporal_store(hu, reinterpret_cast<u32x4_t*>(h + I));
         }
         // SwiGLU on the bf16-rounded h, FP32 arithmetic (hardware exp2 / rcp)
-        const float bg0 = bf16_to_f32(static_cast<uint16_t>(hg & 0xFFFFu));
-        const float bg1 = bf16_to_f32(static_cast<uint16_t>(hg >> 16));
-        const float bu0 = bf16_to_f32(static_cast<uint16_t>(hu & 0xFFFFu));
-        const float bu1 = bf16_to_f32(static_cast<uint16_t>(hu >> 16));
-        const float a0 = bg0 * sigmoid_fast(bg0) * bu0;
-        const float a1 = bg1 * sigmoid_fast(bg1) * bu1;
-        *reinterpret_cast<uint32_t*>(args.act + row * I + i) = pack_bf16x2(a0, a1);
+        u32x4_t a;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float bg0 = bf16_to_f32(static_cast<uint16_t>(hg[w] & 0xFFFFu));
+          const float bg1 = bf16_to_f32(static_cast<uint16_t>(hg[w] >> 16));
+          const float bu0 = bf16_to_f32(static_cast<uint16_t>(hu[w] & 0xFFFFu));
+          const float bu1 = bf16_to_f32(static_cast<uint16_t>(hu[w] >> 16));
+          a[w] = pack_bf16x2(bg0 * sigmoid_fast(bg0) * bu0, bg1 * sigmoid_fast(bg1) * bu1);
+        }
+        __builtin_nontemporal_store(a, reinterpret_cast<u32x4_t*>(args.act + row * I + col));
       }
     }
   }
