@@ -283,12 +283,12 @@ dgrad_kernel(DgradArgs args) {
     const int64_t row = tc.m0 + lrow;
     const u32x4_t v = *reinterpret_cast<const u32x4_t*>(lds + lrow * kOutPitch + (n - n0) * 2);
     if constexpr (MODE == DgradMode::FC1) {
-      *reinterpret_cast<u32x4_t*>(args.out + row * args.N + n) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(args.out + row * args.N + n));
     } else {
       // SwiGLU backward on bf16 dA, gate / up from the saved bf16 h
       const int I = args.I;
-      const u32x4_t hg = *reinterpret_cast<const u32x4_t*>(args.h + row * (2 * I) + n);
-      const u32x4_t hu = *reinterpret_cast<const u32x4_t*>(args.h + row * (2 * I) + I + n);
+      const u32x4_t hg = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(args.h + row * (2 * I) + n));
+      const u32x4_t hu = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(args.h + row * (2 * I) + I + n));
       u32x4_t dg, du;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
@@ -305,8 +305,8 @@ dgrad_kernel(DgradArgs args) {
         dg[d] = pack_bf16x2(rg[0], rg[1]);
         du[d] = pack_bf16x2(ru[0], ru[1]);
       }
-      *reinterpret_cast<u32x4_t*>(args.out + row * (2 * I) + n) = dg;
-      *reinterpret_cast<u32x4_t*>(args.out + row * (2 * I) + I + n) = du;
+      __builtin_nontemporal_store(dg, reinterpret_cast<u32x4_t*>(args.out + row * (2 * I) + n));
+      __builtin_nontemporal_store(du, reinterpret_cast<u32x4_t*>(args.out + row * (2 * I) + I + n));
     }
   }
 }
@@ -534,8 +534,9 @@ wgrad_kernel(WgradArgs args) {
         const int c = tid + j * kThreads;
         const int s = c >> 5, n = tc.n0 + (c & 31) * 8;
         if (n >= args.N) continue;
-        *reinterpret_cast<u32x4_t*>(out + static_cast<int64_t>(tc.m0 + round_tile_row(s, q)) * args.N + n) =
-            *reinterpret_cast<const u32x4_t*>(so + stage_offset(s, n - tc.n0));
+        __builtin_nontemporal_store(
+            *reinterpret_cast<const u32x4_t*>(so + stage_offset(s, n - tc.n0)),
+            reinterpret_cast<u32x4_t*>(out + static_cast<int64_t>(tc.m0 + round_tile_row(s, q)) * args.N + n));
       }
       if (q < 3) __syncthreads();   // staging free for the next round
     }
