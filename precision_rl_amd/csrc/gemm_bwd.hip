@@ -252,9 +252,14 @@ dgrad_kernel(DgradArgs args) {
   zero_acc(acc);
   const int nk = args.K / kBK;
   for (int s = 0; s < kAhead && s < nk; ++s) issue(s);
+  // A wave whose 64 rows all lie past the expert's end (the padding half of
+  // a ragged last tile) only copies and waits: its SIMD's matrix core goes to
+  // the other workgroup on the CU.
+  const bool rows_live = tc.m0 + wrow < tc.m_end;
   for (int kt = 0; kt < nk; ++kt) {
     wait_stage(min(kAhead - 1, nk - 1 - kt));
     if (kt + kAhead < nk) issue(kt + kAhead);
+    if (!rows_live) continue;
     const uint8_t* st = lds + (kt % kStages) * kStageBytes;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {

@@ -259,10 +259,15 @@ fwd_gemm_kernel(FwdArgs args) {
   const int nk = args.K / kBK;
   for (int s = 0; s < kAhead && s < nk; ++s) issue(s);
 
+  // A wave whose 64 rows all lie past the expert's end (the padding half of
+  // a ragged last tile) only copies and waits: its SIMD's matrix core goes to
+  // the other workgroup on the CU.
+  const bool rows_live = tc.m0 + wm * kWM < tc.m_end;
   for (int kt = 0; kt < nk; ++kt) {
     stage_ready(kt, nk);
     if (kt + kAhead < nk) issue(kt + kAhead);   // refills the slot read in iteration kt-1
                                                 // (grouped scales: buffer of group kt/4 - 1, done)
+    if (!rows_live) continue;
     const uint8_t* st = lds + (kt % kStages) * L::kStage;
     // scale dword of row r (scale-row numbering) for this stage
     const uint8_t* sbase = GS ? lds + kGsScaleOffset + ((kt / kGroup) % 2) * kScaleBufBytes + (kt % kGroup) * 4
@@ -287,18 +292,26 @@ fwd_gemm_kernel(FwdArgs args) {
     for (int f = 0; f < 2; ++f) scale_pairs(as[f], hl, ad[f][0], ad[f][1]);
 #pragma unroll
     for (int f = 0; f < 4; ++f) scale_pairs(bs[f], hl, bd[f][0], bd[f][1]);
+    // Software-pipelined issue order: decode task t (k slice t / 6; fragments
+    // A0, B0, B1, B2, B3, A1) is issued right after MFMA t - 2, so a wave's
+    // own decode runs under its MFMAs (one 8-instruction decode lasts about
+    // one MFMA); the fences keep the compiler from regrouping them.
+    half8_t da[4][2], db[4][4];
+    auto decode_task = [&](int t) {
+      const int s4 = t / 6, i = t % 6;
+      if (i == 0) da[s4][0] = decode8(ac[0][s4], ad[0][s4 >> 1]);
+      else if (i == 5) da[s4][1] = decode8(ac[1][s4], ad[1][s4 >> 1]);
+      else db[s4][i - 1] = decode8(bc[i - 1][s4], bd[i - 1][s4 >> 1]);
+    };
+    decode_task(0);
+    decode_task(1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      half8_t af[2], bf[4];
-#pragma unroll
-      for (int f = 0; f < 2; ++f) af[f] = decode8(ac[f][s4], ad[f][s4 >> 1]);
-#pragma unroll
-      for (int f = 0; f < 4; ++f) bf[f] = decode8(bc[f][s4], bd[f][s4 >> 1]);
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
+    for (int m = 0; m < 32; ++m) {
+      const int s4 = m >> 3, mi = (m >> 2) & 1, ni = m & 3;
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(da[s4][mi], db[s4][ni], acc[mi][ni], 0, 0, 0);
+      if (m + 2 < 24) decode_task(m + 2);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   __syncthreads();   // s_gx visible (written before the loop; every wave passed a barrier since)
