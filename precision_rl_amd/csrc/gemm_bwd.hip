@@ -54,6 +54,15 @@ __device__ __forceinline__ short4_t ds_read_tr(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) short4_t*)(p));
 }
+// LDS pointer from a 32-bit LDS byte address.
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(3))) T* lds_ptr(uint32_t a) {
+  return reinterpret_cast<const __attribute__((address_space(3))) T*>(static_cast<uintptr_t>(a));
+}
+__device__ __forceinline__ short4_t ds_read_tr(const __attribute__((address_space(3))) uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) short4_t*)(p));
+}
 
 // ---- K-contiguous tile: 256 rows x 32 k, 64 B per row, chunk c of row r at
 // slot c ^ ((r >> 2) & 3).  Copy q (16 rows): lane i fills row 16 q + i / 4,
@@ -154,6 +163,11 @@ __device__ __forceinline__ void wait_stage(int later) {
   if (later >= 1) wait_vm_barrier<kDmaPerStage>();
   else wait_vm_barrier<0>();
 }
+// Same, and this wave's LDS reads have completed (lgkmcnt 0) before the barrier.
+__device__ __forceinline__ void wait_stage_lds(int later) {
+  if (later >= 1) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kDmaPerStage) : "memory");
+  else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // Writes the wave's accumulators as bf16 into the staging tile (row-major,
 // kOutPitch bytes per row); the caller synchronises around it.
@@ -235,47 +249,79 @@ dgrad_kernel(DgradArgs args) {
                 st + kABytes + (kBCopies * wave + c) * 1024);
   };
 
-  // ---- fragment addresses (within a stage)
-  int a_off[kMI][2], b_off[kNI][2][2];
+  // ---- fragment addresses within a stage: a per-lane offset for the first
+  // 32-row (A) / 32-column (B) block; the rest are immediates: +2048 per 32 A
+  // rows, +8192 per 16-k slice of B, +2048 for the second 4-k half of B.
+  uint32_t a_lane[2], b_lane[kNI];
 #pragma unroll
-  for (int f = 0; f < kMI; ++f)
+  for (int ks = 0; ks < 2; ++ks) a_lane[ks] = krow_frag_offset(wrow + r32, ks, hl);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) a_off[f][ks] = krow_frag_offset(wrow + f * 32 + r32, ks, hl);
-#pragma unroll
-  for (int f = 0; f < kNI; ++f)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int r = 0; r < 2; ++r) b_off[f][ks][r] = kABytes + BCol::frag_offset(wcol + f * 32, ks, r, lane);
-
+  for (int f = 0; f < kNI; ++f) b_lane[f] = kABytes + BCol::frag_offset(wcol + f * 32, 0, 0, lane);
   floatx16_t acc[kMI][kNI];
   zero_acc(acc);
-  const int nk = args.K / kBK;
-  for (int s = 0; s < kAhead && s < nk; ++s) issue(s);
-  // A wave whose 64 rows all lie past the expert's end (the padding half of
-  // a ragged last tile) only copies and waits: its SIMD's matrix core goes to
-  // the other workgroup on the CU.
-  const bool rows_live = tc.m0 + wrow < tc.m_end;
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_stage(min(kAhead - 1, nk - 1 - kt));
-    if (kt + kAhead < nk) issue(kt + kAhead);
-    if (!rows_live) continue;
-    const uint8_t* st = lds + (kt % kStages) * kStageBytes;
+  struct Slice {
+    bf16x8_t a[kMI], b[kNI];
+  };
+  // LDS byte addresses of this lane's fragments in one ring slot (one add
+  // each per stage; everything else is an immediate offset of the reads).
+  struct Bases {
+    uint32_t a[2], b[kNI];
+  };
+  auto stage_bases = [&](int kt, Bases& bs) {
+    uint32_t st = lds0 + (kt % kStages) * kStageBytes;
+    asm volatile("" : "+s"(st));   // a wave-uniform value: keep the compiler from re-deriving it per lane
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8_t af[kMI], bf[kNI];
+    for (int ks = 0; ks < 2; ++ks) bs.a[ks] = st + a_lane[ks];
 #pragma unroll
-      for (int f = 0; f < kMI; ++f) af[f] = *reinterpret_cast<const bf16x8_t*>(st + a_off[f][ks]);
+    for (int f = 0; f < kNI; ++f) bs.b[f] = st + b_lane[f];
+  };
+  auto load_slice = [&](const Bases& bs, int ks, Slice& sl) {
 #pragma unroll
-      for (int f = 0; f < kNI; ++f)
-        bf[f] = join_bf16(ds_read_tr(st + b_off[f][ks][0]), ds_read_tr(st + b_off[f][ks][1]));
+    for (int f = 0; f < kMI; ++f) sl.a[f] = *lds_ptr<bf16x8_t>(bs.a[ks] + f * 2048);
 #pragma unroll
-      for (int mi = 0; mi < kMI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < kNI; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
+    for (int f = 0; f < kNI; ++f) {
+      const uint32_t p = bs.b[f] + ks * 8192;
+      sl.b[f] = join_bf16(ds_read_tr(lds_ptr<uint8_t>(p)), ds_read_tr(lds_ptr<uint8_t>(p + 2048)));
     }
+  };
+  // The slice's MFMAs; the next slice's LDS reads go out right after the
+  // first one, so their latency hides under the other seven.
+  auto mfma_slice = [&](const Slice& sl, auto&& load_next) {
+    acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sl.a[0], sl.b[0], acc[0][0], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_next();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int m = 1; m < kMI * kNI; ++m) {
+      const int mi = m / kNI, ni = m % kNI;
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sl.a[mi], sl.b[ni], acc[mi][ni], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  const int nk = args.K / kBK;   // >= 1
+  for (int s = 0; s < kAhead && s < nk; ++s) issue(s);
+  // Pipeline (3-slot ring, two 16-k slices per stage): the wait for stage
+  // kt+1 sits between the two slices of stage kt, so the first slice of
+  // kt+1 is read from LDS under the MFMAs of the second slice of kt.  After
+  // that barrier every wave has finished reading stage kt (lgkmcnt 0), so the
+  // copy of stage kt+3 refills its slot.
+  wait_stage(min(kAhead - 1, nk - 1));
+  if (kAhead < nk) issue(kAhead);
+  Slice s0, s1;
+  Bases bc;
+  stage_bases(0, bc);
+  load_slice(bc, 0, s0);
+  int kt = 0;
+  for (; kt + 1 < nk; ++kt) {
+    mfma_slice(s0, [&] { load_slice(bc, 1, s1); });
+    wait_stage_lds(min(kAhead - 1, nk - 2 - kt));
+    if (kt + 1 + kAhead < nk) issue(kt + 1 + kAhead);
+    stage_bases(kt + 1, bc);
+    mfma_slice(s1, [&] { load_slice(bc, 0, s0); });
   }
+  mfma_slice(s0, [&] { load_slice(bc, 1, s1); });
+  mfma_slice(s1, [] {});
 
   ring_idle_barrier();
   stage_out(lds, acc, wrow, wcol, r32, hl);
@@ -363,6 +409,12 @@ __device__ __forceinline__ void wait_stage(int later) {
   if (later >= 2) wait_vm_barrier<2 * kDmaPerStage>();
   else if (later == 1) wait_vm_barrier<kDmaPerStage>();
   else wait_vm_barrier<0>();
+}
+// Same, and this wave's LDS reads have completed (lgkmcnt 0) before the barrier.
+__device__ __forceinline__ void wait_stage_lds(int later) {
+  if (later >= 2) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * kDmaPerStage) : "memory");
+  else if (later == 1) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kDmaPerStage) : "memory");
+  else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // All waves are past their last LDS read of the ring and every copy has
@@ -465,19 +517,40 @@ wgrad_kernel(WgradArgs args) {
     }
   };
 
-  int a_off[kMI][2][2], b_off[kNI][2][2];
+  // ---- fragment addresses within a stage: a per-lane offset for each
+  // 32-column block (A: M, B: N); +8192 per 16-k slice and +2048 for the
+  // second 4-k half are immediates of the reads.
+  uint32_t a_lane[kMI], b_lane[kNI];
 #pragma unroll
-  for (int f = 0; f < kMI; ++f)
+  for (int f = 0; f < kMI; ++f) a_lane[f] = kcol_frag_offset(wrow + f * 32, 0, 0, lane);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+  for (int f = 0; f < kNI; ++f) b_lane[f] = kABytes + kcol_frag_offset(wcol + f * 32, 0, 0, lane);
+  struct Slice {
+    bf16x8_t a[kMI], b[kNI];
+  };
+  struct Bases {
+    uint32_t a[kMI], b[kNI];
+  };
+  auto stage_bases = [&](int kt, Bases& bs) {
+    uint32_t st = lds0 + (kt % kStages) * kStageBytes;
+    asm volatile("" : "+s"(st));   // a wave-uniform value: keep the compiler from re-deriving it per lane
 #pragma unroll
-      for (int r = 0; r < 2; ++r) a_off[f][ks][r] = kcol_frag_offset(wrow + f * 32, ks, r, lane);
+    for (int f = 0; f < kMI; ++f) bs.a[f] = st + a_lane[f];
 #pragma unroll
-  for (int f = 0; f < kNI; ++f)
+    for (int f = 0; f < kNI; ++f) bs.b[f] = st + b_lane[f];
+  };
+  auto load_slice = [&](const Bases& bs, int ks, Slice& sl) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int f = 0; f < kMI; ++f) {
+      const uint32_t p = bs.a[f] + ks * 8192;
+      sl.a[f] = join_bf16(ds_read_tr(lds_ptr<uint8_t>(p)), ds_read_tr(lds_ptr<uint8_t>(p + 2048)));
+    }
 #pragma unroll
-      for (int r = 0; r < 2; ++r) b_off[f][ks][r] = kABytes + kcol_frag_offset(wcol + f * 32, ks, r, lane);
+    for (int f = 0; f < kNI; ++f) {
+      const uint32_t p = bs.b[f] + ks * 8192;
+      sl.b[f] = join_bf16(ds_read_tr(lds_ptr<uint8_t>(p)), ds_read_tr(lds_ptr<uint8_t>(p + 2048)));
+    }
+  };
 
   setup(tc);
   for (int s = 0; s < kAhead && s < tc.nk; ++s) issue(tc, s);
@@ -485,14 +558,28 @@ wgrad_kernel(WgradArgs args) {
   for (int it = 1;; ++it) {
     floatx16_t acc[kMI][kNI];
     zero_acc(acc);
-    const int nk = tc.nk;
+    // The slice's MFMAs; the next slice's LDS reads go out right after the
+    // first one, so their latency hides under the other seven.
+    auto mfma_slice = [&](const Slice& sl, auto&& load_next) {
+      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sl.a[0], sl.b[0], acc[0][0], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      load_next();
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int m = 1; m < kMI * kNI; ++m) {
+        const int mi = m / kNI, ni = m % kNI;
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sl.a[mi], sl.b[ni], acc[mi][ni], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    const int nk = tc.nk;   // 0 for an empty expert: its dW tile is zero
     const int tail = static_cast<int>(tc.r_end - tc.r_begin - static_cast<int64_t>(nk - 1) * kBK);
-    for (int kt = 0; kt < nk; ++kt) {
-      wait_stage(min(kAhead - 1, nk - 1 - kt));
-      uint8_t* st = lds + (kt % kStages) * kStageBytes;
+    // Once every copy of the last stage has landed in all waves (vmcnt 0 and
+    // a barrier): zero its k-rows past the expert's end in both operands,
+    // then synchronise again.
+    auto zero_tail = [&](int kt) {
       if (kt == nk - 1 && tail < kBK) {
-        // every copy of the workgroup has landed (vmcnt 0 + barrier above): zero
-        // the k-rows past the expert's end in both operands, then sync again
+        uint8_t* st = lds + (kt % kStages) * kStageBytes;
         for (int i = tid; i < (kBK - tail) * 64; i += kThreads) {
           const int op = i / ((kBK - tail) * 32), rem = i % ((kBK - tail) * 32);
           *reinterpret_cast<u32x4_t*>(st + op * kABytes + (tail + rem / 32) * 512 + (rem % 32) * 16) =
@@ -500,22 +587,31 @@ wgrad_kernel(WgradArgs args) {
         }
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       }
-      if (kt + kAhead < nk) issue(tc, kt + kAhead);
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        bf16x8_t af[kMI], bf[kNI];
-#pragma unroll
-        for (int f = 0; f < kMI; ++f)
-          af[f] = join_bf16(ds_read_tr(st + a_off[f][ks][0]), ds_read_tr(st + a_off[f][ks][1]));
-#pragma unroll
-        for (int f = 0; f < kNI; ++f)
-          bf[f] = join_bf16(ds_read_tr(st + b_off[f][ks][0]), ds_read_tr(st + b_off[f][ks][1]));
-#pragma unroll
-        for (int mi = 0; mi < kMI; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < kNI; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
+    };
+    // Pipeline (4-slot ring, two 16-k slices per stage): the wait for stage
+    // kt+1 sits between the two slices of stage kt, so the first slice of
+    // kt+1 is read from LDS under the MFMAs of the second slice of kt.  After
+    // that barrier every wave has finished reading stage kt (lgkmcnt 0), so
+    // the copy of stage kt+4 refills its slot.
+    if (nk > 0) {
+      wait_stage(min(kAhead - 1, nk - 1));
+      zero_tail(0);
+      if (kAhead < nk) issue(tc, kAhead);
+      Slice s0, s1;
+      Bases bc;
+      stage_bases(0, bc);
+      load_slice(bc, 0, s0);
+      int kt = 0;
+      for (; kt + 1 < nk; ++kt) {
+        mfma_slice(s0, [&] { load_slice(bc, 1, s1); });
+        wait_stage_lds(min(kAhead - 1, nk - 2 - kt));
+        zero_tail(kt + 1);
+        if (kt + 1 + kAhead < nk) issue(tc, kt + 1 + kAhead);
+        stage_bases(kt + 1, bc);
+        mfma_slice(s1, [&] { load_slice(bc, 0, s0); });
       }
+      mfma_slice(s0, [&] { load_slice(bc, 1, s1); });
+      mfma_slice(s1, [] {});
     }
 
     // ---- next tile's first stages, then the epilogue of this one
