@@ -54,11 +54,6 @@ __device__ __forceinline__ short4_t ds_read_tr(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) short4_t*)(p));
 }
-// LDS pointer from a 32-bit LDS byte address.
-template <typename T>
-__device__ __forceinline__ const __attribute__((address_space(3))) T* lds_ptr(uint32_t a) {
-  return reinterpret_cast<const __attribute__((address_space(3))) T*>(static_cast<uintptr_t>(a));
-}
 __device__ __forceinline__ short4_t ds_read_tr(const __attribute__((address_space(3))) uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) short4_t*)(p));

@@ -121,6 +121,19 @@ constexpr int waitcnt_vm(int vm) {
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));   // low half of the flat address
 }
+// LDS pointer from a 32-bit LDS byte address (reads through it are ds_read
+// with the constant part of the address as an immediate offset).
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(3))) T* lds_ptr(uint32_t a) {
+  return reinterpret_cast<const __attribute__((address_space(3))) T*>(static_cast<uintptr_t>(a));
+}
+// Keeps a wave-uniform value in a scalar register and opaque to the compiler,
+// so that addresses derived from it stay "per-lane offset + this value"
+// instead of being re-derived per lane.
+__device__ __forceinline__ uint32_t opaque_sgpr(uint32_t v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
 // A pointer that is the same in every lane, moved to scalar registers.
 __device__ __forceinline__ const void* uniform_ptr(const void* p) {
   const uint64_t v = reinterpret_cast<uint64_t>(p);

@@ -128,9 +128,9 @@ __device__ __forceinline__ half8_t decode8(uint32_t codes8, half2_t d2) {
 }
 
 // The lane's two E4M3 block scales of a stage (blocks 2h, 2h+1 of the row's
-// four) as f16 pairs (d, d).
-__device__ __forceinline__ void scale_pairs(uint32_t word, int hl, half2_t& d0, half2_t& d1) {
-  const half2_t v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word >> (16 * hl), 1.0f, false);
+// four, the low 16 bits of `pair`) as f16 pairs (d, d).
+__device__ __forceinline__ void scale_pairs(uint32_t pair, half2_t& d0, half2_t& d1) {
+  const half2_t v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pair, 1.0f, false);
   d0 = half2_t{v[0], v[0]};
   d1 = half2_t{v[1], v[1]};
 }
@@ -256,6 +256,14 @@ fwd_gemm_kernel(FwdArgs args) {
       for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
 
   const int a_row0 = wm * kWM + r32, b_row0 = wn * kWN + r32;
+  // This lane's LDS offsets within a stage: its code chunk (k half hl) of the
+  // first A / B row block, and its half (2 of the row's 4 block scales) of the
+  // scale dword of the same rows.
+  constexpr int kSStride = GS ? 16 : 4;   // bytes per scale row
+  const uint32_t a_code_lane = a_row0 * kCodeRow + code_slot(a_row0, hl) * 16;
+  const uint32_t b_code_lane = kACodes + b_row0 * kCodeRow + code_slot(b_row0, hl) * 16;
+  const uint32_t a_scale_lane = a_row0 * kSStride + 2 * hl;
+  const uint32_t b_scale_lane = (kBScaleRow0 + b_row0) * kSStride + 2 * hl;
   const int nk = args.K / kBK;
   for (int s = 0; s < kAhead && s < nk; ++s) issue(s);
 
@@ -268,30 +276,31 @@ fwd_gemm_kernel(FwdArgs args) {
     if (kt + kAhead < nk) issue(kt + kAhead);   // refills the slot read in iteration kt-1
                                                 // (grouped scales: buffer of group kt/4 - 1, done)
     if (!rows_live) continue;
-    const uint8_t* st = lds + (kt % kStages) * L::kStage;
-    // scale dword of row r (scale-row numbering) for this stage
-    const uint8_t* sbase = GS ? lds + kGsScaleOffset + ((kt / kGroup) % 2) * kScaleBufBytes + (kt % kGroup) * 4
-                              : st + kScalesOffset;
-    const int sstride = GS ? 16 : 4;
+    // LDS addresses: the stage's base (a scalar) plus this lane's offsets;
+    // the other fragments are immediates (+1024 per 32 code rows, +32 scale
+    // rows)
+    const uint32_t st = opaque_sgpr(lds0 + (kt % kStages) * L::kStage);
+    const uint32_t sb = opaque_sgpr(GS ? lds0 + kGsScaleOffset + ((kt / kGroup) % 2) * kScaleBufBytes + (kt % kGroup) * 4
+                                       : st + kScalesOffset);
+    const uint32_t pa = st + a_code_lane, pb = st + b_code_lane;
+    const uint32_t qa = sb + a_scale_lane, qb = sb + b_scale_lane;
     u32x4_t ac[2], bc[4];
     uint32_t as[2], bs[4];
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
-      const int r = a_row0 + f * 32;
-      ac[f] = *reinterpret_cast<const u32x4_t*>(st + r * kCodeRow + code_slot(r, hl) * 16);
-      as[f] = *reinterpret_cast<const uint32_t*>(sbase + r * sstride);
+      ac[f] = *lds_ptr<u32x4_t>(pa + f * 32 * kCodeRow);
+      as[f] = *lds_ptr<uint16_t>(qa + f * 32 * kSStride);
     }
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-      const int r = b_row0 + f * 32;
-      bc[f] = *reinterpret_cast<const u32x4_t*>(st + kACodes + r * kCodeRow + code_slot(r, hl) * 16);
-      bs[f] = *reinterpret_cast<const uint32_t*>(sbase + (kBScaleRow0 + r) * sstride);
+      bc[f] = *lds_ptr<u32x4_t>(pb + f * 32 * kCodeRow);
+      bs[f] = *lds_ptr<uint16_t>(qb + f * 32 * kSStride);
     }
     half2_t ad[2][2], bd[4][2];
 #pragma unroll
-    for (int f = 0; f < 2; ++f) scale_pairs(as[f], hl, ad[f][0], ad[f][1]);
+    for (int f = 0; f < 2; ++f) scale_pairs(as[f], ad[f][0], ad[f][1]);
 #pragma unroll
-    for (int f = 0; f < 4; ++f) scale_pairs(bs[f], hl, bd[f][0], bd[f][1]);
+    for (int f = 0; f < 4; ++f) scale_pairs(bs[f], bd[f][0], bd[f][1]);
     // Software-pipelined issue order: decode task t (k slice t / 6; fragments
     // A0, B0, B1, B2, B3, A1) is issued right after MFMA t - 2, so a wave's
     // own decode runs under its MFMAs (one 8-instruction decode lasts about
