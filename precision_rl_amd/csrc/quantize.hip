@@ -646,7 +646,15 @@ bool launch_rows(const char* name, const uint16_t* x, int64_t n_rows, int K, con
     }
     return launch_ok(name);
   };
+  // One block pair per lane in a team that covers the row (a wave then
+  // writes whole rows, which the 8-way scatter needs); rows of 24, 48 or 96
+  // pairs, which would leave a quarter of a 32/64/128-lane team idle, take
+  // three pairs per lane in a team of 8/16/32 instead.
   using I1 = std::integral_constant<int, 1>;
+  using I3 = std::integral_constant<int, 3>;
+  if (pairs == 24) return go(std::integral_constant<int, 8>{}, I3{});
+  if (pairs == 48) return go(std::integral_constant<int, 16>{}, I3{});
+  if (pairs == 96) return go(std::integral_constant<int, 32>{}, I3{});
   if (pairs <= 8) return go(std::integral_constant<int, 8>{}, I1{});
   if (pairs <= 16) return go(std::integral_constant<int, 16>{}, I1{});
   if (pairs <= 32) return go(std::integral_constant<int, 32>{}, I1{});

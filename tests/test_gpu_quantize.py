@@ -59,6 +59,20 @@ def test_quantize_permute_ragged_empty():
         _compare_qp(d, E, A, got)
 
 
+@pytest.mark.parametrize("H", [768, 1536, 3072])
+def test_quantize_permute_three_pairs_per_lane(H):
+    """Row widths of 24, 48 and 96 block pairs, which the row encoder spreads
+    three pairs per lane over teams of 8, 16 and 32 lanes; with k=8 the
+    narrowest team still covers every destination row."""
+    b = _binding()
+    T, E, k = 700, 24, 8
+    d = synth.make_inputs(T, H, E, k, routing="zipf", x_dist="t3", seed=H, n_empty=3)
+    print_case("quantize_permute_3pairs", T=T, H=H, E=E, k=k)
+    got = b.w4a4_quantize_permute(bf16_dev(d["x"], torch), torch.from_numpy(d["topk_idx"]).cuda(), E, 1)
+    torch.cuda.synchronize()
+    _compare_qp(d, E, 1, got)
+
+
 def test_quantize_permute_full_qp_workload():
     """The quantize+permute workload at full size: T=16384, H=2048, E=128,
     k=8, Student-t(3) activations."""
