@@ -207,8 +207,10 @@ dgrad_kernel(DgradArgs args) {
   const int wrow = (wave & 1) * kWM, wcol = (wave >> 1) * kWN;
   const int r32 = lane & 31, hl = lane >> 5;
   const int n_tiles = (args.N + kBN - 1) / kBN;
-  TileCoord tc = grouped_m_tile<kBM>(args.offsets, args.E, n_tiles,
-                                     reinterpret_cast<int*>(lds + kSlotOffset));
+  // FC1 dgrad: an expert's 6 MiB weight slab exceeds the XCD's L2 and its
+  // dH rows (3 MiB at 1024 rows) do not, so M tiles run fastest.
+  TileCoord tc = grouped_m_tile<kBM, MODE == DgradMode::FC1>(args.offsets, args.E, n_tiles,
+                                                             reinterpret_cast<int*>(lds + kSlotOffset));
   if (!tc.valid) return;
   const int n0 = tc.n_tile * kBN;
   const int a_rows = static_cast<int>(min<int64_t>(kBM, args.rows_alloc - tc.m0));   // >= 1

@@ -29,10 +29,12 @@ struct TileCoord {
 // The number of tiles exists only on the device; wave 0 of every workgroup
 // recomputes it from the offsets (lane-local sums and a wave prefix scan) and
 // publishes the result through `slot` (LDS, 4 ints).  Logical tiles are
-// ordered expert-major, N fastest, and dealt out in contiguous runs per XCD
-// so that an expert's weight tiles and an M tile's activations stay in one
-// XCD's L2.  Contains one __syncthreads().
-template <int TM = kTileM>
+// ordered expert-major and dealt out in contiguous runs per XCD, so that an
+// expert's operands stay in one XCD's L2; within an expert N runs fastest
+// (tiles that run together share activation rows), or with M_FAST the M
+// tiles run fastest (tiles that run together share a weight slab, for a
+// weight operand larger than the L2).  Contains one __syncthreads().
+template <int TM = kTileM, bool M_FAST = false>
 __device__ inline TileCoord grouped_m_tile(const int32_t* __restrict__ offsets, int E, int n_tiles,
                                            int* slot) {
   const int tid = threadIdx.x;
@@ -65,9 +67,15 @@ __device__ inline TileCoord grouped_m_tile(const int32_t* __restrict__ offsets, 
           const int t = (offsets[e + 1] - offsets[e] + TM - 1) / TM;
           if (mt < first + t) {
             slot[0] = e;
-            slot[1] = offsets[e] + (mt - first) * TM;
             slot[2] = offsets[e + 1];
-            slot[3] = static_cast<int>(L % n_tiles);
+            if constexpr (M_FAST) {
+              const int64_t le = L - static_cast<int64_t>(first) * n_tiles;   // tile within the expert
+              slot[1] = offsets[e] + static_cast<int>(le % t) * TM;
+              slot[3] = static_cast<int>(le / t);
+            } else {
+              slot[1] = offsets[e] + (mt - first) * TM;
+              slot[3] = static_cast<int>(L % n_tiles);
+            }
             break;
           }
           first += t;
