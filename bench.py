@@ -65,6 +65,10 @@ def algorithmic_work(T, H, E, k, I):
     return fl, by
 
 
+# Kernels the library runs concurrently with another one (second stream).
+CONCURRENT = {"dx_gather_sum": "gemm_wgrad_fc1"}
+
+
 def source_hash(name):
     path = os.path.join(ROOT, "precision_rl_amd", "csrc", KERNEL_SOURCES[name])
     with open(path, "rb") as f:
@@ -209,6 +213,10 @@ def main():
         elif name in by:
             entry["gbs"] = round(by[name] / (avg_ms * 1e-3) / 1e9, 1)
             entry["frac_hbm"] = round(entry["gbs"] / PEAK_HBM_GBS, 4)
+        if name in CONCURRENT:
+            # launched on a second stream beside another kernel: its duration is
+            # time shared with that kernel, not its standalone rate
+            entry["runs_beside"] = CONCURRENT[name]
         per_kernel[name] = entry
     dom = max(kern, key=lambda n: kern[n]["total_ms"])
     dom_avg_s = kern[dom]["total_ms"] / kern[dom]["count"] * 1e-3

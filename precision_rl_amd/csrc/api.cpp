@@ -1,6 +1,9 @@
 // Host side of the C ABI declared in include/w4a4_moe.h: argument validation,
-// workspace carving and the launch sequence of each call.  No allocation, no
-// synchronisation, no device reads on the host.
+// workspace carving and the launch sequence of each call.  No device-memory
+// allocation, no synchronisation, no device reads on the host.  The backward
+// runs its dX gather-sum on a second stream of the same device (default
+// priority, created once per device with two events), forked from and joined
+// back into the caller's stream.
 
 #include <hip/hip_runtime.h>
 
@@ -31,6 +34,30 @@ w4a4_status fail(w4a4_status st, const char* fmt, ...) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// The side stream of the current device and its fork / join events.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+bool side_stream(SideStream& out) {
+  static std::mutex mu;
+  static std::map<int, SideStream> per_device;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = per_device.find(dev);
+  if (it == per_device.end()) {
+    SideStream ss;
+    if (hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)
+      return false;
+    it = per_device.emplace(dev, ss).first;
+  }
+  out = it->second;
+  return true;
+}
 
 constexpr size_t kAlign = 256;
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -309,10 +336,19 @@ w4a4_status w4a4_expert_bwd(int64_t T, int H, int I, int E, int k, int row_align
     return W4A4_ERR_LAUNCH;
   if (cap > 0 && !launch_dgrad_fc1(cap, H, I, E, expert_offsets, dH, W1, dXp, s))
     return W4A4_ERR_LAUNCH;
+  // The dX gather-sum needs only dXp and the FC1 wgrad only dH: the gather
+  // (HBM-bound, few registers, no LDS) runs on the side stream beside the
+  // wgrad (MFMA-bound), and the caller's stream waits for both.
+  SideStream side;
+  if (!side_stream(side)) return fail(W4A4_ERR_LAUNCH, "side stream / events could not be created");
+  if (hipEventRecord(side.fork, s) != hipSuccess || hipStreamWaitEvent(side.stream, side.fork, 0) != hipSuccess)
+    return fail(W4A4_ERR_LAUNCH, "fork to the side stream failed");
   if (!launch_wgrad_fc1(H, I, E, expert_offsets, dH, xp, static_cast<uint16_t*>(dw1), s))
     return W4A4_ERR_LAUNCH;
-  if (!launch_gather_sum(T, H, k, dXp, row_map, static_cast<uint16_t*>(dx), s))
+  if (!launch_gather_sum(T, H, k, dXp, row_map, static_cast<uint16_t*>(dx), side.stream))
     return W4A4_ERR_LAUNCH;
+  if (hipEventRecord(side.join, side.stream) != hipSuccess || hipStreamWaitEvent(s, side.join, 0) != hipSuccess)
+    return fail(W4A4_ERR_LAUNCH, "join from the side stream failed");
   return W4A4_OK;
 }
 

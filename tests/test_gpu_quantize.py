@@ -73,6 +73,20 @@ def test_quantize_permute_three_pairs_per_lane(H):
     _compare_qp(d, E, 1, got)
 
 
+@pytest.mark.parametrize("K", [16, 48, 4112])
+def test_quantize_permute_row_lengths_off_the_fast_path(K):
+    """Row lengths that are not a multiple of 32 elements, or longer than 4096,
+    take the per-block encoder: routed (k=4 of 12 experts, row_align 16) and
+    bit-exact like the row encoder."""
+    b = _binding()
+    T, E, k = 300, 12, 4
+    d = synth.make_inputs(T, K, E, k, routing="zipf", x_dist="t3", seed=K + 7, n_empty=2)
+    print_case("quantize_permute_blocks", T=T, K=K, E=E, k=k)
+    got = b.w4a4_quantize_permute(bf16_dev(d["x"], torch), torch.from_numpy(d["topk_idx"]).cuda(), E, 16)
+    torch.cuda.synchronize()
+    _compare_qp(d, E, 16, got)
+
+
 def test_quantize_permute_full_qp_workload():
     """The quantize+permute workload at full size: T=16384, H=2048, E=128,
     k=8, Student-t(3) activations."""
