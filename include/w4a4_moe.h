@@ -19,6 +19,10 @@
  *    do not depend on the other tokens of the batch (per-token scale domain).
  *  - Calls are thread-safe; concurrent calls on different streams need
  *    different workspaces.
+ *  - w4a4_expert_bwd runs its dX gather-sum on a second stream of the current
+ *    device (created on first use, default priority), forked from `stream`
+ *    after the FC1 dgrad and joined back into it: work enqueued on `stream`
+ *    after the call sees every output.
  *
  * Data formats (miniTE Technical Report, sections 2.2 and 5.1; rainbus review
  * of the miniTE paper, "prerequisites: the NVFP4 format" and method step 4):

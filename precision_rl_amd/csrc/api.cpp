@@ -35,17 +35,21 @@ w4a4_status fail(w4a4_status st, const char* fmt, ...) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// The side stream of the current device and its fork / join events.
+// The side stream of the current device and its fork / join events.  Callers
+// hold side_mutex() from the fork to the join, so that concurrent calls on
+// different streams never interleave their event records and waits.
 struct SideStream {
   hipStream_t stream = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
 };
-bool side_stream(SideStream& out) {
+std::mutex& side_mutex() {
   static std::mutex mu;
+  return mu;
+}
+bool side_stream(SideStream& out) {   // call with side_mutex() held
   static std::map<int, SideStream> per_device;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return false;
-  std::lock_guard<std::mutex> lock(mu);
   auto it = per_device.find(dev);
   if (it == per_device.end()) {
     SideStream ss;
@@ -339,6 +343,7 @@ w4a4_status w4a4_expert_bwd(int64_t T, int H, int I, int E, int k, int row_align
   // The dX gather-sum needs only dXp and the FC1 wgrad only dH: the gather
   // (HBM-bound, few registers, no LDS) runs on the side stream beside the
   // wgrad (MFMA-bound), and the caller's stream waits for both.
+  std::lock_guard<std::mutex> lock(side_mutex());
   SideStream side;
   if (!side_stream(side)) return fail(W4A4_ERR_LAUNCH, "side stream / events could not be created");
   if (hipEventRecord(side.fork, s) != hipSuccess || hipStreamWaitEvent(side.stream, side.fork, 0) != hipSuccess)
