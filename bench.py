@@ -36,7 +36,7 @@ KERNEL_SOURCES = {
     "gemm_dgrad_fc1": "gemm_bwd.hip", "gemm_dgrad_fc2": "gemm_bwd.hip",
     "gemm_wgrad_fc1": "gemm_bwd.hip", "gemm_wgrad_fc2": "gemm_bwd.hip",
     "quantize_scatter": "quantize.hip", "requant": "quantize.hip",
-    "unpermute": "elementwise.hip", "dy_x_scatter": "elementwise.hip",
+    "unpermute": "elementwise.hip", "dy_scatter": "elementwise.hip", "x_scatter": "elementwise.hip",
     "dx_gather_sum": "elementwise.hip",
 }
 
@@ -58,15 +58,18 @@ def algorithmic_work(T, H, E, k, I):
         "quantize_scatter": T * (H * 2 + k * 4) + M * (H // 2 + H // 16 + 4) + T * k * 4 + M * 4,
         "requant": M * (I * 2 + I // 2 + I // 16 + 4),
         "unpermute": T * (k * H * 2 + k * 8 + H * 2),
-        # read dY[t], x[t] and the token's k maps / weights; write k rows of dO and of xp
-        "dy_x_scatter": T * (2 * H * 2 + k * 8) + 2 * M * H * 2,
+        # read dY[t] and the token's k maps / weights; write k rows of dO
+        "dy_scatter": T * (H * 2 + k * 8) + M * H * 2,
+        # read x[t] and the token's k maps; write k rows of xp
+        "x_scatter": T * (H * 2 + k * 4) + M * H * 2,
         "dx_gather_sum": T * (k * H * 2 + k * 4 + H * 2),
     }
     return fl, by
 
 
 # Kernels the library runs concurrently with another one (second stream).
-CONCURRENT = {"dx_gather_sum": "gemm_wgrad_fc1"}
+CONCURRENT = {"x_scatter": "gemm_wgrad_fc2, gemm_dgrad_fc1",
+              "dx_gather_sum": "gemm_wgrad_fc1"}
 
 
 def source_hash(name):

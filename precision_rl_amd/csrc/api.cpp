@@ -1,8 +1,8 @@
 // Host side of the C ABI declared in include/w4a4_moe.h: argument validation,
 // workspace carving and the launch sequence of each call.  No device-memory
 // allocation, no synchronisation, no device reads on the host.  The backward
-// runs its dX gather-sum on a second stream of the same device (default
-// priority, created once per device with two events), forked from and joined
+// runs two HBM-bound kernels on a second stream of the same device (default
+// priority, created once per device with its events), forked from and joined
 // back into the caller's stream.
 
 #include <hip/hip_runtime.h>
@@ -40,7 +40,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // different streams never interleave their event records and waits.
 struct SideStream {
   hipStream_t stream = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t fork[2] = {nullptr, nullptr}, join[2] = {nullptr, nullptr};
 };
 std::mutex& side_mutex() {
   static std::mutex mu;
@@ -53,10 +53,11 @@ bool side_stream(SideStream& out) {   // call with side_mutex() held
   auto it = per_device.find(dev);
   if (it == per_device.end()) {
     SideStream ss;
-    if (hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) != hipSuccess ||
-        hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)
-      return false;
+    if (hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) != hipSuccess) return false;
+    for (int i = 0; i < 2; ++i)
+      if (hipEventCreateWithFlags(&ss.fork[i], hipEventDisableTiming) != hipSuccess ||
+          hipEventCreateWithFlags(&ss.join[i], hipEventDisableTiming) != hipSuccess)
+        return false;
     it = per_device.emplace(dev, ss).first;
   }
   out = it->second;
@@ -330,30 +331,44 @@ w4a4_status w4a4_expert_bwd(int64_t T, int H, int I, int E, int k, int row_align
   const uint16_t* W1 = static_cast<const uint16_t*>(w1);
   const uint16_t* W2 = static_cast<const uint16_t*>(w2);
 
-  if (!launch_scatter(T, H, k, static_cast<const uint16_t*>(dy), static_cast<const uint16_t*>(x), row_map,
-                      topk_w, dO, xp, s))
+  // Side stream: the copy of x to the expert rows (xp, read only by the last
+  // GEMM) runs beside the FC2 wgrad and the FC1 dgrad; the dX gather-sum
+  // (needs only dXp) beside the FC1 wgrad (needs only dH and xp).  Both are
+  // HBM-bound with few registers and no LDS; the GEMMs are MFMA-bound.  The
+  // caller's stream waits for both before the call's work ends.
+  std::lock_guard<std::mutex> lock(side_mutex());
+  SideStream side;
+  if (!side_stream(side)) return fail(W4A4_ERR_LAUNCH, "side stream / events could not be created");
+  auto fork = [&](int i) {
+    return hipEventRecord(side.fork[i], s) == hipSuccess &&
+           hipStreamWaitEvent(side.stream, side.fork[i], 0) == hipSuccess;
+  };
+  auto join = [&](int i) {
+    return hipEventRecord(side.join[i], side.stream) == hipSuccess &&
+           hipStreamWaitEvent(s, side.join[i], 0) == hipSuccess;
+  };
+  if (!launch_scatter_dy(T, H, k, static_cast<const uint16_t*>(dy), row_map, topk_w, dO, s))
     return W4A4_ERR_LAUNCH;
-  if (row_align > 1 && !launch_zero_pad_rows(cap, H, src_row, expert_offsets, E, dO, xp, s))
+  if (row_align > 1 && !launch_zero_pad_rows(cap, H, src_row, expert_offsets, E, dO, s))
     return W4A4_ERR_LAUNCH;
   if (cap > 0 && !launch_dgrad_fc2(cap, H, I, E, expert_offsets, dO, W2, h, dH, s)) return W4A4_ERR_LAUNCH;
+  // (forked after the FC2 dgrad: beside the persistent FC2 wgrad the copy
+  // costs the GEMM little; beside the FC2 dgrad it took that kernel's slots)
+  if (!fork(0)) return fail(W4A4_ERR_LAUNCH, "fork to the side stream failed");
+  if (!launch_scatter_x(T, H, k, static_cast<const uint16_t*>(x), row_map, xp, side.stream))
+    return W4A4_ERR_LAUNCH;
+  if (row_align > 1 && !launch_zero_pad_rows(cap, H, src_row, expert_offsets, E, xp, side.stream))
+    return W4A4_ERR_LAUNCH;
   if (!launch_wgrad_fc2(H, I, E, expert_offsets, dO, a, static_cast<uint16_t*>(dw2), s))
     return W4A4_ERR_LAUNCH;
   if (cap > 0 && !launch_dgrad_fc1(cap, H, I, E, expert_offsets, dH, W1, dXp, s))
     return W4A4_ERR_LAUNCH;
-  // The dX gather-sum needs only dXp and the FC1 wgrad only dH: the gather
-  // (HBM-bound, few registers, no LDS) runs on the side stream beside the
-  // wgrad (MFMA-bound), and the caller's stream waits for both.
-  std::lock_guard<std::mutex> lock(side_mutex());
-  SideStream side;
-  if (!side_stream(side)) return fail(W4A4_ERR_LAUNCH, "side stream / events could not be created");
-  if (hipEventRecord(side.fork, s) != hipSuccess || hipStreamWaitEvent(side.stream, side.fork, 0) != hipSuccess)
-    return fail(W4A4_ERR_LAUNCH, "fork to the side stream failed");
+  if (!join(0) || !fork(1)) return fail(W4A4_ERR_LAUNCH, "side stream fork / join failed");
   if (!launch_wgrad_fc1(H, I, E, expert_offsets, dH, xp, static_cast<uint16_t*>(dw1), s))
     return W4A4_ERR_LAUNCH;
   if (!launch_gather_sum(T, H, k, dXp, row_map, static_cast<uint16_t*>(dx), side.stream))
     return W4A4_ERR_LAUNCH;
-  if (hipEventRecord(side.join, side.stream) != hipSuccess || hipStreamWaitEvent(s, side.join, 0) != hipSuccess)
-    return fail(W4A4_ERR_LAUNCH, "join from the side stream failed");
+  if (!join(1)) return fail(W4A4_ERR_LAUNCH, "join from the side stream failed");
   return W4A4_OK;
 }
 

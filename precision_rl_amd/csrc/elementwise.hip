@@ -1,7 +1,7 @@
 // HBM-bound gathers of the expert path (gfx950):
 //   unpermute:     y[t]  = bf16( sum_j p[t,j] * o[row_map[t,j]] )
 //   gather-sum:    dX[t] = bf16( sum_j dXp[row_map[t,j]] )
-//   scatter:       dO[row_map[t,j]] = bf16( p[t,j] * dY[t] ),  xp[row_map[t,j]] = x[t]
+//   scatter:       dO[row_map[t,j]] = bf16( p[t,j] * dY[t] );  xp[row_map[t,j]] = x[t]
 // The router coefficients enter in the unpermute, on the bf16 expert outputs,
 // summed in FP32 in ascending j (a reading of the pages, which name the
 // router-coefficient position as a choice the execution specification must fix:
@@ -54,13 +54,15 @@ gather_sum_kernel(int H, int k, const uint16_t* __restrict__ src, const int32_t*
   }
 }
 
-// One workgroup per token t: dY[t] and x[t] are read once and written, dY
-// scaled by the router weight, to each of the token's k dispatched rows.
-// Token order keeps the reads sequential; the writes are whole rows.
+// One workgroup per token t.  DY: dY[t] is read once and written, scaled by
+// the router weight, to each of the token's k dispatched rows of dO.  X: x[t]
+// is read once and copied to the token's k rows of xp.  Token order keeps the
+// reads sequential; the writes are whole rows.  The two run as separate
+// kernels: dO is needed first, xp only by the last GEMM.
+template <bool DY>
 __global__ void __launch_bounds__(kThreads)
-scatter_kernel(int H, int k, const uint16_t* __restrict__ dy, const uint16_t* __restrict__ x,
-               const int32_t* __restrict__ row_map, const float* __restrict__ w,
-               uint16_t* __restrict__ dO, uint16_t* __restrict__ xp) {
+scatter_kernel(int H, int k, const uint16_t* __restrict__ src, const int32_t* __restrict__ row_map,
+               const float* __restrict__ w, uint16_t* __restrict__ dst) {
   const int64_t t = blockIdx.x;
   int32_t rows[16];
   float ps[16];
@@ -68,38 +70,36 @@ scatter_kernel(int H, int k, const uint16_t* __restrict__ dy, const uint16_t* __
   for (int j = 0; j < 16; ++j) {
     if (j < k) {
       rows[j] = row_map[t * k + j];
-      ps[j] = w[t * k + j];
+      if constexpr (DY) ps[j] = w[t * k + j];
     }
   }
   for (int c = threadIdx.x; c < H / 8; c += kThreads) {
-    const u32x4_t g = *reinterpret_cast<const u32x4_t*>(dy + t * H + c * 8);
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(x + t * H + c * 8);
+    const u32x4_t g = *reinterpret_cast<const u32x4_t*>(src + t * H + c * 8);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       if (j < k) {
-        u32x4_t o;
+        u32x4_t o = g;
+        if constexpr (DY) {
 #pragma unroll
-        for (int d = 0; d < 4; ++d)
-          o[d] = pack_bf16x2(ps[j] * bf16_to_f32(static_cast<uint16_t>(g[d] & 0xFFFFu)),
-                             ps[j] * bf16_to_f32(static_cast<uint16_t>(g[d] >> 16)));
+          for (int d = 0; d < 4; ++d)
+            o[d] = pack_bf16x2(ps[j] * bf16_to_f32(static_cast<uint16_t>(g[d] & 0xFFFFu)),
+                               ps[j] * bf16_to_f32(static_cast<uint16_t>(g[d] >> 16)));
+        }
         const int64_t r = rows[j];
-        *reinterpret_cast<u32x4_t*>(dO + r * H + c * 8) = o;
-        *reinterpret_cast<u32x4_t*>(xp + r * H + c * 8) = v;
+        *reinterpret_cast<u32x4_t*>(dst + r * H + c * 8) = o;
       }
     }
   }
 }
 
-// Pad rows (src_row < 0, rows [0, offsets[E])) of dO and xp: zeros.
+// Pad rows (src_row < 0, rows [0, offsets[E])) of a [rows, H] bf16 buffer: zeros.
 __global__ void __launch_bounds__(kThreads)
 zero_pad_rows_kernel(int H, const int32_t* __restrict__ src_row, const int32_t* __restrict__ offsets,
-                     int E, uint16_t* __restrict__ dO, uint16_t* __restrict__ xp) {
+                     int E, uint16_t* __restrict__ dst) {
   const int64_t r = blockIdx.x;
   if (r >= offsets[E] || src_row[r] >= 0) return;
-  for (int c = threadIdx.x; c < H / 8; c += kThreads) {
-    *reinterpret_cast<u32x4_t*>(dO + r * H + c * 8) = u32x4_t{0u, 0u, 0u, 0u};
-    *reinterpret_cast<u32x4_t*>(xp + r * H + c * 8) = u32x4_t{0u, 0u, 0u, 0u};
-  }
+  for (int c = threadIdx.x; c < H / 8; c += kThreads)
+    *reinterpret_cast<u32x4_t*>(dst + r * H + c * 8) = u32x4_t{0u, 0u, 0u, 0u};
 }
 
 }  // namespace
@@ -126,25 +126,33 @@ bool launch_gather_sum(int64_t T, int H, int k, const uint16_t* dXp, const int32
   return launch_ok("dx_gather_sum");
 }
 
-bool launch_scatter(int64_t T, int H, int k, const uint16_t* dy, const uint16_t* x,
-                    const int32_t* row_map, const float* topk_w, uint16_t* dO, uint16_t* xp,
-                    hipStream_t s) {
+bool launch_scatter_dy(int64_t T, int H, int k, const uint16_t* dy, const int32_t* row_map,
+                       const float* topk_w, uint16_t* dO, hipStream_t s) {
   if (T == 0) return true;
   {
-    ProfScope p("dy_x_scatter", s);
-    scatter_kernel<<<dim3(static_cast<unsigned>(T)), dim3(kThreads), 0, s>>>(H, k, dy, x, row_map, topk_w,
-                                                                             dO, xp);
+    ProfScope p("dy_scatter", s);
+    scatter_kernel<true><<<dim3(static_cast<unsigned>(T)), dim3(kThreads), 0, s>>>(H, k, dy, row_map, topk_w, dO);
   }
-  return launch_ok("dy_x_scatter");
+  return launch_ok("dy_scatter");
+}
+
+bool launch_scatter_x(int64_t T, int H, int k, const uint16_t* x, const int32_t* row_map, uint16_t* xp,
+                      hipStream_t s) {
+  if (T == 0) return true;
+  {
+    ProfScope p("x_scatter", s);
+    scatter_kernel<false><<<dim3(static_cast<unsigned>(T)), dim3(kThreads), 0, s>>>(H, k, x, row_map, nullptr, xp);
+  }
+  return launch_ok("x_scatter");
 }
 
 bool launch_zero_pad_rows(int64_t rows_alloc, int H, const int32_t* src_row, const int32_t* offsets,
-                          int E, uint16_t* dO, uint16_t* xp, hipStream_t s) {
+                          int E, uint16_t* dst, hipStream_t s) {
   if (rows_alloc == 0) return true;
   {
     ProfScope p("zero_pad_rows", s);
     zero_pad_rows_kernel<<<dim3(static_cast<unsigned>(rows_alloc)), dim3(kThreads), 0, s>>>(
-        H, src_row, offsets, E, dO, xp);
+        H, src_row, offsets, E, dst);
   }
   return launch_ok("zero_pad_rows");
 }

@@ -59,14 +59,15 @@ bool launch_fc2(int64_t rows_alloc, int H, int I, int E, const int32_t* offsets,
 bool launch_unpermute(int64_t T, int H, int k, const uint16_t* o, const int32_t* row_map,
                       const float* topk_w, uint16_t* y, hipStream_t s);
 
-// Token-order scatter of the backward's row operands: for each token t and
-// slot j, dO[row_map[t,j]] = bf16(p[t,j] dY[t]) and xp[row_map[t,j]] = x[t].
-bool launch_scatter(int64_t T, int H, int k, const uint16_t* dy, const uint16_t* x,
-                    const int32_t* row_map, const float* topk_w, uint16_t* dO, uint16_t* xp,
-                    hipStream_t s);
-// Zeros in the pad rows (src_row < 0) of dO and xp.
+// Token-order scatters of the backward's row operands: for each token t and
+// slot j, dO[row_map[t,j]] = bf16(p[t,j] dY[t]), resp. xp[row_map[t,j]] = x[t].
+bool launch_scatter_dy(int64_t T, int H, int k, const uint16_t* dy, const int32_t* row_map,
+                       const float* topk_w, uint16_t* dO, hipStream_t s);
+bool launch_scatter_x(int64_t T, int H, int k, const uint16_t* x, const int32_t* row_map, uint16_t* xp,
+                      hipStream_t s);
+// Zeros in the pad rows (src_row < 0) of a [rows, H] bf16 buffer (dO or xp).
 bool launch_zero_pad_rows(int64_t rows_alloc, int H, const int32_t* src_row, const int32_t* offsets,
-                          int E, uint16_t* dO, uint16_t* xp, hipStream_t s);
+                          int E, uint16_t* dst, hipStream_t s);
 
 // FC2 dgrad with the SwiGLU backward fused: dA = bf16(dO_e W2[e]) then the SwiGLU backward -> dH.
 bool launch_dgrad_fc2(int64_t rows_alloc, int H, int I, int E, const int32_t* offsets,
