@@ -156,19 +156,16 @@ w4a4_status check_moe_shape(int64_t T, int H, int I, int E, int k, int row_align
 
 }  // namespace
 
-void prof_begin(const char* name, hipStream_t s) {
+ProfEvents prof_events(const char* name) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  if (!g_prof_on) return;
+  ProfEvents ev;
+  if (!g_prof_on) return ev;
   ProfEntry e{name, prof_event(), prof_event()};
-  if (!e.start || !e.stop) return;
-  (void)hipEventRecord(e.start, s);
+  if (!e.start || !e.stop) return ev;
   g_prof_entries.push_back(e);
-}
-
-void prof_end(hipStream_t s) {
-  std::lock_guard<std::mutex> lk(g_prof_mu);
-  if (!g_prof_on || g_prof_entries.empty()) return;
-  (void)hipEventRecord(g_prof_entries.back().stop, s);
+  ev.start = e.start;
+  ev.stop = e.stop;
+  return ev;
 }
 
 bool launch_ok(const char* what) {

@@ -107,53 +107,40 @@ zero_pad_rows_kernel(int H, const int32_t* __restrict__ src_row, const int32_t* 
 bool launch_unpermute(int64_t T, int H, int k, const uint16_t* o, const int32_t* row_map,
                       const float* topk_w, uint16_t* y, hipStream_t s) {
   if (T == 0) return true;
-  {
-    ProfScope p("unpermute", s);
-    gather_sum_kernel<<<dim3(static_cast<unsigned>(T)), dim3(kThreads), 0, s>>>(H, k, o, row_map,
-                                                                                topk_w, y);
-  }
+  launch_kernel("unpermute", gather_sum_kernel, dim3(static_cast<unsigned>(T)), dim3(kThreads), 0, s, H, k, o,
+                row_map, topk_w, y);
   return launch_ok("unpermute");
 }
 
 bool launch_gather_sum(int64_t T, int H, int k, const uint16_t* dXp, const int32_t* row_map,
                        uint16_t* dx, hipStream_t s) {
   if (T == 0) return true;
-  {
-    ProfScope p("dx_gather_sum", s);
-    gather_sum_kernel<<<dim3(static_cast<unsigned>(T)), dim3(kThreads), 0, s>>>(H, k, dXp, row_map,
-                                                                                nullptr, dx);
-  }
+  launch_kernel("dx_gather_sum", gather_sum_kernel, dim3(static_cast<unsigned>(T)), dim3(kThreads), 0, s, H, k,
+                dXp, row_map, static_cast<const float*>(nullptr), dx);
   return launch_ok("dx_gather_sum");
 }
 
 bool launch_scatter_dy(int64_t T, int H, int k, const uint16_t* dy, const int32_t* row_map,
                        const float* topk_w, uint16_t* dO, hipStream_t s) {
   if (T == 0) return true;
-  {
-    ProfScope p("dy_scatter", s);
-    scatter_kernel<true><<<dim3(static_cast<unsigned>(T)), dim3(kThreads), 0, s>>>(H, k, dy, row_map, topk_w, dO);
-  }
+  launch_kernel("dy_scatter", scatter_kernel<true>, dim3(static_cast<unsigned>(T)), dim3(kThreads), 0, s, H, k,
+                dy, row_map, topk_w, dO);
   return launch_ok("dy_scatter");
 }
 
 bool launch_scatter_x(int64_t T, int H, int k, const uint16_t* x, const int32_t* row_map, uint16_t* xp,
                       hipStream_t s) {
   if (T == 0) return true;
-  {
-    ProfScope p("x_scatter", s);
-    scatter_kernel<false><<<dim3(static_cast<unsigned>(T)), dim3(kThreads), 0, s>>>(H, k, x, row_map, nullptr, xp);
-  }
+  launch_kernel("x_scatter", scatter_kernel<false>, dim3(static_cast<unsigned>(T)), dim3(kThreads), 0, s, H, k,
+                x, row_map, static_cast<const float*>(nullptr), xp);
   return launch_ok("x_scatter");
 }
 
 bool launch_zero_pad_rows(int64_t rows_alloc, int H, const int32_t* src_row, const int32_t* offsets,
                           int E, uint16_t* dst, hipStream_t s) {
   if (rows_alloc == 0) return true;
-  {
-    ProfScope p("zero_pad_rows", s);
-    zero_pad_rows_kernel<<<dim3(static_cast<unsigned>(rows_alloc)), dim3(kThreads), 0, s>>>(
-        H, src_row, offsets, E, dst);
-  }
+  launch_kernel("zero_pad_rows", zero_pad_rows_kernel, dim3(static_cast<unsigned>(rows_alloc)), dim3(kThreads), 0,
+                s, H, src_row, offsets, E, dst);
   return launch_ok("zero_pad_rows");
 }
 

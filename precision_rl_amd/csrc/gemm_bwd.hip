@@ -675,10 +675,7 @@ bool launch_dgrad(const dg::DgradArgs& a, const char* name, hipStream_t s) {
   if (attr != hipSuccess) return launch_ok(name) && false;
   const int64_t tiles = grouped_m_tiles_bound(a.rows_alloc, a.E, dg::kBM) * ((a.N + dg::kBN - 1) / dg::kBN);
   if (tiles == 0) return true;
-  {
-    ProfScope p(name, s);
-    dg::dgrad_kernel<MODE><<<dim3(xcd_grid(tiles)), dim3(dg::kThreads), dg::kLdsBytes, s>>>(a);
-  }
+  launch_kernel(name, dg::dgrad_kernel<MODE>, dim3(xcd_grid(tiles)), dim3(dg::kThreads), dg::kLdsBytes, s, a);
   return launch_ok(name);
 }
 
@@ -687,10 +684,7 @@ bool launch_wgrad(const wg::WgradArgs& a, const char* name, hipStream_t s) {
   if (attr != hipSuccess) return launch_ok(name) && false;
   const int64_t tiles = static_cast<int64_t>(a.E) * (a.M / wg::kBM) * ((a.N + wg::kBN - 1) / wg::kBN);
   if (tiles == 0) return true;
-  {
-    ProfScope p(name, s);
-    wg::wgrad_kernel<<<dim3(persistent_grid(tiles)), dim3(wg::kThreads), wg::kLdsBytes, s>>>(a);
-  }
+  launch_kernel(name, wg::wgrad_kernel, dim3(persistent_grid(tiles)), dim3(wg::kThreads), wg::kLdsBytes, s, a);
   return launch_ok(name);
 }
 

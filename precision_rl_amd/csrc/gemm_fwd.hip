@@ -429,10 +429,8 @@ bool launch_fwd_variant(const FwdArgs& args, int64_t tiles, const char* name, hi
       reinterpret_cast<const void*>(&fwd_gemm_kernel<MODE, GS>),
       hipFuncAttributeMaxDynamicSharedMemorySize, FwdLds<GS>::kBytes);
   if (attr != hipSuccess) return launch_ok(name) && false;
-  {
-    ProfScope p(name, s);
-    fwd_gemm_kernel<MODE, GS><<<dim3(xcd_grid(tiles)), dim3(kThreads), FwdLds<GS>::kBytes, s>>>(args);
-  }
+  launch_kernel(name, fwd_gemm_kernel<MODE, GS>, dim3(xcd_grid(tiles)), dim3(kThreads), FwdLds<GS>::kBytes, s,
+                args);
   return launch_ok(name);
 }
 

@@ -639,11 +639,8 @@ bool launch_rows(const char* name, const uint16_t* x, int64_t n_rows, int K, con
     const int64_t need = (n_rows + rows_per_block - 1) / rows_per_block;
     const int64_t blocks = std::min<int64_t>(need, 256 * 16);
     if (blocks == 0) return true;
-    {
-      ProfScope p(name, s);
-      quant_rows_kernel<TEAM, PB, MODE><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s>>>(
-          x, n_rows, K, topk_idx, k, E, codes, scales, outer, offsets, row_map, src_row, chunk_base);
-    }
+    launch_kernel(name, quant_rows_kernel<TEAM, PB, MODE>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                  s, x, n_rows, K, topk_idx, k, E, codes, scales, outer, offsets, row_map, src_row, chunk_base);
     return launch_ok(name);
   };
   // One block pair per lane in a team that covers the row (a wave then
@@ -692,27 +689,18 @@ bool launch_quantize_permute(const uint16_t* x, int64_t T, int K, const int32_t*
   int32_t* counts = static_cast<int32_t*>(ws);
   int32_t* expert_count = counts + n_chunks * E;
   if (T == 0) {  // nothing routed: every group is empty
-    {
-      ProfScope p("route_scan", s);
-      zero_offsets_kernel<<<1, 256, 0, s>>>(offsets, E + 1);
-    }
+    launch_kernel("route_scan", zero_offsets_kernel, dim3(1), dim3(256), 0, s, offsets, E + 1);
     return launch_ok("zero_offsets");
   }
   if (topk_idx != nullptr) {
-    {
-      ProfScope p("route_count", s);
-      size_t lds = static_cast<size_t>(E) * (kRouteChunk / 32) * sizeof(uint32_t);
-      route_count_kernel<<<dim3(static_cast<unsigned>(n_chunks)), dim3(kRouteChunk), lds, s>>>(
-          topk_idx, T, k, E, row_map, counts);
-    }
+    const uint32_t lds = static_cast<uint32_t>(E) * (kRouteChunk / 32) * sizeof(uint32_t);
+    launch_kernel("route_count", route_count_kernel, dim3(static_cast<unsigned>(n_chunks)), dim3(kRouteChunk), lds,
+                  s, topk_idx, T, k, E, row_map, counts);
     if (!launch_ok("route_count")) return false;
   }
   if (topk_idx != nullptr) {
-    {
-      ProfScope p("route_scan", s);
-      route_scan_kernel<<<1, kScanThreads, 0, s>>>(counts, static_cast<int>(n_chunks), E, row_align,
-                                                    offsets, expert_count);
-    }
+    launch_kernel("route_scan", route_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, counts,
+                  static_cast<int>(n_chunks), E, row_align, offsets, expert_count);
     if (!launch_ok("route_scan")) return false;
   }
   if (rows_path(K)) {
@@ -723,11 +711,8 @@ bool launch_quantize_permute(const uint16_t* x, int64_t T, int K, const int32_t*
                                          offsets, row_map, src_row, nullptr, s);
     if (!ok) return false;
     if (topk_idx != nullptr && row_align > 1) {
-      {
-        ProfScope p("pad_rows", s);
-        pad_rows_kernel<<<dim3(static_cast<unsigned>((E + kWavesPerBlock - 1) / kWavesPerBlock)), dim3(kThreads),
-                          0, s>>>(K, E, offsets, expert_count, codes, scales, outer, src_row);
-      }
+      launch_kernel("pad_rows", pad_rows_kernel, dim3(static_cast<unsigned>((E + kWavesPerBlock - 1) / kWavesPerBlock)),
+                    dim3(kThreads), 0, s, K, E, offsets, expert_count, codes, scales, outer, src_row);
       return launch_ok("pad_rows");
     }
     return true;
@@ -738,13 +723,9 @@ bool launch_quantize_permute(const uint16_t* x, int64_t T, int K, const int32_t*
   const int64_t blocks = token_blocks + pad_blocks;
   if (blocks == 0) return true;
   return dispatch_maxb(K, [&](auto mb) {
-    {
-      ProfScope p("quantize_scatter", s);
-      quantize_scatter_kernel<decltype(mb)::value>
-          <<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s>>>(
-              x, T, K, topk_idx, k, E, row_align, codes, scales, outer, offsets, row_map,
-              src_row, counts, expert_count, token_blocks);
-    }
+    launch_kernel("quantize_scatter", quantize_scatter_kernel<decltype(mb)::value>,
+                  dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, x, T, K, topk_idx, k, E, row_align,
+                  codes, scales, outer, offsets, row_map, src_row, counts, expert_count, token_blocks);
     return launch_ok("quantize_scatter");
   });
 }
@@ -758,11 +739,8 @@ bool launch_requant(const uint16_t* a, int64_t rows_alloc, int K, const int32_t*
   const int64_t blocks = (rows_alloc + kWavesPerBlock - 1) / kWavesPerBlock;
   if (blocks == 0) return true;
   return dispatch_maxb(K, [&](auto mb) {
-    {
-      ProfScope p("requant", s);
-      requant_kernel<decltype(mb)::value><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s>>>(
-          a, rows_alloc, K, offsets, E, codes, scales, outer);
-    }
+    launch_kernel("requant", requant_kernel<decltype(mb)::value>, dim3(static_cast<unsigned>(blocks)),
+                  dim3(kThreads), 0, s, a, rows_alloc, K, offsets, E, codes, scales, outer);
     return launch_ok("requant");
   });
 }
