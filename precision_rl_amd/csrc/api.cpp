@@ -168,6 +168,17 @@ ProfEvents prof_events(const char* name) {
   return ev;
 }
 
+int device_cu_count() {
+  static const int n = [] {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    return cus;
+  }();
+  return n;
+}
+
 bool launch_ok(const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {

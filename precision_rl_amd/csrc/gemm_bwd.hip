@@ -645,21 +645,10 @@ wgrad_kernel(WgradArgs args) {
 
 }  // namespace wg
 
-int cu_count() {
-  static const int n = [] {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-    return cus;
-  }();
-  return n;
-}
-
 // Persistent grid: one workgroup per CU (a multiple of the XCD count), or
 // fewer when there are fewer tiles.
 unsigned persistent_grid(int64_t tiles) {
-  const int64_t cap = std::max<int64_t>(kXcds, cu_count() / kXcds * kXcds);
+  const int64_t cap = std::max<int64_t>(kXcds, device_cu_count() / kXcds * kXcds);
   return xcd_grid(std::min<int64_t>(tiles, cap));
 }
 

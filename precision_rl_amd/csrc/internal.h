@@ -32,6 +32,9 @@ inline void launch_kernel(const char* name, void (*kernel)(Params...), dim3 grid
 // Records the HIP error of the last launch; returns false on failure.
 bool launch_ok(const char* what);
 
+// Compute units of the current device (queried once).
+int device_cu_count();
+
 // ------------------------------------------------------------ routing / quant
 constexpr int kRouteChunk = 256;      // tokens per routing chunk (one workgroup)
 

@@ -635,9 +635,12 @@ bool launch_rows(const char* name, const uint16_t* x, int64_t n_rows, int K, con
   auto go = [&](auto team, auto pb) {
     constexpr int TEAM = decltype(team)::value, PB = decltype(pb)::value;
     constexpr int rows_per_block = kWavesPerBlock * (kWave / TEAM);
-    // enough workgroups to fill the chip twice over; each wave then loops
+    // Up to 16 workgroups per CU: at the workloads' sizes every wave takes one
+    // row group, and the waves that wait on memory are many (a grid sized to
+    // the resident waves, each striding over several row groups, measured
+    // slower); larger inputs make the waves stride.
     const int64_t need = (n_rows + rows_per_block - 1) / rows_per_block;
-    const int64_t blocks = std::min<int64_t>(need, 256 * 16);
+    const int64_t blocks = std::min<int64_t>(need, static_cast<int64_t>(device_cu_count()) * 16);
     if (blocks == 0) return true;
     launch_kernel(name, quant_rows_kernel<TEAM, PB, MODE>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
                   s, x, n_rows, K, topk_idx, k, E, codes, scales, outer, offsets, row_map, src_row, chunk_base);
