@@ -5,7 +5,8 @@
 // The router coefficients enter in the unpermute, on the bf16 expert outputs,
 // summed in FP32 in ascending j (a reading of the pages, which name the
 // router-coefficient position as a choice the execution specification must fix:
-// AI summary, "Methodology in Plain English").  All loads and stores are 16 B.
+// AI summary, "Methodology in Plain English").  All loads and stores are 16 B
+// and non-temporal (every row is touched once).
 
 #include "device_common.h"
 #include "internal.h"
@@ -43,14 +44,15 @@ gather_sum_kernel(int H, int k, const uint16_t* __restrict__ src, const int32_t*
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       if (j < k) {
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(src + static_cast<int64_t>(rows[j]) * H + c * 8);
+        const u32x4_t v = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4_t*>(src + static_cast<int64_t>(rows[j]) * H + c * 8));
         acc_bf16x8(acc, v, ws[j]);
       }
     }
     u32x4_t o;
 #pragma unroll
     for (int d = 0; d < 4; ++d) o[d] = pack_bf16x2(acc[2 * d], acc[2 * d + 1]);
-    *reinterpret_cast<u32x4_t*>(out + t * H + c * 8) = o;
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(out + t * H + c * 8));
   }
 }
 
@@ -86,7 +88,9 @@ scatter_kernel(int H, int k, const uint16_t* __restrict__ src, const int32_t* __
                                ps[j] * bf16_to_f32(static_cast<uint16_t>(g[d] >> 16)));
         }
         const int64_t r = rows[j];
-        *reinterpret_cast<u32x4_t*>(dst + r * H + c * 8) = o;
+        // non-temporal: the next kernel reads dO / xp from HBM anyway, and
+        // dirty lines left in L2 cost the FC2 dgrad more than they save here
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(dst + r * H + c * 8));
       }
     }
   }
