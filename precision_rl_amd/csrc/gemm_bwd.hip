@@ -325,36 +325,64 @@ dgrad_kernel(DgradArgs args) {
   __syncthreads();
   const int rows = static_cast<int>(min<int64_t>(kBM, tc.m_end - tc.m0));
   constexpr int kChunksPerRow = kBN / 8;
-  for (int c = tid; c < kBM * kChunksPerRow; c += kThreads) {
-    const int lrow = c / kChunksPerRow, n = n0 + (c % kChunksPerRow) * 8;
-    if (lrow >= rows || n >= args.N) continue;
-    const int64_t row = tc.m0 + lrow;
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(lds + lrow * kOutPitch + (n - n0) * 2);
-    if constexpr (MODE == DgradMode::FC1) {
-      __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(args.out + row * args.N + n));
-    } else {
-      // SwiGLU backward on bf16 dA, gate / up from the saved bf16 h
-      const int I = args.I;
-      const u32x4_t hg = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(args.h + row * (2 * I) + n));
-      const u32x4_t hu = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(args.h + row * (2 * I) + I + n));
-      u32x4_t dg, du;
+  constexpr int kIters = kBM * kChunksPerRow / kThreads;   // 16-byte chunks per thread
+  static_assert(kBM * kChunksPerRow % kThreads == 0, "whole chunks per thread");
+  if constexpr (MODE == DgradMode::FC1) {
+#pragma unroll 4
+    for (int it = 0; it < kIters; ++it) {
+      const int c = tid + it * kThreads;
+      const int lrow = c / kChunksPerRow, n = n0 + (c % kChunksPerRow) * 8;
+      if (lrow >= rows || n >= args.N) continue;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(lds + lrow * kOutPitch + (n - n0) * 2);
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(args.out + (tc.m0 + lrow) * args.N + n));
+    }
+  } else {
+    // SwiGLU backward on bf16 dA, gate / up from the saved bf16 h.  The h
+    // loads of eight chunks go out together (the accumulators are staged,
+    // so registers are free), then the eight are computed and stored.
+    const int I = args.I;
+    constexpr int kBatch = 8;
+    static_assert(kIters % kBatch == 0, "whole batches");
+#pragma unroll 1
+    for (int b0 = 0; b0 < kIters; b0 += kBatch) {
+      u32x4_t hg[kBatch], hu[kBatch];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        float rg[2], ru[2];
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const float da = bf16_to_f32(static_cast<uint16_t>(v[d] >> (16 * p)));
-          const float gt = bf16_to_f32(static_cast<uint16_t>(hg[d] >> (16 * p)));
-          const float up = bf16_to_f32(static_cast<uint16_t>(hu[d] >> (16 * p)));
-          const float sg = sigmoid_fast(gt);
-          rg[p] = da * up * sg * (1.0f + gt * (1.0f - sg));
-          ru[p] = da * gt * sg;
-        }
-        dg[d] = pack_bf16x2(rg[0], rg[1]);
-        du[d] = pack_bf16x2(ru[0], ru[1]);
+      for (int i = 0; i < kBatch; ++i) {
+        // unconditional (clamped to the tile's last row and the last column
+        // chunk, both valid) so that no lane mask splits the batch
+        const int c = tid + (b0 + i) * kThreads;
+        const int lrow = min(c / kChunksPerRow, rows - 1);
+        const int n = min(n0 + (c % kChunksPerRow) * 8, args.N - 8);
+        const uint16_t* hr = args.h + (tc.m0 + lrow) * (2 * I) + n;
+        hg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(hr));
+        hu[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(hr + I));
       }
-      __builtin_nontemporal_store(dg, reinterpret_cast<u32x4_t*>(args.out + row * (2 * I) + n));
-      __builtin_nontemporal_store(du, reinterpret_cast<u32x4_t*>(args.out + row * (2 * I) + I + n));
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int c = tid + (b0 + i) * kThreads;
+        const int lrow = c / kChunksPerRow, n = n0 + (c % kChunksPerRow) * 8;
+        if (lrow >= rows || n >= args.N) continue;
+        const int64_t row = tc.m0 + lrow;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(lds + lrow * kOutPitch + (n - n0) * 2);
+        u32x4_t dg, du;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          float rg[2], ru[2];
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            const float da = bf16_to_f32(static_cast<uint16_t>(v[d] >> (16 * p)));
+            const float gt = bf16_to_f32(static_cast<uint16_t>(hg[i][d] >> (16 * p)));
+            const float up = bf16_to_f32(static_cast<uint16_t>(hu[i][d] >> (16 * p)));
+            const float sg = sigmoid_fast(gt);
+            rg[p] = da * up * sg * (1.0f + gt * (1.0f - sg));
+            ru[p] = da * gt * sg;
+          }
+          dg[d] = pack_bf16x2(rg[0], rg[1]);
+          du[d] = pack_bf16x2(ru[0], ru[1]);
+        }
+        __builtin_nontemporal_store(dg, reinterpret_cast<u32x4_t*>(args.out + row * (2 * I) + n));
+        __builtin_nontemporal_store(du, reinterpret_cast<u32x4_t*>(args.out + row * (2 * I) + I + n));
+      }
     }
   }
 }
