@@ -244,8 +244,28 @@ fwd_gemm_kernel(FwdArgs args) {
   };
 
   // outer scales of the tile's rows, read by the epilogue
-  float* s_gx = reinterpret_cast<float*>(lds + L::kGx);
-  if (tid < kBM) s_gx[tid] = args.a.outer[tc.m0 + min(tid, a_rows - 1)];
+  // outer scales of the tile's rows (written to LDS after the main loop, for
+  // the epilogue: loading them now and waiting then keeps the load's latency
+  // out of the tile's start)
+  const float gx_row = args.a.outer[tc.m0 + min(tid % kBM, a_rows - 1)];
+  // and this lane's four weight outer scales (its output columns: FC2 four
+  // consecutive n; FC1 the gate and up halves of two features), loaded here
+  // so that the epilogue does not wait for them
+  float gw[4];
+  {
+    const float* wouter = args.w.outer + static_cast<int64_t>(tc.e) * args.N;
+    if constexpr (MODE == FwdMode::FC2) {
+      const int n = tc.n_tile * kBN + wn * kWN + 4 * r32;
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) gw[ni] = wouter[n + ni];
+    } else {
+      const int i = tc.n_tile * 128 + wn * 64 + 2 * r32;
+      gw[0] = wouter[i];
+      gw[1] = wouter[i + 1];
+      gw[2] = wouter[args.I + i];
+      gw[3] = wouter[args.I + i + 1];
+    }
+  }
 
   floatx16_t acc[2][4];
 #pragma unroll
@@ -323,7 +343,9 @@ fwd_gemm_kernel(FwdArgs args) {
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  __syncthreads();   // s_gx visible (written before the loop; every wave passed a barrier since)
+  float* s_gx = reinterpret_cast<float*>(lds + L::kGx);
+  if (tid < kBM) s_gx[tid] = gx_row;
+  __syncthreads();   // s_gx visible; every wave is past its last read of the ring
 
   // ---------------------------------------------------------------- epilogue
   // The tile leaves in two rounds of 64 rows (MFMA row block mi = q of both
@@ -332,14 +354,10 @@ fwd_gemm_kernel(FwdArgs args) {
   // tile row (s / 32) * 64 + 32 q + s % 32.  FC1 stages h (gate half, then up
   // half, 128 features each) and computes the SwiGLU on the staged bf16 values
   // while storing.
-  const float* wouter = args.w.outer + static_cast<int64_t>(tc.e) * args.N;
   uint8_t* so = lds;
   auto tile_row = [&](int s, int q) { return (s >> 5) * kWM + 32 * q + (s & 31); };
   if constexpr (MODE == FwdMode::FC2) {
     const int n_loc = wn * kWN + 4 * r32;
-    float gw[4];
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) gw[ni] = wouter[tc.n_tile * kBN + n_loc + ni];
     uint16_t* out = args.out + tc.n_tile * kBN;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -368,8 +386,7 @@ fwd_gemm_kernel(FwdArgs args) {
     const int I = args.I;
     const int i_loc = wn * 64 + 2 * r32;
     const int i = tc.n_tile * 128 + i_loc;
-    const float gw_g0 = wouter[i], gw_g1 = wouter[i + 1];
-    const float gw_u0 = wouter[I + i], gw_u1 = wouter[I + i + 1];
+    const float gw_g0 = gw[0], gw_g1 = gw[1], gw_u0 = gw[2], gw_u1 = gw[3];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       if (q > 0) __syncthreads();   // previous round's reads done
