@@ -302,3 +302,45 @@ def test_full_skew_workload_sampled():
     assert rel_l2(bf16_host(run.g["dw2"][small]), rb["dW2"][0]) <= BWD_TOL
     for e in empty:
         assert not run.g["dw1"][e].any() and not run.g["dw2"][e].any()
+
+
+def test_backward_concurrent_calls_on_two_streams():
+    """Two host threads run the backward at the same time on two streams with
+    their own workspaces (the library's second stream and its fork / join
+    events are shared, under a lock).  Each result equals the sequential one
+    bit for bit; the second thread's dy is 2 dy, so its results are exactly
+    twice the first's (a power-of-two scale commutes with every rounding)."""
+    import threading
+    b = _binding()
+    T, H, E, k, I = 1500, 512, 12, 4, 256
+    d = synth.make_inputs(T, H, E, k, I, routing="zipf", backward=True, seed=77, n_empty=2)
+    print_case("backward_two_streams", T=T, H=H, E=E, k=k, I=I)
+    run = Run(d, T, H, E, k, I, A=16, backward=True)
+    ref = {n: v.clone() for n, v in run.g.items()}
+    dys = [run.dy, run.dy * 2]
+    torch.cuda.synchronize()   # inputs and the reference complete before the side streams start
+    outs = [[], []]
+    errors = []
+
+    def worker(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for _ in range(3):
+                    outs[i].append(b.w4a4_expert_bwd(dys[i], run.x, run.w1, run.w2, run.f["h"], run.f["a"],
+                                                     run.p, run.xq, T, H, I, E, k, 16))
+            s.synchronize()
+        except Exception as e:   # surfaced below
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i, scale in ((0, 1.0), (1, 2.0)):
+        for g in outs[i]:
+            for n in ("dx", "dw1", "dw2"):
+                assert torch.equal(g[n], ref[n] * scale), (i, n)
