@@ -344,3 +344,44 @@ def test_backward_concurrent_calls_on_two_streams():
         for g in outs[i]:
             for n in ("dx", "dw1", "dw2"):
                 assert torch.equal(g[n], ref[n] * scale), (i, n)
+
+
+def test_graph_capture_of_a_learner_step():
+    """quantize+permute, forward and backward captured in one HIP graph (the
+    backward's second stream joins the capture through its fork / join
+    events) and replayed three times with eager work between the replays:
+    every replay equals the eager step bit for bit."""
+    b = _binding()
+    T, H, E, k, I = 700, 512, 8, 2, 256
+    d = synth.make_inputs(T, H, E, k, I, routing="zipf", backward=True, seed=91, n_empty=1)
+    print_case("graph_capture_step", T=T, H=H, E=E, k=k, I=I)
+    x, dy = bf16_dev(d["x"], torch), bf16_dev(d["dy"], torch)
+    idx, p = torch.from_numpy(d["topk_idx"]).cuda(), torch.from_numpy(d["topk_w"]).cuda()
+    w1, w2 = bf16_dev(d["w1"], torch), bf16_dev(d["w2"], torch)
+    w1q, w2q = b.quantize_weights(w1), b.quantize_weights(w2)
+
+    def step():
+        xq = b.w4a4_quantize_permute(x, idx, E, 16)
+        f = b.w4a4_grouped_expert_fwd(xq, p, w1q, w2q, T, H, I, E, k, 16, save=True)
+        g = b.w4a4_expert_bwd(dy, x, w1, w2, f["h"], f["a"], p, xq, T, H, I, E, k, 16)
+        return [f["y"], g["dx"], g["dw1"], g["dw2"]]
+
+    eager = [t.clone() for t in step()]
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = step()
+    for i in range(3):
+        noise = torch.randn(1 << 20, device="cuda") * 3.0   # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        del noise
+        for j, (a, e) in enumerate(zip(out, eager)):
+            assert torch.equal(a, e), (i, j)
