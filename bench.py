@@ -132,8 +132,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=6144)
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
-              "the expert path is single-GPU here, see the sharding notes in the design document.",
+        print(f"bench.py: the benchmark runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the library's expert path is single-GPU (sharding is described in the design notes).",
               file=sys.stderr)
         sys.exit(2)
 
