@@ -19,10 +19,11 @@
  *    do not depend on the other tokens of the batch (per-token scale domain).
  *  - Calls are thread-safe; concurrent calls on different streams need
  *    different workspaces.
- *  - w4a4_expert_bwd runs its dX gather-sum on a second stream of the current
- *    device (created on first use, default priority), forked from `stream`
- *    after the FC1 dgrad and joined back into it: work enqueued on `stream`
- *    after the call sees every output.
+ *  - w4a4_expert_bwd runs three of its kernels (the wgrad tile schedule, the
+ *    copy of x to the expert rows, the dX gather-sum) on a second stream of
+ *    the current device (created on first use, default priority), forked from
+ *    `stream` and joined back into it: work enqueued on `stream` after the
+ *    call sees every output.
  *
  * Data formats (miniTE Technical Report, sections 2.2 and 5.1; rainbus review
  * of the miniTE paper, "prerequisites: the NVFP4 format" and method step 4):
@@ -180,6 +181,8 @@ w4a4_status w4a4_grouped_expert_fwd(
  *   topk_w, expert_offsets, row_map, src_row as in the forward.
  *   dx [T, H], dw1 [E, 2I, H], dw2 [E, H, I] bf16 out, fully overwritten
  *   (zeros for an expert with no rows).
+ *   The workspace (W4A4_WS_BACKWARD) holds dO, dH, dXp, the expert-row copy
+ *   of x and the wgrad tile schedule, all written by the call before use.
  *   Requirements: H % 256 == 0, I % 128 == 0 (else W4A4_ERR_UNSUPPORTED).
  */
 w4a4_status w4a4_expert_bwd(

@@ -40,7 +40,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // different streams never interleave their event records and waits.
 struct SideStream {
   hipStream_t stream = nullptr;
-  hipEvent_t fork[2] = {nullptr, nullptr}, join[2] = {nullptr, nullptr};
+  static constexpr int kEvents = 3;
+  hipEvent_t fork[kEvents] = {}, join[kEvents] = {};
 };
 std::mutex& side_mutex() {
   static std::mutex mu;
@@ -54,7 +55,7 @@ bool side_stream(SideStream& out) {   // call with side_mutex() held
   if (it == per_device.end()) {
     SideStream ss;
     if (hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) != hipSuccess) return false;
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < SideStream::kEvents; ++i)
       if (hipEventCreateWithFlags(&ss.fork[i], hipEventDisableTiming) != hipSuccess ||
           hipEventCreateWithFlags(&ss.join[i], hipEventDisableTiming) != hipSuccess)
         return false;
@@ -114,11 +115,12 @@ FwdWs fwd_ws(int64_t cap, int H, int I) {
   return w;
 }
 struct BwdWs {
-  size_t dO, dH, dXp, xp, total;
+  size_t sched, dO, dH, dXp, xp, total;
 };
-BwdWs bwd_ws(int64_t cap, int H, int I) {
+BwdWs bwd_ws(int64_t cap, int H, int I, int E) {
   BwdWs w;
   size_t off = 0;
+  w.sched = off; off += round_up(wgrad_schedule_ints(H, I, E) * 4);
   w.dO = off; off += round_up(static_cast<size_t>(cap) * H * 2);
   w.dH = off; off += round_up(static_cast<size_t>(cap) * 2 * I * 2);
   w.dXp = off; off += round_up(static_cast<size_t>(cap) * H * 2);
@@ -210,7 +212,7 @@ size_t w4a4_workspace_size(int kind, int64_t T, int H, int I, int E, int k, int 
       return fwd_ws(cap, H, I).total;
     case W4A4_WS_BACKWARD:
       if (I <= 0) return 0;
-      return bwd_ws(cap, H, I).total;
+      return bwd_ws(cap, H, I, E).total;
     default:
       return 0;
   }
@@ -324,12 +326,13 @@ w4a4_status w4a4_expert_bwd(int64_t T, int H, int I, int E, int k, int row_align
     REQUIRE_PTR(topk_w); REQUIRE_PTR(row_map); REQUIRE_PTR(src_row); REQUIRE_PTR(dx);
   }
   const int64_t cap = w4a4_rows_capacity(T, k, E, row_align);
-  const BwdWs L = bwd_ws(cap, H, I);
+  const BwdWs L = bwd_ws(cap, H, I, E);
   if (workspace == nullptr || workspace_bytes < L.total)
     return fail(W4A4_ERR_WORKSPACE, "workspace needs %zu bytes", L.total);
   OPTIONAL_PTR(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int32_t* sched = reinterpret_cast<int32_t*>(ws + L.sched);
   uint16_t* dO = reinterpret_cast<uint16_t*>(ws + L.dO);
   uint16_t* dH = reinterpret_cast<uint16_t*>(ws + L.dH);
   uint16_t* dXp = reinterpret_cast<uint16_t*>(ws + L.dXp);
@@ -355,24 +358,34 @@ w4a4_status w4a4_expert_bwd(int64_t T, int H, int I, int E, int k, int row_align
     return hipEventRecord(side.join[i], side.stream) == hipSuccess &&
            hipStreamWaitEvent(s, side.join[i], 0) == hipSuccess;
   };
+  // The wgrad tile schedule (one workgroup) is computed on the side stream
+  // beside the dY scatter and the FC2 dgrad; the FC2 wgrad waits for it.
+  if (!fork(2)) return fail(W4A4_ERR_LAUNCH, "fork to the side stream failed");
+  if (!launch_wgrad_schedule(H, I, E, expert_offsets, sched, side.stream)) return W4A4_ERR_LAUNCH;
+  if (hipEventRecord(side.join[2], side.stream) != hipSuccess)
+    return fail(W4A4_ERR_LAUNCH, "event record on the side stream failed");
   if (!launch_scatter_dy(T, H, k, static_cast<const uint16_t*>(dy), row_map, topk_w, dO, s))
     return W4A4_ERR_LAUNCH;
   if (row_align > 1 && !launch_zero_pad_rows(cap, H, src_row, expert_offsets, E, dO, s))
     return W4A4_ERR_LAUNCH;
   if (cap > 0 && !launch_dgrad_fc2(cap, H, I, E, expert_offsets, dO, W2, h, dH, s)) return W4A4_ERR_LAUNCH;
   // (forked after the FC2 dgrad: beside the persistent FC2 wgrad the copy
-  // costs the GEMM little; beside the FC2 dgrad it took that kernel's slots)
+  // costs the GEMM little; beside the FC2 dgrad it took that kernel's slots.
+  // The wait for the schedule comes before the fork, so that the FC2 wgrad
+  // is dispatched first and takes its CUs before the copy does.)
+  if (hipStreamWaitEvent(s, side.join[2], 0) != hipSuccess)
+    return fail(W4A4_ERR_LAUNCH, "wait for the side stream failed");
   if (!fork(0)) return fail(W4A4_ERR_LAUNCH, "fork to the side stream failed");
   if (!launch_scatter_x(T, H, k, static_cast<const uint16_t*>(x), row_map, xp, side.stream))
     return W4A4_ERR_LAUNCH;
   if (row_align > 1 && !launch_zero_pad_rows(cap, H, src_row, expert_offsets, E, xp, side.stream))
     return W4A4_ERR_LAUNCH;
-  if (!launch_wgrad_fc2(H, I, E, expert_offsets, dO, a, static_cast<uint16_t*>(dw2), s))
+  if (!launch_wgrad_fc2(H, I, E, dO, a, static_cast<uint16_t*>(dw2), sched, s))
     return W4A4_ERR_LAUNCH;
   if (cap > 0 && !launch_dgrad_fc1(cap, H, I, E, expert_offsets, dH, W1, dXp, s))
     return W4A4_ERR_LAUNCH;
   if (!join(0) || !fork(1)) return fail(W4A4_ERR_LAUNCH, "side stream fork / join failed");
-  if (!launch_wgrad_fc1(H, I, E, expert_offsets, dH, xp, static_cast<uint16_t*>(dw1), s))
+  if (!launch_wgrad_fc1(H, I, E, dH, xp, static_cast<uint16_t*>(dw1), sched, s))
     return W4A4_ERR_LAUNCH;
   if (!launch_gather_sum(T, H, k, dXp, row_map, static_cast<uint16_t*>(dx), side.stream))
     return W4A4_ERR_LAUNCH;

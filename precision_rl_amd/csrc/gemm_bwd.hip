@@ -413,7 +413,7 @@ constexpr int kRoundRows = 64;
 constexpr int kRowBytes = kBN * 2;
 constexpr int kOutOffset = kRingBytes;
 constexpr int kLdsBytes = kOutOffset + kRoundRows * kRowBytes;   // 160 KB: one workgroup per CU
-// The next tile's coordinates are published through ring slot 3, which holds
+// The next tile's table entry is published through ring slot 3, which holds
 // no data between the end of a tile's last stage and the first copy of the
 // next tile's stage 3.
 constexpr int kSlotOffset = (kStages - 1) * kStageBytes;
@@ -476,12 +476,199 @@ __device__ __forceinline__ void stage_round(uint8_t* so, const floatx16_t (&acc)
 __device__ __forceinline__ int round_tile_row(int s, int q) { return (s >> 4) * kWM + 16 * q + (s & 15); }
 
 // ------------------------------------------------------------------ wgrad
+// Tile schedule of the two wgrad GEMMs, computed on the device from the
+// expert offsets before they run (one workgroup of 1024 threads, E <= 1024).
+// The tiles are listed expert by expert in descending order of the expert's
+// row count (an expert's tiles N fastest), each costing its K stages plus a
+// constant for the epilogue.  An expert's tiles form one chunk, or, when
+// they are so costly that an XCD running them in rounds of its workgroups
+// would take longer than the ideal share of one workgroup, chunks of at
+// most one tile per workgroup of an XCD.  The chunks are dealt to the XCDs
+// in list order, each to the XCD with the least work so far, and an XCD's
+// workgroups take the tiles of its chunks in order from an atomic counter.
+// An expert's operands stay in one XCD's L2 (two or more for the few large
+// experts), and a skewed routing no longer leaves one XCD with most of the
+// work.
+constexpr int kTileCostEpilogue = 2;   // stage-equivalents of a tile's epilogue
+constexpr int kMaxChunks = 2048;
+// Per GEMM: the first entry of each XCD's tiles in the tile table, their
+// count, and the XCDs' tile counters; then the tile table: per XCD, in
+// order, {L, expert, first row, end row} for the tile at list position L.
+constexpr int kSchedBegin = 0, kSchedCount = 8, kSchedCounters = 16, kSchedTable = 32;
+
+struct SchedGemm {
+  int tpe;       // tiles per expert
+  int per_xcd;   // workgroups per XCD of the GEMM's grid
+  int32_t* out;  // kSchedTable + 4 E tpe ints
+};
+
+// Inclusive prefix sum over the workgroup (1024 threads); `total` gets the
+// sum of all values.  s_wave: 16 entries of scratch.
+__device__ int64_t block_scan(int64_t v, int64_t& total, int64_t* s_wave) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int64_t u = __shfl_up(v, d, 64);
+    if (lane >= d) v += u;
+  }
+  if (lane == 63) s_wave[w] = v;
+  __syncthreads();
+  int64_t add = 0, all = 0;
+  for (int i = 0; i < 16; ++i) {
+    const int64_t x = s_wave[i];
+    add += i < w ? x : 0;
+    all += x;
+  }
+  __syncthreads();
+  total = all;
+  return v + add;
+}
+
+__global__ void __launch_bounds__(1024)
+schedule_kernel(const int32_t* __restrict__ offsets, int E, SchedGemm g0, SchedGemm g1) {
+  __shared__ int s_rows[1024];
+  __shared__ int s_cost[1024];   // per-tile cost of the expert at each sorted position
+  __shared__ int s_e[1024], s_rb[1024], s_re[1024];
+  __shared__ int s_base[1024];   // first chunk of the expert
+  __shared__ int s_csize[1024];  // tiles per chunk of the expert
+  __shared__ uint32_t s_csum[kMaxChunks];
+  __shared__ uint16_t s_ctiles[kMaxChunks];
+  __shared__ uint8_t s_xcd[kMaxChunks];
+  __shared__ int s_off[kMaxChunks];
+  __shared__ int s_begin[kXcds];
+  __shared__ int64_t s_wave[16];
+  const int t = threadIdx.x;
+  const int n = t < E ? offsets[t + 1] - offsets[t] : -1;
+  s_rows[t] = n;
+  __syncthreads();
+  if (t < E) {
+    int rank = 0;
+    for (int i = 0; i < E; ++i) {
+      const int m = s_rows[i];
+      rank += (m > n) || (m == n && i < t);
+    }
+    s_e[rank] = t;
+    s_rb[rank] = offsets[t];
+    s_re[rank] = offsets[t + 1];
+    s_cost[rank] = (n + kBK - 1) / kBK + kTileCostEpilogue;
+  }
+  __syncthreads();
+  const int c = t < E ? s_cost[t] : 0;   // thread t: sorted position t
+  int64_t cost_sum;
+  block_scan(c, cost_sum, s_wave);
+  for (int g = 0; g < 2; ++g) {
+    const SchedGemm p = g ? g1 : g0;
+    const int64_t tpe = p.tpe, tiles = tpe * E, total = tpe * cost_sum;
+    // split an expert whose tiles, run whole on one XCD, would take longer
+    // than the ideal share of one workgroup
+    const int64_t ideal = total / (static_cast<int64_t>(kXcds) * p.per_xcd);
+    const int kc = static_cast<int>((tpe + p.per_xcd - 1) / p.per_xcd);
+    int nc = t < E ? (kc > 1 && static_cast<int64_t>(c) * kc > ideal ? kc : 1) : 0;
+    int64_t nch;
+    int64_t incl = block_scan(nc, nch, s_wave);
+    if (nch > kMaxChunks) {   // too many chunks: whole experts
+      nc = t < E ? 1 : 0;
+      incl = t + 1;
+      nch = E;
+    }
+    const int csize = nc > 0 ? static_cast<int>((tpe + nc - 1) / nc) : 0;
+    // chunk costs, scaled to fit 31 bits
+    int shift = 0;
+    while ((total >> shift) >= (int64_t{1} << 31)) ++shift;
+    if (t < E) {
+      const int base = static_cast<int>(incl) - nc;
+      s_base[t] = base;
+      s_csize[t] = csize;
+      for (int i = 0; i < nc; ++i) {
+        const int size = static_cast<int>(min<int64_t>(csize, tpe - static_cast<int64_t>(i) * csize));
+        s_ctiles[base + i] = static_cast<uint16_t>(size);
+        s_csum[base + i] = static_cast<uint32_t>((static_cast<int64_t>(size) * c) >> shift);
+      }
+    }
+    __syncthreads();
+    // Chunks, in list order, each to the XCD with the least work so far.
+    // Wave 0 runs the loop in step (every value is the same in all lanes,
+    // so it runs on the scalar unit); lane i keeps the result of chunk
+    // c0 + i of the batch.
+    if (t < kWave) {
+      uint32_t load[kXcds], ntiles[kXcds];
+#pragma unroll
+      for (int x = 0; x < kXcds; ++x) load[x] = ntiles[x] = 0;
+      for (int c0 = 0; c0 < nch; c0 += kWave) {
+        const bool mine = c0 + t < nch;
+        const uint32_t v_sum = mine ? s_csum[c0 + t] : 0u;
+        const uint32_t v_tiles = mine ? s_ctiles[c0 + t] : 0u;
+        uint32_t v_xcd = 0, v_off = 0;
+        const int m = static_cast<int>(min<int64_t>(kWave, nch - c0));
+        for (int i = 0; i < m; ++i) {
+          const uint32_t sum = __builtin_amdgcn_readlane(v_sum, i);
+          const uint32_t size = __builtin_amdgcn_readlane(v_tiles, i);
+          int x = 0;
+          uint32_t lo = load[0];
+#pragma unroll
+          for (int y = 1; y < kXcds; ++y)
+            if (load[y] < lo) {
+              lo = load[y];
+              x = y;
+            }
+          uint32_t off = 0;
+#pragma unroll
+          for (int y = 0; y < kXcds; ++y)
+            if (y == x) {
+              off = ntiles[y];
+              load[y] += sum;
+              ntiles[y] += size;
+            }
+          if (t == i) {
+            v_xcd = static_cast<uint32_t>(x);
+            v_off = off;
+          }
+        }
+        if (mine) {
+          s_xcd[c0 + t] = static_cast<uint8_t>(v_xcd);
+          s_off[c0 + t] = static_cast<int>(v_off);
+        }
+      }
+      if (t == 0) {
+        uint32_t acc = 0;
+#pragma unroll
+        for (int x = 0; x < kXcds; ++x) {
+          s_begin[x] = static_cast<int>(acc);
+          p.out[kSchedBegin + x] = static_cast<int32_t>(acc);
+          p.out[kSchedCount + x] = static_cast<int32_t>(ntiles[x]);
+          p.out[kSchedCounters + x] = 2 * p.per_xcd;   // tickets below it are dealt statically
+          acc += ntiles[x];
+        }
+      }
+    }
+    __syncthreads();
+    // (tile L = expert j, tile li of it; stepped by 1024 without divisions)
+    u32x4_t* table = reinterpret_cast<u32x4_t*>(p.out + kSchedTable);
+    const int tp = p.tpe, jstep = 1024 / tp, lstep = 1024 % tp;
+    int j = t / tp, li = t % tp;
+    for (int L = t; L < static_cast<int>(tiles); L += 1024) {
+      const int cs = s_csize[j], i = li / cs;
+      const int ch = s_base[j] + i;
+      const int at = s_begin[s_xcd[ch]] + s_off[ch] + (li - i * cs);
+      table[at] = u32x4_t{static_cast<uint32_t>(L), static_cast<uint32_t>(s_e[j]),
+                          static_cast<uint32_t>(s_rb[j]), static_cast<uint32_t>(s_re[j])};
+      j += jstep;
+      li += lstep;
+      if (li >= tp) {
+        li -= tp;
+        ++j;
+      }
+    }
+    __syncthreads();
+  }
+}
+
 struct WgradArgs {
   int M, N, E;             // dW[e] is [M, N]
-  const int32_t* offsets;
   const uint16_t* g;       // G [rows, M]:  A(m, r) = G[r][m]
   const uint16_t* s;       // S [rows, N]:  B(r, n) = S[r][n]
   uint16_t* out;           // [E, M, N]
+  int32_t* sched;          // this GEMM's schedule (its tile counters are updated)
 };
 
 struct WTile {
@@ -498,24 +685,74 @@ wgrad_kernel(WgradArgs args) {
   const int wrow = wm * kWM, wcol = (wave >> 2) * kWN;
   const int r32 = lane & 31, hl = lane >> 5;
   const int m_tiles = args.M / kBM, n_tiles = (args.N + kBN - 1) / kBN;
-  const int64_t total = static_cast<int64_t>(args.E) * m_tiles * n_tiles;
-  const int64_t per_xcd = (total + kXcds - 1) / kXcds;
-  // This workgroup's i-th tile (false: none left).  Logical tiles are
-  // expert-major, N fastest; XCD x owns a contiguous run of them.
-  auto tile = [&](int i, WTile& t) -> bool {
-    const int64_t y = blockIdx.x / kXcds + static_cast<int64_t>(i) * (gridDim.x / kXcds);
-    const int64_t L = (blockIdx.x % kXcds) * per_xcd + y;
-    if (!(y < per_xcd && L < total)) return false;
-    t.e = static_cast<int>(L / (m_tiles * n_tiles));
-    t.m0 = static_cast<int>((L / n_tiles) % m_tiles) * kBM;
-    t.n0 = static_cast<int>(L % n_tiles) * kBN;
-    t.r_begin = args.offsets[t.e];
-    t.r_end = args.offsets[t.e + 1];
+  const int tpe = m_tiles * n_tiles;   // tiles per expert
+  // Tiles come from this workgroup's XCD's part of the tile table.  The
+  // first two tickets of each workgroup are dealt statically (blockIdx /
+  // kXcds and that plus the workgroups per XCD; the counters start past
+  // them), later ones come from the XCD's counter.  Only thread 0 draws
+  // tickets and loads table entries, two tiles ahead: the ticket of the
+  // tile after next is drawn as the current tile's copies start, and its
+  // entry is loaded when the current tile ends, so that both have landed
+  // long before they are used (when a tile ends, every copy has landed and
+  // waiting costs nothing).
+  const int xcd = static_cast<int>(blockIdx.x % kXcds);
+  const int per_xcd = static_cast<int>(gridDim.x / kXcds);
+  int32_t* counter = args.sched + kSchedCounters + xcd;
+  const u32x4_t* table = reinterpret_cast<const u32x4_t*>(args.sched + kSchedTable);
+  const u32x4_t none{static_cast<uint32_t>(-1), 0u, 0u, 0u};
+  // A zero offset hidden in a vector register: with an address it sees as
+  // uniform, the compiler combines a wave's atomics and reads the result at
+  // once, which would wait for every copy in flight.
+  uint32_t vzero = 0;
+  asm volatile("" : "+v"(vzero));
+  // thread 0: this XCD's part of the table; `done` once a ticket past its
+  // end was seen (no more are drawn)
+  int32_t begin = 0, count = 0;
+  bool done = false;
+  // Thread 0: {L, expert, first row, end row} of ticket q (L = -1: past the
+  // end of the XCD's tiles).
+  auto entry = [&](int32_t q) -> u32x4_t {
+    if (q < count) return table[begin + q];
+    done = true;
+    return none;
+  };
+  // The next tile passes from thread 0 to all waves through ring slot 3
+  // (written only while no wave reads the ring, read by all waves before the
+  // slot is refilled).
+  u32x4_t* slot = reinterpret_cast<u32x4_t*>(lds + kSlotOffset);
+  auto tile = [&](WTile& t) -> bool {
+    const u32x4_t p = *slot;
+    const int L = static_cast<int>(__builtin_amdgcn_readfirstlane(p[0]));
+    if (L < 0) return false;
+    const int local = L % tpe;
+    t.e = static_cast<int>(__builtin_amdgcn_readfirstlane(p[1]));
+    t.m0 = (local / n_tiles) * kBM;
+    t.n0 = (local % n_tiles) * kBN;
+    t.r_begin = static_cast<int32_t>(__builtin_amdgcn_readfirstlane(p[2]));
+    t.r_end = static_cast<int32_t>(__builtin_amdgcn_readfirstlane(p[3]));
     t.nk = static_cast<int>((t.r_end - t.r_begin + kBK - 1) / kBK);
     return true;
   };
+  // Thread 0: ticket of the tile after next (not reset per tile: a write to
+  // a register that an atomic or load may still fill waits for it, and with
+  // it for every copy in flight) and the entry of the next tile.
+  int32_t q_ahead = 0;
+  u32x4_t e_next = none;
+  auto draw = [&] {
+    if (tid == 0 && !done) q_ahead = atomicAdd(counter + vzero, 1);
+  };
+  if (tid == 0) {
+    begin = args.sched[kSchedBegin + xcd];
+    count = args.sched[kSchedCount + xcd];
+    const int32_t q0 = static_cast<int32_t>(blockIdx.x / kXcds);
+    const u32x4_t e0 = entry(q0);
+    e_next = entry(q0 + per_xcd);
+    *slot = e0;
+  }
+  __syncthreads();
   WTile tc;
-  if (!tile(0, tc)) return;
+  if (!tile(tc)) return;
+  draw();
 
   // ---- copies: both operands [k = row][256 columns]; rows past the expert's
   // end are re-read from its last row and zeroed in LDS; columns past N are
@@ -641,9 +878,15 @@ wgrad_kernel(WgradArgs args) {
 
     // ---- next tile's first stages, then the epilogue of this one
     ring_idle_barrier();
+    if (tid == 0) {
+      *slot = e_next;
+      e_next = done ? none : entry(q_ahead);
+    }
+    __syncthreads();
     WTile tn;
-    const bool more = tile(it, tn);
+    const bool more = tile(tn);
     if (more) {
+      draw();
       setup(tn);
       for (int s = 0; s < kAhead && s < tn.nk; ++s) issue(tn, s);
     }
@@ -696,12 +939,29 @@ bool launch_dgrad(const dg::DgradArgs& a, const char* name, hipStream_t s) {
   return launch_ok(name);
 }
 
+// Grid of a wgrad GEMM of E experts' [M, N] tiles: one workgroup per CU,
+// at most one per tile.
+struct WgradPlan {
+  int64_t tiles;
+  unsigned grid;
+  int tpe, per_xcd;
+};
+WgradPlan wgrad_plan(int M, int N, int E) {
+  WgradPlan p;
+  p.tpe = (M / wg::kBM) * ((N + wg::kBN - 1) / wg::kBN);
+  p.tiles = static_cast<int64_t>(E) * p.tpe;
+  p.grid = persistent_grid(p.tiles);
+  p.per_xcd = std::max(1, static_cast<int>(p.grid / kXcds));
+  return p;
+}
+size_t wgrad_sched_ints(const WgradPlan& p) { return wg::kSchedTable + 4 * static_cast<size_t>(p.tiles); }
+
 bool launch_wgrad(const wg::WgradArgs& a, const char* name, hipStream_t s) {
   static const hipError_t attr = set_lds(&wg::wgrad_kernel, wg::kLdsBytes);
   if (attr != hipSuccess) return launch_ok(name) && false;
-  const int64_t tiles = static_cast<int64_t>(a.E) * (a.M / wg::kBM) * ((a.N + wg::kBN - 1) / wg::kBN);
-  if (tiles == 0) return true;
-  launch_kernel(name, wg::wgrad_kernel, dim3(persistent_grid(tiles)), dim3(wg::kThreads), wg::kLdsBytes, s, a);
+  const WgradPlan p = wgrad_plan(a.M, a.N, a.E);
+  if (p.tiles == 0) return true;
+  launch_kernel(name, wg::wgrad_kernel, dim3(p.grid), dim3(wg::kThreads), wg::kLdsBytes, s, a);
   return launch_ok(name);
 }
 
@@ -720,15 +980,29 @@ bool launch_dgrad_fc1(int64_t rows_alloc, int H, int I, int E, const int32_t* of
   return launch_dgrad<dg::DgradMode::FC1>(a, "gemm_dgrad_fc1", s);
 }
 
-bool launch_wgrad_fc2(int H, int I, int E, const int32_t* offsets, const uint16_t* dO,
-                      const uint16_t* a, uint16_t* dW2, hipStream_t s) {
-  wg::WgradArgs w{H, I, E, offsets, dO, a, dW2};
+size_t wgrad_schedule_ints(int H, int I, int E) {
+  if (E < 1 || H < wg::kBM || I < wg::kBM / 2) return 2 * wg::kSchedTable;
+  return wgrad_sched_ints(wgrad_plan(H, I, E)) + wgrad_sched_ints(wgrad_plan(2 * I, H, E));
+}
+
+bool launch_wgrad_schedule(int H, int I, int E, const int32_t* offsets, int32_t* sched, hipStream_t s) {
+  if (E < 1 || E > 1024) return false;
+  const WgradPlan p2 = wgrad_plan(H, I, E), p1 = wgrad_plan(2 * I, H, E);
+  launch_kernel("wgrad_schedule", wg::schedule_kernel, dim3(1), dim3(1024), 0, s, offsets, E,
+                wg::SchedGemm{p2.tpe, p2.per_xcd, sched},
+                wg::SchedGemm{p1.tpe, p1.per_xcd, sched + wgrad_sched_ints(p2)});
+  return launch_ok("wgrad_schedule");
+}
+
+bool launch_wgrad_fc2(int H, int I, int E, const uint16_t* dO, const uint16_t* a, uint16_t* dW2,
+                      int32_t* sched, hipStream_t s) {
+  wg::WgradArgs w{H, I, E, dO, a, dW2, sched};
   return launch_wgrad(w, "gemm_wgrad_fc2", s);
 }
 
-bool launch_wgrad_fc1(int H, int I, int E, const int32_t* offsets, const uint16_t* dH,
-                      const uint16_t* xp, uint16_t* dW1, hipStream_t s) {
-  wg::WgradArgs w{2 * I, H, E, offsets, dH, xp, dW1};
+bool launch_wgrad_fc1(int H, int I, int E, const uint16_t* dH, const uint16_t* xp, uint16_t* dW1,
+                      int32_t* sched, hipStream_t s) {
+  wg::WgradArgs w{2 * I, H, E, dH, xp, dW1, sched + wgrad_sched_ints(wgrad_plan(H, I, E))};
   return launch_wgrad(w, "gemm_wgrad_fc1", s);
 }
 

@@ -90,11 +90,20 @@ bool launch_dgrad_fc2(int64_t rows_alloc, int H, int I, int E, const int32_t* of
 bool launch_dgrad_fc1(int64_t rows_alloc, int H, int I, int E, const int32_t* offsets,
                       const uint16_t* dH, const uint16_t* w1, uint16_t* dXp, hipStream_t s);
 
+// Tile schedule of the two wgrad GEMMs (experts by row count, blocks of
+// tiles dealt to the XCDs longest first, tile counters), computed on the
+// device from the offsets; `sched` holds wgrad_schedule_ints(H, I, E) ints
+// and is read and updated by the two wgrad launches that follow on the same
+// stream (each launch consumes its counters: the schedule is written again
+// before the next pair).  1 <= E <= 1024.
+size_t wgrad_schedule_ints(int H, int I, int E);
+bool launch_wgrad_schedule(int H, int I, int E, const int32_t* offsets, int32_t* sched, hipStream_t s);
+
 // FC2 wgrad: dW2[e] = bf16(dO_e^T a_e).   FC1 wgrad: dW1[e] = bf16(dH_e^T x[src_row]).
-bool launch_wgrad_fc2(int H, int I, int E, const int32_t* offsets, const uint16_t* dO,
-                      const uint16_t* a, uint16_t* dW2, hipStream_t s);
-bool launch_wgrad_fc1(int H, int I, int E, const int32_t* offsets, const uint16_t* dH,
-                      const uint16_t* xp, uint16_t* dW1, hipStream_t s);
+bool launch_wgrad_fc2(int H, int I, int E, const uint16_t* dO, const uint16_t* a, uint16_t* dW2,
+                      int32_t* sched, hipStream_t s);
+bool launch_wgrad_fc1(int H, int I, int E, const uint16_t* dH, const uint16_t* xp, uint16_t* dW1,
+                      int32_t* sched, hipStream_t s);
 
 // dX gather-sum: dX[t] = bf16(sum_j dXp[row_map[t,j]]).
 bool launch_gather_sum(int64_t T, int H, int k, const uint16_t* dXp, const int32_t* row_map,

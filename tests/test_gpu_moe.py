@@ -217,6 +217,32 @@ def test_backward_ragged_empty():
         assert not run.g["dw1"][e].any() and not run.g["dw2"][e].any()
 
 
+def test_backward_skewed_split_experts():
+    """Few experts of very different sizes: the wgrad schedule deals the
+    tiles of the costly experts in chunks (their tiles, run whole on one
+    XCD's workgroups in rounds, would take longer than an even share) and
+    those of the cheapest expert whole.  Every expert's dW1 and dW2, and dX,
+    against the oracle."""
+    T, H, E, k, I = 4096, 1024, 4, 1, 512
+    d = synth.make_inputs(T, H, E, k, I, routing="zipf", backward=True, seed=303, n_empty=0)
+    counts = np.bincount(d["topk_idx"].reshape(-1), minlength=E)
+    # wgrad FC1: 4 x 4 tiles per expert and a grid of 64 workgroups (8 per
+    # XCD), so an expert runs whole in two rounds or in two chunks of 8;
+    # wgrad FC2: 4 x 2 tiles, 32 workgroups, the same split
+    cost = (counts + 31) // 32 + 2
+    split = 2 * cost > 16 * cost.sum() // 64
+    assert split.any() and not split.all(), (counts, cost)
+    print_case("backward_split", T=T, H=H, E=E, k=k, I=I, counts=counts.tolist())
+    run = Run(d, T, H, E, k, I, backward=True)
+    ref, _, _ = _oracle_fwd(d, E, 1)
+    rb = _oracle_bwd(d, E, 1, ref)
+    print(_check_backward(run, rb))
+    dw1, dw2 = bf16_host(run.g["dw1"]), bf16_host(run.g["dw2"])
+    for e in range(E):
+        assert rel_l2(dw1[e], rb["dW1"][e]) <= BWD_TOL, e
+        assert rel_l2(dw2[e], rb["dW2"][e]) <= BWD_TOL, e
+
+
 def test_backward_full_learner_workload_sampled():
     """Learner workload at full size (T=16384, H=2048, E=128, k=8, I=768):
     dX of sampled tokens and dW of sampled experts against the oracle on the
