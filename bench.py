@@ -68,7 +68,8 @@ def algorithmic_work(T, H, E, k, I):
 
 
 # Kernels the library runs concurrently with another one (second stream).
-CONCURRENT = {"x_scatter": "gemm_wgrad_fc2, gemm_dgrad_fc1",
+CONCURRENT = {"wgrad_schedule": "dy_scatter, gemm_dgrad_fc2",
+              "x_scatter": "gemm_wgrad_fc2, gemm_dgrad_fc1",
               "dx_gather_sum": "gemm_wgrad_fc1"}
 
 
