@@ -38,6 +38,8 @@ KERNEL_SOURCES = {
     "quantize_scatter": "quantize.hip", "requant": "quantize.hip",
     "unpermute": "elementwise.hip", "dy_scatter": "elementwise.hip", "x_scatter": "elementwise.hip",
     "dx_gather_sum": "elementwise.hip",
+    "gemm_linear": "gemm_fwd.hip", "gemm_linear_dgrad": "gemm_bwd.hip",
+    "gemm_linear_wgrad": "gemm_bwd.hip",
 }
 
 
@@ -92,6 +94,105 @@ def stored_traffic(name):
     return rec.get("hbm_bytes_per_launch")
 
 
+# Dense linear workload: a Qwen3-30B-A3B query projection (hidden 2048 -> 32
+# heads x 128) at the learner batch.
+LINEAR = dict(T=16384, K=2048, N=4096)
+LINEAR_METRIC = "W4A4 dense per-token NVFP4 linear fwd+bwd tokens/s, Qwen3-30B-A3B q projection"
+
+
+def linear_work(T, K, N):
+    """Per-launch algorithmic flops / bytes of the dense linear step."""
+    fl = {n: 2.0 * T * K * N for n in ("gemm_linear", "gemm_linear_dgrad", "gemm_linear_wgrad")}
+    # read x; write codes, scales, outer, row_map, src_row (identity routing)
+    by = {"quantize_scatter": T * (K * 2 + K // 2 + K // 16 + 12)}
+    return fl, by
+
+
+def cpu_baseline_linear(x, w, dy, tokens):
+    """The FP64 oracle's linear forward + backward on the first `tokens` tokens
+    (the weight's quantisation inside the oracle call is included)."""
+    from oracle import linear, nvfp4 as q
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    xf, wf, dyf = (q.bf16_bits_to_f64(v) for v in (x[:tokens], w, dy[:tokens]))
+    t0 = time.perf_counter()
+    linear.forward(xf, wf)
+    linear.backward(dyf, xf, wf)
+    dt = time.perf_counter() - t0
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{tokens} tokens of the linear workload (K={w.shape[1]}, N={w.shape[0]}), "
+                      f"FP64 numpy, quantize (x and W) + forward + backward, {dt:.1f} s",
+            "seconds": dt, "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main_linear(args):
+    import torch
+    from precision_rl_amd import binding as b, synth
+
+    T, K, N = LINEAR["T"], LINEAR["K"], LINEAR["N"]
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(1005)))
+    xb = synth.normal_bf16(rng, (T, K))
+    wb = synth.normal_bf16(rng, (N, K), synth.W_STD)
+    dyb = synth.normal_bf16(rng, (T, N))
+    dev = torch.device("cuda:0")
+
+    def bf(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x, W, dy = bf(xb), bf(wb), bf(dyb)
+    wq = b.w4a4_quantize_permute(W, None, 1)      # offline, untimed
+    xq = dict(codes=torch.empty(T, K // 2, dtype=torch.uint8, device=dev),
+              scales=torch.empty(T, K // 16, dtype=torch.uint8, device=dev),
+              outer=torch.empty(T, dtype=torch.float32, device=dev),
+              offsets=torch.empty(2, dtype=torch.int32, device=dev),
+              row_map=torch.empty(T, 1, dtype=torch.int32, device=dev),
+              src_row=torch.empty(T, dtype=torch.int32, device=dev))
+    ws_qp = torch.empty(b.workspace_size(b.WS_QUANTIZE_PERMUTE, T, K, 0, 1, 1, 1) + 256,
+                        dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(b.workspace_size(b.WS_LINEAR_BACKWARD, 0, K, N, 1, 1, 1),
+                       dtype=torch.uint8, device=dev)
+    y = torch.empty(T, N, dtype=torch.bfloat16, device=dev)
+    grads = dict(dx=torch.empty(T, K, dtype=torch.bfloat16, device=dev),
+                 dw=torch.empty(N, K, dtype=torch.bfloat16, device=dev))
+
+    calibration_copy(torch, dev)
+
+    def step():
+        b.w4a4_quantize_permute(x, None, 1, out=xq, workspace=ws_qp)
+        b.w4a4_linear_fwd(xq, wq, T, K, N, y=y)
+        b.w4a4_linear_bwd(dy, x, W, xq, T, K, N, out=grads, workspace=ws_b)
+
+    ms, kern = time_steps(b, torch, step, args)
+    fl, by = linear_work(T, K, N)
+    per_kernel, roof = summarize(kern, ms, args.steps, fl, by)
+    out = {
+        "metric": LINEAR_METRIC,
+        "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4->f16 MFMA fwd, bf16 MFMA bwd, fp32 accumulate",
+        "data": "synthetic (seeded; random-init weight of the layer's shape)",
+        "config": {"workload": "linear: quantize + NVFP4 linear fwd + BF16 STE bwd",
+                   "T": T, "K": K, "N": N},
+        "roofline": roof,
+        "step_mfma_tflops": round(sum(fl.values()) / (ms * 1e-3) / 1e12, 1),
+        "kernels": per_kernel,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the FP64 oracle on the host", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline_linear(xb, wb, dyb, tokens=T)
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline(d, w, tokens=512, experts=8):
     """The FP64 oracle on a bounded sample of the learner workload: the first
     `tokens` tokens, each routed to all `experts` experts (k = 8 per token as
@@ -124,6 +225,74 @@ def cpu_baseline(d, w, tokens=512, experts=8):
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def calibration_copy(torch, dev):
+    """A plain elementwise copy of known size (reads 256 MiB, writes 256 MiB),
+    run once before timing, for scaling the HBM counters of --pmc runs."""
+    calib = torch.ones(128 << 20, dtype=torch.bfloat16, device=dev)
+    calib_out = torch.empty_like(calib)
+    torch.cuda.synchronize()
+    torch.neg(calib, out=calib_out)
+    del calib, calib_out
+
+
+def time_steps(b, torch, step, args):
+    """W untimed warm-up steps, then K timed steps between synchronisations,
+    with the library's per-launch profiler on.  Returns (ms per step, the
+    profiler's per-kernel record)."""
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    b.w4a4_profiler_enable(True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    kern = b.w4a4_profiler_report()
+    b.w4a4_profiler_enable(False)
+    print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+    return ms, kern
+
+
+def summarize(kern, ms, steps, fl, by):
+    """Per-kernel table and the roofline object of the dominant kernel."""
+    per_kernel = {}
+    for name, rec in sorted(kern.items(), key=lambda kv: -kv[1]["total_ms"]):
+        avg_ms = rec["total_ms"] / rec["count"]
+        entry = {"avg_ms": round(avg_ms, 4), "launches": rec["count"],
+                 "share": round(rec["total_ms"] / (ms * steps), 4)}
+        if name in fl:
+            entry["tflops"] = round(fl[name] / (avg_ms * 1e-3) / 1e12, 1)
+            entry["frac_mfma"] = round(entry["tflops"] / PEAK_MFMA_TFLOPS, 4)
+        elif name in by:
+            entry["gbs"] = round(by[name] / (avg_ms * 1e-3) / 1e9, 1)
+            entry["frac_hbm"] = round(entry["gbs"] / PEAK_HBM_GBS, 4)
+        if name in CONCURRENT:
+            # launched on a second stream beside another kernel: its duration is
+            # time shared with that kernel, not its standalone rate
+            entry["runs_beside"] = CONCURRENT[name]
+        per_kernel[name] = entry
+    dom = max(kern, key=lambda n: kern[n]["total_ms"])
+    dom_avg_s = kern[dom]["total_ms"] / kern[dom]["count"] * 1e-3
+    if dom in fl:
+        ach = fl[dom] / dom_avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_MFMA_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_MFMA_TFLOPS, 4)}
+    else:
+        ach = by[dom] / dom_avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4)}
+    roof["kernel"] = dom
+    roof["avg_ms"] = round(dom_avg_s * 1e3, 4)
+    roof["traffic"] = stored_traffic(dom)
+
+    return per_kernel, roof
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -131,12 +300,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=6144)
+    ap.add_argument("--workload", choices=["learner", "linear"], default="learner",
+                    help="learner: the MoE expert step (default); linear: the dense projection")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: the benchmark runs on one GPU only (asked for --gpus {args.gpus}); "
               "the library's expert path is single-GPU (sharding is described in the design notes).",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "linear":
+        return main_linear(args)
 
     import torch
     from precision_rl_amd import binding as b, synth
@@ -172,13 +346,7 @@ def main():
                  dw1=torch.empty(E, 2 * I, H, dtype=torch.bfloat16, device=dev),
                  dw2=torch.empty(E, H, I, dtype=torch.bfloat16, device=dev))
 
-    # a plain elementwise copy of known size (reads 256 MiB, writes 256 MiB), for
-    # scaling the HBM counters of --pmc runs
-    calib = torch.ones(128 << 20, dtype=torch.bfloat16, device=dev)
-    calib_out = torch.empty_like(calib)
-    torch.cuda.synchronize()
-    torch.neg(calib, out=calib_out)
-    del calib, calib_out
+    calibration_copy(torch, dev)
 
     def step():
         b.w4a4_quantize_permute(x, idx, E, A, out=xq, workspace=ws_qp)
@@ -187,54 +355,9 @@ def main():
         b.w4a4_expert_bwd(dy, x, w1, w2, saved["h"], saved["a"], p, xq, T, H, I, E, k, A,
                           out=grads, workspace=ws_b)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
-
-    b.w4a4_profiler_enable(True)
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        step()
-    stop.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / args.steps
-    kern = b.w4a4_profiler_report()
-    b.w4a4_profiler_enable(False)
-    print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
-
+    ms, kern = time_steps(b, torch, step, args)
     fl, by = algorithmic_work(T, H, E, k, I)
-    per_kernel = {}
-    for name, rec in sorted(kern.items(), key=lambda kv: -kv[1]["total_ms"]):
-        avg_ms = rec["total_ms"] / rec["count"]
-        entry = {"avg_ms": round(avg_ms, 4), "launches": rec["count"],
-                 "share": round(rec["total_ms"] / (ms * args.steps), 4)}
-        if name in fl:
-            entry["tflops"] = round(fl[name] / (avg_ms * 1e-3) / 1e12, 1)
-            entry["frac_mfma"] = round(entry["tflops"] / PEAK_MFMA_TFLOPS, 4)
-        elif name in by:
-            entry["gbs"] = round(by[name] / (avg_ms * 1e-3) / 1e9, 1)
-            entry["frac_hbm"] = round(entry["gbs"] / PEAK_HBM_GBS, 4)
-        if name in CONCURRENT:
-            # launched on a second stream beside another kernel: its duration is
-            # time shared with that kernel, not its standalone rate
-            entry["runs_beside"] = CONCURRENT[name]
-        per_kernel[name] = entry
-    dom = max(kern, key=lambda n: kern[n]["total_ms"])
-    dom_avg_s = kern[dom]["total_ms"] / kern[dom]["count"] * 1e-3
-    if dom in fl:
-        ach = fl[dom] / dom_avg_s / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_MFMA_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_MFMA_TFLOPS, 4)}
-    else:
-        ach = by[dom] / dom_avg_s / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4)}
-    roof["kernel"] = dom
-    roof["avg_ms"] = round(dom_avg_s * 1e3, 4)
-    roof["traffic"] = stored_traffic(dom)
+    per_kernel, roof = summarize(kern, ms, args.steps, fl, by)
 
     gemm_ms = sum(kern[n]["total_ms"] for n in kern if n in fl) / args.steps
     total_flop = sum(fl.values())

@@ -68,7 +68,8 @@ typedef enum {
 typedef enum {
   W4A4_WS_QUANTIZE_PERMUTE = 0,
   W4A4_WS_FORWARD = 1,
-  W4A4_WS_BACKWARD = 2
+  W4A4_WS_BACKWARD = 2,
+  W4A4_WS_LINEAR_BACKWARD = 3   /* w4a4_linear_bwd: H = K, I = N; T, E, k, row_align unused */
 } w4a4_workspace_kind;
 
 /* Padded dispatched-row capacity: T*k + E*(row_align-1).  Returns -1 on bad
@@ -192,6 +193,50 @@ w4a4_status w4a4_expert_bwd(
     const void* save_h, const void* save_a, const float* topk_w,
     const int32_t* expert_offsets, const int32_t* row_map, const int32_t* src_row,
     void* dx, void* dw1, void* dw2,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * w4a4_linear_fwd -- dense per-token NVFP4 linear layer, y = x W^T: the
+ * MoE path's quantisation and GEMM with a single group and no permutation.
+ *   Defined by: miniTE Technical Report, section 4.1 (ordinary linear layers
+ *   beside the MoE GroupedLinear, behind the same quantisation interface) and
+ *   section 4.3 (the nvfp4_per_token recipe: one activation outer scale per
+ *   token, one weight outer scale per output row).
+ *
+ *   y[t, n] = bf16(g_x[t] * g_w[n] * sum_k (d c)_x[t, k] (d c)_w[n, k]),
+ *   the sum and the outer factors in FP32.
+ *
+ *   x_codes [T, K/2], x_scales [T, K/16], x_outer [T], offsets [2] = {0, T}:
+ *   the outputs of w4a4_quantize_permute(x, T, K, NULL, ...) (identity
+ *   routing).  w_codes [N, K/2], w_scales [N, K/16], w_outer [N]: the same
+ *   call on the weight W [N, K].  y [T, N] bf16 out (device).
+ *   Requirements: K % 256 == 0, N % 256 == 0, K, N <= 8192 (else
+ *   W4A4_ERR_UNSUPPORTED).  No workspace.
+ */
+w4a4_status w4a4_linear_fwd(
+    int64_t T, int K, int N,
+    const uint8_t* x_codes, const uint8_t* x_scales, const float* x_outer,
+    const int32_t* offsets,
+    const uint8_t* w_codes, const uint8_t* w_scales, const float* w_outer,
+    void* y, void* stream);
+
+/*
+ * w4a4_linear_bwd -- straight-through BF16 backward of w4a4_linear_fwd on the
+ * saved bf16 x and W (Technical Report, section 4.3: the layer bypass).
+ *
+ *   dx = bf16(dy W)        [T, K]      dw = bf16(dy^T x)      [N, K]
+ *   both accumulated in FP32.
+ *
+ *   dy [T, N], x [T, K], w [N, K] bf16 (device); offsets: the {0, T} of the
+ *   forward's quantisation (device).  dx [T, K] and dw [N, K] bf16 out
+ *   (dw is zeros when T = 0).  workspace: w4a4_workspace_size(
+ *   W4A4_WS_LINEAR_BACKWARD, 0, K, N, 1, 1, 1) bytes (the weight-gradient
+ *   tile schedule, written by the call).  Requirements as the forward.
+ */
+w4a4_status w4a4_linear_bwd(
+    int64_t T, int K, int N,
+    const void* dy, const void* x, const void* w, const int32_t* offsets,
+    void* dx, void* dw,
     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a status code. */

@@ -29,13 +29,17 @@ _SIGS = {
     "w4a4_expert_bwd": (c_int, [c_i64, c_int, c_int, c_int, c_int, c_int,
                                 c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                 c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "w4a4_linear_fwd": (c_int, [c_i64, c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                c_vp, c_vp]),
+    "w4a4_linear_bwd": (c_int, [c_i64, c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                c_vp, c_sz, c_vp]),
     "w4a4_status_string": (ctypes.c_char_p, [c_int]),
     "w4a4_last_error": (ctypes.c_char_p, []),
     "w4a4_profiler_enable": (c_int, [c_int]),
     "w4a4_profiler_report": (c_int, [ctypes.c_char_p, c_sz]),
 }
 
-WS_QUANTIZE_PERMUTE, WS_FORWARD, WS_BACKWARD = 0, 1, 2
+WS_QUANTIZE_PERMUTE, WS_FORWARD, WS_BACKWARD, WS_LINEAR_BACKWARD = 0, 1, 2, 3
 
 
 class W4A4Error(RuntimeError):
@@ -181,6 +185,32 @@ def w4a4_expert_bwd(dy, x, w1, w2, h, a, topk_w, xq, T, H, I, E, k, row_align=1,
         T, H, I, E, k, row_align, _p(dy), _p(x), _p(w1), _p(w2), _p(h), _p(a), _p(topk_w),
         _p(xq["offsets"]), _p(xq["row_map"]), _p(xq["src_row"]),
         _p(out["dx"]), _p(out["dw1"]), _p(out["dw2"]), _p(ws), ws.numel(), _stream()))
+    return out
+
+
+def w4a4_linear_fwd(xq, wq, T, K, N, y=None):
+    """Dense per-token NVFP4 linear layer y = x W^T.  xq: w4a4_quantize_permute(x, None, 1)
+    of x [T, K]; wq: the same of W [N, K].  Returns y [T, N] bf16."""
+    lib = load()
+    dev = wq["codes"].device
+    if y is None:
+        y = torch.empty(T, N, dtype=torch.bfloat16, device=dev)
+    _check(lib.w4a4_linear_fwd(T, K, N, _p(xq["codes"]), _p(xq["scales"]), _p(xq["outer"]),
+                               _p(xq["offsets"]), _p(wq["codes"]), _p(wq["scales"]),
+                               _p(wq["outer"]), _p(y), _stream()))
+    return y
+
+
+def w4a4_linear_bwd(dy, x, w, xq, T, K, N, out=None, workspace=None):
+    """Straight-through BF16 backward of w4a4_linear_fwd.  Returns dict(dx [T, K], dw [N, K]) bf16."""
+    lib = load()
+    dev = w.device
+    if out is None:
+        out = dict(dx=torch.empty(T, K, dtype=torch.bfloat16, device=dev),
+                   dw=torch.empty(N, K, dtype=torch.bfloat16, device=dev))
+    ws = _workspace(workspace_size(WS_LINEAR_BACKWARD, 0, K, N, 1, 1), dev, workspace)
+    _check(lib.w4a4_linear_bwd(T, K, N, _p(dy), _p(x), _p(w), _p(xq["offsets"]),
+                               _p(out["dx"]), _p(out["dw"]), _p(ws), ws.numel(), _stream()))
     return out
 
 

@@ -202,6 +202,10 @@ int64_t w4a4_rows_capacity(int64_t T, int k, int E, int row_align) {
 }
 
 size_t w4a4_workspace_size(int kind, int64_t T, int H, int I, int E, int k, int row_align) {
+  if (kind == W4A4_WS_LINEAR_BACKWARD) {   // H = K (in features), I = N (out features)
+    if (H <= 0 || I <= 0 || H % 256 || I % 256) return 0;
+    return round_up(linear_wgrad_schedule_ints(H, I) * 4);
+  }
   const int64_t cap = w4a4_rows_capacity(T, k, E, row_align);
   if (cap < 0 || H <= 0) return 0;
   switch (kind) {
@@ -390,6 +394,61 @@ w4a4_status w4a4_expert_bwd(int64_t T, int H, int I, int E, int k, int row_align
   if (!launch_gather_sum(T, H, k, dXp, row_map, static_cast<uint16_t*>(dx), side.stream))
     return W4A4_ERR_LAUNCH;
   if (!join(1)) return fail(W4A4_ERR_LAUNCH, "join from the side stream failed");
+  return W4A4_OK;
+}
+
+namespace {
+w4a4_status check_linear_shape(int64_t T, int K, int N) {
+  if (T < 0 || K <= 0 || N <= 0)
+    return fail(W4A4_ERR_INVALID_ARG, "non-positive size (T=%lld K=%d N=%d)", static_cast<long long>(T), K, N);
+  if (K % 256 || N % 256)
+    return fail(W4A4_ERR_UNSUPPORTED, "kernels need K %% 256 == 0 and N %% 256 == 0 (K=%d N=%d)", K, N);
+  if (K > kMaxRowLen || N > kMaxRowLen)
+    return fail(W4A4_ERR_UNSUPPORTED, "K and N must be <= %d", kMaxRowLen);
+  if (T > (int64_t{1} << 31) - 1) return fail(W4A4_ERR_UNSUPPORTED, "T must be < 2^31");
+  return W4A4_OK;
+}
+}  // namespace
+
+w4a4_status w4a4_linear_fwd(int64_t T, int K, int N, const uint8_t* x_codes, const uint8_t* x_scales,
+                            const float* x_outer, const int32_t* offsets, const uint8_t* w_codes,
+                            const uint8_t* w_scales, const float* w_outer, void* y, void* stream) {
+  g_last_error.clear();
+  w4a4_status st = check_linear_shape(T, K, N);
+  if (st != W4A4_OK) return st;
+  REQUIRE_PTR(w_codes); REQUIRE_PTR(w_scales); REQUIRE_PTR(w_outer);
+  if (T == 0) return W4A4_OK;
+  REQUIRE_PTR(x_codes); REQUIRE_PTR(x_scales); REQUIRE_PTR(x_outer); REQUIRE_PTR(offsets);
+  REQUIRE_PTR(y);
+  if (!launch_linear_fwd(T, K, N, offsets, Fp4Operand{x_codes, x_scales, x_outer},
+                         Fp4Operand{w_codes, w_scales, w_outer}, static_cast<uint16_t*>(y),
+                         static_cast<hipStream_t>(stream)))
+    return W4A4_ERR_LAUNCH;
+  return W4A4_OK;
+}
+
+w4a4_status w4a4_linear_bwd(int64_t T, int K, int N, const void* dy, const void* x, const void* w,
+                            const int32_t* offsets, void* dx, void* dw, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  w4a4_status st = check_linear_shape(T, K, N);
+  if (st != W4A4_OK) return st;
+  REQUIRE_PTR(w); REQUIRE_PTR(dw); REQUIRE_PTR(offsets);
+  if (T > 0) {
+    REQUIRE_PTR(dy); REQUIRE_PTR(x); REQUIRE_PTR(dx);
+  }
+  const size_t need = round_up(linear_wgrad_schedule_ints(K, N) * 4);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(W4A4_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  OPTIONAL_PTR(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint16_t* DY = static_cast<const uint16_t*>(dy);
+  if (T > 0 && !launch_linear_dgrad(T, K, N, offsets, DY, static_cast<const uint16_t*>(w),
+                                    static_cast<uint16_t*>(dx), s))
+    return W4A4_ERR_LAUNCH;
+  if (!launch_linear_wgrad(T, K, N, offsets, DY, static_cast<const uint16_t*>(x),
+                           static_cast<uint16_t*>(dw), static_cast<int32_t*>(workspace), s))
+    return W4A4_ERR_LAUNCH;
   return W4A4_OK;
 }
 

@@ -499,7 +499,7 @@ constexpr int kSchedBegin = 0, kSchedCount = 8, kSchedCounters = 16, kSchedTable
 struct SchedGemm {
   int tpe;       // tiles per expert
   int per_xcd;   // workgroups per XCD of the GEMM's grid
-  int32_t* out;  // kSchedTable + 4 E tpe ints
+  int32_t* out;  // kSchedTable + 4 E tpe ints (nullptr: no GEMM)
 };
 
 // Inclusive prefix sum over the workgroup (1024 threads); `total` gets the
@@ -558,6 +558,7 @@ schedule_kernel(const int32_t* __restrict__ offsets, int E, SchedGemm g0, SchedG
   block_scan(c, cost_sum, s_wave);
   for (int g = 0; g < 2; ++g) {
     const SchedGemm p = g ? g1 : g0;
+    if (p.out == nullptr) continue;   // (the same in every thread)
     const int64_t tpe = p.tpe, tiles = tpe * E, total = tpe * cost_sum;
     // split an expert whose tiles, run whole on one XCD, would take longer
     // than the ideal share of one workgroup
@@ -1004,6 +1005,25 @@ bool launch_wgrad_fc1(int H, int I, int E, const uint16_t* dH, const uint16_t* x
                       int32_t* sched, hipStream_t s) {
   wg::WgradArgs w{2 * I, H, E, dH, xp, dW1, sched + wgrad_sched_ints(wgrad_plan(H, I, E))};
   return launch_wgrad(w, "gemm_wgrad_fc1", s);
+}
+
+size_t linear_wgrad_schedule_ints(int K, int N) { return wgrad_sched_ints(wgrad_plan(N, K, 1)); }
+
+bool launch_linear_dgrad(int64_t T, int K, int N, const int32_t* offsets, const uint16_t* dy,
+                         const uint16_t* w, uint16_t* dx, hipStream_t s) {
+  dg::DgradArgs a{T, N, K, N / 2, 1, offsets, dy, w, nullptr, dx};
+  return launch_dgrad<dg::DgradMode::FC1>(a, "gemm_linear_dgrad", s);
+}
+
+bool launch_linear_wgrad(int64_t T, int K, int N, const int32_t* offsets, const uint16_t* dy,
+                         const uint16_t* x, uint16_t* dw, int32_t* sched, hipStream_t s) {
+  (void)T;
+  const WgradPlan p = wgrad_plan(N, K, 1);
+  launch_kernel("wgrad_schedule", wg::schedule_kernel, dim3(1), dim3(1024), 0, s, offsets, 1,
+                wg::SchedGemm{p.tpe, p.per_xcd, sched}, wg::SchedGemm{0, 1, nullptr});
+  if (!launch_ok("wgrad_schedule")) return false;
+  wg::WgradArgs w{N, K, 1, dy, x, dw, sched};
+  return launch_wgrad(w, "gemm_linear_wgrad", s);
 }
 
 }  // namespace w4a4

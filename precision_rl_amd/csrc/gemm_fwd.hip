@@ -473,4 +473,10 @@ bool launch_fc2(int64_t rows_alloc, int H, int I, int E, const int32_t* offsets,
   return launch_fwd<FwdMode::FC2>(args, H / kBN, "gemm_fc2", s);
 }
 
+bool launch_linear_fwd(int64_t T, int K, int N, const int32_t* offsets, Fp4Operand x, Fp4Operand w,
+                       uint16_t* y, hipStream_t s) {
+  FwdArgs args{T, K, N, K, 1, offsets, x, w, y, nullptr, nullptr};
+  return launch_fwd<FwdMode::FC2>(args, N / kBN, "gemm_linear", s);
+}
+
 }  // namespace w4a4

@@ -67,6 +67,10 @@ bool launch_fc1(int64_t rows_alloc, int H, int I, int E, const int32_t* offsets,
 bool launch_fc2(int64_t rows_alloc, int H, int I, int E, const int32_t* offsets, Fp4Operand a,
                 Fp4Operand w2, uint16_t* o_out, hipStream_t s);
 
+// Dense linear layer y = x W^T (one group of T rows; offsets = {0, T}).
+bool launch_linear_fwd(int64_t T, int K, int N, const int32_t* offsets, Fp4Operand x, Fp4Operand w,
+                       uint16_t* y, hipStream_t s);
+
 // Unpermute: y[t] = bf16(sum_j p[t,j] o[row_map[t,j]]).
 bool launch_unpermute(int64_t T, int H, int k, const uint16_t* o, const int32_t* row_map,
                       const float* topk_w, uint16_t* y, hipStream_t s);
@@ -104,6 +108,15 @@ bool launch_wgrad_fc2(int H, int I, int E, const uint16_t* dO, const uint16_t* a
                       int32_t* sched, hipStream_t s);
 bool launch_wgrad_fc1(int H, int I, int E, const uint16_t* dH, const uint16_t* xp, uint16_t* dW1,
                       int32_t* sched, hipStream_t s);
+
+// Dense linear backward: dx = bf16(dy W) [T, K]; dw = bf16(dy^T x) [N, K]
+// (the wgrad launch computes its tile schedule first, into `sched` of
+// linear_wgrad_schedule_ints(K, N) ints).
+size_t linear_wgrad_schedule_ints(int K, int N);
+bool launch_linear_dgrad(int64_t T, int K, int N, const int32_t* offsets, const uint16_t* dy,
+                         const uint16_t* w, uint16_t* dx, hipStream_t s);
+bool launch_linear_wgrad(int64_t T, int K, int N, const int32_t* offsets, const uint16_t* dy,
+                         const uint16_t* x, uint16_t* dw, int32_t* sched, hipStream_t s);
 
 // dX gather-sum: dX[t] = bf16(sum_j dXp[row_map[t,j]]).
 bool launch_gather_sum(int64_t T, int H, int k, const uint16_t* dXp, const int32_t* row_map,
