@@ -86,12 +86,15 @@ def route_fast(topk_idx, E, row_align=1):
 # ---------------------------------------------------------------------------
 # Quantize + permute (per-token amax, encode, scatter).
 # ---------------------------------------------------------------------------
-def quantize_permute(x, topk_idx, E, row_align=1, routed=None):
+def quantize_permute(x, topk_idx, E, row_align=1, routed=None, group_rows=1):
     """Per-token NVFP4 of x, written to every destination row of the token.
 
     The amax is per token (per dispatched row; the k copies of a token are
     identical because the scale domain is the row), as in the rainbus
     review's method step 4.  Pad rows get codes 0, scales 0 and g = 0.
+    With ``group_rows`` > 1 the outer scale is shared by groups of that many
+    consecutive tokens (group_rows = T: the per-tensor variant);
+    see nvfp4.quantize_rows_grouped.
 
     Returns dict(codes [rows, K] unpacked, packed [rows, K/2], scales
     [rows, K/16], outer [rows], offsets, row_map, src_row).
@@ -102,7 +105,7 @@ def quantize_permute(x, topk_idx, E, row_align=1, routed=None):
     offsets, row_map, src_row = routed
     rows = int(offsets[-1])
     T, K = x.shape
-    tc, ts, tg = q.quantize_rows(x)          # token rows; copies share them
+    tc, ts, tg = q.quantize_rows_grouped(x, group_rows)   # token rows; copies share them
     codes = np.zeros((rows, K), dtype=np.uint8)
     scales = np.zeros((rows, K // q.BLOCK), dtype=np.uint8)
     outer = np.zeros(rows, dtype=np.float32)
@@ -114,16 +117,17 @@ def quantize_permute(x, topk_idx, E, row_align=1, routed=None):
                 offsets=offsets, row_map=row_map, src_row=src_row)
 
 
-def quantize_weights(w):
+def quantize_weights(w, per_expert=False):
     """Offline weight quantisation: per-row NVFP4 of stacked expert weights [E, N, K] (per output row n).
 
     READING of "per row of the flattened expert weights" (Technical Report,
     section 4.3 table): one outer scale per output feature n, over the
-    reduction axis K.
+    reduction axis K.  ``per_expert``: one outer scale per expert weight
+    tensor instead (the table's miniTE CUTLASS column), stored once per row.
     """
     w = np.asarray(w, dtype=np.float64)
     E, N, K = w.shape
-    c, s, g = q.quantize_rows(w.reshape(E * N, K))
+    c, s, g = q.quantize_rows_grouped(w.reshape(E * N, K), N if per_expert else 1)
     return dict(codes=c.reshape(E, N, K), packed=q.pack_codes(c).reshape(E, N, K // 2),
                 scales=s.reshape(E, N, K // q.BLOCK), outer=g.reshape(E, N))
 
@@ -174,7 +178,7 @@ def swiglu(h, I):
     return gate / (1.0 + np.exp(-gate)) * up
 
 
-def forward(x, topk_idx, topk_w, w1q, w2q, E, row_align=1):
+def forward(x, topk_idx, topk_w, w1q, w2q, E, row_align=1, act_group_rows=1):
     """Whole forward: quantize+permute, FC1, SwiGLU, requantize, FC2, unpermute.
 
     Cast points (READING of "casts to BF16 only at the end", AI summary):
@@ -182,11 +186,13 @@ def forward(x, topk_idx, topk_w, w1q, w2q, E, row_align=1):
     Router coefficients (READING; their position is an explicit
     implementation freedom on the pages): applied in the unpermute, to the
     bf16 o, summed over j in ascending order, one final bf16 rounding.
+    ``act_group_rows``: outer-scale domain of the input activations (1 per
+    token; T per tensor); the FC2 input stays per dispatched row.
     """
     x = np.asarray(x, dtype=np.float64)
     T, H = x.shape
     I = w1q["codes"].shape[1] // 2
-    xq = quantize_permute(x, topk_idx, E, row_align)
+    xq = quantize_permute(x, topk_idx, E, row_align, group_rows=act_group_rows)
     h64 = grouped_gemm_nvfp4(xq["codes"], xq["scales"], xq["outer"], xq["offsets"],
                              w1q["codes"], w1q["scales"], w1q["outer"])
     h = q.round_bf16(h64)

@@ -154,7 +154,7 @@ def round_f32(v):
 # ---------------------------------------------------------------------------
 # Row quantiser.
 # ---------------------------------------------------------------------------
-def quantize_rows(x):
+def quantize_rows(x, scale_amax=None):
     """Two-level NVFP4 quantisation of each row of ``x`` (float64, bf16 values).
 
     Follows the block-scale equation of the miniTE Technical Report, section
@@ -173,6 +173,9 @@ def quantize_rows(x):
     (g = 0) or an underflowed block (d_b = 0) encodes every element as a zero
     code carrying the sign bit of x.
 
+    ``scale_amax`` (float64 [R]), when given, replaces the row's own max in
+    step 1: the outer scale of a wider scale domain (quantize_rows_grouped).
+
     Returns (codes uint8 [R, K] unpacked 0..15, scales uint8 [R, K/16] E4M3
     bytes, outer float32 [R]).
     """
@@ -183,7 +186,10 @@ def quantize_rows(x):
     ax = np.abs(x)
 
     # 1-2: per-row outer scale, stored as float32.
-    a = ax.max(axis=1) if K else np.zeros(R)
+    if scale_amax is not None:
+        a = np.asarray(scale_amax, dtype=np.float64)
+    else:
+        a = ax.max(axis=1) if K else np.zeros(R)
     g32 = round_f32(a / OUTER_DIVISOR)
     g = g32.astype(np.float64)
 
@@ -203,6 +209,27 @@ def quantize_rows(x):
     codes = e2m1_magnitude_code(mag).reshape(R, K)
     codes |= (np.signbit(x).astype(np.uint8) << 3)
     return codes, scales, g32
+
+
+def quantize_rows_grouped(x, group_rows):
+    """quantize_rows with one outer scale per group of ``group_rows``
+    consecutive rows (the last group may be shorter): step 1 takes the max
+    over the whole group.  group_rows = 1 is the per-row domain; R the
+    per-tensor domain; the rows of one expert's weight the per-expert domain
+    (miniTE Technical Report, section 2.2: the recipe decides whether the
+    outer scale is per tensor, per expert or per row; section 4.3 table:
+    miniTE CUTLASS keeps one outer scale per expert weight tensor).  Block
+    scales and codes are per row as before, against the group's g.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    R = x.shape[0]
+    if group_rows < 1:
+        raise ValueError("group_rows >= 1")
+    row_max = np.abs(x).max(axis=1) if x.shape[1] else np.zeros(R)
+    grp = np.arange(R) // group_rows
+    gmax = np.zeros(grp.max() + 1 if R else 0)
+    np.maximum.at(gmax, grp, row_max)
+    return quantize_rows(x, scale_amax=gmax[grp])
 
 
 def pack_codes(codes):
