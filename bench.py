@@ -193,6 +193,93 @@ def main_linear(args):
     print(json.dumps(out), flush=True)
 
 
+QP_METRIC = "W4A4 quantize+permute tokens/s and % HBM peak (route + per-row amax + NVFP4 encode + scatter)"
+
+
+def qp_work(T, H, k, outer):
+    """Per-launch algorithmic bytes of quantize+permute (c2 shape)."""
+    M = T * k
+    by = {"quantize_scatter": T * (H * 2 + k * 4) + M * (H // 2 + H // 16 + 4) + T * k * 4 + M * 4}
+    if outer == "tensor":
+        by["group_amax"] = T * H * 2     # one extra read of x
+    return {}, by
+
+
+def cpu_baseline_qp(d, tokens, group_rows):
+    from oracle import moe, nvfp4 as q
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    x = q.bf16_bits_to_f64(d["x"][:tokens])
+    idx = d["topk_idx"][:tokens]
+    E = int(d["topk_idx"].max()) + 1
+    t0 = time.perf_counter()
+    moe.quantize_permute(x, idx, E, 1, group_rows=min(group_rows, tokens))
+    dt = time.perf_counter() - t0
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{tokens} tokens of the quantize+permute workload, FP64 numpy, {dt:.1f} s",
+            "seconds": dt, "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main_qp(args):
+    import torch
+    from precision_rl_amd import binding as b, synth
+
+    w = synth.WORKLOADS["qp"]
+    T, H, E, k = w.T, w.H, w.E, w.k
+    d = synth.workload_inputs("qp")
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).to(dev)
+    idx = torch.from_numpy(d["topk_idx"]).to(dev)
+    cap = b.rows_capacity(T, k, E, 1)
+    xq = dict(codes=torch.empty(cap, H // 2, dtype=torch.uint8, device=dev),
+              scales=torch.empty(cap, H // 16, dtype=torch.uint8, device=dev),
+              outer=torch.empty(cap, dtype=torch.float32, device=dev),
+              offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+              row_map=torch.empty(T, k, dtype=torch.int32, device=dev),
+              src_row=torch.empty(cap, dtype=torch.int32, device=dev))
+    per_tensor = args.outer == "tensor"
+    kind = b.WS_QUANTIZE_PERMUTE_DOMAIN if per_tensor else b.WS_QUANTIZE_PERMUTE
+    ws = torch.empty(b.workspace_size(kind, T, H, 0, E, k, 1) + 256, dtype=torch.uint8, device=dev)
+    calibration_copy(torch, dev)
+
+    def step():
+        if per_tensor:
+            b.w4a4_quantize_permute_domain(x, idx, E, 1, group_rows=T, out=xq, workspace=ws)
+        else:
+            b.w4a4_quantize_permute(x, idx, E, 1, out=xq, workspace=ws)
+
+    ms, kern = time_steps(b, torch, step, args)
+    fl, by = qp_work(T, H, k, args.outer)
+    per_kernel, roof = summarize(kern, ms, args.steps, fl, by)
+    alg = sum(by.values()) - by.get("group_amax", 0)
+    out = {
+        "metric": QP_METRIC,
+        "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 -> nvfp4 (u8 codes, e4m3 scales, f32 outer)",
+        "data": "synthetic (seeded; Student-t x)",
+        "config": {"workload": f"qp: route + quantize+permute, outer scale per {args.outer}",
+                   "T": T, "H": H, "E": E, "top_k": k},
+        "roofline": roof,
+        "call_hbm_frac": round(alg / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "kernels": per_kernel,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the FP64 oracle on the host", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline_qp(d, 8192, T if per_tensor else 1)
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline(d, w, tokens=512, experts=8):
     """The FP64 oracle on a bounded sample of the learner workload: the first
     `tokens` tokens, each routed to all `experts` experts (k = 8 per token as
@@ -300,8 +387,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=6144)
-    ap.add_argument("--workload", choices=["learner", "linear"], default="learner",
-                    help="learner: the MoE expert step (default); linear: the dense projection")
+    ap.add_argument("--workload", choices=["learner", "linear", "qp"], default="learner",
+                    help="learner: the MoE expert step (default); linear: the dense projection; "
+                         "qp: quantize+permute alone")
+    ap.add_argument("--outer", choices=["token", "tensor"], default="token",
+                    help="qp: outer-scale domain of the activations")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: the benchmark runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -311,6 +401,8 @@ def main():
 
     if args.workload == "linear":
         return main_linear(args)
+    if args.workload == "qp":
+        return main_qp(args)
 
     import torch
     from precision_rl_amd import binding as b, synth

@@ -69,7 +69,8 @@ typedef enum {
   W4A4_WS_QUANTIZE_PERMUTE = 0,
   W4A4_WS_FORWARD = 1,
   W4A4_WS_BACKWARD = 2,
-  W4A4_WS_LINEAR_BACKWARD = 3   /* w4a4_linear_bwd: H = K, I = N; T, E, k, row_align unused */
+  W4A4_WS_LINEAR_BACKWARD = 3,  /* w4a4_linear_bwd: H = K, I = N; T, E, k, row_align unused */
+  W4A4_WS_QUANTIZE_PERMUTE_DOMAIN = 4   /* w4a4_quantize_permute_domain, any group_rows; H = K */
 } w4a4_workspace_kind;
 
 /* Padded dispatched-row capacity: T*k + E*(row_align-1).  Returns -1 on bad
@@ -107,6 +108,37 @@ size_t w4a4_workspace_size(int kind, int64_t T, int H, int I, int E, int k, int 
 w4a4_status w4a4_quantize_permute(
     const void* x, int64_t T, int K,
     const int32_t* topk_idx, int k, int E, int row_align,
+    uint8_t* codes, uint8_t* scales, float* outer,
+    int32_t* expert_offsets, int32_t* row_map, int32_t* src_row,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * w4a4_quantize_permute_domain -- w4a4_quantize_permute with an outer-scale
+ * domain wider than a row: one FP32 outer scale per group of `group_rows`
+ * consecutive input rows (the last group may be shorter).
+ *   Defined by: miniTE Technical Report, section 2.2 (the recipe decides
+ *   whether the outer scale is per tensor, per expert or per row) and the
+ *   section 4.3 table (miniTE CUTLASS: one outer scale per expert weight
+ *   tensor); AI summary, "Methodology in Plain English" (the per-tensor
+ *   reference breaks the context-swap invariance that per-token scales keep).
+ *
+ *   g = RN_f32(max |x| over the group / (6*448)); every row of the group is
+ *   then encoded as in w4a4_quantize_permute against that g (block scales
+ *   and codes per row), and every destination row stores the group's g in
+ *   `outer`, so the GEMM entry points consume the result unchanged.
+ *   group_rows = 1: per token (the same result as w4a4_quantize_permute);
+ *   group_rows = T: per tensor; identity routing over the E*N rows of stacked
+ *   expert weights [E, N, K] with group_rows = N: per expert weight tensor.
+ *
+ *   Arguments and outputs as w4a4_quantize_permute.  Requirements: also
+ *   K % 32 == 0 and K <= 4096 (else W4A4_ERR_UNSUPPORTED); group_rows >= 1.
+ *   workspace: w4a4_workspace_size(W4A4_WS_QUANTIZE_PERMUTE_DOMAIN, T, K,
+ *   0, E, k, row_align) bytes (also for identity routing).  Adds one pass
+ *   over x (the group maxima) before the encoding.
+ */
+w4a4_status w4a4_quantize_permute_domain(
+    const void* x, int64_t T, int K,
+    const int32_t* topk_idx, int k, int E, int row_align, int64_t group_rows,
     uint8_t* codes, uint8_t* scales, float* outer,
     int32_t* expert_offsets, int32_t* row_map, int32_t* src_row,
     void* workspace, size_t workspace_bytes, void* stream);

@@ -29,6 +29,8 @@ _SIGS = {
     "w4a4_expert_bwd": (c_int, [c_i64, c_int, c_int, c_int, c_int, c_int,
                                 c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                 c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "w4a4_quantize_permute_domain": (c_int, [c_vp, c_i64, c_int, c_vp, c_int, c_int, c_int, c_i64,
+                                             c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "w4a4_linear_fwd": (c_int, [c_i64, c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                 c_vp, c_vp]),
     "w4a4_linear_bwd": (c_int, [c_i64, c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
@@ -40,6 +42,7 @@ _SIGS = {
 }
 
 WS_QUANTIZE_PERMUTE, WS_FORWARD, WS_BACKWARD, WS_LINEAR_BACKWARD = 0, 1, 2, 3
+WS_QUANTIZE_PERMUTE_DOMAIN = 4
 
 
 class W4A4Error(RuntimeError):
@@ -127,11 +130,43 @@ def w4a4_quantize_permute(x, topk_idx, E, row_align=1, out=None, workspace=None)
     return out
 
 
-def quantize_weights(w):
-    """Per-row NVFP4 of stacked expert weights w [E, N, K] bf16 (offline, identity routing).
+def w4a4_quantize_permute_domain(x, topk_idx, E, row_align=1, group_rows=1, out=None, workspace=None):
+    """w4a4_quantize_permute with one outer scale per group of `group_rows` consecutive
+    input rows (T: per tensor).  Same outputs."""
+    lib = load()
+    T, K = x.shape
+    dev = x.device
+    if topk_idx is None:
+        k, E, row_align = 1, 1, 1
+    else:
+        k = topk_idx.shape[1]
+    cap = rows_capacity(T, k, E, row_align)
+    if out is None:
+        out = dict(
+            codes=torch.empty(cap, K // 2, dtype=torch.uint8, device=dev),
+            scales=torch.empty(cap, K // 16, dtype=torch.uint8, device=dev),
+            outer=torch.empty(cap, dtype=torch.float32, device=dev),
+            offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+            row_map=torch.empty(T, k, dtype=torch.int32, device=dev),
+            src_row=torch.empty(cap, dtype=torch.int32, device=dev))
+    need = workspace_size(WS_QUANTIZE_PERMUTE_DOMAIN, T, K, 0, E, k, row_align)
+    ws = _workspace(need, dev, workspace)
+    _check(lib.w4a4_quantize_permute_domain(
+        _p(x), T, K, _p(topk_idx), k, E, row_align, group_rows,
+        _p(out["codes"]), _p(out["scales"]), _p(out["outer"]), _p(out["offsets"]),
+        _p(out["row_map"]), _p(out["src_row"]), _p(ws), ws.numel(), _stream()))
+    return out
+
+
+def quantize_weights(w, per_expert=False):
+    """NVFP4 of stacked expert weights w [E, N, K] bf16 (offline, identity routing): one
+    outer scale per row, or per expert weight tensor with `per_expert`.
     Returns dict(codes [E, N, K/2], scales [E, N, K/16], outer [E, N])."""
     E, N, K = w.shape
-    q = w4a4_quantize_permute(w.reshape(E * N, K), None, 1)
+    if per_expert:
+        q = w4a4_quantize_permute_domain(w.reshape(E * N, K), None, 1, group_rows=N)
+    else:
+        q = w4a4_quantize_permute(w.reshape(E * N, K), None, 1)
     return dict(codes=q["codes"].view(E, N, K // 2), scales=q["scales"].view(E, N, K // 16),
                 outer=q["outer"].view(E, N))
 

@@ -211,6 +211,8 @@ size_t w4a4_workspace_size(int kind, int64_t T, int H, int I, int E, int k, int 
   switch (kind) {
     case W4A4_WS_QUANTIZE_PERMUTE:
       return round_up(route_workspace_bytes(T, E));
+    case W4A4_WS_QUANTIZE_PERMUTE_DOMAIN:   // any group_rows >= 1
+      return round_up(route_workspace_bytes(T, E)) + round_up(grouped_amax_bytes(T, 1));
     case W4A4_WS_FORWARD:
       if (I <= 0) return 0;
       return fwd_ws(cap, H, I).total;
@@ -222,12 +224,12 @@ size_t w4a4_workspace_size(int kind, int64_t T, int H, int I, int E, int k, int 
   }
 }
 
-w4a4_status w4a4_quantize_permute(const void* x, int64_t T, int K, const int32_t* topk_idx, int k,
-                                  int E, int row_align, uint8_t* codes, uint8_t* scales,
-                                  float* outer, int32_t* expert_offsets, int32_t* row_map,
-                                  int32_t* src_row, void* workspace, size_t workspace_bytes,
-                                  void* stream) {
-  g_last_error.clear();
+namespace {
+// Argument checks shared by the two quantize+permute entry points.
+w4a4_status check_quantize_permute(const void* x, int64_t T, int K, const int32_t* topk_idx, int k,
+                                   int E, int row_align, uint8_t* codes, uint8_t* scales,
+                                   float* outer, int32_t* expert_offsets, int32_t* row_map,
+                                   int32_t* src_row) {
   if (T < 0) return fail(W4A4_ERR_INVALID_ARG, "T < 0");
   if (K < 16 || K % 16) return fail(W4A4_ERR_INVALID_ARG, "K=%d must be a positive multiple of 16", K);
   if (K > kMaxRowLen) return fail(W4A4_ERR_UNSUPPORTED, "K=%d > %d", K, kMaxRowLen);
@@ -252,6 +254,45 @@ w4a4_status w4a4_quantize_permute(const void* x, int64_t T, int K, const int32_t
   }
   if (T * static_cast<int64_t>(k) > (int64_t{1} << 31) - 1)
     return fail(W4A4_ERR_UNSUPPORTED, "T*k exceeds int32 row indices");
+  return W4A4_OK;
+}
+}  // namespace
+
+w4a4_status w4a4_quantize_permute_domain(const void* x, int64_t T, int K, const int32_t* topk_idx,
+                                         int k, int E, int row_align, int64_t group_rows,
+                                         uint8_t* codes, uint8_t* scales, float* outer,
+                                         int32_t* expert_offsets, int32_t* row_map, int32_t* src_row,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  w4a4_status st = check_quantize_permute(x, T, K, topk_idx, k, E, row_align, codes, scales, outer,
+                                          expert_offsets, row_map, src_row);
+  if (st != W4A4_OK) return st;
+  if (group_rows < 1) return fail(W4A4_ERR_INVALID_ARG, "group_rows=%lld < 1", static_cast<long long>(group_rows));
+  if (K % 32 || K > 4096)
+    return fail(W4A4_ERR_UNSUPPORTED, "grouped outer scales need K %% 32 == 0 and K <= 4096 (K=%d)", K);
+  const size_t route = round_up(route_workspace_bytes(T, topk_idx ? E : 1));
+  const size_t need = route + round_up(grouped_amax_bytes(T, group_rows));
+  if (T > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(W4A4_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  OPTIONAL_PTR(workspace);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  if (!launch_quantize_permute_grouped(static_cast<const uint16_t*>(x), T, K, topk_idx, k, E, row_align,
+                                       group_rows, codes, scales, outer, expert_offsets, row_map, src_row,
+                                       ws, T > 0 ? reinterpret_cast<uint32_t*>(ws + route) : nullptr,
+                                       static_cast<hipStream_t>(stream)))
+    return W4A4_ERR_LAUNCH;
+  return W4A4_OK;
+}
+
+w4a4_status w4a4_quantize_permute(const void* x, int64_t T, int K, const int32_t* topk_idx, int k,
+                                  int E, int row_align, uint8_t* codes, uint8_t* scales,
+                                  float* outer, int32_t* expert_offsets, int32_t* row_map,
+                                  int32_t* src_row, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  g_last_error.clear();
+  w4a4_status st = check_quantize_permute(x, T, K, topk_idx, k, E, row_align, codes, scales, outer,
+                                          expert_offsets, row_map, src_row);
+  if (st != W4A4_OK) return st;
   const size_t need = w4a4_workspace_size(W4A4_WS_QUANTIZE_PERMUTE, T, K, 0, E, k, row_align);
   if (topk_idx != nullptr && T > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(W4A4_ERR_WORKSPACE, "workspace needs %zu bytes", need);

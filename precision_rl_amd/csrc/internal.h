@@ -48,6 +48,16 @@ bool launch_quantize_permute(const uint16_t* x, int64_t T, int K, const int32_t*
 
 // Requantise: per-row NVFP4 of the bf16 rows of `a` ([rows_alloc, K]) for the rows
 // [0, offsets[E]) (device bound); pad rows (src_row < 0) get zeros.
+// Quantize + permute with one outer scale per group of group_rows consecutive
+// input rows (group_rows = T: per tensor; the rows of one expert's weight:
+// per expert).  amax: grouped_amax_bytes(T, group_rows) bytes of scratch.
+// Only for K % 32 == 0, K <= 4096 (returns false otherwise).
+size_t grouped_amax_bytes(int64_t T, int64_t group_rows);
+bool launch_quantize_permute_grouped(const uint16_t* x, int64_t T, int K, const int32_t* topk_idx,
+                                     int k, int E, int row_align, int64_t group_rows, uint8_t* codes,
+                                     uint8_t* scales, float* outer, int32_t* offsets, int32_t* row_map,
+                                     int32_t* src_row, void* ws, uint32_t* amax, hipStream_t s);
+
 bool launch_requant(const uint16_t* a, int64_t rows_alloc, int K, const int32_t* offsets, int E,
                     const int32_t* src_row, uint8_t* codes, uint8_t* scales, float* outer,
                     hipStream_t s);

@@ -490,7 +490,8 @@ quant_rows_kernel(const uint16_t* __restrict__ x, int64_t n_rows, int K,
                   const int32_t* __restrict__ topk_idx, int k, int E,
                   uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ outer,
                   int32_t* __restrict__ offsets, int32_t* __restrict__ row_map,
-                  int32_t* __restrict__ src_row, const int32_t* __restrict__ chunk_base) {
+                  int32_t* __restrict__ src_row, const int32_t* __restrict__ chunk_base,
+                  const uint32_t* __restrict__ group_amax, int64_t group_rows) {
   constexpr int kRowsPerWave = kWave / TEAM;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int team = lane / TEAM, tl = lane % TEAM;
@@ -533,6 +534,8 @@ quant_rows_kernel(const uint16_t* __restrict__ x, int64_t n_rows, int K,
     }
 #pragma unroll
     for (int off = TEAM / 2; off > 0; off >>= 1) amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), off, kWave)));
+    // a wider outer-scale domain: the group's max instead of the row's
+    if (group_amax != nullptr) amax = group_amax[r / group_rows];
     const float g = outer_scale(amax);
 
     // destination rows
@@ -630,7 +633,8 @@ pad_rows_kernel(int K, int E, const int32_t* __restrict__ offsets, const int32_t
 template <RowMode MODE>
 bool launch_rows(const char* name, const uint16_t* x, int64_t n_rows, int K, const int32_t* topk_idx, int k,
                  int E, uint8_t* codes, uint8_t* scales, float* outer, int32_t* offsets,
-                 int32_t* row_map, int32_t* src_row, const int32_t* chunk_base, hipStream_t s) {
+                 int32_t* row_map, int32_t* src_row, const int32_t* chunk_base, hipStream_t s,
+                 const uint32_t* group_amax = nullptr, int64_t group_rows = 1) {
   const int pairs = K / 32;
   auto go = [&](auto team, auto pb) {
     constexpr int TEAM = decltype(team)::value, PB = decltype(pb)::value;
@@ -643,7 +647,8 @@ bool launch_rows(const char* name, const uint16_t* x, int64_t n_rows, int K, con
     const int64_t blocks = std::min<int64_t>(need, static_cast<int64_t>(device_cu_count()) * 16);
     if (blocks == 0) return true;
     launch_kernel(name, quant_rows_kernel<TEAM, PB, MODE>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
-                  s, x, n_rows, K, topk_idx, k, E, codes, scales, outer, offsets, row_map, src_row, chunk_base);
+                  s, x, n_rows, K, topk_idx, k, E, codes, scales, outer, offsets, row_map, src_row, chunk_base,
+                  group_amax, group_rows);
     return launch_ok(name);
   };
   // One block pair per lane in a team that covers the row (a wave then
@@ -663,6 +668,55 @@ bool launch_rows(const char* name, const uint16_t* x, int64_t n_rows, int K, con
 }
 
 bool rows_path(int K) { return K % 32 == 0 && K <= 4096; }
+
+__global__ void zero_u32_kernel(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    p[i] = 0u;
+}
+
+// Max |x| (bf16 magnitude bits) of each group of group_rows consecutive rows
+// into amax[group] (zeroed before).  Workgroup b covers rows [b R, b R + R);
+// the segment of each group in it is reduced over the workgroup and merged
+// with one atomic max (exact and order-independent: bf16 magnitudes compare
+// as integers).
+constexpr int kAmaxThreads = 256;
+__global__ void __launch_bounds__(kAmaxThreads)
+group_amax_kernel(const uint16_t* __restrict__ x, int64_t n_rows, int K, int64_t group_rows,
+                  int64_t rows_per_block, uint32_t* __restrict__ amax) {
+  __shared__ uint32_t s_wave[kAmaxThreads / kWave];
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * rows_per_block;
+  const int64_t r1 = min(n_rows, r0 + rows_per_block);
+  for (int64_t a = r0; a < r1;) {
+    const int64_t grp = a / group_rows;
+    const int64_t b = min(r1, (grp + 1) * group_rows);
+    const int64_t chunks = (b - a) * K / 8;   // 16-byte chunks (K % 32 == 0)
+    const u32x4_t* p = reinterpret_cast<const u32x4_t*>(x + a * K);
+    uint32_t m = 0;
+#pragma unroll 4
+    for (int64_t i = threadIdx.x; i < chunks; i += kAmaxThreads) {
+      const u32x4_t v = __builtin_nontemporal_load(p + i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = v[j] & 0x7FFF7FFFu;
+        m = max(m, max(w & 0xFFFFu, w >> 16));
+      }
+    }
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1)
+      m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), off, kWave)));
+    if (threadIdx.x % kWave == 0) s_wave[threadIdx.x / kWave] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t t = 0;
+#pragma unroll
+      for (int w = 0; w < kAmaxThreads / kWave; ++w) t = max(t, s_wave[w]);
+      if (t > 0) atomicMax(amax + grp, t);
+    }
+    __syncthreads();
+    a = b;
+  }
+}
 
 __global__ void zero_offsets_kernel(int32_t* offsets, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) offsets[i] = 0;
@@ -731,6 +785,56 @@ bool launch_quantize_permute(const uint16_t* x, int64_t T, int K, const int32_t*
                   codes, scales, outer, offsets, row_map, src_row, counts, expert_count, token_blocks);
     return launch_ok("quantize_scatter");
   });
+}
+
+size_t grouped_amax_bytes(int64_t T, int64_t group_rows) {
+  const int64_t groups = group_rows > 0 ? (T + group_rows - 1) / group_rows : 0;
+  return static_cast<size_t>(groups) * sizeof(uint32_t);
+}
+
+bool launch_quantize_permute_grouped(const uint16_t* x, int64_t T, int K, const int32_t* topk_idx,
+                                     int k, int E, int row_align, int64_t group_rows, uint8_t* codes,
+                                     uint8_t* scales, float* outer, int32_t* offsets, int32_t* row_map,
+                                     int32_t* src_row, void* ws, uint32_t* amax, hipStream_t s) {
+  if (!rows_path(K) || group_rows < 1) return false;
+  if (T == 0) return launch_quantize_permute(x, T, K, topk_idx, k, E, row_align, codes, scales, outer,
+                                             offsets, row_map, src_row, ws, s);
+  const int64_t groups = (T + group_rows - 1) / group_rows;
+  launch_kernel("zero_amax", zero_u32_kernel,
+                dim3(static_cast<unsigned>(std::min<int64_t>((groups + 255) / 256, 1024))), dim3(256), 0, s,
+                amax, groups);
+  if (!launch_ok("zero_amax")) return false;
+  const int64_t want_blocks = static_cast<int64_t>(device_cu_count()) * 4;
+  const int64_t rows_per_block = std::max<int64_t>(1, (T + want_blocks - 1) / want_blocks);
+  launch_kernel("group_amax", group_amax_kernel,
+                dim3(static_cast<unsigned>((T + rows_per_block - 1) / rows_per_block)), dim3(kAmaxThreads), 0,
+                s, x, T, K, group_rows, rows_per_block, amax);
+  if (!launch_ok("group_amax")) return false;
+
+  const int64_t n_chunks = (T + kRouteChunk - 1) / kRouteChunk;
+  int32_t* counts = static_cast<int32_t*>(ws);
+  int32_t* expert_count = counts + n_chunks * E;
+  if (topk_idx != nullptr) {
+    const uint32_t lds = static_cast<uint32_t>(E) * (kRouteChunk / 32) * sizeof(uint32_t);
+    launch_kernel("route_count", route_count_kernel, dim3(static_cast<unsigned>(n_chunks)), dim3(kRouteChunk), lds,
+                  s, topk_idx, T, k, E, row_map, counts);
+    if (!launch_ok("route_count")) return false;
+    launch_kernel("route_scan", route_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, counts,
+                  static_cast<int>(n_chunks), E, row_align, offsets, expert_count);
+    if (!launch_ok("route_scan")) return false;
+  }
+  const bool ok = topk_idx != nullptr
+      ? launch_rows<RowMode::Scatter>("quantize_scatter", x, T, K, topk_idx, k, E, codes, scales, outer,
+                                      offsets, row_map, src_row, counts, s, amax, group_rows)
+      : launch_rows<RowMode::Identity>("quantize_scatter", x, T, K, nullptr, 1, 1, codes, scales, outer,
+                                       offsets, row_map, src_row, nullptr, s, amax, group_rows);
+  if (!ok) return false;
+  if (topk_idx != nullptr && row_align > 1) {
+    launch_kernel("pad_rows", pad_rows_kernel, dim3(static_cast<unsigned>((E + kWavesPerBlock - 1) / kWavesPerBlock)),
+                  dim3(kThreads), 0, s, K, E, offsets, expert_count, codes, scales, outer, src_row);
+    return launch_ok("pad_rows");
+  }
+  return true;
 }
 
 bool launch_requant(const uint16_t* a, int64_t rows_alloc, int K, const int32_t* offsets, int E,

@@ -83,3 +83,25 @@ def test_invalid_arguments_rejected_before_launch():
 
     assert bwd() == -3                                 # no workspace
     assert bwd(I=100) == -1
+
+    def qpd(T=4, K=64, G=1, wsb=1 << 20):
+        return lib.w4a4_quantize_permute_domain(p, T, K, p, 2, 8, 1, G, p, p, p, p, p, p, p, wsb, None)
+
+    assert qpd(K=48) == -2                             # grouped scales need K % 32 == 0
+    assert qpd(K=8192) == -2                           # and K <= 4096
+    assert qpd(G=0) == -1                              # group_rows >= 1
+    assert qpd(wsb=0) == -3
+    assert lib.w4a4_workspace_size(4, 4, 64, 0, 8, 2, 1) >= lib.w4a4_workspace_size(0, 4, 64, 0, 8, 2, 1)
+
+    def lin_fwd(K=256, N=256, T=4):
+        return lib.w4a4_linear_fwd(T, K, N, p, p, p, p, p, p, p, p, None)
+
+    def lin_bwd(K=256, N=256, T=4, ws=p, wsb=1 << 20):
+        return lib.w4a4_linear_bwd(T, K, N, p, p, p, p, p, p, ws, wsb, None)
+
+    assert lin_fwd(K=128) == -2                        # K % 256
+    assert lin_fwd(N=384) == -2                        # N % 256
+    assert lin_fwd(T=-1) == -1
+    assert lin_bwd(ws=None) == -3
+    assert lib.w4a4_workspace_size(3, 0, 256, 256, 1, 1, 1) > 0
+    assert lib.w4a4_workspace_size(3, 0, 128, 256, 1, 1, 1) == 0
