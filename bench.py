@@ -105,6 +105,9 @@ def linear_work(T, K, N):
     fl = {n: 2.0 * T * K * N for n in ("gemm_linear", "gemm_linear_dgrad", "gemm_linear_wgrad")}
     # read x; write codes, scales, outer, row_map, src_row (identity routing)
     by = {"quantize_scatter": T * (K * 2 + K // 2 + K // 16 + 12)}
+    # the K split of the weight gradient (2 pieces at this shape on 256 CUs):
+    # read the FP32 sums of the pieces, write bf16 dW
+    by["splitk_reduce"] = N * K * (2 * 4 + 2)
     return fl, by
 
 
@@ -167,7 +170,7 @@ def main_linear(args):
 
     ms, kern = time_steps(b, torch, step, args)
     fl, by = linear_work(T, K, N)
-    per_kernel, roof = summarize(kern, ms, args.steps, fl, by)
+    per_kernel, roof = summarize(kern, ms, args.steps, fl, by, concurrent={})
     out = {
         "metric": LINEAR_METRIC,
         "value": round(T / (ms * 1e-3), 1),
@@ -253,7 +256,7 @@ def main_qp(args):
 
     ms, kern = time_steps(b, torch, step, args)
     fl, by = qp_work(T, H, k, args.outer)
-    per_kernel, roof = summarize(kern, ms, args.steps, fl, by)
+    per_kernel, roof = summarize(kern, ms, args.steps, fl, by, concurrent={})
     alg = sum(by.values()) - by.get("group_amax", 0)
     out = {
         "metric": QP_METRIC,
@@ -345,8 +348,10 @@ def time_steps(b, torch, step, args):
     return ms, kern
 
 
-def summarize(kern, ms, steps, fl, by):
-    """Per-kernel table and the roofline object of the dominant kernel."""
+def summarize(kern, ms, steps, fl, by, concurrent=None):
+    """Per-kernel table and the roofline object of the dominant kernel.
+    `concurrent`: kernels that run on the library's second stream."""
+    concurrent = CONCURRENT if concurrent is None else concurrent
     per_kernel = {}
     for name, rec in sorted(kern.items(), key=lambda kv: -kv[1]["total_ms"]):
         avg_ms = rec["total_ms"] / rec["count"]
@@ -358,10 +363,10 @@ def summarize(kern, ms, steps, fl, by):
         elif name in by:
             entry["gbs"] = round(by[name] / (avg_ms * 1e-3) / 1e9, 1)
             entry["frac_hbm"] = round(entry["gbs"] / PEAK_HBM_GBS, 4)
-        if name in CONCURRENT:
+        if name in concurrent:
             # launched on a second stream beside another kernel: its duration is
             # time shared with that kernel, not its standalone rate
-            entry["runs_beside"] = CONCURRENT[name]
+            entry["runs_beside"] = concurrent[name]
         per_kernel[name] = entry
     dom = max(kern, key=lambda n: kern[n]["total_ms"])
     dom_avg_s = kern[dom]["total_ms"] / kern[dom]["count"] * 1e-3

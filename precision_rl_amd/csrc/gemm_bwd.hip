@@ -499,7 +499,8 @@ constexpr int kSchedBegin = 0, kSchedCount = 8, kSchedCounters = 16, kSchedTable
 struct SchedGemm {
   int tpe;       // tiles per expert
   int per_xcd;   // workgroups per XCD of the GEMM's grid
-  int32_t* out;  // kSchedTable + 4 E tpe ints (nullptr: no GEMM)
+  int split;     // K splits per tile (1: none)
+  int32_t* out;  // kSchedTable + 4 E tpe split ints (nullptr: no GEMM)
 };
 
 // Inclusive prefix sum over the workgroup (1024 threads); `total` gets the
@@ -527,7 +528,7 @@ __device__ int64_t block_scan(int64_t v, int64_t& total, int64_t* s_wave) {
 __global__ void __launch_bounds__(1024)
 schedule_kernel(const int32_t* __restrict__ offsets, int E, SchedGemm g0, SchedGemm g1) {
   __shared__ int s_rows[1024];
-  __shared__ int s_cost[1024];   // per-tile cost of the expert at each sorted position
+  __shared__ int s_nk[1024];     // K stages of the expert at each sorted position
   __shared__ int s_e[1024], s_rb[1024], s_re[1024];
   __shared__ int s_base[1024];   // first chunk of the expert
   __shared__ int s_csize[1024];  // tiles per chunk of the expert
@@ -550,16 +551,20 @@ schedule_kernel(const int32_t* __restrict__ offsets, int E, SchedGemm g0, SchedG
     s_e[rank] = t;
     s_rb[rank] = offsets[t];
     s_re[rank] = offsets[t + 1];
-    s_cost[rank] = (n + kBK - 1) / kBK + kTileCostEpilogue;
+    s_nk[rank] = (n + kBK - 1) / kBK;
   }
   __syncthreads();
-  const int c = t < E ? s_cost[t] : 0;   // thread t: sorted position t
-  int64_t cost_sum;
-  block_scan(c, cost_sum, s_wave);
   for (int g = 0; g < 2; ++g) {
     const SchedGemm p = g ? g1 : g0;
     if (p.out == nullptr) continue;   // (the same in every thread)
-    const int64_t tpe = p.tpe, tiles = tpe * E, total = tpe * cost_sum;
+    // A tile split over K in p.split pieces: pieces of span stages each (the
+    // last one shorter), each listed as a tile of its own.
+    const int nkt = t < E ? s_nk[t] : 0;   // thread t: sorted position t
+    const int span = (nkt + p.split - 1) / p.split;
+    const int c = t < E ? span + kTileCostEpilogue : 0;
+    int64_t cost_sum;
+    block_scan(c, cost_sum, s_wave);
+    const int64_t tpe = static_cast<int64_t>(p.tpe) * p.split, tiles = tpe * E, total = tpe * cost_sum;
     // split an expert whose tiles, run whole on one XCD, would take longer
     // than the ideal share of one workgroup
     const int64_t ideal = total / (static_cast<int64_t>(kXcds) * p.per_xcd);
@@ -643,16 +648,21 @@ schedule_kernel(const int32_t* __restrict__ offsets, int E, SchedGemm g0, SchedG
       }
     }
     __syncthreads();
-    // (tile L = expert j, tile li of it; stepped by 1024 without divisions)
+    // (list entry L = piece li of expert j: tile li / split, K piece
+    // li % split; stepped by 1024 without divisions)
     u32x4_t* table = reinterpret_cast<u32x4_t*>(p.out + kSchedTable);
-    const int tp = p.tpe, jstep = 1024 / tp, lstep = 1024 % tp;
+    const int tp = static_cast<int>(tpe), jstep = 1024 / tp, lstep = 1024 % tp;
     int j = t / tp, li = t % tp;
     for (int L = t; L < static_cast<int>(tiles); L += 1024) {
       const int cs = s_csize[j], i = li / cs;
       const int ch = s_base[j] + i;
       const int at = s_begin[s_xcd[ch]] + s_off[ch] + (li - i * cs);
-      table[at] = u32x4_t{static_cast<uint32_t>(L), static_cast<uint32_t>(s_e[j]),
-                          static_cast<uint32_t>(s_rb[j]), static_cast<uint32_t>(s_re[j])};
+      const int tile = li / p.split, piece = li % p.split;
+      const int rb = s_rb[j], rows = s_re[j] - rb;
+      const int pspan = ((s_nk[j] + p.split - 1) / p.split) * kBK;
+      table[at] = u32x4_t{static_cast<uint32_t>(tile | (piece << 24)), static_cast<uint32_t>(s_e[j]),
+                          static_cast<uint32_t>(rb + min(rows, piece * pspan)),
+                          static_cast<uint32_t>(rb + min(rows, (piece + 1) * pspan))};
       j += jstep;
       li += lstep;
       if (li >= tp) {
@@ -670,10 +680,11 @@ struct WgradArgs {
   const uint16_t* s;       // S [rows, N]:  B(r, n) = S[r][n]
   uint16_t* out;           // [E, M, N]
   int32_t* sched;          // this GEMM's schedule (its tile counters are updated)
+  float* partial;          // K split (E = 1): [split, M, N] FP32 sums of the pieces; else nullptr
 };
 
 struct WTile {
-  int e, m0, n0;
+  int e, m0, n0, piece;
   int64_t r_begin, r_end;
   int nk;
 };
@@ -725,7 +736,8 @@ wgrad_kernel(WgradArgs args) {
     const u32x4_t p = *slot;
     const int L = static_cast<int>(__builtin_amdgcn_readfirstlane(p[0]));
     if (L < 0) return false;
-    const int local = L % tpe;
+    const int local = L & 0xFFFFFF;   // the tile of the expert; the K piece above
+    t.piece = L >> 24;
     t.e = static_cast<int>(__builtin_amdgcn_readfirstlane(p[1]));
     t.m0 = (local / n_tiles) * kBM;
     t.n0 = (local % n_tiles) * kBN;
@@ -891,6 +903,26 @@ wgrad_kernel(WgradArgs args) {
       setup(tn);
       for (int s = 0; s < kAhead && s < tn.nk; ++s) issue(tn, s);
     }
+    if (args.partial != nullptr) {
+      // a K piece: its FP32 sums, stored straight from the accumulators (a
+      // lane's 32 columns of a row are 128 contiguous bytes)
+      float* po = args.partial + static_cast<int64_t>(tc.piece) * args.M * args.N;
+#pragma unroll
+      for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < kNI; ++ni) {
+          const int n = tc.n0 + wcol + ni * 32 + r32;
+          if (n >= args.N) continue;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int m = tc.m0 + acc_row(wrow, mi, v, hl);
+            __builtin_nontemporal_store(acc[mi][ni][v], po + static_cast<int64_t>(m) * args.N + n);
+          }
+        }
+      if (!more) break;
+      tc = tn;
+      continue;
+    }
     uint16_t* out = args.out + static_cast<int64_t>(tc.e) * args.M * args.N;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -913,6 +945,34 @@ wgrad_kernel(WgradArgs args) {
     if (!more) break;
     tc = tn;
   }
+}
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// out = bf16(sum_s partial[s]) over the K pieces, in piece order (a fixed
+// order: the result is reproducible).  8 elements per thread.
+__global__ void __launch_bounds__(256)
+splitk_reduce_kernel(const float* __restrict__ partial, int split, int64_t n, uint16_t* __restrict__ out) {
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 8;
+  if (i >= n) return;
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+  for (int sp = 0; sp < split; ++sp) {
+    const float* p = partial + sp * n + i;
+    const f32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+    const f32x4_t b = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p + 4));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[j] += a[j];
+      acc[4 + j] += b[j];
+    }
+  }
+  u32x4_t o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    o[j] = static_cast<uint32_t>(f32_to_bf16(acc[2 * j])) | (static_cast<uint32_t>(f32_to_bf16(acc[2 * j + 1])) << 16);
+  __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(out + i));
 }
 
 }  // namespace wg
@@ -943,24 +1003,33 @@ bool launch_dgrad(const dg::DgradArgs& a, const char* name, hipStream_t s) {
 // Grid of a wgrad GEMM of E experts' [M, N] tiles: one workgroup per CU,
 // at most one per tile.
 struct WgradPlan {
-  int64_t tiles;
+  int64_t tiles;   // list entries: tiles times K pieces
   unsigned grid;
-  int tpe, per_xcd;
+  int tpe, per_xcd, split;
 };
-WgradPlan wgrad_plan(int M, int N, int E) {
+WgradPlan wgrad_plan(int M, int N, int E, int split = 1) {
   WgradPlan p;
   p.tpe = (M / wg::kBM) * ((N + wg::kBN - 1) / wg::kBN);
-  p.tiles = static_cast<int64_t>(E) * p.tpe;
+  p.split = split;
+  p.tiles = static_cast<int64_t>(E) * p.tpe * split;
   p.grid = persistent_grid(p.tiles);
   p.per_xcd = std::max(1, static_cast<int>(p.grid / kXcds));
   return p;
 }
+// K pieces per tile of a one-group wgrad whose tiles do not fill the chip:
+// enough for one list entry per CU, at most 8.
+int wgrad_split_max(int M, int N) {
+  const int64_t tiles = static_cast<int64_t>(M / wg::kBM) * ((N + wg::kBN - 1) / wg::kBN);
+  const int64_t cus = device_cu_count();
+  if (tiles >= cus) return 1;
+  return static_cast<int>(std::min<int64_t>(8, (cus + tiles - 1) / tiles));
+}
 size_t wgrad_sched_ints(const WgradPlan& p) { return wg::kSchedTable + 4 * static_cast<size_t>(p.tiles); }
 
-bool launch_wgrad(const wg::WgradArgs& a, const char* name, hipStream_t s) {
+bool launch_wgrad(const wg::WgradArgs& a, const char* name, hipStream_t s, int split = 1) {
   static const hipError_t attr = set_lds(&wg::wgrad_kernel, wg::kLdsBytes);
   if (attr != hipSuccess) return launch_ok(name) && false;
-  const WgradPlan p = wgrad_plan(a.M, a.N, a.E);
+  const WgradPlan p = wgrad_plan(a.M, a.N, a.E, split);
   if (p.tiles == 0) return true;
   launch_kernel(name, wg::wgrad_kernel, dim3(p.grid), dim3(wg::kThreads), wg::kLdsBytes, s, a);
   return launch_ok(name);
@@ -990,24 +1059,30 @@ bool launch_wgrad_schedule(int H, int I, int E, const int32_t* offsets, int32_t*
   if (E < 1 || E > 1024) return false;
   const WgradPlan p2 = wgrad_plan(H, I, E), p1 = wgrad_plan(2 * I, H, E);
   launch_kernel("wgrad_schedule", wg::schedule_kernel, dim3(1), dim3(1024), 0, s, offsets, E,
-                wg::SchedGemm{p2.tpe, p2.per_xcd, sched},
-                wg::SchedGemm{p1.tpe, p1.per_xcd, sched + wgrad_sched_ints(p2)});
+                wg::SchedGemm{p2.tpe, p2.per_xcd, 1, sched},
+                wg::SchedGemm{p1.tpe, p1.per_xcd, 1, sched + wgrad_sched_ints(p2)});
   return launch_ok("wgrad_schedule");
 }
 
 bool launch_wgrad_fc2(int H, int I, int E, const uint16_t* dO, const uint16_t* a, uint16_t* dW2,
                       int32_t* sched, hipStream_t s) {
-  wg::WgradArgs w{H, I, E, dO, a, dW2, sched};
+  wg::WgradArgs w{H, I, E, dO, a, dW2, sched, nullptr};
   return launch_wgrad(w, "gemm_wgrad_fc2", s);
 }
 
 bool launch_wgrad_fc1(int H, int I, int E, const uint16_t* dH, const uint16_t* xp, uint16_t* dW1,
                       int32_t* sched, hipStream_t s) {
-  wg::WgradArgs w{2 * I, H, E, dH, xp, dW1, sched + wgrad_sched_ints(wgrad_plan(H, I, E))};
+  wg::WgradArgs w{2 * I, H, E, dH, xp, dW1, sched + wgrad_sched_ints(wgrad_plan(H, I, E)), nullptr};
   return launch_wgrad(w, "gemm_wgrad_fc1", s);
 }
 
-size_t linear_wgrad_schedule_ints(int K, int N) { return wgrad_sched_ints(wgrad_plan(N, K, 1)); }
+// Linear wgrad workspace: the schedule (room for the largest K split), then
+// the FP32 sums of the K pieces when the tiles are split.
+size_t linear_wgrad_schedule_ints(int K, int N) {
+  const int split = wgrad_split_max(N, K);
+  const size_t sched = (wgrad_sched_ints(wgrad_plan(N, K, 1, split)) + 63) / 64 * 64;
+  return sched + (split > 1 ? static_cast<size_t>(split) * N * K : 0);
+}
 
 bool launch_linear_dgrad(int64_t T, int K, int N, const int32_t* offsets, const uint16_t* dy,
                          const uint16_t* w, uint16_t* dx, hipStream_t s) {
@@ -1017,13 +1092,23 @@ bool launch_linear_dgrad(int64_t T, int K, int N, const int32_t* offsets, const 
 
 bool launch_linear_wgrad(int64_t T, int K, int N, const int32_t* offsets, const uint16_t* dy,
                          const uint16_t* x, uint16_t* dw, int32_t* sched, hipStream_t s) {
-  (void)T;
-  const WgradPlan p = wgrad_plan(N, K, 1);
+  // split K only while each piece keeps at least 32 stages
+  const int64_t nk = (T + wg::kBK - 1) / wg::kBK;
+  int split = wgrad_split_max(N, K);
+  while (split > 1 && nk / split < 32) --split;
+  const WgradPlan p = wgrad_plan(N, K, 1, split);
   launch_kernel("wgrad_schedule", wg::schedule_kernel, dim3(1), dim3(1024), 0, s, offsets, 1,
-                wg::SchedGemm{p.tpe, p.per_xcd, sched}, wg::SchedGemm{0, 1, nullptr});
+                wg::SchedGemm{p.tpe, p.per_xcd, split, sched}, wg::SchedGemm{0, 1, 1, nullptr});
   if (!launch_ok("wgrad_schedule")) return false;
-  wg::WgradArgs w{N, K, 1, dy, x, dw, sched};
-  return launch_wgrad(w, "gemm_linear_wgrad", s);
+  const size_t sched_ints = (wgrad_sched_ints(wgrad_plan(N, K, 1, wgrad_split_max(N, K))) + 63) / 64 * 64;
+  float* partial = split > 1 ? reinterpret_cast<float*>(sched + sched_ints) : nullptr;
+  wg::WgradArgs w{N, K, 1, dy, x, dw, sched, partial};
+  if (!launch_wgrad(w, "gemm_linear_wgrad", s, split)) return false;
+  if (split == 1) return true;
+  const int64_t n = static_cast<int64_t>(N) * K;   // a multiple of 8 (K % 256 == 0)
+  launch_kernel("splitk_reduce", wg::splitk_reduce_kernel, dim3(static_cast<unsigned>((n / 8 + 255) / 256)),
+                dim3(256), 0, s, partial, split, n, dw);
+  return launch_ok("splitk_reduce");
 }
 
 }  // namespace w4a4

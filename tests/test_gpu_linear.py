@@ -46,7 +46,10 @@ def _check_y(y, ref_y):
     return e, same
 
 
-@pytest.mark.parametrize("T,K,N", [(300, 512, 768), (1, 256, 256), (1000, 1024, 512)])
+# (4096, 256, 256) and (2500, 512, 512): one group with fewer weight-gradient
+# tiles than CUs, split over K (4 and 2 pieces, the last one ragged)
+@pytest.mark.parametrize("T,K,N", [(300, 512, 768), (1, 256, 256), (1000, 1024, 512),
+                                   (4096, 256, 256), (2500, 512, 512)])
 def test_linear_small(T, K, N):
     x, w, dy = _inputs(T, K, N, 500 + T)
     print_case("linear_small", T=T, K=K, N=N)
@@ -65,11 +68,12 @@ def test_linear_small(T, K, N):
     print("bwd", errs)
 
 
-def test_linear_backward_deterministic_and_empty():
+@pytest.mark.parametrize("T,K,N", [(700, 512, 512), (4096, 256, 256)])
+def test_linear_backward_deterministic_and_empty(T, K, N):
     """Two backward calls give bit-identical results (the weight-gradient
-    tiles are taken dynamically); with T = 0 dW is all zeros."""
+    tiles are taken dynamically; with a K split, the pieces are summed in a
+    fixed order); with T = 0 dW is all zeros."""
     from precision_rl_amd import binding as b
-    T, K, N = 700, 512, 512
     x, w, dy = _inputs(T, K, N, 77)
     print_case("linear_determinism", T=T, K=K, N=N)
     _, _, _, g1 = _run(x, w, dy, T, K, N)
