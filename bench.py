@@ -9,7 +9,8 @@ saved) and the straight-through BF16 backward (dX, dW1, dW2).  Weights are
 quantised once before timing (offline, as on the pages).
 
 Prints ONE JSON line.  `value` is tokens/s of the whole step; `roofline`
-reports the dominant kernel (by total time in the timed region) against its
+reports the dominant kernel (by total time in the timed region, among the
+kernels that do not run beside another on the second stream) against its
 bound, from HIP events recorded around each library launch on the launch
 stream; `cpu_baseline` times the FP64 oracle on a bounded sample on the host.
 """
@@ -368,7 +369,11 @@ def summarize(kern, ms, steps, fl, by, concurrent=None):
             # time shared with that kernel, not its standalone rate
             entry["runs_beside"] = concurrent[name]
         per_kernel[name] = entry
-    dom = max(kern, key=lambda n: kern[n]["total_ms"])
+    # the dominant kernel is taken among those that own the GPU while they run:
+    # a second-stream kernel's duration includes the time it shares with the
+    # kernel beside it, so it states no rate of its own
+    alone = [n for n in kern if n not in concurrent] or list(kern)
+    dom = max(alone, key=lambda n: kern[n]["total_ms"])
     dom_avg_s = kern[dom]["total_ms"] / kern[dom]["count"] * 1e-3
     if dom in fl:
         ach = fl[dom] / dom_avg_s / 1e12
