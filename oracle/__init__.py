@@ -20,7 +20,11 @@ Modules
 -------
 ``nvfp4``  the E2M1 / E4M3 / BF16 codecs and the row quantiser.
 ``moe``    routing, quantize+permute, the grouped expert forward and the
-           straight-through backward.
+           straight-through backward (NVFP4; and the forward of the MXFP4
+           recipe).
+``mxfp4``  the MXFP4 recipe's E8M0 codec and row quantiser (E2M1 elements,
+           one power-of-two scale per 32).
+``linear`` the dense per-token NVFP4 linear layer.
 
 Parity status: every function here is pinned by tests under ``tests/``
 (``-m "not gpu"``) against closed forms, exact rational brute force, worked
@@ -30,4 +34,4 @@ closed forms and the autograd check of their derivatives (see the docstrings
 in ``moe``).
 """
 
-from . import nvfp4, moe  # noqa: F401
+from . import nvfp4, mxfp4, moe  # noqa: F401

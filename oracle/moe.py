@@ -19,6 +19,7 @@ saved high-precision operands.  Points they leave open are marked READING.
 
 import numpy as np
 
+from . import mxfp4 as mx
 from . import nvfp4 as q
 
 
@@ -285,3 +286,77 @@ def backward(dy, x, w1, w2, h, a, topk_w, offsets, row_map, src_row, rnd=True):
         dX += dXp[row_map[:, j]]
     dX = R(dX)
     return dict(dO=dO, dA=dA, dH=dH, dXp=dXp, dX=dX, dW1=dW1, dW2=dW2)
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 recipe (E2M1 + E8M0 per 32; see mxfp4): the same forward with the
+# NVFP4 quantiser replaced and no outer scales.
+# ---------------------------------------------------------------------------
+def quantize_permute_mx(x, topk_idx, E, row_align=1, routed=None):
+    """MXFP4 of every token row, written to each of its k destination rows.
+
+    Same routing and scatter as ``quantize_permute``; a row's scales depend
+    on that row alone.  Pad rows get codes 0 and scale bytes 0.
+    Returns dict(codes [rows, K], packed [rows, K/2], scales [rows, K/32],
+    offsets, row_map, src_row).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if routed is None:
+        routed = route_fast(topk_idx, E, row_align)
+    offsets, row_map, src_row = routed
+    rows = int(offsets[-1])
+    T, K = x.shape
+    tc, ts = mx.quantize_rows_mx(x)
+    codes = np.zeros((rows, K), dtype=np.uint8)
+    scales = np.zeros((rows, K // mx.MX_BLOCK), dtype=np.uint8)
+    live = src_row >= 0
+    codes[live] = tc[src_row[live]]
+    scales[live] = ts[src_row[live]]
+    return dict(codes=codes, packed=q.pack_codes(codes), scales=scales,
+                offsets=offsets, row_map=row_map, src_row=src_row)
+
+
+def quantize_weights_mx(w):
+    """Offline MXFP4 of stacked expert weights [E, N, K], blocks along K."""
+    w = np.asarray(w, dtype=np.float64)
+    E, N, K = w.shape
+    c, s = mx.quantize_rows_mx(w.reshape(E * N, K))
+    return dict(codes=c.reshape(E, N, K), packed=q.pack_codes(c).reshape(E, N, K // 2),
+                scales=s.reshape(E, N, K // mx.MX_BLOCK))
+
+
+def grouped_gemm_mx(a_codes, a_scales, offsets, w_codes, w_scales):
+    """out[r, n] = sum_k (c 2^X)_a[r, k] (c 2^X)_w[e, n, k] for row r of expert e.
+
+    Every term is exact in float64; returns the float64 value the GPU's FP32
+    accumulation approximates.
+    """
+    offsets = np.asarray(offsets, dtype=np.int64)
+    rows = int(offsets[-1])
+    E, N, _ = w_codes.shape
+    out = np.zeros((rows, N))
+    for e in range(E):
+        r0, r1 = offsets[e], offsets[e + 1]
+        if r1 == r0:
+            continue
+        out[r0:r1] = mx.block_values_mx(a_codes[r0:r1], a_scales[r0:r1]) @ \
+            mx.block_values_mx(w_codes[e], w_scales[e]).T
+    return out
+
+
+def forward_mx(x, topk_idx, topk_w, w1q, w2q, E, row_align=1):
+    """Whole forward in the MXFP4 recipe: quantize+permute, FC1, SwiGLU,
+    requantise, FC2, unpermute, with the cast points and router-coefficient
+    position of ``forward``."""
+    x = np.asarray(x, dtype=np.float64)
+    I = w1q["codes"].shape[1] // 2
+    xq = quantize_permute_mx(x, topk_idx, E, row_align)
+    h64 = grouped_gemm_mx(xq["codes"], xq["scales"], xq["offsets"], w1q["codes"], w1q["scales"])
+    h = q.round_bf16(h64)
+    a = q.round_bf16(swiglu(h, I))
+    ac, as_ = mx.quantize_rows_mx(a)
+    o64 = grouped_gemm_mx(ac, as_, xq["offsets"], w2q["codes"], w2q["scales"])
+    o = q.round_bf16(o64)
+    y = q.round_bf16(unpermute_sum(o, xq["row_map"], topk_w))
+    return dict(xq=xq, h64=h64, h=h, a=a, a_codes=ac, a_scales=as_, o64=o64, o=o, y=y,
+                live=xq["src_row"] >= 0)
