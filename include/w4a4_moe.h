@@ -271,6 +271,60 @@ w4a4_status w4a4_linear_bwd(
     void* dx, void* dw,
     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * MXFP4 recipe -- E2M1 codes with one E8M0 (power-of-two) scale per 32
+ * consecutive elements of a row and no FP32 outer scale.  The miniTE
+ * Technical Report's appendix D1 format sweep measures this "E2M1 + E8M0"
+ * scale format beside NVFP4's E4M3 block scales (2-3 dB lower SNR); the
+ * format itself is the OCP Microscaling (MX) v1.0 FP4 format (section 6.3:
+ * shared exponent X = floor(log2(block amax)) - 2 clamped to [-127, 127],
+ * scale byte X + 127, codes Q_E2M1(x / 2^X) round-to-nearest-even saturating
+ * at 6; an all-zero block takes byte 0).  gfx950's scaled FP4 matrix
+ * instructions take these operands as stored.  It is a different recipe
+ * from NVFP4: its results are not those of the NVFP4 calls.
+ *
+ * w4a4_mx_quantize_permute -- w4a4_quantize_permute for the MXFP4 recipe.
+ *   x [T, K] bf16 with K % 32 == 0 and K <= 4096.  codes [cap, K/2] uint8
+ *   out, scales [cap, K/32] uint8 (E8M0) out; no outer scales.  Routing
+ *   arguments, row_align, the maps, the workspace (same size as
+ *   W4A4_WS_QUANTIZE_PERMUTE) and topk_idx = NULL (identity routing, for
+ *   weight rows) as in w4a4_quantize_permute.  Pad rows get codes 0 and
+ *   scale bytes 0.
+ */
+w4a4_status w4a4_mx_quantize_permute(
+    const void* x, int64_t T, int K,
+    const int32_t* topk_idx, int k, int E, int row_align,
+    uint8_t* codes, uint8_t* scales,
+    int32_t* expert_offsets, int32_t* row_map, int32_t* src_row,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * w4a4_mx_grouped_expert_fwd -- w4a4_grouped_expert_fwd for the MXFP4
+ * recipe: FC1 = sum_k (c 2^X)_x (c 2^X)_w1 accumulated in FP32 on the scaled
+ * FP4 MFMA, h = bf16(FC1), a = bf16(SwiGLU(h)), a requantised to MXFP4,
+ * o = bf16(FC2), y[t] = bf16(sum_j p[t,j] o[row_map[t,j]]).  Same routing,
+ * cast points and router-coefficient position as the NVFP4 forward.
+ *   x_codes [cap, H/2], x_scales [cap, H/32] from w4a4_mx_quantize_permute.
+ *   w1_codes [E, 2I, H/2], w1_scales [E, 2I, H/32]; w2_codes [E, H, I/2],
+ *   w2_scales [E, H, I/32] (MXFP4 of the weight rows along the reduction
+ *   axis: w4a4_mx_quantize_permute with identity routing).
+ *   H % 256 == 0, I % 128 == 0.  y, save_h, save_a, dbg_fc1_f32 as in
+ *   w4a4_grouped_expert_fwd; dbg_a_codes [cap, I/2] and dbg_a_scales
+ *   [cap, I/32]: both or neither.  workspace >= w4a4_workspace_size(
+ *   W4A4_WS_FORWARD, ...) bytes.  The saved h and a feed w4a4_expert_bwd
+ *   unchanged (its straight-through backward does not see the recipe).
+ */
+w4a4_status w4a4_mx_grouped_expert_fwd(
+    int64_t T, int H, int I, int E, int k, int row_align,
+    const uint8_t* x_codes, const uint8_t* x_scales,
+    const int32_t* expert_offsets, const int32_t* row_map, const int32_t* src_row,
+    const float* topk_w,
+    const uint8_t* w1_codes, const uint8_t* w1_scales,
+    const uint8_t* w2_codes, const uint8_t* w2_scales,
+    void* y, void* save_h, void* save_a, float* dbg_fc1_f32,
+    uint8_t* dbg_a_codes, uint8_t* dbg_a_scales,
+    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* w4a4_status_string(int status);
 

@@ -35,6 +35,13 @@ _SIGS = {
                                 c_vp, c_vp]),
     "w4a4_linear_bwd": (c_int, [c_i64, c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                 c_vp, c_sz, c_vp]),
+    "w4a4_mx_quantize_permute": (c_int, [c_vp, c_i64, c_int, c_vp, c_int, c_int, c_int,
+                                         c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "w4a4_mx_grouped_expert_fwd": (c_int, [c_i64, c_int, c_int, c_int, c_int, c_int,
+                                           c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                           c_vp, c_vp, c_vp, c_vp,
+                                           c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                           c_vp, c_sz, c_vp]),
     "w4a4_status_string": (ctypes.c_char_p, [c_int]),
     "w4a4_last_error": (ctypes.c_char_p, []),
     "w4a4_profiler_enable": (c_int, [c_int]),
@@ -247,6 +254,73 @@ def w4a4_linear_bwd(dy, x, w, xq, T, K, N, out=None, workspace=None):
     _check(lib.w4a4_linear_bwd(T, K, N, _p(dy), _p(x), _p(w), _p(xq["offsets"]),
                                _p(out["dx"]), _p(out["dw"]), _p(ws), ws.numel(), _stream()))
     return out
+
+
+# ------------------------------------------------------------ MXFP4 recipe
+def w4a4_mx_quantize_permute(x, topk_idx, E, row_align=1, out=None, workspace=None):
+    """Route + MXFP4 encode (E2M1, one E8M0 scale per 32) + scatter.  x: [T, K] bf16 cuda,
+    K % 32 == 0; topk_idx: [T, k] int32 or None (identity routing).  Returns a dict:
+    codes [cap, K/2] u8, scales [cap, K/32] u8, offsets [E+1], row_map [T, k], src_row [cap]."""
+    lib = load()
+    T, K = x.shape
+    dev = x.device
+    if topk_idx is None:
+        k, E, row_align = 1, 1, 1
+    else:
+        k = topk_idx.shape[1]
+    cap = rows_capacity(T, k, E, row_align)
+    if out is None:
+        out = dict(
+            codes=torch.empty(cap, K // 2, dtype=torch.uint8, device=dev),
+            scales=torch.empty(cap, K // 32, dtype=torch.uint8, device=dev),
+            offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+            row_map=torch.empty(T, k, dtype=torch.int32, device=dev),
+            src_row=torch.empty(cap, dtype=torch.int32, device=dev))
+    need = workspace_size(WS_QUANTIZE_PERMUTE, T, K, 0, E, k, row_align)
+    ws = _workspace(need, dev, workspace)
+    _check(lib.w4a4_mx_quantize_permute(
+        _p(x), T, K, _p(topk_idx), k, E, row_align, _p(out["codes"]), _p(out["scales"]),
+        _p(out["offsets"]), _p(out["row_map"]), _p(out["src_row"]), _p(ws), ws.numel(), _stream()))
+    return out
+
+
+def quantize_weights_mx(w):
+    """MXFP4 of stacked expert weights w [E, N, K] bf16 along K (offline, identity routing).
+    Returns dict(codes [E, N, K/2], scales [E, N, K/32])."""
+    E, N, K = w.shape
+    q = w4a4_mx_quantize_permute(w.reshape(E * N, K), None, 1)
+    return dict(codes=q["codes"].view(E, N, K // 2), scales=q["scales"].view(E, N, K // 32))
+
+
+def w4a4_mx_grouped_expert_fwd(xq, topk_w, w1q, w2q, T, H, I, E, k, row_align=1,
+                               save=False, debug=False, y=None, workspace=None, saved=None):
+    """MXFP4 grouped expert forward: FC1 -> SwiGLU -> requantise -> FC2 -> unpermute on the
+    scaled FP4 MFMA.  xq: result of ``w4a4_mx_quantize_permute``; w1q / w2q: of
+    ``quantize_weights_mx``.  Returns dict(y, h/a when ``save``, fc1_f32 and the FC2-input
+    encoding a_codes / a_scales when ``debug``)."""
+    lib = load()
+    dev = xq["codes"].device
+    cap = rows_capacity(T, k, E, row_align)
+    res = {}
+    res["y"] = y if y is not None else torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    if save:
+        if saved is None:
+            saved = dict(h=torch.empty(cap, 2 * I, dtype=torch.bfloat16, device=dev),
+                         a=torch.empty(cap, I, dtype=torch.bfloat16, device=dev))
+        res.update(saved)
+    if debug:
+        res["fc1_f32"] = torch.empty(cap, 2 * I, dtype=torch.float32, device=dev)
+        res["a_codes"] = torch.empty(cap, I // 2, dtype=torch.uint8, device=dev)
+        res["a_scales"] = torch.empty(cap, I // 32, dtype=torch.uint8, device=dev)
+    need = workspace_size(WS_FORWARD, T, H, I, E, k, row_align)
+    ws = _workspace(need, dev, workspace)
+    _check(lib.w4a4_mx_grouped_expert_fwd(
+        T, H, I, E, k, row_align, _p(xq["codes"]), _p(xq["scales"]),
+        _p(xq["offsets"]), _p(xq["row_map"]), _p(xq["src_row"]), _p(topk_w),
+        _p(w1q["codes"]), _p(w1q["scales"]), _p(w2q["codes"]), _p(w2q["scales"]),
+        _p(res["y"]), _p(res.get("h")), _p(res.get("a")), _p(res.get("fc1_f32")),
+        _p(res.get("a_codes")), _p(res.get("a_scales")), _p(ws), ws.numel(), _stream()))
+    return res
 
 
 def w4a4_profiler_enable(on=True):

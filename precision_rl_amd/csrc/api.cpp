@@ -493,6 +493,77 @@ w4a4_status w4a4_linear_bwd(int64_t T, int K, int N, const void* dy, const void*
   return W4A4_OK;
 }
 
+w4a4_status w4a4_mx_quantize_permute(const void* x, int64_t T, int K, const int32_t* topk_idx, int k, int E,
+                                     int row_align, uint8_t* codes, uint8_t* scales, int32_t* expert_offsets,
+                                     int32_t* row_map, int32_t* src_row, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  // the NVFP4 checks with a stand-in for the absent outer scales
+  float* no_outer = reinterpret_cast<float*>(codes);
+  w4a4_status st = check_quantize_permute(x, T, K, topk_idx, k, E, row_align, codes, scales, no_outer,
+                                          expert_offsets, row_map, src_row);
+  if (st != W4A4_OK) return st;
+  if (K % 32 || K > 4096)
+    return fail(W4A4_ERR_UNSUPPORTED, "MXFP4 rows need K %% 32 == 0 and K <= 4096 (K=%d)", K);
+  const size_t need = w4a4_workspace_size(W4A4_WS_QUANTIZE_PERMUTE, T, K, 0, E, k, row_align);
+  if (topk_idx != nullptr && T > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(W4A4_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  OPTIONAL_PTR(workspace);
+  if (!launch_quantize_permute_mx(static_cast<const uint16_t*>(x), T, K, topk_idx, k, E, row_align, codes,
+                                  scales, expert_offsets, row_map, src_row, workspace,
+                                  static_cast<hipStream_t>(stream)))
+    return W4A4_ERR_LAUNCH;
+  return W4A4_OK;
+}
+
+w4a4_status w4a4_mx_grouped_expert_fwd(
+    int64_t T, int H, int I, int E, int k, int row_align, const uint8_t* x_codes,
+    const uint8_t* x_scales, const int32_t* expert_offsets, const int32_t* row_map,
+    const int32_t* src_row, const float* topk_w, const uint8_t* w1_codes, const uint8_t* w1_scales,
+    const uint8_t* w2_codes, const uint8_t* w2_scales, void* y, void* save_h, void* save_a,
+    float* dbg_fc1_f32, uint8_t* dbg_a_codes, uint8_t* dbg_a_scales, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  w4a4_status st = check_moe_shape(T, H, I, E, k, row_align);
+  if (st != W4A4_OK) return st;
+  REQUIRE_PTR(expert_offsets);
+  REQUIRE_PTR(w1_codes); REQUIRE_PTR(w1_scales);
+  REQUIRE_PTR(w2_codes); REQUIRE_PTR(w2_scales);
+  if (T > 0) {
+    REQUIRE_PTR(x_codes); REQUIRE_PTR(x_scales);
+    REQUIRE_PTR(row_map); REQUIRE_PTR(src_row); REQUIRE_PTR(topk_w); REQUIRE_PTR(y);
+  }
+  OPTIONAL_PTR(save_h); OPTIONAL_PTR(save_a); OPTIONAL_PTR(dbg_fc1_f32);
+  OPTIONAL_PTR(dbg_a_codes); OPTIONAL_PTR(dbg_a_scales);
+  const int nd = (dbg_a_codes != nullptr) + (dbg_a_scales != nullptr);
+  if (nd == 1) return fail(W4A4_ERR_INVALID_ARG, "dbg_a_codes, dbg_a_scales: both or neither");
+  const int64_t cap = w4a4_rows_capacity(T, k, E, row_align);
+  const FwdWs L = fwd_ws(cap, H, I);
+  if (workspace == nullptr || workspace_bytes < L.total)
+    return fail(W4A4_ERR_WORKSPACE, "workspace needs %zu bytes", L.total);
+  OPTIONAL_PTR(workspace);
+  if (cap == 0) return W4A4_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint16_t* a_buf = save_a ? static_cast<uint16_t*>(save_a) : reinterpret_cast<uint16_t*>(ws + L.a);
+  // the NVFP4 layout's code and scale areas hold the MXFP4 ones (fewer scale bytes)
+  uint8_t* a_codes = nd ? dbg_a_codes : ws + L.a_codes;
+  uint8_t* a_scales = nd ? dbg_a_scales : ws + L.a_scales;
+  uint16_t* o_buf = reinterpret_cast<uint16_t*>(ws + L.o);
+
+  if (!launch_fc1_mx(cap, H, I, E, expert_offsets, Fp4Operand{x_codes, x_scales, nullptr},
+                     Fp4Operand{w1_codes, w1_scales, nullptr}, static_cast<uint16_t*>(save_h), a_buf,
+                     dbg_fc1_f32, s))
+    return W4A4_ERR_LAUNCH;
+  if (!launch_requant_mx(a_buf, cap, I, expert_offsets, E, a_codes, a_scales, s)) return W4A4_ERR_LAUNCH;
+  if (!launch_fc2_mx(cap, H, I, E, expert_offsets, Fp4Operand{a_codes, a_scales, nullptr},
+                     Fp4Operand{w2_codes, w2_scales, nullptr}, o_buf, s))
+    return W4A4_ERR_LAUNCH;
+  if (!launch_unpermute(T, H, k, o_buf, row_map, topk_w, static_cast<uint16_t*>(y), s))
+    return W4A4_ERR_LAUNCH;
+  return W4A4_OK;
+}
+
 const char* w4a4_status_string(int status) {
   switch (status) {
     case W4A4_OK: return "ok";

@@ -11,6 +11,7 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));   // scaled-MFMA operand (FP4 uses the low four)
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;

@@ -135,6 +135,111 @@ __device__ __forceinline__ void scale_pairs(uint32_t pair, half2_t& d0, half2_t&
   d1 = half2_t{v[1], v[1]};
 }
 
+// Epilogue of the forward GEMMs: out = bf16(acc * (g_x[row] * g_w[n])) (FP32
+// products; 1.0 factors where the recipe has no outer scales), FC1 with the
+// SwiGLU.  s_gx: the tile's row outer scales in LDS; gw: this lane's four
+// weight outer scales; lds: the idle ring, used as staging.
+template <FwdMode MODE>
+__device__ __forceinline__ void fwd_epilogue(const FwdArgs& args, floatx16_t (&acc)[2][4], const TileCoord& tc,
+                                             const float* s_gx, const float (&gw)[4], uint8_t* lds) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int r32 = lane & 31, hl = lane >> 5;
+  // ---------------------------------------------------------------- epilogue
+  // The tile leaves in two rounds of 64 rows (MFMA row block mi = q of both
+  // wave rows) staged as bf16 in the idle ring, so that every global store is
+  // a 16-byte chunk of a row and a wave writes whole rows.  Staging row s holds
+  // tile row (s / 32) * 64 + 32 q + s % 32.  FC1 stages h (gate half, then up
+  // half, 128 features each) and computes the SwiGLU on the staged bf16 values
+  // while storing.
+  uint8_t* so = lds;
+  auto tile_row = [&](int s, int q) { return (s >> 5) * kWM + 32 * q + (s & 31); };
+  if constexpr (MODE == FwdMode::FC2) {
+    const int n_loc = wn * kWN + 4 * r32;
+    uint16_t* out = args.out + tc.n_tile * kBN;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if (q > 0) __syncthreads();   // previous round's reads done
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int s = wm * 32 + acc_row(0, 0, v, hl);
+        const float gx = s_gx[tile_row(s, q)];
+        u32x2_t pk;
+        pk[0] = pack_bf16x2(acc[q][0][v] * (gx * gw[0]), acc[q][1][v] * (gx * gw[1]));
+        pk[1] = pack_bf16x2(acc[q][2][v] * (gx * gw[2]), acc[q][3][v] * (gx * gw[3]));
+        *reinterpret_cast<u32x2_t*>(so + s * kOutPitch + n_loc * 2) = pk;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kOutRows * 32 / kThreads; ++j) {
+        const int c = tid + j * kThreads;
+        const int s = c >> 5, ch = c & 31;
+        const int64_t row = tc.m0 + tile_row(s, q);
+        if (row < tc.m_end)
+          __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t*>(so + s * kOutPitch + ch * 16),
+                                      reinterpret_cast<u32x4_t*>(out + row * args.N + ch * 8));
+      }
+    }
+  } else {
+    const int I = args.I;
+    const int i_loc = wn * 64 + 2 * r32;
+    const int i = tc.n_tile * 128 + i_loc;
+    const float gw_g0 = gw[0], gw_g1 = gw[1], gw_u0 = gw[2], gw_u1 = gw[3];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if (q > 0) __syncthreads();   // previous round's reads done
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int s = wm * 32 + acc_row(0, 0, v, hl);
+        const float gx = s_gx[tile_row(s, q)];
+        const float g0 = acc[q][0][v] * (gx * gw_g0);
+        const float g1 = acc[q][1][v] * (gx * gw_g1);
+        const float u0 = acc[q][2][v] * (gx * gw_u0);
+        const float u1 = acc[q][3][v] * (gx * gw_u1);
+        if (args.dbg != nullptr) {
+          const int64_t row = tc.m0 + tile_row(s, q);
+          if (row < tc.m_end) {
+            float* d = args.dbg + row * (2 * I);
+            *reinterpret_cast<float2*>(d + i) = make_float2(g0, g1);
+            *reinterpret_cast<float2*>(d + I + i) = make_float2(u0, u1);
+          }
+        }
+        *reinterpret_cast<uint32_t*>(so + s * kOutPitch + i_loc * 2) = pack_bf16x2(g0, g1);
+        *reinterpret_cast<uint32_t*>(so + s * kOutPitch + 256 + i_loc * 2) = pack_bf16x2(u0, u1);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kOutRows * 16 / kThreads; ++j) {
+        const int c = tid + j * kThreads;
+        const int s = c >> 4, ch = c & 15;
+        const int64_t row = tc.m0 + tile_row(s, q);
+        if (row >= tc.m_end) continue;
+        const u32x4_t hg = *reinterpret_cast<const u32x4_t*>(so + s * kOutPitch + ch * 16);
+        const u32x4_t hu = *reinterpret_cast<const u32x4_t*>(so + s * kOutPitch + 256 + ch * 16);
+        const int64_t col = tc.n_tile * 128 + ch * 8;
+        if (args.out != nullptr) {
+          uint16_t* h = args.out + row * (2 * I) + col;
+          __builtin_nontemporal_store(hg, reinterpret_cast<u32x4_t*>(h));
+          __builtin_nontemporal_store(hu, reinterpret_cast<u32x4_t*>(h + I));
+        }
+        // SwiGLU on the bf16-rounded h, FP32 arithmetic (hardware exp2 / rcp)
+        u32x4_t a;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float bg0 = bf16_to_f32(static_cast<uint16_t>(hg[w] & 0xFFFFu));
+          const float bg1 = bf16_to_f32(static_cast<uint16_t>(hg[w] >> 16));
+          const float bu0 = bf16_to_f32(static_cast<uint16_t>(hu[w] & 0xFFFFu));
+          const float bu1 = bf16_to_f32(static_cast<uint16_t>(hu[w] >> 16));
+          a[w] = pack_bf16x2(bg0 * sigmoid_fast(bg0) * bu0, bg1 * sigmoid_fast(bg1) * bu1);
+        }
+        __builtin_nontemporal_store(a, reinterpret_cast<u32x4_t*>(args.act + row * I + col));
+      }
+    }
+  }
+}
+
 template <FwdMode MODE, bool GS>
 __global__ void __launch_bounds__(kThreads, 2)
 fwd_gemm_kernel(FwdArgs args) {
@@ -347,97 +452,176 @@ fwd_gemm_kernel(FwdArgs args) {
   if (tid < kBM) s_gx[tid] = gx_row;
   __syncthreads();   // s_gx visible; every wave is past its last read of the ring
 
-  // ---------------------------------------------------------------- epilogue
-  // The tile leaves in two rounds of 64 rows (MFMA row block mi = q of both
-  // wave rows) staged as bf16 in the idle ring, so that every global store is
-  // a 16-byte chunk of a row and a wave writes whole rows.  Staging row s holds
-  // tile row (s / 32) * 64 + 32 q + s % 32.  FC1 stages h (gate half, then up
-  // half, 128 features each) and computes the SwiGLU on the staged bf16 values
-  // while storing.
-  uint8_t* so = lds;
-  auto tile_row = [&](int s, int q) { return (s >> 5) * kWM + 32 * q + (s & 31); };
-  if constexpr (MODE == FwdMode::FC2) {
-    const int n_loc = wn * kWN + 4 * r32;
-    uint16_t* out = args.out + tc.n_tile * kBN;
+  fwd_epilogue<MODE>(args, acc, tc, s_gx, gw, lds);
+}
+
+// ------------------------------------------------------------ MXFP4 recipe
+// The same grouped GEMMs for MXFP4 operands (E2M1 codes, one E8M0 scale per
+// 32 elements along K, no outer scales): gfx950's scaled FP4 MFMA
+// (32x32x64, f32 accumulate) consumes the packed codes and the scale bytes
+// as they are, so nothing is decoded.  Lane l of a 32x32x64 operand holds
+// row l % 32, elements 32 (l / 32) .. +31 of the 64 (16 bytes, element 2j in
+// the low nibble of byte j) and that run's E8M0 byte, which is exactly the
+// 16-byte chunk and block scale the NVFP4 kernel's lanes read.
+// A stage covers 128 of K: 64 B of codes per row (four 16-byte chunks,
+// stored at chunk slot c ^ ((r >> 2) & 3), so that the 16 rows one
+// ds_read_b128 phase touches fill all 64 banks) and 4 scale bytes per row
+// (one dword, same 512-row numbering as the NVFP4 stage); three stages ring,
+// two in flight, 78.5 KB: two workgroups per CU.  K % 128 == 0.
+constexpr int kMxBK = 128;
+constexpr int kMxStages = 3;
+constexpr int kMxAhead = kMxStages - 1;
+constexpr int kMxCodeRow = kMxBK / 2;                          // 64 B
+constexpr int kMxACodes = kBM * kMxCodeRow;                    // 8 KB
+constexpr int kMxBCodes = kBN * kMxCodeRow;                    // 16 KB
+constexpr int kMxScalesOffset = kMxACodes + kMxBCodes;
+constexpr int kMxStageBytes = kMxScalesOffset + kScaleRows * 4;   // 26 KB
+constexpr int kMxDmaPerStage = 8;            // per wave: 2 A-code, 4 B-code, 2 scale copies
+constexpr int kMxGx = kMxStages * kMxStageBytes;
+constexpr int kMxSlot = kMxGx + kBM * 4;
+constexpr int kMxLdsBytes = kMxSlot + 16;
+static_assert(2 * kMxLdsBytes <= 160 * 1024, "two workgroups per CU must fit in LDS");
+static_assert(kOutRows * kOutPitch <= kMxStages * kMxStageBytes, "staging fits in the ring");
+
+__device__ __forceinline__ int mx_code_slot(int r, int c) { return c ^ ((r >> 2) & 3); }
+
+template <FwdMode MODE>
+__global__ void __launch_bounds__(kThreads, 2)
+fwd_mx_kernel(FwdArgs args) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int r32 = lane & 31, hl = lane >> 5;
+
+  const int n_tiles = MODE == FwdMode::FC1 ? args.I / 128 : args.N / kBN;
+  TileCoord tc = grouped_m_tile<kBM>(args.offsets, args.E, n_tiles, reinterpret_cast<int*>(lds + kMxSlot));
+  if (!tc.valid) return;
+
+  const int64_t K2 = args.K / 2, K32 = args.K / 32;
+  const int64_t last_row = args.rows_alloc - 1;
+  const uint8_t* a_codes = args.a.codes + tc.m0 * K2;
+  const uint8_t* w_codes = args.w.codes + static_cast<int64_t>(tc.e) * args.N * K2;
+  const uint8_t* w_scales = args.w.scales + static_cast<int64_t>(tc.e) * args.N * K32;
+  const int a_rows = static_cast<int>(min<int64_t>(kBM, last_row + 1 - tc.m0));   // >= 1
+  // Code copies: copy q of this wave fills 16 staged rows (1 KB), lane i
+  // row 16 q' + i / 4 at slot i % 4; A: q' = 2 wave + q, B: q' = 4 wave + q.
+  // Rows past the allocation are clamped (they feed only rows never stored).
+  uint32_t a_code_off[2], b_code_off[4];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      if (q > 0) __syncthreads();   // previous round's reads done
+  for (int q = 0; q < 2; ++q) {
+    const int row = 16 * (2 * wave + q) + (lane >> 2);
+    a_code_off[q] = static_cast<uint32_t>(min(row, a_rows - 1) * K2 + mx_code_slot(row, lane & 3) * 16);
+  }
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int s = wm * 32 + acc_row(0, 0, v, hl);
-        const float gx = s_gx[tile_row(s, q)];
-        u32x2_t pk;
-        pk[0] = pack_bf16x2(acc[q][0][v] * (gx * gw[0]), acc[q][1][v] * (gx * gw[1]));
-        pk[1] = pack_bf16x2(acc[q][2][v] * (gx * gw[2]), acc[q][3][v] * (gx * gw[3]));
-        *reinterpret_cast<u32x2_t*>(so + s * kOutPitch + n_loc * 2) = pk;
-      }
-      __syncthreads();
+  for (int q = 0; q < 4; ++q) {
+    const int row = 16 * (4 * wave + q) + (lane >> 2);
+    b_code_off[q] = static_cast<uint32_t>(b_row_of<MODE>(row, tc.n_tile, args.I) * K2 +
+                                          mx_code_slot(row, lane & 3) * 16);
+  }
+  // Scale copies: one dword (the stage's 4 blocks) per staged row.
+  const uint8_t* scale_src[2];
 #pragma unroll
-      for (int j = 0; j < kOutRows * 32 / kThreads; ++j) {
-        const int c = tid + j * kThreads;
-        const int s = c >> 5, ch = c & 31;
-        const int64_t row = tc.m0 + tile_row(s, q);
-        if (row < tc.m_end)
-          __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t*>(so + s * kOutPitch + ch * 16),
-                                      reinterpret_cast<u32x4_t*>(out + row * args.N + ch * 8));
-      }
-    }
-  } else {
-    const int I = args.I;
-    const int i_loc = wn * 64 + 2 * r32;
-    const int i = tc.n_tile * 128 + i_loc;
-    const float gw_g0 = gw[0], gw_g1 = gw[1], gw_u0 = gw[2], gw_u1 = gw[3];
+  for (int c = 0; c < 2; ++c) {
+    const int q = 128 * wave + 64 * c + lane;
+    if (q < kBScaleRow0)
+      scale_src[c] = args.a.scales + (tc.m0 + min(q, a_rows - 1)) * K32;
+    else if (q < kBScaleRow0 + kBN)
+      scale_src[c] = w_scales + static_cast<int64_t>(b_row_of<MODE>(q - kBScaleRow0, tc.n_tile, args.I)) * K32;
+    else
+      scale_src[c] = args.a.scales + tc.m0 * K32;            // filler: a valid row, never read
+  }
+  const uint32_t lds0 = lds_addr(lds);
+  auto issue = [&](int kt) {
+    const uint32_t st = lds0 + (kt % kMxStages) * kMxStageBytes;
+    const int cb = kt * kMxCodeRow;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      if (q > 0) __syncthreads();   // previous round's reads done
+    for (int q = 0; q < 2; ++q) dma16_off(a_codes + cb, a_code_off[q], st + (2 * wave + q) * 1024);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int s = wm * 32 + acc_row(0, 0, v, hl);
-        const float gx = s_gx[tile_row(s, q)];
-        const float g0 = acc[q][0][v] * (gx * gw_g0);
-        const float g1 = acc[q][1][v] * (gx * gw_g1);
-        const float u0 = acc[q][2][v] * (gx * gw_u0);
-        const float u1 = acc[q][3][v] * (gx * gw_u1);
-        if (args.dbg != nullptr) {
-          const int64_t row = tc.m0 + tile_row(s, q);
-          if (row < tc.m_end) {
-            float* d = args.dbg + row * (2 * I);
-            *reinterpret_cast<float2*>(d + i) = make_float2(g0, g1);
-            *reinterpret_cast<float2*>(d + I + i) = make_float2(u0, u1);
-          }
+    for (int q = 0; q < 4; ++q) dma16_off(w_codes + cb, b_code_off[q], st + kMxACodes + (4 * wave + q) * 1024);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) dma4(scale_src[c] + kt * 4, st + kMxScalesOffset + (2 * wave + c) * 256);
+  };
+
+  floatx16_t acc[2][4];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
+
+  const int a_row0 = wm * kWM + r32, b_row0 = wn * kWN + r32;
+  // This lane's LDS offsets within a stage: its chunk (K-step s, half hl) of
+  // the first A / B row block (the slot is the same for every row block:
+  // they are 32 rows apart), and its rows' scale dwords.
+  const int sw = (r32 >> 2) & 3;
+  uint32_t a_lane[2], b_lane[2];
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+    a_lane[s2] = a_row0 * kMxCodeRow + ((2 * s2 + hl) ^ sw) * 16;
+    b_lane[s2] = kMxACodes + b_row0 * kMxCodeRow + ((2 * s2 + hl) ^ sw) * 16;
+  }
+  const uint32_t a_scale_lane = kMxScalesOffset + a_row0 * 4;
+  const uint32_t b_scale_lane = kMxScalesOffset + (kBScaleRow0 + b_row0) * 4;
+  const int nk = args.K / kMxBK;
+  for (int s0 = 0; s0 < kMxAhead && s0 < nk; ++s0) issue(s0);
+
+  const bool rows_live = tc.m0 + wm * kWM < tc.m_end;
+  for (int kt = 0; kt < nk; ++kt) {
+    // stage kt has landed in every wave: at most the copies issued after it
+    // (stage kt + 1, if any) are pending
+    if (kt + 1 < nk) wait_vm_barrier<kMxDmaPerStage>();
+    else wait_vm_barrier<0>();
+    if (kt + kMxAhead < nk) issue(kt + kMxAhead);   // refills the slot read in iteration kt-1
+    if (!rows_live) continue;
+    const uint32_t st = opaque_sgpr(lds0 + (kt % kMxStages) * kMxStageBytes);
+    uint32_t as[2], bs[4];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) as[f] = *lds_ptr<uint32_t>(st + a_scale_lane + f * 32 * 4);
+#pragma unroll
+    for (int f = 0; f < 4; ++f) bs[f] = *lds_ptr<uint32_t>(st + b_scale_lane + f * 32 * 4);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      u32x4_t ac[2], bc[4];
+#pragma unroll
+      for (int f = 0; f < 2; ++f) ac[f] = *lds_ptr<u32x4_t>(st + a_lane[s2] + f * 32 * kMxCodeRow);
+#pragma unroll
+      for (int f = 0; f < 4; ++f) bc[f] = *lds_ptr<u32x4_t>(st + b_lane[s2] + f * 32 * kMxCodeRow);
+      const int sh = 8 * (2 * s2 + hl);   // this lane's block within the stage's four
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        const i32x8_t av = {static_cast<int>(ac[mi][0]), static_cast<int>(ac[mi][1]),
+                            static_cast<int>(ac[mi][2]), static_cast<int>(ac[mi][3]), 0, 0, 0, 0};
+        const int sa = static_cast<int>((as[mi] >> sh) & 0xFFu);
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+          const i32x8_t bv = {static_cast<int>(bc[ni][0]), static_cast<int>(bc[ni][1]),
+                              static_cast<int>(bc[ni][2]), static_cast<int>(bc[ni][3]), 0, 0, 0, 0};
+          const int sb = static_cast<int>((bs[ni] >> sh) & 0xFFu);
+          // formats 4 = FP4 E2M1 for both operands; scale bytes in bits 7:0
+          acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[mi][ni], 4, 4, 0, sa, 0, sb);
         }
-        *reinterpret_cast<uint32_t*>(so + s * kOutPitch + i_loc * 2) = pack_bf16x2(g0, g1);
-        *reinterpret_cast<uint32_t*>(so + s * kOutPitch + 256 + i_loc * 2) = pack_bf16x2(u0, u1);
-      }
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < kOutRows * 16 / kThreads; ++j) {
-        const int c = tid + j * kThreads;
-        const int s = c >> 4, ch = c & 15;
-        const int64_t row = tc.m0 + tile_row(s, q);
-        if (row >= tc.m_end) continue;
-        const u32x4_t hg = *reinterpret_cast<const u32x4_t*>(so + s * kOutPitch + ch * 16);
-        const u32x4_t hu = *reinterpret_cast<const u32x4_t*>(so + s * kOutPitch + 256 + ch * 16);
-        const int64_t col = tc.n_tile * 128 + ch * 8;
-        if (args.out != nullptr) {
-          uint16_t* h = args.out + row * (2 * I) + col;
-          __builtin_nontemporal_store(hg, reinterpret_cast<u32x4_t*>(h));
-          __builtin_nontemporal_store(hu, reinterpret_cast<u32x4_t*>(h + I));
-        }
-        // SwiGLU on the bf16-rounded h, FP32 arithmetic (hardware exp2 / rcp)
-        u32x4_t a;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float bg0 = bf16_to_f32(static_cast<uint16_t>(hg[w] & 0xFFFFu));
-          const float bg1 = bf16_to_f32(static_cast<uint16_t>(hg[w] >> 16));
-          const float bu0 = bf16_to_f32(static_cast<uint16_t>(hu[w] & 0xFFFFu));
-          const float bu1 = bf16_to_f32(static_cast<uint16_t>(hu[w] >> 16));
-          a[w] = pack_bf16x2(bg0 * sigmoid_fast(bg0) * bu0, bg1 * sigmoid_fast(bg1) * bu1);
-        }
-        __builtin_nontemporal_store(a, reinterpret_cast<u32x4_t*>(args.act + row * I + col));
       }
     }
   }
+  float* s_gx = reinterpret_cast<float*>(lds + kMxGx);
+  if (tid < kBM) s_gx[tid] = 1.0f;   // no outer scales: the epilogue's factors are 1
+  __syncthreads();   // s_gx visible; every wave is past its last read of the ring
+  const float gw[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+  fwd_epilogue<MODE>(args, acc, tc, s_gx, gw, lds);
+}
+
+template <FwdMode MODE>
+bool launch_fwd_mx(const FwdArgs& args, int n_tiles, const char* name, hipStream_t s) {
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_mx_kernel<MODE>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, kMxLdsBytes);
+  if (attr != hipSuccess) return launch_ok(name) && false;
+  const int64_t tiles = grouped_m_tiles_bound(args.rows_alloc, args.E, kBM) * n_tiles;
+  if (tiles == 0) return true;
+  launch_kernel(name, fwd_mx_kernel<MODE>, dim3(xcd_grid(tiles)), dim3(kThreads), kMxLdsBytes, s, args);
+  return launch_ok(name);
 }
 
 template <FwdMode MODE, bool GS>
@@ -477,6 +661,20 @@ bool launch_linear_fwd(int64_t T, int K, int N, const int32_t* offsets, Fp4Opera
                        uint16_t* y, hipStream_t s) {
   FwdArgs args{T, K, N, K, 1, offsets, x, w, y, nullptr, nullptr};
   return launch_fwd<FwdMode::FC2>(args, N / kBN, "gemm_linear", s);
+}
+
+bool launch_fc1_mx(int64_t rows_alloc, int H, int I, int E, const int32_t* offsets, Fp4Operand x,
+                   Fp4Operand w1, uint16_t* h_out, uint16_t* a_out, float* dbg_f32, hipStream_t s) {
+  if (H % kMxBK) return false;
+  FwdArgs args{rows_alloc, H, 2 * I, I, E, offsets, x, w1, h_out, a_out, dbg_f32};
+  return launch_fwd_mx<FwdMode::FC1>(args, I / 128, "mx_gemm_fc1", s);
+}
+
+bool launch_fc2_mx(int64_t rows_alloc, int H, int I, int E, const int32_t* offsets, Fp4Operand a,
+                   Fp4Operand w2, uint16_t* o_out, hipStream_t s) {
+  if (I % kMxBK) return false;
+  FwdArgs args{rows_alloc, I, H, I, E, offsets, a, w2, o_out, nullptr, nullptr};
+  return launch_fwd_mx<FwdMode::FC2>(args, H / kBN, "mx_gemm_fc2", s);
 }
 
 }  // namespace w4a4

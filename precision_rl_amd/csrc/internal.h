@@ -62,6 +62,15 @@ bool launch_requant(const uint16_t* a, int64_t rows_alloc, int K, const int32_t*
                     const int32_t* src_row, uint8_t* codes, uint8_t* scales, float* outer,
                     hipStream_t s);
 
+// MXFP4 recipe (E2M1 codes, one E8M0 scale per 32 along the row, no outer
+// scale): the same routing and scatter, the MX row encoder.  K % 32 == 0,
+// K <= 4096 (returns false otherwise).  topk_idx = NULL: identity (weights).
+bool launch_quantize_permute_mx(const uint16_t* x, int64_t T, int K, const int32_t* topk_idx, int k, int E,
+                                int row_align, uint8_t* codes, uint8_t* scales, int32_t* offsets,
+                                int32_t* row_map, int32_t* src_row, void* ws, hipStream_t s);
+bool launch_requant_mx(const uint16_t* a, int64_t rows_alloc, int K, const int32_t* offsets, int E,
+                       uint8_t* codes, uint8_t* scales, hipStream_t s);
+
 // --------------------------------------------------------------- grouped GEMMs
 struct Fp4Operand {
   const uint8_t* codes;   // [rows, K/2]
@@ -76,6 +85,13 @@ bool launch_fc1(int64_t rows_alloc, int H, int I, int E, const int32_t* offsets,
 // FC2 over expert groups.
 bool launch_fc2(int64_t rows_alloc, int H, int I, int E, const int32_t* offsets, Fp4Operand a,
                 Fp4Operand w2, uint16_t* o_out, hipStream_t s);
+
+// MXFP4 FC1 / FC2 (scaled FP4 MFMA; operands' outer pointers unused).  The
+// reduction length (H for FC1, I for FC2) must be a multiple of 128.
+bool launch_fc1_mx(int64_t rows_alloc, int H, int I, int E, const int32_t* offsets, Fp4Operand x,
+                   Fp4Operand w1, uint16_t* h_out, uint16_t* a_out, float* dbg_f32, hipStream_t s);
+bool launch_fc2_mx(int64_t rows_alloc, int H, int I, int E, const int32_t* offsets, Fp4Operand a,
+                   Fp4Operand w2, uint16_t* o_out, hipStream_t s);
 
 // Dense linear layer y = x W^T (one group of T rows; offsets = {0, T}).
 bool launch_linear_fwd(int64_t T, int K, int N, const int32_t* offsets, Fp4Operand x, Fp4Operand w,

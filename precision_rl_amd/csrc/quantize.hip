@@ -484,7 +484,11 @@ enum class RowMode { Scatter, Identity, Requant };
 //   Scatter:  rows are tokens, written to their k expert rows (routing done);
 //   Identity: row r -> row r (weights), also writes row_map / src_row / offsets;
 //   Requant:  row r -> row r for the rows [0, offsets[E]).
-template <int TEAM, int PB, RowMode MODE>
+// MX: the MXFP4 recipe instead of NVFP4 -- each lane's 32 elements are one
+// block with an E8M0 scale 2^X, X = floor(log2 amax) - 2 clamped to
+// [-127, 127] (OCP Microscaling v1.0, section 6.3), codes Q_E2M1(x / 2^X);
+// one scale byte per 32 elements, no outer scale.
+template <int TEAM, int PB, RowMode MODE, bool MX = false>
 __global__ void __launch_bounds__(kThreads)
 quant_rows_kernel(const uint16_t* __restrict__ x, int64_t n_rows, int K,
                   const int32_t* __restrict__ topk_idx, int k, int E,
@@ -496,7 +500,7 @@ quant_rows_kernel(const uint16_t* __restrict__ x, int64_t n_rows, int K,
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int team = lane / TEAM, tl = lane % TEAM;
   const int pairs = K / 32;
-  const int64_t K2 = K / 2, K16 = K / 16;
+  const int64_t K2 = K / 2, K16 = K / 16, K32 = K / 32;
   int64_t n = n_rows;
   if constexpr (MODE == RowMode::Requant) n = min<int64_t>(n, offsets[E]);
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kWavesPerBlock * kRowsPerWave;
@@ -518,7 +522,7 @@ quant_rows_kernel(const uint16_t* __restrict__ x, int64_t n_rows, int K,
   for (; r < n; r += stride) {
     if (r + stride < n) load(r + stride, nxt);
 
-    // row amax over the team
+    // block amaxes; row amax over the team (NVFP4 only)
     uint32_t bm[PB][2];
     uint32_t amax = 0;
 #pragma unroll
@@ -532,11 +536,14 @@ quant_rows_kernel(const uint16_t* __restrict__ x, int64_t n_rows, int K,
         amax = max(amax, bm[i][h]);
       }
     }
+    float g = 0.0f;
+    if constexpr (!MX) {
 #pragma unroll
-    for (int off = TEAM / 2; off > 0; off >>= 1) amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), off, kWave)));
-    // a wider outer-scale domain: the group's max instead of the row's
-    if (group_amax != nullptr) amax = group_amax[r / group_rows];
-    const float g = outer_scale(amax);
+      for (int off = TEAM / 2; off > 0; off >>= 1) amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), off, kWave)));
+      // a wider outer-scale domain: the group's max instead of the row's
+      if (group_amax != nullptr) amax = group_amax[r / group_rows];
+      g = outer_scale(amax);
+    }
 
     // destination rows
     int64_t dst[8];
@@ -570,6 +577,24 @@ quant_rows_kernel(const uint16_t* __restrict__ x, int64_t n_rows, int K,
       if (p >= pairs) continue;
       u32x4_t cw;
       uint32_t sc2 = 0;
+      if constexpr (MX) {
+        // E8M0 byte X + 127 from the bf16 exponent field eb of the block max:
+        // floor(log2 amax) = eb - 127 for a normal amax, so the byte is
+        // eb - 2; zero and subnormal maxima (and eb <= 2) clamp to byte 0
+        const uint32_t eb = max(bm[i][0], bm[i][1]) >> 7;
+        sc2 = eb > 2u ? eb - 2u : 0u;
+        // 2^X as a double (X >= -127: a normal double), exact midpoints
+        const double unit = __longlong_as_double(static_cast<long long>(sc2 - 127 + 1023) << 52);
+        const PackedThr pt = pack_thresholds(make_thresholds(unit));
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t w[8] = {cur[i][2 * h][0], cur[i][2 * h][1], cur[i][2 * h][2], cur[i][2 * h][3],
+                                 cur[i][2 * h + 1][0], cur[i][2 * h + 1][1], cur[i][2 * h + 1][2], cur[i][2 * h + 1][3]};
+          const u32x2_t c2 = encode16(w, pt);
+          cw[2 * h] = c2[0];
+          cw[2 * h + 1] = c2[1];
+        }
+      } else {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const uint32_t w[8] = {cur[i][2 * h][0], cur[i][2 * h][1], cur[i][2 * h][2], cur[i][2 * h][3],
@@ -584,15 +609,19 @@ quant_rows_kernel(const uint16_t* __restrict__ x, int64_t n_rows, int K,
         cw[2 * h + 1] = c2[1];
         sc2 |= dbits << (8 * h);
       }
+      }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         if (j < ndst) {
           *reinterpret_cast<u32x4_t*>(codes + dst[j] * K2 + p * 16) = cw;
-          *reinterpret_cast<uint16_t*>(scales + dst[j] * K16 + p * 2) = static_cast<uint16_t>(sc2);
+          if constexpr (MX)
+            scales[dst[j] * K32 + p] = static_cast<uint8_t>(sc2);
+          else
+            *reinterpret_cast<uint16_t*>(scales + dst[j] * K16 + p * 2) = static_cast<uint16_t>(sc2);
         }
       }
     }
-    if (tl < ndst) {
+    if (!MX && tl < ndst) {
       int64_t d = dst[0];
 #pragma unroll
       for (int j = 1; j < 8; ++j)
@@ -607,7 +636,9 @@ quant_rows_kernel(const uint16_t* __restrict__ x, int64_t n_rows, int K,
 }
 
 // Pad rows of the expert groups (rows [offsets[e] + count[e], offsets[e+1])):
-// zero codes, scales and g; src_row = -1.  One wave per expert.
+// zero codes, scales and g (MX: no g; one scale per 32); src_row = -1.  One
+// wave per expert.
+template <bool MX = false>
 __global__ void __launch_bounds__(kThreads)
 pad_rows_kernel(int K, int E, const int32_t* __restrict__ offsets, const int32_t* __restrict__ expert_count,
                 uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ outer,
@@ -620,17 +651,18 @@ pad_rows_kernel(int K, int E, const int32_t* __restrict__ offsets, const int32_t
   for (int64_t r = r0; r < r1; ++r) {
     for (int b = lane; b < K / 16; b += kWave) {
       *reinterpret_cast<u32x2_t*>(codes + r * K2 + b * 8) = u32x2_t{0u, 0u};
-      scales[r * K16 + b] = 0;
+      if (!MX) scales[r * K16 + b] = 0;
+      else if (b < K / 32) scales[r * (K / 32) + b] = 0;
     }
     if (lane == 0) {
-      outer[r] = 0.0f;
+      if (!MX) outer[r] = 0.0f;
       src_row[r] = -1;
     }
   }
 }
 
 // Launches quant_rows_kernel with the team shape for K (K % 32 == 0, K <= 4096).
-template <RowMode MODE>
+template <RowMode MODE, bool MX = false>
 bool launch_rows(const char* name, const uint16_t* x, int64_t n_rows, int K, const int32_t* topk_idx, int k,
                  int E, uint8_t* codes, uint8_t* scales, float* outer, int32_t* offsets,
                  int32_t* row_map, int32_t* src_row, const int32_t* chunk_base, hipStream_t s,
@@ -646,7 +678,7 @@ bool launch_rows(const char* name, const uint16_t* x, int64_t n_rows, int K, con
     const int64_t need = (n_rows + rows_per_block - 1) / rows_per_block;
     const int64_t blocks = std::min<int64_t>(need, static_cast<int64_t>(device_cu_count()) * 16);
     if (blocks == 0) return true;
-    launch_kernel(name, quant_rows_kernel<TEAM, PB, MODE>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+    launch_kernel(name, quant_rows_kernel<TEAM, PB, MODE, MX>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
                   s, x, n_rows, K, topk_idx, k, E, codes, scales, outer, offsets, row_map, src_row, chunk_base,
                   group_amax, group_rows);
     return launch_ok(name);
@@ -768,7 +800,7 @@ bool launch_quantize_permute(const uint16_t* x, int64_t T, int K, const int32_t*
                                          offsets, row_map, src_row, nullptr, s);
     if (!ok) return false;
     if (topk_idx != nullptr && row_align > 1) {
-      launch_kernel("pad_rows", pad_rows_kernel, dim3(static_cast<unsigned>((E + kWavesPerBlock - 1) / kWavesPerBlock)),
+      launch_kernel("pad_rows", pad_rows_kernel<false>, dim3(static_cast<unsigned>((E + kWavesPerBlock - 1) / kWavesPerBlock)),
                     dim3(kThreads), 0, s, K, E, offsets, expert_count, codes, scales, outer, src_row);
       return launch_ok("pad_rows");
     }
@@ -830,7 +862,7 @@ bool launch_quantize_permute_grouped(const uint16_t* x, int64_t T, int K, const 
                                        offsets, row_map, src_row, nullptr, s, amax, group_rows);
   if (!ok) return false;
   if (topk_idx != nullptr && row_align > 1) {
-    launch_kernel("pad_rows", pad_rows_kernel, dim3(static_cast<unsigned>((E + kWavesPerBlock - 1) / kWavesPerBlock)),
+    launch_kernel("pad_rows", pad_rows_kernel<false>, dim3(static_cast<unsigned>((E + kWavesPerBlock - 1) / kWavesPerBlock)),
                   dim3(kThreads), 0, s, K, E, offsets, expert_count, codes, scales, outer, src_row);
     return launch_ok("pad_rows");
   }
@@ -850,6 +882,48 @@ bool launch_requant(const uint16_t* a, int64_t rows_alloc, int K, const int32_t*
                   dim3(kThreads), 0, s, a, rows_alloc, K, offsets, E, codes, scales, outer);
     return launch_ok("requant");
   });
+}
+
+// MXFP4: route (as above), then the MX row encoder; K % 32 == 0, K <= 4096.
+bool launch_quantize_permute_mx(const uint16_t* x, int64_t T, int K, const int32_t* topk_idx, int k, int E,
+                                int row_align, uint8_t* codes, uint8_t* scales, int32_t* offsets,
+                                int32_t* row_map, int32_t* src_row, void* ws, hipStream_t s) {
+  if (!rows_path(K)) return false;
+  const int64_t n_chunks = (T + kRouteChunk - 1) / kRouteChunk;
+  int32_t* counts = static_cast<int32_t*>(ws);
+  int32_t* expert_count = counts + n_chunks * E;
+  if (T == 0) {
+    launch_kernel("route_scan", zero_offsets_kernel, dim3(1), dim3(256), 0, s, offsets, topk_idx ? E + 1 : 2);
+    return launch_ok("zero_offsets");
+  }
+  if (topk_idx != nullptr) {
+    const uint32_t lds = static_cast<uint32_t>(E) * (kRouteChunk / 32) * sizeof(uint32_t);
+    launch_kernel("route_count", route_count_kernel, dim3(static_cast<unsigned>(n_chunks)), dim3(kRouteChunk), lds,
+                  s, topk_idx, T, k, E, row_map, counts);
+    if (!launch_ok("route_count")) return false;
+    launch_kernel("route_scan", route_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, counts,
+                  static_cast<int>(n_chunks), E, row_align, offsets, expert_count);
+    if (!launch_ok("route_scan")) return false;
+  }
+  const bool ok = topk_idx != nullptr
+      ? launch_rows<RowMode::Scatter, true>("mx_quantize_scatter", x, T, K, topk_idx, k, E, codes, scales,
+                                            nullptr, offsets, row_map, src_row, counts, s)
+      : launch_rows<RowMode::Identity, true>("mx_quantize_scatter", x, T, K, nullptr, 1, 1, codes, scales,
+                                             nullptr, offsets, row_map, src_row, nullptr, s);
+  if (!ok) return false;
+  if (topk_idx != nullptr && row_align > 1) {
+    launch_kernel("pad_rows", pad_rows_kernel<true>, dim3(static_cast<unsigned>((E + kWavesPerBlock - 1) / kWavesPerBlock)),
+                  dim3(kThreads), 0, s, K, E, offsets, expert_count, codes, scales, nullptr, src_row);
+    return launch_ok("pad_rows");
+  }
+  return true;
+}
+
+bool launch_requant_mx(const uint16_t* a, int64_t rows_alloc, int K, const int32_t* offsets, int E,
+                       uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  if (!rows_path(K)) return false;
+  return launch_rows<RowMode::Requant, true>("mx_requant", a, rows_alloc, K, nullptr, 1, E, codes, scales,
+                                             nullptr, const_cast<int32_t*>(offsets), nullptr, nullptr, nullptr, s);
 }
 
 }  // namespace w4a4

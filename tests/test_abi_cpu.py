@@ -105,3 +105,30 @@ def test_invalid_arguments_rejected_before_launch():
     assert lin_bwd(ws=None) == -3
     assert lib.w4a4_workspace_size(3, 0, 256, 256, 1, 1, 1) > 0
     assert lib.w4a4_workspace_size(3, 0, 128, 256, 1, 1, 1) == 0
+
+
+def test_mx_calls_reject_invalid_arguments_before_launch():
+    lib = _lib()
+    buf = ctypes.create_string_buffer(4096)
+    p = ctypes.c_void_p(ctypes.addressof(buf) + (-ctypes.addressof(buf)) % 16)
+
+    def mqp(T=4, K=64, idx=p, k=2, E=8, A=1, x=p, ws=p, wsb=1 << 20):
+        return lib.w4a4_mx_quantize_permute(x, T, K, idx, k, E, A, p, p, p, p, p, ws, wsb, None)
+
+    assert mqp(K=48) == -2                             # MX blocks of 32: K % 32 == 0
+    assert mqp(K=24) == -1                             # not even a multiple of 16
+    assert mqp(K=8192) == -2                           # K <= 4096
+    assert mqp(k=9, E=8) == -1
+    assert mqp(x=None) == -1
+    assert mqp(ws=None) == -3
+    assert mqp(idx=None, k=2) == -1
+
+    def mfwd(H=256, I=128, T=4, ws=p, wsb=1 << 40, dc=None, ds=None):
+        return lib.w4a4_mx_grouped_expert_fwd(T, H, I, 8, 2, 1, p, p, p, p, p, p, p, p, p, p,
+                                              p, None, None, None, dc, ds, ws, wsb, None)
+
+    assert mfwd(H=250) == -1
+    assert mfwd(H=288) == -2
+    assert mfwd(I=96) == -2
+    assert mfwd(ws=None) == -3
+    assert mfwd(dc=p) == -1                            # debug codes without debug scales
