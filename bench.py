@@ -29,6 +29,9 @@ sys.path.insert(0, ROOT)
 METRIC = "W4A4 MoE expert fwd+bwd tokens/s and % MFMA/HBM peak, Qwen3-30B-A3B layer"
 WORKLOAD = "learner"
 PEAK_MFMA_TFLOPS = 2500.0      # MI355X dense f16 / bf16 MFMA
+PEAK_MFMA_FP4_TFLOPS = 10100.0  # MI355X dense MXFP4 (scaled FP4) MFMA
+# kernels whose MFMA peak is not the f16 / bf16 one
+KERNEL_PEAK = {"mx_gemm_fc1": PEAK_MFMA_FP4_TFLOPS, "mx_gemm_fc2": PEAK_MFMA_FP4_TFLOPS}
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 # kernel name -> source file whose content decides whether stored counters still apply
@@ -41,6 +44,8 @@ KERNEL_SOURCES = {
     "dx_gather_sum": "elementwise.hip",
     "gemm_linear": "gemm_fwd.hip", "gemm_linear_dgrad": "gemm_bwd.hip",
     "gemm_linear_wgrad": "gemm_bwd.hip",
+    "mx_gemm_fc1": "gemm_fwd.hip", "mx_gemm_fc2": "gemm_fwd.hip",
+    "mx_quantize_scatter": "quantize.hip", "mx_requant": "quantize.hip",
 }
 
 
@@ -66,7 +71,12 @@ def algorithmic_work(T, H, E, k, I):
         # read x[t] and the token's k maps; write k rows of xp
         "x_scatter": T * (H * 2 + k * 4) + M * H * 2,
         "dx_gather_sum": T * (k * H * 2 + k * 4 + H * 2),
+        # MXFP4 recipe: one E8M0 byte per 32 elements, no outer scales
+        "mx_quantize_scatter": T * (H * 2 + k * 4) + M * (H // 2 + H // 32) + T * k * 4 + M * 4,
+        "mx_requant": M * (I * 2 + I // 2 + I // 32),
     }
+    fl["mx_gemm_fc1"] = fl["gemm_fc1"]
+    fl["mx_gemm_fc2"] = fl["gemm_fc2"]
     return fl, by
 
 
@@ -284,11 +294,12 @@ def main_qp(args):
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(d, w, tokens=512, experts=8):
+def cpu_baseline(d, w, tokens=512, experts=8, recipe="nvfp4"):
     """The FP64 oracle on a bounded sample of the learner workload: the first
     `tokens` tokens, each routed to all `experts` experts (k = 8 per token as
     in the workload, so the per-token work is the same), expert weights
-    quantised before timing.  Times quantize+permute + forward + backward."""
+    quantised before timing.  Times quantize+permute + forward + backward
+    (the forward of the given recipe)."""
     from oracle import moe, nvfp4 as q
     try:
         from threadpoolctl import threadpool_info
@@ -303,15 +314,18 @@ def cpu_baseline(d, w, tokens=512, experts=8):
     w2 = q.bf16_bits_to_f64(d["w2"][:experts])
     idx = np.tile(np.arange(k, dtype=np.int32), (tokens, 1))
     p = d["topk_w"][:tokens]
-    w1q, w2q = moe.quantize_weights(w1), moe.quantize_weights(w2)
+    mx = recipe == "mxfp4"
+    quant = moe.quantize_weights_mx if mx else moe.quantize_weights
+    w1q, w2q = quant(w1), quant(w2)
     t0 = time.perf_counter()
-    f = moe.forward(x, idx, p, w1q, w2q, experts)
+    f = (moe.forward_mx if mx else moe.forward)(x, idx, p, w1q, w2q, experts)
     xq = f["xq"]
     moe.backward(dy, x, w1, w2, f["h"], f["a"], p, xq["offsets"], xq["row_map"], xq["src_row"])
     dt = time.perf_counter() - t0
     return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{tokens} tokens of the learner workload (H={w.H}, I={w.I}, k={k}) routed "
-                      f"to {experts} experts, FP64 numpy, quantize+permute+forward+backward, "
+                      f"to {experts} experts, FP64 numpy, quantize+permute+forward+backward"
+                      f"{' (MXFP4 recipe)' if mx else ''}, "
                       f"{dt:.1f} s", "seconds": dt,
             "host_cpus": len(os.sched_getaffinity(0))}
 
@@ -360,7 +374,7 @@ def summarize(kern, ms, steps, fl, by, concurrent=None):
                  "share": round(rec["total_ms"] / (ms * steps), 4)}
         if name in fl:
             entry["tflops"] = round(fl[name] / (avg_ms * 1e-3) / 1e12, 1)
-            entry["frac_mfma"] = round(entry["tflops"] / PEAK_MFMA_TFLOPS, 4)
+            entry["frac_mfma"] = round(entry["tflops"] / KERNEL_PEAK.get(name, PEAK_MFMA_TFLOPS), 4)
         elif name in by:
             entry["gbs"] = round(by[name] / (avg_ms * 1e-3) / 1e9, 1)
             entry["frac_hbm"] = round(entry["gbs"] / PEAK_HBM_GBS, 4)
@@ -377,8 +391,9 @@ def summarize(kern, ms, steps, fl, by, concurrent=None):
     dom_avg_s = kern[dom]["total_ms"] / kern[dom]["count"] * 1e-3
     if dom in fl:
         ach = fl[dom] / dom_avg_s / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_MFMA_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_MFMA_TFLOPS, 4)}
+        peak = KERNEL_PEAK.get(dom, PEAK_MFMA_TFLOPS)
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(ach / peak, 4)}
     else:
         ach = by[dom] / dom_avg_s / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
@@ -402,6 +417,10 @@ def main():
                          "qp: quantize+permute alone")
     ap.add_argument("--outer", choices=["token", "tensor"], default="token",
                     help="qp: outer-scale domain of the activations")
+    ap.add_argument("--recipe", choices=["nvfp4", "mxfp4"], default="nvfp4",
+                    help="learner: the forward's format -- nvfp4 (E4M3 per 16 + FP32 outer "
+                         "scales, exact f16 decode, the default) or mxfp4 (E8M0 per 32, scaled "
+                         "FP4 MFMA)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: the benchmark runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -428,15 +447,20 @@ def main():
     x, w1, w2, dy = bf(d["x"]), bf(d["w1"]), bf(d["w2"]), bf(d["dy"])
     idx = torch.from_numpy(d["topk_idx"]).to(dev)
     p = torch.from_numpy(d["topk_w"]).to(dev)
-    w1q, w2q = b.quantize_weights(w1), b.quantize_weights(w2)      # offline, untimed
+    mx = args.recipe == "mxfp4"
+    if mx:
+        w1q, w2q = b.quantize_weights_mx(w1), b.quantize_weights_mx(w2)   # offline, untimed
+    else:
+        w1q, w2q = b.quantize_weights(w1), b.quantize_weights(w2)         # offline, untimed
 
     cap = b.rows_capacity(T, k, E, A)
     xq = dict(codes=torch.empty(cap, H // 2, dtype=torch.uint8, device=dev),
-              scales=torch.empty(cap, H // 16, dtype=torch.uint8, device=dev),
-              outer=torch.empty(cap, dtype=torch.float32, device=dev),
+              scales=torch.empty(cap, H // (32 if mx else 16), dtype=torch.uint8, device=dev),
               offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
               row_map=torch.empty(T, k, dtype=torch.int32, device=dev),
               src_row=torch.empty(cap, dtype=torch.int32, device=dev))
+    if not mx:
+        xq["outer"] = torch.empty(cap, dtype=torch.float32, device=dev)
     ws_qp = torch.empty(b.workspace_size(b.WS_QUANTIZE_PERMUTE, T, H, I, E, k, A) + 256,
                         dtype=torch.uint8, device=dev)
     ws_f = torch.empty(b.workspace_size(b.WS_FORWARD, T, H, I, E, k, A), dtype=torch.uint8, device=dev)
@@ -451,9 +475,14 @@ def main():
     calibration_copy(torch, dev)
 
     def step():
-        b.w4a4_quantize_permute(x, idx, E, A, out=xq, workspace=ws_qp)
-        b.w4a4_grouped_expert_fwd(xq, p, w1q, w2q, T, H, I, E, k, A, save=True, y=y,
-                                  workspace=ws_f, saved=saved)
+        if mx:
+            b.w4a4_mx_quantize_permute(x, idx, E, A, out=xq, workspace=ws_qp)
+            b.w4a4_mx_grouped_expert_fwd(xq, p, w1q, w2q, T, H, I, E, k, A, save=True, y=y,
+                                         workspace=ws_f, saved=saved)
+        else:
+            b.w4a4_quantize_permute(x, idx, E, A, out=xq, workspace=ws_qp)
+            b.w4a4_grouped_expert_fwd(xq, p, w1q, w2q, T, H, I, E, k, A, save=True, y=y,
+                                      workspace=ws_f, saved=saved)
         b.w4a4_expert_bwd(dy, x, w1, w2, saved["h"], saved["a"], p, xq, T, H, I, E, k, A,
                           out=grads, workspace=ws_b)
 
@@ -462,7 +491,7 @@ def main():
     per_kernel, roof = summarize(kern, ms, args.steps, fl, by)
 
     gemm_ms = sum(kern[n]["total_ms"] for n in kern if n in fl) / args.steps
-    total_flop = sum(fl.values())
+    total_flop = sum(v for n, v in fl.items() if not n.startswith("mx_"))
     out = {
         "metric": METRIC,
         "value": round(T / (ms * 1e-3), 1),
@@ -474,9 +503,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "nvfp4->f16 MFMA fwd, bf16 MFMA bwd, fp32 accumulate",
+        "dtype": ("mxfp4 scaled-FP4 MFMA fwd" if mx else "nvfp4->f16 MFMA fwd")
+                 + ", bf16 MFMA bwd, fp32 accumulate",
         "data": "synthetic (seeded; random-init weights of the layer's shape)",
-        "config": {"workload": f"{WORKLOAD}: quantize+permute + grouped expert fwd + BF16 STE bwd",
+        "config": {"workload": f"{WORKLOAD}: quantize+permute + grouped expert fwd + BF16 STE bwd"
+                               + (" (MXFP4 recipe: E2M1 + E8M0 per 32)" if mx else ""),
                    "T": T, "H": H, "E": E, "top_k": k, "I": I, "row_align": A,
                    "routing": w.routing},
         "roofline": roof,
@@ -486,7 +517,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the FP64 oracle on the host", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(d, w, tokens=args.cpu_tokens)
+        out["cpu_baseline"] = cpu_baseline(d, w, tokens=args.cpu_tokens, recipe=args.recipe)
     print(json.dumps(out), flush=True)
 
 
