@@ -70,7 +70,8 @@ typedef enum {
   W4A4_WS_FORWARD = 1,
   W4A4_WS_BACKWARD = 2,
   W4A4_WS_LINEAR_BACKWARD = 3,  /* w4a4_linear_bwd: H = K, I = N; T, E, k, row_align unused */
-  W4A4_WS_QUANTIZE_PERMUTE_DOMAIN = 4   /* w4a4_quantize_permute_domain, any group_rows; H = K */
+  W4A4_WS_QUANTIZE_PERMUTE_DOMAIN = 4,  /* w4a4_quantize_permute_domain, any group_rows; H = K */
+  W4A4_WS_MX8_BACKWARD = 5              /* w4a4_mx8_expert_bwd */
 } w4a4_workspace_kind;
 
 /* Padded dispatched-row capacity: T*k + E*(row_align-1).  Returns -1 on bad
@@ -323,6 +324,35 @@ w4a4_status w4a4_mx_grouped_expert_fwd(
     const uint8_t* w2_codes, const uint8_t* w2_scales,
     void* y, void* save_h, void* save_a, float* dbg_fc1_f32,
     uint8_t* dbg_a_codes, uint8_t* dbg_a_scales,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * w4a4_mx8_expert_bwd -- the straight-through backward with every GEMM
+ * operand in MXFP8 instead of BF16: the variant the pages measure against
+ * their BF16 backward (AI summary, key findings: BF16 backward about 1.21x
+ * faster, gradient rel-L2 0.001663 against 0.037653 for MXFP8; Technical
+ * Report, section 4.3: backward precision is set apart from the forward).
+ * Each operand is quantised from the same bf16 tensors the BF16 backward
+ * uses, along that GEMM's reduction axis (E4M3 elements, one E8M0 scale per
+ * 32, OCP Microscaling v1.0 section 6.3: X = floor(log2 amax) - 8, elements
+ * Q_E4M3(x / 2^X) round-to-nearest-even, saturating at 448):
+ *   dA = bf16(Q_H(dO) Q_H(W2[e])), dW2[e] = bf16(Q_r(dO_e)^T Q_r(a_e)),
+ *   dH = SwiGLU backward (bf16, as w4a4_expert_bwd),
+ *   dXp = bf16(Q_2I(dH) Q_2I(W1[e])), dW1[e] = bf16(Q_r(dH_e)^T Q_r(xp_e)),
+ *   dX[t] = bf16(sum_j dXp[row_map[t,j]]),
+ * where Q_r quantises along the expert's dispatched rows; the GEMMs run on
+ * gfx950's scaled FP8 MFMA with FP32 accumulation.  Arguments as in
+ * w4a4_expert_bwd, with row_align == 128 (the row blocks of 32 never
+ * straddle two experts and each expert's rows are whole K stages), I % 256
+ * == 0, and a workspace of w4a4_workspace_size(W4A4_WS_MX8_BACKWARD, ...)
+ * bytes.  Runs on `stream` alone.  dW of an empty expert is zeros.
+ */
+w4a4_status w4a4_mx8_expert_bwd(
+    int64_t T, int H, int I, int E, int k, int row_align,
+    const void* dy, const void* x, const void* w1, const void* w2,
+    const void* save_h, const void* save_a, const float* topk_w,
+    const int32_t* expert_offsets, const int32_t* row_map, const int32_t* src_row,
+    void* dx, void* dw1, void* dw2,
     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a status code. */

@@ -360,3 +360,73 @@ def forward_mx(x, topk_idx, topk_w, w1q, w2q, E, row_align=1):
     y = q.round_bf16(unpermute_sum(o, xq["row_map"], topk_w))
     return dict(xq=xq, h64=h64, h=h, a=a, a_codes=ac, a_scales=as_, o64=o64, o=o, y=y,
                 live=xq["src_row"] >= 0)
+
+
+def backward_mx8(dy, x, w1, w2, h, a, topk_w, offsets, row_map, src_row):
+    """Straight-through backward with every GEMM operand in MXFP8.
+
+    The pages compare their BF16 backward with an MXFP8 one (AI summary,
+    key findings; Technical Report, section 4.3: backward precision is
+    configured apart from the forward).  READING of the MXFP8 backward: each
+    GEMM operand is quantised to MXFP8 (E4M3 elements, one E8M0 scale per 32,
+    mxfp4.quantize_rows_mx8) along that GEMM's reduction axis, from the same
+    bf16 tensors the BF16 backward uses, and the bf16 cast points are the
+    BF16 backward's:
+
+      FC2 dgrad  dA     = bf16(Q_H(dO_e) Q_H(W2[e]))        blocks along H
+      FC2 wgrad  dW2[e] = bf16(Q_r(dO_e)^T Q_r(a_e))        blocks along the expert's rows
+      SwiGLU bwd on the bf16 dA and h (as ``backward``)
+      FC1 dgrad  dXp    = bf16(Q_2I(dH_e) Q_2I(W1[e]))      blocks along 2I
+      FC1 wgrad  dW1[e] = bf16(Q_r(dH_e)^T Q_r(xp_e))
+      dX gather  as ``backward``
+
+    Blocks along the rows never straddle two experts: every expert group's
+    first row must be a multiple of 32 (row_align a multiple of 32), and the
+    zero pad rows fill the last block.
+    """
+    R = q.round_bf16
+    offsets = np.asarray(offsets, dtype=np.int64)
+    if np.any(offsets % mx.MX_BLOCK):
+        raise ValueError("expert groups must start at multiples of 32 rows")
+    x = np.asarray(x, dtype=np.float64)
+    T, H = x.shape
+    E, I2, _ = w1.shape
+    I = I2 // 2
+    rows = int(offsets[-1])
+    k = row_map.shape[1]
+    p = np.asarray(topk_w, dtype=np.float64)
+
+    dO = np.zeros((rows, H))
+    for j in range(k):
+        dO[row_map[:, j]] = R(p[:, j:j + 1] * dy)
+    qdO_h = mx.mx8_along_rows(dO)
+    dA = np.zeros((rows, I))
+    dW2 = np.zeros((E, H, I))
+    for e in range(E):
+        r0, r1 = offsets[e], offsets[e + 1]
+        dA[r0:r1] = R(qdO_h[r0:r1] @ mx.mx8_along_columns(w2[e]))
+        if r1 > r0:
+            dW2[e] = R(mx.mx8_along_columns(dO[r0:r1]).T @ mx.mx8_along_columns(a[r0:r1]))
+
+    gate, up = h[:, :I], h[:, I:]
+    s = 1.0 / (1.0 + np.exp(-gate))
+    dH = np.concatenate([R(dA * up * s * (1.0 + gate * (1.0 - s))),
+                         R(dA * gate * s)], axis=1)
+
+    xs = np.zeros((rows, H))
+    live = src_row >= 0
+    xs[live] = x[src_row[live]]
+    qdH = mx.mx8_along_rows(dH)
+    dXp = np.zeros((rows, H))
+    dW1 = np.zeros((E, I2, H))
+    for e in range(E):
+        r0, r1 = offsets[e], offsets[e + 1]
+        dXp[r0:r1] = R(qdH[r0:r1] @ mx.mx8_along_columns(w1[e]))
+        if r1 > r0:
+            dW1[e] = R(mx.mx8_along_columns(dH[r0:r1]).T @ mx.mx8_along_columns(xs[r0:r1]))
+
+    dX = np.zeros((T, H))
+    for j in range(k):
+        dX += dXp[row_map[:, j]]
+    dX = R(dX)
+    return dict(dO=dO, dA=dA, dH=dH, dXp=dXp, dX=dX, dW1=dW1, dW2=dW2)

@@ -97,3 +97,68 @@ def block_values_mx(codes, scales):
     R, K = codes.shape
     s = e8m0_decode(scales)
     return (q.e2m1_decode(codes).reshape(R, K // MX_BLOCK, MX_BLOCK) * s[:, :, None]).reshape(R, K)
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 (E4M3 elements, one E8M0 scale per 32): the backward's format in the
+# MXFP8-backward variant the pages compare against their BF16 backward.
+# ---------------------------------------------------------------------------
+# Exponent of E4M3's largest magnitude: 448 = 1.75 * 2^8.
+E4M3_EMAX = 8
+
+
+def shared_exponent_e4m3(amax):
+    """X = floor(log2 amax) - 8 clamped to [-127, 127]; amax = 0 gives -127
+    (OCP Microscaling v1.0, section 6.3, with E4M3's emax = 8)."""
+    a = np.asarray(amax, dtype=np.float64)
+    X = np.full(a.shape, E8M0_MIN_EXP, dtype=np.int64)
+    nz = a > 0
+    _, ex = np.frexp(a[nz])
+    X[nz] = np.clip(ex.astype(np.int64) - 1 - E4M3_EMAX, E8M0_MIN_EXP, E8M0_MAX_EXP)
+    return X
+
+
+def quantize_rows_mx8(x):
+    """MXFP8 (E4M3) of each row of ``x`` along the row, blocks of 32.
+
+    Per block: X = shared_exponent_e4m3(amax), scale byte X + 127, element
+    Q_E4M3(x / 2^X): round to nearest, ties to even, subnormals kept,
+    saturating at 448 (amax / 2^X lies in [256, 512), so the block max can
+    exceed 448 and clamps to it).  Returns (values float64 [R, K]: the
+    E4M3 values (sign included) without the scale, scales uint8 [R, K/32]).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if x.ndim != 2 or x.shape[1] % MX_BLOCK:
+        raise ValueError("rows of a multiple of 32 elements expected")
+    R, K = x.shape
+    blocks = x.reshape(R, K // MX_BLOCK, MX_BLOCK)
+    X = shared_exponent_e4m3(np.abs(blocks).max(axis=2) if K else np.zeros((R, 0)))
+    mag = q.e4m3_round(np.ldexp(np.abs(blocks), -X[:, :, None]))
+    vals = np.where(np.signbit(blocks), -mag, mag).reshape(R, K)
+    return vals, (X + E8M0_BIAS).astype(np.uint8)
+
+
+def e4m3_bytes(vals):
+    """Signed E4M3 values (float64) -> E4M3FN bytes (sign in bit 7; -0 -> 0x80)."""
+    vals = np.asarray(vals, dtype=np.float64)
+    return (q.e4m3_encode_exact(np.abs(vals)) | (np.signbit(vals).astype(np.uint8) << 7)).astype(np.uint8)
+
+
+def mx8_values(vals, scales):
+    """E4M3 value times 2^X per element (float64)."""
+    vals = np.asarray(vals, dtype=np.float64)
+    R, K = vals.shape
+    s = e8m0_decode(scales)
+    return (vals.reshape(R, K // MX_BLOCK, MX_BLOCK) * s[:, :, None]).reshape(R, K)
+
+
+def mx8_along_rows(x):
+    """The MXFP8 reconstruction of x quantised along its rows (axis 1)."""
+    v, s = quantize_rows_mx8(x)
+    return mx8_values(v, s)
+
+
+def mx8_along_columns(x):
+    """The MXFP8 reconstruction of x quantised along its columns (axis 0):
+    blocks of 32 consecutive rows of one column share a scale."""
+    return mx8_along_rows(np.asarray(x, dtype=np.float64).T).T

@@ -42,6 +42,9 @@ _SIGS = {
                                            c_vp, c_vp, c_vp, c_vp,
                                            c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                            c_vp, c_sz, c_vp]),
+    "w4a4_mx8_expert_bwd": (c_int, [c_i64, c_int, c_int, c_int, c_int, c_int,
+                                    c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                    c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "w4a4_status_string": (ctypes.c_char_p, [c_int]),
     "w4a4_last_error": (ctypes.c_char_p, []),
     "w4a4_profiler_enable": (c_int, [c_int]),
@@ -50,6 +53,7 @@ _SIGS = {
 
 WS_QUANTIZE_PERMUTE, WS_FORWARD, WS_BACKWARD, WS_LINEAR_BACKWARD = 0, 1, 2, 3
 WS_QUANTIZE_PERMUTE_DOMAIN = 4
+WS_MX8_BACKWARD = 5
 
 
 class W4A4Error(RuntimeError):
@@ -224,6 +228,25 @@ def w4a4_expert_bwd(dy, x, w1, w2, h, a, topk_w, xq, T, H, I, E, k, row_align=1,
     need = workspace_size(WS_BACKWARD, T, H, I, E, k, row_align)
     ws = _workspace(need, dev, workspace)
     _check(lib.w4a4_expert_bwd(
+        T, H, I, E, k, row_align, _p(dy), _p(x), _p(w1), _p(w2), _p(h), _p(a), _p(topk_w),
+        _p(xq["offsets"]), _p(xq["row_map"]), _p(xq["src_row"]),
+        _p(out["dx"]), _p(out["dw1"]), _p(out["dw2"]), _p(ws), ws.numel(), _stream()))
+    return out
+
+
+def w4a4_mx8_expert_bwd(dy, x, w1, w2, h, a, topk_w, xq, T, H, I, E, k, row_align=128,
+                        out=None, workspace=None):
+    """Straight-through backward with MXFP8 GEMM operands (row_align 128).
+    Returns dict(dx [T, H], dw1 [E, 2I, H], dw2 [E, H, I]) bf16."""
+    lib = load()
+    dev = dy.device
+    if out is None:
+        out = dict(dx=torch.empty(T, H, dtype=torch.bfloat16, device=dev),
+                   dw1=torch.empty(E, 2 * I, H, dtype=torch.bfloat16, device=dev),
+                   dw2=torch.empty(E, H, I, dtype=torch.bfloat16, device=dev))
+    need = workspace_size(WS_MX8_BACKWARD, T, H, I, E, k, row_align)
+    ws = _workspace(need, dev, workspace)
+    _check(lib.w4a4_mx8_expert_bwd(
         T, H, I, E, k, row_align, _p(dy), _p(x), _p(w1), _p(w2), _p(h), _p(a), _p(topk_w),
         _p(xq["offsets"]), _p(xq["row_map"]), _p(xq["src_row"]),
         _p(out["dx"]), _p(out["dw1"]), _p(out["dw2"]), _p(ws), ws.numel(), _stream()))

@@ -129,6 +129,37 @@ BwdWs bwd_ws(int64_t cap, int H, int I, int E) {
   return w;
 }
 
+// MXFP8 backward: the BF16 backward's buffers plus the MXFP8 operands, each
+// GEMM operand quantised along that GEMM's reduction axis; transposed
+// operands (columns = dispatched rows) have P = roundup(cap, 128) columns.
+struct Mx8Ws {
+  size_t dO, xp, dA, dH, dXp, dOq, dOqs, dOt, dOts, at, ats, w2t, w2ts, dHq, dHqs, dHt, dHts, w1t, w1ts, xpt,
+      xpts, total;
+  int64_t P;
+};
+Mx8Ws mx8_ws(int64_t cap, int H, int I, int E) {
+  Mx8Ws w;
+  w.P = (cap + 127) / 128 * 128;
+  const size_t c = static_cast<size_t>(cap), P = static_cast<size_t>(w.P), e = static_cast<size_t>(E);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off += round_up(bytes); return o; };
+  w.dO = take(c * H * 2);
+  w.xp = take(c * H * 2);
+  w.dA = take(c * I * 2);
+  w.dH = take(c * 2 * I * 2);
+  w.dXp = take(c * H * 2);
+  w.dOq = take(c * H);          w.dOqs = take(c * H / 32);
+  w.dOt = take(H * P);          w.dOts = take(H * P / 32);
+  w.at = take(I * P);           w.ats = take(I * P / 32);
+  w.w2t = take(e * I * H);      w.w2ts = take(e * I * H / 32);
+  w.dHq = take(c * 2 * I);      w.dHqs = take(c * 2 * I / 32);
+  w.dHt = take(2 * I * P);      w.dHts = take(2 * I * P / 32);
+  w.w1t = take(e * H * 2 * I);  w.w1ts = take(e * H * 2 * I / 32);
+  w.xpt = take(H * P);          w.xpts = take(H * P / 32);
+  w.total = off;
+  return w;
+}
+
 w4a4_status check_moe_shape(int64_t T, int H, int I, int E, int k, int row_align) {
   if (T < 0 || H <= 0 || I <= 0 || E <= 0 || k <= 0)
     return fail(W4A4_ERR_INVALID_ARG, "non-positive size (T=%lld H=%d I=%d E=%d k=%d)",
@@ -219,6 +250,9 @@ size_t w4a4_workspace_size(int kind, int64_t T, int H, int I, int E, int k, int 
     case W4A4_WS_BACKWARD:
       if (I <= 0) return 0;
       return bwd_ws(cap, H, I, E).total;
+    case W4A4_WS_MX8_BACKWARD:
+      if (I <= 0) return 0;
+      return mx8_ws(cap, H, I, E).total;
     default:
       return 0;
   }
@@ -561,6 +595,76 @@ w4a4_status w4a4_mx_grouped_expert_fwd(
     return W4A4_ERR_LAUNCH;
   if (!launch_unpermute(T, H, k, o_buf, row_map, topk_w, static_cast<uint16_t*>(y), s))
     return W4A4_ERR_LAUNCH;
+  return W4A4_OK;
+}
+
+w4a4_status w4a4_mx8_expert_bwd(int64_t T, int H, int I, int E, int k, int row_align, const void* dy,
+                                const void* x, const void* w1, const void* w2, const void* save_h,
+                                const void* save_a, const float* topk_w, const int32_t* expert_offsets,
+                                const int32_t* row_map, const int32_t* src_row, void* dx, void* dw1, void* dw2,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  w4a4_status st = check_moe_shape(T, H, I, E, k, row_align);
+  if (st != W4A4_OK) return st;
+  if (row_align != 128)
+    return fail(W4A4_ERR_UNSUPPORTED, "the MXFP8 backward needs row_align 128 (row_align=%d)", row_align);
+  if (I % 256) return fail(W4A4_ERR_UNSUPPORTED, "the MXFP8 backward needs I %% 256 == 0 (I=%d)", I);
+  REQUIRE_PTR(expert_offsets);
+  REQUIRE_PTR(w1); REQUIRE_PTR(w2); REQUIRE_PTR(dw1); REQUIRE_PTR(dw2);
+  if (T > 0) {
+    REQUIRE_PTR(dy); REQUIRE_PTR(x); REQUIRE_PTR(save_h); REQUIRE_PTR(save_a);
+    REQUIRE_PTR(topk_w); REQUIRE_PTR(row_map); REQUIRE_PTR(src_row); REQUIRE_PTR(dx);
+  }
+  const int64_t cap = w4a4_rows_capacity(T, k, E, row_align);
+  const Mx8Ws L = mx8_ws(cap, H, I, E);
+  if (workspace == nullptr || workspace_bytes < L.total)
+    return fail(W4A4_ERR_WORKSPACE, "workspace needs %zu bytes", L.total);
+  OPTIONAL_PTR(workspace);
+  if (L.P * static_cast<int64_t>(H) > (int64_t{1} << 31))
+    return fail(W4A4_ERR_UNSUPPORTED, "too many dispatched rows for the MXFP8 backward's 32-bit offsets");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  auto bf = [&](size_t o) { return reinterpret_cast<uint16_t*>(ws + o); };
+  uint16_t *dO = bf(L.dO), *xp = bf(L.xp), *dA = bf(L.dA), *dH = bf(L.dH), *dXp = bf(L.dXp);
+  const uint16_t* h = static_cast<const uint16_t*>(save_h);
+  const uint16_t* a = static_cast<const uint16_t*>(save_a);
+  const uint16_t* W1 = static_cast<const uint16_t*>(w1);
+  const uint16_t* W2 = static_cast<const uint16_t*>(w2);
+  const int32_t* off = expert_offsets;
+  const int64_t P = L.P;
+
+  // the row operands in expert order (as the BF16 backward), pad rows zero
+  if (!launch_scatter_dy(T, H, k, static_cast<const uint16_t*>(dy), row_map, topk_w, dO, s) ||
+      !launch_zero_pad_rows(cap, H, src_row, off, E, dO, s) ||
+      !launch_scatter_x(T, H, k, static_cast<const uint16_t*>(x), row_map, xp, s) ||
+      !launch_zero_pad_rows(cap, H, src_row, off, E, xp, s))
+    return W4A4_ERR_LAUNCH;
+  // FC2: dA = Q_H(dO) Q_H(W2[e]);  dW2[e] = Q_r(dO_e)^T Q_r(a_e)
+  if (!launch_q8_rows(dO, cap, H, off, E, ws + L.dOq, ws + L.dOqs, s) ||
+      !launch_q8_cols(dO, cap, H, 1, off, E, P, ws + L.dOt, ws + L.dOts, s) ||
+      !launch_q8_cols(a, cap, I, 1, off, E, P, ws + L.at, ws + L.ats, s) ||
+      !launch_q8_cols(W2, H, I, E, nullptr, 0, H, ws + L.w2t, ws + L.w2ts, s))
+    return W4A4_ERR_LAUNCH;
+  if (cap > 0 && !launch_mx8_dgrad(cap, H, I, E, off, ws + L.dOq, ws + L.dOqs, ws + L.w2t, ws + L.w2ts, dA,
+                                   "mx8_dgrad_fc2", s))
+    return W4A4_ERR_LAUNCH;
+  if (!launch_mx8_wgrad(H, I, E, off, ws + L.dOt, ws + L.dOts, ws + L.at, ws + L.ats, P,
+                        static_cast<uint16_t*>(dw2), "mx8_wgrad_fc2", s))
+    return W4A4_ERR_LAUNCH;
+  if (!launch_swiglu_bwd(dA, h, cap, I, off, E, dH, s)) return W4A4_ERR_LAUNCH;
+  // FC1: dXp = Q_2I(dH) Q_2I(W1[e]);  dW1[e] = Q_r(dH_e)^T Q_r(xp_e)
+  if (!launch_q8_rows(dH, cap, 2 * I, off, E, ws + L.dHq, ws + L.dHqs, s) ||
+      !launch_q8_cols(dH, cap, 2 * I, 1, off, E, P, ws + L.dHt, ws + L.dHts, s) ||
+      !launch_q8_cols(W1, 2 * I, H, E, nullptr, 0, 2 * I, ws + L.w1t, ws + L.w1ts, s) ||
+      !launch_q8_cols(xp, cap, H, 1, off, E, P, ws + L.xpt, ws + L.xpts, s))
+    return W4A4_ERR_LAUNCH;
+  if (cap > 0 && !launch_mx8_dgrad(cap, 2 * I, H, E, off, ws + L.dHq, ws + L.dHqs, ws + L.w1t, ws + L.w1ts, dXp,
+                                   "mx8_dgrad_fc1", s))
+    return W4A4_ERR_LAUNCH;
+  if (!launch_mx8_wgrad(2 * I, H, E, off, ws + L.dHt, ws + L.dHts, ws + L.xpt, ws + L.xpts, P,
+                        static_cast<uint16_t*>(dw1), "mx8_wgrad_fc1", s))
+    return W4A4_ERR_LAUNCH;
+  if (!launch_gather_sum(T, H, k, dXp, row_map, static_cast<uint16_t*>(dx), s)) return W4A4_ERR_LAUNCH;
   return W4A4_OK;
 }
 

@@ -624,6 +624,231 @@ bool launch_fwd_mx(const FwdArgs& args, int n_tiles, const char* name, hipStream
   return launch_ok(name);
 }
 
+// ---------------------------------------------------- MXFP8 backward GEMMs
+// C = A B^T with MXFP8 operands (E4M3 bytes, one E8M0 scale per 32 along K,
+// both operands K-contiguous) on the scaled FP8 MFMA (32x32x64), bf16 out.
+//   dgrad (WGRAD = false): A rows grouped by expert (offsets), B = the
+//     expert's [N, K] slab; the reduction runs over K.
+//   wgrad (WGRAD = true): per expert e, A [M1, pitch] and B [N, pitch] are
+//     transposed operands whose columns are dispatched rows; the reduction
+//     runs over the expert's rows [offsets[e], offsets[e+1]) (a multiple of
+//     128: row_align 128), out = dW[e] [M1, N]; an empty expert writes zeros.
+// Lane layout of the FP8 operand (checked on the box with one-hot inputs):
+// lane l holds row l % 32; its 32 bytes are K [16 h, 16 h + 16) and
+// [32 + 16 h, 32 + 16 h + 16) for h = l / 32, bytes 0-15 scaled by lane half
+// 0's scale byte of the row and 16-31 by lane half 1's; so lane half h
+// supplies the scale of 32-block h.  A stage covers 64 of K (64 B per row,
+// the four 16-byte chunks swizzled as in the MXFP4 kernel); the scales of two
+// stages (one dword per row) arrive with every other stage in one of two
+// buffers.  Three-stage ring, 77.5 KB: two workgroups per CU.
+constexpr int kM8BK = 64;
+constexpr int kM8Stages = 3;
+constexpr int kM8Ahead = kM8Stages - 1;
+constexpr int kM8Row = kM8BK;                                  // 64 B of codes per row per stage
+constexpr int kM8A = kBM * kM8Row;                             // 8 KB
+constexpr int kM8Stage = kM8A + kBN * kM8Row;                  // 24 KB
+constexpr int kM8ScaleBuf = kM8Stages * kM8Stage;              // two buffers of 512 rows x 4 B
+constexpr int kM8Gx = kM8ScaleBuf + 2 * kScaleRows * 4;
+constexpr int kM8Slot = kM8Gx + kBM * 4;
+constexpr int kM8LdsBytes = kM8Slot + 16;
+static_assert(2 * kM8LdsBytes <= 160 * 1024, "two workgroups per CU must fit in LDS");
+static_assert(kOutRows * kOutPitch <= kM8Stages * kM8Stage, "staging fits in the ring");
+
+struct Mx8Args {
+  int64_t rows_alloc;       // dgrad: rows of A
+  int K;                    // dgrad: reduction length
+  int N;                    // columns of C (rows of B)
+  int M1;                   // wgrad: rows of C (rows of A)
+  int E;
+  const int32_t* offsets;
+  const uint8_t* a;         // codes
+  const uint8_t* as;        // scales
+  const uint8_t* b;
+  const uint8_t* bs;
+  int64_t pitch;            // wgrad: bytes per row of A and B (a multiple of 128)
+  uint16_t* out;
+};
+
+template <bool WGRAD>
+__global__ void __launch_bounds__(kThreads, 2)
+mx8_gemm_kernel(Mx8Args args) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int r32 = lane & 31, hl = lane >> 5;
+  const int n_tiles = args.N / kBN;
+
+  TileCoord tc;
+  int64_t kofs = 0;        // wgrad: first K column (the expert's first row)
+  int kext;                // reduction length of this tile
+  const uint8_t* a_base;
+  const uint8_t* b_base;
+  const uint8_t* as_base;
+  const uint8_t* bs_base;
+  int64_t a_pitch, b_pitch;
+  int a_rows;
+  uint16_t* out = args.out;
+  if constexpr (!WGRAD) {
+    tc = grouped_m_tile<kBM>(args.offsets, args.E, n_tiles, reinterpret_cast<int*>(lds + kM8Slot));
+    if (!tc.valid) return;
+    kext = args.K;
+    a_pitch = b_pitch = args.K;
+    a_rows = static_cast<int>(min<int64_t>(kBM, args.rows_alloc - tc.m0));
+    a_base = args.a + tc.m0 * a_pitch;
+    as_base = args.as + tc.m0 * (a_pitch / 32);
+    b_base = args.b + static_cast<int64_t>(tc.e) * args.N * b_pitch;
+    bs_base = args.bs + static_cast<int64_t>(tc.e) * args.N * (b_pitch / 32);
+  } else {
+    // expert-major tiles, dealt in contiguous runs per XCD
+    const int m_tiles = args.M1 / kBM;
+    const int64_t total = static_cast<int64_t>(args.E) * m_tiles * n_tiles;
+    const int64_t per_xcd = (total + kXcds - 1) / kXcds;
+    const int64_t bid = blockIdx.x;
+    const int64_t L = (bid % kXcds) * per_xcd + bid / kXcds;
+    if (bid / kXcds >= per_xcd || L >= total) return;
+    const int e = static_cast<int>(L / (m_tiles * n_tiles));
+    const int rem = static_cast<int>(L % (m_tiles * n_tiles));
+    tc.e = e;
+    tc.m0 = static_cast<int64_t>(rem / n_tiles) * kBM;
+    tc.m_end = args.M1;
+    tc.n_tile = rem % n_tiles;
+    tc.valid = true;
+    kofs = args.offsets[e];
+    kext = args.offsets[e + 1] - static_cast<int>(kofs);
+    a_pitch = b_pitch = args.pitch;
+    a_rows = kBM;
+    a_base = args.a + tc.m0 * a_pitch + kofs;
+    as_base = args.as + tc.m0 * (a_pitch / 32) + kofs / 32;
+    b_base = args.b + kofs;
+    bs_base = args.bs + kofs / 32;
+    out += static_cast<int64_t>(e) * args.M1 * args.N;
+  }
+
+  // code copies: copy q of this wave fills 16 staged rows (1 KB), lane i row
+  // 16 q' + i / 4 at slot i % 4 (A: q' = 2 wave + q; B: q' = 4 wave + q)
+  uint32_t a_off[2], b_off[4];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int row = 16 * (2 * wave + q) + (lane >> 2);
+    a_off[q] = static_cast<uint32_t>(min(row, a_rows - 1) * a_pitch + mx_code_slot(row, lane & 3) * 16);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = 16 * (4 * wave + q) + (lane >> 2);
+    b_off[q] = static_cast<uint32_t>(b_row_of<FwdMode::FC2>(row, tc.n_tile, 0) * b_pitch +
+                                     mx_code_slot(row, lane & 3) * 16);
+  }
+  // scale copies: one dword (two stages' blocks) per staged row
+  const uint8_t* scale_src[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int q = 128 * wave + 64 * c + lane;
+    if (q < kBScaleRow0)
+      scale_src[c] = as_base + static_cast<int64_t>(min(q, a_rows - 1)) * (a_pitch / 32);
+    else if (q < kBScaleRow0 + kBN)
+      scale_src[c] = bs_base + static_cast<int64_t>(b_row_of<FwdMode::FC2>(q - kBScaleRow0, tc.n_tile, 0)) *
+                                   (b_pitch / 32);
+    else
+      scale_src[c] = as_base;                                  // filler: a valid row, never read
+  }
+  // The copies' global offsets are 32-bit: bound checked by the host.
+  const uint32_t lds0 = lds_addr(lds);
+  auto issue = [&](int kt) {
+    if (kt % 2 == 0) {   // the pair's scales go out first: they land before the stage's codes
+      const uint32_t sb = lds0 + kM8ScaleBuf + ((kt / 2) % 2) * (kScaleRows * 4);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) dma4(scale_src[c] + (kt / 2) * 4, sb + (2 * wave + c) * 256);
+    }
+    const uint32_t st = lds0 + (kt % kM8Stages) * kM8Stage;
+    const int cb = kt * kM8Row;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) dma16_off(a_base + cb, a_off[q], st + (2 * wave + q) * 1024);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dma16_off(b_base + cb, b_off[q], st + kM8A + (4 * wave + q) * 1024);
+  };
+
+  floatx16_t acc[2][4];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
+
+  const int a_row0 = wm * kWM + r32, b_row0 = wn * kWN + r32;
+  const int sw = (r32 >> 2) & 3;
+  const uint32_t a_lane0 = a_row0 * kM8Row + (hl ^ sw) * 16, a_lane1 = a_row0 * kM8Row + ((2 + hl) ^ sw) * 16;
+  const uint32_t b_lane0 = kM8A + b_row0 * kM8Row + (hl ^ sw) * 16;
+  const uint32_t b_lane1 = kM8A + b_row0 * kM8Row + ((2 + hl) ^ sw) * 16;
+  const uint32_t a_scale_lane = a_row0 * 4, b_scale_lane = (kBScaleRow0 + b_row0) * 4;
+  const int nk = kext / kM8BK;
+  for (int s0 = 0; s0 < kM8Ahead && s0 < nk; ++s0) issue(s0);
+
+  const bool rows_live = tc.m0 + wm * kWM < tc.m_end;
+  for (int kt = 0; kt < nk; ++kt) {
+    // stage kt (and its pair's scales) has landed in every wave: at most the
+    // copies of stage kt + 1, if issued, are pending
+    if (kt + 1 < nk) {
+      if ((kt + 1) % 2 == 0) wait_vm_barrier<8>();
+      else wait_vm_barrier<6>();
+    } else {
+      wait_vm_barrier<0>();
+    }
+    if (kt + kM8Ahead < nk) issue(kt + kM8Ahead);
+    if (!rows_live) continue;
+    const uint32_t st = opaque_sgpr(lds0 + (kt % kM8Stages) * kM8Stage);
+    const uint32_t sb = opaque_sgpr(lds0 + kM8ScaleBuf + ((kt / 2) % 2) * (kScaleRows * 4));
+    const int sh = 8 * (2 * (kt % 2) + hl);   // this lane's block among the dword's four
+    int sa[2], sbv[4];
+    i32x8_t av[2], bv[4];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      const u32x4_t lo = *lds_ptr<u32x4_t>(st + a_lane0 + f * 32 * kM8Row);
+      const u32x4_t hi = *lds_ptr<u32x4_t>(st + a_lane1 + f * 32 * kM8Row);
+      av[f] = i32x8_t{static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]),
+                      static_cast<int>(lo[3]), static_cast<int>(hi[0]), static_cast<int>(hi[1]),
+                      static_cast<int>(hi[2]), static_cast<int>(hi[3])};
+      sa[f] = static_cast<int>((*lds_ptr<uint32_t>(sb + a_scale_lane + f * 32 * 4) >> sh) & 0xFFu);
+    }
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const u32x4_t lo = *lds_ptr<u32x4_t>(st + b_lane0 + f * 32 * kM8Row);
+      const u32x4_t hi = *lds_ptr<u32x4_t>(st + b_lane1 + f * 32 * kM8Row);
+      bv[f] = i32x8_t{static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]),
+                      static_cast<int>(lo[3]), static_cast<int>(hi[0]), static_cast<int>(hi[1]),
+                      static_cast<int>(hi[2]), static_cast<int>(hi[3])};
+      sbv[f] = static_cast<int>((*lds_ptr<uint32_t>(sb + b_scale_lane + f * 32 * 4) >> sh) & 0xFFu);
+    }
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+        // formats 0 = FP8 E4M3 for both operands; scale bytes in bits 7:0
+        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[mi], bv[ni], acc[mi][ni], 0, 0, 0,
+                                                                      sa[mi], 0, sbv[ni]);
+  }
+  float* s_gx = reinterpret_cast<float*>(lds + kM8Gx);
+  if (tid < kBM) s_gx[tid] = 1.0f;
+  __syncthreads();   // s_gx visible; every wave is past its last read of the ring
+  const float gw[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+  FwdArgs fa{};
+  fa.N = args.N;
+  fa.out = out;
+  fwd_epilogue<FwdMode::FC2>(fa, acc, tc, s_gx, gw, lds);
+}
+
+template <bool WGRAD>
+bool launch_mx8(const Mx8Args& args, int64_t tiles, const char* name, hipStream_t s) {
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&mx8_gemm_kernel<WGRAD>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, kM8LdsBytes);
+  if (attr != hipSuccess) return launch_ok(name) && false;
+  if (tiles == 0) return true;
+  launch_kernel(name, mx8_gemm_kernel<WGRAD>, dim3(xcd_grid(tiles)), dim3(kThreads), kM8LdsBytes, s, args);
+  return launch_ok(name);
+}
+
 template <FwdMode MODE, bool GS>
 bool launch_fwd_variant(const FwdArgs& args, int64_t tiles, const char* name, hipStream_t s) {
   static const hipError_t attr = hipFuncSetAttribute(
@@ -675,6 +900,26 @@ bool launch_fc2_mx(int64_t rows_alloc, int H, int I, int E, const int32_t* offse
   if (I % kMxBK) return false;
   FwdArgs args{rows_alloc, I, H, I, E, offsets, a, w2, o_out, nullptr, nullptr};
   return launch_fwd_mx<FwdMode::FC2>(args, H / kBN, "mx_gemm_fc2", s);
+}
+
+bool launch_mx8_dgrad(int64_t rows_alloc, int K, int N, int E, const int32_t* offsets, const uint8_t* a,
+                      const uint8_t* as, const uint8_t* b, const uint8_t* bs, uint16_t* out, const char* name,
+                      hipStream_t s) {
+  if (K % 128 || N % kBN) return false;
+  if (static_cast<int64_t>(kBM) * K > (int64_t{1} << 31) || static_cast<int64_t>(N) * K > (int64_t{1} << 31))
+    return false;   // 32-bit per-lane copy offsets
+  Mx8Args args{rows_alloc, K, N, 0, E, offsets, a, as, b, bs, 0, out};
+  return launch_mx8<false>(args, grouped_m_tiles_bound(rows_alloc, E, kBM) * (N / kBN), name, s);
+}
+
+bool launch_mx8_wgrad(int M1, int N, int E, const int32_t* offsets, const uint8_t* a, const uint8_t* as,
+                      const uint8_t* b, const uint8_t* bs, int64_t pitch, uint16_t* out, const char* name,
+                      hipStream_t s) {
+  if (M1 % kBM || N % kBN || pitch % 128) return false;
+  if (static_cast<int64_t>(N) * pitch > (int64_t{1} << 31) || static_cast<int64_t>(kBM) * pitch > (int64_t{1} << 31))
+    return false;   // 32-bit per-lane copy offsets
+  Mx8Args args{0, 0, N, M1, E, offsets, a, as, b, bs, pitch, out};
+  return launch_mx8<true>(args, static_cast<int64_t>(E) * (M1 / kBM) * (N / kBN), name, s);
 }
 
 }  // namespace w4a4

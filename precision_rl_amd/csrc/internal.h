@@ -93,6 +93,28 @@ bool launch_fc1_mx(int64_t rows_alloc, int H, int I, int E, const int32_t* offse
 bool launch_fc2_mx(int64_t rows_alloc, int H, int I, int E, const int32_t* offsets, Fp4Operand a,
                    Fp4Operand w2, uint16_t* o_out, hipStream_t s);
 
+// MXFP8 backward pieces.  Quantisers (E4M3 + E8M0 per 32): along rows of a
+// [rows, K] bf16 matrix (rows [0, offsets[E]) when offsets is given) into
+// q [rows, K], s [rows, K/32]; along columns of `batch` [R, C] matrices into
+// q [batch][C, pitch], s [batch][C, pitch/32] (row blocks [0, offsets[E])
+// when given; C % 256 == 0, pitch % 16 == 0).
+bool launch_q8_rows(const uint16_t* x, int64_t rows, int K, const int32_t* offsets, int E, uint8_t* q,
+                    uint8_t* s, hipStream_t st);
+bool launch_q8_cols(const uint16_t* x, int64_t R, int C, int batch, const int32_t* offsets, int E,
+                    int64_t pitch, uint8_t* q, uint8_t* s, hipStream_t st);
+// dH = SwiGLU backward of dA [rows, I] on the saved h [rows, 2I], rows [0, offsets[E]).
+bool launch_swiglu_bwd(const uint16_t* dA, const uint16_t* h, int64_t rows, int I, const int32_t* offsets, int E,
+                       uint16_t* dH, hipStream_t st);
+// C = A B^T on the scaled FP8 MFMA, bf16 out.  dgrad: A [rows_alloc, K] grouped
+// by offsets, B [E][N, K]; wgrad: per expert, A [M1, pitch] and B [N, pitch]
+// over the columns [offsets[e], offsets[e+1]) (multiples of 128), out [E][M1, N].
+bool launch_mx8_dgrad(int64_t rows_alloc, int K, int N, int E, const int32_t* offsets, const uint8_t* a,
+                      const uint8_t* as, const uint8_t* b, const uint8_t* bs, uint16_t* out, const char* name,
+                      hipStream_t s);
+bool launch_mx8_wgrad(int M1, int N, int E, const int32_t* offsets, const uint8_t* a, const uint8_t* as,
+                      const uint8_t* b, const uint8_t* bs, int64_t pitch, uint16_t* out, const char* name,
+                      hipStream_t s);
+
 // Dense linear layer y = x W^T (one group of T rows; offsets = {0, T}).
 bool launch_linear_fwd(int64_t T, int K, int N, const int32_t* offsets, Fp4Operand x, Fp4Operand w,
                        uint16_t* y, hipStream_t s);

@@ -132,3 +132,20 @@ def test_mx_calls_reject_invalid_arguments_before_launch():
     assert mfwd(I=96) == -2
     assert mfwd(ws=None) == -3
     assert mfwd(dc=p) == -1                            # debug codes without debug scales
+
+
+def test_mx8_backward_rejects_invalid_arguments_before_launch():
+    lib = _lib()
+    buf = ctypes.create_string_buffer(4096)
+    p = ctypes.c_void_p(ctypes.addressof(buf) + (-ctypes.addressof(buf)) % 16)
+
+    def bwd(H=256, I=256, T=4, A=128, ws=p, wsb=1 << 40):
+        return lib.w4a4_mx8_expert_bwd(T, H, I, 8, 2, A, p, p, p, p, p, p, p, p, p, p, p, p, p,
+                                       ws, wsb, None)
+
+    assert bwd(A=16) == -2                             # row blocks of 32 per expert: row_align 128
+    assert bwd(I=128) == -2                            # I % 256
+    assert bwd(ws=None) == -3
+    assert bwd(wsb=16) == -3
+    assert bwd(H=250) == -1
+    assert lib.w4a4_workspace_size(5, 64, 256, 256, 8, 2, 128) > lib.w4a4_workspace_size(2, 64, 256, 256, 8, 2, 128)
