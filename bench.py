@@ -31,7 +31,10 @@ WORKLOAD = "learner"
 PEAK_MFMA_TFLOPS = 2500.0      # MI355X dense f16 / bf16 MFMA
 PEAK_MFMA_FP4_TFLOPS = 10100.0  # MI355X dense MXFP4 (scaled FP4) MFMA
 # kernels whose MFMA peak is not the f16 / bf16 one
-KERNEL_PEAK = {"mx_gemm_fc1": PEAK_MFMA_FP4_TFLOPS, "mx_gemm_fc2": PEAK_MFMA_FP4_TFLOPS}
+PEAK_MFMA_FP8_TFLOPS = 5000.0   # MI355X dense FP8 (scaled FP8) MFMA
+KERNEL_PEAK = {"mx_gemm_fc1": PEAK_MFMA_FP4_TFLOPS, "mx_gemm_fc2": PEAK_MFMA_FP4_TFLOPS,
+               "mx8_dgrad_fc2": PEAK_MFMA_FP8_TFLOPS, "mx8_wgrad_fc2": PEAK_MFMA_FP8_TFLOPS,
+               "mx8_dgrad_fc1": PEAK_MFMA_FP8_TFLOPS, "mx8_wgrad_fc1": PEAK_MFMA_FP8_TFLOPS}
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 # kernel name -> source file whose content decides whether stored counters still apply
@@ -46,7 +49,12 @@ KERNEL_SOURCES = {
     "gemm_linear_wgrad": "gemm_bwd.hip",
     "mx_gemm_fc1": "gemm_fwd.hip", "mx_gemm_fc2": "gemm_fwd.hip",
     "mx_quantize_scatter": "quantize.hip", "mx_requant": "quantize.hip",
+    "mx8_dgrad_fc2": "gemm_fwd.hip", "mx8_wgrad_fc2": "gemm_fwd.hip",
+    "mx8_dgrad_fc1": "gemm_fwd.hip", "mx8_wgrad_fc1": "gemm_fwd.hip",
+    "swiglu_bwd": "mx8.hip",
 }
+for _n in ("rows_dO", "rows_dH", "cols_dO", "cols_a", "cols_w2", "cols_dH", "cols_w1", "cols_xp"):
+    KERNEL_SOURCES["mx8_quant_" + _n] = "mx8.hip"
 
 
 def algorithmic_work(T, H, E, k, I):
@@ -77,6 +85,16 @@ def algorithmic_work(T, H, E, k, I):
     }
     fl["mx_gemm_fc1"] = fl["gemm_fc1"]
     fl["mx_gemm_fc2"] = fl["gemm_fc2"]
+    for n in ("dgrad_fc2", "wgrad_fc2", "dgrad_fc1", "wgrad_fc1"):
+        fl["mx8_" + n] = fl["gemm_" + n]
+    # SwiGLU backward: read dA and h, write dH
+    by["swiglu_bwd"] = M * (I * 2 + 2 * I * 2 + 2 * I * 2)
+    # MXFP8 quantisers: read bf16, write one E4M3 byte per element and one E8M0 byte per 32
+    q8 = lambda n: n * (2 + 1) + n // 32
+    by.update({"mx8_quant_rows_dO": q8(M * H), "mx8_quant_rows_dH": q8(M * 2 * I),
+               "mx8_quant_cols_dO": q8(M * H), "mx8_quant_cols_a": q8(M * I),
+               "mx8_quant_cols_dH": q8(M * 2 * I), "mx8_quant_cols_xp": q8(M * H),
+               "mx8_quant_cols_w2": q8(E * H * I), "mx8_quant_cols_w1": q8(E * 2 * I * H)})
     return fl, by
 
 
@@ -294,7 +312,7 @@ def main_qp(args):
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(d, w, tokens=512, experts=8, recipe="nvfp4"):
+def cpu_baseline(d, w, tokens=512, experts=8, recipe="nvfp4", bwd="bf16"):
     """The FP64 oracle on a bounded sample of the learner workload: the first
     `tokens` tokens, each routed to all `experts` experts (k = 8 per token as
     in the workload, so the per-token work is the same), expert weights
@@ -320,12 +338,13 @@ def cpu_baseline(d, w, tokens=512, experts=8, recipe="nvfp4"):
     t0 = time.perf_counter()
     f = (moe.forward_mx if mx else moe.forward)(x, idx, p, w1q, w2q, experts)
     xq = f["xq"]
-    moe.backward(dy, x, w1, w2, f["h"], f["a"], p, xq["offsets"], xq["row_map"], xq["src_row"])
+    (moe.backward_mx8 if bwd == "mxfp8" else moe.backward)(
+        dy, x, w1, w2, f["h"], f["a"], p, xq["offsets"], xq["row_map"], xq["src_row"])
     dt = time.perf_counter() - t0
     return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{tokens} tokens of the learner workload (H={w.H}, I={w.I}, k={k}) routed "
                       f"to {experts} experts, FP64 numpy, quantize+permute+forward+backward"
-                      f"{' (MXFP4 recipe)' if mx else ''}, "
+                      f"{' (MXFP4 recipe)' if mx else ''}{' (MXFP8 backward)' if bwd == 'mxfp8' else ''}, "
                       f"{dt:.1f} s", "seconds": dt,
             "host_cpus": len(os.sched_getaffinity(0))}
 
@@ -386,10 +405,12 @@ def summarize(kern, ms, steps, fl, by, concurrent=None):
     # the dominant kernel is taken among those that own the GPU while they run:
     # a second-stream kernel's duration includes the time it shares with the
     # kernel beside it, so it states no rate of its own
-    alone = [n for n in kern if n not in concurrent] or list(kern)
+    alone = [n for n in kern if n not in concurrent and (n in fl or n in by)] or list(kern)
     dom = max(alone, key=lambda n: kern[n]["total_ms"])
     dom_avg_s = kern[dom]["total_ms"] / kern[dom]["count"] * 1e-3
-    if dom in fl:
+    if dom not in fl and dom not in by:
+        roof = {"bound": None, "achieved": None, "peak": None, "unit": None, "frac": None}
+    elif dom in fl:
         ach = fl[dom] / dom_avg_s / 1e12
         peak = KERNEL_PEAK.get(dom, PEAK_MFMA_TFLOPS)
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak,
@@ -417,6 +438,10 @@ def main():
                          "qp: quantize+permute alone")
     ap.add_argument("--outer", choices=["token", "tensor"], default="token",
                     help="qp: outer-scale domain of the activations")
+    ap.add_argument("--bwd", choices=["bf16", "mxfp8"], default="bf16",
+                    help="learner: the straight-through backward's GEMM operands -- bf16 (the "
+                         "default) or mxfp8 (E4M3 + E8M0 per 32 along each GEMM's reduction axis, "
+                         "scaled FP8 MFMA; routes with row_align 128)")
     ap.add_argument("--recipe", choices=["nvfp4", "mxfp4"], default="nvfp4",
                     help="learner: the forward's format -- nvfp4 (E4M3 per 16 + FP32 outer "
                          "scales, exact f16 decode, the default) or mxfp4 (E8M0 per 32, scaled "
@@ -437,7 +462,8 @@ def main():
     from precision_rl_amd import binding as b, synth
 
     w = synth.WORKLOADS[WORKLOAD]
-    T, H, E, k, I, A = w.T, w.H, w.E, w.k, w.I, 1
+    mx8 = args.bwd == "mxfp8"
+    T, H, E, k, I, A = w.T, w.H, w.E, w.k, w.I, (128 if mx8 else 1)
     d = synth.workload_inputs(WORKLOAD)
     dev = torch.device("cuda:0")
 
@@ -464,7 +490,8 @@ def main():
     ws_qp = torch.empty(b.workspace_size(b.WS_QUANTIZE_PERMUTE, T, H, I, E, k, A) + 256,
                         dtype=torch.uint8, device=dev)
     ws_f = torch.empty(b.workspace_size(b.WS_FORWARD, T, H, I, E, k, A), dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(b.workspace_size(b.WS_BACKWARD, T, H, I, E, k, A), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(b.workspace_size(b.WS_MX8_BACKWARD if mx8 else b.WS_BACKWARD, T, H, I, E, k, A),
+                       dtype=torch.uint8, device=dev)
     y = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
     saved = dict(h=torch.empty(cap, 2 * I, dtype=torch.bfloat16, device=dev),
                  a=torch.empty(cap, I, dtype=torch.bfloat16, device=dev))
@@ -483,15 +510,16 @@ def main():
             b.w4a4_quantize_permute(x, idx, E, A, out=xq, workspace=ws_qp)
             b.w4a4_grouped_expert_fwd(xq, p, w1q, w2q, T, H, I, E, k, A, save=True, y=y,
                                       workspace=ws_f, saved=saved)
-        b.w4a4_expert_bwd(dy, x, w1, w2, saved["h"], saved["a"], p, xq, T, H, I, E, k, A,
-                          out=grads, workspace=ws_b)
+        bwd = b.w4a4_mx8_expert_bwd if mx8 else b.w4a4_expert_bwd
+        bwd(dy, x, w1, w2, saved["h"], saved["a"], p, xq, T, H, I, E, k, A, out=grads, workspace=ws_b)
 
     ms, kern = time_steps(b, torch, step, args)
     fl, by = algorithmic_work(T, H, E, k, I)
-    per_kernel, roof = summarize(kern, ms, args.steps, fl, by)
+    # the MXFP8 backward runs on the caller's stream alone
+    per_kernel, roof = summarize(kern, ms, args.steps, fl, by, concurrent={} if mx8 else None)
 
     gemm_ms = sum(kern[n]["total_ms"] for n in kern if n in fl) / args.steps
-    total_flop = sum(v for n, v in fl.items() if not n.startswith("mx_"))
+    total_flop = sum(v for n, v in fl.items() if n.startswith("gemm_"))
     out = {
         "metric": METRIC,
         "value": round(T / (ms * 1e-3), 1),
@@ -504,9 +532,10 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": ("mxfp4 scaled-FP4 MFMA fwd" if mx else "nvfp4->f16 MFMA fwd")
-                 + ", bf16 MFMA bwd, fp32 accumulate",
+                 + (", mxfp8 scaled-FP8 MFMA bwd" if mx8 else ", bf16 MFMA bwd") + ", fp32 accumulate",
         "data": "synthetic (seeded; random-init weights of the layer's shape)",
-        "config": {"workload": f"{WORKLOAD}: quantize+permute + grouped expert fwd + BF16 STE bwd"
+        "config": {"workload": f"{WORKLOAD}: quantize+permute + grouped expert fwd + "
+                               + ("MXFP8" if mx8 else "BF16") + " STE bwd"
                                + (" (MXFP4 recipe: E2M1 + E8M0 per 32)" if mx else ""),
                    "T": T, "H": H, "E": E, "top_k": k, "I": I, "row_align": A,
                    "routing": w.routing},
@@ -517,7 +546,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the FP64 oracle on the host", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(d, w, tokens=args.cpu_tokens, recipe=args.recipe)
+        out["cpu_baseline"] = cpu_baseline(d, w, tokens=args.cpu_tokens, recipe=args.recipe, bwd=args.bwd)
     print(json.dumps(out), flush=True)
 
 

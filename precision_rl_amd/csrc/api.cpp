@@ -640,10 +640,10 @@ w4a4_status w4a4_mx8_expert_bwd(int64_t T, int H, int I, int E, int k, int row_a
       !launch_zero_pad_rows(cap, H, src_row, off, E, xp, s))
     return W4A4_ERR_LAUNCH;
   // FC2: dA = Q_H(dO) Q_H(W2[e]);  dW2[e] = Q_r(dO_e)^T Q_r(a_e)
-  if (!launch_q8_rows(dO, cap, H, off, E, ws + L.dOq, ws + L.dOqs, s) ||
-      !launch_q8_cols(dO, cap, H, 1, off, E, P, ws + L.dOt, ws + L.dOts, s) ||
-      !launch_q8_cols(a, cap, I, 1, off, E, P, ws + L.at, ws + L.ats, s) ||
-      !launch_q8_cols(W2, H, I, E, nullptr, 0, H, ws + L.w2t, ws + L.w2ts, s))
+  if (!launch_q8_rows(dO, cap, H, off, E, ws + L.dOq, ws + L.dOqs, "mx8_quant_rows_dO", s) ||
+      !launch_q8_cols(dO, cap, H, 1, off, E, P, ws + L.dOt, ws + L.dOts, "mx8_quant_cols_dO", s) ||
+      !launch_q8_cols(a, cap, I, 1, off, E, P, ws + L.at, ws + L.ats, "mx8_quant_cols_a", s) ||
+      !launch_q8_cols(W2, H, I, E, nullptr, 0, H, ws + L.w2t, ws + L.w2ts, "mx8_quant_cols_w2", s))
     return W4A4_ERR_LAUNCH;
   if (cap > 0 && !launch_mx8_dgrad(cap, H, I, E, off, ws + L.dOq, ws + L.dOqs, ws + L.w2t, ws + L.w2ts, dA,
                                    "mx8_dgrad_fc2", s))
@@ -653,10 +653,10 @@ w4a4_status w4a4_mx8_expert_bwd(int64_t T, int H, int I, int E, int k, int row_a
     return W4A4_ERR_LAUNCH;
   if (!launch_swiglu_bwd(dA, h, cap, I, off, E, dH, s)) return W4A4_ERR_LAUNCH;
   // FC1: dXp = Q_2I(dH) Q_2I(W1[e]);  dW1[e] = Q_r(dH_e)^T Q_r(xp_e)
-  if (!launch_q8_rows(dH, cap, 2 * I, off, E, ws + L.dHq, ws + L.dHqs, s) ||
-      !launch_q8_cols(dH, cap, 2 * I, 1, off, E, P, ws + L.dHt, ws + L.dHts, s) ||
-      !launch_q8_cols(W1, 2 * I, H, E, nullptr, 0, 2 * I, ws + L.w1t, ws + L.w1ts, s) ||
-      !launch_q8_cols(xp, cap, H, 1, off, E, P, ws + L.xpt, ws + L.xpts, s))
+  if (!launch_q8_rows(dH, cap, 2 * I, off, E, ws + L.dHq, ws + L.dHqs, "mx8_quant_rows_dH", s) ||
+      !launch_q8_cols(dH, cap, 2 * I, 1, off, E, P, ws + L.dHt, ws + L.dHts, "mx8_quant_cols_dH", s) ||
+      !launch_q8_cols(W1, 2 * I, H, E, nullptr, 0, 2 * I, ws + L.w1t, ws + L.w1ts, "mx8_quant_cols_w1", s) ||
+      !launch_q8_cols(xp, cap, H, 1, off, E, P, ws + L.xpt, ws + L.xpts, "mx8_quant_cols_xp", s))
     return W4A4_ERR_LAUNCH;
   if (cap > 0 && !launch_mx8_dgrad(cap, 2 * I, H, E, off, ws + L.dHq, ws + L.dHqs, ws + L.w1t, ws + L.w1ts, dXp,
                                    "mx8_dgrad_fc1", s))

@@ -97,11 +97,11 @@ bool launch_fc2_mx(int64_t rows_alloc, int H, int I, int E, const int32_t* offse
 // [rows, K] bf16 matrix (rows [0, offsets[E]) when offsets is given) into
 // q [rows, K], s [rows, K/32]; along columns of `batch` [R, C] matrices into
 // q [batch][C, pitch], s [batch][C, pitch/32] (row blocks [0, offsets[E])
-// when given; C % 256 == 0, pitch % 16 == 0).
+// when given, in whole tiles of 128 rows; C % 64 == 0, pitch % 128 == 0).
 bool launch_q8_rows(const uint16_t* x, int64_t rows, int K, const int32_t* offsets, int E, uint8_t* q,
-                    uint8_t* s, hipStream_t st);
+                    uint8_t* s, const char* name, hipStream_t st);
 bool launch_q8_cols(const uint16_t* x, int64_t R, int C, int batch, const int32_t* offsets, int E,
-                    int64_t pitch, uint8_t* q, uint8_t* s, hipStream_t st);
+                    int64_t pitch, uint8_t* q, uint8_t* s, const char* name, hipStream_t st);
 // dH = SwiGLU backward of dA [rows, I] on the saved h [rows, 2I], rows [0, offsets[E]).
 bool launch_swiglu_bwd(const uint16_t* dA, const uint16_t* h, int64_t rows, int I, const int32_t* offsets, int E,
                        uint16_t* dH, hipStream_t st);

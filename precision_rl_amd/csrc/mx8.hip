@@ -96,42 +96,41 @@ q8_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int K, const int32_
 // ---------------------------------------------------------- along columns
 // x: `batch` matrices [R, C] bf16 (batch stride R*C).  Output per matrix:
 // q [C, pitch] E4M3 (row c holds column c of x, quantised in blocks of 32
-// consecutive rows), s [C, pitch/32].  A workgroup takes 32 rows x 256
-// columns through LDS; thread c encodes column c's block.  Row blocks at or
-// past offsets[E] (when given) are skipped.  R % 32 == 0 is not required of
-// the allocation, only of the rows encoded (row_align multiple of 32 for
-// dispatched rows).
-constexpr int kColTile = 256;
+// consecutive rows), s [C, pitch/32].  A workgroup takes 128 rows x 64
+// columns through LDS (each input row segment is one 128-byte line); four
+// consecutive threads encode the four 32-row blocks of one column, so that
+// together they write the column's 128 output bytes as one line.  Row tiles
+// at or past offsets[E] (when given) are skipped: the rows encoded must come
+// in whole tiles of 128 (row_align 128 for dispatched rows; R % 128 == 0
+// for weights).
+constexpr int kColTileRows = 128, kColTileCols = 64;
+constexpr int kColPitch = kColTileCols + 2;   // elements; 2-way LDS conflicts at most on the column reads
 __global__ void __launch_bounds__(kQ8Threads)
 q8_cols_kernel(const uint16_t* __restrict__ x, int64_t R, int C, const int32_t* __restrict__ offsets, int E,
                int64_t pitch, uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
-  __shared__ uint16_t tile[32][kColTile + 2];
-  const int64_t rb = blockIdx.x;             // block of 32 rows
-  const int ct = blockIdx.y;                 // tile of 256 columns
+  __shared__ uint16_t tile[kColTileRows * kColPitch];
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kColTileRows;
+  const int c0 = blockIdx.y * kColTileCols;
   const int mat = blockIdx.z;
-  const int64_t r0 = rb * 32;
   const int64_t rlim = offsets != nullptr ? min<int64_t>(R, offsets[E]) : R;
   if (r0 >= rlim) return;
   const uint16_t* xm = x + static_cast<int64_t>(mat) * R * C;
-  const int c0 = ct * kColTile;
   const int t = threadIdx.x;
-  // load: thread t moves 16 bytes of each of 4 rows (row t / 32 + 8 i, chunk t % 32)
+  // load: thread t moves the 16-byte chunk t % 8 of rows t / 8 + 32 i
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int lr = t / 32 + 8 * i, ch = t % 32;
-    const int64_t r = min(r0 + lr, R - 1);
-    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(xm + r * C + c0 + ch * 8));
+    const int lr = t / 8 + 32 * i, ch = t % 8;
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(xm + (r0 + lr) * C + c0 + ch * 8));
+    uint32_t* dst = reinterpret_cast<uint32_t*>(tile + lr * kColPitch + ch * 8);
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      tile[lr][ch * 8 + 2 * d] = static_cast<uint16_t>(v[d]);
-      tile[lr][ch * 8 + 2 * d + 1] = static_cast<uint16_t>(v[d] >> 16);
-    }
+    for (int d = 0; d < 4; ++d) dst[d] = v[d];
   }
   __syncthreads();
-  const int c = t;
+  const int c = t / 4, blk = t % 4;
+  const uint16_t* col = tile + (32 * blk) * kColPitch + c;
   uint32_t amax = 0;
 #pragma unroll
-  for (int r = 0; r < 32; ++r) amax = max(amax, static_cast<uint32_t>(tile[r][c] & 0x7FFFu));
+  for (int r = 0; r < 32; ++r) amax = max(amax, static_cast<uint32_t>(col[r * kColPitch] & 0x7FFFu));
   const uint32_t byte = mx8_scale_byte(amax);
   const float inv = mx8_inv_scale(byte);
   u32x4_t o[2];
@@ -139,15 +138,14 @@ q8_cols_kernel(const uint16_t* __restrict__ x, int64_t R, int C, const int32_t* 
   for (int r = 0; r < 32; r += 4) {
     uint32_t wd = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) wd |= e4m3_of_bf16(tile[r + j][c], inv) << (8 * j);
+    for (int j = 0; j < 4; ++j) wd |= e4m3_of_bf16(col[(r + j) * kColPitch], inv) << (8 * j);
     o[r >> 4][(r >> 2) & 3] = wd;
   }
-  const int64_t col = c0 + c;
-  uint8_t* qm = q + static_cast<int64_t>(mat) * C * pitch;
-  u32x4_t* dst = reinterpret_cast<u32x4_t*>(qm + col * pitch + r0);
+  const int64_t cc = c0 + c;
+  u32x4_t* dst = reinterpret_cast<u32x4_t*>(q + static_cast<int64_t>(mat) * C * pitch + cc * pitch + r0 + 32 * blk);
   __builtin_nontemporal_store(o[0], dst);
   __builtin_nontemporal_store(o[1], dst + 1);
-  s[static_cast<int64_t>(mat) * C * (pitch / 32) + col * (pitch / 32) + rb] = static_cast<uint8_t>(byte);
+  s[(static_cast<int64_t>(mat) * C + cc) * (pitch / 32) + r0 / 32 + blk] = static_cast<uint8_t>(byte);
 }
 
 // ------------------------------------------------------- SwiGLU backward
@@ -198,20 +196,22 @@ unsigned grid_for(int64_t work) {
 }  // namespace
 
 bool launch_q8_rows(const uint16_t* x, int64_t rows, int K, const int32_t* offsets, int E, uint8_t* q,
-                    uint8_t* s, hipStream_t st) {
+                    uint8_t* s, const char* name, hipStream_t st) {
   if (rows == 0) return true;
-  launch_kernel("mx8_quant_rows", q8_rows_kernel, dim3(grid_for(rows * (K / 32))), dim3(kQ8Threads), 0, st, x,
-                rows, K, offsets, E, q, s);
-  return launch_ok("mx8_quant_rows");
+  launch_kernel(name, q8_rows_kernel, dim3(grid_for(rows * (K / 32))), dim3(kQ8Threads), 0, st, x, rows, K,
+                offsets, E, q, s);
+  return launch_ok(name);
 }
 
 bool launch_q8_cols(const uint16_t* x, int64_t R, int C, int batch, const int32_t* offsets, int E,
-                    int64_t pitch, uint8_t* q, uint8_t* s, hipStream_t st) {
+                    int64_t pitch, uint8_t* q, uint8_t* s, const char* name, hipStream_t st) {
   if (R == 0 || batch == 0) return true;
-  const dim3 grid(static_cast<unsigned>((R + 31) / 32), static_cast<unsigned>(C / kColTile),
+  if (C % kColTileCols || pitch % 128) return false;
+  if (offsets == nullptr && R % kColTileRows) return false;
+  const dim3 grid(static_cast<unsigned>(R / kColTileRows), static_cast<unsigned>(C / kColTileCols),
                   static_cast<unsigned>(batch));
-  launch_kernel("mx8_quant_cols", q8_cols_kernel, grid, dim3(kQ8Threads), 0, st, x, R, C, offsets, E, pitch, q, s);
-  return launch_ok("mx8_quant_cols");
+  launch_kernel(name, q8_cols_kernel, grid, dim3(kQ8Threads), 0, st, x, R, C, offsets, E, pitch, q, s);
+  return launch_ok(name);
 }
 
 bool launch_swiglu_bwd(const uint16_t* dA, const uint16_t* h, int64_t rows, int I, const int32_t* offsets, int E,
