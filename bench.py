@@ -51,9 +51,9 @@ KERNEL_SOURCES = {
     "mx_quantize_scatter": "quantize.hip", "mx_requant": "quantize.hip",
     "mx8_dgrad_fc2": "gemm_fwd.hip", "mx8_wgrad_fc2": "gemm_fwd.hip",
     "mx8_dgrad_fc1": "gemm_fwd.hip", "mx8_wgrad_fc1": "gemm_fwd.hip",
-    "swiglu_bwd": "mx8.hip",
+    "mx8_swiglu_quant_dual_dH": "mx8.hip",
 }
-for _n in ("rows_dO", "rows_dH", "cols_dO", "cols_a", "cols_w2", "cols_dH", "cols_w1", "cols_xp"):
+for _n in ("dual_dO", "cols_a", "cols_w2", "cols_w1", "cols_xp"):
     KERNEL_SOURCES["mx8_quant_" + _n] = "mx8.hip"
 
 
@@ -87,13 +87,12 @@ def algorithmic_work(T, H, E, k, I):
     fl["mx_gemm_fc2"] = fl["gemm_fc2"]
     for n in ("dgrad_fc2", "wgrad_fc2", "dgrad_fc1", "wgrad_fc1"):
         fl["mx8_" + n] = fl["gemm_" + n]
-    # SwiGLU backward: read dA and h, write dH
-    by["swiglu_bwd"] = M * (I * 2 + 2 * I * 2 + 2 * I * 2)
     # MXFP8 quantisers: read bf16, write one E4M3 byte per element and one E8M0 byte per 32
     q8 = lambda n: n * (2 + 1) + n // 32
-    by.update({"mx8_quant_rows_dO": q8(M * H), "mx8_quant_rows_dH": q8(M * 2 * I),
-               "mx8_quant_cols_dO": q8(M * H), "mx8_quant_cols_a": q8(M * I),
-               "mx8_quant_cols_dH": q8(M * 2 * I), "mx8_quant_cols_xp": q8(M * H),
+    by.update({"mx8_quant_dual_dO": M * H * 2 + 2 * (M * H + M * H // 32),
+               # the SwiGLU backward's inputs dA and h; both forms of dH out
+               "mx8_swiglu_quant_dual_dH": M * I * 2 + M * 2 * I * 2 + 2 * (M * 2 * I + M * 2 * I // 32),
+               "mx8_quant_cols_a": q8(M * I), "mx8_quant_cols_xp": q8(M * H),
                "mx8_quant_cols_w2": q8(E * H * I), "mx8_quant_cols_w1": q8(E * 2 * I * H)})
     return fl, by
 

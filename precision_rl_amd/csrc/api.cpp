@@ -133,7 +133,7 @@ BwdWs bwd_ws(int64_t cap, int H, int I, int E) {
 // GEMM operand quantised along that GEMM's reduction axis; transposed
 // operands (columns = dispatched rows) have P = roundup(cap, 128) columns.
 struct Mx8Ws {
-  size_t dO, xp, dA, dH, dXp, dOq, dOqs, dOt, dOts, at, ats, w2t, w2ts, dHq, dHqs, dHt, dHts, w1t, w1ts, xpt,
+  size_t dO, xp, dA, dXp, dOq, dOqs, dOt, dOts, at, ats, w2t, w2ts, dHq, dHqs, dHt, dHts, w1t, w1ts, xpt,
       xpts, total;
   int64_t P;
 };
@@ -146,7 +146,6 @@ Mx8Ws mx8_ws(int64_t cap, int H, int I, int E) {
   w.dO = take(c * H * 2);
   w.xp = take(c * H * 2);
   w.dA = take(c * I * 2);
-  w.dH = take(c * 2 * I * 2);
   w.dXp = take(c * H * 2);
   w.dOq = take(c * H);          w.dOqs = take(c * H / 32);
   w.dOt = take(H * P);          w.dOts = take(H * P / 32);
@@ -625,7 +624,7 @@ w4a4_status w4a4_mx8_expert_bwd(int64_t T, int H, int I, int E, int k, int row_a
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   auto bf = [&](size_t o) { return reinterpret_cast<uint16_t*>(ws + o); };
-  uint16_t *dO = bf(L.dO), *xp = bf(L.xp), *dA = bf(L.dA), *dH = bf(L.dH), *dXp = bf(L.dXp);
+  uint16_t *dO = bf(L.dO), *xp = bf(L.xp), *dA = bf(L.dA), *dXp = bf(L.dXp);
   const uint16_t* h = static_cast<const uint16_t*>(save_h);
   const uint16_t* a = static_cast<const uint16_t*>(save_a);
   const uint16_t* W1 = static_cast<const uint16_t*>(w1);
@@ -640,8 +639,8 @@ w4a4_status w4a4_mx8_expert_bwd(int64_t T, int H, int I, int E, int k, int row_a
       !launch_zero_pad_rows(cap, H, src_row, off, E, xp, s))
     return W4A4_ERR_LAUNCH;
   // FC2: dA = Q_H(dO) Q_H(W2[e]);  dW2[e] = Q_r(dO_e)^T Q_r(a_e)
-  if (!launch_q8_rows(dO, cap, H, off, E, ws + L.dOq, ws + L.dOqs, "mx8_quant_rows_dO", s) ||
-      !launch_q8_cols(dO, cap, H, 1, off, E, P, ws + L.dOt, ws + L.dOts, "mx8_quant_cols_dO", s) ||
+  if (!launch_q8_dual(dO, nullptr, cap, H, 0, off, E, P, ws + L.dOq, ws + L.dOqs, ws + L.dOt, ws + L.dOts,
+                      "mx8_quant_dual_dO", s) ||
       !launch_q8_cols(a, cap, I, 1, off, E, P, ws + L.at, ws + L.ats, "mx8_quant_cols_a", s) ||
       !launch_q8_cols(W2, H, I, E, nullptr, 0, H, ws + L.w2t, ws + L.w2ts, "mx8_quant_cols_w2", s))
     return W4A4_ERR_LAUNCH;
@@ -651,10 +650,10 @@ w4a4_status w4a4_mx8_expert_bwd(int64_t T, int H, int I, int E, int k, int row_a
   if (!launch_mx8_wgrad(H, I, E, off, ws + L.dOt, ws + L.dOts, ws + L.at, ws + L.ats, P,
                         static_cast<uint16_t*>(dw2), "mx8_wgrad_fc2", s))
     return W4A4_ERR_LAUNCH;
-  if (!launch_swiglu_bwd(dA, h, cap, I, off, E, dH, s)) return W4A4_ERR_LAUNCH;
-  // FC1: dXp = Q_2I(dH) Q_2I(W1[e]);  dW1[e] = Q_r(dH_e)^T Q_r(xp_e)
-  if (!launch_q8_rows(dH, cap, 2 * I, off, E, ws + L.dHq, ws + L.dHqs, "mx8_quant_rows_dH", s) ||
-      !launch_q8_cols(dH, cap, 2 * I, 1, off, E, P, ws + L.dHt, ws + L.dHts, "mx8_quant_cols_dH", s) ||
+  // FC1: dXp = Q_2I(dH) Q_2I(W1[e]);  dW1[e] = Q_r(dH_e)^T Q_r(xp_e), with dH the SwiGLU
+  // backward of dA, formed tile by tile inside its quantiser
+  if (!launch_q8_dual(dA, h, cap, 2 * I, I, off, E, P, ws + L.dHq, ws + L.dHqs, ws + L.dHt, ws + L.dHts,
+                      "mx8_swiglu_quant_dual_dH", s) ||
       !launch_q8_cols(W1, 2 * I, H, E, nullptr, 0, 2 * I, ws + L.w1t, ws + L.w1ts, "mx8_quant_cols_w1", s) ||
       !launch_q8_cols(xp, cap, H, 1, off, E, P, ws + L.xpt, ws + L.xpts, "mx8_quant_cols_xp", s))
     return W4A4_ERR_LAUNCH;

@@ -93,18 +93,19 @@ bool launch_fc1_mx(int64_t rows_alloc, int H, int I, int E, const int32_t* offse
 bool launch_fc2_mx(int64_t rows_alloc, int H, int I, int E, const int32_t* offsets, Fp4Operand a,
                    Fp4Operand w2, uint16_t* o_out, hipStream_t s);
 
-// MXFP8 backward pieces.  Quantisers (E4M3 + E8M0 per 32): along rows of a
-// [rows, K] bf16 matrix (rows [0, offsets[E]) when offsets is given) into
-// q [rows, K], s [rows, K/32]; along columns of `batch` [R, C] matrices into
-// q [batch][C, pitch], s [batch][C, pitch/32] (row blocks [0, offsets[E])
-// when given, in whole tiles of 128 rows; C % 64 == 0, pitch % 128 == 0).
-bool launch_q8_rows(const uint16_t* x, int64_t rows, int K, const int32_t* offsets, int E, uint8_t* q,
-                    uint8_t* s, const char* name, hipStream_t st);
+// MXFP8 backward pieces.  Quantiser (E4M3 + E8M0 per 32) along columns of
+// `batch` [R, C] matrices into q [batch][C, pitch], s [batch][C, pitch/32]
+// (row blocks [0, offsets[E]) when given, in whole tiles of 128 rows;
+// C % 64 == 0, pitch % 128 == 0).
 bool launch_q8_cols(const uint16_t* x, int64_t R, int C, int batch, const int32_t* offsets, int E,
                     int64_t pitch, uint8_t* q, uint8_t* s, const char* name, hipStream_t st);
-// dH = SwiGLU backward of dA [rows, I] on the saved h [rows, 2I], rows [0, offsets[E]).
-bool launch_swiglu_bwd(const uint16_t* dA, const uint16_t* h, int64_t rows, int I, const int32_t* offsets, int E,
-                       uint16_t* dH, hipStream_t st);
+// Both forms of one [R, C] matrix from one read (rows [0, offsets[E]), whole
+// tiles of 128): along rows into q_r [R, C], s_r [R, C/32]; along columns into
+// q_c [C, pitch], s_c [C, pitch/32].  h != NULL: the matrix is the SwiGLU
+// backward dH [R, 2I] of x = dA [R, I] on the saved h (C = 2I), never stored.
+bool launch_q8_dual(const uint16_t* x, const uint16_t* h, int64_t R, int C, int I, const int32_t* offsets, int E,
+                    int64_t pitch, uint8_t* q_r, uint8_t* s_r, uint8_t* q_c, uint8_t* s_c, const char* name,
+                    hipStream_t st);
 // C = A B^T on the scaled FP8 MFMA, bf16 out.  dgrad: A [rows_alloc, K] grouped
 // by offsets, B [E][N, K]; wgrad: per expert, A [M1, pitch] and B [N, pitch]
 // over the columns [offsets[e], offsets[e+1]) (multiples of 128), out [E][M1, N].

@@ -1,6 +1,7 @@
 // MXFP8 operand preparation for the MXFP8 variant of the straight-through
-// backward on gfx950: quantisers along rows and along columns (transposing),
-// and the SwiGLU backward as a pass of its own.
+// backward on gfx950: a quantiser along columns (transposing; the weights),
+// and one that writes both forms of a matrix from a single read (dO; and dH,
+// formed from dA and h by the SwiGLU backward inside the pass).
 //
 // Format (OCP Microscaling Formats v1.0, section 6.3, with E4M3 elements;
 // the backward the pages compare against their BF16 one, AI summary, key
@@ -47,50 +48,6 @@ __device__ __forceinline__ float mx8_inv_scale(uint32_t byte) {
 __device__ __forceinline__ uint32_t e4m3_of_bf16(uint32_t x16, float inv) {
   const float v = bf16_to_f32(static_cast<uint16_t>(x16 & 0x7FFFu)) * inv;
   return e4m3_of(v) | ((x16 >> 8) & 0x80u);
-}
-
-// ------------------------------------------------------------- along rows
-// One thread per block of 32 elements of a row: 64 B read, 32 B of E4M3 and
-// one scale byte written.  Rows [0, offsets[E]) when offsets is given (the
-// dispatched rows; pad rows are zeros and encode as zeros), else all rows.
-__global__ void __launch_bounds__(kQ8Threads)
-q8_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int K, const int32_t* __restrict__ offsets, int E,
-               uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
-  const int nb = K / 32;
-  int64_t n = rows;
-  if (offsets != nullptr) n = min<int64_t>(n, offsets[E]);
-  const int64_t total = n * nb;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kQ8Threads + threadIdx.x; i < total;
-       i += static_cast<int64_t>(gridDim.x) * kQ8Threads) {
-    const int64_t r = i / nb;
-    const int b = static_cast<int>(i % nb);
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + r * K + b * 32);
-    u32x4_t w[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) w[j] = __builtin_nontemporal_load(src + j);
-    uint32_t amax = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int d = 0; d < 4; ++d) amax = max(amax, max(w[j][d] & 0x7FFFu, (w[j][d] >> 16) & 0x7FFFu));
-    const uint32_t byte = mx8_scale_byte(amax);
-    const float inv = mx8_inv_scale(byte);
-    u32x4_t o[2];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t lo = e4m3_of_bf16(w[j][d] & 0xFFFFu, inv), hi = e4m3_of_bf16(w[j][d] >> 16, inv);
-        const int e = 8 * j + 2 * d;   // element index within the block
-        const uint32_t pair = lo | (hi << 8);
-        if ((e & 3) == 0) o[e >> 4][(e >> 2) & 3] = pair;
-        else o[e >> 4][(e >> 2) & 3] |= pair << 16;
-      }
-    u32x4_t* dst = reinterpret_cast<u32x4_t*>(q + r * K + b * 32);
-    __builtin_nontemporal_store(o[0], dst);
-    __builtin_nontemporal_store(o[1], dst + 1);
-    s[r * nb + b] = static_cast<uint8_t>(byte);
-  }
 }
 
 // ---------------------------------------------------------- along columns
@@ -148,42 +105,105 @@ q8_cols_kernel(const uint16_t* __restrict__ x, int64_t R, int C, const int32_t* 
   s[(static_cast<int64_t>(mat) * C + cc) * (pitch / 32) + r0 / 32 + blk] = static_cast<uint8_t>(byte);
 }
 
-// ------------------------------------------------------- SwiGLU backward
-// dH = [dA u s (1 + g (1 - s)), dA g s] with g, u the bf16 gate / up halves
-// of h and s = sigmoid(g), FP32 arithmetic, bf16 results (the formula and
-// arithmetic of the BF16 backward's fused epilogue).  One thread per 8
-// features of a row; rows [0, offsets[E]).
+// ------------------------------------------------- both axes in one pass
+// The two MXFP8 forms of one [R, C] bf16 matrix from a single read: along
+// rows (q_r [R, C], s_r [R, C/32], the dgrad operand) and along columns
+// (q_c [C, pitch], s_c [C, pitch/32], the wgrad operand).  Same 128 x 64
+// tile as q8_cols_kernel; thread t also encodes row t / 2's 32-column block
+// t % 2 of the tile.  SWIGLU: the matrix is dH [R, 2I], computed in the load
+// from dA [R, I] and the saved h [R, 2I] (the SwiGLU backward's formula and
+// FP32 arithmetic, bf16-rounded as the BF16 path stores dH), so dH itself is
+// never written.  Row tiles at or past offsets[E] are skipped.
+template <bool SWIGLU>
 __global__ void __launch_bounds__(kQ8Threads)
-swiglu_bwd_kernel(const uint16_t* __restrict__ dA, const uint16_t* __restrict__ h, int64_t rows, int I,
-                  const int32_t* __restrict__ offsets, int E, uint16_t* __restrict__ dH) {
-  const int64_t n = min<int64_t>(rows, offsets[E]);
-  const int per_row = I / 8;
-  const int64_t total = n * per_row;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kQ8Threads + threadIdx.x; i < total;
-       i += static_cast<int64_t>(gridDim.x) * kQ8Threads) {
-    const int64_t r = i / per_row;
-    const int c = static_cast<int>(i % per_row) * 8;
-    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(dA + r * I + c));
-    const u32x4_t hg = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(h + r * (2 * I) + c));
-    const u32x4_t hu = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(h + r * (2 * I) + I + c));
-    u32x4_t dg, du;
+q8_dual_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ h, int64_t R, int C, int I,
+               const int32_t* __restrict__ offsets, int E, int64_t pitch, uint8_t* __restrict__ q_r,
+               uint8_t* __restrict__ s_r, uint8_t* __restrict__ q_c, uint8_t* __restrict__ s_c) {
+  __shared__ uint16_t tile[kColTileRows * kColPitch];
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kColTileRows;
+  const int c0 = blockIdx.y * kColTileCols;
+  if (r0 >= min<int64_t>(R, offsets[E])) return;
+  const int t = threadIdx.x;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      float rg[2], ru[2];
+  for (int i = 0; i < 4; ++i) {
+    const int lr = t / 8 + 32 * i, ch = t % 8;
+    const int64_t r = r0 + lr;
+    u32x4_t v;
+    if constexpr (!SWIGLU) {
+      v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + r * C + c0 + ch * 8));
+    } else {
+      const bool gate_half = c0 < I;                 // a tile lies in one half (I % 64 == 0)
+      const int i0 = (gate_half ? c0 : c0 - I) + ch * 8;
+      const u32x4_t da = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + r * I + i0));
+      const u32x4_t hg = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(h + r * (2 * I) + i0));
+      const u32x4_t hu = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(h + r * (2 * I) + I + i0));
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const float da = bf16_to_f32(static_cast<uint16_t>(v[d] >> (16 * p)));
-        const float gt = bf16_to_f32(static_cast<uint16_t>(hg[d] >> (16 * p)));
-        const float up = bf16_to_f32(static_cast<uint16_t>(hu[d] >> (16 * p)));
-        const float sg = sigmoid_fast(gt);
-        rg[p] = da * up * sg * (1.0f + gt * (1.0f - sg));
-        ru[p] = da * gt * sg;
+      for (int d = 0; d < 4; ++d) {
+        float o2[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const float a = bf16_to_f32(static_cast<uint16_t>(da[d] >> (16 * p)));
+          const float gt = bf16_to_f32(static_cast<uint16_t>(hg[d] >> (16 * p)));
+          const float up = bf16_to_f32(static_cast<uint16_t>(hu[d] >> (16 * p)));
+          const float sg = sigmoid_fast(gt);
+          o2[p] = gate_half ? a * up * sg * (1.0f + gt * (1.0f - sg)) : a * gt * sg;
+        }
+        v[d] = pack_bf16x2(o2[0], o2[1]);
       }
-      dg[d] = pack_bf16x2(rg[0], rg[1]);
-      du[d] = pack_bf16x2(ru[0], ru[1]);
     }
-    __builtin_nontemporal_store(dg, reinterpret_cast<u32x4_t*>(dH + r * (2 * I) + c));
-    __builtin_nontemporal_store(du, reinterpret_cast<u32x4_t*>(dH + r * (2 * I) + I + c));
+    uint32_t* dst = reinterpret_cast<uint32_t*>(tile + lr * kColPitch + ch * 8);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) dst[d] = v[d];
+  }
+  __syncthreads();
+  // along columns: thread (column t / 4, 32-row block t % 4)
+  {
+    const int c = t / 4, blk = t % 4;
+    const uint16_t* col = tile + (32 * blk) * kColPitch + c;
+    uint32_t amax = 0;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) amax = max(amax, static_cast<uint32_t>(col[r * kColPitch] & 0x7FFFu));
+    const uint32_t byte = mx8_scale_byte(amax);
+    const float inv = mx8_inv_scale(byte);
+    u32x4_t o[2];
+#pragma unroll
+    for (int r = 0; r < 32; r += 4) {
+      uint32_t wd = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wd |= e4m3_of_bf16(col[(r + j) * kColPitch], inv) << (8 * j);
+      o[r >> 4][(r >> 2) & 3] = wd;
+    }
+    const int64_t cc = c0 + c;
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(q_c + cc * pitch + r0 + 32 * blk);
+    __builtin_nontemporal_store(o[0], dst);
+    __builtin_nontemporal_store(o[1], dst + 1);
+    s_c[cc * (pitch / 32) + r0 / 32 + blk] = static_cast<uint8_t>(byte);
+  }
+  // along rows: thread (row t / 2, 32-column block t % 2)
+  {
+    const int lr = t / 2, blk = t % 2;
+    const uint32_t* rowp = reinterpret_cast<const uint32_t*>(tile + lr * kColPitch + 32 * blk);
+    uint32_t w[16];
+    uint32_t amax = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      w[j] = rowp[j];
+      amax = max(amax, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
+    }
+    const uint32_t byte = mx8_scale_byte(amax);
+    const float inv = mx8_inv_scale(byte);
+    u32x4_t o[2];
+#pragma unroll
+    for (int j = 0; j < 16; j += 2) {
+      const uint32_t b0 = e4m3_of_bf16(w[j] & 0xFFFFu, inv), b1 = e4m3_of_bf16(w[j] >> 16, inv);
+      const uint32_t b2 = e4m3_of_bf16(w[j + 1] & 0xFFFFu, inv), b3 = e4m3_of_bf16(w[j + 1] >> 16, inv);
+      o[j >> 3][(j >> 1) & 3] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+    }
+    const int64_t r = r0 + lr;
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(q_r + r * C + c0 + 32 * blk);
+    __builtin_nontemporal_store(o[0], dst);
+    __builtin_nontemporal_store(o[1], dst + 1);
+    s_r[r * (C / 32) + c0 / 32 + blk] = static_cast<uint8_t>(byte);
   }
 }
 
@@ -194,14 +214,6 @@ unsigned grid_for(int64_t work) {
 }
 
 }  // namespace
-
-bool launch_q8_rows(const uint16_t* x, int64_t rows, int K, const int32_t* offsets, int E, uint8_t* q,
-                    uint8_t* s, const char* name, hipStream_t st) {
-  if (rows == 0) return true;
-  launch_kernel(name, q8_rows_kernel, dim3(grid_for(rows * (K / 32))), dim3(kQ8Threads), 0, st, x, rows, K,
-                offsets, E, q, s);
-  return launch_ok(name);
-}
 
 bool launch_q8_cols(const uint16_t* x, int64_t R, int C, int batch, const int32_t* offsets, int E,
                     int64_t pitch, uint8_t* q, uint8_t* s, const char* name, hipStream_t st) {
@@ -214,12 +226,20 @@ bool launch_q8_cols(const uint16_t* x, int64_t R, int C, int batch, const int32_
   return launch_ok(name);
 }
 
-bool launch_swiglu_bwd(const uint16_t* dA, const uint16_t* h, int64_t rows, int I, const int32_t* offsets, int E,
-                       uint16_t* dH, hipStream_t st) {
-  if (rows == 0) return true;
-  launch_kernel("swiglu_bwd", swiglu_bwd_kernel, dim3(grid_for(rows * (I / 8))), dim3(kQ8Threads), 0, st, dA, h,
-                rows, I, offsets, E, dH);
-  return launch_ok("swiglu_bwd");
+bool launch_q8_dual(const uint16_t* x, const uint16_t* h, int64_t R, int C, int I, const int32_t* offsets, int E,
+                    int64_t pitch, uint8_t* q_r, uint8_t* s_r, uint8_t* q_c, uint8_t* s_c, const char* name,
+                    hipStream_t st) {
+  if (R == 0) return true;
+  if (C % kColTileCols || pitch % 128 || (h != nullptr && (C != 2 * I || I % kColTileCols))) return false;
+  const dim3 grid(static_cast<unsigned>((R + kColTileRows - 1) / kColTileRows),
+                  static_cast<unsigned>(C / kColTileCols));
+  if (h == nullptr)
+    launch_kernel(name, q8_dual_kernel<false>, grid, dim3(kQ8Threads), 0, st, x, h, R, C, I, offsets, E, pitch, q_r,
+                  s_r, q_c, s_c);
+  else
+    launch_kernel(name, q8_dual_kernel<true>, grid, dim3(kQ8Threads), 0, st, x, h, R, C, I, offsets, E, pitch, q_r,
+                  s_r, q_c, s_c);
+  return launch_ok(name);
 }
 
 }  // namespace w4a4
