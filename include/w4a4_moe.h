@@ -355,6 +355,22 @@ w4a4_status w4a4_mx8_expert_bwd(
     void* dx, void* dw1, void* dw2,
     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * w4a4_mx8_quantize -- the MXFP8 operand quantiser of w4a4_mx8_expert_bwd as
+ * a call of its own: both forms of a bf16 matrix from one read.
+ *   x       [R, C] bf16, R % 128 == 0, C % 64 == 0.
+ *   q_rows  [R, C] E4M3 bytes, s_rows [R, C/32] E8M0: blocks of 32 along rows.
+ *   q_cols  [C, pitch] E4M3 bytes, s_cols [C, pitch/32] E8M0: column c of x
+ *           in row c, blocks of 32 consecutive rows; pitch >= R, a multiple
+ *           of 128; bytes [R, pitch) of each row are not written.
+ * Format and rounding as in w4a4_mx8_expert_bwd (E4M3FN bytes, sign in bit 7,
+ * -0 encodes as 0x80).
+ */
+w4a4_status w4a4_mx8_quantize(
+    const void* x, int64_t R, int C,
+    uint8_t* q_rows, uint8_t* s_rows, uint8_t* q_cols, uint8_t* s_cols, int64_t pitch,
+    void* stream);
+
 /* Static description of a status code. */
 const char* w4a4_status_string(int status);
 

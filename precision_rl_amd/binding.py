@@ -45,6 +45,7 @@ _SIGS = {
     "w4a4_mx8_expert_bwd": (c_int, [c_i64, c_int, c_int, c_int, c_int, c_int,
                                     c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                     c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "w4a4_mx8_quantize": (c_int, [c_vp, c_i64, c_int, c_vp, c_vp, c_vp, c_vp, c_i64, c_vp]),
     "w4a4_status_string": (ctypes.c_char_p, [c_int]),
     "w4a4_last_error": (ctypes.c_char_p, []),
     "w4a4_profiler_enable": (c_int, [c_int]),
@@ -250,6 +251,24 @@ def w4a4_mx8_expert_bwd(dy, x, w1, w2, h, a, topk_w, xq, T, H, I, E, k, row_alig
         T, H, I, E, k, row_align, _p(dy), _p(x), _p(w1), _p(w2), _p(h), _p(a), _p(topk_w),
         _p(xq["offsets"]), _p(xq["row_map"]), _p(xq["src_row"]),
         _p(out["dx"]), _p(out["dw1"]), _p(out["dw2"]), _p(ws), ws.numel(), _stream()))
+    return out
+
+
+def w4a4_mx8_quantize(x):
+    """MXFP8 (E4M3 + E8M0 per 32) of x [R, C] bf16 along rows and along columns.
+    Returns dict(q_rows [R, C], s_rows [R, C/32], q_cols [C, R], s_cols [C, R/32]) uint8."""
+    lib = load()
+    R, C = x.shape
+    dev = x.device
+    pitch = (R + 127) // 128 * 128
+    out = dict(q_rows=torch.empty(R, C, dtype=torch.uint8, device=dev),
+               s_rows=torch.empty(R, C // 32, dtype=torch.uint8, device=dev),
+               q_cols=torch.empty(C, pitch, dtype=torch.uint8, device=dev),
+               s_cols=torch.empty(C, pitch // 32, dtype=torch.uint8, device=dev))
+    _check(lib.w4a4_mx8_quantize(_p(x), R, C, _p(out["q_rows"]), _p(out["s_rows"]), _p(out["q_cols"]),
+                                 _p(out["s_cols"]), pitch, _stream()))
+    out["q_cols"] = out["q_cols"][:, :R]
+    out["s_cols"] = out["s_cols"][:, :R // 32]
     return out
 
 

@@ -667,6 +667,22 @@ w4a4_status w4a4_mx8_expert_bwd(int64_t T, int H, int I, int E, int k, int row_a
   return W4A4_OK;
 }
 
+w4a4_status w4a4_mx8_quantize(const void* x, int64_t R, int C, uint8_t* q_rows, uint8_t* s_rows, uint8_t* q_cols,
+                              uint8_t* s_cols, int64_t pitch, void* stream) {
+  g_last_error.clear();
+  if (R < 0 || C <= 0) return fail(W4A4_ERR_INVALID_ARG, "bad size (R=%lld C=%d)", static_cast<long long>(R), C);
+  if (R % 128 || C % 64)
+    return fail(W4A4_ERR_UNSUPPORTED, "needs R %% 128 == 0 and C %% 64 == 0 (R=%lld C=%d)",
+                static_cast<long long>(R), C);
+  if (pitch < R || pitch % 128) return fail(W4A4_ERR_INVALID_ARG, "pitch must be >= R and a multiple of 128");
+  if (R == 0) return W4A4_OK;
+  REQUIRE_PTR(x); REQUIRE_PTR(q_rows); REQUIRE_PTR(s_rows); REQUIRE_PTR(q_cols); REQUIRE_PTR(s_cols);
+  if (!launch_q8_dual(static_cast<const uint16_t*>(x), nullptr, R, C, 0, nullptr, 0, pitch, q_rows, s_rows, q_cols,
+                      s_cols, "mx8_quant_dual", static_cast<hipStream_t>(stream)))
+    return W4A4_ERR_LAUNCH;
+  return W4A4_OK;
+}
+
 const char* w4a4_status_string(int status) {
   switch (status) {
     case W4A4_OK: return "ok";

@@ -113,7 +113,8 @@ q8_cols_kernel(const uint16_t* __restrict__ x, int64_t R, int C, const int32_t* 
 // t % 2 of the tile.  SWIGLU: the matrix is dH [R, 2I], computed in the load
 // from dA [R, I] and the saved h [R, 2I] (the SwiGLU backward's formula and
 // FP32 arithmetic, bf16-rounded as the BF16 path stores dH), so dH itself is
-// never written.  Row tiles at or past offsets[E] are skipped.
+// never written.  Row tiles at or past offsets[E] (when given; else R, a
+// multiple of 128) are skipped.
 template <bool SWIGLU>
 __global__ void __launch_bounds__(kQ8Threads)
 q8_dual_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ h, int64_t R, int C, int I,
@@ -122,7 +123,7 @@ q8_dual_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ h, i
   __shared__ uint16_t tile[kColTileRows * kColPitch];
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kColTileRows;
   const int c0 = blockIdx.y * kColTileCols;
-  if (r0 >= min<int64_t>(R, offsets[E])) return;
+  if (r0 >= (offsets != nullptr ? min<int64_t>(R, offsets[E]) : R)) return;
   const int t = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -231,6 +232,7 @@ bool launch_q8_dual(const uint16_t* x, const uint16_t* h, int64_t R, int C, int 
                     hipStream_t st) {
   if (R == 0) return true;
   if (C % kColTileCols || pitch % 128 || (h != nullptr && (C != 2 * I || I % kColTileCols))) return false;
+  if (offsets == nullptr && R % kColTileRows) return false;
   const dim3 grid(static_cast<unsigned>((R + kColTileRows - 1) / kColTileRows),
                   static_cast<unsigned>(C / kColTileCols));
   if (h == nullptr)

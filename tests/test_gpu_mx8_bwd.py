@@ -119,3 +119,38 @@ def test_mx8_backward_full_learner_sampled():
         rb, _ = _oracle(sub, 1)
         assert rel_l2(bf16_host(run.g["dw1"][e]), rb["dW1"][0]) <= BWD_TOL
         assert rel_l2(bf16_host(run.g["dw2"][e]), rb["dW2"][0]) <= BWD_TOL
+
+
+def test_mx8_quantizer_bytes_bit_exact():
+    """The MXFP8 quantiser's bytes (both axes) equal the oracle's: heavy
+    tails, blocks spread over many binades, zeros, -0, E4M3 midpoints and
+    their bf16 neighbours, saturation and subnormal E4M3 results."""
+    rng = np.random.default_rng(41)
+    R, C = 256, 192
+    v = rng.standard_t(3, (R, C)) * np.ldexp(1.0, rng.integers(-40, 40, (R // 32, C // 32)).repeat(32, 0).repeat(32, 1))
+    v[:32, :32] = 0.0
+    v[5, 40:72] = -0.0
+    # rows 64..95, columns 0..31: block max 256 (X = 0) and E4M3 midpoints (17, 19, 2^-10 ...) +- one bf16 ulp
+    mids = np.array([17.0, 19.0, 2.0 ** -10, 3 * 2.0 ** -10, 464.0 / 2, 0.0078125 * 1.5, 300.0, 250.0])
+    v[64:96, 0] = 256.0
+    v[64:96, 1:9] = mids
+    v[64:96, 25:32] = 1.0
+    bits = q.f64_to_bf16_bits(v)
+    b = bits.astype(np.int64)
+    bits[64:96, 9:17] = (b[64:96, 1:9] + 1).astype(np.uint16)
+    bits[64:96, 17:25] = (b[64:96, 1:9] - 1).astype(np.uint16)
+    # column-direction midpoints: column 100, rows 128..159
+    bits[128:160, 100] = q.f64_to_bf16_bits(np.ones(32))
+    bits[128, 100] = q.f64_to_bf16_bits(np.array([256.0]))[0]
+    bits[129:137, 100] = q.f64_to_bf16_bits(mids)
+    print_case("mx8_quantizer_bytes", R=R, C=C)
+    got = _b().w4a4_mx8_quantize(bf16_dev(bits, torch))
+    torch.cuda.synchronize()
+    from oracle import mxfp4 as mxo
+    xv = q.bf16_bits_to_f64(bits)
+    vr, sr = mxo.quantize_rows_mx8(xv)
+    vc, sc = mxo.quantize_rows_mx8(xv.T)
+    assert np.array_equal(got["q_rows"].cpu().numpy(), mxo.e4m3_bytes(vr))
+    assert np.array_equal(got["s_rows"].cpu().numpy(), sr)
+    assert np.array_equal(got["q_cols"].cpu().numpy(), mxo.e4m3_bytes(vc))
+    assert np.array_equal(got["s_cols"].cpu().numpy(), sc)
