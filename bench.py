@@ -227,16 +227,19 @@ def main_linear(args):
 QP_METRIC = "W4A4 quantize+permute tokens/s and % HBM peak (route + per-row amax + NVFP4 encode + scatter)"
 
 
-def qp_work(T, H, k, outer):
+def qp_work(T, H, k, outer, recipe="nvfp4"):
     """Per-launch algorithmic bytes of quantize+permute (c2 shape)."""
     M = T * k
-    by = {"quantize_scatter": T * (H * 2 + k * 4) + M * (H // 2 + H // 16 + 4) + T * k * 4 + M * 4}
+    by = {"quantize_scatter": T * (H * 2 + k * 4) + M * (H // 2 + H // 16 + 4) + T * k * 4 + M * 4,
+          # MXFP4: one E8M0 byte per 32 elements, no outer scale
+          "mx_quantize_scatter": T * (H * 2 + k * 4) + M * (H // 2 + H // 32) + T * k * 4 + M * 4}
+    by = {n: v for n, v in by.items() if n.startswith("mx_") == (recipe == "mxfp4")}
     if outer == "tensor":
         by["group_amax"] = T * H * 2     # one extra read of x
     return {}, by
 
 
-def cpu_baseline_qp(d, tokens, group_rows):
+def cpu_baseline_qp(d, tokens, group_rows, recipe="nvfp4"):
     from oracle import moe, nvfp4 as q
     try:
         from threadpoolctl import threadpool_info
@@ -247,10 +250,14 @@ def cpu_baseline_qp(d, tokens, group_rows):
     idx = d["topk_idx"][:tokens]
     E = int(d["topk_idx"].max()) + 1
     t0 = time.perf_counter()
-    moe.quantize_permute(x, idx, E, 1, group_rows=min(group_rows, tokens))
+    if recipe == "mxfp4":
+        moe.quantize_permute_mx(x, idx, E, 1)
+    else:
+        moe.quantize_permute(x, idx, E, 1, group_rows=min(group_rows, tokens))
     dt = time.perf_counter() - t0
     return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{tokens} tokens of the quantize+permute workload, FP64 numpy, {dt:.1f} s",
+            "sample": f"{tokens} tokens of the quantize+permute workload"
+                      f"{' (MXFP4)' if recipe == 'mxfp4' else ''}, FP64 numpy, {dt:.1f} s",
             "seconds": dt, "host_cpus": len(os.sched_getaffinity(0))}
 
 
@@ -265,29 +272,36 @@ def main_qp(args):
     x = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).to(dev)
     idx = torch.from_numpy(d["topk_idx"]).to(dev)
     cap = b.rows_capacity(T, k, E, 1)
+    mx = args.recipe == "mxfp4"
+    if mx and args.outer != "token":
+        print("bench.py: the MXFP4 recipe has no outer scale (--outer applies to nvfp4)", file=sys.stderr)
+        sys.exit(2)
     xq = dict(codes=torch.empty(cap, H // 2, dtype=torch.uint8, device=dev),
-              scales=torch.empty(cap, H // 16, dtype=torch.uint8, device=dev),
-              outer=torch.empty(cap, dtype=torch.float32, device=dev),
+              scales=torch.empty(cap, H // (32 if mx else 16), dtype=torch.uint8, device=dev),
               offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
               row_map=torch.empty(T, k, dtype=torch.int32, device=dev),
               src_row=torch.empty(cap, dtype=torch.int32, device=dev))
+    if not mx:
+        xq["outer"] = torch.empty(cap, dtype=torch.float32, device=dev)
     per_tensor = args.outer == "tensor"
     kind = b.WS_QUANTIZE_PERMUTE_DOMAIN if per_tensor else b.WS_QUANTIZE_PERMUTE
     ws = torch.empty(b.workspace_size(kind, T, H, 0, E, k, 1) + 256, dtype=torch.uint8, device=dev)
     calibration_copy(torch, dev)
 
     def step():
-        if per_tensor:
+        if mx:
+            b.w4a4_mx_quantize_permute(x, idx, E, 1, out=xq, workspace=ws)
+        elif per_tensor:
             b.w4a4_quantize_permute_domain(x, idx, E, 1, group_rows=T, out=xq, workspace=ws)
         else:
             b.w4a4_quantize_permute(x, idx, E, 1, out=xq, workspace=ws)
 
     ms, kern = time_steps(b, torch, step, args)
-    fl, by = qp_work(T, H, k, args.outer)
+    fl, by = qp_work(T, H, k, args.outer, args.recipe)
     per_kernel, roof = summarize(kern, ms, args.steps, fl, by, concurrent={})
     alg = sum(by.values()) - by.get("group_amax", 0)
     out = {
-        "metric": QP_METRIC,
+        "metric": QP_METRIC.replace("NVFP4", "MXFP4") if mx else QP_METRIC,
         "value": round(T / (ms * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -297,9 +311,10 @@ def main_qp(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 -> nvfp4 (u8 codes, e4m3 scales, f32 outer)",
+        "dtype": "bf16 -> mxfp4 (u8 codes, e8m0 scales)" if mx else "bf16 -> nvfp4 (u8 codes, e4m3 scales, f32 outer)",
         "data": "synthetic (seeded; Student-t x)",
-        "config": {"workload": f"qp: route + quantize+permute, outer scale per {args.outer}",
+        "config": {"workload": "qp: route + quantize+permute, MXFP4" if mx else
+                               f"qp: route + quantize+permute, outer scale per {args.outer}",
                    "T": T, "H": H, "E": E, "top_k": k},
         "roofline": roof,
         "call_hbm_frac": round(alg / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
@@ -307,7 +322,7 @@ def main_qp(args):
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the FP64 oracle on the host", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline_qp(d, 8192, T if per_tensor else 1)
+        out["cpu_baseline"] = cpu_baseline_qp(d, 8192, T if per_tensor else 1, args.recipe)
     print(json.dumps(out), flush=True)
 
 
@@ -442,7 +457,7 @@ def main():
                          "default) or mxfp8 (E4M3 + E8M0 per 32 along each GEMM's reduction axis, "
                          "scaled FP8 MFMA; routes with row_align 128)")
     ap.add_argument("--recipe", choices=["nvfp4", "mxfp4"], default="nvfp4",
-                    help="learner: the forward's format -- nvfp4 (E4M3 per 16 + FP32 outer "
+                    help="learner and qp: the forward's format -- nvfp4 (E4M3 per 16 + FP32 outer "
                          "scales, exact f16 decode, the default) or mxfp4 (E8M0 per 32, scaled "
                          "FP4 MFMA)")
     args = ap.parse_args()

@@ -224,3 +224,41 @@ def test_mx_forward_full_workload_sampled():
     assert np.mean(gc != ref["a_codes"][rows_ref]) <= CODE_FLIP_BUDGET
     y = bf16_host(run.f["y"])[sample]
     assert rel_l2(y, ref["y"]) <= Y_TOL
+
+
+def test_mx_forward_full_skew_sampled():
+    """Skewed workload at full size (T=32768, H=2048, E=128, k=8, I=768;
+    Zipf(1.2) popularity, 10 experts without tokens) in the MXFP4 recipe:
+    the permutation bit-exact against the oracle's routing of all tokens;
+    the encodings and forward outputs of sampled tokens (the first and last
+    rows of the most and least popular experts) against the oracle on those
+    tokens alone."""
+    w = synth.WORKLOADS["skew"]
+    d = synth.make_inputs(w.T, w.H, w.E, w.k, w.I, w.routing, w.x_dist, seed=1000 + w.index)
+    print_case("mx_skew_full_sampled", T=w.T, H=w.H, E=w.E, k=w.k, I=w.I)
+    run = MxRun(d, w.T, w.H, w.E, w.k, w.I)
+    offsets, row_map, src_row = moe.route_fast(d["topk_idx"], w.E, 1)
+    assert np.array_equal(run.xq["offsets"].cpu().numpy(), offsets)
+    assert np.array_equal(run.xq["row_map"].cpu().numpy(), row_map)
+    counts = np.diff(offsets)
+    assert (counts == 0).sum() == 10
+    big = int(np.argmax(counts))
+    small = int(np.argmin(np.where(counts > 0, counts, counts.max() + 1)))
+    picks = [src_row[offsets[big]], src_row[offsets[big + 1] - 1], src_row[offsets[small]],
+             src_row[offsets[small + 1] - 1], 0, w.T - 1]
+    sample = np.unique(np.array(picks))
+    experts = np.unique(d["topk_idx"][sample])
+    remap = -np.ones(w.E, dtype=np.int64)
+    remap[experts] = np.arange(experts.size)
+    sub = dict(x=d["x"][sample], topk_idx=remap[d["topk_idx"][sample]].astype(np.int32),
+               topk_w=d["topk_w"][sample], w1=d["w1"][experts], w2=d["w2"][experts])
+    ref, _, _ = _oracle(sub, experts.size, 1)
+    rows_gpu = row_map[sample].reshape(-1)
+    rows_ref = ref["xq"]["row_map"].reshape(-1)
+    assert np.array_equal(u8(run.xq["codes"])[rows_gpu], ref["xq"]["packed"][rows_ref])
+    assert np.array_equal(u8(run.xq["scales"])[rows_gpu], ref["xq"]["scales"][rows_ref])
+    fc1 = run.f["fc1_f32"].cpu().numpy()[rows_gpu]
+    assert rel_l2(fc1, ref["h64"][rows_ref]) <= FC1_TOL
+    gc = q.unpack_codes(u8(run.f["a_codes"])[rows_gpu])
+    assert np.mean(gc != ref["a_codes"][rows_ref]) <= CODE_FLIP_BUDGET
+    assert rel_l2(bf16_host(run.f["y"])[sample], ref["y"]) <= Y_TOL
