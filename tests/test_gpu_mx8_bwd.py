@@ -154,3 +154,37 @@ def test_mx8_quantizer_bytes_bit_exact():
     assert np.array_equal(got["s_rows"].cpu().numpy(), sr)
     assert np.array_equal(got["q_cols"].cpu().numpy(), mxo.e4m3_bytes(vc))
     assert np.array_equal(got["s_cols"].cpu().numpy(), sc)
+
+
+def test_mx8_backward_full_skew_sampled():
+    """Skewed workload at full size (T=32768, H=2048, E=128, k=8, I=768;
+    Zipf(1.2) popularity, 10 experts without tokens), MXFP8 backward: dX of
+    the last token of the least popular live expert and of the first and
+    last tokens, dW of the least popular live expert against the oracle on
+    its rows alone, dW of the empty experts exactly zero."""
+    w = synth.WORKLOADS["skew"]
+    d = synth.make_inputs(w.T, w.H, w.E, w.k, w.I, w.routing, w.x_dist, backward=True, seed=1000 + w.index)
+    print_case("mx8_bwd_skew_full_sampled", T=w.T, H=w.H, E=w.E, k=w.k, I=w.I, A=A)
+    run = Mx8Run(d, w.T, w.H, w.E, w.k, w.I)
+    counts = np.bincount(d["topk_idx"].reshape(-1), minlength=w.E)
+    empty = np.nonzero(counts == 0)[0]
+    assert empty.size == 10
+    small = int(np.argmin(np.where(counts > 0, counts, counts.max() + 1)))
+    tok_small = np.nonzero((d["topk_idx"] == small).any(axis=1))[0]
+    sample = np.unique(np.array([tok_small[-1], 0, w.T - 1]))
+    experts = np.unique(d["topk_idx"][sample])
+    remap = -np.ones(w.E, dtype=np.int64)
+    remap[experts] = np.arange(experts.size)
+    sub = dict(x=d["x"][sample], topk_idx=remap[d["topk_idx"][sample]].astype(np.int32),
+               topk_w=d["topk_w"][sample], w1=d["w1"][experts], w2=d["w2"][experts], dy=d["dy"][sample])
+    rb, _ = _oracle(sub, experts.size)
+    assert rel_l2(bf16_host(run.g["dx"])[sample], rb["dX"]) <= BWD_TOL
+    tok, slot = np.nonzero(d["topk_idx"] == small)
+    sub = dict(x=d["x"][tok], topk_idx=np.zeros((tok.size, 1), np.int32),
+               topk_w=d["topk_w"][tok, slot][:, None].copy(), w1=d["w1"][small:small + 1],
+               w2=d["w2"][small:small + 1], dy=d["dy"][tok])
+    rb, _ = _oracle(sub, 1)
+    assert rel_l2(bf16_host(run.g["dw1"][small]), rb["dW1"][0]) <= BWD_TOL
+    assert rel_l2(bf16_host(run.g["dw2"][small]), rb["dW2"][0]) <= BWD_TOL
+    for e in empty:
+        assert not run.g["dw1"][e].any() and not run.g["dw2"][e].any()
