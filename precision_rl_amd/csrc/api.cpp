@@ -259,10 +259,11 @@ size_t w4a4_workspace_size(int kind, int64_t T, int H, int I, int E, int k, int 
 
 namespace {
 // Argument checks shared by the two quantize+permute entry points.
+// `outer` is checked only when need_outer (the MXFP4 recipe has no outer scales).
 w4a4_status check_quantize_permute(const void* x, int64_t T, int K, const int32_t* topk_idx, int k,
                                    int E, int row_align, uint8_t* codes, uint8_t* scales,
                                    float* outer, int32_t* expert_offsets, int32_t* row_map,
-                                   int32_t* src_row) {
+                                   int32_t* src_row, bool need_outer = true) {
   if (T < 0) return fail(W4A4_ERR_INVALID_ARG, "T < 0");
   if (K < 16 || K % 16) return fail(W4A4_ERR_INVALID_ARG, "K=%d must be a positive multiple of 16", K);
   if (K > kMaxRowLen) return fail(W4A4_ERR_UNSUPPORTED, "K=%d > %d", K, kMaxRowLen);
@@ -281,7 +282,7 @@ w4a4_status check_quantize_permute(const void* x, int64_t T, int K, const int32_
     REQUIRE_PTR(x);
     REQUIRE_PTR(codes);
     REQUIRE_PTR(scales);
-    REQUIRE_PTR(outer);
+    if (need_outer) REQUIRE_PTR(outer);
     REQUIRE_PTR(row_map);
     REQUIRE_PTR(src_row);
   }
@@ -531,10 +532,8 @@ w4a4_status w4a4_mx_quantize_permute(const void* x, int64_t T, int K, const int3
                                      int32_t* row_map, int32_t* src_row, void* workspace,
                                      size_t workspace_bytes, void* stream) {
   g_last_error.clear();
-  // the NVFP4 checks with a stand-in for the absent outer scales
-  float* no_outer = reinterpret_cast<float*>(codes);
-  w4a4_status st = check_quantize_permute(x, T, K, topk_idx, k, E, row_align, codes, scales, no_outer,
-                                          expert_offsets, row_map, src_row);
+  w4a4_status st = check_quantize_permute(x, T, K, topk_idx, k, E, row_align, codes, scales, nullptr,
+                                          expert_offsets, row_map, src_row, /*need_outer=*/false);
   if (st != W4A4_OK) return st;
   if (K % 32 || K > 4096)
     return fail(W4A4_ERR_UNSUPPORTED, "MXFP4 rows need K %% 32 == 0 and K <= 4096 (K=%d)", K);
