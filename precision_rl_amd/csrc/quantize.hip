@@ -892,8 +892,8 @@ bool launch_quantize_permute_mx(const uint16_t* x, int64_t T, int K, const int32
   const int64_t n_chunks = (T + kRouteChunk - 1) / kRouteChunk;
   int32_t* counts = static_cast<int32_t*>(ws);
   int32_t* expert_count = counts + n_chunks * E;
-  if (T == 0) {
-    launch_kernel("route_scan", zero_offsets_kernel, dim3(1), dim3(256), 0, s, offsets, topk_idx ? E + 1 : 2);
+  if (T == 0) {   // every group empty; all E + 1 offsets (an empty routing tensor may arrive as NULL)
+    launch_kernel("route_scan", zero_offsets_kernel, dim3(1), dim3(256), 0, s, offsets, E + 1);
     return launch_ok("zero_offsets");
   }
   if (topk_idx != nullptr) {

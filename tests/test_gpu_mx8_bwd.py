@@ -188,3 +188,34 @@ def test_mx8_backward_full_skew_sampled():
     assert rel_l2(bf16_host(run.g["dw2"][small]), rb["dW2"][0]) <= BWD_TOL
     for e in empty:
         assert not run.g["dw1"][e].any() and not run.g["dw2"][e].any()
+
+
+def test_empty_batch_through_every_forward_and_backward():
+    """T = 0 through both forwards and both backwards, with padding rows
+    configured (row_align 16 / 128): every call succeeds, the offsets are all
+    zero and every weight gradient is exactly zero."""
+    b = _b()
+    H, E, k, I = 256, 8, 2, 256
+    rng = np.random.default_rng(3)
+    w1 = bf16_dev(q.f64_to_bf16_bits(rng.standard_normal((E, 2 * I, H)) * 0.02), torch)
+    w2 = bf16_dev(q.f64_to_bf16_bits(rng.standard_normal((E, H, I)) * 0.02), torch)
+    x = torch.empty(0, H, dtype=torch.bfloat16, device="cuda")
+    dy = torch.empty(0, H, dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty(0, k, dtype=torch.int32, device="cuda")
+    p = torch.empty(0, k, dtype=torch.float32, device="cuda")
+    print_case("empty_batch_all_paths", H=H, E=E, k=k, I=I)
+    for mx_fwd, bwd, align in ((False, "bf16", 16), (True, "bf16", 16), (False, "mxfp8", 128)):
+        if mx_fwd:
+            w1q, w2q = b.quantize_weights_mx(w1), b.quantize_weights_mx(w2)
+            xq = b.w4a4_mx_quantize_permute(x, idx, E, align)
+            f = b.w4a4_mx_grouped_expert_fwd(xq, p, w1q, w2q, 0, H, I, E, k, align, save=True)
+        else:
+            w1q, w2q = b.quantize_weights(w1), b.quantize_weights(w2)
+            xq = b.w4a4_quantize_permute(x, idx, E, align)
+            f = b.w4a4_grouped_expert_fwd(xq, p, w1q, w2q, 0, H, I, E, k, align, save=True)
+        call = b.w4a4_mx8_expert_bwd if bwd == "mxfp8" else b.w4a4_expert_bwd
+        g = call(dy, x, w1, w2, f["h"], f["a"], p, xq, 0, H, I, E, k, align)
+        torch.cuda.synchronize()
+        assert xq["offsets"].cpu().numpy().tolist() == [0] * (E + 1)
+        assert f["y"].shape == (0, H) and g["dx"].shape == (0, H)
+        assert not g["dw1"].any() and not g["dw2"].any()
