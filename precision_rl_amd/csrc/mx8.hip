@@ -12,7 +12,8 @@
 // the bf16 exponent field eb of the block amax the byte is max(eb - 8, 0).
 // x / 2^X is exact in FP32 (a bf16 value scaled by a power of two; results
 // below FP32's subnormal range lie far below E4M3's smallest midpoint), so the
-// rounding acts on the exact quotient.
+// rounding acts on the exact quotient.  The rounding itself is the
+// hardware's FP8 conversion (checked byte for byte against the oracle).
 
 #include <algorithm>
 
@@ -24,17 +25,7 @@ namespace {
 
 constexpr int kQ8Threads = 256;
 
-// E4M3FN byte of v >= 0 (finite), RNE, subnormals kept, saturating at 448.
-__device__ __forceinline__ uint32_t e4m3_of(float v) {
-  if (v >= 448.0f) return 0x7Eu;
-  if (v < 0.015625f)                                             // below 2^-6: spacing 2^-9
-    return static_cast<uint32_t>(__builtin_rintf(v * 512.0f));   // 0..8; 8 is 2^-6 = 0x08
-  const uint32_t b = __float_as_uint(v);
-  const uint32_t m3 = (b >> 20) & 7u, rem = b & 0xFFFFFu;
-  uint32_t r = ((((b >> 23) & 0xFFu) - 120u) << 3) | m3;         // biased exponent e + 7
-  if (rem > 0x80000u || (rem == 0x80000u && (m3 & 1u))) ++r;    // carries into the exponent
-  return r < 0x7Eu ? r : 0x7Eu;
-}
+typedef short short2_t __attribute__((ext_vector_type(2)));
 
 // Scale byte and 2^-X of a block from its amax (bf16 magnitude bits).
 __device__ __forceinline__ uint32_t mx8_scale_byte(uint32_t amax16) {
@@ -45,9 +36,18 @@ __device__ __forceinline__ float mx8_inv_scale(uint32_t byte) {
   return __uint_as_float((254u - byte) << 23);   // 2^(127 - byte) = 2^-X, X in [-127, 119]
 }
 
-__device__ __forceinline__ uint32_t e4m3_of_bf16(uint32_t x16, float inv) {
-  const float v = bf16_to_f32(static_cast<uint16_t>(x16 & 0x7FFFu)) * inv;
-  return e4m3_of(v) | ((x16 >> 8) & 0x80u);
+// E4M3FN bytes of two bf16 values x0, x1 scaled by inv (a power of two):
+// byte 0 from x0, byte 1 from x1.  The magnitudes |x| * inv are exact in FP32;
+// clamped to 448 they go through the hardware's OCP FP8 conversion (round to
+// nearest even, subnormals kept), which then never overflows: saturating
+// RNE of anything at or above 448 is 448.  The sign bits are copied from x
+// (-0 encodes as 0x80).
+__device__ __forceinline__ uint32_t e4m3_pair_of_bf16(uint32_t x0, uint32_t x1, float inv) {
+  const float v0 = fminf(bf16_to_f32(static_cast<uint16_t>(x0 & 0x7FFFu)) * inv, 448.0f);
+  const float v1 = fminf(bf16_to_f32(static_cast<uint16_t>(x1 & 0x7FFFu)) * inv, 448.0f);
+  const short2_t r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(short2_t{0, 0}, v0, v1, 1.0f, false);
+  const uint32_t m = static_cast<uint32_t>(static_cast<uint16_t>(r[0]));
+  return m | ((x0 >> 8) & 0x80u) | (x1 & 0x8000u);
 }
 
 // ---------------------------------------------------------- along columns
@@ -93,10 +93,9 @@ q8_cols_kernel(const uint16_t* __restrict__ x, int64_t R, int C, const int32_t* 
   u32x4_t o[2];
 #pragma unroll
   for (int r = 0; r < 32; r += 4) {
-    uint32_t wd = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) wd |= e4m3_of_bf16(col[(r + j) * kColPitch], inv) << (8 * j);
-    o[r >> 4][(r >> 2) & 3] = wd;
+    const uint32_t lo = e4m3_pair_of_bf16(col[r * kColPitch], col[(r + 1) * kColPitch], inv);
+    const uint32_t hi = e4m3_pair_of_bf16(col[(r + 2) * kColPitch], col[(r + 3) * kColPitch], inv);
+    o[r >> 4][(r >> 2) & 3] = lo | (hi << 16);
   }
   const int64_t cc = c0 + c;
   u32x4_t* dst = reinterpret_cast<u32x4_t*>(q + static_cast<int64_t>(mat) * C * pitch + cc * pitch + r0 + 32 * blk);
@@ -169,10 +168,9 @@ q8_dual_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ h, i
     u32x4_t o[2];
 #pragma unroll
     for (int r = 0; r < 32; r += 4) {
-      uint32_t wd = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) wd |= e4m3_of_bf16(col[(r + j) * kColPitch], inv) << (8 * j);
-      o[r >> 4][(r >> 2) & 3] = wd;
+      const uint32_t lo = e4m3_pair_of_bf16(col[r * kColPitch], col[(r + 1) * kColPitch], inv);
+      const uint32_t hi = e4m3_pair_of_bf16(col[(r + 2) * kColPitch], col[(r + 3) * kColPitch], inv);
+      o[r >> 4][(r >> 2) & 3] = lo | (hi << 16);
     }
     const int64_t cc = c0 + c;
     u32x4_t* dst = reinterpret_cast<u32x4_t*>(q_c + cc * pitch + r0 + 32 * blk);
@@ -196,9 +194,9 @@ q8_dual_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ h, i
     u32x4_t o[2];
 #pragma unroll
     for (int j = 0; j < 16; j += 2) {
-      const uint32_t b0 = e4m3_of_bf16(w[j] & 0xFFFFu, inv), b1 = e4m3_of_bf16(w[j] >> 16, inv);
-      const uint32_t b2 = e4m3_of_bf16(w[j + 1] & 0xFFFFu, inv), b3 = e4m3_of_bf16(w[j + 1] >> 16, inv);
-      o[j >> 3][(j >> 1) & 3] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+      const uint32_t lo = e4m3_pair_of_bf16(w[j] & 0xFFFFu, w[j] >> 16, inv);
+      const uint32_t hi = e4m3_pair_of_bf16(w[j + 1] & 0xFFFFu, w[j + 1] >> 16, inv);
+      o[j >> 3][(j >> 1) & 3] = lo | (hi << 16);
     }
     const int64_t r = r0 + lr;
     u32x4_t* dst = reinterpret_cast<u32x4_t*>(q_r + r * C + c0 + 32 * blk);
