@@ -358,7 +358,7 @@ w4a4_status w4a4_mx8_expert_bwd(
 /*
  * w4a4_mx8_quantize -- the MXFP8 operand quantiser of w4a4_mx8_expert_bwd as
  * a call of its own: both forms of a bf16 matrix from one read.
- *   x       [R, C] bf16, R % 128 == 0, C % 64 == 0.
+ *   x       [R, C] bf16, R % 128 == 0, C % 128 == 0.
  *   q_rows  [R, C] E4M3 bytes, s_rows [R, C/32] E8M0: blocks of 32 along rows.
  *   q_cols  [C, pitch] E4M3 bytes, s_cols [C, pitch/32] E8M0: column c of x
  *           in row c, blocks of 32 consecutive rows; pitch >= R, a multiple

@@ -670,8 +670,8 @@ w4a4_status w4a4_mx8_quantize(const void* x, int64_t R, int C, uint8_t* q_rows, 
                               uint8_t* s_cols, int64_t pitch, void* stream) {
   g_last_error.clear();
   if (R < 0 || C <= 0) return fail(W4A4_ERR_INVALID_ARG, "bad size (R=%lld C=%d)", static_cast<long long>(R), C);
-  if (R % 128 || C % 64)
-    return fail(W4A4_ERR_UNSUPPORTED, "needs R %% 128 == 0 and C %% 64 == 0 (R=%lld C=%d)",
+  if (R % 128 || C % 128)
+    return fail(W4A4_ERR_UNSUPPORTED, "needs R %% 128 == 0 and C %% 128 == 0 (R=%lld C=%d)",
                 static_cast<long long>(R), C);
   if (pitch < R || pitch % 128) return fail(W4A4_ERR_INVALID_ARG, "pitch must be >= R and a multiple of 128");
   if (R == 0) return W4A4_OK;

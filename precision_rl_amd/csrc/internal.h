@@ -96,7 +96,7 @@ bool launch_fc2_mx(int64_t rows_alloc, int H, int I, int E, const int32_t* offse
 // MXFP8 backward pieces.  Quantiser (E4M3 + E8M0 per 32) along columns of
 // `batch` [R, C] matrices into q [batch][C, pitch], s [batch][C, pitch/32]
 // (row blocks [0, offsets[E]) when given, in whole tiles of 128 rows;
-// C % 64 == 0, pitch % 128 == 0).
+// C % 128 == 0, pitch % 128 == 0).
 bool launch_q8_cols(const uint16_t* x, int64_t R, int C, int batch, const int32_t* offsets, int E,
                     int64_t pitch, uint8_t* q, uint8_t* s, const char* name, hipStream_t st);
 // Both forms of one [R, C] matrix from one read (rows [0, offsets[E]), whole

@@ -50,18 +50,64 @@ __device__ __forceinline__ uint32_t e4m3_pair_of_bf16(uint32_t x0, uint32_t x1, 
   return m | ((x0 >> 8) & 0x80u) | (x1 & 0x8000u);
 }
 
-// ---------------------------------------------------------- along columns
+// ------------------------------------------------------ column / row passes
+// Tiles of 128 rows x 128 columns go through LDS (each input row segment is
+// two 128-byte lines).  Along columns, four consecutive threads encode the
+// four 32-row blocks of one column, so that together they write its 128
+// output bytes as one line and its four scale bytes as one dword; along rows
+// (the dual pass), four consecutive threads encode the four 32-column blocks
+// of one row, likewise one line and one dword.
+constexpr int kColTileRows = 128, kColTileCols = 128;
+constexpr int kColPitch = kColTileCols + 2;   // elements; 2-way LDS conflicts at most on the column reads
+
+// The four scale bytes of lanes 4j .. 4j+3 (byte of lane 4j + b in bits 8b) in every one of them.
+__device__ __forceinline__ uint32_t gather4(uint32_t byte, int blk) {
+  uint32_t v = byte << (8 * blk);
+  v |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), 1, kWave));
+  v |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), 2, kWave));
+  return v;
+}
+
+// Encodes 32 values of the tile, `stride` elements apart from `p`: the E4M3
+// bytes into o[0..1], returns the scale byte.
+__device__ __forceinline__ uint32_t encode32(const uint16_t* p, int stride, u32x4_t (&o)[2]) {
+  uint32_t amax = 0;
+#pragma unroll
+  for (int r = 0; r < 32; ++r) amax = max(amax, static_cast<uint32_t>(p[r * stride] & 0x7FFFu));
+  const uint32_t byte = mx8_scale_byte(amax);
+  const float inv = mx8_inv_scale(byte);
+#pragma unroll
+  for (int r = 0; r < 32; r += 4) {
+    const uint32_t lo = e4m3_pair_of_bf16(p[r * stride], p[(r + 1) * stride], inv);
+    const uint32_t hi = e4m3_pair_of_bf16(p[(r + 2) * stride], p[(r + 3) * stride], inv);
+    o[r >> 4][(r >> 2) & 3] = lo | (hi << 16);
+  }
+  return byte;
+}
+
+// Along columns of the staged tile into q_c [C, pitch], s_c [C, pitch/32].
+__device__ __forceinline__ void tile_columns(const uint16_t* tile, int64_t r0, int c0, int64_t pitch, uint8_t* q_c,
+                                             uint8_t* s_c) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int task = t + 256 * i, c = task / 4, blk = task % 4;
+    u32x4_t o[2];
+    const uint32_t byte = encode32(tile + (32 * blk) * kColPitch + c, kColPitch, o);
+    const int64_t cc = c0 + c;
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(q_c + cc * pitch + r0 + 32 * blk);
+    __builtin_nontemporal_store(o[0], dst);
+    __builtin_nontemporal_store(o[1], dst + 1);
+    const uint32_t four = gather4(byte, blk);
+    if (blk == 0) *reinterpret_cast<uint32_t*>(s_c + cc * (pitch / 32) + r0 / 32) = four;
+  }
+}
+
 // x: `batch` matrices [R, C] bf16 (batch stride R*C).  Output per matrix:
 // q [C, pitch] E4M3 (row c holds column c of x, quantised in blocks of 32
-// consecutive rows), s [C, pitch/32].  A workgroup takes 128 rows x 64
-// columns through LDS (each input row segment is one 128-byte line); four
-// consecutive threads encode the four 32-row blocks of one column, so that
-// together they write the column's 128 output bytes as one line.  Row tiles
-// at or past offsets[E] (when given) are skipped: the rows encoded must come
-// in whole tiles of 128 (row_align 128 for dispatched rows; R % 128 == 0
-// for weights).
-constexpr int kColTileRows = 128, kColTileCols = 64;
-constexpr int kColPitch = kColTileCols + 2;   // elements; 2-way LDS conflicts at most on the column reads
+// consecutive rows), s [C, pitch/32].  Row tiles at or past offsets[E] (when
+// given) are skipped: the rows encoded must come in whole tiles of 128
+// (row_align 128 for dispatched rows; R % 128 == 0 for weights).
 __global__ void __launch_bounds__(kQ8Threads)
 q8_cols_kernel(const uint16_t* __restrict__ x, int64_t R, int C, const int32_t* __restrict__ offsets, int E,
                int64_t pitch, uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
@@ -73,47 +119,28 @@ q8_cols_kernel(const uint16_t* __restrict__ x, int64_t R, int C, const int32_t* 
   if (r0 >= rlim) return;
   const uint16_t* xm = x + static_cast<int64_t>(mat) * R * C;
   const int t = threadIdx.x;
-  // load: thread t moves the 16-byte chunk t % 8 of rows t / 8 + 32 i
+  // load: thread t moves the 16-byte chunk t % 16 of rows t / 16 + 16 i
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int lr = t / 8 + 32 * i, ch = t % 8;
+  for (int i = 0; i < 8; ++i) {
+    const int lr = t / 16 + 16 * i, ch = t % 16;
     const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(xm + (r0 + lr) * C + c0 + ch * 8));
     uint32_t* dst = reinterpret_cast<uint32_t*>(tile + lr * kColPitch + ch * 8);
 #pragma unroll
     for (int d = 0; d < 4; ++d) dst[d] = v[d];
   }
   __syncthreads();
-  const int c = t / 4, blk = t % 4;
-  const uint16_t* col = tile + (32 * blk) * kColPitch + c;
-  uint32_t amax = 0;
-#pragma unroll
-  for (int r = 0; r < 32; ++r) amax = max(amax, static_cast<uint32_t>(col[r * kColPitch] & 0x7FFFu));
-  const uint32_t byte = mx8_scale_byte(amax);
-  const float inv = mx8_inv_scale(byte);
-  u32x4_t o[2];
-#pragma unroll
-  for (int r = 0; r < 32; r += 4) {
-    const uint32_t lo = e4m3_pair_of_bf16(col[r * kColPitch], col[(r + 1) * kColPitch], inv);
-    const uint32_t hi = e4m3_pair_of_bf16(col[(r + 2) * kColPitch], col[(r + 3) * kColPitch], inv);
-    o[r >> 4][(r >> 2) & 3] = lo | (hi << 16);
-  }
-  const int64_t cc = c0 + c;
-  u32x4_t* dst = reinterpret_cast<u32x4_t*>(q + static_cast<int64_t>(mat) * C * pitch + cc * pitch + r0 + 32 * blk);
-  __builtin_nontemporal_store(o[0], dst);
-  __builtin_nontemporal_store(o[1], dst + 1);
-  s[(static_cast<int64_t>(mat) * C + cc) * (pitch / 32) + r0 / 32 + blk] = static_cast<uint8_t>(byte);
+  tile_columns(tile, r0, c0, pitch, q + static_cast<int64_t>(mat) * C * pitch,
+               s + static_cast<int64_t>(mat) * C * (pitch / 32));
 }
 
 // ------------------------------------------------- both axes in one pass
 // The two MXFP8 forms of one [R, C] bf16 matrix from a single read: along
 // rows (q_r [R, C], s_r [R, C/32], the dgrad operand) and along columns
-// (q_c [C, pitch], s_c [C, pitch/32], the wgrad operand).  Same 128 x 64
-// tile as q8_cols_kernel; thread t also encodes row t / 2's 32-column block
-// t % 2 of the tile.  SWIGLU: the matrix is dH [R, 2I], computed in the load
-// from dA [R, I] and the saved h [R, 2I] (the SwiGLU backward's formula and
-// FP32 arithmetic, bf16-rounded as the BF16 path stores dH), so dH itself is
-// never written.  Row tiles at or past offsets[E] (when given; else R, a
-// multiple of 128) are skipped.
+// (q_c [C, pitch], s_c [C, pitch/32], the wgrad operand).  SWIGLU: the
+// matrix is dH [R, 2I], computed in the load from dA [R, I] and the saved h
+// [R, 2I] (the SwiGLU backward's formula and FP32 arithmetic, bf16-rounded as
+// the BF16 path stores dH), so dH itself is never written.  Row tiles at or
+// past offsets[E] (when given; else R, a multiple of 128) are skipped.
 template <bool SWIGLU>
 __global__ void __launch_bounds__(kQ8Threads)
 q8_dual_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ h, int64_t R, int C, int I,
@@ -125,14 +152,14 @@ q8_dual_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ h, i
   if (r0 >= (offsets != nullptr ? min<int64_t>(R, offsets[E]) : R)) return;
   const int t = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int lr = t / 8 + 32 * i, ch = t % 8;
+  for (int i = 0; i < 8; ++i) {
+    const int lr = t / 16 + 16 * i, ch = t % 16;
     const int64_t r = r0 + lr;
     u32x4_t v;
     if constexpr (!SWIGLU) {
       v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + r * C + c0 + ch * 8));
     } else {
-      const bool gate_half = c0 < I;                 // a tile lies in one half (I % 64 == 0)
+      const bool gate_half = c0 < I;                 // a tile lies in one half (I % 128 == 0)
       const int i0 = (gate_half ? c0 : c0 - I) + ch * 8;
       const u32x4_t da = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + r * I + i0));
       const u32x4_t hg = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(h + r * (2 * I) + i0));
@@ -156,53 +183,19 @@ q8_dual_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ h, i
     for (int d = 0; d < 4; ++d) dst[d] = v[d];
   }
   __syncthreads();
-  // along columns: thread (column t / 4, 32-row block t % 4)
-  {
-    const int c = t / 4, blk = t % 4;
-    const uint16_t* col = tile + (32 * blk) * kColPitch + c;
-    uint32_t amax = 0;
+  tile_columns(tile, r0, c0, pitch, q_c, s_c);
+  // along rows: thread (row task / 4, 32-column block task % 4)
 #pragma unroll
-    for (int r = 0; r < 32; ++r) amax = max(amax, static_cast<uint32_t>(col[r * kColPitch] & 0x7FFFu));
-    const uint32_t byte = mx8_scale_byte(amax);
-    const float inv = mx8_inv_scale(byte);
+  for (int i = 0; i < 2; ++i) {
+    const int task = t + 256 * i, lr = task / 4, blk = task % 4;
     u32x4_t o[2];
-#pragma unroll
-    for (int r = 0; r < 32; r += 4) {
-      const uint32_t lo = e4m3_pair_of_bf16(col[r * kColPitch], col[(r + 1) * kColPitch], inv);
-      const uint32_t hi = e4m3_pair_of_bf16(col[(r + 2) * kColPitch], col[(r + 3) * kColPitch], inv);
-      o[r >> 4][(r >> 2) & 3] = lo | (hi << 16);
-    }
-    const int64_t cc = c0 + c;
-    u32x4_t* dst = reinterpret_cast<u32x4_t*>(q_c + cc * pitch + r0 + 32 * blk);
-    __builtin_nontemporal_store(o[0], dst);
-    __builtin_nontemporal_store(o[1], dst + 1);
-    s_c[cc * (pitch / 32) + r0 / 32 + blk] = static_cast<uint8_t>(byte);
-  }
-  // along rows: thread (row t / 2, 32-column block t % 2)
-  {
-    const int lr = t / 2, blk = t % 2;
-    const uint32_t* rowp = reinterpret_cast<const uint32_t*>(tile + lr * kColPitch + 32 * blk);
-    uint32_t w[16];
-    uint32_t amax = 0;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      w[j] = rowp[j];
-      amax = max(amax, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
-    }
-    const uint32_t byte = mx8_scale_byte(amax);
-    const float inv = mx8_inv_scale(byte);
-    u32x4_t o[2];
-#pragma unroll
-    for (int j = 0; j < 16; j += 2) {
-      const uint32_t lo = e4m3_pair_of_bf16(w[j] & 0xFFFFu, w[j] >> 16, inv);
-      const uint32_t hi = e4m3_pair_of_bf16(w[j + 1] & 0xFFFFu, w[j + 1] >> 16, inv);
-      o[j >> 3][(j >> 1) & 3] = lo | (hi << 16);
-    }
+    const uint32_t byte = encode32(tile + lr * kColPitch + 32 * blk, 1, o);
     const int64_t r = r0 + lr;
     u32x4_t* dst = reinterpret_cast<u32x4_t*>(q_r + r * C + c0 + 32 * blk);
     __builtin_nontemporal_store(o[0], dst);
     __builtin_nontemporal_store(o[1], dst + 1);
-    s_r[r * (C / 32) + c0 / 32 + blk] = static_cast<uint8_t>(byte);
+    const uint32_t four = gather4(byte, blk);
+    if (blk == 0) *reinterpret_cast<uint32_t*>(s_r + r * (C / 32) + c0 / 32) = four;
   }
 }
 
@@ -219,8 +212,8 @@ bool launch_q8_cols(const uint16_t* x, int64_t R, int C, int batch, const int32_
   if (R == 0 || batch == 0) return true;
   if (C % kColTileCols || pitch % 128) return false;
   if (offsets == nullptr && R % kColTileRows) return false;
-  const dim3 grid(static_cast<unsigned>(R / kColTileRows), static_cast<unsigned>(C / kColTileCols),
-                  static_cast<unsigned>(batch));
+  const dim3 grid(static_cast<unsigned>((R + kColTileRows - 1) / kColTileRows),
+                  static_cast<unsigned>(C / kColTileCols), static_cast<unsigned>(batch));
   launch_kernel(name, q8_cols_kernel, grid, dim3(kQ8Threads), 0, st, x, R, C, offsets, E, pitch, q, s);
   return launch_ok(name);
 }
@@ -229,7 +222,7 @@ bool launch_q8_dual(const uint16_t* x, const uint16_t* h, int64_t R, int C, int 
                     int64_t pitch, uint8_t* q_r, uint8_t* s_r, uint8_t* q_c, uint8_t* s_c, const char* name,
                     hipStream_t st) {
   if (R == 0) return true;
-  if (C % kColTileCols || pitch % 128 || (h != nullptr && (C != 2 * I || I % kColTileCols))) return false;
+  if (C % kColTileCols || pitch % 128 || (h != nullptr && (C != 2 * I || I % kColTileCols))) return false;   // C % 128
   if (offsets == nullptr && R % kColTileRows) return false;
   const dim3 grid(static_cast<unsigned>((R + kColTileRows - 1) / kColTileRows),
                   static_cast<unsigned>(C / kColTileCols));

@@ -150,10 +150,10 @@ def test_mx8_backward_rejects_invalid_arguments_before_launch():
     assert bwd(H=250) == -1
     assert lib.w4a4_workspace_size(5, 64, 256, 256, 8, 2, 128) > lib.w4a4_workspace_size(2, 64, 256, 256, 8, 2, 128)
 
-    def q8(R=128, C=64, pitch=128, x=p):
+    def q8(R=128, C=128, pitch=128, x=p):
         return lib.w4a4_mx8_quantize(x, R, C, p, p, p, p, pitch, None)
 
     assert q8(R=96) == -2                              # whole 128-row tiles
-    assert q8(C=32) == -2
+    assert q8(C=64) == -2                              # C % 128
     assert q8(pitch=64) == -1                          # pitch >= R
     assert q8(x=None) == -1
