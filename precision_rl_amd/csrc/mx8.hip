@@ -134,57 +134,13 @@ q8_cols_kernel(const uint16_t* __restrict__ x, int64_t R, int C, const int32_t* 
 }
 
 // ------------------------------------------------- both axes in one pass
-// The two MXFP8 forms of one [R, C] bf16 matrix from a single read: along
-// rows (q_r [R, C], s_r [R, C/32], the dgrad operand) and along columns
-// (q_c [C, pitch], s_c [C, pitch/32], the wgrad operand).  SWIGLU: the
-// matrix is dH [R, 2I], computed in the load from dA [R, I] and the saved h
-// [R, 2I] (the SwiGLU backward's formula and FP32 arithmetic, bf16-rounded as
-// the BF16 path stores dH), so dH itself is never written.  Row tiles at or
-// past offsets[E] (when given; else R, a multiple of 128) are skipped.
-template <bool SWIGLU>
-__global__ void __launch_bounds__(kQ8Threads)
-q8_dual_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ h, int64_t R, int C, int I,
-               const int32_t* __restrict__ offsets, int E, int64_t pitch, uint8_t* __restrict__ q_r,
-               uint8_t* __restrict__ s_r, uint8_t* __restrict__ q_c, uint8_t* __restrict__ s_c) {
-  __shared__ uint16_t tile[kColTileRows * kColPitch];
-  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kColTileRows;
-  const int c0 = blockIdx.y * kColTileCols;
-  if (r0 >= (offsets != nullptr ? min<int64_t>(R, offsets[E]) : R)) return;
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int lr = t / 16 + 16 * i, ch = t % 16;
-    const int64_t r = r0 + lr;
-    u32x4_t v;
-    if constexpr (!SWIGLU) {
-      v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + r * C + c0 + ch * 8));
-    } else {
-      const bool gate_half = c0 < I;                 // a tile lies in one half (I % 128 == 0)
-      const int i0 = (gate_half ? c0 : c0 - I) + ch * 8;
-      const u32x4_t da = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + r * I + i0));
-      const u32x4_t hg = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(h + r * (2 * I) + i0));
-      const u32x4_t hu = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(h + r * (2 * I) + I + i0));
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        float o2[2];
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const float a = bf16_to_f32(static_cast<uint16_t>(da[d] >> (16 * p)));
-          const float gt = bf16_to_f32(static_cast<uint16_t>(hg[d] >> (16 * p)));
-          const float up = bf16_to_f32(static_cast<uint16_t>(hu[d] >> (16 * p)));
-          const float sg = sigmoid_fast(gt);
-          o2[p] = gate_half ? a * up * sg * (1.0f + gt * (1.0f - sg)) : a * gt * sg;
-        }
-        v[d] = pack_bf16x2(o2[0], o2[1]);
-      }
-    }
-    uint32_t* dst = reinterpret_cast<uint32_t*>(tile + lr * kColPitch + ch * 8);
-#pragma unroll
-    for (int d = 0; d < 4; ++d) dst[d] = v[d];
-  }
-  __syncthreads();
+// Both MXFP8 forms of the staged tile (columns [c0, c0 + 128) of an [R, C]
+// matrix): along columns, and along rows (four consecutive threads: one
+// row's four 32-column blocks, one 128-byte line and one 4-byte scale store).
+__device__ __forceinline__ void tile_both(const uint16_t* tile, int64_t r0, int c0, int C, int64_t pitch,
+                                          uint8_t* q_r, uint8_t* s_r, uint8_t* q_c, uint8_t* s_c) {
   tile_columns(tile, r0, c0, pitch, q_c, s_c);
-  // along rows: thread (row task / 4, 32-column block task % 4)
+  const int t = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int task = t + 256 * i, lr = task / 4, blk = task % 4;
@@ -196,6 +152,80 @@ q8_dual_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ h, i
     __builtin_nontemporal_store(o[1], dst + 1);
     const uint32_t four = gather4(byte, blk);
     if (blk == 0) *reinterpret_cast<uint32_t*>(s_r + r * (C / 32) + c0 / 32) = four;
+  }
+}
+
+__device__ __forceinline__ void tile_store(uint16_t* tile, int lr, int ch, const u32x4_t& v) {
+  uint32_t* dst = reinterpret_cast<uint32_t*>(tile + lr * kColPitch + ch * 8);
+#pragma unroll
+  for (int d = 0; d < 4; ++d) dst[d] = v[d];
+}
+
+// The two MXFP8 forms of one [R, C] bf16 matrix from a single read: along
+// rows (q_r [R, C], s_r [R, C/32], the dgrad operand) and along columns
+// (q_c [C, pitch], s_c [C, pitch/32], the wgrad operand).  SWIGLU: the
+// matrix is dH [R, 2I] = [dgate | dup], computed in the load from dA [R, I]
+// and the saved h [R, 2I] (the SwiGLU backward's formula and FP32
+// arithmetic, bf16-rounded as the BF16 path stores dH), so dH itself is never
+// written; a workgroup takes the gate-half tile at c0 and the up-half tile at
+// I + c0, which read the same dA and h columns, from one read (two LDS tiles,
+// 66.5 KB: two workgroups per CU).  Row tiles at
+// or past offsets[E] (when given; else R, a multiple of 128) are skipped.
+constexpr int kTileElems = kColTileRows * kColPitch;
+template <bool SWIGLU>
+constexpr uint32_t dual_lds_bytes() { return (SWIGLU ? 2 : 1) * kTileElems * sizeof(uint16_t); }
+
+template <bool SWIGLU>
+__global__ void __launch_bounds__(kQ8Threads)
+q8_dual_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ h, int64_t R, int C, int I,
+               const int32_t* __restrict__ offsets, int E, int64_t pitch, uint8_t* __restrict__ q_r,
+               uint8_t* __restrict__ s_r, uint8_t* __restrict__ q_c, uint8_t* __restrict__ s_c) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t tile[];   // SWIGLU: gate tile, then up tile
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kColTileRows;
+  const int c0 = blockIdx.y * kColTileCols;
+  if (r0 >= (offsets != nullptr ? min<int64_t>(R, offsets[E]) : R)) return;
+  const int t = threadIdx.x;
+  if constexpr (!SWIGLU) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int lr = t / 16 + 16 * i, ch = t % 16;
+      tile_store(tile, lr, ch,
+                 __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + (r0 + lr) * C + c0 + ch * 8)));
+    }
+    __syncthreads();
+    tile_both(tile, r0, c0, C, pitch, q_r, s_r, q_c, s_c);
+  } else {
+    uint16_t* tile_u = tile + kTileElems;
+#pragma unroll 2
+    for (int i = 0; i < 8; ++i) {
+      const int lr = t / 16 + 16 * i, ch = t % 16;
+      const int64_t r = r0 + lr;
+      const int i0 = c0 + ch * 8;   // feature index in [0, I)
+      const u32x4_t da = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + r * I + i0));
+      const u32x4_t hg = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(h + r * (2 * I) + i0));
+      const u32x4_t hu = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(h + r * (2 * I) + I + i0));
+      u32x4_t vg, vu;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        float g2[2], u2[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const float a = bf16_to_f32(static_cast<uint16_t>(da[d] >> (16 * p)));
+          const float gt = bf16_to_f32(static_cast<uint16_t>(hg[d] >> (16 * p)));
+          const float up = bf16_to_f32(static_cast<uint16_t>(hu[d] >> (16 * p)));
+          const float sg = sigmoid_fast(gt);
+          g2[p] = a * up * sg * (1.0f + gt * (1.0f - sg));
+          u2[p] = a * gt * sg;
+        }
+        vg[d] = pack_bf16x2(g2[0], g2[1]);
+        vu[d] = pack_bf16x2(u2[0], u2[1]);
+      }
+      tile_store(tile, lr, ch, vg);
+      tile_store(tile_u, lr, ch, vu);
+    }
+    __syncthreads();
+    tile_both(tile, r0, c0, C, pitch, q_r, s_r, q_c, s_c);
+    tile_both(tile_u, r0, I + c0, C, pitch, q_r, s_r, q_c, s_c);
   }
 }
 
@@ -224,14 +254,20 @@ bool launch_q8_dual(const uint16_t* x, const uint16_t* h, int64_t R, int C, int 
   if (R == 0) return true;
   if (C % kColTileCols || pitch % 128 || (h != nullptr && (C != 2 * I || I % kColTileCols))) return false;   // C % 128
   if (offsets == nullptr && R % kColTileRows) return false;
+  // SWIGLU: one workgroup per gate-half tile (it also writes the up-half tile)
   const dim3 grid(static_cast<unsigned>((R + kColTileRows - 1) / kColTileRows),
-                  static_cast<unsigned>(C / kColTileCols));
-  if (h == nullptr)
-    launch_kernel(name, q8_dual_kernel<false>, grid, dim3(kQ8Threads), 0, st, x, h, R, C, I, offsets, E, pitch, q_r,
-                  s_r, q_c, s_c);
-  else
-    launch_kernel(name, q8_dual_kernel<true>, grid, dim3(kQ8Threads), 0, st, x, h, R, C, I, offsets, E, pitch, q_r,
-                  s_r, q_c, s_c);
+                  static_cast<unsigned>((h == nullptr ? C : I) / kColTileCols));
+  if (h == nullptr) {
+    launch_kernel(name, q8_dual_kernel<false>, grid, dim3(kQ8Threads), dual_lds_bytes<false>(), st, x, h, R, C, I,
+                  offsets, E, pitch, q_r, s_r, q_c, s_c);
+  } else {
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&q8_dual_kernel<true>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       dual_lds_bytes<true>());
+    if (attr != hipSuccess) return launch_ok(name) && false;
+    launch_kernel(name, q8_dual_kernel<true>, grid, dim3(kQ8Threads), dual_lds_bytes<true>(), st, x, h, R, C, I,
+                  offsets, E, pitch, q_r, s_r, q_c, s_c);
+  }
   return launch_ok(name);
 }
 
