@@ -411,3 +411,21 @@ def test_graph_capture_of_a_learner_step():
         del noise
         for j, (a, e) in enumerate(zip(out, eager)):
             assert torch.equal(a, e), (i, j)
+
+
+def test_requant_bit_exact_on_the_gpus_own_a():
+    """The FC2-input requantisation equals the oracle quantiser applied to
+    the bf16 a the GPU itself saved, bit for bit: codes, E4M3 scales and
+    FP32 outer scales of every dispatched row (the tolerance-checked
+    comparison with the FP64 forward allows flips only where a itself
+    differs by an ulp)."""
+    T, H, E, k, I = 512, 512, 8, 4, 768
+    d = synth.make_inputs(T, H, E, k, I, seed=31)
+    print_case("requant_bit_exact", T=T, H=H, E=E, k=k, I=I)
+    run = Run(d, T, H, E, k, I, A=16)
+    rows = run.rows
+    a = bf16_host(run.f["a"])[:rows]
+    c, s, g = q.quantize_rows(a)
+    assert np.array_equal(u8(run.f["a_codes"])[:rows], q.pack_codes(c))
+    assert np.array_equal(u8(run.f["a_scales"])[:rows], s)
+    assert np.array_equal(f32_bits(run.f["a_outer"])[:rows], g.view(np.uint32))

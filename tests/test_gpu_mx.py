@@ -262,3 +262,17 @@ def test_mx_forward_full_skew_sampled():
     gc = q.unpack_codes(u8(run.f["a_codes"])[rows_gpu])
     assert np.mean(gc != ref["a_codes"][rows_ref]) <= CODE_FLIP_BUDGET
     assert rel_l2(bf16_host(run.f["y"])[sample], ref["y"]) <= Y_TOL
+
+
+def test_mx_requant_bit_exact_on_the_gpus_own_a():
+    """The MXFP4 FC2-input requantisation equals the oracle's MXFP4 of the
+    bf16 a the GPU saved, bit for bit (codes and E8M0 scales)."""
+    T, H, E, k, I = 512, 512, 8, 4, 768
+    d = synth.make_inputs(T, H, E, k, I, seed=31)
+    print_case("mx_requant_bit_exact", T=T, H=H, E=E, k=k, I=I)
+    run = MxRun(d, T, H, E, k, I, A=16)
+    rows = run.rows
+    a = bf16_host(run.f["a"])[:rows]
+    c, s = mx.quantize_rows_mx(a)
+    assert np.array_equal(u8(run.f["a_codes"])[:rows], q.pack_codes(c))
+    assert np.array_equal(u8(run.f["a_scales"])[:rows], s)
