@@ -488,7 +488,10 @@ enum class RowMode { Scatter, Identity, Requant };
 // block with an E8M0 scale 2^X, X = floor(log2 amax) - 2 clamped to
 // [-127, 127] (OCP Microscaling v1.0, section 6.3), codes Q_E2M1(x / 2^X);
 // one scale byte per 32 elements, no outer scale.
-template <int TEAM, int PB, RowMode MODE, bool MX = false>
+// PF: load the wave's next row group while encoding the current one.  Worth
+// it only when the waves stride over several row groups; without it the
+// second row buffer's registers are free and more waves fit on a SIMD.
+template <int TEAM, int PB, RowMode MODE, bool MX = false, bool PF = true>
 __global__ void __launch_bounds__(kThreads)
 quant_rows_kernel(const uint16_t* __restrict__ x, int64_t n_rows, int K,
                   const int32_t* __restrict__ topk_idx, int k, int E,
@@ -520,7 +523,8 @@ quant_rows_kernel(const uint16_t* __restrict__ x, int64_t n_rows, int K,
   };
   if (r < n) load(r, cur);
   for (; r < n; r += stride) {
-    if (r + stride < n) load(r + stride, nxt);
+    if constexpr (PF)
+      if (r + stride < n) load(r + stride, nxt);
 
     // block amaxes; row amax over the team (NVFP4 only)
     uint32_t bm[PB][2];
@@ -628,10 +632,14 @@ quant_rows_kernel(const uint16_t* __restrict__ x, int64_t n_rows, int K,
         if (tl == j) d = dst[j];
       outer[d] = g;
     }
+    if constexpr (PF) {
 #pragma unroll
-    for (int i = 0; i < PB; ++i)
+      for (int i = 0; i < PB; ++i)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) cur[i][q] = nxt[i][q];
+        for (int q = 0; q < 4; ++q) cur[i][q] = nxt[i][q];
+    } else if (r + stride < n) {
+      load(r + stride, cur);
+    }
   }
 }
 
@@ -678,7 +686,11 @@ bool launch_rows(const char* name, const uint16_t* x, int64_t n_rows, int K, con
     const int64_t need = (n_rows + rows_per_block - 1) / rows_per_block;
     const int64_t blocks = std::min<int64_t>(need, static_cast<int64_t>(device_cu_count()) * 16);
     if (blocks == 0) return true;
-    launch_kernel(name, quant_rows_kernel<TEAM, PB, MODE, MX>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+    // Requant bounds its rows by offsets[E] on the device: n_rows is the
+    // allocation, an upper bound, so the choice is made on that bound.
+    auto kernel = need > blocks ? quant_rows_kernel<TEAM, PB, MODE, MX, true>
+                                : quant_rows_kernel<TEAM, PB, MODE, MX, false>;
+    launch_kernel(name, kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
                   s, x, n_rows, K, topk_idx, k, E, codes, scales, outer, offsets, row_map, src_row, chunk_base,
                   group_amax, group_rows);
     return launch_ok(name);
