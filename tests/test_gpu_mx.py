@@ -264,11 +264,14 @@ def test_mx_forward_full_skew_sampled():
     assert rel_l2(bf16_host(run.f["y"])[sample], ref["y"]) <= Y_TOL
 
 
-def test_mx_requant_bit_exact_on_the_gpus_own_a():
+@pytest.mark.parametrize("T,H,E,k,seed", [(512, 512, 8, 4, 31), (16500, 256, 16, 8, 32)])
+def test_mx_requant_bit_exact_on_the_gpus_own_a(T, H, E, k, seed):
     """The MXFP4 FC2-input requantisation equals the oracle's MXFP4 of the
-    bf16 a the GPU saved, bit for bit (codes and E8M0 scales)."""
-    T, H, E, k, I = 512, 512, 8, 4, 768
-    d = synth.make_inputs(T, H, E, k, I, seed=31)
+    bf16 a the GPU saved, bit for bit (codes and E8M0 scales).  The second
+    case has more rows than 16 workgroups per CU take in one pass, so the
+    encoder's waves stride over a second row group."""
+    I = 768
+    d = synth.make_inputs(T, H, E, k, I, seed=seed)
     print_case("mx_requant_bit_exact", T=T, H=H, E=E, k=k, I=I)
     run = MxRun(d, T, H, E, k, I, A=16)
     rows = run.rows

@@ -100,6 +100,33 @@ def test_quantize_permute_full_qp_workload():
     _compare_qp(d, w.E, 1, got)
 
 
+@pytest.mark.parametrize("recipe", ["nvfp4", "mxfp4"])
+def test_quantize_permute_waves_striding_over_row_groups(recipe):
+    """More tokens than 16 workgroups per CU cover at one row per team
+    (T=20000 rows of 33 block pairs, 4 rows per workgroup, 5000 > 16 x 256
+    workgroups): the encoder's waves take a second row group, loading it
+    while they encode the first.  Bit-exact like the one-pass launches."""
+    b = _binding()
+    T, H, E, k = 20000, 1056, 64, 4
+    d = synth.make_inputs(T, H, E, k, routing="zipf", x_dist="t3", seed=2024, weights=False, n_empty=3)
+    print_case("quantize_permute_striding", T=T, H=H, E=E, k=k, recipe=recipe)
+    x, idx = bf16_dev(d["x"], torch), torch.from_numpy(d["topk_idx"]).cuda()
+    if recipe == "nvfp4":
+        got = b.w4a4_quantize_permute(x, idx, E, 1)
+        torch.cuda.synchronize()
+        _compare_qp(d, E, 1, got)
+        return
+    got = b.w4a4_mx_quantize_permute(x, idx, E, 1)
+    torch.cuda.synchronize()
+    ref = moe.quantize_permute_mx(q.bf16_bits_to_f64(d["x"]), d["topk_idx"], E, 1)
+    rows = int(ref["offsets"][-1])
+    assert np.array_equal(got["offsets"].cpu().numpy(), ref["offsets"])
+    assert np.array_equal(got["row_map"].cpu().numpy(), ref["row_map"])
+    assert np.array_equal(got["src_row"].cpu().numpy()[:rows], ref["src_row"])
+    assert np.array_equal(u8(got["codes"])[:rows], ref["packed"])
+    assert np.array_equal(u8(got["scales"])[:rows], ref["scales"])
+
+
 @pytest.mark.parametrize("name", ["w1_g_exactly_one.txt", "w2_g_rounds_up.txt",
                                   "p6_e4m3_edges.txt"])
 def test_golden_rows_on_gpu(name):
