@@ -8,11 +8,21 @@ grouped expert forward (FC1 + SwiGLU, requantise, FC2, unpermute; h and a
 saved) and the straight-through BF16 backward (dX, dW1, dW2).  Weights are
 quantised once before timing (offline, as on the pages).
 
-Prints ONE JSON line.  `value` is tokens/s of the whole step; `roofline`
-reports the dominant kernel (by total time in the timed region, among the
-kernels that do not run beside another on the second stream) against its
-bound, from HIP events recorded around each library launch on the launch
-stream; `cpu_baseline` times the FP64 oracle on a bounded sample on the host.
+Timing: W warm-up steps, then K reps, each preceded by a write of a 1 GiB
+scratch buffer (evicting the L2s and the 256 MB MALL) and bracketed by HIP
+events on the caller's stream; `value` = T / the median rep, with min, max
+and mean beside it.  Per-kernel times come from a second pass of the same
+flushed reps with the library's per-launch timing on (events attached to the
+dispatches on the launch stream), so those events stay out of the measured
+reps.
+
+Prints ONE JSON line.  `value` is tokens/s of the learner step; `roofline`
+reports the dominant kernel (by total time, among the kernels that do not
+run beside another on the second stream) against its bound; `configs` holds
+the other layer configurations timed the same way (quantize+permute alone on
+Student-t activations, the forward at T=8192, the skewed routing at
+T=32768 forward and forward + backward), each with its own roofline;
+`cpu_baseline` times the FP64 oracle on a bounded sample on the host.
 """
 import argparse
 import hashlib
@@ -99,8 +109,7 @@ def algorithmic_work(T, H, E, k, I):
 
 # Kernels the library runs concurrently with another one (second stream).
 CONCURRENT = {"wgrad_schedule": "dy_scatter, gemm_dgrad_fc2",
-              "x_scatter": "gemm_wgrad_fc2, gemm_dgrad_fc1",
-              "dx_gather_sum": "gemm_wgrad_fc1"}
+              "x_scatter": "gemm_wgrad_fc2, gemm_dgrad_fc1"}
 
 
 def source_hash(name):
@@ -196,7 +205,9 @@ def main_linear(args):
         b.w4a4_linear_fwd(xq, wq, T, K, N, y=y)
         b.w4a4_linear_bwd(dy, x, W, xq, T, K, N, out=grads, workspace=ws_b)
 
-    ms, kern = time_steps(b, torch, step, args)
+    flush = Flusher(torch, dev)
+    st, kern = time_steps(b, torch, step, args, flush, "linear step")
+    ms = st["median"]
     fl, by = linear_work(T, K, N)
     per_kernel, roof = summarize(kern, ms, args.steps, fl, by, concurrent={})
     out = {
@@ -207,6 +218,7 @@ def main_linear(args):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "timing": time_fields(st, args.steps),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -296,7 +308,9 @@ def main_qp(args):
         else:
             b.w4a4_quantize_permute(x, idx, E, 1, out=xq, workspace=ws)
 
-    ms, kern = time_steps(b, torch, step, args)
+    flush = Flusher(torch, dev)
+    st, kern = time_steps(b, torch, step, args, flush, "quantize+permute")
+    ms = st["median"]
     fl, by = qp_work(T, H, k, args.outer, args.recipe)
     per_kernel, roof = summarize(kern, ms, args.steps, fl, by, concurrent={})
     alg = sum(by.values()) - by.get("group_amax", 0)
@@ -308,6 +322,7 @@ def main_qp(args):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "timing": time_fields(st, args.steps),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -373,27 +388,74 @@ def calibration_copy(torch, dev):
     del calib, calib_out
 
 
-def time_steps(b, torch, step, args):
-    """W untimed warm-up steps, then K timed steps between synchronisations,
-    with the library's per-launch profiler on.  Returns (ms per step, the
-    profiler's per-kernel record)."""
-    for _ in range(args.warmup):
+FLUSH_BYTES = 1 << 30   # > the 256 MB MALL plus every XCD's 4 MB L2
+
+
+class Flusher:
+    """Writes a 1 GiB scratch buffer on the current stream, which evicts the
+    L2s and the MALL, so that every timed rep starts with cold caches."""
+
+    def __init__(self, torch, dev):
+        self.buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+        self.n = 0
+
+    def __call__(self):
+        self.n += 1
+        self.buf.fill_(self.n)
+
+
+def measure(torch, step, reps, warmup, flush):
+    """`warmup` untimed steps, then `reps` timed steps, each after a cache
+    flush and between two HIP events on the current stream (the library
+    launches on it and joins its second stream back into it).  The loop is
+    bracketed by device synchronisations.  Returns the per-rep times (ms)."""
+    for _ in range(warmup):
+        flush()
         step()
     torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for s, e in ev:
+        flush()
+        s.record()
+        step()
+        e.record()
+    torch.cuda.synchronize()
+    return [s.elapsed_time(e) for s, e in ev]
+
+
+def stats(times):
+    t = sorted(times)
+    n = len(t)
+    med = t[n // 2] if n % 2 else 0.5 * (t[n // 2 - 1] + t[n // 2])
+    return {"median": med, "min": t[0], "max": t[-1], "mean": sum(t) / n}
+
+
+def profile(b, torch, step, reps, flush):
+    """The same flushed reps with the library's per-launch timing on (a
+    separate pass: its events stay out of the measured reps).  Returns the
+    per-kernel record {name: {count, total_ms}}."""
     b.w4a4_profiler_enable(True)
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        step()
-    stop.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / args.steps
+    measure(torch, step, reps, 0, flush)
     kern = b.w4a4_profiler_report()
     b.w4a4_profiler_enable(False)
-    print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
-    return ms, kern
+    return kern
+
+
+def time_steps(b, torch, step, args, flush, label="step"):
+    """Flushed, event-timed reps (the value) and a profiled pass (per-kernel
+    times).  Returns (stats in ms, per-kernel record)."""
+    times = measure(torch, step, args.steps, args.warmup, flush)
+    st = stats(times)
+    print(f"[bench] {label}: {args.steps} flushed reps, median {st['median']:.3f} ms "
+          f"(min {st['min']:.3f}, max {st['max']:.3f})", file=sys.stderr, flush=True)
+    kern = profile(b, torch, step, args.steps, flush)
+    return st, kern
+
+
+def time_fields(st, steps):
+    return {"ms_median": round(st["median"], 4), "ms_min": round(st["min"], 4),
+            "ms_max": round(st["max"], 4), "ms_mean": round(st["mean"], 4), "reps": steps}
 
 
 def summarize(kern, ms, steps, fl, by, concurrent=None):
@@ -440,12 +502,141 @@ def summarize(kern, ms, steps, fl, by, concurrent=None):
     return per_kernel, roof
 
 
+def moe_buffers(torch, dev, b, T, H, E, k, I, A, mx, mx8):
+    """Preallocated outputs and workspaces of one quantize+permute + forward
+    (+ backward) of a MoE layer."""
+    cap = b.rows_capacity(T, k, E, A)
+    xq = dict(codes=torch.empty(cap, H // 2, dtype=torch.uint8, device=dev),
+              scales=torch.empty(cap, H // (32 if mx else 16), dtype=torch.uint8, device=dev),
+              offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+              row_map=torch.empty(T, k, dtype=torch.int32, device=dev),
+              src_row=torch.empty(cap, dtype=torch.int32, device=dev))
+    if not mx:
+        xq["outer"] = torch.empty(cap, dtype=torch.float32, device=dev)
+    return dict(
+        xq=xq,
+        ws_qp=torch.empty(b.workspace_size(b.WS_QUANTIZE_PERMUTE, T, H, I, E, k, A) + 256,
+                          dtype=torch.uint8, device=dev),
+        ws_f=torch.empty(b.workspace_size(b.WS_FORWARD, T, H, I, E, k, A), dtype=torch.uint8, device=dev),
+        ws_b=torch.empty(b.workspace_size(b.WS_MX8_BACKWARD if mx8 else b.WS_BACKWARD, T, H, I, E, k, A),
+                         dtype=torch.uint8, device=dev),
+        y=torch.empty(T, H, dtype=torch.bfloat16, device=dev),
+        saved=dict(h=torch.empty(cap, 2 * I, dtype=torch.bfloat16, device=dev),
+                   a=torch.empty(cap, I, dtype=torch.bfloat16, device=dev)),
+        grads=dict(dx=torch.empty(T, H, dtype=torch.bfloat16, device=dev),
+                   dw1=torch.empty(E, 2 * I, H, dtype=torch.bfloat16, device=dev),
+                   dw2=torch.empty(E, H, I, dtype=torch.bfloat16, device=dev)))
+
+
+def moe_step(b, bufs, x, idx, p, w1q, w2q, w1, w2, dy, T, H, E, k, I, A, mx=False, mx8=False,
+             backward=True):
+    """One pass of the hot path: quantize+permute, the grouped expert forward
+    (saving h and a) and, with `backward`, the straight-through backward."""
+    xq, saved, grads = bufs["xq"], bufs["saved"], bufs["grads"]
+
+    def step():
+        if mx:
+            b.w4a4_mx_quantize_permute(x, idx, E, A, out=xq, workspace=bufs["ws_qp"])
+            b.w4a4_mx_grouped_expert_fwd(xq, p, w1q, w2q, T, H, I, E, k, A, save=backward, y=bufs["y"],
+                                         workspace=bufs["ws_f"], saved=saved if backward else None)
+        else:
+            b.w4a4_quantize_permute(x, idx, E, A, out=xq, workspace=bufs["ws_qp"])
+            b.w4a4_grouped_expert_fwd(xq, p, w1q, w2q, T, H, I, E, k, A, save=backward, y=bufs["y"],
+                                      workspace=bufs["ws_f"], saved=saved if backward else None)
+        if backward:
+            bwd = b.w4a4_mx8_expert_bwd if mx8 else b.w4a4_expert_bwd
+            bwd(dy, x, w1, w2, saved["h"], saved["a"], p, xq, T, H, I, E, k, A, out=grads,
+                workspace=bufs["ws_b"])
+    return step
+
+
+def gemm_fracs(per_kernel):
+    return {n: e["frac_mfma"] for n, e in per_kernel.items() if "frac_mfma" in e}
+
+
+def sub_config(name, workload, timed, st, kern, steps, T, fl, by, concurrent, extra=None):
+    """One secondary configuration's record for the JSON line."""
+    per_kernel, roof = summarize(kern, st["median"], steps, fl, by, concurrent=concurrent)
+    rec = {"workload": workload, "timed": timed, "T": T,
+           "tokens_per_s": round(T / (st["median"] * 1e-3), 1)}
+    rec.update(time_fields(st, steps))
+    rec["roofline"] = roof
+    rec["gemm_frac_mfma"] = gemm_fracs(per_kernel)
+    rec["kernels"] = {n: {k2: v for k2, v in e.items() if k2 in ("avg_ms", "frac_mfma", "frac_hbm", "runs_beside")}
+                      for n, e in per_kernel.items()}
+    if extra:
+        rec.update(extra)
+    print(f"[bench] {name}: {rec['tokens_per_s']:.4g} tokens/s", file=sys.stderr, flush=True)
+    return rec
+
+
+def secondary_configs(b, torch, dev, args, flush, weights):
+    """The other layer configurations, each timed like the main step (flushed
+    reps, median) with its own per-kernel pass: quantize+permute alone on
+    Student-t activations (T=16384), the forward at T=8192 (near-uniform
+    routing), and the skewed routing at T=32768 (Zipf 1.2, 10 experts
+    without tokens), forward and forward + backward.  The expert weights are
+    the main workload's (same shapes and distribution)."""
+    from precision_rl_amd import synth
+    w1q, w2q, w1, w2 = weights
+    out = {}
+
+    # c2: quantize+permute alone
+    wq = synth.WORKLOADS["qp"]
+    d = synth.workload_inputs("qp")
+    T, H, E, k = wq.T, wq.H, wq.E, wq.k
+    x = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).to(dev)
+    idx = torch.from_numpy(d["topk_idx"]).to(dev)
+    bufs = moe_buffers(torch, dev, b, T, H, E, k, 0, 1, False, False)
+
+    def qp_step():
+        b.w4a4_quantize_permute(x, idx, E, 1, out=bufs["xq"], workspace=bufs["ws_qp"])
+    st, kern = time_steps(b, torch, qp_step, args, flush, "c2 quantize+permute")
+    _, by = qp_work(T, H, k, "token")
+    alg = sum(by.values())
+    out["c2_quantize_permute"] = sub_config(
+        "c2", "qp: route + quantize+permute, Student-t x (T=16384, H=2048, E=128, top-8)",
+        "w4a4_quantize_permute (routing included)", st, kern, args.steps, T, {}, by, {},
+        extra={"call_bytes": alg, "call_gbs": round(alg / (st["median"] * 1e-3) / 1e9, 1),
+               "call_hbm_frac": round(alg / (st["median"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)})
+    del x, idx, bufs, d
+
+    for key, wl, backward in (("c3_forward", "fwd", False), ("c4_skew_forward", "skew", False),
+                              ("c4_skew_forward_backward", "skew", True)):
+        w = synth.WORKLOADS[wl]
+        T, H, E, k, I = w.T, w.H, w.E, w.k, w.I
+        d = synth.make_inputs(T, H, E, k, I, w.routing, w.x_dist, backward=backward,
+                              seed=1000 + w.index, weights=False)
+        bf = lambda bits: torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        x = bf(d["x"])
+        dy = bf(d["dy"]) if backward else None
+        idx = torch.from_numpy(d["topk_idx"]).to(dev)
+        p = torch.from_numpy(d["topk_w"]).to(dev)
+        bufs = moe_buffers(torch, dev, b, T, H, E, k, I, 1, False, False)
+        step = moe_step(b, bufs, x, idx, p, w1q, w2q, w1, w2, dy, T, H, E, k, I, 1, backward=backward)
+        st, kern = time_steps(b, torch, step, args, flush, key)
+        fl, by = algorithmic_work(T, H, E, k, I)
+        if not backward:
+            fl = {n: v for n, v in fl.items() if n in ("gemm_fc1", "gemm_fc2")}
+        out[key] = sub_config(
+            key, f"{wl}: quantize+permute + grouped expert fwd" + (" + BF16 STE bwd" if backward else "")
+            + f" (T={T}, H={H}, E={E}, top-{k}, I={I}, {w.routing} routing)",
+            "quantize_permute + fwd" + (" + bwd" if backward else ""), st, kern, args.steps, T, fl, by,
+            None if backward else {})
+        del x, dy, idx, p, bufs, d, step
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="learner: skip the other layer configurations (quantize+permute alone, "
+                         "forward at T=8192, skewed routing at T=32768)")
     ap.add_argument("--cpu-tokens", type=int, default=6144)
     ap.add_argument("--workload", choices=["learner", "linear", "qp"], default="learner",
                     help="learner: the MoE expert step (default); linear: the dense projection; "
@@ -493,41 +684,13 @@ def main():
     else:
         w1q, w2q = b.quantize_weights(w1), b.quantize_weights(w2)         # offline, untimed
 
-    cap = b.rows_capacity(T, k, E, A)
-    xq = dict(codes=torch.empty(cap, H // 2, dtype=torch.uint8, device=dev),
-              scales=torch.empty(cap, H // (32 if mx else 16), dtype=torch.uint8, device=dev),
-              offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
-              row_map=torch.empty(T, k, dtype=torch.int32, device=dev),
-              src_row=torch.empty(cap, dtype=torch.int32, device=dev))
-    if not mx:
-        xq["outer"] = torch.empty(cap, dtype=torch.float32, device=dev)
-    ws_qp = torch.empty(b.workspace_size(b.WS_QUANTIZE_PERMUTE, T, H, I, E, k, A) + 256,
-                        dtype=torch.uint8, device=dev)
-    ws_f = torch.empty(b.workspace_size(b.WS_FORWARD, T, H, I, E, k, A), dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(b.workspace_size(b.WS_MX8_BACKWARD if mx8 else b.WS_BACKWARD, T, H, I, E, k, A),
-                       dtype=torch.uint8, device=dev)
-    y = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
-    saved = dict(h=torch.empty(cap, 2 * I, dtype=torch.bfloat16, device=dev),
-                 a=torch.empty(cap, I, dtype=torch.bfloat16, device=dev))
-    grads = dict(dx=torch.empty(T, H, dtype=torch.bfloat16, device=dev),
-                 dw1=torch.empty(E, 2 * I, H, dtype=torch.bfloat16, device=dev),
-                 dw2=torch.empty(E, H, I, dtype=torch.bfloat16, device=dev))
-
+    bufs = moe_buffers(torch, dev, b, T, H, E, k, I, A, mx, mx8)
+    step = moe_step(b, bufs, x, idx, p, w1q, w2q, w1, w2, dy, T, H, E, k, I, A, mx=mx, mx8=mx8)
     calibration_copy(torch, dev)
+    flush = Flusher(torch, dev)
 
-    def step():
-        if mx:
-            b.w4a4_mx_quantize_permute(x, idx, E, A, out=xq, workspace=ws_qp)
-            b.w4a4_mx_grouped_expert_fwd(xq, p, w1q, w2q, T, H, I, E, k, A, save=True, y=y,
-                                         workspace=ws_f, saved=saved)
-        else:
-            b.w4a4_quantize_permute(x, idx, E, A, out=xq, workspace=ws_qp)
-            b.w4a4_grouped_expert_fwd(xq, p, w1q, w2q, T, H, I, E, k, A, save=True, y=y,
-                                      workspace=ws_f, saved=saved)
-        bwd = b.w4a4_mx8_expert_bwd if mx8 else b.w4a4_expert_bwd
-        bwd(dy, x, w1, w2, saved["h"], saved["a"], p, xq, T, H, I, E, k, A, out=grads, workspace=ws_b)
-
-    ms, kern = time_steps(b, torch, step, args)
+    st, kern = time_steps(b, torch, step, args, flush, "learner step")
+    ms = st["median"]
     fl, by = algorithmic_work(T, H, E, k, I)
     # the MXFP8 backward runs on the caller's stream alone
     per_kernel, roof = summarize(kern, ms, args.steps, fl, by, concurrent={} if mx8 else None)
@@ -553,11 +716,18 @@ def main():
                                + (" (MXFP4 recipe: E2M1 + E8M0 per 32)" if mx else ""),
                    "T": T, "H": H, "E": E, "top_k": k, "I": I, "row_align": A,
                    "routing": w.routing},
+        "timing": dict(time_fields(st, args.steps), flush_bytes=FLUSH_BYTES,
+                       method="HIP events around each rep on the caller's stream, L2 + MALL flushed "
+                              "before each rep; value from the median; per-kernel times from a "
+                              "separate profiled pass"),
         "roofline": roof,
         "step_mfma_tflops": round(total_flop / (ms * 1e-3) / 1e12, 1),
         "gemm_ms_per_step": round(gemm_ms, 4),
+        "gemm_frac_mfma": gemm_fracs(per_kernel),
         "kernels": per_kernel,
     }
+    if not args.no_secondary and not mx and not mx8:
+        out["configs"] = secondary_configs(b, torch, dev, args, flush, (w1q, w2q, w1, w2))
     if not args.no_cpu_baseline:
         print("[bench] timing the FP64 oracle on the host", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(d, w, tokens=args.cpu_tokens, recipe=args.recipe, bwd=args.bwd)
