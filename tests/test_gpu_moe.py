@@ -145,35 +145,6 @@ def test_forward_deterministic():
         assert torch.equal(r1.f[key], r2.f[key]), key
 
 
-def test_forward_full_fwd_workload_sampled():
-    """The forward workload at full size (T=8192, H=2048, E=128, k=8, I=768);
-    outputs of sampled tokens checked against the oracle computed on those
-    tokens alone (a token's outputs depend only on its own row)."""
-    w = synth.WORKLOADS["fwd"]
-    d = synth.workload_inputs("fwd")
-    print_case("forward_full_sampled", T=w.T, H=w.H, E=w.E, k=w.k, I=w.I)
-    run = Run(d, w.T, w.H, w.E, w.k, w.I)
-    sample = np.array([0, 1, 4097, w.T - 1])
-    experts = np.unique(d["topk_idx"][sample])
-    # oracle on the sampled tokens, with only the experts they use
-    remap = -np.ones(w.E, dtype=np.int64)
-    remap[experts] = np.arange(experts.size)
-    sub = dict(x=d["x"][sample], topk_idx=remap[d["topk_idx"][sample]].astype(np.int32),
-               topk_w=d["topk_w"][sample], w1=d["w1"][experts], w2=d["w2"][experts])
-    ref, w1q, _ = _oracle_fwd(sub, experts.size, 1)
-    # weight encodings of those experts: bit-exact
-    assert np.array_equal(u8(run.w1q["codes"])[experts], w1q["packed"])
-    assert np.array_equal(u8(run.w1q["scales"])[experts], w1q["scales"])
-    rows_gpu = run.xq["row_map"].cpu().numpy()[sample].reshape(-1)
-    rows_ref = ref["xq"]["row_map"].reshape(-1)
-    fc1 = run.f["fc1_f32"].cpu().numpy()[rows_gpu]
-    assert rel_l2(fc1, ref["h64"][rows_ref]) <= FC1_TOL
-    gc = q.unpack_codes(u8(run.f["a_codes"])[rows_gpu])
-    assert np.mean(gc != ref["a_codes"][rows_ref]) <= CODE_FLIP_BUDGET
-    y = bf16_host(run.f["y"])[sample]
-    assert rel_l2(y, ref["y"]) <= Y_TOL
-
-
 # ------------------------------------------------------------------ backward
 def _oracle_bwd(d, E, A, ref_fwd):
     x = q.bf16_bits_to_f64(d["x"])
@@ -241,93 +212,6 @@ def test_backward_skewed_split_experts():
     for e in range(E):
         assert rel_l2(dw1[e], rb["dW1"][e]) <= BWD_TOL, e
         assert rel_l2(dw2[e], rb["dW2"][e]) <= BWD_TOL, e
-
-
-def test_backward_full_learner_workload_sampled():
-    """Learner workload at full size (T=16384, H=2048, E=128, k=8, I=768):
-    dX of sampled tokens and dW of sampled experts against the oracle on the
-    corresponding sub-problems (a token's dX needs only its own k rows; an
-    expert's dW needs only the rows routed to it)."""
-    w = synth.WORKLOADS["learner"]
-    d = synth.workload_inputs("learner")
-    print_case("backward_full_sampled", T=w.T, H=w.H, E=w.E, k=w.k, I=w.I)
-    run = Run(d, w.T, w.H, w.E, w.k, w.I, backward=True)
-    # dX of a few tokens
-    sample = np.array([3, 9000, w.T - 2])
-    experts = np.unique(d["topk_idx"][sample])
-    remap = -np.ones(w.E, dtype=np.int64)
-    remap[experts] = np.arange(experts.size)
-    sub = dict(x=d["x"][sample], topk_idx=remap[d["topk_idx"][sample]].astype(np.int32),
-               topk_w=d["topk_w"][sample], w1=d["w1"][experts], w2=d["w2"][experts],
-               dy=d["dy"][sample])
-    ref, _, _ = _oracle_fwd(sub, experts.size, 1)
-    rb = _oracle_bwd(sub, experts.size, 1, ref)
-    assert rel_l2(bf16_host(run.g["dx"])[sample], rb["dX"]) <= BWD_TOL
-    # dW of two experts: sub-problem of the tokens routed to e with k = 1
-    for e in (5, 77):
-        tok, slot = np.nonzero(d["topk_idx"] == e)
-        sub = dict(x=d["x"][tok], topk_idx=np.zeros((tok.size, 1), np.int32),
-                   topk_w=d["topk_w"][tok, slot][:, None].copy(), w1=d["w1"][e:e + 1],
-                   w2=d["w2"][e:e + 1], dy=d["dy"][tok])
-        ref, _, _ = _oracle_fwd(sub, 1, 1)
-        rb = _oracle_bwd(sub, 1, 1, ref)
-        assert rel_l2(bf16_host(run.g["dw1"][e]), rb["dW1"][0]) <= BWD_TOL
-        assert rel_l2(bf16_host(run.g["dw2"][e]), rb["dW2"][0]) <= BWD_TOL
-
-
-def test_full_skew_workload_sampled():
-    """Skewed workload at full size (T=32768, H=2048, E=128, k=8, I=768;
-    Zipf(1.2) expert popularity, 10 experts without tokens), forward and
-    backward: the permutation bit-exact against the oracle's routing of all
-    tokens; forward outputs and dX of sampled tokens, including the last
-    tokens of the most popular expert (its last, partial M tile) and of the
-    least popular live one; dW of the least popular live expert against the
-    oracle on its rows; dW of the empty experts exactly zero."""
-    w = synth.WORKLOADS["skew"]
-    d = synth.make_inputs(w.T, w.H, w.E, w.k, w.I, w.routing, w.x_dist, backward=True,
-                          seed=1000 + w.index)
-    print_case("skew_full_sampled", T=w.T, H=w.H, E=w.E, k=w.k, I=w.I)
-    run = Run(d, w.T, w.H, w.E, w.k, w.I, backward=True)
-    offsets, row_map, src_row = moe.route_fast(d["topk_idx"], w.E, 1)
-    assert np.array_equal(run.xq["offsets"].cpu().numpy(), offsets)
-    assert np.array_equal(run.xq["row_map"].cpu().numpy(), row_map)
-    assert np.array_equal(run.xq["src_row"].cpu().numpy()[:offsets[-1]], src_row)
-    counts = np.diff(offsets)
-    empty = np.nonzero(counts == 0)[0]
-    assert empty.size == 10
-    big = int(np.argmax(counts))
-    small = int(np.argmin(np.where(counts > 0, counts, counts.max() + 1)))
-    # sampled tokens: first / last rows of the largest and smallest experts
-    picks = [src_row[offsets[big]], src_row[offsets[big + 1] - 1], src_row[offsets[big + 1] - 2],
-             src_row[offsets[small]], src_row[offsets[small + 1] - 1], 0, w.T - 1]
-    sample = np.unique(np.array(picks))
-    experts = np.unique(d["topk_idx"][sample])
-    remap = -np.ones(w.E, dtype=np.int64)
-    remap[experts] = np.arange(experts.size)
-    sub = dict(x=d["x"][sample], topk_idx=remap[d["topk_idx"][sample]].astype(np.int32),
-               topk_w=d["topk_w"][sample], w1=d["w1"][experts], w2=d["w2"][experts],
-               dy=d["dy"][sample])
-    ref, _, _ = _oracle_fwd(sub, experts.size, 1)
-    rows_gpu = row_map[sample].reshape(-1)
-    rows_ref = ref["xq"]["row_map"].reshape(-1)
-    fc1 = run.f["fc1_f32"].cpu().numpy()[rows_gpu]
-    assert rel_l2(fc1, ref["h64"][rows_ref]) <= FC1_TOL
-    gc = q.unpack_codes(u8(run.f["a_codes"])[rows_gpu])
-    assert np.mean(gc != ref["a_codes"][rows_ref]) <= CODE_FLIP_BUDGET
-    assert rel_l2(bf16_host(run.f["y"])[sample], ref["y"]) <= Y_TOL
-    rb = _oracle_bwd(sub, experts.size, 1, ref)
-    assert rel_l2(bf16_host(run.g["dx"])[sample], rb["dX"]) <= BWD_TOL
-    # dW of the least popular live expert: its rows alone, k = 1
-    tok, slot = np.nonzero(d["topk_idx"] == small)
-    sub = dict(x=d["x"][tok], topk_idx=np.zeros((tok.size, 1), np.int32),
-               topk_w=d["topk_w"][tok, slot][:, None].copy(), w1=d["w1"][small:small + 1],
-               w2=d["w2"][small:small + 1], dy=d["dy"][tok])
-    ref, _, _ = _oracle_fwd(sub, 1, 1)
-    rb = _oracle_bwd(sub, 1, 1, ref)
-    assert rel_l2(bf16_host(run.g["dw1"][small]), rb["dW1"][0]) <= BWD_TOL
-    assert rel_l2(bf16_host(run.g["dw2"][small]), rb["dW2"][0]) <= BWD_TOL
-    for e in empty:
-        assert not run.g["dw1"][e].any() and not run.g["dw2"][e].any()
 
 
 def test_backward_concurrent_calls_on_two_streams():
