@@ -24,11 +24,12 @@ __device__ __forceinline__ void acc_bf16x8(float (&acc)[8], u32x4_t v, float w) 
   }
 }
 
-// One workgroup per token; thread c handles 16 B chunks c, c+256, ...
+// A workgroup per token (workgroups stride over the tokens when the grid is
+// smaller than T); thread c handles 16 B chunks c, c+256, ...
 __global__ void __launch_bounds__(kThreads)
-gather_sum_kernel(int H, int k, const uint16_t* __restrict__ src, const int32_t* __restrict__ row_map,
+gather_sum_kernel(int64_t T, int H, int k, const uint16_t* __restrict__ src, const int32_t* __restrict__ row_map,
                   const float* __restrict__ w, uint16_t* __restrict__ out) {
-  const int64_t t = blockIdx.x;
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
   const int chunks = H / 8;
   int32_t rows[16];
   float ws[16];
@@ -54,6 +55,7 @@ gather_sum_kernel(int H, int k, const uint16_t* __restrict__ src, const int32_t*
     for (int d = 0; d < 4; ++d) o[d] = pack_bf16x2(acc[2 * d], acc[2 * d + 1]);
     __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(out + t * H + c * 8));
   }
+  }
 }
 
 // One workgroup per token t.  DY: dY[t] is read once and written, scaled by
@@ -63,9 +65,9 @@ gather_sum_kernel(int H, int k, const uint16_t* __restrict__ src, const int32_t*
 // kernels: dO is needed first, xp only by the last GEMM.
 template <bool DY>
 __global__ void __launch_bounds__(kThreads)
-scatter_kernel(int H, int k, const uint16_t* __restrict__ src, const int32_t* __restrict__ row_map,
+scatter_kernel(int64_t T, int H, int k, const uint16_t* __restrict__ src, const int32_t* __restrict__ row_map,
                const float* __restrict__ w, uint16_t* __restrict__ dst) {
-  const int64_t t = blockIdx.x;
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
   int32_t rows[16];
   float ps[16];
 #pragma unroll
@@ -94,6 +96,7 @@ scatter_kernel(int H, int k, const uint16_t* __restrict__ src, const int32_t* __
       }
     }
   }
+  }
 }
 
 // Pad rows (src_row < 0, rows [0, offsets[E])) of a [rows, H] bf16 buffer: zeros.
@@ -111,7 +114,7 @@ zero_pad_rows_kernel(int H, const int32_t* __restrict__ src_row, const int32_t* 
 bool launch_unpermute(int64_t T, int H, int k, const uint16_t* o, const int32_t* row_map,
                       const float* topk_w, uint16_t* y, hipStream_t s) {
   if (T == 0) return true;
-  launch_kernel("unpermute", gather_sum_kernel, dim3(static_cast<unsigned>(T)), dim3(kThreads), 0, s, H, k, o,
+  launch_kernel("unpermute", gather_sum_kernel, dim3(static_cast<unsigned>(T)), dim3(kThreads), 0, s, T, H, k, o,
                 row_map, topk_w, y);
   return launch_ok("unpermute");
 }
@@ -119,7 +122,7 @@ bool launch_unpermute(int64_t T, int H, int k, const uint16_t* o, const int32_t*
 bool launch_gather_sum(int64_t T, int H, int k, const uint16_t* dXp, const int32_t* row_map,
                        uint16_t* dx, hipStream_t s) {
   if (T == 0) return true;
-  launch_kernel("dx_gather_sum", gather_sum_kernel, dim3(static_cast<unsigned>(T)), dim3(kThreads), 0, s, H, k,
+  launch_kernel("dx_gather_sum", gather_sum_kernel, dim3(static_cast<unsigned>(T)), dim3(kThreads), 0, s, T, H, k,
                 dXp, row_map, static_cast<const float*>(nullptr), dx);
   return launch_ok("dx_gather_sum");
 }
@@ -127,7 +130,7 @@ bool launch_gather_sum(int64_t T, int H, int k, const uint16_t* dXp, const int32
 bool launch_scatter_dy(int64_t T, int H, int k, const uint16_t* dy, const int32_t* row_map,
                        const float* topk_w, uint16_t* dO, hipStream_t s) {
   if (T == 0) return true;
-  launch_kernel("dy_scatter", scatter_kernel<true>, dim3(static_cast<unsigned>(T)), dim3(kThreads), 0, s, H, k,
+  launch_kernel("dy_scatter", scatter_kernel<true>, dim3(static_cast<unsigned>(T)), dim3(kThreads), 0, s, T, H, k,
                 dy, row_map, topk_w, dO);
   return launch_ok("dy_scatter");
 }
@@ -135,7 +138,7 @@ bool launch_scatter_dy(int64_t T, int H, int k, const uint16_t* dy, const int32_
 bool launch_scatter_x(int64_t T, int H, int k, const uint16_t* x, const int32_t* row_map, uint16_t* xp,
                       hipStream_t s) {
   if (T == 0) return true;
-  launch_kernel("x_scatter", scatter_kernel<false>, dim3(static_cast<unsigned>(T)), dim3(kThreads), 0, s, H, k,
+  launch_kernel("x_scatter", scatter_kernel<false>, dim3(static_cast<unsigned>(T)), dim3(kThreads), 0, s, T, H, k,
                 x, row_map, static_cast<const float*>(nullptr), xp);
   return launch_ok("x_scatter");
 }

@@ -440,6 +440,10 @@ fwd_gemm_kernel(FwdArgs args) {
     decode_task(0);
     decode_task(1);
     __builtin_amdgcn_sched_barrier(0);
+    // The stage's MFMAs at raised wave priority: the SIMD's arbiter then
+    // prefers this wave's next MFMA (and the decode between them) to the
+    // other workgroup's wave while it copies, waits or stores (FC1 -3%).
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int m = 0; m < 32; ++m) {
       const int s4 = m >> 3, mi = (m >> 2) & 1, ni = m & 3;
@@ -447,6 +451,7 @@ fwd_gemm_kernel(FwdArgs args) {
       if (m + 2 < 24) decode_task(m + 2);
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
   }
   float* s_gx = reinterpret_cast<float*>(lds + L::kGx);
   if (tid < kBM) s_gx[tid] = gx_row;
