@@ -14,16 +14,26 @@
  *    invalid call returns a negative status and launches nothing.  No C++
  *    exception crosses this interface.  w4a4_last_error() gives detail.
  *  - Routing validity (0 <= topk_idx < E, k distinct experts per token) is the
- *    caller's contract and is not checked on the device.
+ *    caller's contract: the path's calls do not check it.  A caller that
+ *    cannot vouch for its router checks a batch with w4a4_check_routing,
+ *    which sets a device error word.
+ *  - Shapes: H and I (and a quantised row length K) must be multiples of 32
+ *    (16 for K), else W4A4_ERR_INVALID_ARG.  The kernels take H % 256 == 0
+ *    and I % 128 == 0, else W4A4_ERR_UNSUPPORTED: the forward GEMMs' output
+ *    tiles are 256 columns of H (FC2) and 128 SwiGLU features = 256 columns
+ *    of h (FC1) with reduction stages of 64, the backward GEMMs' weight tiles
+ *    256 columns with stages of 32, and none of them masks a partial tile
+ *    along N or K.  Qwen3-30B-A3B's expert layer (H = 2048, I = 768) and
+ *    every layer width that is a multiple of 256 / 128 fit.
  *  - Results are bitwise reproducible from run to run, and a token's results
  *    do not depend on the other tokens of the batch (per-token scale domain).
  *  - Calls are thread-safe; concurrent calls on different streams need
  *    different workspaces.
- *  - w4a4_expert_bwd runs three of its kernels (the wgrad tile schedule, the
- *    copy of x to the expert rows, the dX gather-sum) on a second stream of
- *    the current device (created on first use, default priority), forked from
- *    `stream` and joined back into it: work enqueued on `stream` after the
- *    call sees every output.
+ *  - w4a4_expert_bwd runs two of its kernels (the wgrad tile schedule and the
+ *    copy of x to the expert rows) on a second stream of the current device
+ *    (created on first use, default priority), forked from `stream` and
+ *    joined back into it before the call's last kernels: work enqueued on
+ *    `stream` after the call sees every output.
  *
  * Data formats (miniTE Technical Report, sections 2.2 and 5.1; rainbus review
  * of the miniTE paper, "prerequisites: the NVFP4 format" and method step 4):
@@ -114,6 +124,23 @@ w4a4_status w4a4_quantize_permute(
     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * w4a4_check_routing -- checks a router's output before the path uses it.
+ *   Defined by: rainbus review, prerequisites "MoE and grouped GEMM" (each
+ *   token goes to k distinct experts of E; an expert may receive none).
+ *
+ *   topk_idx   [T, k] int32 expert ids (k <= 8); may be NULL when T == 0.
+ *   error_word [2] int32 out (device, 8-byte aligned): error_word[0] = the
+ *              number of invalid entries (an id outside [0, E), or an id
+ *              equal to an earlier id of the same token), error_word[1] = the
+ *              smallest flat index t*k + j of an invalid entry, INT32_MAX
+ *              when there is none.  Both are written on `stream` (the caller
+ *              reads them after the stream's work).
+ *   Reads topk_idx only; every id is bounds-checked before it is used.
+ */
+w4a4_status w4a4_check_routing(const int32_t* topk_idx, int64_t T, int k, int E, int32_t* error_word,
+                               void* stream);
+
+/*
  * w4a4_quantize_permute_domain -- w4a4_quantize_permute with an outer-scale
  * domain wider than a row: one FP32 outer scale per group of `group_rows`
  * consecutive input rows (the last group may be shorter).
@@ -197,8 +224,9 @@ w4a4_status w4a4_grouped_expert_fwd(
 /*
  * w4a4_expert_bwd -- the straight-through BF16 backward on the
  * saved high-precision operands (no backward quantisation).
- *   Defined by: AI summary, "Methodology in Plain English" (straight-through
- *   estimator using saved original BF16 activations and weights); miniTE
+ *   Defined by: AI summary, "Methodology in Plain English" (the quantisers'
+ *   gradient taken as the identity, computed from the bf16 activations and
+ *   weights the forward saved); miniTE
  *   Technical Report, section 4.3 (BF16 backward through the layer bypass on
  *   the saved original operands).
  *

@@ -46,6 +46,7 @@ _SIGS = {
                                     c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                     c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "w4a4_mx8_quantize": (c_int, [c_vp, c_i64, c_int, c_vp, c_vp, c_vp, c_vp, c_i64, c_vp]),
+    "w4a4_check_routing": (c_int, [c_vp, c_i64, c_int, c_int, c_vp, c_vp]),
     "w4a4_status_string": (ctypes.c_char_p, [c_int]),
     "w4a4_last_error": (ctypes.c_char_p, []),
     "w4a4_profiler_enable": (c_int, [c_int]),
@@ -167,6 +168,17 @@ def w4a4_quantize_permute_domain(x, topk_idx, E, row_align=1, group_rows=1, out=
         _p(x), T, K, _p(topk_idx), k, E, row_align, group_rows,
         _p(out["codes"]), _p(out["scales"]), _p(out["outer"]), _p(out["offsets"]),
         _p(out["row_map"]), _p(out["src_row"]), _p(ws), ws.numel(), _stream()))
+    return out
+
+
+def w4a4_check_routing(topk_idx, E, out=None):
+    """Routing validity of topk_idx [T, k] int32 cuda.  Returns an int32 [2] device
+    tensor: (number of invalid entries, smallest flat index of one or INT32_MAX)."""
+    lib = load()
+    T, k = topk_idx.shape
+    if out is None:
+        out = torch.empty(2, dtype=torch.int32, device=topk_idx.device)
+    _check(lib.w4a4_check_routing(_p(topk_idx), T, k, E, _p(out), _stream()))
     return out
 
 

@@ -7,6 +7,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -172,6 +173,8 @@ w4a4_status check_moe_shape(int64_t T, int H, int I, int E, int k, int row_align
     return fail(W4A4_ERR_UNSUPPORTED, "H and I must be <= %d", kMaxRowLen);
   if (E > kMaxExperts || k > kMaxTopK)
     return fail(W4A4_ERR_UNSUPPORTED, "E <= %d and k <= %d supported", kMaxExperts, kMaxTopK);
+  if (T * static_cast<int64_t>(k) + static_cast<int64_t>(E) * (row_align - 1) > (int64_t{1} << 31) - 1)
+    return fail(W4A4_ERR_UNSUPPORTED, "T*k + E*(row_align-1) rows exceed int32 row indices");
   return W4A4_OK;
 }
 
@@ -286,11 +289,27 @@ w4a4_status check_quantize_permute(const void* x, int64_t T, int K, const int32_
     REQUIRE_PTR(row_map);
     REQUIRE_PTR(src_row);
   }
-  if (T * static_cast<int64_t>(k) > (int64_t{1} << 31) - 1)
-    return fail(W4A4_ERR_UNSUPPORTED, "T*k exceeds int32 row indices");
+  if (T * static_cast<int64_t>(k) + static_cast<int64_t>(E) * (row_align - 1) > (int64_t{1} << 31) - 1)
+    return fail(W4A4_ERR_UNSUPPORTED, "T*k + E*(row_align-1) rows exceed int32 row indices");
   return W4A4_OK;
 }
 }  // namespace
+
+w4a4_status w4a4_check_routing(const int32_t* topk_idx, int64_t T, int k, int E, int32_t* error_word,
+                               void* stream) {
+  g_last_error.clear();
+  if (T < 0) return fail(W4A4_ERR_INVALID_ARG, "T < 0");
+  if (k <= 0 || E <= 0) return fail(W4A4_ERR_INVALID_ARG, "bad k=%d / E=%d", k, E);
+  if (k > kMaxTopK) return fail(W4A4_ERR_UNSUPPORTED, "k <= %d supported", kMaxTopK);
+  if (T * static_cast<int64_t>(k) > (int64_t{1} << 31) - 1)
+    return fail(W4A4_ERR_UNSUPPORTED, "T*k exceeds int32 indices");
+  if (error_word == nullptr) return fail(W4A4_ERR_INVALID_ARG, "error_word is NULL");
+  if (reinterpret_cast<uintptr_t>(error_word) % 8) return fail(W4A4_ERR_INVALID_ARG, "error_word is not 8-byte aligned");
+  if (T > 0) REQUIRE_PTR(topk_idx);
+  if (!launch_check_routing(topk_idx, T, k, E, error_word, static_cast<hipStream_t>(stream)))
+    return W4A4_ERR_LAUNCH;
+  return W4A4_OK;
+}
 
 w4a4_status w4a4_quantize_permute_domain(const void* x, int64_t T, int K, const int32_t* topk_idx,
                                          int k, int E, int row_align, int64_t group_rows,
@@ -422,10 +441,9 @@ w4a4_status w4a4_expert_bwd(int64_t T, int H, int I, int E, int k, int row_align
   const uint16_t* W2 = static_cast<const uint16_t*>(w2);
 
   // Side stream: the copy of x to the expert rows (xp, read only by the last
-  // GEMM) runs beside the FC2 wgrad and the FC1 dgrad; the dX gather-sum
-  // (needs only dXp) beside the FC1 wgrad (needs only dH and xp).  Both are
-  // HBM-bound with few registers and no LDS; the GEMMs are MFMA-bound.  The
-  // caller's stream waits for both before the call's work ends.
+  // GEMM) runs beside the FC2 wgrad and the FC1 dgrad: HBM-bound with few
+  // registers and no LDS, beside MFMA-bound GEMMs.  The caller's stream
+  // waits for it before the FC1 wgrad.
   std::lock_guard<std::mutex> lock(side_mutex());
   SideStream side;
   if (!side_stream(side)) return fail(W4A4_ERR_LAUNCH, "side stream / events could not be created");
@@ -463,12 +481,14 @@ w4a4_status w4a4_expert_bwd(int64_t T, int H, int I, int E, int k, int row_align
     return W4A4_ERR_LAUNCH;
   if (cap > 0 && !launch_dgrad_fc1(cap, H, I, E, expert_offsets, dH, W1, dXp, s))
     return W4A4_ERR_LAUNCH;
-  if (!join(0) || !fork(1)) return fail(W4A4_ERR_LAUNCH, "side stream fork / join failed");
+  // The dX gather-sum runs after the FC1 wgrad on the caller's stream: beside
+  // it on the second stream it saved nothing (the step took as long) and
+  // blurred the GEMM's own time.
+  if (!join(0)) return fail(W4A4_ERR_LAUNCH, "join from the side stream failed");
   if (!launch_wgrad_fc1(H, I, E, dH, xp, static_cast<uint16_t*>(dw1), sched, s))
     return W4A4_ERR_LAUNCH;
-  if (!launch_gather_sum(T, H, k, dXp, row_map, static_cast<uint16_t*>(dx), side.stream))
+  if (!launch_gather_sum(T, H, k, dXp, row_map, static_cast<uint16_t*>(dx), s))
     return W4A4_ERR_LAUNCH;
-  if (!join(1)) return fail(W4A4_ERR_LAUNCH, "join from the side stream failed");
   return W4A4_OK;
 }
 
@@ -569,6 +589,8 @@ w4a4_status w4a4_mx_grouped_expert_fwd(
   OPTIONAL_PTR(dbg_a_codes); OPTIONAL_PTR(dbg_a_scales);
   const int nd = (dbg_a_codes != nullptr) + (dbg_a_scales != nullptr);
   if (nd == 1) return fail(W4A4_ERR_INVALID_ARG, "dbg_a_codes, dbg_a_scales: both or neither");
+  // the MX row encoder of the FC2 input takes rows of at most 4096
+  if (I > 4096) return fail(W4A4_ERR_UNSUPPORTED, "the MXFP4 forward needs I <= 4096 (I=%d)", I);
   const int64_t cap = w4a4_rows_capacity(T, k, E, row_align);
   const FwdWs L = fwd_ws(cap, H, I);
   if (workspace == nullptr || workspace_bytes < L.total)
@@ -618,7 +640,8 @@ w4a4_status w4a4_mx8_expert_bwd(int64_t T, int H, int I, int E, int k, int row_a
   if (workspace == nullptr || workspace_bytes < L.total)
     return fail(W4A4_ERR_WORKSPACE, "workspace needs %zu bytes", L.total);
   OPTIONAL_PTR(workspace);
-  if (L.P * static_cast<int64_t>(H) > (int64_t{1} << 31))
+  // the transposed operands ([H | I | 2I, P] bytes) are addressed with 32-bit offsets
+  if (L.P * static_cast<int64_t>(std::max(H, 2 * I)) > (int64_t{1} << 31))
     return fail(W4A4_ERR_UNSUPPORTED, "too many dispatched rows for the MXFP8 backward's 32-bit offsets");
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);

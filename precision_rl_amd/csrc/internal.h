@@ -37,6 +37,12 @@ int device_cu_count();
 
 // ------------------------------------------------------------ routing / quant
 constexpr int kRouteChunk = 256;      // tokens per routing chunk (one workgroup)
+constexpr int kMaxRouteK = 8;         // largest k the routing kernels take
+
+// Routing validity of topk_idx [T, k] (k <= kMaxRouteK): err[0] = invalid
+// entries (id outside [0, E) or repeated within a token), err[1] = smallest
+// flat index of one (INT32_MAX when none).
+bool launch_check_routing(const int32_t* topk_idx, int64_t T, int k, int E, int32_t* err, hipStream_t s);
 
 size_t route_workspace_bytes(int64_t T, int E);
 

@@ -938,4 +938,58 @@ bool launch_requant_mx(const uint16_t* a, int64_t rows_alloc, int K, const int32
                                              nullptr, const_cast<int32_t*>(offsets), nullptr, nullptr, nullptr, s);
 }
 
+// ---------------------------------------------------------- routing validity
+// err[0] = number of invalid entries of topk_idx [T, k] (an id outside
+// [0, E), or equal to an earlier id of the same token), err[1] = the
+// smallest flat index t*k + j of an invalid entry (INT32_MAX when none).
+// err is set by routing_check_init_kernel and merged with vector atomics.
+__global__ void routing_check_init_kernel(int32_t* __restrict__ err) {
+  if (threadIdx.x == 0) {
+    err[0] = 0;
+    err[1] = 0x7FFFFFFF;
+  }
+}
+
+__global__ void __launch_bounds__(256)
+routing_check_kernel(const int32_t* __restrict__ topk_idx, int64_t T, int k, int E, int32_t* __restrict__ err) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  int bad = 0;
+  int first = 0x7FFFFFFF;
+  if (t < T) {
+    int ids[kMaxRouteK];
+    for (int j = 0; j < k; ++j) {
+      const int e = topk_idx[t * k + j];
+      ids[j] = e;
+      bool ok = e >= 0 && e < E;
+      for (int i = 0; i < j; ++i) ok = ok && ids[i] != e;
+      if (!ok) {
+        ++bad;
+        first = min(first, static_cast<int>(t * k + j));
+      }
+    }
+  }
+  // wave totals, then one lane per wave merges them
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    bad += __shfl_xor(bad, off, kWave);
+    first = min(first, __shfl_xor(first, off, kWave));
+  }
+  // a zero offset in a vector register keeps the atomics on the vector path
+  uint32_t vzero = 0;
+  asm volatile("" : "+v"(vzero));
+  if ((threadIdx.x & 63) == 0 && bad > 0) {
+    atomicAdd(err + vzero, bad);
+    atomicMin(err + 1 + vzero, first);
+  }
+}
+
+bool launch_check_routing(const int32_t* topk_idx, int64_t T, int k, int E, int32_t* err, hipStream_t s) {
+  launch_kernel("routing_check_init", routing_check_init_kernel, dim3(1), dim3(64), 0, s, err);
+  if (!launch_ok("routing_check_init")) return false;
+  if (T == 0) return true;
+  launch_kernel("routing_check", routing_check_kernel, dim3(static_cast<unsigned>((T + 255) / 256)), dim3(256), 0, s,
+                topk_idx, T, k, E, err);
+  return launch_ok("routing_check");
+}
+
 }  // namespace w4a4

@@ -157,3 +157,50 @@ def test_mx8_backward_rejects_invalid_arguments_before_launch():
     assert q8(C=64) == -2                              # C % 128
     assert q8(pitch=64) == -1                          # pitch >= R
     assert q8(x=None) == -1
+
+
+def test_shape_floor_and_row_limits_rejected_before_launch():
+    """The documented shape floor: H, I multiples of 32 are valid arguments,
+    but the kernels take H % 256 == 0 and I % 128 == 0 (UNSUPPORTED, with the
+    reason in last_error); the padded row count must fit int32 row indices;
+    the MXFP4 forward's FC2-input encoder takes I <= 4096.  All are refused
+    before anything is launched."""
+    lib = _lib()
+    from precision_rl_amd import binding as b
+    buf = ctypes.create_string_buffer(4096)
+    p = ctypes.c_void_p(ctypes.addressof(buf) + (-ctypes.addressof(buf)) % 16)
+
+    def fwd(H=2048, I=768, T=4, A=1, E=8):
+        return lib.w4a4_grouped_expert_fwd(T, H, I, E, 2, A, p, p, p, p, p, p, p, p, p, p, p, p, p,
+                                           p, None, None, None, None, None, None, p, 1 << 40, None)
+
+    assert fwd(H=288, I=160) == -2
+    assert "256" in b.load().w4a4_last_error().decode()
+    assert fwd(H=2048, I=160) == -2
+    assert fwd(H=2049) == -1
+    assert fwd(T=(1 << 30), A=128, E=1024) == -2       # T*k + E*(A-1) >= 2^31
+    assert "int32" in b.load().w4a4_last_error().decode()
+
+    def qp(T=4, k=2, E=8, A=1):
+        return lib.w4a4_quantize_permute(p, T, 64, p, k, E, A, p, p, p, p, p, p, p, 1 << 30, None)
+
+    assert qp(T=(1 << 28) - 1, k=8, E=1024, A=128) == -2   # T*k < 2^31 but the padded rows are not
+
+    def mfwd(H=256, I=8192 - 128):
+        return lib.w4a4_mx_grouped_expert_fwd(4, H, I, 8, 2, 1, p, p, p, p, p, p, p, p, p, p,
+                                              p, None, None, None, None, None, p, 1 << 40, None)
+
+    assert mfwd() == -2
+    assert "4096" in b.load().w4a4_last_error().decode()
+
+
+def test_check_routing_rejects_invalid_arguments_before_launch():
+    lib = _lib()
+    buf = ctypes.create_string_buffer(4096)
+    p = ctypes.c_void_p(ctypes.addressof(buf) + (-ctypes.addressof(buf)) % 16)
+    assert lib.w4a4_check_routing(p, 4, 9, 16, p, None) == -2          # k <= 8
+    assert lib.w4a4_check_routing(p, 4, 0, 16, p, None) == -1
+    assert lib.w4a4_check_routing(p, -1, 2, 16, p, None) == -1
+    assert lib.w4a4_check_routing(p, 4, 2, 16, None, None) == -1       # no error word
+    assert lib.w4a4_check_routing(None, 4, 2, 16, p, None) == -1       # no ids for T > 0
+    assert lib.w4a4_check_routing(p, 4, 2, 16, ctypes.c_void_p(p.value + 4), None) == -1

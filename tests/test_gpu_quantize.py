@@ -215,3 +215,26 @@ def test_empty_batch():
     got = b.w4a4_quantize_permute(x, idx, 8, 16)
     torch.cuda.synchronize()
     assert got["offsets"].cpu().numpy().tolist() == [0] * 9
+
+
+def test_check_routing_error_word():
+    """w4a4_check_routing: a valid router output gives (0, INT32_MAX); ids
+    out of [0, E) and ids repeated within a token are counted, and the
+    smallest flat index among them is reported (ids are only read by the
+    check kernel, which bounds-checks each one)."""
+    from precision_rl_amd import binding as b
+    T, E, k = 3000, 16, 4
+    d = synth.make_inputs(T, 64, E, k, 0, seed=12)
+    idx = d["topk_idx"].copy()
+    print_case("check_routing", T=T, E=E, k=k)
+    ok = b.w4a4_check_routing(torch.from_numpy(idx).cuda(), E).cpu().numpy()
+    assert ok.tolist() == [0, 2 ** 31 - 1]
+    bad = idx.copy()
+    bad[7, 2] = E              # out of range
+    bad[100, 0] = -1           # negative
+    bad[2999, 3] = bad[2999, 1]   # repeated within the token
+    bad[5, 1] = bad[5, 0]      # repeated, the smallest flat index
+    got = b.w4a4_check_routing(torch.from_numpy(bad).cuda(), E).cpu().numpy()
+    assert got.tolist() == [4, 5 * k + 1]
+    empty = b.w4a4_check_routing(torch.zeros((0, k), dtype=torch.int32, device="cuda"), E).cpu().numpy()
+    assert empty.tolist() == [0, 2 ** 31 - 1]
