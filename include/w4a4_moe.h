@@ -124,6 +124,28 @@ w4a4_status w4a4_quantize_permute(
     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * w4a4_quantize_permute_noalloc -- w4a4_quantize_permute for callers that
+ * cannot allocate (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid device allocation): the same arguments, results and
+ * kernels without the workspace.  Its routing scratch is a 1 MiB array held
+ * by the library on each GPU it runs on (until the process ends); the call
+ * itself allocates nothing.
+ *   Limit: the routing scratch, 4 * (E * ceil(T / 256) + E) bytes rounded up
+ *   to 256, must fit in 1 MiB (T <= 524,032 tokens at E = 128); larger
+ *   calls return W4A4_ERR_UNSUPPORTED and launch nothing.  Identity routing
+ *   (topk_idx = NULL) uses no scratch.
+ *   Every call on one GPU shares that GPU's scratch: calls that overlap on
+ *   one GPU (different streams, or host threads on one stream without
+ *   ordering) race and must not be issued.
+ */
+w4a4_status w4a4_quantize_permute_noalloc(
+    const void* x, int64_t T, int K,
+    const int32_t* topk_idx, int k, int E, int row_align,
+    uint8_t* codes, uint8_t* scales, float* outer,
+    int32_t* expert_offsets, int32_t* row_map, int32_t* src_row,
+    void* stream);
+
+/*
  * w4a4_check_routing -- checks a router's output before the path uses it.
  *   Defined by: rainbus review, prerequisites "MoE and grouped GEMM" (each
  *   token goes to k distinct experts of E; an expert may receive none).

@@ -47,6 +47,8 @@ _SIGS = {
                                     c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "w4a4_mx8_quantize": (c_int, [c_vp, c_i64, c_int, c_vp, c_vp, c_vp, c_vp, c_i64, c_vp]),
     "w4a4_check_routing": (c_int, [c_vp, c_i64, c_int, c_int, c_vp, c_vp]),
+    "w4a4_quantize_permute_noalloc": (c_int, [c_vp, c_i64, c_int, c_vp, c_int, c_int, c_int,
+                                              c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "w4a4_status_string": (ctypes.c_char_p, [c_int]),
     "w4a4_last_error": (ctypes.c_char_p, []),
     "w4a4_profiler_enable": (c_int, [c_int]),
@@ -168,6 +170,33 @@ def w4a4_quantize_permute_domain(x, topk_idx, E, row_align=1, group_rows=1, out=
         _p(x), T, K, _p(topk_idx), k, E, row_align, group_rows,
         _p(out["codes"]), _p(out["scales"]), _p(out["outer"]), _p(out["offsets"]),
         _p(out["row_map"]), _p(out["src_row"]), _p(ws), ws.numel(), _stream()))
+    return out
+
+
+def w4a4_quantize_permute_noalloc(x, topk_idx, E, row_align=1, out=None):
+    """w4a4_quantize_permute without a workspace (the library's per-GPU scratch holds
+    the routing counts).  `out`: preallocated outputs as w4a4_quantize_permute returns
+    them (allocated here when None)."""
+    lib = load()
+    T, K = x.shape
+    dev = x.device
+    if topk_idx is None:
+        k, E, row_align = 1, 1, 1
+    else:
+        k = topk_idx.shape[1]
+    cap = rows_capacity(T, k, E, row_align)
+    if out is None:
+        out = dict(
+            codes=torch.empty(cap, K // 2, dtype=torch.uint8, device=dev),
+            scales=torch.empty(cap, K // 16, dtype=torch.uint8, device=dev),
+            outer=torch.empty(cap, dtype=torch.float32, device=dev),
+            offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+            row_map=torch.empty(T, k, dtype=torch.int32, device=dev),
+            src_row=torch.empty(cap, dtype=torch.int32, device=dev))
+    _check(lib.w4a4_quantize_permute_noalloc(
+        _p(x), T, K, _p(topk_idx), k, E, row_align,
+        _p(out["codes"]), _p(out["scales"]), _p(out["outer"]), _p(out["offsets"]),
+        _p(out["row_map"]), _p(out["src_row"]), _stream()))
     return out
 
 

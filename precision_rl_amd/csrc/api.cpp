@@ -295,6 +295,29 @@ w4a4_status check_quantize_permute(const void* x, int64_t T, int K, const int32_
 }
 }  // namespace
 
+w4a4_status w4a4_quantize_permute_noalloc(const void* x, int64_t T, int K, const int32_t* topk_idx, int k,
+                                          int E, int row_align, uint8_t* codes, uint8_t* scales, float* outer,
+                                          int32_t* expert_offsets, int32_t* row_map, int32_t* src_row,
+                                          void* stream) {
+  g_last_error.clear();
+  w4a4_status st = check_quantize_permute(x, T, K, topk_idx, k, E, row_align, codes, scales, outer,
+                                          expert_offsets, row_map, src_row);
+  if (st != W4A4_OK) return st;
+  const size_t need = topk_idx != nullptr ? round_up(route_workspace_bytes(T, E)) : 0;
+  if (need > kNoAllocScratchBytes)
+    return fail(W4A4_ERR_UNSUPPORTED,
+                "routing scratch of %zu bytes exceeds the library's %zu-byte scratch "
+                "(fewer tokens or experts, or w4a4_quantize_permute with a workspace)",
+                need, kNoAllocScratchBytes);
+  void* scratch_ptr = noalloc_scratch();
+  if (scratch_ptr == nullptr) return fail(W4A4_ERR_LAUNCH, "the scratch address of the current device was not found");
+  if (!launch_quantize_permute(static_cast<const uint16_t*>(x), T, K, topk_idx, k, E, row_align, codes, scales,
+                               outer, expert_offsets, row_map, src_row, scratch_ptr,
+                               static_cast<hipStream_t>(stream)))
+    return W4A4_ERR_LAUNCH;
+  return W4A4_OK;
+}
+
 w4a4_status w4a4_check_routing(const int32_t* topk_idx, int64_t T, int k, int E, int32_t* error_word,
                                void* stream) {
   g_last_error.clear();

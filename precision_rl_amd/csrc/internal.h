@@ -46,6 +46,12 @@ bool launch_check_routing(const int32_t* topk_idx, int64_t T, int k, int E, int3
 
 size_t route_workspace_bytes(int64_t T, int E);
 
+// Scratch of the allocation-free quantize+permute: a file-scope device array
+// of kNoAllocScratchBytes per GPU; noalloc_scratch() returns the current
+// device's address of it (looked up once per device; nullptr on failure).
+constexpr size_t kNoAllocScratchBytes = size_t{1} << 20;
+void* noalloc_scratch();
+
 // Route, per-token amax, two-level NVFP4, scatter to k rows.
 bool launch_quantize_permute(const uint16_t* x, int64_t T, int K, const int32_t* topk_idx,
                              int k, int E, int row_align, uint8_t* codes, uint8_t* scales,

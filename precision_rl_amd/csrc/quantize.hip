@@ -19,6 +19,7 @@
 // the per-element work is seven integer compares on the bf16 bit pattern.
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "device_common.h"
@@ -990,6 +991,33 @@ bool launch_check_routing(const int32_t* topk_idx, int64_t T, int k, int E, int3
   launch_kernel("routing_check", routing_check_kernel, dim3(static_cast<unsigned>((T + 255) / 256)), dim3(256), 0, s,
                 topk_idx, T, k, E, err);
   return launch_ok("routing_check");
+}
+
+// ------------------------------------------------- allocation-free scratch
+// The routing scratch (per-chunk expert counts and expert totals) of the
+// allocation-free quantize+permute entry point lives in this file-scope
+// array: each GPU the library runs on holds its own copy until the process
+// ends.  Host code never passes the array's name to a kernel (on the host it
+// is only a stand-in for the symbol); it looks up each device's address once,
+// with that device current, and passes that.  Every call on one GPU shares
+// the array, so calls that overlap on one GPU race.  Nothing in it has to
+// start at zero: the count kernel writes every chunk's counts and the scan
+// writes every expert total before they are read.
+__device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+void* noalloc_scratch() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    ptrs[dev] = p;
+  }
+  return ptrs[dev];
 }
 
 }  // namespace w4a4
