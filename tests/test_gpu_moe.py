@@ -311,7 +311,7 @@ def test_requant_bit_exact_on_the_gpus_own_a(T, H, E, k, seed):
     print_case("requant_bit_exact", T=T, H=H, E=E, k=k, I=I)
     run = Run(d, T, H, E, k, I, A=16)
     rows = run.rows
-    a = bf16_host(run.f["a"])[:rows]
+    a = bf16_host(run.f["a"][:rows])
     c, s, g = q.quantize_rows(a)
     assert np.array_equal(u8(run.f["a_codes"])[:rows], q.pack_codes(c))
     assert np.array_equal(u8(run.f["a_scales"])[:rows], s)
