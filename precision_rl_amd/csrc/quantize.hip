@@ -518,7 +518,13 @@ quant_rows_kernel(const uint16_t* __restrict__ x, int64_t n_rows, int K,
       const int p = tl + i * TEAM;
       if (p < pairs) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) buf[i][q] = src[p * 4 + q];
+        for (int q = 0; q < 4; ++q) {
+          // the activations are read once, from HBM: non-temporal (encoder
+          // -8% flushed); the requantised a was just written by FC1 and may
+          // still sit in the MALL: plain loads
+          if constexpr (MODE == RowMode::Requant) buf[i][q] = src[p * 4 + q];
+          else buf[i][q] = __builtin_nontemporal_load(src + p * 4 + q);
+        }
       }
     }
   };
