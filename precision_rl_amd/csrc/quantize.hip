@@ -10,13 +10,19 @@
 //   g   = RN_f32(max|x| / (6*448))
 //   d_b = Q_E4M3(amax(block b) / (6 g))          one E4M3 scale per 16 elements
 //   c   = Q_E2M1(x / (g d_b))                    round to nearest, ties to even
-// Every Q(.) rounds the exact quotient.  The E4M3 quotient is formed as one
+// Every Q(.) rounds the exact quotient.  Directly, the E4M3 quotient is one
 // correctly rounded float64 division, which keeps the side of every rounding
-// midpoint (operands have <= 8 and <= 26 significant bits).  For the E2M1 codes
-// the seven midpoints mu * g * d_b (mu in .25 .75 1.25 1.75 2.5 3.5 5) are
-// exact float64 products; each is turned into the smallest bf16 value that a
-// bf16 |x| must reach to cross it (ties resolved towards the even code), so
-// the per-element work is seven integer compares on the bf16 bit pattern.
+// midpoint (operands have <= 8 and <= 26 significant bits), and for the E2M1
+// codes the seven midpoints mu * g * d_b (mu in .25 .75 1.25 1.75 2.5 3.5 5)
+// are exact float64 products, each turned into the smallest bf16 value that a
+// bf16 |x| must reach to cross it (ties resolved towards the even code); the
+// per-element work is then a three-step search over those thresholds on the
+// bf16 bit patterns.  The row encoder takes a cheaper route to the same bytes
+// for outer scales in [2^-100, 2^100]: a per-row reciprocal of 6 g with an
+// exact check at E4M3 midpoints, and a per-row table of the thresholds of the
+// eight E4M3 mantissas that each block shifts by its scale's exponent (see the
+// table section below; checked against the direct route over every pair of
+// row and block maxima).
 
 #include <algorithm>
 #include <mutex>
@@ -423,18 +429,33 @@ __device__ __forceinline__ PackedThr pack_thresholds(const BlockThresholds& th) 
   return p;
 }
 
+// A constant the compiler cannot see through (an empty asm statement, which
+// it may still hoist and merge): the patterns below stay the instructions they
+// are written as instead of being rewritten for the known value.
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm("" : "+s"(v));
+  return v;
+}
+
+typedef int16_t i16x2_t __attribute__((ext_vector_type(2)));
+
 // 0xFFFF in each 16-bit half whose magnitude reaches the threshold: the sign
-// of t' - m, spread over the half (two packed 16-bit integer instructions,
-// written out because the compiler otherwise unpacks them into compares).
+// of t' - m, spread over the half (v_pk_sub_i16 and v_pk_ashrrev_i16; with a
+// visible shift count of 15 the compiler turns the shift into compares on
+// unpacked halves).
 __device__ __forceinline__ uint32_t reach(uint32_t tp, uint32_t m) {
-  uint32_t r;
-  asm("v_pk_sub_i16 %0, %1, %2\n\tv_pk_ashrrev_i16 %0, %3, %0"
-      : "=&v"(r) : "v"(tp), "v"(m), "s"(0x000F000Fu));   // shift count 15 in both halves
-  return r;
+  const i16x2_t d = __builtin_bit_cast(i16x2_t, tp) - __builtin_bit_cast(i16x2_t, m);
+  return __builtin_bit_cast(uint32_t, d >> __builtin_bit_cast(i16x2_t, opaque(0x000F000Fu)));
 }
 
 __device__ __forceinline__ uint32_t select_bits(uint32_t mask, uint32_t a, uint32_t b) {
   return (a & mask) | (b & ~mask);   // v_bfi_b32
+}
+
+// (a & mask) | (b & ~mask) as one v_bfi_b32 (with a visible constant mask the
+// compiler splits nested inserts into ands and ors)
+__device__ __forceinline__ uint32_t bit_insert(uint32_t mask, uint32_t a, uint32_t b) {
+  return select_bits(opaque(mask), a, b);
 }
 
 // Two bf16 (one dword, element 2j low) -> two 4-bit codes in the low nibble
@@ -445,7 +466,16 @@ __device__ __forceinline__ uint32_t code_pair(uint32_t w, const PackedThr& p) {
   const uint32_t s2 = reach(select_bits(s4, p.t[5], p.t[1]), m);
   const uint32_t t1 = select_bits(s4, select_bits(s2, p.t[6], p.t[4]), select_bits(s2, p.t[2], p.t[0]));
   const uint32_t s1 = reach(t1, m);
-  return (s4 & 0x00040004u) | (s2 & 0x00020002u) | (s1 & 0x00010001u) | ((w >> 12) & 0x00080008u);
+  // magnitude bits 2..0 of both halves from the masks, bit 3 the element's
+  // sign (w >> 12 moves bits 15 and 31 to 3 and 19 and leaves 20..31 clear)
+  const uint32_t y = bit_insert(0x00070007u, bit_insert(0x00040004u, s4, bit_insert(0x00020002u, s2, s1)),
+                                w >> 12);
+  // the high element's nibble (bits 16..19) next to the low one's: bits 8..31
+  // of the result come from y >> 12, whose bits 8..31 are clear.  Kept opaque
+  // so that the byte shifts of the caller are not folded back into the inserts.
+  uint32_t b = bit_insert(0x0000000Fu, y, y >> 12);
+  asm("" : "+v"(b));
+  return b;
 }
 
 // 16 bf16 (8 dwords) -> 8 code bytes (2 dwords), element 2j in the low nibble of byte j.
@@ -453,26 +483,110 @@ __device__ __forceinline__ u32x2_t encode16(const uint32_t (&w)[8], const Packed
   u32x2_t out;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    uint32_t v = 0;
+    uint32_t v = code_pair(w[4 * h], p);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t c = code_pair(w[4 * h + i], p);
-      v |= ((c | (c >> 12)) & 0xFFu) << (8 * i);
-    }
+    for (int i = 1; i < 4; ++i) v |= code_pair(w[4 * h + i], p) << (8 * i);
     out[h] = v;
   }
   return out;
 }
 
+typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, a),
+                                                                __builtin_bit_cast(u16x2_t, b)));
+}
+
+// Largest bf16 magnitude of 16 elements (magnitudes compare as integers),
+// two at a time in packed 16-bit maxima.
 __device__ __forceinline__ uint32_t amax16_of(const uint32_t (&w)[8]) {
-  uint32_t m = 0;
+  uint32_t m[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t a = w[i] & 0x7FFF7FFFu;
-    const uint32_t lo = a & 0xFFFFu, hi = a >> 16;
-    m = max(m, max(lo, hi));
+  for (int i = 0; i < 8; ++i) m[i] = w[i] & 0x7FFF7FFFu;
+  const uint32_t a = pk_max_u16(pk_max_u16(pk_max_u16(m[0], m[1]), pk_max_u16(m[2], m[3])),
+                                pk_max_u16(pk_max_u16(m[4], m[5]), pk_max_u16(m[6], m[7])));
+  return max(a & 0xFFFFu, a >> 16);
+}
+
+// ------------------------------------------------ per-row threshold table
+// With outer scale g, a block whose E4M3 scale is the normal value
+// d = (1 + f/8) 2^e has the crossing thresholds
+//   t_j = bf16ceil(mu_j g (1 + f/8) 2^e) = bf16ceil(mu_j g (1 + f/8)) + 128 e
+// as bf16 bit patterns, whenever both sides are normal bf16 numbers: scaling
+// by 2^e maps the bf16 grid of one binade onto that of another, so the
+// smallest bf16 value at or above a point moves with it.  For
+// 2^-100 <= g <= 2^100 every threshold of every normal E4M3 scale
+// (2^-6 <= d <= 448) lies between 2^-103 and 2^113, so a row needs only the
+// 8 x 7 thresholds of d in [1, 2); each block adds 128 e to both halves of the
+// packed search form.  The table sits in LDS, one 9-row table per team (row 8:
+// the zero scale's never-crossed sentinel, stored pre-biased for the shift
+// e = -7 that a zero code implies).  Blocks with a subnormal E4M3 scale, and
+// rows with g outside those bounds, build their thresholds directly.
+constexpr int kThrRows = 9;
+constexpr int kThrStride = 8;                                       // seven thresholds and a pad
+constexpr uint32_t kZeroScaleRow = 0x7FFF7FFFu + 7u * 0x00800080u;  // 0x7FFF in both halves after the shift
+
+// Packed search form (t - 1 in both halves) of threshold j (midpoint
+// mu_j = mu4 / 4) of d = (8 + f) / 8.  The product P = g mu_j (8 + f) / 8 has
+// at most 33 significant bits; it is split into its float rounding hi and the
+// exact residual lo = P - hi (an fma; no underflow for g >= 2^-100), whose sign
+// places P against hi: the smallest float >= P (odd j: reaching the midpoint
+// crosses it) or > P (even j: a tie stays on the even code below) is hi or
+// the float above it.
+__device__ __forceinline__ uint32_t table_threshold(float g, float mu4, int j, int f) {
+  const float c = mu4 * static_cast<float>(8 + f) * 0x1p-5f;   // exact: <= 9 significant bits
+  const float hi = __fmul_rn(g, c);
+  const float lo = __fmaf_rn(g, c, -hi);
+  const bool up = (j & 1) ? lo > 0.0f : lo >= 0.0f;
+  const uint32_t t = (__float_as_uint(hi) + (up ? 1u : 0u) + 0xFFFFu) >> 16;
+  return ((t - 1u) & 0xFFFFu) * 0x00010001u;
+}
+
+// E4M3 code of q = amax / (6 g), rounded to nearest even and saturated at 448,
+// from q' = amax * RN64(1 / (6 g)).  q' is within 2^-51 of q (relative); when
+// q is not itself a rounding midpoint it differs from every E4M3 midpoint M
+// by more than 2^-31 of M (M has <= 5 significant bits, amax <= 8, 6 g <= 26),
+// so q' and its float rounding lie on the same side of M as q.  Only when the
+// float lands exactly on a midpoint is the side decided by the exact product
+// 6 g M (<= 31 significant bits, exact in FP64) against amax.
+__device__ __forceinline__ uint32_t e4m3_code_fast(uint32_t amax16, double inv6g, double g6) {
+  const double ab = static_cast<double>(bf16_to_f32(static_cast<uint16_t>(amax16)));
+  const float q = static_cast<float>(ab * inv6g);
+  const uint32_t qb = __float_as_uint(q);
+  const float qs = q * 512.0f;          // subnormal E4M3 values are multiples of 2^-9
+  const bool sub = q < 0x1p-6f;
+  // normal range: keep 3 mantissa bits, round half to even on the float's bits
+  // (a carry moves to the next binade); the code is the shifted pattern
+  // rebased from float exponent bias 127 to E4M3 bias 7
+  uint32_t c = sub ? static_cast<uint32_t>(rintf(qs)) : ((qb + 0x7FFFFu + ((qb >> 20) & 1u)) >> 20) - 960u;
+  const bool mid = sub ? (qs - floorf(qs)) == 0.5f : (qb & 0xFFFFFu) == 0x80000u;
+  if (mid) {
+    const double m = g6 * static_cast<double>(q);
+    const uint32_t lo = sub ? static_cast<uint32_t>(floorf(qs)) : (qb >> 20) - 960u;
+    if (ab > m) c = lo + 1u;
+    else if (ab < m) c = lo;
   }
-  return m;
+  return min(c, 0x7Eu);
+}
+
+// The thresholds of a block with normal E4M3 scale code c (or c = 0) from its
+// row's table.
+__device__ __forceinline__ PackedThr table_thresholds(const uint32_t* tbl, uint32_t c) {
+  const uint32_t ex = c >> 3;                          // biased exponent e + 7; 0 for c = 0
+  const uint32_t row = ex != 0u ? (c & 7u) : 8u;
+  const uint32_t shift = (ex - 7u) * 0x00800080u;      // 128 e in both halves (mod 2^32)
+  const u32x4_t a = *reinterpret_cast<const u32x4_t*>(tbl + row * kThrStride);
+  const u32x4_t b = *reinterpret_cast<const u32x4_t*>(tbl + row * kThrStride + 4);
+  PackedThr p;
+  p.t[0] = a[0] + shift;
+  p.t[1] = a[1] + shift;
+  p.t[2] = a[2] + shift;
+  p.t[3] = a[3] + shift;
+  p.t[4] = b[0] + shift;
+  p.t[5] = b[1] + shift;
+  p.t[6] = b[2] + shift;
+  return p;
 }
 
 enum class RowMode { Scatter, Identity, Requant };
@@ -509,6 +623,13 @@ quant_rows_kernel(const uint16_t* __restrict__ x, int64_t n_rows, int K,
   if constexpr (MODE == RowMode::Requant) n = min<int64_t>(n, offsets[E]);
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kWavesPerBlock * kRowsPerWave;
   int64_t r = (static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave) * kRowsPerWave + team;
+
+  // the team's threshold table (NVFP4 only)
+  __shared__ uint32_t thr_lds[MX ? 1 : kWavesPerBlock * kRowsPerWave * kThrRows * kThrStride];
+  uint32_t* const tbl = thr_lds + (MX ? 0 : (wave * kRowsPerWave + team) * kThrRows * kThrStride);
+  // lane tl fills column j = tl % 8 of rows tl / 8, tl / 8 + TEAM / 8, ...
+  const int tj = tl & 7;
+  const float mu4 = static_cast<float>(((tj < 4 ? 0x07050301u : 0x00140E0Au) >> (8 * (tj & 3))) & 0xFFu);
 
   u32x4_t cur[PB][4], nxt[PB][4];
   auto load = [&](int64_t row, u32x4_t (&buf)[PB][4]) {
@@ -548,12 +669,30 @@ quant_rows_kernel(const uint16_t* __restrict__ x, int64_t n_rows, int K,
       }
     }
     float g = 0.0f;
+    bool fast = false;
+    double g6 = 0.0, inv6g = 0.0;
     if constexpr (!MX) {
 #pragma unroll
       for (int off = TEAM / 2; off > 0; off >>= 1) amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), off, kWave)));
       // a wider outer-scale domain: the group's max instead of the row's
       if (group_amax != nullptr) amax = group_amax[r / group_rows];
       g = outer_scale(amax);
+      fast = g == 0.0f || (g >= 0x1p-100f && g <= 0x1p100f);
+      g6 = 6.0 * static_cast<double>(g);
+      inv6g = g > 0.0f ? 1.0 / g6 : 0.0;
+      // this row's table; the wave's reads of the previous row's table come
+      // first (a wave's LDS operations complete in order)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int s = 0; s < 64 / TEAM; ++s) {
+        const int f = (tl >> 3) + s * (TEAM / 8);
+        if (tj < 7) tbl[f * kThrStride + tj] = table_threshold(g, mu4, tj, f);
+      }
+      if (tl < 8) tbl[8 * kThrStride + tl] = kZeroScaleRow;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 
     // destination rows
@@ -610,11 +749,20 @@ quant_rows_kernel(const uint16_t* __restrict__ x, int64_t n_rows, int K,
       for (int h = 0; h < 2; ++h) {
         const uint32_t w[8] = {cur[i][2 * h][0], cur[i][2 * h][1], cur[i][2 * h][2], cur[i][2 * h][3],
                                cur[i][2 * h + 1][0], cur[i][2 * h + 1][1], cur[i][2 * h + 1][2], cur[i][2 * h + 1][3]};
-        const double ab = static_cast<double>(bf16_to_f32(static_cast<uint16_t>(bm[i][h])));
-        double dval = 0.0;
         uint32_t dbits = 0;
-        if (g > 0.0f) dbits = e4m3_rne(ab / (6.0 * static_cast<double>(g)), &dval);
-        const PackedThr pt = pack_thresholds(make_thresholds(static_cast<double>(g) * dval));
+        PackedThr pt;
+        if (fast) {
+          dbits = e4m3_code_fast(bm[i][h], inv6g, g6);
+          if (dbits - 1u < 7u)   // subnormal E4M3 scale dbits * 2^-9
+            pt = pack_thresholds(make_thresholds(static_cast<double>(g) * (static_cast<double>(dbits) * 0x1p-9)));
+          else
+            pt = table_thresholds(tbl, dbits);
+        } else {
+          const double ab = static_cast<double>(bf16_to_f32(static_cast<uint16_t>(bm[i][h])));
+          double dval = 0.0;
+          if (g > 0.0f) dbits = e4m3_rne(ab / g6, &dval);
+          pt = pack_thresholds(make_thresholds(static_cast<double>(g) * dval));
+        }
         const u32x2_t c2 = encode16(w, pt);
         cw[2 * h] = c2[0];
         cw[2 * h + 1] = c2[1];

@@ -1,0 +1,177 @@
+// Host restatement of the NVFP4 row encoder's per-block scale and threshold
+// arithmetic (precision_rl_amd/csrc/quantize.hip), checked exhaustively.
+//
+// The encoder picks a block's E4M3 scale code d and the seven bf16 crossing
+// thresholds of its E2M1 midpoints from two numbers only: the bf16 magnitude
+// of the row (or outer-scale group) maximum, which fixes g = RN_f32(amax/2688),
+// and the bf16 magnitude of the block maximum (miniTE Technical Report,
+// section 5.1, block-scale equation).  The kernel has two ways to get them:
+//   direct:  d = RNE_E4M3(b / (6 g)) by one correctly rounded FP64 division,
+//            thresholds = the smallest bf16 value at or above (or above)
+//            mu_j * g * d, each from an exact FP64 product;
+//   table:   d from b * RN64(1/(6 g)) with an exact check at E4M3 midpoints,
+//            thresholds from a per-row table of the eight E4M3 mantissas at
+//            exponent 0, shifted by the block's exponent.
+// This program runs both over every pair (row maximum, block maximum <= row
+// maximum) of finite bf16 magnitudes -- the whole input domain of that step --
+// and reports any pair where the scale byte or a packed threshold differs.
+// Arithmetic: IEEE binary32/binary64 round-to-nearest and fused multiply-add,
+// as on the GPU (built without contraction).
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <thread>
+
+namespace {
+
+uint32_t bits_of(float f) { uint32_t u; std::memcpy(&u, &f, 4); return u; }
+float float_of(uint32_t u) { float f; std::memcpy(&f, &u, 4); return f; }
+float bf16_value(uint32_t b) { return float_of(b << 16); }
+
+// ---------------------------------------------------------------- direct
+uint32_t e4m3_rne(double q, double* val) {
+  if (!(q > 0.0)) { *val = 0.0; return 0u; }
+  if (q >= 448.0) { *val = 448.0; return 0x7Eu; }
+  int ex;
+  std::frexp(q, &ex);
+  int e = std::max(ex - 1, -6);
+  const double v = std::ldexp(std::rint(std::ldexp(q, 3 - e)), e - 3);
+  *val = v;
+  if (v == 0.0) return 0u;
+  std::frexp(v, &ex);
+  const int e2 = ex - 1;
+  if (e2 < -6) return static_cast<uint32_t>(std::ldexp(v, 9));
+  return static_cast<uint32_t>(((e2 + 7) << 3) | (static_cast<int>(std::ldexp(v, 3 - e2)) - 8));
+}
+
+uint32_t ceil_bf16(float f) { return (bits_of(f) + 0xFFFFu) >> 16; }
+uint32_t at_or_above(double t) {
+  float f = static_cast<float>(t);
+  if (static_cast<double>(f) < t) f = float_of(bits_of(f) + 1u);
+  return ceil_bf16(f);
+}
+uint32_t above(double t) {
+  float f = static_cast<float>(t);
+  if (static_cast<double>(f) <= t) f = float_of(bits_of(f) + 1u);
+  return ceil_bf16(f);
+}
+
+struct Packed { uint32_t t[7]; };
+
+Packed direct_thresholds(double u) {
+  static const double mu[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
+  Packed p;
+  for (int j = 0; j < 7; ++j) {
+    uint32_t t = 0xFFFFu;
+    if (u > 0.0) t = (j & 1) ? at_or_above(mu[j] * u) : above(mu[j] * u);
+    const uint32_t v = t >= 0x8000u ? 0x7FFFu : ((t - 1u) & 0xFFFFu);
+    p.t[j] = v * 0x00010001u;
+  }
+  return p;
+}
+
+void direct(float g, uint32_t b, uint32_t* code, Packed* p) {
+  double d = 0.0;
+  *code = g > 0.0f ? e4m3_rne(static_cast<double>(bf16_value(b)) / (6.0 * static_cast<double>(g)), &d) : 0u;
+  *p = direct_thresholds(static_cast<double>(g) * d);
+}
+
+// ----------------------------------------------------------------- table
+struct Row {
+  float g;
+  bool table;
+  double g6, inv6g;
+  uint32_t tbl[9][8];
+};
+
+uint32_t table_entry(float g, float mu4, int j, int f) {
+  const float c = mu4 * static_cast<float>(8 + f) * 0x1p-5f;
+  volatile float rounded = g * c;          // a plain product, not fused below
+  const float hi = rounded;
+  const float lo = std::fmaf(g, c, -hi);
+  const bool up = (j & 1) ? lo > 0.0f : lo >= 0.0f;
+  const uint32_t t = (bits_of(hi) + (up ? 1u : 0u) + 0xFFFFu) >> 16;
+  return ((t - 1u) & 0xFFFFu) * 0x00010001u;
+}
+
+void make_row(uint32_t amax, Row* r) {
+  r->g = static_cast<float>(static_cast<double>(bf16_value(amax)) / 2688.0);
+  const float g = r->g;
+  r->table = g == 0.0f || (g >= 0x1p-100f && g <= 0x1p100f);
+  r->g6 = 6.0 * static_cast<double>(g);
+  r->inv6g = g > 0.0f ? 1.0 / r->g6 : 0.0;
+  static const float mu4[7] = {1, 3, 5, 7, 10, 14, 20};
+  for (int f = 0; f < 8; ++f)
+    for (int j = 0; j < 7; ++j) r->tbl[f][j] = table_entry(g, mu4[j], j, f);
+  for (int j = 0; j < 8; ++j) r->tbl[8][j] = 0x7FFF7FFFu + 7u * 0x00800080u;
+}
+
+uint32_t e4m3_code_table(uint32_t b, double inv6g, double g6) {
+  const double ab = static_cast<double>(bf16_value(b));
+  const float q = static_cast<float>(ab * inv6g);
+  const uint32_t qb = bits_of(q);
+  const float qs = q * 512.0f;
+  const bool sub = q < 0x1p-6f;
+  uint32_t c = sub ? static_cast<uint32_t>(std::rint(qs)) : ((qb + 0x7FFFFu + ((qb >> 20) & 1u)) >> 20) - 960u;
+  const bool mid = sub ? (qs - std::floor(qs)) == 0.5f : (qb & 0xFFFFFu) == 0x80000u;
+  if (mid) {
+    const double m = g6 * static_cast<double>(q);
+    const uint32_t lo = sub ? static_cast<uint32_t>(std::floor(qs)) : (qb >> 20) - 960u;
+    if (ab > m) c = lo + 1u;
+    else if (ab < m) c = lo;
+  }
+  return std::min(c, 0x7Eu);
+}
+
+void table(const Row& r, uint32_t b, uint32_t* code, Packed* p) {
+  if (!r.table) { direct(r.g, b, code, p); return; }
+  const uint32_t c = e4m3_code_table(b, r.inv6g, r.g6);
+  *code = c;
+  if (c - 1u < 7u) { *p = direct_thresholds(static_cast<double>(r.g) * (static_cast<double>(c) * 0x1p-9)); return; }
+  const uint32_t ex = c >> 3, row = ex != 0u ? (c & 7u) : 8u, shift = (ex - 7u) * 0x00800080u;
+  for (int j = 0; j < 7; ++j) p->t[j] = r.tbl[row][j] + shift;
+}
+
+}  // namespace
+
+int main() {
+  std::atomic<long> pairs{0}, mismatches{0}, on_midpoint{0}, near_ties{0};
+  auto work = [&](uint32_t first, uint32_t step) {
+    long n = 0, bad = 0, mids = 0, near = 0;
+    for (uint32_t amax = first; amax < 0x7F80u; amax += step) {
+      Row r;
+      make_row(amax, &r);
+      for (uint32_t b = 0; b <= amax; ++b) {
+        uint32_t c0, c1;
+        Packed p0, p1;
+        direct(r.g, b, &c0, &p0);
+        table(r, b, &c1, &p1);
+        ++n;
+        bool same = c0 == c1;
+        for (int j = 0; j < 7; ++j) same = same && p0.t[j] == p1.t[j];
+        if (!same) {
+          if (bad < 4) std::printf("mismatch: row max %04x block max %04x scale %02x vs %02x\n", amax, b, c0, c1);
+          ++bad;
+        }
+        if (r.table && r.g > 0.0f) {
+          const double ab = static_cast<double>(bf16_value(b));
+          const float q = static_cast<float>(ab * r.inv6g);
+          const float qs = q * 512.0f;
+          const bool mid = q < 0x1p-6f ? (qs - std::floor(qs)) == 0.5f : (bits_of(q) & 0xFFFFFu) == 0x80000u;
+          if (mid) { ++mids; if (r.g6 * static_cast<double>(q) != ab) ++near; }
+        }
+      }
+    }
+    pairs += n; mismatches += bad; on_midpoint += mids; near_ties += near;
+  };
+  const unsigned n_threads = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+  std::thread pool[16];
+  for (unsigned t = 0; t < n_threads; ++t) pool[t] = std::thread(work, t, n_threads);
+  for (unsigned t = 0; t < n_threads; ++t) pool[t].join();
+  std::printf("pairs %ld mismatches %ld midpoint %ld near_ties %ld\n", pairs.load(), mismatches.load(),
+              on_midpoint.load(), near_ties.load());
+  return mismatches.load() == 0 ? 0 : 1;
+}

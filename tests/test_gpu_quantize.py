@@ -169,6 +169,57 @@ def test_quantize_edge_rows():
     assert np.array_equal(f32_bits(got["outer"]), g.view(np.uint32))
 
 
+def _scale_midpoint_rows(rng, n_rows):
+    """Rows of 16 blocks whose block maxima b put b / (6 g) on an E4M3
+    rounding midpoint after rounding to float32: exact ties, and quotients
+    within half a float32 ulp of a midpoint, whose side only the exact
+    quotient decides.  Row maxima sweep the bf16 range (outer scales from
+    2^-137 to 2^116), with four rows on either side of g = 2^-100 and
+    g = 2^100."""
+    K = 256
+    mags = np.arange(0x0001, 0x7F80, dtype=np.uint32)
+    vals = (mags << 16).view(np.float32).astype(np.float64)
+    row_max = list(rng.integers(0x0100, 0x7F00, n_rows - 4)) + [0x1327, 0x1328, 0x7728, 0x7729]
+    rows = []
+    for a in row_max:
+        A = float(np.uint32(a << 16).view(np.float32))
+        g = float(np.float32(A / 2688.0))
+        with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+            q = (vals / (6.0 * g)).astype(np.float32)
+            qb = q.view(np.uint32)
+            qs = q.astype(np.float64) * 512.0
+            mid = np.where(q < 2.0 ** -6, qs - np.floor(qs) == 0.5, (qb & 0xFFFFF) == 0x80000)
+        cand = mags[mid & (mags <= a)]
+        b = list(rng.permutation(cand)[:15])
+        b += list(rng.integers(0, a + 1, 15 - len(b)))
+        blocks = [a] + b
+        row = np.empty(K)
+        for i, bm in enumerate(blocks):
+            m = float(np.uint32(int(bm) << 16).view(np.float32))
+            blk = rng.uniform(-m, m, 16)
+            blk[rng.integers(16)] = m * rng.choice([-1.0, 1.0])
+            row[16 * i:16 * i + 16] = blk
+        rows.append(row)
+    return np.array(rows)
+
+
+def test_quantize_scale_midpoint_rows():
+    """Block scales whose quotient lies on or next to an E4M3 midpoint, over
+    the whole range of outer scales: identity routing, bit-exact."""
+    b = _binding()
+    rng = np.random.default_rng(77)
+    x = q.round_bf16(_scale_midpoint_rows(rng, 192))
+    bits = q.f64_to_bf16_bits(x)
+    x = q.bf16_bits_to_f64(bits)
+    print_case("scale_midpoint_rows", rows=x.shape[0], K=x.shape[1])
+    got = b.w4a4_quantize_permute(bf16_dev(bits, torch), None, 1)
+    torch.cuda.synchronize()
+    c, s, g = q.quantize_rows(x)
+    assert np.array_equal(f32_bits(got["outer"]), g.view(np.uint32))
+    assert np.array_equal(u8(got["scales"]), s)
+    assert np.array_equal(u8(got["codes"]), q.pack_codes(c))
+
+
 def test_weight_quantization_identity_mode():
     b = _binding()
     d = synth.make_inputs(16, 512, 4, 2, 256, seed=5)
