@@ -31,9 +31,12 @@
  *    different workspaces.
  *  - w4a4_expert_bwd runs two of its kernels (the wgrad tile schedule and the
  *    copy of x to the expert rows) on a second stream of the current device
- *    (created on first use, default priority), forked from `stream` and
- *    joined back into it before the call's last kernels: work enqueued on
- *    `stream` after the call sees every output.
+ *    (one per device, created on first use, default priority), forked from
+ *    `stream` and joined back into it before the call's last kernels: work
+ *    enqueued on `stream` after the call sees every output.  Each host
+ *    thread forks and joins with events of its own, so concurrent calls from
+ *    several threads enqueue without a common lock; their side-stream
+ *    kernels share that stream in enqueue order.
  *
  * Data formats (miniTE Technical Report, sections 2.2 and 5.1; rainbus review
  * of the miniTE paper, "prerequisites: the NVFP4 format" and method step 4):

@@ -1,9 +1,9 @@
 // Host side of the C ABI declared in include/w4a4_moe.h: argument validation,
 // workspace carving and the launch sequence of each call.  No device-memory
 // allocation, no synchronisation, no device reads on the host.  The backward
-// runs two HBM-bound kernels on a second stream of the same device (default
-// priority, created once per device with its events), forked from and joined
-// back into the caller's stream.
+// runs two of its kernels on a second stream of the same device (default
+// priority, created once per device; fork / join events per host thread),
+// forked from and joined back into the caller's stream.
 
 #include <hip/hip_runtime.h>
 
@@ -36,31 +36,41 @@ w4a4_status fail(w4a4_status st, const char* fmt, ...) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// The side stream of the current device and its fork / join events.  Callers
-// hold side_mutex() from the fork to the join, so that concurrent calls on
-// different streams never interleave their event records and waits.
+// The side stream of the current device (one per device, created once under
+// a lock) and this host thread's fork / join events for it (created on the
+// thread's first backward on the device, held until the process ends).
+// Calls from different threads record and wait on their own events, so their
+// enqueues share no lock; their side-stream kernels run on the one stream in
+// enqueue order, each behind the fork event of its own call.
 struct SideStream {
   hipStream_t stream = nullptr;
   static constexpr int kEvents = 3;
   hipEvent_t fork[kEvents] = {}, join[kEvents] = {};
 };
-std::mutex& side_mutex() {
+bool side_stream(SideStream& out) {
   static std::mutex mu;
-  return mu;
-}
-bool side_stream(SideStream& out) {   // call with side_mutex() held
-  static std::map<int, SideStream> per_device;
+  static std::map<int, hipStream_t> streams;
+  thread_local std::map<int, SideStream> mine;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return false;
-  auto it = per_device.find(dev);
-  if (it == per_device.end()) {
+  auto it = mine.find(dev);
+  if (it == mine.end()) {
     SideStream ss;
-    if (hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) != hipSuccess) return false;
+    {
+      std::lock_guard<std::mutex> lock(mu);
+      auto st = streams.find(dev);
+      if (st == streams.end()) {
+        hipStream_t created = nullptr;
+        if (hipStreamCreateWithFlags(&created, hipStreamNonBlocking) != hipSuccess) return false;
+        st = streams.emplace(dev, created).first;
+      }
+      ss.stream = st->second;
+    }
     for (int i = 0; i < SideStream::kEvents; ++i)
       if (hipEventCreateWithFlags(&ss.fork[i], hipEventDisableTiming) != hipSuccess ||
           hipEventCreateWithFlags(&ss.join[i], hipEventDisableTiming) != hipSuccess)
         return false;
-    it = per_device.emplace(dev, ss).first;
+    it = mine.emplace(dev, ss).first;
   }
   out = it->second;
   return true;
@@ -467,7 +477,6 @@ w4a4_status w4a4_expert_bwd(int64_t T, int H, int I, int E, int k, int row_align
   // GEMM) runs beside the FC2 wgrad and the FC1 dgrad: HBM-bound with few
   // registers and no LDS, beside MFMA-bound GEMMs.  The caller's stream
   // waits for it before the FC1 wgrad.
-  std::lock_guard<std::mutex> lock(side_mutex());
   SideStream side;
   if (!side_stream(side)) return fail(W4A4_ERR_LAUNCH, "side stream / events could not be created");
   auto fork = [&](int i) {

@@ -216,8 +216,9 @@ def test_backward_skewed_split_experts():
 
 def test_backward_concurrent_calls_on_two_streams():
     """Two host threads run the backward at the same time on two streams with
-    their own workspaces (the library's second stream and its fork / join
-    events are shared, under a lock).  Each result equals the sequential one
+    their own workspaces (the library's second stream is shared; each thread
+    forks and joins with events of its own, with no common lock around the
+    enqueue).  Each result equals the sequential one
     bit for bit; the second thread's dy is 2 dy, so its results are exactly
     twice the first's (a power-of-two scale commutes with every rounding)."""
     import threading
