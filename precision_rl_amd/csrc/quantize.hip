@@ -63,6 +63,13 @@ __device__ __forceinline__ uint32_t e4m3_rne(double q, double* val) {
   return static_cast<uint32_t>(((e2 + 7) << 3) | (static_cast<int>(ldexp(v, 3 - e2)) - 8));
 }
 
+// Value of an E4M3FN code (no NaN codes occur here): subnormal m * 2^-9,
+// normal (8 + m) * 2^(e - 10).
+__device__ __forceinline__ double e4m3_value(uint32_t c) {
+  const uint32_t e = c >> 3, m = c & 7u;
+  return e == 0u ? static_cast<double>(m) * 0x1p-9 : ldexp(static_cast<double>(8u + m), static_cast<int>(e) - 10);
+}
+
 __device__ __forceinline__ float next_up(float f) {  // f >= 0, finite
   return __uint_as_float(__float_as_uint(f) + 1u);
 }
@@ -750,19 +757,17 @@ quant_rows_kernel(const uint16_t* __restrict__ x, int64_t n_rows, int K,
         const uint32_t w[8] = {cur[i][2 * h][0], cur[i][2 * h][1], cur[i][2 * h][2], cur[i][2 * h][3],
                                cur[i][2 * h + 1][0], cur[i][2 * h + 1][1], cur[i][2 * h + 1][2], cur[i][2 * h + 1][3]};
         uint32_t dbits = 0;
-        PackedThr pt;
         if (fast) {
           dbits = e4m3_code_fast(bm[i][h], inv6g, g6);
-          if (dbits - 1u < 7u)   // subnormal E4M3 scale dbits * 2^-9
-            pt = pack_thresholds(make_thresholds(static_cast<double>(g) * (static_cast<double>(dbits) * 0x1p-9)));
-          else
-            pt = table_thresholds(tbl, dbits);
-        } else {
-          const double ab = static_cast<double>(bf16_to_f32(static_cast<uint16_t>(bm[i][h])));
-          double dval = 0.0;
-          if (g > 0.0f) dbits = e4m3_rne(ab / g6, &dval);
-          pt = pack_thresholds(make_thresholds(static_cast<double>(g) * dval));
+        } else if (g > 0.0f) {
+          double dval;
+          dbits = e4m3_rne(static_cast<double>(bf16_to_f32(static_cast<uint16_t>(bm[i][h]))) / g6, &dval);
         }
+        // the table for normal scales (and the zero scale) of in-range rows;
+        // subnormal scales and out-of-range rows build the thresholds directly
+        PackedThr pt;
+        if (fast && dbits - 1u >= 7u) pt = table_thresholds(tbl, dbits);
+        else pt = pack_thresholds(make_thresholds(static_cast<double>(g) * e4m3_value(dbits)));
         const u32x2_t c2 = encode16(w, pt);
         cw[2 * h] = c2[0];
         cw[2 * h + 1] = c2[1];

@@ -126,18 +126,38 @@ uint32_t e4m3_code_table(uint32_t b, double inv6g, double g6) {
   return std::min(c, 0x7Eu);
 }
 
+// Value of an E4M3FN code: subnormal m 2^-9, normal (8 + m) 2^(e - 10).
+double e4m3_value(uint32_t c) {
+  const uint32_t e = c >> 3, m = c & 7u;
+  return e == 0u ? static_cast<double>(m) * 0x1p-9 : std::ldexp(static_cast<double>(8u + m), static_cast<int>(e) - 10);
+}
+
 void table(const Row& r, uint32_t b, uint32_t* code, Packed* p) {
-  if (!r.table) { direct(r.g, b, code, p); return; }
-  const uint32_t c = e4m3_code_table(b, r.inv6g, r.g6);
+  uint32_t c = 0;
+  if (r.table) {
+    c = e4m3_code_table(b, r.inv6g, r.g6);
+  } else if (r.g > 0.0f) {
+    double unused;
+    c = e4m3_rne(static_cast<double>(bf16_value(b)) / r.g6, &unused);
+  }
   *code = c;
-  if (c - 1u < 7u) { *p = direct_thresholds(static_cast<double>(r.g) * (static_cast<double>(c) * 0x1p-9)); return; }
-  const uint32_t ex = c >> 3, row = ex != 0u ? (c & 7u) : 8u, shift = (ex - 7u) * 0x00800080u;
-  for (int j = 0; j < 7; ++j) p->t[j] = r.tbl[row][j] + shift;
+  if (r.table && c - 1u >= 7u) {
+    const uint32_t ex = c >> 3, row = ex != 0u ? (c & 7u) : 8u, shift = (ex - 7u) * 0x00800080u;
+    for (int j = 0; j < 7; ++j) p->t[j] = r.tbl[row][j] + shift;
+  } else {
+    *p = direct_thresholds(static_cast<double>(r.g) * e4m3_value(c));
+  }
 }
 
 }  // namespace
 
 int main() {
+  // the decoded value of every code is the value the direct rounding returns
+  for (uint32_t c = 0; c <= 0x7Eu; ++c) {
+    double v;
+    const double q = c == 0 ? 0.0 : e4m3_value(c);
+    if (e4m3_rne(q, &v) != c || v != q) { std::printf("e4m3 value mismatch at code %02x\n", c); return 1; }
+  }
   std::atomic<long> pairs{0}, mismatches{0}, on_midpoint{0}, near_ties{0};
   auto work = [&](uint32_t first, uint32_t step) {
     long n = 0, bad = 0, mids = 0, near = 0;
