@@ -709,8 +709,7 @@ wgrad_kernel(WgradArgs args) {
   const int wm = wave & 3;
   const int wrow = wm * kWM, wcol = (wave >> 2) * kWN;
   const int r32 = lane & 31, hl = lane >> 5;
-  const int m_tiles = args.M / kBM, n_tiles = (args.N + kBN - 1) / kBN;
-  const int tpe = m_tiles * n_tiles;   // tiles per expert
+  const int n_tiles = (args.N + kBN - 1) / kBN;
   // Tiles come from this workgroup's XCD's part of the tile table.  The
   // first two tickets of each workgroup are dealt statically (blockIdx /
   // kXcds and that plus the workgroups per XCD; the counters start past
@@ -841,7 +840,7 @@ wgrad_kernel(WgradArgs args) {
   setup(tc);
   for (int s = 0; s < kAhead && s < tc.nk; ++s) issue(tc, s);
   uint8_t* so = lds + kOutOffset;
-  for (int it = 1;; ++it) {
+  for (;;) {
     floatx16_t acc[kMI][kNI];
     zero_acc(acc);
     // The slice's MFMAs, the next slice's fragments loaded one at a time in
