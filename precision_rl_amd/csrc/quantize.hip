@@ -18,11 +18,12 @@
 // bf16 |x| must reach to cross it (ties resolved towards the even code); the
 // per-element work is then a three-step search over those thresholds on the
 // bf16 bit patterns.  The row encoder takes a cheaper route to the same bytes
-// for outer scales in [2^-100, 2^100]: a per-row reciprocal of 6 g with an
-// exact check at E4M3 midpoints, and a per-row table of the thresholds of the
-// eight E4M3 mantissas that each block shifts by its scale's exponent (see the
-// table section below; checked against the direct route over every pair of
-// row and block maxima).
+// for outer scales in [2^-100, 2^100]: the E4M3 code from a per-row reciprocal
+// of 6 g with an exact check at E4M3 midpoints (checked against the direct
+// route over every pair of row and block maxima), and the E2M1 codes from the
+// hardware FP4 conversion of the quotient bracketed from below and above,
+// which decides every element but those next to an E2M1 midpoint; blocks
+// holding such an element take the exact thresholds.
 
 #include <algorithm>
 #include <mutex>
@@ -516,40 +517,6 @@ __device__ __forceinline__ uint32_t amax16_of(const uint32_t (&w)[8]) {
   return max(a & 0xFFFFu, a >> 16);
 }
 
-// ------------------------------------------------ per-row threshold table
-// With outer scale g, a block whose E4M3 scale is the normal value
-// d = (1 + f/8) 2^e has the crossing thresholds
-//   t_j = bf16ceil(mu_j g (1 + f/8) 2^e) = bf16ceil(mu_j g (1 + f/8)) + 128 e
-// as bf16 bit patterns, whenever both sides are normal bf16 numbers: scaling
-// by 2^e maps the bf16 grid of one binade onto that of another, so the
-// smallest bf16 value at or above a point moves with it.  For
-// 2^-100 <= g <= 2^100 every threshold of every normal E4M3 scale
-// (2^-6 <= d <= 448) lies between 2^-103 and 2^113, so a row needs only the
-// 8 x 7 thresholds of d in [1, 2); each block adds 128 e to both halves of the
-// packed search form.  The table sits in LDS, one 9-row table per team (row 8:
-// the zero scale's never-crossed sentinel, stored pre-biased for the shift
-// e = -7 that a zero code implies).  Blocks with a subnormal E4M3 scale, and
-// rows with g outside those bounds, build their thresholds directly.
-constexpr int kThrRows = 9;
-constexpr int kThrStride = 8;                                       // seven thresholds and a pad
-constexpr uint32_t kZeroScaleRow = 0x7FFF7FFFu + 7u * 0x00800080u;  // 0x7FFF in both halves after the shift
-
-// Packed search form (t - 1 in both halves) of threshold j (midpoint
-// mu_j = mu4 / 4) of d = (8 + f) / 8.  The product P = g mu_j (8 + f) / 8 has
-// at most 33 significant bits; it is split into its float rounding hi and the
-// exact residual lo = P - hi (an fma; no underflow for g >= 2^-100), whose sign
-// places P against hi: the smallest float >= P (odd j: reaching the midpoint
-// crosses it) or > P (even j: a tie stays on the even code below) is hi or
-// the float above it.
-__device__ __forceinline__ uint32_t table_threshold(float g, float mu4, int j, int f) {
-  const float c = mu4 * static_cast<float>(8 + f) * 0x1p-5f;   // exact: <= 9 significant bits
-  const float hi = __fmul_rn(g, c);
-  const float lo = __fmaf_rn(g, c, -hi);
-  const bool up = (j & 1) ? lo > 0.0f : lo >= 0.0f;
-  const uint32_t t = (__float_as_uint(hi) + (up ? 1u : 0u) + 0xFFFFu) >> 16;
-  return ((t - 1u) & 0xFFFFu) * 0x00010001u;
-}
-
 // E4M3 code of q = amax / (6 g), rounded to nearest even and saturated at 448,
 // from q' = amax * RN64(1 / (6 g)).  q' is within 2^-51 of q (relative); when
 // q is not itself a rounding midpoint it differs from every E4M3 midpoint M
@@ -577,23 +544,97 @@ __device__ __forceinline__ uint32_t e4m3_code_fast(uint32_t amax16, double inv6g
   return min(c, 0x7Eu);
 }
 
-// The thresholds of a block with normal E4M3 scale code c (or c = 0) from its
-// row's table.
-__device__ __forceinline__ PackedThr table_thresholds(const uint32_t* tbl, uint32_t c) {
-  const uint32_t ex = c >> 3;                          // biased exponent e + 7; 0 for c = 0
-  const uint32_t row = ex != 0u ? (c & 7u) : 8u;
-  const uint32_t shift = (ex - 7u) * 0x00800080u;      // 128 e in both halves (mod 2^32)
-  const u32x4_t a = *reinterpret_cast<const u32x4_t*>(tbl + row * kThrStride);
-  const u32x4_t b = *reinterpret_cast<const u32x4_t*>(tbl + row * kThrStride + 4);
-  PackedThr p;
-  p.t[0] = a[0] + shift;
-  p.t[1] = a[1] + shift;
-  p.t[2] = a[2] + shift;
-  p.t[3] = a[3] + shift;
-  p.t[4] = b[0] + shift;
-  p.t[5] = b[1] + shift;
-  p.t[6] = b[2] + shift;
-  return p;
+// Value of E4M3 code c (0 < c <= 0x7E) as a float: normal codes are the
+// float with exponent field e + 120 and mantissa m << 20, subnormal ones m 2^-9.
+__device__ __forceinline__ float e4m3_float(uint32_t c) {
+  return c >= 8u ? __uint_as_float((c << 20) + (120u << 23)) : static_cast<float>(c) * 0x1p-9f;
+}
+
+// E2M1 codes of 16 bf16 elements (8 dwords, element 2j low; 8 code bytes,
+// element 2j in the low nibble of byte j) of a block with effective scale
+// D = d g, by the hardware conversion v_cvt_scalef32_pk_fp4_f32 (round to
+// nearest even onto E2M1, saturating at 6, the sign in bit 3), applied to x / D
+// bracketed from both sides.  With ilo = RN(inv (1 - 2^-19)) and
+// ihi = RN(inv (1 + 2^-19)), inv = rcp(RN(D)) within one float ulp, every
+// product RN(x ilo) lies below |x| / D and RN(x ihi) above it (by more than
+// 2^-20 of it: the four roundings add at most 2^-21.4); products that
+// underflow only meet code 0, with the sign of x.  The conversion is monotone,
+// so where the codes of the two products agree (`lo` = `hi`) they are the code
+// of x / D itself; where they differ, by one, an E2M1 midpoint lies between
+// the two products and the element is left to the exact check below.  D = 0 (a
+// zero block scale): ilo = ihi = 0 gives the zero codes with the elements'
+// signs.
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+// Codes of the bf16 pair v, the quotients scaled by `inv`, into byte B of `acc`.
+template <int B>
+__device__ __forceinline__ uint32_t fp4_pair(uint32_t acc, uint32_t v, float inv) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, bf16_lo(v) * inv, bf16_hi(v) * inv, 1.0f, B);
+}
+
+__device__ __forceinline__ void encode16_hw(const uint32_t (&w)[8], float ilo, float ihi, u32x2_t& lo, u32x2_t& hi) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t* p = w + 4 * h;
+    lo[h] = fp4_pair<3>(fp4_pair<2>(fp4_pair<1>(fp4_pair<0>(0u, p[0], ilo), p[1], ilo), p[2], ilo), p[3], ilo);
+    hi[h] = fp4_pair<3>(fp4_pair<2>(fp4_pair<1>(fp4_pair<0>(0u, p[0], ihi), p[1], ihi), p[2], ihi), p[3], ihi);
+  }
+}
+
+// The exact codes of the elements the bracket left open.  The 32 elements of
+// a block pair: code dword k holds elements 8k .. 8k+7 (nibble n: element
+// 8k + n), whose bf16 values are the four dwords of x[k]; nonzero nibbles of
+// `open` mark the undecided elements, whose nibble in `cw` holds the lower of
+// the two candidate codes c and c + 1.  The element takes c + 1 when its
+// magnitude exceeds mu d g, mu the E2M1 midpoint between c and c + 1, or equals
+// it and c is odd (the tie goes to the even code); mu d g has at most 31
+// significant bits (mu <= 3, d <= 4, g 24), so the FP64 product and the
+// comparison are exact.  One element per lane and iteration; the wave loops
+// while any lane has one left (usually once: about one element in 500 is open
+// for continuous data, mostly where rounding g to float32 put x / D within 2^-24
+// of a midpoint).
+__device__ __forceinline__ void settle_open(u32x4_t& cw, u32x4_t open, const u32x4_t (&x)[4], uint32_t sc2, float g) {
+  // 4 mu for c = 0 .. 6 (0.25 0.75 1.25 1.75 2.5 3.5 5), 5 bits each
+  constexpr uint64_t kMid4 = 1ull | 3ull << 5 | 5ull << 10 | 7ull << 15 | 10ull << 20 | 14ull << 25 | 20ull << 30;
+  // the element values as plain registers: selecting among them must stay
+  // v_cndmask (a select between array elements may become a dynamic index,
+  // which would move the row buffer to scratch memory)
+  uint32_t xs[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    xs[j] = x[j >> 2][j & 3];
+    asm("" : "+v"(xs[j]));
+  }
+  while ((open[0] | open[1] | open[2] | open[3]) != 0u) {
+    const bool k0 = open[0] != 0u, k1 = !k0 && open[1] != 0u, k2 = !k0 && !k1 && open[2] != 0u;
+    const bool k3 = !k0 && !k1 && !k2;
+    const uint32_t f = k0 ? open[0] : k1 ? open[1] : k2 ? open[2] : open[3];
+    const uint32_t c = k0 ? cw[0] : k1 ? cw[1] : k2 ? cw[2] : cw[3];
+    const uint32_t sh = static_cast<uint32_t>(__builtin_ctz(f)) & ~3u;   // 4 n
+    const uint32_t n = sh >> 2;
+    uint32_t xq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xq[q] = k0 ? xs[q] : k1 ? xs[4 + q] : k2 ? xs[8 + q] : xs[12 + q];
+    const uint32_t wd = n < 2u ? xq[0] : n < 4u ? xq[1] : n < 6u ? xq[2] : xq[3];
+    const uint32_t mag = ((n & 1u) ? (wd >> 16) : wd) & 0x7FFFu;
+    const uint32_t clo = (c >> sh) & 7u;
+    const uint32_t dbits = (sc2 >> ((k2 || k3) ? 8 : 0)) & 0xFFu;
+    const double mu = static_cast<double>(static_cast<uint32_t>(kMid4 >> (5u * clo)) & 31u) * 0.25;
+    const double t = mu * (e4m3_value(dbits) * static_cast<double>(g));
+    const double xm = static_cast<double>(bf16_to_f32(static_cast<uint16_t>(mag)));
+    const uint32_t up = (xm > t || (xm == t && (clo & 1u) != 0u)) ? 1u : 0u;
+    const uint32_t nc = c + (up << sh);       // c + 1 <= 7: no carry into the sign bit
+    const uint32_t clear = ~(0xFu << sh);
+    cw[0] = k0 ? nc : cw[0];
+    cw[1] = k1 ? nc : cw[1];
+    cw[2] = k2 ? nc : cw[2];
+    cw[3] = k3 ? nc : cw[3];
+    open[0] = k0 ? (open[0] & clear) : open[0];
+    open[1] = k1 ? (open[1] & clear) : open[1];
+    open[2] = k2 ? (open[2] & clear) : open[2];
+    open[3] = k3 ? (open[3] & clear) : open[3];
+  }
 }
 
 enum class RowMode { Scatter, Identity, Requant };
@@ -630,13 +671,6 @@ quant_rows_kernel(const uint16_t* __restrict__ x, int64_t n_rows, int K,
   if constexpr (MODE == RowMode::Requant) n = min<int64_t>(n, offsets[E]);
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kWavesPerBlock * kRowsPerWave;
   int64_t r = (static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave) * kRowsPerWave + team;
-
-  // the team's threshold table (NVFP4 only)
-  __shared__ uint32_t thr_lds[MX ? 1 : kWavesPerBlock * kRowsPerWave * kThrRows * kThrStride];
-  uint32_t* const tbl = thr_lds + (MX ? 0 : (wave * kRowsPerWave + team) * kThrRows * kThrStride);
-  // lane tl fills column j = tl % 8 of rows tl / 8, tl / 8 + TEAM / 8, ...
-  const int tj = tl & 7;
-  const float mu4 = static_cast<float>(((tj < 4 ? 0x07050301u : 0x00140E0Au) >> (8 * (tj & 3))) & 0xFFu);
 
   u32x4_t cur[PB][4], nxt[PB][4];
   auto load = [&](int64_t row, u32x4_t (&buf)[PB][4]) {
@@ -687,19 +721,6 @@ quant_rows_kernel(const uint16_t* __restrict__ x, int64_t n_rows, int K,
       fast = g == 0.0f || (g >= 0x1p-100f && g <= 0x1p100f);
       g6 = 6.0 * static_cast<double>(g);
       inv6g = g > 0.0f ? 1.0 / g6 : 0.0;
-      // this row's table; the wave's reads of the previous row's table come
-      // first (a wave's LDS operations complete in order)
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int s = 0; s < 64 / TEAM; ++s) {
-        const int f = (tl >> 3) + s * (TEAM / 8);
-        if (tj < 7) tbl[f * kThrStride + tj] = table_threshold(g, mu4, tj, f);
-      }
-      if (tl < 8) tbl[8 * kThrStride + tl] = kZeroScaleRow;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 
     // destination rows
@@ -752,6 +773,7 @@ quant_rows_kernel(const uint16_t* __restrict__ x, int64_t n_rows, int K,
           cw[2 * h + 1] = c2[1];
         }
       } else {
+      u32x4_t open = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const uint32_t w[8] = {cur[i][2 * h][0], cur[i][2 * h][1], cur[i][2 * h][2], cur[i][2 * h][3],
@@ -763,16 +785,25 @@ quant_rows_kernel(const uint16_t* __restrict__ x, int64_t n_rows, int K,
           double dval;
           dbits = e4m3_rne(static_cast<double>(bf16_to_f32(static_cast<uint16_t>(bm[i][h]))) / g6, &dval);
         }
-        // the table for normal scales (and the zero scale) of in-range rows;
-        // subnormal scales and out-of-range rows build the thresholds directly
-        PackedThr pt;
-        if (fast && dbits - 1u >= 7u) pt = table_thresholds(tbl, dbits);
-        else pt = pack_thresholds(make_thresholds(static_cast<double>(g) * e4m3_value(dbits)));
-        const u32x2_t c2 = encode16(w, pt);
-        cw[2 * h] = c2[0];
-        cw[2 * h + 1] = c2[1];
+        // in-range rows: the hardware conversion of the bracketed quotient
+        // (its open elements are settled below); out-of-range rows: the
+        // exact thresholds
+        if (fast) {
+          const float inv = dbits != 0u ? __builtin_amdgcn_rcpf(e4m3_float(dbits) * g) : 0.0f;
+          u32x2_t lo, hi;
+          encode16_hw(w, inv * (1.0f - 0x1p-19f), inv * (1.0f + 0x1p-19f), lo, hi);
+          cw[2 * h] = lo[0];
+          cw[2 * h + 1] = lo[1];
+          open[2 * h] = lo[0] ^ hi[0];
+          open[2 * h + 1] = lo[1] ^ hi[1];
+        } else {
+          const u32x2_t c2 = encode16(w, pack_thresholds(make_thresholds(static_cast<double>(g) * e4m3_value(dbits))));
+          cw[2 * h] = c2[0];
+          cw[2 * h + 1] = c2[1];
+        }
         sc2 |= dbits << (8 * h);
       }
+      if (fast) settle_open(cw, open, cur[i], sc2, g);
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {

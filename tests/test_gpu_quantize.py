@@ -220,6 +220,100 @@ def test_quantize_scale_midpoint_rows():
     assert np.array_equal(u8(got["codes"]), q.pack_codes(c))
 
 
+_MIDPOINTS = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
+
+
+def _bf16_exact(v):
+    return q.round_bf16(np.asarray(v, dtype=np.float64)) == v
+
+
+def _element_tie_rows(rng):
+    """Rows of 16 blocks (K = 256) whose elements sit on, or next to, an E2M1
+    rounding midpoint of their block: x = mu d g exactly (outer scales
+    g = 2^k and 1.5 2^k, with k across and beyond [-100, 100]), the bf16
+    neighbours of those, and for generic outer scales the bf16 values nearest
+    to mu d g found within 2^-17 of it.  Every block keeps its maximum at
+    6 d g (rounded to bf16), so its E4M3 scale is d."""
+    K = 256
+    rows = []
+    e4m3 = q.e4m3_decode(np.arange(1, 0x7F, dtype=np.uint8))   # every positive finite E4M3 value
+
+    def block_of(d, g, elems):
+        bmax = float(q.round_bf16(6.0 * d * g))
+        blk = list(elems)[:15]
+        while len(blk) < 15:
+            blk.append(float(rng.uniform(-bmax, bmax)))
+        blk.append(bmax * rng.choice([-1.0, 1.0]))
+        blk = np.array(blk)
+        rng.shuffle(blk)
+        return np.clip(q.round_bf16(blk), -bmax, bmax)
+
+    # exact ties and their neighbours: g with one or two significant bits
+    for k in (-120, -100, -99, -60, -7, 0, 3, 40, 99, 100, 101, 115):
+        for lead in (1.0, 1.5):
+            if k == 115 and lead == 1.5:
+                continue   # 2688 * 1.5 * 2^115 is past the bf16 range
+            g = lead * 2.0 ** k
+            A = 2688.0 * g
+            assert _bf16_exact(A)
+            blocks = [block_of(448.0, g, [A])]
+            for _ in range(15):
+                d = float(rng.choice(e4m3))
+                elems = []
+                for mu in _MIDPOINTS:
+                    t = mu * d * g
+                    if not _bf16_exact(t):
+                        continue
+                    b = int(q.f64_to_bf16_bits(np.array([t]))[0])
+                    for bb in (b - 1, b, b + 1):
+                        v = float(q.bf16_bits_to_f64(np.array([bb], dtype=np.uint16))[0])
+                        elems.append(v * rng.choice([-1.0, 1.0]))
+                rng.shuffle(elems)
+                blocks.append(block_of(d, g, elems))
+            rows.append(np.concatenate(blocks))
+    # near ties: generic outer scales; per block a random scale d and the
+    # bf16 values nearest to mu d g that lie within 2^-17 of it (not on it)
+    normal = e4m3[e4m3 >= 2.0 ** -6]
+    for _ in range(4):
+        A = float(q.bf16_bits_to_f64(np.array([rng.integers(0x0D00, 0x7300)], dtype=np.uint16))[0])
+        g = float(np.float32(A / 2688.0))
+        blocks = [block_of(448.0, g, [A])]
+        while len(blocks) < 16:
+            elems = []
+            for _ in range(64):
+                d = float(rng.choice(normal))
+                for mu in _MIDPOINTS:
+                    t = mu * d * g
+                    b0 = int(q.f64_to_bf16_bits(np.array([t]))[0])
+                    for bb in (b0 - 1, b0, b0 + 1):
+                        v = float(q.bf16_bits_to_f64(np.array([bb], dtype=np.uint16))[0])
+                        if v != t and abs(v / (d * g) - mu) < mu * 2.0 ** -17:
+                            elems.append(v * rng.choice([-1.0, 1.0]))
+                if elems:
+                    break
+            blocks.append(block_of(d, g, elems))
+        rows.append(np.concatenate(blocks))
+    return np.array(rows)
+
+
+def test_quantize_element_ties():
+    """Elements on and next to E2M1 rounding midpoints (exact ties, bf16
+    neighbours, near ties within 2^-17), over outer scales inside and outside
+    [2^-100, 2^100]: identity routing, bit-exact."""
+    b = _binding()
+    rng = np.random.default_rng(5)
+    x = q.round_bf16(_element_tie_rows(rng))
+    bits = q.f64_to_bf16_bits(x)
+    x = q.bf16_bits_to_f64(bits)
+    print_case("element_tie_rows", rows=x.shape[0], K=x.shape[1])
+    got = b.w4a4_quantize_permute(bf16_dev(bits, torch), None, 1)
+    torch.cuda.synchronize()
+    c, s, g = q.quantize_rows(x)
+    assert np.array_equal(f32_bits(got["outer"]), g.view(np.uint32))
+    assert np.array_equal(u8(got["scales"]), s)
+    assert np.array_equal(u8(got["codes"]), q.pack_codes(c))
+
+
 def test_weight_quantization_identity_mode():
     b = _binding()
     d = synth.make_inputs(16, 512, 4, 2, 256, seed=5)
