@@ -180,93 +180,135 @@ __device__ __forceinline__ float outer_scale(uint32_t amax16) {
 // ------------------------------------------------------------------ routing
 // One workgroup per chunk of kRouteChunk tokens: a bit mask per expert marks
 // the chunk's tokens routed to it; a token's rank inside the chunk is the
-// popcount of the mask below it (stable: ascending token order).  The local
-// rank is parked in row_map and the per-chunk counts in `counts`.
+// number of set bits below it (stable: ascending token order), from a per
+// expert prefix of the mask words' popcounts and the popcount of its own
+// word below its bit.  The local rank is parked in row_map and the
+// per-chunk counts in `counts`.  A token's ids are read once and kept in
+// registers (k <= kMaxRouteK).
 __global__ void __launch_bounds__(kRouteChunk)
 route_count_kernel(const int32_t* __restrict__ topk_idx, int64_t T, int k, int E,
                    int32_t* __restrict__ row_map, int32_t* __restrict__ counts) {
-  extern __shared__ uint32_t masks[];  // [E][kRouteChunk / 32]
   constexpr int W = kRouteChunk / 32;
+  extern __shared__ uint32_t masks[];      // [W][E] masks, then [W][E] popcount prefixes
+  uint32_t* const prefix = masks + E * W;
   const int c = blockIdx.x;
   const int tid = threadIdx.x;
   for (int i = tid; i < E * W; i += kRouteChunk) masks[i] = 0u;
-  __syncthreads();
   const int64_t t = static_cast<int64_t>(c) * kRouteChunk + tid;
   const bool live = t < T;
-  if (live) {
-    for (int j = 0; j < k; ++j) {
-      int e = topk_idx[t * k + j];
-      atomicOr(&masks[e * W + tid / 32], 1u << (tid % 32));
+  int ids[kMaxRouteK];
+#pragma unroll
+  for (int j = 0; j < kMaxRouteK; ++j) ids[j] = (live && j < k) ? topk_idx[t * k + j] : 0;
+  __syncthreads();
+  const int word = tid / 32;
+  const uint32_t bit = 1u << (tid % 32);
+#pragma unroll
+  for (int j = 0; j < kMaxRouteK; ++j)
+    if (live && j < k) atomicOr(&masks[word * E + ids[j]], bit);
+  __syncthreads();
+  for (int e = tid; e < E; e += kRouteChunk) {
+    uint32_t run = 0;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      prefix[w * E + e] = run;
+      run += __popc(masks[w * E + e]);
     }
+    counts[static_cast<int64_t>(c) * E + e] = static_cast<int32_t>(run);
   }
   __syncthreads();
-  if (live) {
-    for (int j = 0; j < k; ++j) {
-      int e = topk_idx[t * k + j];
-      const uint32_t* m = masks + e * W;
-      int rank = __popc(m[tid / 32] & ((1u << (tid % 32)) - 1u));
-      for (int w = 0; w < tid / 32; ++w) rank += __popc(m[w]);
-      row_map[t * k + j] = rank;
+#pragma unroll
+  for (int j = 0; j < kMaxRouteK; ++j) {
+    if (live && j < k) {
+      const int m = word * E + ids[j];
+      row_map[t * k + j] = static_cast<int32_t>(prefix[m] + __popc(masks[m] & (bit - 1u)));
     }
   }
-  for (int e = tid; e < E; e += kRouteChunk) {
-    int n = 0;
-#pragma unroll
-    for (int w = 0; w < W; ++w) n += __popc(masks[e * W + w]);
-    counts[static_cast<int64_t>(c) * E + e] = n;
-  }
+}
+
+// Dynamic LDS of route_count_kernel for E experts.
+inline uint32_t route_count_lds(int E) {
+  return 2u * static_cast<uint32_t>(E) * (kRouteChunk / 32) * sizeof(uint32_t);
 }
 
 // Single workgroup: per expert, exclusive prefix of the chunk counts (in
 // place, giving each chunk's first rank), the expert totals, and the padded
 // expert offsets.  Thread (e, s) owns expert e and a contiguous segment s of
-// the chunks (S = 1024 / E segments): it sums its segment, the segment sums
-// are scanned in LDS, and it then writes its chunks' running prefix.
+// the chunks (S = 1024 / E segments): it sums its segment (keeping the first
+// kKeep counts in registers), the segment sums meet in LDS, and it then
+// writes its chunks' running prefix.  Wave 0 then forms the expert totals and
+// scans the padded group sizes (each lane q = E / 64 consecutive experts in
+// turn, the lanes by a wave prefix sum).
 constexpr int kScanThreads = 1024;
 
 __global__ void __launch_bounds__(kScanThreads)
 route_scan_kernel(int32_t* __restrict__ counts, int n_chunks, int E, int row_align,
                   int32_t* __restrict__ offsets, int32_t* __restrict__ expert_count) {
+  constexpr int kKeep = 16;
   __shared__ int32_t seg[kScanThreads];
-  __shared__ int32_t scan[kScanThreads];
   const int tid = threadIdx.x;
   const int S = max(1, kScanThreads / E);
   const int e = tid % E, sgi = tid / E;
   const bool owner = sgi < S && tid < E * S;
   const int per = (n_chunks + S - 1) / S;
   const int c0 = min(n_chunks, sgi * per), c1 = min(n_chunks, c0 + per);
+  int keep[kKeep];
   int sum = 0;
+#pragma unroll
+  for (int i = 0; i < kKeep; ++i) {
+    keep[i] = (owner && c0 + i < c1) ? counts[static_cast<int64_t>(c0 + i) * E + e] : 0;
+    sum += keep[i];
+  }
   if (owner)
-    for (int c = c0; c < c1; ++c) sum += counts[static_cast<int64_t>(c) * E + e];
+    for (int c = c0 + kKeep; c < c1; ++c) sum += counts[static_cast<int64_t>(c) * E + e];
   seg[tid] = sum;
   __syncthreads();
   if (owner) {
     int run = 0;
     for (int j = 0; j < sgi; ++j) run += seg[j * E + e];   // segments before mine
-    for (int c = c0; c < c1; ++c) {
+#pragma unroll
+    for (int i = 0; i < kKeep; ++i) {
+      if (c0 + i < c1) {
+        counts[static_cast<int64_t>(c0 + i) * E + e] = run;
+        run += keep[i];
+      }
+    }
+    for (int c = c0 + kKeep; c < c1; ++c) {
       const int64_t i = static_cast<int64_t>(c) * E + e;
       const int v = counts[i];
       counts[i] = run;
       run += v;
     }
   }
-  // expert totals and the exclusive scan of the padded group sizes (E <= 1024)
-  int padded = 0;
-  if (tid < E) {
-    int n = 0;
-    for (int j = 0; j < S; ++j) n += seg[j * E + tid];
-    expert_count[tid] = n;
-    padded = (n + row_align - 1) / row_align * row_align;
+  if (tid >= kWave) return;
+  // wave 0: expert totals and the exclusive scan of the padded group sizes
+  // (E <= 1024: at most 16 experts per lane)
+  const int q = (E + kWave - 1) / kWave;
+  int tot = 0;
+  for (int i = 0; i < q; ++i) {
+    const int ee = tid * q + i;
+    if (ee < E) {
+      int n = 0;
+      for (int j = 0; j < S; ++j) n += seg[j * E + ee];
+      expert_count[ee] = n;
+      tot += (n + row_align - 1) / row_align * row_align;
+    }
   }
-  scan[tid] = padded;
-  __syncthreads();
-  for (int off = 1; off < kScanThreads; off <<= 1) {
-    const int v = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += v;
-    __syncthreads();
+  int incl = tot;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int v = __shfl_up(incl, d, kWave);
+    if (tid >= d) incl += v;
   }
-  if (tid < E) offsets[tid + 1] = scan[tid];
+  int run = incl - tot;
+  for (int i = 0; i < q; ++i) {
+    const int ee = tid * q + i;
+    if (ee < E) {
+      int n = 0;
+      for (int j = 0; j < S; ++j) n += seg[j * E + ee];
+      run += (n + row_align - 1) / row_align * row_align;
+      offsets[ee + 1] = run;
+    }
+  }
   if (tid == 0) offsets[0] = 0;
 }
 
@@ -985,8 +1027,8 @@ bool launch_quantize_permute(const uint16_t* x, int64_t T, int K, const int32_t*
     return launch_ok("zero_offsets");
   }
   if (topk_idx != nullptr) {
-    const uint32_t lds = static_cast<uint32_t>(E) * (kRouteChunk / 32) * sizeof(uint32_t);
-    launch_kernel("route_count", route_count_kernel, dim3(static_cast<unsigned>(n_chunks)), dim3(kRouteChunk), lds,
+    launch_kernel("route_count", route_count_kernel, dim3(static_cast<unsigned>(n_chunks)), dim3(kRouteChunk),
+                  route_count_lds(E),
                   s, topk_idx, T, k, E, row_map, counts);
     if (!launch_ok("route_count")) return false;
   }
@@ -1050,8 +1092,8 @@ bool launch_quantize_permute_grouped(const uint16_t* x, int64_t T, int K, const 
   int32_t* counts = static_cast<int32_t*>(ws);
   int32_t* expert_count = counts + n_chunks * E;
   if (topk_idx != nullptr) {
-    const uint32_t lds = static_cast<uint32_t>(E) * (kRouteChunk / 32) * sizeof(uint32_t);
-    launch_kernel("route_count", route_count_kernel, dim3(static_cast<unsigned>(n_chunks)), dim3(kRouteChunk), lds,
+    launch_kernel("route_count", route_count_kernel, dim3(static_cast<unsigned>(n_chunks)), dim3(kRouteChunk),
+                  route_count_lds(E),
                   s, topk_idx, T, k, E, row_map, counts);
     if (!launch_ok("route_count")) return false;
     launch_kernel("route_scan", route_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, counts,
@@ -1100,8 +1142,8 @@ bool launch_quantize_permute_mx(const uint16_t* x, int64_t T, int K, const int32
     return launch_ok("zero_offsets");
   }
   if (topk_idx != nullptr) {
-    const uint32_t lds = static_cast<uint32_t>(E) * (kRouteChunk / 32) * sizeof(uint32_t);
-    launch_kernel("route_count", route_count_kernel, dim3(static_cast<unsigned>(n_chunks)), dim3(kRouteChunk), lds,
+    launch_kernel("route_count", route_count_kernel, dim3(static_cast<unsigned>(n_chunks)), dim3(kRouteChunk),
+                  route_count_lds(E),
                   s, topk_idx, T, k, E, row_map, counts);
     if (!launch_ok("route_count")) return false;
     launch_kernel("route_scan", route_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, counts,
