@@ -624,6 +624,20 @@ __device__ __forceinline__ void encode16_hw(const uint32_t (&w)[8], float ilo, f
   }
 }
 
+// E2M1 codes of the 8 bf16 elements of v (element 2j low in dword j) times
+// 2^sh (one code dword, element 2j in the low nibble of byte j).
+__device__ __forceinline__ uint32_t fp4x8_ldexp(const u32x4_t& v, int sh) {
+  auto pair = [&](uint32_t acc, uint32_t w, auto byte) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, __builtin_amdgcn_ldexpf(bf16_lo(w), sh),
+                                                    __builtin_amdgcn_ldexpf(bf16_hi(w), sh), 1.0f,
+                                                    decltype(byte)::value);
+  };
+  uint32_t r = pair(0u, v[0], std::integral_constant<int, 0>{});
+  r = pair(r, v[1], std::integral_constant<int, 1>{});
+  r = pair(r, v[2], std::integral_constant<int, 2>{});
+  return pair(r, v[3], std::integral_constant<int, 3>{});
+}
+
 // The exact codes of the elements the bracket left open.  The 32 elements of
 // a block pair: code dword k holds elements 8k .. 8k+7 (nibble n: element
 // 8k + n), whose bf16 values are the four dwords of x[k]; nonzero nibbles of
@@ -803,17 +817,13 @@ quant_rows_kernel(const uint16_t* __restrict__ x, int64_t n_rows, int K,
         // eb - 2; zero and subnormal maxima (and eb <= 2) clamp to byte 0
         const uint32_t eb = max(bm[i][0], bm[i][1]) >> 7;
         sc2 = eb > 2u ? eb - 2u : 0u;
-        // 2^X as a double (X >= -127: a normal double), exact midpoints
-        const double unit = __longlong_as_double(static_cast<long long>(sc2 - 127 + 1023) << 52);
-        const PackedThr pt = pack_thresholds(make_thresholds(unit));
+        // the codes of x 2^-X (|x 2^-X| < 8): a bf16 times a power of two is
+        // exact down to 2^-126, and anything smaller meets a zero code (with
+        // the sign of x) either way; the hardware conversion rounds it to
+        // nearest even onto E2M1, saturating at 6
+        const int sh = 127 - static_cast<int>(sc2);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint32_t w[8] = {cur[i][2 * h][0], cur[i][2 * h][1], cur[i][2 * h][2], cur[i][2 * h][3],
-                                 cur[i][2 * h + 1][0], cur[i][2 * h + 1][1], cur[i][2 * h + 1][2], cur[i][2 * h + 1][3]};
-          const u32x2_t c2 = encode16(w, pt);
-          cw[2 * h] = c2[0];
-          cw[2 * h + 1] = c2[1];
-        }
+        for (int q = 0; q < 4; ++q) cw[q] = fp4x8_ldexp(cur[i][q], sh);
       } else {
       u32x4_t open = {0u, 0u, 0u, 0u};
 #pragma unroll

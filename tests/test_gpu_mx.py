@@ -105,18 +105,34 @@ def test_mx_quantize_permute_student_t(A):
 
 
 def test_mx_quantize_edge_rows():
-    """Zero rows, -0, subnormal and huge blocks (scale bytes 0 and 252),
+    """Zero rows, -0, subnormal and huge blocks (scale bytes 0 and 252), and
+    blocks of E2M1 midpoints times 2^X with their bf16 neighbours (exact ties
+    of x / 2^X) for X from the subnormal clamp to the top of the range;
     identity routing."""
     rng = np.random.default_rng(5)
-    v = rng.standard_normal((8, 256))
+    v = rng.standard_normal((12, 256))
     v[0] = 0.0
     v[1, :] = -0.0
     v[2, :32] = 2.0 ** -133
     v[3, 32:64] *= 2.0 ** 126
     v[4, 64:96] *= 2.0 ** -120
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    xs = [-127, -126, -125, -100, -9, -2, 0, 3, 50, 100, 124, 125, -60, 7, -1, 1,
+          20, -20, 64, -64, 110, -110, 90, -90, 30, -30, 11, -11, 2, -3, 5, -5]
+    for blk, X in enumerate(xs):
+        r, c0 = 5 + blk // 8, 32 * (blk % 8)
+        t = mids * 2.0 ** X
+        b = q.f64_to_bf16_bits(t).astype(np.int64)
+        nb = np.concatenate([b - 1, b, b + 1])
+        vals = q.bf16_bits_to_f64(nb[(nb > 0) & (nb < 0x7F80)].astype(np.uint16))
+        vals = vals[np.abs(vals) < 6.0 * 2.0 ** X][:31]
+        row = np.zeros(32)
+        row[:len(vals)] = vals * rng.choice([-1.0, 1.0], len(vals))
+        row[31] = 4.0 * 2.0 ** X * rng.choice([-1.0, 1.0])   # block max: 2^(X+2) sets the scale to 2^X
+        v[r, c0:c0 + 32] = rng.permutation(row)
     bits = q.f64_to_bf16_bits(v)
     x = bf16_dev(bits, torch)
-    print_case("mx_quantize_edges", rows=8, K=256)
+    print_case("mx_quantize_edges", rows=v.shape[0], K=256)
     got = _b().w4a4_mx_quantize_permute(x, None, 1)
     torch.cuda.synchronize()
     c, s = mx.quantize_rows_mx(q.bf16_bits_to_f64(bits))
