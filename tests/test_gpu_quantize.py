@@ -73,6 +73,23 @@ def test_quantize_permute_three_pairs_per_lane(H):
     _compare_qp(d, E, 1, got)
 
 
+@pytest.mark.parametrize("E", [512, 1024])
+def test_quantize_permute_many_experts(E):
+    """Routing over many experts: 36 chunks of 256 tokens, so each scan
+    thread's segment (1024 / E threads per expert) holds 18 or 36 chunk
+    counts, more than the scan keeps in registers; the count kernel loops
+    over E > 256 experts per chunk; the offset scan gives every lane of its
+    wave 8 or 16 experts.  Short rows (H = 64); row_align 1 and 128."""
+    b = _binding()
+    T, H, k = 9000, 64, 8
+    d = synth.make_inputs(T, H, E, k, routing="zipf", x_dist="t3", seed=E + 3, n_empty=7)
+    for A in (1, 128):
+        print_case("quantize_permute_many_experts", T=T, H=H, E=E, k=k, A=A)
+        got = b.w4a4_quantize_permute(bf16_dev(d["x"], torch), torch.from_numpy(d["topk_idx"]).cuda(), E, A)
+        torch.cuda.synchronize()
+        _compare_qp(d, E, A, got)
+
+
 @pytest.mark.parametrize("K", [16, 48, 4112])
 def test_quantize_permute_row_lengths_off_the_fast_path(K):
     """Row lengths that are not a multiple of 32 elements, or longer than 4096,
