@@ -598,8 +598,8 @@ __device__ __forceinline__ float e4m3_float(uint32_t c) {
 // nearest even onto E2M1, saturating at 6, the sign in bit 3), applied to x / D
 // bracketed from both sides.  With ilo = RN(inv (1 - 2^-19)) and
 // ihi = RN(inv (1 + 2^-19)), inv = rcp(RN(D)) within one float ulp, every
-// product RN(x ilo) lies below |x| / D and RN(x ihi) above it (by more than
-// 2^-20 of it: the four roundings add at most 2^-21.4); products that
+// product |RN(x ilo)| lies below |x| / D and |RN(x ihi)| above it (by more
+// than 2^-20 of it: the four roundings add at most 2^-21.4); products that
 // underflow only meet code 0, with the sign of x.  The conversion is monotone,
 // so where the codes of the two products agree (`lo` = `hi`) they are the code
 // of x / D itself; where they differ, by one, an E2M1 midpoint lies between
@@ -645,7 +645,7 @@ __device__ __forceinline__ uint32_t fp4x8_ldexp(const u32x4_t& v, int sh) {
 // the two candidate codes c and c + 1.  The element takes c + 1 when its
 // magnitude exceeds mu d g, mu the E2M1 midpoint between c and c + 1, or equals
 // it and c is odd (the tie goes to the even code); mu d g has at most 31
-// significant bits (mu <= 3, d <= 4, g 24), so the FP64 product and the
+// significant bits (mu at most 3, d 4, g 24), so the FP64 product and the
 // comparison are exact.  One element per lane and iteration; the wave loops
 // while any lane has one left (usually once: about one element in 500 is open
 // for continuous data, mostly where rounding g to float32 put x / D within 2^-24
