@@ -148,6 +148,20 @@ def linear_work(T, K, N):
     return fl, by
 
 
+def host_info():
+    """The host CPUs the oracle may use and their model name (from /proc/cpuinfo)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    return {"host_cpus": len(os.sched_getaffinity(0)), "cpu_model": model}
+
+
 def cpu_baseline_linear(x, w, dy, tokens):
     """The FP64 oracle's linear forward + backward on the first `tokens` tokens
     (the weight's quantisation inside the oracle call is included)."""
@@ -165,7 +179,7 @@ def cpu_baseline_linear(x, w, dy, tokens):
     return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{tokens} tokens of the linear workload (K={w.shape[1]}, N={w.shape[0]}), "
                       f"FP64 numpy, quantize (x and W) + forward + backward, {dt:.1f} s",
-            "seconds": dt, "host_cpus": len(os.sched_getaffinity(0))}
+            "seconds": dt, **host_info()}
 
 
 def main_linear(args):
@@ -270,7 +284,7 @@ def cpu_baseline_qp(d, tokens, group_rows, recipe="nvfp4"):
     return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{tokens} tokens of the quantize+permute workload"
                       f"{' (MXFP4)' if recipe == 'mxfp4' else ''}, FP64 numpy, {dt:.1f} s",
-            "seconds": dt, "host_cpus": len(os.sched_getaffinity(0))}
+            "seconds": dt, **host_info()}
 
 
 def main_qp(args):
@@ -374,8 +388,7 @@ def cpu_baseline(d, w, tokens=512, experts=8, recipe="nvfp4", bwd="bf16"):
             "sample": f"{tokens} tokens of the learner workload (H={w.H}, I={w.I}, k={k}) routed "
                       f"to {experts} experts, FP64 numpy, quantize+permute+forward+backward"
                       f"{' (MXFP4 recipe)' if mx else ''}{' (MXFP8 backward)' if bwd == 'mxfp8' else ''}, "
-                      f"{dt:.1f} s", "seconds": dt,
-            "host_cpus": len(os.sched_getaffinity(0))}
+                      f"{dt:.1f} s", "seconds": dt, **host_info()}
 
 
 def calibration_copy(torch, dev):
