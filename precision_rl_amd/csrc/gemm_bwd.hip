@@ -11,6 +11,14 @@
 //     FC1 wgrad: dW1[e] = dH_e^T . xp_e           M = 2I, N = H   (xp = x gathered by row)
 //
 // MFMA 32x32x16 bf16, FP32 accumulation, waves of 64 x 128 (two per SIMD).
+// The MFMAs take the N-side fragment as their first operand and the M-side
+// fragment as their second (except on the K pieces of a split wgrad, whose
+// FP32 sums leave straight from the registers), which computes the
+// transposed 32 x 32 block: each lane then holds four consecutive columns of
+// one output row per register group, so the epilogue converts them to bf16
+// in pairs and writes them to LDS 8 bytes at a time (a quarter of the LDS
+// writes of the other layout; the products and sums are the same, and so are
+// the results, bit for bit).
 // Operands go global -> LDS through the hardware's copies (no register
 // staging) into a ring a few stages ahead of the MFMAs.  Tiles that are
 // K-contiguous in HBM (dO, dH rows in the dgrad) keep rows of 64 B with their
@@ -28,9 +36,10 @@
 // backward, with 16-byte row-contiguous accesses.
 //
 // wgrad: 256 x 256 tiles, 8 waves, one persistent workgroup per CU with a
-// 4-deep ring of 32 KB stages; at the end of a tile the copies of the next
-// tile's first stages are issued before the epilogue, which moves the bf16
-// tile in four 64-row rounds through a 32 KB staging area with 16-byte stores.
+// 3-deep ring of 32 KB stages (a fourth stage in flight measured no faster);
+// at the end of a tile the copies of the next tile's first stages are issued
+// before the epilogue, which moves the bf16 tile in two 128-row rounds
+// through a 64 KB staging area with 16-byte stores.
 // Both operands are streamed (K = the expert's rows), and the larger tile
 // halves the copy traffic per flop.
 
@@ -102,8 +111,10 @@ constexpr int kRingBytes = kStages * kStageBytes;   // 72 KB
 constexpr int kACopies = kABytes / 1024 / 4;        // 1 KB copies per wave per stage
 constexpr int kBCopies = kBBytes / 1024 / 4;
 constexpr int kDmaPerStage = kACopies + kBCopies;
-// Epilogue staging of the bf16 tile: rows of 512 B padded to 528 B, so the
-// two lane halves of an accumulator write (rows 4 apart) hit different banks.
+// Epilogue staging of the bf16 tile: rows of 512 B padded to 528 B.  An
+// 8-byte accumulator write covers rows r32 = 0..31 of one column group: with
+// the 132-dword pitch, rows r and r + 16 share banks and nothing else does,
+// the two cycles that 128 dwords over 64 banks take anyway.
 constexpr int kOutPitch = kBN * 2 + 16;
 constexpr int kSlotOffset = kRingBytes;
 constexpr int kLdsBytes = kSlotOffset + 16;
@@ -165,7 +176,9 @@ __device__ __forceinline__ void wait_stage_lds(int later) {
 }
 
 // Writes the wave's accumulators as bf16 into the staging tile (row-major,
-// kOutPitch bytes per row); the caller synchronises around it.
+// kOutPitch bytes per row); the caller synchronises around it.  acc[mi][ni]
+// register 4 g + j of lane (r32, hl) is row 32 mi + r32, column
+// 32 ni + 8 g + 4 hl + j of the wave's block.
 __device__ __forceinline__ void stage_out(uint8_t* out_lds, const floatx16_t (&acc)[kMI][kNI],
                                           int wrow, int wcol, int r32, int hl) {
 #pragma unroll
@@ -173,9 +186,12 @@ __device__ __forceinline__ void stage_out(uint8_t* out_lds, const floatx16_t (&a
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni)
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        *reinterpret_cast<uint16_t*>(out_lds + acc_row(wrow, mi, v, hl) * kOutPitch +
-                                     (wcol + ni * 32 + r32) * 2) = f32_to_bf16(acc[mi][ni][v]);
+      for (int vg = 0; vg < 4; ++vg) {
+        const int row = wrow + mi * 32 + r32, col = wcol + ni * 32 + 8 * vg + 4 * hl;
+        const u32x2_t v{pack_bf16x2(acc[mi][ni][4 * vg], acc[mi][ni][4 * vg + 1]),
+                        pack_bf16x2(acc[mi][ni][4 * vg + 2], acc[mi][ni][4 * vg + 3])};
+        *reinterpret_cast<u32x2_t*>(out_lds + row * kOutPitch + col * 2) = v;
+      }
 }
 
 // All waves are past their last LDS read of the ring and every copy has
@@ -293,7 +309,7 @@ dgrad_kernel(DgradArgs args) {
 #pragma unroll
     for (int m = 0; m < kMI * kNI; ++m) {
       const int mi = m / kNI, ni = m % kNI;
-      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sl.a[mi], sl.b[ni], acc[mi][ni], 0, 0, 0);
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sl.b[ni], sl.a[mi], acc[mi][ni], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
       if (have_next) {
         if (m == 0) {
@@ -333,14 +349,14 @@ dgrad_kernel(DgradArgs args) {
   mfma_slice(s0, bc, 1, s1, true);
   mfma_slice(s1, bc, 0, s0, false);
 
-  ring_idle_barrier();
-  stage_out(lds, acc, wrow, wcol, r32, hl);
-  __syncthreads();
   const int rows = static_cast<int>(min<int64_t>(kBM, tc.m_end - tc.m0));
   constexpr int kChunksPerRow = kBN / 8;
   constexpr int kIters = kBM * kChunksPerRow / kThreads;   // 16-byte chunks per thread
   static_assert(kBM * kChunksPerRow % kThreads == 0, "whole chunks per thread");
   if constexpr (MODE == DgradMode::FC1) {
+    ring_idle_barrier();
+    stage_out(lds, acc, wrow, wcol, r32, hl);
+    __syncthreads();
 #pragma unroll 4
     for (int it = 0; it < kIters; ++it) {
       const int c = tid + it * kThreads;
@@ -350,15 +366,15 @@ dgrad_kernel(DgradArgs args) {
       __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(args.out + (tc.m0 + lrow) * args.N + n));
     }
   } else {
-    // SwiGLU backward on bf16 dA, gate / up from the saved bf16 h.  The h
-    // loads of eight chunks go out together (the accumulators are staged,
-    // so registers are free), then the eight are computed and stored.
+    // SwiGLU backward on bf16 dA, gate / up from the saved bf16 h, in two
+    // batches of chunks: the first batch's h loads go out before the
+    // accumulators are staged (their HBM latency runs under the staging),
+    // the second's before the first batch is computed.
     const int I = args.I;
-    constexpr int kBatch = 8;
-    static_assert(kIters % kBatch == 0, "whole batches");
-#pragma unroll 1
-    for (int b0 = 0; b0 < kIters; b0 += kBatch) {
-      u32x4_t hg[kBatch], hu[kBatch];
+    constexpr int kBatch = kIters / 2;
+    static_assert(kIters % 2 == 0, "two whole batches");
+    u32x4_t hg0[kBatch], hu0[kBatch], hg1[kBatch], hu1[kBatch];
+    auto load_h = [&](int b0, u32x4_t (&hg)[kBatch], u32x4_t (&hu)[kBatch]) {
 #pragma unroll
       for (int i = 0; i < kBatch; ++i) {
         // unconditional (clamped to the tile's last row and the last column
@@ -370,6 +386,8 @@ dgrad_kernel(DgradArgs args) {
         hg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(hr));
         hu[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(hr + I));
       }
+    };
+    auto swiglu_store = [&](int b0, const u32x4_t (&hg)[kBatch], const u32x4_t (&hu)[kBatch]) {
 #pragma unroll
       for (int i = 0; i < kBatch; ++i) {
         const int c = tid + (b0 + i) * kThreads;
@@ -396,7 +414,14 @@ dgrad_kernel(DgradArgs args) {
         __builtin_nontemporal_store(dg, reinterpret_cast<u32x4_t*>(args.out + row * (2 * I) + n));
         __builtin_nontemporal_store(du, reinterpret_cast<u32x4_t*>(args.out + row * (2 * I) + I + n));
       }
-    }
+    };
+    load_h(0, hg0, hu0);
+    ring_idle_barrier();
+    stage_out(lds, acc, wrow, wcol, r32, hl);
+    __syncthreads();
+    load_h(kBatch, hg1, hu1);
+    swiglu_store(0, hg0, hu0);
+    swiglu_store(kBatch, hg1, hu1);
   }
 }
 
@@ -405,30 +430,33 @@ dgrad_kernel(DgradArgs args) {
 // ======================================================================= wgrad
 namespace wg {
 
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
 constexpr int kThreads = 512;                       // 8 waves, 4 (M) x 2 (N)
 constexpr int kBM = 256, kBN = 256;                 // workgroup tile
 constexpr int kWM = 64, kWN = 128;                  // wave tile
 constexpr int kMI = kWM / 32, kNI = kWN / 32;
 constexpr int kBK = 32;
-constexpr int kStages = 4;
+constexpr int kStages = 3;
 constexpr int kAhead = kStages - 1;
 constexpr int kABytes = kBM * kBK * 2;              // 16 KB: A, one stage
 constexpr int kBBytes = kBN * kBK * 2;              // 16 KB: B, one stage
 constexpr int kStageBytes = kABytes + kBBytes;
-constexpr int kRingBytes = kStages * kStageBytes;   // 128 KB
+constexpr int kRingBytes = kStages * kStageBytes;   // 96 KB
 constexpr int kACopies = kABytes / 1024 / 8;        // 1 KB copies per wave per stage
 constexpr int kBCopies = kBBytes / 1024 / 8;
 constexpr int kDmaPerStage = kACopies + kBCopies;
-// Epilogue staging: 64 rows of 512 B, 16-byte chunks of rows with bit 2 set
-// swapped by 4 so that the two lane halves of an accumulator write (rows 4
-// apart) land in different banks.
-constexpr int kRoundRows = 64;
+// Epilogue staging: 128 rows of 512 B, the 16-byte chunk c of row s at slot
+// c ^ (s % 32), so that an 8-byte accumulator write (32 rows, one column
+// group) spreads over all banks and a row's 16-byte reads stay a permutation
+// of its chunks.
+constexpr int kRoundRows = 128;
 constexpr int kRowBytes = kBN * 2;
 constexpr int kOutOffset = kRingBytes;
 constexpr int kLdsBytes = kOutOffset + kRoundRows * kRowBytes;   // 160 KB: one workgroup per CU
-// The next tile's table entry is published through ring slot 3, which holds
-// no data between the end of a tile's last stage and the first copy of the
-// next tile's stage 3.
+// The next tile's table entry is published through the last ring slot, which
+// holds no data between the end of a tile's last stage and the first copy of
+// the next tile's stage kStages - 1.
 constexpr int kSlotOffset = (kStages - 1) * kStageBytes;
 
 static_assert(kLdsBytes <= 160 * 1024, "LDS of one workgroup");
@@ -463,30 +491,28 @@ __device__ __forceinline__ void ring_idle_barrier() {
 
 // Byte offset in the staging area of column col of staging row s.
 __device__ __forceinline__ int stage_offset(int s, int col) {
-  return s * kRowBytes + (((col >> 3) ^ (((s >> 2) & 1) * 4)) * 16) + (col & 7) * 2;
+  return s * kRowBytes + (((col >> 3) ^ (s & 31)) * 16) + (col & 7) * 2;
 }
 
-// Round q of the epilogue, first half: every wave writes its accumulator rows
-// [16 q, 16 q + 16) (wave-local) as bf16 into staging rows wm * 16 + 0..15.
+// Round Q of the epilogue, first half: every wave writes its accumulator rows
+// [32 Q, 32 Q + 32) (wave-local, MFMA row block Q) as bf16 into staging rows
+// wm * 32 + 0..31, four consecutive columns per 8-byte write.
 template <int Q>
 __device__ __forceinline__ void stage_round(uint8_t* so, const floatx16_t (&acc)[kMI][kNI], int wm,
                                             int wcol, int r32, int hl) {
-  constexpr int mi = Q >> 1;
 #pragma unroll
-  for (int vb = 0; vb < 2; ++vb)
+  for (int ni = 0; ni < kNI; ++ni)
 #pragma unroll
-    for (int vl = 0; vl < 4; ++vl) {
-      const int v = 4 * (2 * (Q & 1) + vb) + vl;
-      const int s = wm * 16 + 8 * vb + 4 * hl + vl;
-#pragma unroll
-      for (int ni = 0; ni < kNI; ++ni)
-        *reinterpret_cast<uint16_t*>(so + stage_offset(s, wcol + ni * 32 + r32)) =
-            f32_to_bf16(acc[mi][ni][v]);
+    for (int vg = 0; vg < 4; ++vg) {
+      const int sr = wm * 32 + r32, col = wcol + ni * 32 + 8 * vg + 4 * hl;
+      const u32x2_t v{pack_bf16x2(acc[Q][ni][4 * vg], acc[Q][ni][4 * vg + 1]),
+                      pack_bf16x2(acc[Q][ni][4 * vg + 2], acc[Q][ni][4 * vg + 3])};
+      *reinterpret_cast<u32x2_t*>(so + stage_offset(sr, col)) = v;
     }
 }
 
 // Tile row held by staging row s in round q.
-__device__ __forceinline__ int round_tile_row(int s, int q) { return (s >> 4) * kWM + 16 * q + (s & 15); }
+__device__ __forceinline__ int round_tile_row(int s, int q) { return (s >> 5) * kWM + 32 * q + (s & 31); }
 
 // ------------------------------------------------------------------ wgrad
 // Tile schedule of the two wgrad GEMMs, computed on the device from the
@@ -702,6 +728,12 @@ struct WTile {
   int nk;
 };
 
+// SPLIT: the tiles are K pieces whose FP32 sums go to args.partial.  Their
+// MFMAs keep the M-side fragment first, so that a lane holds one column and
+// the 32 lanes of a row write 128 contiguous bytes per store; the transposed
+// order (four columns per lane, for the 8-byte bf16 staging writes) would
+// break those rows into 32-byte pieces (measured 25% slower on split tiles).
+template <bool SPLIT>
 __global__ void __launch_bounds__(kThreads, 1)
 wgrad_kernel(WgradArgs args) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -740,7 +772,7 @@ wgrad_kernel(WgradArgs args) {
     done = true;
     return none;
   };
-  // The next tile passes from thread 0 to all waves through ring slot 3
+  // The next tile passes from thread 0 to all waves through the last ring slot
   // (written only while no wave reads the ring, read by all waves before the
   // slot is refilled).
   u32x4_t* slot = reinterpret_cast<u32x4_t*>(lds + kSlotOffset);
@@ -849,7 +881,10 @@ wgrad_kernel(WgradArgs args) {
 #pragma unroll
       for (int m = 0; m < kMI * kNI; ++m) {
         const int mi = m / kNI, ni = m % kNI;
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sl.a[mi], sl.b[ni], acc[mi][ni], 0, 0, 0);
+        if constexpr (SPLIT)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sl.a[mi], sl.b[ni], acc[mi][ni], 0, 0, 0);
+        else
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sl.b[ni], sl.a[mi], acc[mi][ni], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         if (have_next) {
           if (m == 0) {
@@ -880,11 +915,11 @@ wgrad_kernel(WgradArgs args) {
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       }
     };
-    // Pipeline (4-slot ring, two 16-k slices per stage): the wait for stage
+    // Pipeline (3-slot ring, two 16-k slices per stage): the wait for stage
     // kt+1 sits between the two slices of stage kt, so the first slice of
     // kt+1 is read from LDS under the MFMAs of the second slice of kt.  After
     // that barrier every wave has finished reading stage kt (lgkmcnt 0), so
-    // the copy of stage kt+4 refills its slot.
+    // the copy of stage kt+3 refills its slot.
     if (nk > 0) {
       wait_stage(min(kAhead - 1, nk - 1));
       zero_tail(0);
@@ -920,9 +955,9 @@ wgrad_kernel(WgradArgs args) {
       setup(tn);
       for (int s = 0; s < kAhead && s < tn.nk; ++s) issue(tn, s);
     }
-    if (args.partial != nullptr) {
+    if constexpr (SPLIT) {
       // a K piece: its FP32 sums, stored straight from the accumulators (a
-      // lane's 32 columns of a row are 128 contiguous bytes)
+      // row's 32 columns of an MFMA block are 128 contiguous bytes)
       float* po = args.partial + static_cast<int64_t>(tc.piece) * args.M * args.N;
 #pragma unroll
       for (int mi = 0; mi < kMI; ++mi)
@@ -936,35 +971,29 @@ wgrad_kernel(WgradArgs args) {
             __builtin_nontemporal_store(acc[mi][ni][v], po + static_cast<int64_t>(m) * args.N + n);
           }
         }
-      if (!more) break;
-      tc = tn;
-      continue;
-    }
-    uint16_t* out = args.out + static_cast<int64_t>(tc.e) * args.M * args.N;
+    } else {
+      uint16_t* out = args.out + static_cast<int64_t>(tc.e) * args.M * args.N;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (q == 0) stage_round<0>(so, acc, wm, wcol, r32, hl);
-      else if (q == 1) stage_round<1>(so, acc, wm, wcol, r32, hl);
-      else if (q == 2) stage_round<2>(so, acc, wm, wcol, r32, hl);
-      else stage_round<3>(so, acc, wm, wcol, r32, hl);
-      __syncthreads();
+      for (int q = 0; q < 2; ++q) {
+        if (q == 0) stage_round<0>(so, acc, wm, wcol, r32, hl);
+        else stage_round<1>(so, acc, wm, wcol, r32, hl);
+        __syncthreads();
 #pragma unroll
-      for (int j = 0; j < kRoundRows * 32 / kThreads; ++j) {
-        const int c = tid + j * kThreads;
-        const int s = c >> 5, n = tc.n0 + (c & 31) * 8;
-        if (n >= args.N) continue;
-        __builtin_nontemporal_store(
-            *reinterpret_cast<const u32x4_t*>(so + stage_offset(s, n - tc.n0)),
-            reinterpret_cast<u32x4_t*>(out + static_cast<int64_t>(tc.m0 + round_tile_row(s, q)) * args.N + n));
+        for (int j = 0; j < kRoundRows * 32 / kThreads; ++j) {
+          const int c = tid + j * kThreads;
+          const int s = c >> 5, n = tc.n0 + (c & 31) * 8;
+          if (n >= args.N) continue;
+          __builtin_nontemporal_store(
+              *reinterpret_cast<const u32x4_t*>(so + stage_offset(s, n - tc.n0)),
+              reinterpret_cast<u32x4_t*>(out + static_cast<int64_t>(tc.m0 + round_tile_row(s, q)) * args.N + n));
+        }
+        if (q < 1) __syncthreads();   // staging free for the next round
       }
-      if (q < 3) __syncthreads();   // staging free for the next round
     }
     if (!more) break;
     tc = tn;
   }
 }
-
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // out = bf16(sum_s partial[s]) over the K pieces, in piece order (a fixed
 // order: the result is reproducible).  8 elements per thread.
@@ -1044,11 +1073,15 @@ int wgrad_split_max(int M, int N) {
 size_t wgrad_sched_ints(const WgradPlan& p) { return wg::kSchedTable + 4 * static_cast<size_t>(p.tiles); }
 
 bool launch_wgrad(const wg::WgradArgs& a, const char* name, hipStream_t s, int split = 1) {
-  static const hipError_t attr = set_lds(&wg::wgrad_kernel, wg::kLdsBytes);
-  if (attr != hipSuccess) return launch_ok(name) && false;
+  static const hipError_t attr = set_lds(&wg::wgrad_kernel<false>, wg::kLdsBytes);
+  static const hipError_t attr_split = set_lds(&wg::wgrad_kernel<true>, wg::kLdsBytes);
+  if (attr != hipSuccess || attr_split != hipSuccess) return launch_ok(name) && false;
   const WgradPlan p = wgrad_plan(a.M, a.N, a.E, split);
   if (p.tiles == 0) return true;
-  launch_kernel(name, wg::wgrad_kernel, dim3(p.grid), dim3(wg::kThreads), wg::kLdsBytes, s, a);
+  if (a.partial != nullptr)
+    launch_kernel(name, wg::wgrad_kernel<true>, dim3(p.grid), dim3(wg::kThreads), wg::kLdsBytes, s, a);
+  else
+    launch_kernel(name, wg::wgrad_kernel<false>, dim3(p.grid), dim3(wg::kThreads), wg::kLdsBytes, s, a);
   return launch_ok(name);
 }
 
