@@ -814,13 +814,19 @@ wgrad_kernel(WgradArgs args) {
   // ---- copies: both operands [k = row][256 columns]; rows past the expert's
   // end are re-read from its last row and zeroed in LDS; columns past N are
   // clamped (never stored)
+  // A stage's copies are addressed as a wave-uniform base (the stage's first
+  // row, computed on the scalar unit) plus 32-bit lane offsets fixed per
+  // tile; only an expert's last, partial stage clamps its rows per lane.
   int kk[kACopies], a_col[kACopies], b_col[kBCopies];
+  uint32_t a_off[kACopies], b_off[kBCopies];
   auto setup = [&](const WTile& t) {
 #pragma unroll
     for (int c = 0; c < kACopies; ++c) {
       kk[c] = kcol_copy_k(kACopies * wave + c, lane);
       a_col[c] = t.m0 + kcol_src_chunk(kk[c], lane) * 8;
       b_col[c] = min(t.n0 + kcol_src_chunk(kk[c], lane) * 8, args.N - 8);
+      a_off[c] = static_cast<uint32_t>((kk[c] * args.M + a_col[c]) * 2);
+      b_off[c] = static_cast<uint32_t>((kk[c] * args.N + b_col[c]) * 2);
     }
   };
   static_assert(kACopies == kBCopies, "A and B copies share their k rows");
@@ -828,11 +834,24 @@ wgrad_kernel(WgradArgs args) {
   auto issue = [&](const WTile& t, int kt) {
     const uint32_t st = lds0 + (kt % kStages) * kStageBytes;
     const int64_t r0 = t.r_begin + static_cast<int64_t>(kt) * kBK;
+    const uint16_t* ga = args.g + r0 * args.M;
+    const uint16_t* gb = args.s + r0 * args.N;
+    if (r0 + kBK <= t.r_end) {
 #pragma unroll
-    for (int c = 0; c < kACopies; ++c) {
-      const int64_t r = min(r0 + kk[c], t.r_end - 1);
-      dma16(args.g + r * args.M + a_col[c], st + (kACopies * wave + c) * 1024);
-      dma16(args.s + r * args.N + b_col[c], st + kABytes + (kBCopies * wave + c) * 1024);
+      for (int c = 0; c < kACopies; ++c) {
+        dma16_off(ga, a_off[c], st + (kACopies * wave + c) * 1024);
+        dma16_off(gb, b_off[c], st + kABytes + (kBCopies * wave + c) * 1024);
+      }
+    } else {
+      // rows past the expert's end re-read its last row (zeroed in LDS later)
+      const int last = static_cast<int>(t.r_end - 1 - r0);
+#pragma unroll
+      for (int c = 0; c < kACopies; ++c) {
+        const int kr = min(kk[c], last);
+        dma16_off(ga, static_cast<uint32_t>((kr * args.M + a_col[c]) * 2), st + (kACopies * wave + c) * 1024);
+        dma16_off(gb, static_cast<uint32_t>((kr * args.N + b_col[c]) * 2),
+                  st + kABytes + (kBCopies * wave + c) * 1024);
+      }
     }
   };
 
