@@ -21,19 +21,22 @@
 // the results, bit for bit).
 // Operands go global -> LDS through the hardware's copies (no register
 // staging) into a ring a few stages ahead of the MFMAs.  Tiles that are
-// K-contiguous in HBM (dO, dH rows in the dgrad) keep rows of 64 B with their
-// 16-byte chunks XOR-swizzled by (row / 4) % 4; tiles that are contiguous
+// K-contiguous in HBM (dO, dH rows in the dgrad) arrive two stages at a time,
+// so that each row's copy is one whole 128-byte line (half-line copies took
+// as many L1-to-L2 requests for half the bytes), kept as rows of 128 B with
+// their 16-byte chunks XOR-swizzled by (row / 2) % 8; tiles that are contiguous
 // along M or N in HBM (the weights in the dgrad, both wgrad operands) are kept
 // as [k][columns] rows, chunks swizzled by 4 (k % 4), and read with
 // ds_read_b64_tr_b16, which hands each lane four consecutive k of its column.
 // Both layouts make every read cycle conflict-free.
 //
-// dgrad: 128 x 256 tiles, 4 waves, two workgroups per CU (72 KB of LDS each),
+// dgrad: 128 x 256 tiles, 4 waves, two workgroups per CU (80 KB of LDS each),
 // so that one workgroup's epilogue and waits overlap the other's MFMAs, and
 // an expert's partial last M tile costs at most 128 padded rows.  K advances
-// 32 per stage through a 3-deep ring.  The epilogue stages the bf16 tile in
-// the (then idle) ring and writes it, and reads the saved h of the SwiGLU
-// backward, with 16-byte row-contiguous accesses.
+// 32 per stage: B through a 3-deep ring, A in two buffers of two stages.
+// The epilogue stages the bf16 tile in the (then idle) ring and writes it,
+// and reads the saved h of the SwiGLU backward, with 16-byte row-contiguous
+// accesses.
 //
 // wgrad: 256 x 256 tiles, 8 waves, one persistent workgroup per CU with a
 // 3-deep ring of 32 KB stages (a fourth stage in flight measured no faster);
@@ -68,16 +71,6 @@ __device__ __forceinline__ short4_t ds_read_tr(const __attribute__((address_spac
       (__attribute__((address_space(3))) short4_t*)(p));
 }
 
-// ---- K-contiguous tile: 256 rows x 32 k, 64 B per row, chunk c of row r at
-// slot c ^ ((r >> 2) & 3).  Copy q (16 rows): lane i fills row 16 q + i / 4,
-// slot i % 4.
-__device__ __forceinline__ int krow_src_chunk(int row, int lane) {
-  return (lane & 3) ^ ((row >> 2) & 3);
-}
-__device__ __forceinline__ int krow_frag_offset(int row, int ks, int hl) {
-  return row * 64 + (((ks * 2 + hl) ^ ((row >> 2) & 3)) * 16);
-}
-
 // ---- [k][256] tile: 32 k-rows of 512 B, 16-byte chunk c of k-row k at slot
 // c ^ (4 (k & 3)).  Copy q (2 k-rows): lane i fills k-row 2 q + i / 32, slot
 // i % 32.
@@ -102,37 +95,29 @@ constexpr int kBM = 128, kBN = 256;                 // workgroup tile
 constexpr int kWM = 64, kWN = 128;                  // wave tile
 constexpr int kMI = kWM / 32, kNI = kWN / 32;
 constexpr int kBK = 32;
-constexpr int kStages = 3;
+constexpr int kStages = 3;                          // B ring slots
 constexpr int kAhead = kStages - 1;
-constexpr int kABytes = kBM * kBK * 2;              // 8 KB: A, one stage
+constexpr int kAPairBytes = kBM * 2 * kBK * 2;      // 16 KB: A, two stages (128 B per row)
 constexpr int kBBytes = kBN * kBK * 2;              // 16 KB: B, one stage
-constexpr int kStageBytes = kABytes + kBBytes;
-constexpr int kRingBytes = kStages * kStageBytes;   // 72 KB
-constexpr int kACopies = kABytes / 1024 / 4;        // 1 KB copies per wave per stage
-constexpr int kBCopies = kBBytes / 1024 / 4;
-constexpr int kDmaPerStage = kACopies + kBCopies;
+constexpr int kBOffset = 2 * kAPairBytes;           // two A pair buffers, then the B ring
+constexpr int kRingBytes = kBOffset + kStages * kBBytes;   // 80 KB
+constexpr int kACopies = kAPairBytes / 1024 / 4;    // 1 KB copies per wave per pair
+constexpr int kBCopies = kBBytes / 1024 / 4;        // 1 KB copies per wave per stage
+static_assert(kACopies == kBCopies, "the waits count 4 copies per issue");
 // Epilogue staging of the bf16 tile: rows of 512 B padded to 528 B.  An
 // 8-byte accumulator write covers rows r32 = 0..31 of one column group: with
 // the 132-dword pitch, rows r and r + 16 share banks and nothing else does,
 // the two cycles that 128 dwords over 64 banks take anyway.
 constexpr int kOutPitch = kBN * 2 + 16;
-constexpr int kSlotOffset = kRingBytes;
-constexpr int kLdsBytes = kSlotOffset + 16;
+// The tile map is published through B ring slot 2, which no copy fills
+// before every wave has read it (its first copy follows the first barrier).
+constexpr int kSlotOffset = kBOffset + 2 * kBBytes;
+constexpr int kLdsBytes = kRingBytes;
 
 static_assert(kBM * kOutPitch <= kRingBytes, "output staging must fit in the ring");
 static_assert(2 * kLdsBytes <= 160 * 1024, "two workgroups per CU must fit in LDS");
 
 
-
-// ---- K-contiguous tile: kBM rows x 32 k, 64 B per row, chunk c of row r at
-// slot c ^ ((r >> 2) & 3).  Copy q (16 rows): lane i fills row 16 q + i / 4,
-// slot i % 4.
-__device__ __forceinline__ int krow_src_chunk(int row, int lane) {
-  return (lane & 3) ^ ((row >> 2) & 3);
-}
-__device__ __forceinline__ int krow_frag_offset(int row, int ks, int hl) {
-  return row * 64 + (((ks * 2 + hl) ^ ((row >> 2) & 3)) * 16);
-}
 
 // ---- [k][COLS] tile: 32 k-rows of 2 COLS bytes, 16-byte chunk c of k-row k
 // at slot c ^ (4 (k & 3)).  Copy q (1 KB): lane i fills k-row
@@ -164,14 +149,27 @@ __device__ __forceinline__ void zero_acc(floatx16_t (&acc)[kMI][kNI]) {
       for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
 }
 
-// Waits for stage kt: later = stages issued after it (0 or 1).
-__device__ __forceinline__ void wait_stage(int later) {
-  if (later >= 1) wait_vm_barrier<kDmaPerStage>();
+// Waits for stage s of nk (its A pair and B slot) in every wave.  The copies
+// go out in the order A(0), A(1), B(0), B(1); after the first wait B(2);
+// after the wait for stage kt+1, B(kt+3) and, for odd kt, A((kt+3)/2), four
+// per wave each (pairs and stages that exist).  Loads return in order, so
+// the wait allows the copies issued after stage s's last one: none for the
+// last stage, eight for odd s >= 3, else four (checked against a
+// simulation of this order for every nk < 200).
+__device__ __forceinline__ int copies_after(int s, int nk) {
+  return s == nk - 1 ? 0 : (s >= 3 && (s & 1)) ? 8 : 4;
+}
+__device__ __forceinline__ void wait_stage(int s, int nk) {
+  const int n = copies_after(s, nk);
+  if (n == 8) wait_vm_barrier<8>();
+  else if (n == 4) wait_vm_barrier<4>();
   else wait_vm_barrier<0>();
 }
 // Same, and this wave's LDS reads have completed (lgkmcnt 0) before the barrier.
-__device__ __forceinline__ void wait_stage_lds(int later) {
-  if (later >= 1) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kDmaPerStage) : "memory");
+__device__ __forceinline__ void wait_stage_lds(int s, int nk) {
+  const int n = copies_after(s, nk);
+  if (n == 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if (n == 4) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
@@ -231,17 +229,21 @@ dgrad_kernel(DgradArgs args) {
   const int n0 = tc.n_tile * kBN;
   const int a_rows = static_cast<int>(min<int64_t>(kBM, args.rows_alloc - tc.m0));   // >= 1
 
-  // ---- copies.  A = rows of dO / dH (K-contiguous): scalar base at the
-  // tile's first row plus a lane offset; rows past the allocation are clamped
-  // (they only feed accumulator rows that are never stored).  B = W[e] as
-  // [K][N]: columns past N are clamped (never stored either).
+  // ---- copies.  A = rows of dO / dH (K-contiguous), fetched two stages at
+  // a time so that every row's copy is a whole 128-byte line: pair p (k
+  // 64 p .. 64 p + 63) into buffer p % 2, copy q filling rows 8 q .. 8 q + 7
+  // (lane i: row 8 q + i / 8, slot i % 8, 16-byte chunk c of a row at slot
+  // c ^ ((row / 2) % 8)); rows past the allocation are clamped (they only
+  // feed accumulator rows that are never stored).  B = W[e] as [K][N], one
+  // stage per ring slot: columns past N are clamped (never stored either).
   const uint8_t* a_base = reinterpret_cast<const uint8_t*>(args.g + tc.m0 * args.K);
   const uint8_t* b_base = reinterpret_cast<const uint8_t*>(args.w + static_cast<int64_t>(tc.e) * args.K * args.N);
   uint32_t a_off_src[kACopies], b_off_src[kBCopies];
 #pragma unroll
   for (int c = 0; c < kACopies; ++c) {
-    const int row = 16 * (kACopies * wave + c) + (lane >> 2);
-    a_off_src[c] = static_cast<uint32_t>((min(row, a_rows - 1) * args.K + krow_src_chunk(row, lane) * 8) * 2);
+    const int row = 8 * (kACopies * wave + c) + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+    a_off_src[c] = static_cast<uint32_t>((min(row, a_rows - 1) * args.K + chunk * 8) * 2);
   }
 #pragma unroll
   for (int c = 0; c < kBCopies; ++c) {
@@ -249,27 +251,35 @@ dgrad_kernel(DgradArgs args) {
     const int col = min(n0 + BCol::src_chunk(k, lane) * 8, args.N - 8);
     b_off_src[c] = static_cast<uint32_t>((k * args.N + col) * 2);
   }
-  const int a_step = kBK * 2, b_step = kBK * args.N * 2;   // bytes per stage
+  const int b_step = kBK * args.N * 2;   // bytes per stage
   const uint32_t lds0 = lds_addr(lds);
-  auto issue = [&](int kt) {
-    const uint32_t st = lds0 + (kt % kStages) * kStageBytes;
+  auto issue_a = [&](int p) {
+    const uint32_t st = lds0 + (p & 1) * kAPairBytes;
 #pragma unroll
     for (int c = 0; c < kACopies; ++c)
-      dma16_off(a_base + static_cast<int64_t>(kt) * a_step, a_off_src[c], st + (kACopies * wave + c) * 1024);
+      dma16_off(a_base + static_cast<int64_t>(p) * 128, a_off_src[c], st + (kACopies * wave + c) * 1024);
+  };
+  auto issue_b = [&](int kt) {
+    const uint32_t st = lds0 + kBOffset + (kt % kStages) * kBBytes;
 #pragma unroll
     for (int c = 0; c < kBCopies; ++c)
-      dma16_off(b_base + static_cast<int64_t>(kt) * b_step, b_off_src[c],
-                st + kABytes + (kBCopies * wave + c) * 1024);
+      dma16_off(b_base + static_cast<int64_t>(kt) * b_step, b_off_src[c], st + (kBCopies * wave + c) * 1024);
   };
 
-  // ---- fragment addresses within a stage: a per-lane offset for the first
-  // 32-row (A) / 32-column (B) block; the rest are immediates: +2048 per 32 A
-  // rows, +8192 per 16-k slice of B, +2048 for the second 4-k half of B.
-  uint32_t a_lane[2], b_lane[kNI];
+  // ---- fragment addresses: a per-lane offset for the first 32-row (A) /
+  // 32-column (B) block; the rest are immediates: +4096 per 32 A rows, +8192
+  // per 16-k slice of B, +2048 for the second 4-k half of B.  A's offset
+  // depends on the stage's half of its pair and on the slice.
+  uint32_t a_lane[2][2], b_lane[kNI];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) a_lane[ks] = krow_frag_offset(wrow + r32, ks, hl);
+  for (int h = 0; h < 2; ++h)
 #pragma unroll
-  for (int f = 0; f < kNI; ++f) b_lane[f] = kABytes + BCol::frag_offset(wcol + f * 32, 0, 0, lane);
+    for (int ks = 0; ks < 2; ++ks) {
+      const int row = wrow + r32;
+      a_lane[h][ks] = row * 128 + (((4 * h + 2 * ks + hl) ^ ((row >> 1) & 7)) * 16);
+    }
+#pragma unroll
+  for (int f = 0; f < kNI; ++f) b_lane[f] = BCol::frag_offset(wcol + f * 32, 0, 0, lane);
   floatx16_t acc[kMI][kNI];
   zero_acc(acc);
   struct Slice {
@@ -281,16 +291,24 @@ dgrad_kernel(DgradArgs args) {
     uint32_t a[2], b[kNI];
   };
   auto stage_bases = [&](int kt, Bases& bs) {
-    uint32_t st = lds0 + (kt % kStages) * kStageBytes;
-    asm volatile("" : "+s"(st));   // a wave-uniform value: keep the compiler from re-deriving it per lane
+    uint32_t sa = lds0 + ((kt >> 1) & 1) * kAPairBytes;
+    uint32_t sb = lds0 + kBOffset + (kt % kStages) * kBBytes;
+    asm volatile("" : "+s"(sa), "+s"(sb));   // wave-uniform values: keep the compiler from re-deriving them per lane
+    // the stage's half of its pair picks the lane offsets (a select, not an
+    // indexed load: the four offsets stay in registers)
+    const bool h = kt & 1;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) bs.a[ks] = st + a_lane[ks];
+    for (int ks = 0; ks < 2; ++ks) {
+      uint32_t lo = a_lane[0][ks], hi = a_lane[1][ks];
+      asm volatile("" : "+v"(lo), "+v"(hi));
+      bs.a[ks] = sa + (h ? hi : lo);
+    }
 #pragma unroll
-    for (int f = 0; f < kNI; ++f) bs.b[f] = st + b_lane[f];
+    for (int f = 0; f < kNI; ++f) bs.b[f] = sb + b_lane[f];
   };
   auto load_frag = [&](const Bases& bs, int ks, Slice& sl, int f) {
     if (f < kMI) {
-      sl.a[f] = *lds_ptr<bf16x8_t>(bs.a[ks] + f * 2048);
+      sl.a[f] = *lds_ptr<bf16x8_t>(bs.a[ks] + f * 4096);
     } else {
       const uint32_t p = bs.b[f - kMI] + ks * 8192;
       sl.b[f - kMI] = join_bf16(ds_read_tr(lds_ptr<uint8_t>(p)), ds_read_tr(lds_ptr<uint8_t>(p + 2048)));
@@ -325,15 +343,21 @@ dgrad_kernel(DgradArgs args) {
     }
   };
 
-  const int nk = args.K / kBK;   // >= 1
-  for (int s = 0; s < kAhead && s < nk; ++s) issue(s);
-  // Pipeline (3-slot ring, two 16-k slices per stage): the wait for stage
-  // kt+1 sits between the two slices of stage kt, so the first slice of
-  // kt+1 is read from LDS under the MFMAs of the second slice of kt.  After
-  // that barrier every wave has finished reading stage kt (lgkmcnt 0), so the
-  // copy of stage kt+3 refills its slot.
-  wait_stage(min(kAhead - 1, nk - 1));
-  if (kAhead < nk) issue(kAhead);
+  const int nk = args.K / kBK;   // >= 1, even (K % 64 == 0)
+  const int np = nk / 2;
+  issue_a(0);
+  if (np > 1) issue_a(1);
+  issue_b(0);
+  if (nk > 1) issue_b(1);
+  // Pipeline (two A pair buffers, a 3-slot B ring, two 16-k slices per
+  // stage): the wait for stage kt+1 sits between the two slices of stage kt,
+  // so the first slice of kt+1 is read from LDS under the MFMAs of the
+  // second slice of kt.  After that barrier every wave has finished reading
+  // stage kt (lgkmcnt 0): the copy of stage kt+3 refills its B slot, and
+  // after an odd kt (the pair's second stage) pair (kt+3)/2 refills its A
+  // buffer.
+  wait_stage(0, nk);
+  if (2 < nk) issue_b(2);
   Slice s0, s1;
   Bases bc;
   stage_bases(0, bc);
@@ -341,8 +365,9 @@ dgrad_kernel(DgradArgs args) {
   int kt = 0;
   for (; kt + 1 < nk; ++kt) {
     mfma_slice(s0, bc, 1, s1, true);
-    wait_stage_lds(min(kAhead - 1, nk - 2 - kt));
-    if (kt + 1 + kAhead < nk) issue(kt + 1 + kAhead);
+    wait_stage_lds(kt + 1, nk);
+    if (kt + 3 < nk) issue_b(kt + 3);
+    if ((kt & 1) && (kt + 3) / 2 < np) issue_a((kt + 3) / 2);
     stage_bases(kt + 1, bc);
     mfma_slice(s1, bc, 0, s0, true);
   }
@@ -1059,6 +1084,9 @@ template <dg::DgradMode MODE>
 bool launch_dgrad(const dg::DgradArgs& a, const char* name, hipStream_t s) {
   static const hipError_t attr = set_lds(&dg::dgrad_kernel<MODE>, dg::kLdsBytes);
   if (attr != hipSuccess) return launch_ok(name) && false;
+  // The A operand arrives 64 k at a time: every caller's K (H, 2I, the dense
+  // layer's N) is a multiple of 256, which the shape checks enforce.
+  if (a.K % 64 != 0) return false;
   const int64_t tiles = grouped_m_tiles_bound(a.rows_alloc, a.E, dg::kBM) * ((a.N + dg::kBN - 1) / dg::kBN);
   if (tiles == 0) return true;
   launch_kernel(name, dg::dgrad_kernel<MODE>, dim3(xcd_grid(tiles)), dim3(dg::kThreads), dg::kLdsBytes, s, a);
