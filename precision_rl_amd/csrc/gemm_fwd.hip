@@ -13,21 +13,24 @@
 // E4M3 block scale); decoded operands never touch memory.
 //
 // Tiling: 128 x 256 output tile per workgroup of 4 waves (2 x 2, 64 x 128 per
-// wave), MFMA 32x32x16 f16, and two workgroups per CU (58 KB of LDS and at
-// most 256 registers per wave each), so that one workgroup's epilogue, tile
-// set-up and barrier waits overlap the other's MFMAs, and each SIMD holds two
-// waves whose operand decode interleaves with the other's matrix work.  The
-// 128-row tile also bounds the padding work of an expert's last, partial M
-// tile.  Each pipeline stage covers 64 of K: packed codes (32 B per row) and
-// block scales (4 B per row) of both operands, copied global -> LDS by the
-// hardware (no register staging) into a 4-deep ring, three stages ahead of
-// the MFMAs.  Code rows keep their two 16-byte chunks swapped on every other
-// group of 8 rows, so fragment reads of 16 consecutive rows hit 16 distinct
-// bank groups.  Inside a stage, lane half h (lanes 32-63) owns the stage's
-// second 32 k of its row; A and B use the same assignment, so every MFMA k
-// slot pairs equal k indices (the reduction runs in a permuted K order; FP32
-// rounding of the sum is covered by the tolerance, and sums that are exact in
-// FP32 are order independent).  The epilogue writes the bf16 tile through
+// wave), MFMA 32x32x16 f16, and two workgroups per CU (56.5 / 64.5 KB of LDS
+// and at most 256 registers per wave each), so that one workgroup's
+// epilogue, tile set-up and barrier waits overlap the other's MFMAs, and each
+// SIMD holds two waves whose operand decode interleaves with the other's
+// matrix work.  The 128-row tile also bounds the padding work of an expert's
+// last, partial M tile.  Each pipeline stage covers 64 of K (32 B of packed
+// codes and 4 B of block scales per row of both operands); the codes are
+// copied global -> LDS by the hardware (no register staging) two stages at a
+// time, 64 B per row and copy, into one of two pair buffers (one-stage
+// copies of 32 B per row took as many L1-to-L2 requests for half the bytes);
+// a pair's copies go out in two parts after consecutive stage waits, so that
+// no stage issues them all.  Code rows keep their four 16-byte chunks
+// permuted by (row / 4) % 4, so fragment reads of 16 consecutive rows hit 16
+// distinct bank groups.  Inside a stage, lane half h (lanes 32-63) owns the
+// stage's second 32 k of its row; A and B use the same assignment, so every
+// MFMA k slot pairs equal k indices (the reduction runs in a permuted K
+// order; FP32 rounding of the sum is covered by the tolerance, and sums that
+// are exact in FP32 are order independent).  The epilogue writes the bf16 tile through
 // the idle ring so that global stores are whole 16-byte row chunks
 // (non-temporal: the outputs are read once, by a later kernel).
 
@@ -41,46 +44,46 @@ constexpr int kThreads = 256;                // 4 waves, 2 (M) x 2 (N)
 constexpr int kBM = 128, kBN = 256;          // workgroup tile
 constexpr int kWM = 64, kWN = 128;           // wave tile
 constexpr int kBK = 64;                      // K per stage
-constexpr int kStages = 4;                   // LDS ring depth
-constexpr int kAhead = kStages - 1;          // stages in flight ahead of the MFMAs
 constexpr int kCodeRow = kBK / 2;            // 32 B of codes per row per stage
 constexpr int kScaleRow = kBK / 16;          // 4 scale bytes per row per stage
-constexpr int kACodes = kBM * kCodeRow;      // 4 KB
-constexpr int kBCodes = kBN * kCodeRow;      // 8 KB
 // Scale rows of a stage, 4 B each: A rows 0..127, B rows 128..383, and 128
 // filler rows so that every wave issues the same two copies.
 constexpr int kScaleRows = 512;
 constexpr int kBScaleRow0 = kBM;
-constexpr int kScalesOffset = kACodes + kBCodes;
-constexpr int kStageBytes = kScalesOffset + kScaleRows * 4;     // 14 KB
-constexpr int kDmaPerStage = 5;              // per wave: 1 A-code, 2 B-code, 2 scale copies
+
+// Codes arrive two stages at a time (64 B per row and copy, 16-byte chunk c
+// of row r at slot c ^ ((r >> 2) & 3)) into one of two pair buffers; without
+// grouped scales a pair buffer also holds its two stages' scale dwords.
+constexpr int kPairRow = 2 * kCodeRow;                  // 64 B
+constexpr int kPairACodes = kBM * kPairRow;             // 8 KB
+constexpr int kPairCodes = (kBM + kBN) * kPairRow;      // 24 KB
+constexpr int kPairScales = 2 * kScaleRows * 4;         // 4 KB
 
 // Grouped scales (K a multiple of 256): the scales of four stages, 16 B per
-// row, arrive in one copy issued with the codes of every fourth stage, into
-// one of two 8 KB buffers (same 512-row numbering as above); the ring then
-// holds codes only.
+// row, arrive in one copy issued with the codes of every other pair, into one
+// of two 8 KB buffers after the pair buffers (same 512-row numbering as
+// above).
 constexpr int kGroup = 4;
-constexpr int kCodeStageBytes = kACodes + kBCodes;             // 12 KB
 constexpr int kScaleBufBytes = kScaleRows * 16;                // 8 KB
-constexpr int kGsScaleOffset = kStages * kCodeStageBytes;      // 48 KB
-constexpr int kCodeDmaPerStage = 3;          // per wave: 1 A-code, 2 B-code copies
-constexpr int kScaleDmaPerGroup = 2;         // per wave
+constexpr int kGsScaleOffset = 2 * kPairCodes;                 // 48 KB
 
-// Epilogue staging in the ring: 64 rows of 512 B of bf16 per round, rows
-// padded by 16 B so that the two lane halves' writes (4 rows apart) fall on
-// different banks.
+// Epilogue staging in the pair buffers: 64 rows of 512 B of bf16 per round,
+// rows padded by 16 B so that the two lane halves' writes (4 rows apart) fall
+// on different banks.
 constexpr int kOutRows = 64;
 constexpr int kOutPitch = 528;
-static_assert(kOutRows * kOutPitch <= kStages * kCodeStageBytes, "staging fits in the ring");
+static_assert(kOutRows * kOutPitch <= 2 * kPairCodes, "staging fits in the pair buffers");
 
 template <bool GS>
 struct FwdLds {
-  static constexpr int kStage = GS ? kCodeStageBytes : kStageBytes;
-  static constexpr int kGx = GS ? kGsScaleOffset + 2 * kScaleBufBytes : kStages * kStageBytes;
+  static constexpr int kPair = GS ? kPairCodes : kPairCodes + kPairScales;
+  static constexpr int kGx = GS ? kGsScaleOffset + 2 * kScaleBufBytes : 2 * kPair;
   static constexpr int kSlot = kGx + kBM * 4;
-  static constexpr int kBytes = kSlot + 16;      // 57.9 / 64 KB: two workgroups per CU
+  static constexpr int kBytes = kSlot + 16;      // 56.5 / 64.5 KB: two workgroups per CU
   static_assert(2 * kBytes <= 160 * 1024, "two workgroups per CU must fit in LDS");
 };
+
+__device__ __forceinline__ int pair_slot(int r, int c) { return c ^ ((r >> 2) & 3); }
 
 enum class FwdMode { FC1, FC2 };
 
@@ -113,8 +116,6 @@ __device__ __forceinline__ int b_row_of(int p, int n_tile, int I) {
   }
 }
 
-// LDS position (in 16-byte chunks within the row) of logical code chunk c of row r.
-__device__ __forceinline__ int code_slot(int r, int c) { return c ^ ((r >> 3) & 1); }
 
 __device__ __forceinline__ half8_t decode8(uint32_t codes8, half2_t d2) {
   half2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes8, 1.0f, 0) * d2;
@@ -266,16 +267,19 @@ fwd_gemm_kernel(FwdArgs args) {
   const uint8_t* w_codes = args.w.codes + static_cast<int64_t>(tc.e) * args.N * K2;
   const uint8_t* w_scales = args.w.scales + static_cast<int64_t>(tc.e) * args.N * K16;
   const int a_rows = static_cast<int>(min<int64_t>(kBM, last_row + 1 - tc.m0));   // >= 1
-  uint32_t a_code_off, b_code_off[2];
-  {
-    const int row = 32 * wave + (lane >> 1);                  // A row of this lane's copy
-    a_code_off = static_cast<uint32_t>(min(row, a_rows - 1) * K2 + code_slot(row, lane & 1) * 16);
+  // Code copies per pair: copy q fills 16 staged rows (1 KB), lane i row
+  // 16 q' + i / 4 at slot i % 4; A: q' = 2 wave + q, B: q' = 4 wave + q.
+  uint32_t a_code_off[2], b_code_off[4];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int row = 16 * (2 * wave + q) + (lane >> 2);
+    a_code_off[q] = static_cast<uint32_t>(min(row, a_rows - 1) * K2 + pair_slot(row, lane & 3) * 16);
   }
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int row = 64 * wave + 32 * c + (lane >> 1);        // B row of this lane's copy
-    b_code_off[c] = static_cast<uint32_t>(b_row_of<MODE>(row, tc.n_tile, args.I) * K2 +
-                                          code_slot(row, lane & 1) * 16);
+  for (int q = 0; q < 4; ++q) {
+    const int row = 16 * (4 * wave + q) + (lane >> 2);
+    b_code_off[q] = static_cast<uint32_t>(b_row_of<MODE>(row, tc.n_tile, args.I) * K2 +
+                                          pair_slot(row, lane & 3) * 16);
   }
   // Scales: one dword per scale row per stage, from A or B (per-lane pointer).
   const uint8_t* scale_src[2];
@@ -307,44 +311,59 @@ fwd_gemm_kernel(FwdArgs args) {
     }
   }
   const uint32_t lds0 = lds_addr(lds);
-  auto issue = [&](int kt) {
-    const uint32_t st = lds0 + (kt % kStages) * L::kStage;
+  // Pair p (stages 2p, 2p+1): grouped scales of group p / 2 first (even p),
+  // then the A codes; then the B codes and (ungrouped) the two stages' scale
+  // dwords.  Pairs 0 and 1 go out whole before the loop; later pairs in two
+  // parts, after consecutive waits, so that no stage issues them all.
+  auto issue_a = [&](int p) {
+    const uint32_t st = lds0 + (p & 1) * L::kPair;
     if constexpr (GS) {
-      if (kt % kGroup == 0) {   // the group's scales go out first: they land before the stage's codes
-        const uint32_t sb = lds0 + kGsScaleOffset + ((kt / kGroup) % 2) * kScaleBufBytes;
+      if (p % 2 == 0) {
+        const int g = p / 2;
+        const uint32_t sb = lds0 + kGsScaleOffset + (g % 2) * kScaleBufBytes;
 #pragma unroll
-        for (int c = 0; c < 2; ++c) dma16(gscale_src[c] + (kt / kGroup) * 16, sb + (2 * wave + c) * 1024);
+        for (int c = 0; c < 2; ++c) dma16(gscale_src[c] + g * 16, sb + (2 * wave + c) * 1024);
       }
     }
-    const int cb = kt * kCodeRow;
-    dma16_off(a_codes + cb, a_code_off, st + wave * 1024);
+    const int cb = p * kPairRow;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) dma16_off(w_codes + cb, b_code_off[c], st + kACodes + (2 * wave + c) * 1024);
+    for (int q = 0; q < 2; ++q) dma16_off(a_codes + cb, a_code_off[q], st + (2 * wave + q) * 1024);
+  };
+  auto issue_b = [&](int p) {
+    const uint32_t st = lds0 + (p & 1) * L::kPair;
+    const int cb = p * kPairRow;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dma16_off(w_codes + cb, b_code_off[q], st + kPairACodes + (4 * wave + q) * 1024);
     if constexpr (!GS) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) dma4(scale_src[c] + kt * kScaleRow, st + kScalesOffset + (2 * wave + c) * 256);
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          dma4(scale_src[c] + (2 * p + h) * kScaleRow, st + kPairCodes + h * (kScaleRows * 4) + (2 * wave + c) * 256);
     }
   };
-  // Waits until stage kt (codes and, grouped, its scales) has landed in every
-  // wave: at most the copies this wave issued after stage kt's codes may be
-  // pending.
+  // Waits until stage kt (its pair's codes and its scales) has landed in every
+  // wave.  Pair kt/2 + 1's first part goes out after the wait of each even
+  // kt >= 2 and its second part after the next wait (each part's buffer
+  // region is then done with); loads return in order, so the wait allows the
+  // copies issued after stage kt's last one: at kt <= 1 pair 1's, at odd
+  // kt >= 3 the first part of pair (kt+1)/2, at even kt >= 2 none (checked
+  // against a simulation of this order).
   auto stage_ready = [&](int kt, int nk) {
-    const int later = min(kAhead - 1, nk - 1 - kt);
-    if constexpr (!GS) {
-      if (later >= 2) wait_vm_barrier<2 * kDmaPerStage>();
-      else if (later == 1) wait_vm_barrier<kDmaPerStage>();
-      else wait_vm_barrier<0>();
-    } else {
-      int after = 0;
-      for (int s = kt + 1; s <= kt + later; ++s)
-        after += kCodeDmaPerStage + (s % kGroup == 0 ? kScaleDmaPerGroup : 0);
-      switch (after) {
-        case 8: wait_vm_barrier<8>(); break;
-        case 6: wait_vm_barrier<6>(); break;
-        case 5: wait_vm_barrier<5>(); break;
-        case 3: wait_vm_barrier<3>(); break;
-        default: wait_vm_barrier<0>(); break;
-      }
+    const int np = nk / 2;
+    int after = 0;
+    if (kt <= 1) {
+      after = np > 1 ? (GS ? 6 : 10) : 0;
+    } else if (kt & 1) {
+      const int q = (kt + 1) / 2;
+      after = q < np ? 2 + (GS && q % 2 == 0 ? 2 : 0) : 0;
+    }
+    switch (after) {
+      case 10: wait_vm_barrier<10>(); break;
+      case 6: wait_vm_barrier<6>(); break;
+      case 4: wait_vm_barrier<4>(); break;
+      case 2: wait_vm_barrier<2>(); break;
+      default: wait_vm_barrier<0>(); break;
     }
   };
 
@@ -385,12 +404,22 @@ fwd_gemm_kernel(FwdArgs args) {
   // first A / B row block, and its half (2 of the row's 4 block scales) of the
   // scale dword of the same rows.
   constexpr int kSStride = GS ? 16 : 4;   // bytes per scale row
-  const uint32_t a_code_lane = a_row0 * kCodeRow + code_slot(a_row0, hl) * 16;
-  const uint32_t b_code_lane = kACodes + b_row0 * kCodeRow + code_slot(b_row0, hl) * 16;
+  uint32_t a_code_lane[2], b_code_lane[2];   // by the stage's half of its pair
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    a_code_lane[h] = a_row0 * kPairRow + pair_slot(a_row0, 2 * h + hl) * 16;
+    b_code_lane[h] = kPairACodes + b_row0 * kPairRow + pair_slot(b_row0, 2 * h + hl) * 16;
+  }
   const uint32_t a_scale_lane = a_row0 * kSStride + 2 * hl;
   const uint32_t b_scale_lane = (kBScaleRow0 + b_row0) * kSStride + 2 * hl;
-  const int nk = args.K / kBK;
-  for (int s = 0; s < kAhead && s < nk; ++s) issue(s);
+  const int nk = args.K / kBK;   // even: K % 128 == 0
+  const int np = nk / 2;
+  issue_a(0);
+  issue_b(0);
+  if (np > 1) {
+    issue_a(1);
+    issue_b(1);
+  }
 
   // A wave whose 64 rows all lie past the expert's end (the padding half of
   // a ragged last tile) only copies and waits: its SIMD's matrix core goes to
@@ -398,27 +427,32 @@ fwd_gemm_kernel(FwdArgs args) {
   const bool rows_live = tc.m0 + wm * kWM < tc.m_end;
   for (int kt = 0; kt < nk; ++kt) {
     stage_ready(kt, nk);
-    if (kt + kAhead < nk) issue(kt + kAhead);   // refills the slot read in iteration kt-1
-                                                // (grouped scales: buffer of group kt/4 - 1, done)
+    // refills the buffer of pair kt/2 - 1, read in iterations kt-2 and kt-1
+    // (grouped scales: the buffer of group kt/4 - 1, done)
+    if (kt >= 2 && (kt & 1) == 0 && kt / 2 + 1 < np) issue_a(kt / 2 + 1);
+    if (kt >= 3 && (kt & 1) && (kt + 1) / 2 < np) issue_b((kt + 1) / 2);
     if (!rows_live) continue;
-    // LDS addresses: the stage's base (a scalar) plus this lane's offsets;
-    // the other fragments are immediates (+1024 per 32 code rows, +32 scale
-    // rows)
-    const uint32_t st = opaque_sgpr(lds0 + (kt % kStages) * L::kStage);
+    // LDS addresses: the pair buffer's base (a scalar) plus this lane's
+    // offsets for the stage's half; the other fragments are immediates (+2048
+    // per 32 code rows, +32 scale rows)
+    const uint32_t st = opaque_sgpr(lds0 + ((kt >> 1) & 1) * L::kPair);
     const uint32_t sb = opaque_sgpr(GS ? lds0 + kGsScaleOffset + ((kt / kGroup) % 2) * kScaleBufBytes + (kt % kGroup) * 4
-                                       : st + kScalesOffset);
-    const uint32_t pa = st + a_code_lane, pb = st + b_code_lane;
+                                       : st + kPairCodes + (kt & 1) * (kScaleRows * 4));
+    uint32_t la0 = a_code_lane[0], la1 = a_code_lane[1], lb0 = b_code_lane[0], lb1 = b_code_lane[1];
+    asm volatile("" : "+v"(la0), "+v"(la1), "+v"(lb0), "+v"(lb1));   // a select, not an indexed load
+    const bool h = kt & 1;
+    const uint32_t pa = st + (h ? la1 : la0), pb = st + (h ? lb1 : lb0);
     const uint32_t qa = sb + a_scale_lane, qb = sb + b_scale_lane;
     u32x4_t ac[2], bc[4];
     uint32_t as[2], bs[4];
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
-      ac[f] = *lds_ptr<u32x4_t>(pa + f * 32 * kCodeRow);
+      ac[f] = *lds_ptr<u32x4_t>(pa + f * 32 * kPairRow);
       as[f] = *lds_ptr<uint16_t>(qa + f * 32 * kSStride);
     }
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-      bc[f] = *lds_ptr<u32x4_t>(pb + f * 32 * kCodeRow);
+      bc[f] = *lds_ptr<u32x4_t>(pb + f * 32 * kPairRow);
       bs[f] = *lds_ptr<uint16_t>(qb + f * 32 * kSStride);
     }
     half2_t ad[2][2], bd[4][2];
@@ -869,6 +903,9 @@ template <FwdMode MODE>
 bool launch_fwd(const FwdArgs& args, int n_tiles, const char* name, hipStream_t s) {
   const int64_t tiles = grouped_m_tiles_bound(args.rows_alloc, args.E, kBM) * n_tiles;
   if (tiles == 0) return true;
+  // codes arrive in pairs of 64-k stages: every caller's K (H, I, the dense
+  // layer's K) is a multiple of 128, which the shape checks enforce
+  if (args.K % (2 * kBK) != 0) return false;
   if (args.K % (kGroup * kBK) == 0) return launch_fwd_variant<MODE, true>(args, tiles, name, s);
   return launch_fwd_variant<MODE, false>(args, tiles, name, s);
 }
