@@ -188,6 +188,21 @@ def test_backward_ragged_empty():
         assert not run.g["dw1"][e].any() and not run.g["dw2"][e].any()
 
 
+def test_forward_backward_ungrouped_scales_odd_pairs():
+    """I = 384: FC2's K (384) is not a multiple of 256, so its block scales
+    arrive per stage with the codes (not grouped by four stages), over an odd
+    number (3) of two-stage code copies; FC1 (K = 512) groups them.  The
+    backward's K-contiguous operands arrive in two-stage copies as well
+    (K = 512 and 768).  Forward and backward against the oracle."""
+    T, H, E, k, I = 600, 512, 6, 2, 384
+    d = synth.make_inputs(T, H, E, k, I, routing="zipf", backward=True, seed=384, n_empty=1)
+    print_case("ungrouped_scales", T=T, H=H, E=E, k=k, I=I)
+    run = Run(d, T, H, E, k, I, A=16, backward=True)
+    ref, _, _ = _oracle_fwd(d, E, 16)
+    print(_check_forward(run, ref))
+    print(_check_backward(run, _oracle_bwd(d, E, 16, ref)))
+
+
 def test_backward_skewed_split_experts():
     """Few experts of very different sizes: the wgrad schedule deals the
     tiles of the costly experts in chunks (their tiles, run whole on one
