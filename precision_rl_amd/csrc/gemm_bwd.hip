@@ -323,7 +323,7 @@ dgrad_kernel(DgradArgs args) {
   // MFMAs 1..3, A1 after MFMA 4): each read has seven MFMAs of cover, and the
   // LDS requests of the waves spread over the slice instead of arriving in
   // one burst (FC1 dgrad -1%, both wgrads -2%).
-  auto mfma_slice = [&](const Slice& sl, const Bases& bs, int ks, Slice& nx, bool have_next) {
+  auto mfma_slice = [&](const Slice& sl, const Bases& bs, int ks, Slice& nx, bool have_next, int pair_mid = -1) {
 #pragma unroll
     for (int m = 0; m < kMI * kNI; ++m) {
       const int mi = m / kNI, ni = m % kNI;
@@ -339,6 +339,7 @@ dgrad_kernel(DgradArgs args) {
           load_frag(bs, ks, nx, 1);
         }
       }
+      if (m == kNI && pair_mid >= 0) issue_a(pair_mid);   // apart from the stage's B copies
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -355,7 +356,8 @@ dgrad_kernel(DgradArgs args) {
   // second slice of kt.  After that barrier every wave has finished reading
   // stage kt (lgkmcnt 0): the copy of stage kt+3 refills its B slot, and
   // after an odd kt (the pair's second stage) pair (kt+3)/2 refills its A
-  // buffer.
+  // buffer, issued after the fifth MFMA of the next slice so that its copies
+  // do not queue behind the B copies (FC1 / FC2 dgrad -2%).
   wait_stage(0, nk);
   if (2 < nk) issue_b(2);
   Slice s0, s1;
@@ -367,9 +369,8 @@ dgrad_kernel(DgradArgs args) {
     mfma_slice(s0, bc, 1, s1, true);
     wait_stage_lds(kt + 1, nk);
     if (kt + 3 < nk) issue_b(kt + 3);
-    if ((kt & 1) && (kt + 3) / 2 < np) issue_a((kt + 3) / 2);
     stage_bases(kt + 1, bc);
-    mfma_slice(s1, bc, 0, s0, true);
+    mfma_slice(s1, bc, 0, s0, true, ((kt & 1) && (kt + 3) / 2 < np) ? (kt + 3) / 2 : -1);
   }
   mfma_slice(s0, bc, 1, s1, true);
   mfma_slice(s1, bc, 0, s0, false);
