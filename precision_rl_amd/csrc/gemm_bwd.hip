@@ -922,7 +922,8 @@ wgrad_kernel(WgradArgs args) {
     zero_acc(acc);
     // The slice's MFMAs, the next slice's fragments loaded one at a time in
     // the order the next slice uses them (as in the dgrad).
-    auto mfma_slice = [&](const Slice& sl, const Bases& bs, int ks, Slice& nx, bool have_next) {
+    auto mfma_slice = [&](const Slice& sl, const Bases& bs, int ks, Slice& nx, bool have_next,
+                          int issue_kt = -1) {
 #pragma unroll
       for (int m = 0; m < kMI * kNI; ++m) {
         const int mi = m / kNI, ni = m % kNI;
@@ -941,6 +942,7 @@ wgrad_kernel(WgradArgs args) {
             load_frag(bs, ks, nx, 1);
           }
         }
+        if (m == kNI && issue_kt >= 0) issue(tc, issue_kt);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
@@ -964,7 +966,10 @@ wgrad_kernel(WgradArgs args) {
     // kt+1 sits between the two slices of stage kt, so the first slice of
     // kt+1 is read from LDS under the MFMAs of the second slice of kt.  After
     // that barrier every wave has finished reading stage kt (lgkmcnt 0), so
-    // the copy of stage kt+3 refills its slot.
+    // the copy of stage kt+3 refills its slot; it goes out after the fifth
+    // MFMA of that second slice rather than right at the barrier, where every
+    // wave's copies and first fragment reads would arrive together (both
+    // wgrads -4%).
     if (nk > 0) {
       wait_stage(min(kAhead - 1, nk - 1));
       zero_tail(0);
@@ -978,9 +983,8 @@ wgrad_kernel(WgradArgs args) {
         mfma_slice(s0, bc, 1, s1, true);
         wait_stage_lds(min(kAhead - 1, nk - 2 - kt));
         zero_tail(kt + 1);
-        if (kt + 1 + kAhead < nk) issue(tc, kt + 1 + kAhead);
         stage_bases(kt + 1, bc);
-        mfma_slice(s1, bc, 0, s0, true);
+        mfma_slice(s1, bc, 0, s0, true, kt + 1 + kAhead < nk ? kt + 1 + kAhead : -1);
       }
       mfma_slice(s0, bc, 1, s1, true);
       mfma_slice(s1, bc, 0, s0, false);
