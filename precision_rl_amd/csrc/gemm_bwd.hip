@@ -857,18 +857,21 @@ wgrad_kernel(WgradArgs args) {
   };
   static_assert(kACopies == kBCopies, "A and B copies share their k rows");
   const uint32_t lds0 = lds_addr(lds);
-  auto issue = [&](const WTile& t, int kt) {
+  // part: 1 = the A copies, 2 = the B copies (an expert's last, partial
+  // stage issues all of them with part 2), 3 = both.
+  auto issue = [&](const WTile& t, int kt, int part = 3) {
     const uint32_t st = lds0 + (kt % kStages) * kStageBytes;
     const int64_t r0 = t.r_begin + static_cast<int64_t>(kt) * kBK;
     const uint16_t* ga = args.g + r0 * args.M;
     const uint16_t* gb = args.s + r0 * args.N;
     if (r0 + kBK <= t.r_end) {
 #pragma unroll
-      for (int c = 0; c < kACopies; ++c) {
-        dma16_off(ga, a_off[c], st + (kACopies * wave + c) * 1024);
-        dma16_off(gb, b_off[c], st + kABytes + (kBCopies * wave + c) * 1024);
-      }
-    } else {
+      for (int c = 0; c < kACopies; ++c)
+        if (part & 1) dma16_off(ga, a_off[c], st + (kACopies * wave + c) * 1024);
+#pragma unroll
+      for (int c = 0; c < kBCopies; ++c)
+        if (part & 2) dma16_off(gb, b_off[c], st + kABytes + (kBCopies * wave + c) * 1024);
+    } else if (part & 2) {
       // rows past the expert's end re-read its last row (zeroed in LDS later)
       const int last = static_cast<int>(t.r_end - 1 - r0);
 #pragma unroll
@@ -942,7 +945,8 @@ wgrad_kernel(WgradArgs args) {
             load_frag(bs, ks, nx, 1);
           }
         }
-        if (m == kNI && issue_kt >= 0) issue(tc, issue_kt);
+        if (m == 2 && issue_kt >= 0) issue(tc, issue_kt, 1);
+        if (m == 6 && issue_kt >= 0) issue(tc, issue_kt, 2);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
@@ -966,10 +970,10 @@ wgrad_kernel(WgradArgs args) {
     // kt+1 sits between the two slices of stage kt, so the first slice of
     // kt+1 is read from LDS under the MFMAs of the second slice of kt.  After
     // that barrier every wave has finished reading stage kt (lgkmcnt 0), so
-    // the copy of stage kt+3 refills its slot; it goes out after the fifth
-    // MFMA of that second slice rather than right at the barrier, where every
-    // wave's copies and first fragment reads would arrive together (both
-    // wgrads -4%).
+    // the copy of stage kt+3 refills its slot; its A and B halves go out
+    // after the third and seventh MFMAs of that second slice rather than
+    // right at the barrier, where every wave's copies and first fragment
+    // reads would arrive together (both wgrads -5%).
     if (nk > 0) {
       wait_stage(min(kAhead - 1, nk - 1));
       zero_tail(0);
