@@ -96,7 +96,6 @@ constexpr int kWM = 64, kWN = 128;                  // wave tile
 constexpr int kMI = kWM / 32, kNI = kWN / 32;
 constexpr int kBK = 32;
 constexpr int kStages = 3;                          // B ring slots
-constexpr int kAhead = kStages - 1;
 constexpr int kAPairBytes = kBM * 2 * kBK * 2;      // 16 KB: A, two stages (128 B per row)
 constexpr int kBBytes = kBN * kBK * 2;              // 16 KB: B, one stage
 constexpr int kBOffset = 2 * kAPairBytes;           // two A pair buffers, then the B ring
